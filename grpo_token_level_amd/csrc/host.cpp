@@ -1,0 +1,365 @@
+// Host half of libgrpo: batch plans, group advantages and the step
+// accumulator.  Pure functions of their arguments; no allocation beyond small
+// stack/heap temporaries of the dynamic packer; no HIP calls.
+//
+// Sources: [P1] "Sizing mini-batches and micro-batches"; [P2] "03 Data
+// Protocol and Batch Lifecycle"; [P3] "22 - mini-batch, micro-batch and
+// dynamic batch size"; [P4] "How a context-compaction step fits a variable
+// number of rows into one batch".
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "common.h"
+
+namespace grpo {
+
+namespace {
+thread_local char g_err[512] = "";
+}
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return GRPO_OK;
+}
+
+}  // namespace grpo
+
+using grpo::fail;
+using grpo::ok;
+
+extern "C" const char* grpo_last_error(void) { return grpo::g_err; }
+
+extern "C" const char* grpo_version(void) { return "grpo-mi355x 0.1 (gfx950)"; }
+
+// ---------------------------------------------------------------- plans
+
+// [P1] "The config surface": three replica-level knobs, 0 = unset for mini and
+// micro, derived loop counts, exact divisibility at every level.
+extern "C" int grpo_plan_fixed(int64_t batch, int64_t group_size, int64_t mini, int64_t micro,
+                               int64_t* n_mini, int64_t* n_micro, int64_t* mini_rows,
+                               int64_t* micro_rows) {
+    if (!n_mini || !n_micro || !mini_rows || !micro_rows)
+        return fail(GRPO_EINVAL, "grpo_plan_fixed: NULL output");
+    if (batch <= 0 || group_size <= 0)
+        return fail(GRPO_EINVAL, "grpo_plan_fixed: batch (%lld) and group_size (%lld) must be positive",
+                    (long long)batch, (long long)group_size);
+    if (batch % group_size != 0)
+        return fail(GRPO_EINVAL, "grpo_plan_fixed: batch %lld is not a multiple of group_size %lld",
+                    (long long)batch, (long long)group_size);
+    if (mini < 0 || micro < 0)
+        return fail(GRPO_EINVAL, "grpo_plan_fixed: mini and micro must be >= 0 (0 = unset)");
+    const int64_t mr = mini == 0 ? batch : mini;
+    const int64_t ur = micro == 0 ? mr : micro;
+    if (batch % mr != 0)
+        return fail(GRPO_EDIVISIBLE, "grpo_plan_fixed: mini-batch %lld does not divide batch %lld",
+                    (long long)mr, (long long)batch);
+    if (mr % ur != 0)
+        return fail(GRPO_EDIVISIBLE, "grpo_plan_fixed: micro-batch %lld does not divide mini-batch %lld",
+                    (long long)ur, (long long)mr);
+    *n_mini = batch / mr;
+    *n_micro = mr / ur;
+    *mini_rows = mr;
+    *micro_rows = ur;
+    return ok();
+}
+
+// [P1] "The core idea": chunk (i, j) is the j-th micro slice of the i-th mini
+// slice; the driver only ever names the indices.
+extern "C" int grpo_plan_chunk(int64_t batch, int64_t mini_rows, int64_t micro_rows, int64_t i_mini,
+                               int64_t j_micro, int64_t* row_begin, int64_t* row_end) {
+    if (!row_begin || !row_end) return fail(GRPO_EINVAL, "grpo_plan_chunk: NULL output");
+    if (batch <= 0 || mini_rows <= 0 || micro_rows <= 0 || batch % mini_rows || mini_rows % micro_rows)
+        return fail(GRPO_EINVAL, "grpo_plan_chunk: not a valid fixed plan");
+    if (i_mini < 0 || i_mini >= batch / mini_rows || j_micro < 0 || j_micro >= mini_rows / micro_rows)
+        return fail(GRPO_EINVAL, "grpo_plan_chunk: chunk (%lld, %lld) out of range", (long long)i_mini,
+                    (long long)j_micro);
+    *row_begin = i_mini * mini_rows + j_micro * micro_rows;
+    *row_end = *row_begin + micro_rows;
+    return ok();
+}
+
+// [P3] section 3: token cap per micro-batch, cap >= longest row, box count
+// from the total, workload-balanced assignment, restore index.  The packer is
+// a capacity-constrained greedy (heaviest workload first into the lightest box
+// that fits).  Box loads live in a small array scanned linearly: the box count
+// is ceil(total / budget), tens at most for the budgets in use.
+extern "C" int grpo_plan_dynamic(const int64_t* len, int64_t n_rows, int64_t token_budget,
+                                 int64_t proxy_div, int64_t cap_bins, int64_t* n_bins,
+                                 int64_t* bin_off, int64_t* order, int64_t* restore) {
+    if (!n_bins || n_rows < 0 || (n_rows > 0 && (!len || !order || !restore)) || !bin_off)
+        return fail(GRPO_EINVAL, "grpo_plan_dynamic: NULL pointer or negative n_rows");
+    if (token_budget <= 0 || proxy_div <= 0)
+        return fail(GRPO_EINVAL, "grpo_plan_dynamic: token_budget and proxy_div must be positive");
+    if (cap_bins < 0) return fail(GRPO_EINVAL, "grpo_plan_dynamic: negative cap_bins");
+    int64_t total = 0;
+    for (int64_t i = 0; i < n_rows; ++i) {
+        if (len[i] < 0) return fail(GRPO_EINVAL, "grpo_plan_dynamic: negative length at row %lld", (long long)i);
+        if (len[i] > token_budget)
+            return fail(GRPO_ETOOLONG, "grpo_plan_dynamic: row %lld has %lld tokens > budget %lld",
+                        (long long)i, (long long)len[i], (long long)token_budget);
+        total += len[i];
+    }
+    if (n_rows == 0) {
+        *n_bins = 0;
+        bin_off[0] = 0;
+        return ok();
+    }
+    std::vector<int64_t> work(n_rows);
+    for (int64_t i = 0; i < n_rows; ++i) work[i] = proxy_div * len[i] + len[i] * len[i];
+    std::vector<int64_t> visit(n_rows);
+    std::iota(visit.begin(), visit.end(), int64_t{0});
+    std::sort(visit.begin(), visit.end(), [&](int64_t a, int64_t b) {
+        return work[a] != work[b] ? work[a] > work[b] : a < b;
+    });
+    int64_t k = std::max<int64_t>(1, (total + token_budget - 1) / token_budget);
+    std::vector<int64_t> tok, wsum, box(n_rows);
+    for (;;) {
+        tok.assign(k, 0);
+        wsum.assign(k, 0);
+        bool fits = true;
+        for (int64_t i : visit) {
+            int64_t best = -1;
+            for (int64_t b = 0; b < k; ++b) {
+                if (tok[b] + len[i] > token_budget) continue;
+                if (best < 0 || wsum[b] < wsum[best]) best = b;   // ties keep the lower box
+            }
+            if (best < 0) {
+                fits = false;
+                break;
+            }
+            tok[best] += len[i];
+            wsum[best] += work[i];
+            box[i] = best;
+        }
+        if (fits) break;
+        ++k;
+    }
+    if (k > cap_bins) {
+        *n_bins = k;
+        return fail(GRPO_ECAPACITY, "grpo_plan_dynamic: %lld boxes needed, capacity %lld", (long long)k,
+                    (long long)cap_bins);
+    }
+    // Counting sort by box keeps the original row order inside each box.
+    std::vector<int64_t> count(k + 1, 0);
+    for (int64_t i = 0; i < n_rows; ++i) ++count[box[i] + 1];
+    for (int64_t b = 0; b < k; ++b) count[b + 1] += count[b];
+    for (int64_t b = 0; b <= k; ++b) bin_off[b] = count[b];
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t p = count[box[i]]++;
+        order[p] = i;
+        restore[i] = p;
+    }
+    *n_bins = k;
+    return ok();
+}
+
+// [P4] figure: one row per segment; each group padded to a multiple of Q with
+// pad rows that copy a real row, carry reward 0 and are masked; the step holds
+// exactly the configured rollouts or raises.
+extern "C" int grpo_plan_compaction(const int32_t* rows_per_rollout, int64_t n_rollouts, int64_t n_groups,
+                                    int64_t group_size, int64_t Q, int64_t expected_rollouts,
+                                    int32_t dynamic, int64_t cap_rows, int64_t* n_rows,
+                                    int32_t* row_rollout, int32_t* row_seg, int32_t* row_src,
+                                    uint8_t* row_is_pad, int32_t* group_pad) {
+    if (!n_rows || (n_rollouts > 0 && !rows_per_rollout))
+        return fail(GRPO_EINVAL, "grpo_plan_compaction: NULL pointer");
+    if (dynamic) return fail(GRPO_EINVAL, "grpo_plan_compaction: compaction runs with fixed batching only");
+    if (n_groups <= 0 || group_size <= 0 || Q <= 0)
+        return fail(GRPO_EINVAL, "grpo_plan_compaction: n_groups, group_size and Q must be positive");
+    if (n_groups * group_size != expected_rollouts)
+        return fail(GRPO_ECOUNT, "grpo_plan_compaction: %lld groups x %lld != %lld configured rollouts",
+                    (long long)n_groups, (long long)group_size, (long long)expected_rollouts);
+    if (n_rollouts != expected_rollouts)
+        return fail(GRPO_ECOUNT, "grpo_plan_compaction: the step holds %lld rollouts, %lld configured",
+                    (long long)n_rollouts, (long long)expected_rollouts);
+    int64_t total = 0;
+    for (int64_t r = 0; r < n_rollouts; ++r) {
+        if (rows_per_rollout[r] < 1)
+            return fail(GRPO_EINVAL, "grpo_plan_compaction: rollout %lld has no rows", (long long)r);
+        total += rows_per_rollout[r];
+    }
+    int64_t need = 0;
+    for (int64_t g = 0; g < n_groups; ++g) {
+        int64_t real = 0;
+        for (int64_t r = g * group_size; r < (g + 1) * group_size; ++r) real += rows_per_rollout[r];
+        need += real + ((Q - real % Q) % Q);
+    }
+    if (need > cap_rows) {
+        *n_rows = need;
+        return fail(GRPO_ECAPACITY, "grpo_plan_compaction: %lld rows needed, capacity %lld", (long long)need,
+                    (long long)cap_rows);
+    }
+    if (!row_rollout || !row_seg || !row_src || !row_is_pad || !group_pad)
+        return fail(GRPO_EINVAL, "grpo_plan_compaction: NULL output");
+    (void)total;
+    int64_t out = 0, src = 0;
+    for (int64_t g = 0; g < n_groups; ++g) {
+        const int64_t first = src;
+        int64_t real = 0;
+        for (int64_t r = g * group_size; r < (g + 1) * group_size; ++r) {
+            for (int32_t k = 0; k < rows_per_rollout[r]; ++k) {
+                row_rollout[out] = (int32_t)r;
+                row_seg[out] = k;
+                row_src[out] = (int32_t)(src++);
+                row_is_pad[out] = 0;
+                ++out;
+                ++real;
+            }
+        }
+        const int64_t pad = (Q - real % Q) % Q;
+        group_pad[g] = (int32_t)pad;
+        for (int64_t k = 0; k < pad; ++k) {
+            row_rollout[out] = -1;
+            row_seg[out] = -1;
+            row_src[out] = (int32_t)first;
+            row_is_pad[out] = 1;
+            ++out;
+        }
+    }
+    *n_rows = out;
+    return ok();
+}
+
+extern "C" int grpo_row_offsets(const int64_t* len, const int64_t* order, int64_t n_rows, int64_t* row_off) {
+    if (n_rows < 0 || !row_off || (n_rows > 0 && !len)) return fail(GRPO_EINVAL, "grpo_row_offsets: bad arguments");
+    row_off[0] = 0;
+    for (int64_t k = 0; k < n_rows; ++k) {
+        int64_t r = k;
+        if (order) {
+            r = order[k];
+            if (r < 0 || r >= n_rows) return fail(GRPO_EINVAL, "grpo_row_offsets: order[%lld] out of range", (long long)k);
+        }
+        if (len[r] < 0) return fail(GRPO_EINVAL, "grpo_row_offsets: negative length");
+        row_off[k + 1] = row_off[k] + len[r];
+    }
+    return ok();
+}
+
+// ---------------------------------------------------------------- advantage
+
+// [P2] "Field Lineage": advantages come from trajectory rewards once per
+// update; [P4] item 2: one value per rollout.  Formula not on the pages:
+// (r - mean) / (unbiased std + eps), or r - mean, or 0 for groups of one.
+extern "C" int grpo_group_advantage(const float* reward, int64_t n_rollouts, int64_t group_size, float eps,
+                                    int32_t norm_by_std, float* adv_rollout) {
+    if (n_rollouts < 0 || group_size <= 0 || (n_rollouts > 0 && (!reward || !adv_rollout)))
+        return fail(GRPO_EINVAL, "grpo_group_advantage: bad arguments");
+    if (n_rollouts % group_size != 0)
+        return fail(GRPO_EINVAL, "grpo_group_advantage: %lld rollouts is not a whole number of groups of %lld",
+                    (long long)n_rollouts, (long long)group_size);
+    const int64_t G = group_size;
+    for (int64_t g = 0; g < n_rollouts / G; ++g) {
+        const float* r = reward + g * G;
+        float* a = adv_rollout + g * G;
+        if (G == 1) {
+            a[0] = 0.0f;
+            continue;
+        }
+        double sum = 0.0;
+        for (int64_t k = 0; k < G; ++k) sum += (double)r[k];
+        const double mean = sum / (double)G;
+        double sq = 0.0;
+        for (int64_t k = 0; k < G; ++k) sq += ((double)r[k] - mean) * ((double)r[k] - mean);
+        const double sd = std::sqrt(sq / (double)(G - 1));
+        for (int64_t k = 0; k < G; ++k) {
+            const double d = (double)r[k] - mean;
+            a[k] = (float)(norm_by_std ? d / (sd + (double)eps) : d);
+        }
+    }
+    return ok();
+}
+
+extern "C" int grpo_rows_advantage(const float* adv_rollout, int64_t n_rollouts, const int32_t* row_rollout,
+                                   int64_t n_rows, float* adv_row) {
+    if (n_rows < 0 || n_rollouts < 0 || (n_rows > 0 && (!row_rollout || !adv_row)))
+        return fail(GRPO_EINVAL, "grpo_rows_advantage: bad arguments");
+    for (int64_t i = 0; i < n_rows; ++i) {
+        if (row_rollout[i] >= n_rollouts)
+            return fail(GRPO_EINVAL, "grpo_rows_advantage: row %lld names rollout %d of %lld", (long long)i,
+                        row_rollout[i], (long long)n_rollouts);
+    }
+    for (int64_t i = 0; i < n_rows; ++i) adv_row[i] = row_rollout[i] < 0 ? 0.0f : adv_rollout[row_rollout[i]];
+    return ok();
+}
+
+// ---------------------------------------------------------------- accumulator
+
+namespace {
+void stats_zero(grpo_stats* s) { std::memset(s, 0, sizeof(*s)); }
+void stats_add(grpo_stats* a, const grpo_stats* b) {
+    a->loss_sum += b->loss_sum;
+    a->entropy_sum += b->entropy_sum;
+    a->n_valid += b->n_valid;
+    a->n_clipped += b->n_clipped;
+    a->n_nonfinite += b->n_nonfinite;
+    a->n_valid_rows += b->n_valid_rows;
+}
+}  // namespace
+
+extern "C" int grpo_accum_init(grpo_accum* acc, int64_t n_micro) {
+    if (!acc || n_micro < 1) return fail(GRPO_EINVAL, "grpo_accum_init: n_micro must be >= 1");
+    std::memset(acc, 0, sizeof(*acc));
+    acc->n_micro = n_micro;
+    return ok();
+}
+
+// [P1] "The poisoned-window countdown": on a non-finite chunk the window is
+// discarded and exactly the remaining chunks of that window are swallowed.
+extern "C" int grpo_accum_add(grpo_accum* acc, const grpo_stats* c) {
+    if (!acc || !c || acc->n_micro < 1) return fail(GRPO_EINVAL, "grpo_accum_add: bad arguments");
+    if (acc->done) return fail(GRPO_ESTATE, "grpo_accum_add: finalize the completed window first");
+    if (acc->skip > 0) {
+        --acc->skip;
+        return fail(GRPO_ESKIPPED, "grpo_accum_add: call swallowed, %lld more to skip", (long long)acc->skip);
+    }
+    if (c->n_nonfinite > 0 || !std::isfinite(c->loss_sum) || !std::isfinite(c->entropy_sum)) {
+        acc->skip = acc->n_micro - 1 - acc->pos;
+        acc->pos = 0;
+        stats_zero(&acc->open);
+        return fail(GRPO_ENONFINITE, "grpo_accum_add: non-finite chunk; window discarded, %lld calls to skip",
+                    (long long)acc->skip);
+    }
+    stats_add(&acc->open, c);
+    if (++acc->pos == acc->n_micro) {
+        acc->closed = acc->open;
+        acc->done = 1;
+        acc->pos = 0;
+        stats_zero(&acc->open);
+    }
+    return ok();
+}
+
+// [P1] "Metric roll-up": token-weighted loss, summed counts; "The hard part":
+// one gradient scale 1/max(sum of divisors, 1).
+extern "C" int grpo_accum_finalize(grpo_accum* acc, grpo_step_result* out, int32_t* stepped) {
+    if (!acc || !out || !stepped) return fail(GRPO_EINVAL, "grpo_accum_finalize: NULL argument");
+    if (!acc->done) {
+        *stepped = 0;
+        return ok();
+    }
+    const grpo_stats& s = acc->closed;
+    const double denom = (double)std::max<int64_t>(s.n_valid, 1);
+    out->loss = s.loss_sum / denom;
+    out->entropy = s.entropy_sum / denom;
+    out->grad_scale = 1.0 / denom;
+    out->n_valid = s.n_valid;
+    out->n_valid_rows = s.n_valid_rows;
+    out->n_clipped = s.n_clipped;
+    acc->done = 0;
+    stats_zero(&acc->closed);
+    *stepped = 1;
+    return ok();
+}

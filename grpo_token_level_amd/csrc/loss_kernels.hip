@@ -1,0 +1,771 @@
+// Device half of libgrpo for gfx950 (CDNA4): the fused token-level GRPO loss
+// forward/backward, the forward-only log-prob pass, the row/chunk statistics
+// reductions, and two small layout helpers.
+//
+// Sources: [P1] "Sizing mini-batches and micro-batches" ("The hard part:
+// deferred normalization", "pi_old must be frozen across the window");
+// [P2] "03 Data Protocol and Batch Lifecycle" ("Field Lineage": response
+// mask, advantage broadcast); [P4] "How a context-compaction step fits a
+// variable number of rows into one batch" ("Why the row count does not change
+// the math").
+//
+// Design (HBM-bound streaming, no MFMA: there is no contraction here).
+// One token row of V logits is read from HBM exactly once into registers:
+//   * large V (e.g. 151936 bf16 = 297 KiB): one 1024-thread workgroup per
+//     token; each lane holds NV 16-byte vectors (NV = 19 -> 76 VGPRs).
+//     Reductions: wave64 butterfly, then the 16 wave partials through LDS in a
+//     fixed order.
+//   * small V (<= 4096 bf16 / 2048 fp32): one wave64 per token, four tokens
+//     per 256-thread workgroup, no LDS and no barrier at all.
+// Three sweeps over the registers: max; sum of 2^t and sum of 2^t * t with
+// t = z*log2(e) - max*log2(e) (one FMA + v_exp_f32 per element); then the write
+// of dz = coef * 2^(z*log2(e) - lse*log2(e)) minus coef at the target.  The
+// logits are never re-read, dlogits are written once with 16-byte stores, so
+// the kernel moves V*(in + out) bytes per valid token and V*out per masked one.
+// Rows whose stride or base is not 16-byte aligned, or whose V exceeds what the
+// register file holds, take a generic kernel that streams the row three times
+// from memory (correct for any layout, slower).
+//
+// Every reduction has a fixed order, nothing uses floating-point atomics, so
+// results are bit-for-bit reproducible and a token's outputs depend only on
+// its own row, never on its position in the chunk.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "common.h"
+
+using grpo::fail;
+using grpo::ok;
+
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegClampLog2 = -128.0f;   // below this 2^t is under every fp32 normal
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---------------------------------------------------------------- dtype traits
+
+template <int DT> struct In;
+template <> struct In<GRPO_BF16> {
+    static constexpr int VEC = 8;                      // elements per 16-byte vector
+    static constexpr int BYTES = 2;
+    static constexpr uint32_t NEG_INF2 = 0xff80ff80u;  // two bf16 -inf
+    __device__ static __forceinline__ void unpack(const uint4& v, float (&f)[8]) {
+        f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+        f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+    }
+    __device__ static __forceinline__ float scalar(const void* row, int64_t i) {
+        const uint16_t b = reinterpret_cast<const uint16_t*>(row)[i];
+        return __uint_as_float((uint32_t)b << 16);
+    }
+};
+template <> struct In<GRPO_F32> {
+    static constexpr int VEC = 4;
+    static constexpr int BYTES = 4;
+    static constexpr uint32_t NEG_INF2 = 0xff800000u;  // one fp32 -inf
+    __device__ static __forceinline__ void unpack(const uint4& v, float (&f)[4]) {
+        f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+    }
+    __device__ static __forceinline__ float scalar(const void* row, int64_t i) {
+        return reinterpret_cast<const float*>(row)[i];
+    }
+};
+
+template <int DT> struct Out;
+template <> struct Out<GRPO_BF16> {
+    static constexpr int BYTES = 2;
+    template <int N>
+    __device__ static __forceinline__ void store(void* row, int e0, const float (&d)[N]) {
+        uint16_t* p = reinterpret_cast<uint16_t*>(row) + e0;
+        if constexpr (N == 8) {
+            uint4 v;
+            v.x = pack_bf16x2(d[0], d[1]); v.y = pack_bf16x2(d[2], d[3]);
+            v.z = pack_bf16x2(d[4], d[5]); v.w = pack_bf16x2(d[6], d[7]);
+            *reinterpret_cast<uint4*>(p) = v;
+        } else {
+            uint2 v;
+            v.x = pack_bf16x2(d[0], d[1]); v.y = pack_bf16x2(d[2], d[3]);
+            *reinterpret_cast<uint2*>(p) = v;
+        }
+    }
+    template <int N>
+    __device__ static __forceinline__ void zero(void* row, int e0) {
+        uint16_t* p = reinterpret_cast<uint16_t*>(row) + e0;
+        if constexpr (N == 8) *reinterpret_cast<uint4*>(p) = make_uint4(0, 0, 0, 0);
+        else *reinterpret_cast<uint2*>(p) = make_uint2(0, 0);
+    }
+    __device__ static __forceinline__ void scalar(void* row, int64_t i, float d) {
+        f32x2 v = {d, 0.0f};
+        bf16x2 r = __builtin_convertvector(v, bf16x2);
+        reinterpret_cast<uint16_t*>(row)[i] = (uint16_t)(__builtin_bit_cast(uint32_t, r) & 0xffffu);
+    }
+};
+template <> struct Out<GRPO_F32> {
+    static constexpr int BYTES = 4;
+    template <int N>
+    __device__ static __forceinline__ void store(void* row, int e0, const float (&d)[N]) {
+        float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(row) + e0);
+        p[0] = make_float4(d[0], d[1], d[2], d[3]);
+        if constexpr (N == 8) p[1] = make_float4(d[4], d[5], d[6], d[7]);
+    }
+    template <int N>
+    __device__ static __forceinline__ void zero(void* row, int e0) {
+        float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(row) + e0);
+        p[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (N == 8) p[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __device__ static __forceinline__ void scalar(void* row, int64_t i, float d) {
+        reinterpret_cast<float*>(row)[i] = d;
+    }
+};
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+// Butterfly: every lane ends with the same bits (each step adds the same pair).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+__device__ __forceinline__ long long wave_sum_i(long long x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// An empty asm that claims to rewrite the register-resident row: the unpacked
+// floats of one sweep cannot then be kept alive into the next sweep (that
+// would double the row's register footprint and spill); each sweep re-derives
+// them from the packed registers with one ALU op per element.
+template <int NV>
+__device__ __forceinline__ void opaque_regs(uint4 (&x)[NV]) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) asm volatile("" : "+v"(x[k].x), "+v"(x[k].y), "+v"(x[k].z), "+v"(x[k].w));
+}
+
+// ---------------------------------------------------------------- parameters
+
+struct TokParams {
+    const void* logits;
+    int64_t ld;
+    int64_t n_tok;
+    int64_t V;
+    const int32_t* target;
+    const uint8_t* mask;
+    const float* old_logp;
+    const int32_t* tok_row;
+    const float* adv_row;
+    int64_t n_rows;
+    float eps_low, eps_high, scale;
+    const int64_t* denom;
+    void* dlogits;
+    int64_t ld_out;
+    float* logp;
+    float* lse;
+    float* entropy;
+    float* loss_tok;
+    uint8_t* tok_flags;
+};
+
+// Per-token scalar tail shared by both kernels: from (max-shifted sums, z_y)
+// to logp / entropy / surrogate / gradient coefficient.  c = the log2-domain
+// shift used for the sums, s = sum 2^t, w = sum 2^t * t.
+struct TokenResult {
+    float c2;      // log2-domain logsumexp: p_v = 2^(z_v*log2e - c2)
+    float coef;    // dlogits_v = coef * (p_v - [v == y])
+};
+
+template <bool GRAD>
+__device__ __forceinline__ TokenResult token_tail(const TokParams& p, int64_t t, float c, float s, float w,
+                                                  float zy, bool ybad, bool write) {
+    const float log2s = log2f(s);
+    const float c2 = c + log2s;
+    const float lse = c2 * kLn2;
+    const float logp = ybad ? __builtin_nanf("") : zy - lse;
+    const float H = kLn2 * (log2s - w / s);
+    TokenResult r{c2, 0.0f};
+    if constexpr (!GRAD) {
+        if (write) {
+            p.logp[t] = logp;
+            if (p.lse) p.lse[t] = lse;
+            if (p.entropy) p.entropy[t] = H;
+        }
+        return r;
+    } else {
+        const int32_t row = p.tok_row[t];
+        const float A = ((uint32_t)row < (uint64_t)p.n_rows) ? p.adv_row[row] : __builtin_nanf("");
+        const float rho = expf(logp - p.old_logp[t]);
+        const float lo = 1.0f - p.eps_low, hi = 1.0f + p.eps_high;
+        const float s1 = rho * A;
+        const float s2 = fminf(fmaxf(rho, lo), hi) * A;
+        const float l = -fminf(s1, s2);
+        const bool clipped = (A > 0.0f && rho > hi) || (A < 0.0f && rho < lo);
+        float sc = p.scale;
+        if (p.denom) {
+            const int64_t n = *p.denom;
+            sc = (float)((double)p.scale / (double)(n > 1 ? n : 1));
+        }
+        const float coef = clipped ? 0.0f : sc * A * rho;
+        const bool bad = !(isfinite(logp) && isfinite(l) && isfinite(H));
+        if (write) {
+            p.logp[t] = logp;
+            if (p.lse) p.lse[t] = lse;
+            p.entropy[t] = H;
+            p.loss_tok[t] = l;
+            p.tok_flags[t] = (uint8_t)(1u | (clipped ? 2u : 0u) | (bad ? 4u : 0u));
+        }
+        r.coef = coef;
+        return r;
+    }
+}
+
+template <bool GRAD>
+__device__ __forceinline__ void masked_outputs(const TokParams& p, int64_t t) {
+    p.logp[t] = 0.0f;
+    if (p.lse) p.lse[t] = 0.0f;
+    if (p.entropy) p.entropy[t] = 0.0f;
+    if constexpr (GRAD) {
+        p.loss_tok[t] = 0.0f;
+        p.tok_flags[t] = 0;
+    }
+}
+
+// ---------------------------------------------------------------- register-resident kernel
+//
+// TPR threads per token row, NV 16-byte vectors per thread.  TPR == 64: four
+// token rows per 256-thread block, one wave each, wave-only reductions.
+// TPR > 64: one row per block, cross-wave reduction through LDS.
+template <int DTI, int DTO, int TPR, int NV, bool GRAD>
+__global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const TokParams p) {
+    constexpr int VEC = In<DTI>::VEC;
+    constexpr int WPR = TPR / 64;
+    constexpr int RPB = TPR == 64 ? 4 : 1;
+    const int lrow = RPB == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int tid = RPB == 1 ? (int)threadIdx.x : (int)(threadIdx.x & 63);
+    const int64_t t = (int64_t)blockIdx.x * RPB + lrow;
+    if (t >= p.n_tok) return;   // wave-uniform (RPB > 1) or block-uniform (RPB == 1)
+
+    const int nvec = (int)(p.V / VEC);   // the register path only runs for V / VEC <= TPR * NV
+    void* orow = nullptr;
+    if constexpr (GRAD) {
+        if (p.dlogits) orow = reinterpret_cast<char*>(p.dlogits) + t * p.ld_out * Out<DTO>::BYTES;
+    }
+
+    if (p.mask[t] == 0) {
+        if (tid == 0) masked_outputs<GRAD>(p, t);
+        if constexpr (GRAD) {
+            if (orow) {
+#pragma unroll
+                for (int k = 0; k < NV; ++k) {
+                    const int idx = k * TPR + tid;
+                    if (idx < nvec) Out<DTO>::template zero<VEC>(orow, idx * VEC);
+                }
+            }
+        }
+        return;
+    }
+
+    const char* irow = reinterpret_cast<const char*>(p.logits) + t * p.ld * In<DTI>::BYTES;
+    const uint4* vrow = reinterpret_cast<const uint4*>(irow);
+
+    // Target logit: read by the one lane that owns element y (it alone later
+    // writes dlogits[y], so an in-place update stays ordered).
+    const int32_t y = p.target[t];
+    const bool ybad = (uint32_t)y >= (uint64_t)p.V;
+    const int vy = ybad ? 0 : y / VEC;
+    const int own_tid = vy % TPR;
+    float zy_mine = 0.0f;
+    if (!ybad && tid == own_tid) zy_mine = In<DTI>::scalar(irow, y);
+
+    // Lanes past the row end load the last vector again (in bounds) and then
+    // hold -inf, which no sweep can see: it loses every max, adds 2^-inf = 0.
+    uint4 x[NV];
+    constexpr uint32_t NEG = In<DTI>::NEG_INF2;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int idx = k * TPR + tid;
+        const bool in = idx < nvec;
+        const uint4 v = vrow[in ? idx : nvec - 1];
+        x[k].x = in ? v.x : NEG;
+        x[k].y = in ? v.y : NEG;
+        x[k].z = in ? v.z : NEG;
+        x[k].w = in ? v.w : NEG;
+    }
+
+    // sweep 1: max
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        float f[VEC];
+        In<DTI>::unpack(x[k], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) m = fmaxf(m, f[e]);
+    }
+    m = wave_max(m);
+
+    [[maybe_unused]] __shared__ float s_max[WPR];
+    [[maybe_unused]] __shared__ float s_sum[WPR][2];
+    [[maybe_unused]] __shared__ float s_zy;
+    float zy;
+    if constexpr (WPR == 1) {
+        zy = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zy_mine), own_tid));
+    } else {
+        const int wave = tid >> 6;
+        if ((tid & 63) == 0) s_max[wave] = m;
+        if (tid == own_tid) s_zy = zy_mine;
+        __syncthreads();
+        m = s_max[0];
+#pragma unroll
+        for (int i = 1; i < WPR; ++i) m = fmaxf(m, s_max[i]);
+        zy = s_zy;
+    }
+
+    // sweep 2: s = sum 2^t, w = sum 2^t * t
+    opaque_regs(x);
+    const float c = m * kLog2e;
+    float s = 0.0f, w = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        float f[VEC];
+        In<DTI>::unpack(x[k], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float tt = fmaf(f[e], kLog2e, -c);
+            const float ee = __builtin_amdgcn_exp2f(tt);
+            s += ee;
+            w = fmaf(ee, fmaxf(tt, kNegClampLog2), w);
+        }
+    }
+    s = wave_sum(s);
+    w = wave_sum(w);
+    if constexpr (WPR > 1) {
+        const int wave = tid >> 6;
+        if ((tid & 63) == 0) {
+            s_sum[wave][0] = s;
+            s_sum[wave][1] = w;
+        }
+        __syncthreads();
+        s = s_sum[0][0];
+        w = s_sum[0][1];
+#pragma unroll
+        for (int i = 1; i < WPR; ++i) {
+            s += s_sum[i][0];
+            w += s_sum[i][1];
+        }
+    }
+
+    const TokenResult r = token_tail<GRAD>(p, t, c, s, w, zy, ybad, tid == 0);
+    if constexpr (GRAD) {
+        if (!orow) return;
+        if (r.coef == 0.0f) {   // zero advantage or clipped token: the gradient row is zero
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int idx = k * TPR + tid;
+                if (idx < nvec) Out<DTO>::template zero<VEC>(orow, idx * VEC);
+            }
+            return;
+        }
+        // sweep 3: dz = coef * p, minus coef at the target
+        opaque_regs(x);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int idx = k * TPR + tid;
+            float f[VEC];
+            In<DTI>::unpack(x[k], f);
+            float d[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) d[e] = r.coef * __builtin_amdgcn_exp2f(fmaf(f[e], kLog2e, -r.c2));
+            if (idx == vy && !ybad) {
+                const int ey = y % VEC;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    if (e == ey) d[e] -= r.coef;
+            }
+            if (idx < nvec) Out<DTO>::template store<VEC>(orow, idx * VEC, d);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- generic streaming kernel
+//
+// Any stride, alignment or vocabulary size: 256 threads per token, element
+// loads, three passes over the row in memory.
+template <int DTI, int DTO, bool GRAD>
+__global__ __launch_bounds__(256) void tok_generic_kernel(const TokParams p) {
+    constexpr int TPR = 256;
+    constexpr int WPR = TPR / 64;
+    const int64_t t = blockIdx.x;
+    if (t >= p.n_tok) return;
+    const int tid = threadIdx.x;
+    void* orow = nullptr;
+    if constexpr (GRAD) {
+        if (p.dlogits) orow = reinterpret_cast<char*>(p.dlogits) + t * p.ld_out * Out<DTO>::BYTES;
+    }
+    if (p.mask[t] == 0) {
+        if (tid == 0) masked_outputs<GRAD>(p, t);
+        if constexpr (GRAD) {
+            if (orow)
+                for (int64_t v = tid; v < p.V; v += TPR) Out<DTO>::scalar(orow, v, 0.0f);
+        }
+        return;
+    }
+    const char* irow = reinterpret_cast<const char*>(p.logits) + t * p.ld * In<DTI>::BYTES;
+    const int32_t y = p.target[t];
+    const bool ybad = (uint32_t)y >= (uint64_t)p.V;
+    __shared__ float s_max[WPR];
+    __shared__ float s_sum[WPR][2];
+    __shared__ float s_zy;
+    if (tid == 0) s_zy = ybad ? 0.0f : In<DTI>::scalar(irow, y);
+
+    float m = -INFINITY;
+    for (int64_t v = tid; v < p.V; v += TPR) m = fmaxf(m, In<DTI>::scalar(irow, v));
+    m = wave_max(m);
+    const int wave = tid >> 6;
+    if ((tid & 63) == 0) s_max[wave] = m;
+    __syncthreads();
+    m = s_max[0];
+    for (int i = 1; i < WPR; ++i) m = fmaxf(m, s_max[i]);
+    const float zy = s_zy;
+
+    const float c = m * kLog2e;
+    float s = 0.0f, w = 0.0f;
+    for (int64_t v = tid; v < p.V; v += TPR) {
+        const float tt = fmaf(In<DTI>::scalar(irow, v), kLog2e, -c);
+        const float ee = __builtin_amdgcn_exp2f(tt);
+        s += ee;
+        w = fmaf(ee, fmaxf(tt, kNegClampLog2), w);
+    }
+    s = wave_sum(s);
+    w = wave_sum(w);
+    if ((tid & 63) == 0) {
+        s_sum[wave][0] = s;
+        s_sum[wave][1] = w;
+    }
+    __syncthreads();
+    s = s_sum[0][0];
+    w = s_sum[0][1];
+    for (int i = 1; i < WPR; ++i) {
+        s += s_sum[i][0];
+        w += s_sum[i][1];
+    }
+    const TokenResult r = token_tail<GRAD>(p, t, c, s, w, zy, ybad, tid == 0);
+    if constexpr (GRAD) {
+        if (!orow) return;
+        for (int64_t v = tid; v < p.V; v += TPR) {
+            float d = r.coef * __builtin_amdgcn_exp2f(fmaf(In<DTI>::scalar(irow, v), kLog2e, -r.c2));
+            if (v == y) d -= r.coef;
+            if (r.coef == 0.0f) d = 0.0f;
+            Out<DTO>::scalar(orow, v, d);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- statistics
+
+// One wave per row: lane j takes the row's tokens j, j+64, ...; fixed
+// butterfly.  A row's stats depend only on its own tokens.
+__global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ loss_tok,
+                                                        const float* __restrict__ entropy,
+                                                        const uint8_t* __restrict__ flags,
+                                                        const int64_t* __restrict__ row_off, int64_t n_rows,
+                                                        int64_t n_tok, grpo_stats* __restrict__ out) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= n_rows) return;
+    int64_t b = row_off[r], e = row_off[r + 1];
+    b = b < 0 ? 0 : (b > n_tok ? n_tok : b);
+    e = e < b ? b : (e > n_tok ? n_tok : e);
+    double ls = 0.0, es = 0.0;
+    long long nv = 0, nc = 0, nn = 0;
+    for (int64_t t = b + lane; t < e; t += 64) {
+        const uint8_t f = flags[t];
+        if (f & 1u) {
+            ls += (double)loss_tok[t];
+            es += (double)entropy[t];
+            nv += 1;
+            nc += (f >> 1) & 1u;
+            nn += (f >> 2) & 1u;
+        }
+    }
+    ls = wave_sum_d(ls);
+    es = wave_sum_d(es);
+    nv = wave_sum_i(nv);
+    nc = wave_sum_i(nc);
+    nn = wave_sum_i(nn);
+    if (lane == 0) {
+        grpo_stats s;
+        s.loss_sum = ls;
+        s.entropy_sum = es;
+        s.n_valid = nv;
+        s.n_clipped = nc;
+        s.n_nonfinite = nn;
+        s.n_valid_rows = nv > 0 ? 1 : 0;
+        out[r] = s;
+    }
+}
+
+// One block: thread i sums rows i, i+256, ... in order, then a fixed tree.
+__global__ __launch_bounds__(256) void chunk_stats_kernel(const grpo_stats* __restrict__ rows, int64_t n_rows,
+                                                          grpo_stats* __restrict__ out) {
+    __shared__ double s_ls[256], s_es[256];
+    __shared__ long long s_nv[256], s_nc[256], s_nn[256], s_nr[256];
+    const int i = threadIdx.x;
+    double ls = 0.0, es = 0.0;
+    long long nv = 0, nc = 0, nn = 0, nr = 0;
+    for (int64_t r = i; r < n_rows; r += 256) {
+        ls += rows[r].loss_sum;
+        es += rows[r].entropy_sum;
+        nv += rows[r].n_valid;
+        nc += rows[r].n_clipped;
+        nn += rows[r].n_nonfinite;
+        nr += rows[r].n_valid_rows;
+    }
+    s_ls[i] = ls; s_es[i] = es; s_nv[i] = nv; s_nc[i] = nc; s_nn[i] = nn; s_nr[i] = nr;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (i < h) {
+            s_ls[i] += s_ls[i + h]; s_es[i] += s_es[i + h];
+            s_nv[i] += s_nv[i + h]; s_nc[i] += s_nc[i + h];
+            s_nn[i] += s_nn[i + h]; s_nr[i] += s_nr[i + h];
+        }
+        __syncthreads();
+    }
+    if (i == 0) {
+        grpo_stats s;
+        s.loss_sum = s_ls[0];
+        s.entropy_sum = s_es[0];
+        s.n_valid = s_nv[0];
+        s.n_clipped = s_nc[0];
+        s.n_nonfinite = s_nn[0];
+        s.n_valid_rows = s_nr[0];
+        *out = s;
+    }
+}
+
+// N = number of non-zero mask bytes; one 1024-thread block, 16-byte loads
+// when the mask is 16-byte aligned.
+__global__ __launch_bounds__(1024) void count_valid_kernel(const uint8_t* __restrict__ mask, int64_t n,
+                                                           int64_t* __restrict__ out) {
+    __shared__ long long s_part[16];
+    const int i = threadIdx.x;
+    long long c = 0;
+    int64_t done = 0;
+    if ((reinterpret_cast<uintptr_t>(mask) & 15u) == 0) {
+        const int64_t nv = n / 16;
+        const uint4* v = reinterpret_cast<const uint4*>(mask);
+        for (int64_t k = i; k < nv; k += 1024) {
+            const uint4 q = v[k];
+            const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t x = w4[j];
+                c += ((x & 0xffu) != 0) + ((x & 0xff00u) != 0) + ((x & 0xff0000u) != 0) + ((x & 0xff000000u) != 0);
+            }
+        }
+        done = nv * 16;
+    }
+    for (int64_t k = done + i; k < n; k += 1024) c += mask[k] != 0;
+    c = wave_sum_i(c);
+    if ((i & 63) == 0) s_part[i >> 6] = c;
+    __syncthreads();
+    if (i == 0) {
+        long long tot = 0;
+        for (int k = 0; k < 16; ++k) tot += s_part[k];
+        *out = tot;
+    }
+}
+
+__global__ __launch_bounds__(256) void tok_row_kernel(const int64_t* __restrict__ row_off, int64_t n_rows,
+                                                      int64_t n_tok, int32_t* __restrict__ tok_row) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n_tok) return;
+    // last r with row_off[r] <= t, then check t < row_off[r+1]
+    int64_t lo = 0, hi = n_rows;   // answer in [0, n_rows)
+    if (n_rows <= 0 || row_off[0] > t) {
+        tok_row[t] = -1;
+        return;
+    }
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (row_off[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    tok_row[t] = t < row_off[lo + 1] ? (int32_t)lo : -1;
+}
+
+// ---------------------------------------------------------------- dispatch
+
+struct RegCfg {
+    int tpr;
+    int nv;
+};
+
+// Register-resident configurations, in order of preference; the first whose
+// capacity tpr * nv covers the row's 16-byte vectors is used.
+// NV stops at 19: at 1024 threads a lane has 128 VGPRs, and 19 vectors (76
+// VGPRs of row data) is the most that compiles without spilling.
+constexpr RegCfg kRegCfgs[] = {{64, 1}, {64, 2}, {64, 4}, {64, 8}, {256, 4}, {256, 8},
+                               {1024, 4}, {1024, 8}, {1024, 12}, {1024, 16}, {1024, 19}};
+
+template <int DTI, int DTO, bool GRAD>
+hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st) {
+    const int rpb = c.tpr == 64 ? 4 : 1;
+    const dim3 grid((unsigned)((p.n_tok + rpb - 1) / rpb));
+    const dim3 block(c.tpr == 64 ? 256 : c.tpr);
+#define GRPO_REG_CASE(TPR_, NV_)                                                                  \
+    if (c.tpr == TPR_ && c.nv == NV_) {                                                           \
+        hipLaunchKernelGGL((tok_reg_kernel<DTI, DTO, TPR_, NV_, GRAD>), grid, block, 0, st, p); \
+        return hipGetLastError();                                                                 \
+    }
+    GRPO_REG_CASE(64, 1)
+    GRPO_REG_CASE(64, 2)
+    GRPO_REG_CASE(64, 4)
+    GRPO_REG_CASE(64, 8)
+    GRPO_REG_CASE(256, 4)
+    GRPO_REG_CASE(256, 8)
+    GRPO_REG_CASE(1024, 4)
+    GRPO_REG_CASE(1024, 8)
+    GRPO_REG_CASE(1024, 12)
+    GRPO_REG_CASE(1024, 16)
+    GRPO_REG_CASE(1024, 19)
+#undef GRPO_REG_CASE
+    return hipErrorInvalidValue;
+}
+
+template <int DTI, int DTO, bool GRAD>
+hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st) {
+    if (p.n_tok == 0) return hipSuccess;
+    if (vec_ok) {
+        const int64_t nvec = p.V / In<DTI>::VEC;
+        for (const RegCfg& c : kRegCfgs)
+            if ((int64_t)c.tpr * c.nv >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st);
+    }
+    hipLaunchKernelGGL((tok_generic_kernel<DTI, DTO, GRAD>), dim3((unsigned)p.n_tok), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int check_launch(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(GRPO_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- C ABI
+
+extern "C" int grpo_count_valid(void* stream, const uint8_t* mask, int64_t n_tok, int64_t* n_valid) {
+    if (n_tok < 0 || !n_valid || (n_tok > 0 && !mask)) return fail(GRPO_EINVAL, "grpo_count_valid: bad arguments");
+    hipLaunchKernelGGL(count_valid_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, mask, n_tok, n_valid);
+    return check_launch(hipGetLastError(), "grpo_count_valid");
+}
+
+extern "C" int grpo_tok_row(void* stream, const int64_t* row_off, int64_t n_rows, int64_t n_tok, int32_t* tok_row) {
+    if (n_tok < 0 || n_rows < 0 || (n_tok > 0 && (!tok_row || !row_off)))
+        return fail(GRPO_EINVAL, "grpo_tok_row: bad arguments");
+    if (n_tok == 0) return ok();
+    hipLaunchKernelGGL(tok_row_kernel, dim3((unsigned)((n_tok + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       row_off, n_rows, n_tok, tok_row);
+    return check_launch(hipGetLastError(), "grpo_tok_row");
+}
+
+extern "C" int grpo_logprob_fwd(void* stream, int32_t dtype, const void* logits, int64_t ld, int64_t n_tok,
+                                int64_t V, const int32_t* target, const uint8_t* mask, float* logp, float* lse,
+                                float* entropy) {
+    if (dtype != GRPO_F32 && dtype != GRPO_BF16) return fail(GRPO_EINVAL, "grpo_logprob_fwd: unknown dtype %d", dtype);
+    if (n_tok < 0 || V < 1 || ld < V) return fail(GRPO_EINVAL, "grpo_logprob_fwd: need n_tok >= 0, V >= 1, ld >= V");
+    if (n_tok > 0 && (!logits || !target || !mask || !logp)) return fail(GRPO_EINVAL, "grpo_logprob_fwd: NULL pointer");
+    if (n_tok > 0x7fffffffLL * 4) return fail(GRPO_EINVAL, "grpo_logprob_fwd: too many tokens for one launch");
+    TokParams p{};
+    p.logits = logits; p.ld = ld; p.n_tok = n_tok; p.V = V;
+    p.target = target; p.mask = mask;
+    p.logp = logp; p.lse = lse; p.entropy = entropy;
+    const int vec = dtype == GRPO_BF16 ? 8 : 4;
+    const bool vec_ok = aligned16(logits) && ld % vec == 0 && V % vec == 0;
+    hipError_t e = dtype == GRPO_BF16 ? launch_tok<GRPO_BF16, GRPO_BF16, false>(p, vec_ok, (hipStream_t)stream)
+                                      : launch_tok<GRPO_F32, GRPO_F32, false>(p, vec_ok, (hipStream_t)stream);
+    return check_launch(e, "grpo_logprob_fwd");
+}
+
+extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
+    if (!a) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: NULL args");
+    if (a->struct_size != (int32_t)sizeof(grpo_loss_args))
+        return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: struct_size %d != %d", a->struct_size, (int)sizeof(grpo_loss_args));
+    const int di = a->in_dtype, dout = a->out_dtype;
+    if ((di != GRPO_F32 && di != GRPO_BF16) || (dout != GRPO_F32 && dout != GRPO_BF16))
+        return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: unknown dtype");
+    if (a->n_tok < 0 || a->V < 1 || a->ld < a->V || a->n_rows < 0)
+        return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: need n_tok >= 0, V >= 1, ld >= V, n_rows >= 0");
+    if (a->n_tok > 0 && a->n_rows < 1) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: tokens without rows");
+    if (a->n_tok > 0x7fffffffLL) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: too many tokens for one launch");
+    if (!a->chunk_stats || (a->n_rows > 0 && (!a->row_stats || !a->row_off)))
+        return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: NULL stats pointer");
+    if (a->n_tok > 0 && (!a->logits || !a->target || !a->mask || !a->old_logp || !a->tok_row || !a->adv_row ||
+                         !a->logp || !a->entropy || !a->loss_tok || !a->tok_flags))
+        return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: NULL pointer");
+    if (!(a->eps_low >= 0.0f && a->eps_low <= 1.0f && a->eps_high >= 0.0f && std::isfinite(a->eps_high)))
+        return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: need 0 <= eps_low <= 1 and finite eps_high >= 0");
+    if (!std::isfinite(a->scale)) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: scale must be finite");
+    const int in_b = di == GRPO_BF16 ? 2 : 4, out_b = dout == GRPO_BF16 ? 2 : 4;
+    if (a->dlogits && a->n_tok > 0) {
+        if (a->ld_out < a->V) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: ld_out < V");
+        const uintptr_t i0 = (uintptr_t)a->logits, i1 = i0 + (uintptr_t)((a->n_tok - 1) * a->ld + a->V) * in_b;
+        const uintptr_t o0 = (uintptr_t)a->dlogits, o1 = o0 + (uintptr_t)((a->n_tok - 1) * a->ld_out + a->V) * out_b;
+        const bool overlap = o0 < i1 && i0 < o1;
+        if (overlap && !(o0 == i0 && di == dout && a->ld == a->ld_out))
+            return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: dlogits overlaps logits without being the same buffer");
+    }
+    TokParams p{};
+    p.logits = a->logits; p.ld = a->ld; p.n_tok = a->n_tok; p.V = a->V;
+    p.target = a->target; p.mask = a->mask; p.old_logp = a->old_logp;
+    p.tok_row = a->tok_row; p.adv_row = a->adv_row; p.n_rows = a->n_rows;
+    p.eps_low = a->eps_low; p.eps_high = a->eps_high; p.scale = a->scale; p.denom = a->denom;
+    p.dlogits = a->dlogits; p.ld_out = a->ld_out;
+    p.logp = a->logp; p.lse = a->lse; p.entropy = a->entropy; p.loss_tok = a->loss_tok; p.tok_flags = a->tok_flags;
+    const int vec = di == GRPO_BF16 ? 8 : 4;
+    bool vec_ok = aligned16(a->logits) && a->ld % vec == 0 && a->V % vec == 0;
+    if (a->dlogits) vec_ok = vec_ok && aligned16(a->dlogits) && (a->ld_out * out_b) % 16 == 0 && ((int64_t)vec * out_b) % 8 == 0;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (di == GRPO_BF16 && dout == GRPO_BF16) e = launch_tok<GRPO_BF16, GRPO_BF16, true>(p, vec_ok, st);
+    else if (di == GRPO_BF16) e = launch_tok<GRPO_BF16, GRPO_F32, true>(p, vec_ok, st);
+    else if (dout == GRPO_BF16) e = launch_tok<GRPO_F32, GRPO_BF16, true>(p, vec_ok, st);
+    else e = launch_tok<GRPO_F32, GRPO_F32, true>(p, vec_ok, st);
+    if (e != hipSuccess) return check_launch(e, "grpo_loss_fwd_bwd (token kernel)");
+    if (a->n_rows > 0) {
+        hipLaunchKernelGGL(row_stats_kernel, dim3((unsigned)((a->n_rows + 3) / 4)), dim3(256), 0, st, a->loss_tok,
+                           a->entropy, a->tok_flags, a->row_off, a->n_rows, a->n_tok, a->row_stats);
+        e = hipGetLastError();
+        if (e != hipSuccess) return check_launch(e, "grpo_loss_fwd_bwd (row stats)");
+    }
+    hipLaunchKernelGGL(chunk_stats_kernel, dim3(1), dim3(256), 0, st, a->row_stats, a->n_rows, a->chunk_stats);
+    return check_launch(hipGetLastError(), "grpo_loss_fwd_bwd (chunk stats)");
+}

@@ -1,0 +1,270 @@
+"""Python face of libgrpo: the same calls as include/grpo.h, taking numpy
+arrays (host calls) and torch tensors (device calls).
+
+Marshalling only.  PyTorch supplies device memory and the current HIP stream;
+every computation runs in libgrpo (host C++ or gfx950 kernels).  Device calls
+insist on GPU tensors and never fall back to a CPU path.
+"""
+
+import ctypes
+
+import numpy as np
+
+from . import _capi as C
+from ._capi import GrpoError, STATS_DTYPE, STATS_BYTES  # noqa: F401  (re-exported)
+
+# ---------------------------------------------------------------- host calls
+
+
+def version():
+    return C.lib().grpo_version().decode()
+
+
+def plan_fixed(batch, group_size, mini=0, micro=0):
+    """-> (n_mini, n_micro, mini_rows, micro_rows).  See grpo_plan_fixed."""
+    o = [ctypes.c_int64() for _ in range(4)]
+    C.check(C.lib().grpo_plan_fixed(batch, group_size, mini, micro, *[ctypes.byref(x) for x in o]))
+    return tuple(x.value for x in o)
+
+
+def plan_chunk(batch, mini_rows, micro_rows, i_mini, j_micro):
+    """-> (row_begin, row_end) of chunk (i, j)."""
+    b, e = ctypes.c_int64(), ctypes.c_int64()
+    C.check(C.lib().grpo_plan_chunk(batch, mini_rows, micro_rows, i_mini, j_micro, ctypes.byref(b), ctypes.byref(e)))
+    return b.value, e.value
+
+
+def plan_dynamic(lengths, token_budget, proxy_div=4096):
+    """Token-budget packing -> dict(n_bins, bin_off, order, restore) (int64 arrays)."""
+    L = np.ascontiguousarray(lengths, dtype=np.int64)
+    n = L.shape[0]
+    order = np.zeros(max(n, 1), np.int64)
+    restore = np.zeros(max(n, 1), np.int64)
+    cap = 8
+    while True:
+        nb = ctypes.c_int64()
+        off = np.zeros(cap + 1, np.int64)
+        code = C.lib().grpo_plan_dynamic(C.ptr64(L), n, token_budget, proxy_div, cap, ctypes.byref(nb),
+                                         C.ptr64(off), C.ptr64(order), C.ptr64(restore))
+        if code == -7:           # ECAPACITY: grow to the reported need
+            cap = nb.value
+            continue
+        C.check(code)
+        k = nb.value
+        return {"n_bins": k, "bin_off": off[:k + 1].copy(), "order": order[:n].copy(),
+                "restore": restore[:n].copy()}
+
+
+def plan_compaction(rows_per_rollout, n_groups, group_size, Q, expected_rollouts, dynamic=False):
+    """Context-compaction rows -> dict of int arrays (see grpo_plan_compaction)."""
+    R = np.ascontiguousarray(rows_per_rollout, dtype=np.int32)
+    n = R.shape[0]
+    cap = max(1, int(R.sum()) + n_groups * max(Q - 1, 0)) if n else 1
+    out_n = ctypes.c_int64()
+    rr = np.zeros(cap, np.int32)
+    rs = np.zeros(cap, np.int32)
+    src = np.zeros(cap, np.int32)
+    pad = np.zeros(cap, np.uint8)
+    gp = np.zeros(max(n_groups, 1), np.int32)
+    C.check(C.lib().grpo_plan_compaction(C.ptr32(R), n, n_groups, group_size, Q, expected_rollouts,
+                                         1 if dynamic else 0, cap, ctypes.byref(out_n), C.ptr32(rr),
+                                         C.ptr32(rs), C.ptr32(src), C.ptru8(pad), C.ptr32(gp)))
+    k = out_n.value
+    return {"n_rows": k, "row_rollout": rr[:k].copy(), "row_seg": rs[:k].copy(), "row_src": src[:k].copy(),
+            "is_pad": pad[:k].copy(), "group_pad": gp[:n_groups].copy()}
+
+
+def row_offsets(lengths, order=None):
+    L = np.ascontiguousarray(lengths, dtype=np.int64)
+    n = L.shape[0]
+    off = np.zeros(n + 1, np.int64)
+    if order is None:
+        C.check(C.lib().grpo_row_offsets(C.ptr64(L), None, n, C.ptr64(off)))
+    else:
+        O = np.ascontiguousarray(order, dtype=np.int64)
+        C.check(C.lib().grpo_row_offsets(C.ptr64(L), C.ptr64(O), n, C.ptr64(off)))
+    return off
+
+
+def group_advantage(reward, group_size, eps=1e-6, norm_by_std=True):
+    r = np.ascontiguousarray(reward, dtype=np.float32)
+    out = np.zeros(max(r.shape[0], 1), np.float32)
+    C.check(C.lib().grpo_group_advantage(C.ptrf32(r), r.shape[0], group_size, eps, 1 if norm_by_std else 0,
+                                         C.ptrf32(out)))
+    return out[:r.shape[0]]
+
+
+def rows_advantage(adv_rollout, row_rollout):
+    a = np.ascontiguousarray(adv_rollout, dtype=np.float32)
+    rr = np.ascontiguousarray(row_rollout, dtype=np.int32)
+    out = np.zeros(max(rr.shape[0], 1), np.float32)
+    C.check(C.lib().grpo_rows_advantage(C.ptrf32(a), a.shape[0], C.ptr32(rr), rr.shape[0], C.ptrf32(out)))
+    return out[:rr.shape[0]]
+
+
+class Accumulator:
+    """Host step accumulator (grpo_accum_*): add() returns 'OK', 'NONFINITE' or
+    'SKIPPED'; finalize() returns a dict or None."""
+
+    def __init__(self, n_micro):
+        self._a = C.Accum()
+        C.check(C.lib().grpo_accum_init(ctypes.byref(self._a), n_micro))
+
+    def add(self, stats):
+        s = C.Stats(**{k: stats[k] for k in STATS_DTYPE.names})
+        code = C.lib().grpo_accum_add(ctypes.byref(self._a), ctypes.byref(s))
+        if code == 0:
+            return "OK"
+        if code == -5:
+            return "NONFINITE"
+        if code == -6:
+            return "SKIPPED"
+        if code == -9:
+            return "STATE"
+        C.check(code)
+
+    def finalize(self):
+        r = C.StepResult()
+        stepped = ctypes.c_int32()
+        C.check(C.lib().grpo_accum_finalize(ctypes.byref(self._a), ctypes.byref(r), ctypes.byref(stepped)))
+        if not stepped.value:
+            return None
+        return {k: getattr(r, k) for k, _ in C.StepResult._fields_}
+
+
+def stats_to_dicts(raw):
+    """uint8 bytes of a grpo_stats array (numpy or torch) -> list of dicts."""
+    if hasattr(raw, "cpu"):
+        raw = raw.cpu().numpy()
+    arr = np.ascontiguousarray(raw).view(STATS_DTYPE).reshape(-1)
+    return [{k: (float(a[k]) if k.endswith("_sum") else int(a[k])) for k in STATS_DTYPE.names} for a in arr]
+
+
+# ---------------------------------------------------------------- device calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libgrpo has no CPU path)")
+    if not t.is_contiguous() and t.dim() == 1:
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return C.GRPO_BF16
+    if t.dtype == torch.float32:
+        return C.GRPO_F32
+    raise ValueError(f"unsupported logits dtype {t.dtype} (bf16 or fp32)")
+
+
+def _rows2d(x, name):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit stride along the vocabulary")
+    return x.stride(0)
+
+
+def count_valid(mask, out=None):
+    """Device int64 [1] tensor holding the number of non-zero mask bytes."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(1, dtype=torch.int64, device=mask.device)
+    C.check(C.lib().grpo_count_valid(_stream(), _dev(mask, "mask"), mask.numel(), _dev(out, "out")))
+    return out
+
+
+def tok_row(row_off, n_tok, out=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty(n_tok, dtype=torch.int32, device=row_off.device)
+    C.check(C.lib().grpo_tok_row(_stream(), _dev(row_off, "row_off"), row_off.numel() - 1, n_tok,
+                                 _dev(out, "tok_row")))
+    return out
+
+
+def logprob_fwd(logits, target, mask, want_lse=True, want_entropy=True):
+    """Forward-only per-token (logp, lse, entropy) float32 tensors."""
+    torch = _torch()
+    ld = _rows2d(logits, "logits")
+    n, V = logits.shape
+    logp = torch.empty(n, dtype=torch.float32, device=logits.device)
+    lse = torch.empty_like(logp) if want_lse else None
+    ent = torch.empty_like(logp) if want_entropy else None
+    C.check(C.lib().grpo_logprob_fwd(_stream(), _dtype_code(logits), _dev(logits, "logits"), ld, n, V,
+                                     _dev(target, "target"), _dev(mask, "mask"), _dev(logp, "logp"),
+                                     _dev(lse, "lse"), _dev(ent, "entropy")))
+    return logp, lse, ent
+
+
+def loss_workspace(n_tok, n_rows, device):
+    """Per-token and per-row output buffers for loss_fwd_bwd."""
+    torch = _torch()
+    f = dict(dtype=torch.float32, device=device)
+    return {"logp": torch.empty(n_tok, **f), "lse": torch.empty(n_tok, **f), "entropy": torch.empty(n_tok, **f),
+            "loss_tok": torch.empty(n_tok, **f),
+            "tok_flags": torch.empty(n_tok, dtype=torch.uint8, device=device),
+            "row_stats": torch.empty((max(n_rows, 1), STATS_BYTES), dtype=torch.uint8, device=device),
+            "chunk_stats": torch.empty((1, STATS_BYTES), dtype=torch.uint8, device=device)}
+
+
+def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, scale=1.0, denom=None,
+                 eps_low=0.2, eps_high=0.2, dlogits="new", out_dtype=None, ws=None):
+    """Fused GRPO loss forward/backward over one chunk (grpo_loss_fwd_bwd).
+
+    ``dlogits``: "new" (allocate, dtype ``out_dtype`` or the logits dtype),
+    "inplace" (overwrite ``logits``), None (no gradient), or a tensor.
+    Returns the workspace dict with ``dlogits`` added."""
+    torch = _torch()
+    ld = _rows2d(logits, "logits")
+    n, V = logits.shape
+    n_rows = row_off.numel() - 1
+    if ws is None:
+        ws = loss_workspace(n, n_rows, logits.device)
+    if isinstance(dlogits, str) and dlogits == "new":
+        dl = torch.empty((n, V), dtype=out_dtype or logits.dtype, device=logits.device)
+    elif isinstance(dlogits, str) and dlogits == "inplace":
+        dl = logits
+    else:
+        dl = dlogits
+    a = C.LossArgs()
+    a.struct_size = ctypes.sizeof(C.LossArgs)
+    a.in_dtype = _dtype_code(logits)
+    a.out_dtype = _dtype_code(dl) if dl is not None else a.in_dtype
+    a.logits = logits.data_ptr() if n else None
+    a.ld, a.n_tok, a.V = ld, n, V
+    a.target = target.data_ptr() if n else None
+    a.mask = mask.data_ptr() if n else None
+    a.old_logp = old_logp.data_ptr() if n else None
+    a.tok_row = tok_row_.data_ptr() if n else None
+    a.adv_row = adv_row.data_ptr() if n_rows else None
+    a.row_off = row_off.data_ptr()
+    a.n_rows = n_rows
+    a.eps_low, a.eps_high, a.scale = eps_low, eps_high, scale
+    a.denom = denom.data_ptr() if denom is not None else None
+    if dl is not None:
+        a.dlogits = dl.data_ptr() if n else None
+        a.ld_out = _rows2d(dl, "dlogits")
+    for k in ("logp", "lse", "entropy", "loss_tok", "tok_flags", "row_stats", "chunk_stats"):
+        t = ws[k]
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{k} must be a GPU tensor")
+        setattr(a, k, t.data_ptr() if t is not None else None)
+    for name, t in (("logits", logits), ("target", target), ("mask", mask), ("old_logp", old_logp),
+                    ("tok_row", tok_row_), ("adv_row", adv_row), ("row_off", row_off)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (libgrpo has no CPU path)")
+    C.check(C.lib().grpo_loss_fwd_bwd(_stream(), ctypes.byref(a)))
+    ws["dlogits"] = dl
+    return ws

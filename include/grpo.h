@@ -1,0 +1,266 @@
+/*
+ * grpo.h -- C ABI of libgrpo: the token-level GRPO policy-loss hot path on
+ * AMD MI355X (gfx950).
+ *
+ * Sources (cited by title and section):
+ *   [P1] "Sizing mini-batches and micro-batches" (cosmos-framework post-training
+ *        how-to on batching)
+ *   [P2] "03 Data Protocol and Batch Lifecycle" (verl source reading)
+ *   [P3] "22 - mini-batch, micro-batch and dynamic batch size" (verl article)
+ *   [P4] "How a context-compaction step fits a variable number of rows into
+ *        one batch" (NeMo-RL explainer)
+ *
+ * Conventions
+ *   - Every call returns a status: GRPO_OK (0) or a negative GRPO_E* code.  A
+ *     readable message for the last failure on the calling thread is in
+ *     grpo_last_error() (static storage, valid until the thread's next call).
+ *   - Host functions ("host") are pure and re-entrant, read and write host
+ *     memory only, never allocate, and write their outputs only on GRPO_OK
+ *     (GRPO_ECAPACITY writes back the capacity that is needed).
+ *   - Device functions ("device") take a hipStream_t as void*, enqueue kernels
+ *     on it and return without synchronising.  All their pointers are device
+ *     pointers owned by the caller; the library allocates no memory.  Arguments
+ *     are checked on the host before any launch; a launch failure returns
+ *     GRPO_EDEVICE.  Device-side data errors (a target outside [0, V), a token
+ *     whose row index is outside [0, n_rows)) never read out of bounds: the
+ *     token is reported non-finite instead.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef GRPO_H
+#define GRPO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+#define GRPO_OK          0
+#define GRPO_EINVAL     (-1)  /* malformed arguments */
+#define GRPO_EDIVISIBLE (-2)  /* a batch level does not divide the one above ([P1] "The config surface") */
+#define GRPO_ETOOLONG   (-3)  /* a row exceeds the micro-batch token budget ([P3] section 3) */
+#define GRPO_ECOUNT     (-4)  /* a step does not hold the configured rollouts ([P4] opening paragraphs) */
+#define GRPO_ENONFINITE (-5)  /* a chunk's loss is not finite: window discarded ([P1] "The poisoned-window countdown") */
+#define GRPO_ESKIPPED   (-6)  /* the call was swallowed by the countdown */
+#define GRPO_ECAPACITY  (-7)  /* an output buffer is too small; the needed size was written back */
+#define GRPO_EDEVICE    (-8)  /* a HIP launch or runtime call failed */
+#define GRPO_ESTATE     (-9)  /* accumulator misuse: a completed window was not finalized */
+
+typedef enum grpo_dtype { GRPO_F32 = 0, GRPO_BF16 = 1 } grpo_dtype;
+
+/* Sums over a row or a chunk.  [P1] "Metric roll-up: token-weighted, not
+ * averaged": losses are carried as sums with their token counts so that the
+ * step loss is sum(loss_sum) / sum(n_valid); counts sum.  n_valid is the
+ * chunk's divisor ([P1] "The hard part: deferred normalization").
+ * n_valid_rows counts rows holding at least one valid token ([P4] "What it
+ * costs": row counts can exceed rollouts under compaction; pads never count). */
+typedef struct grpo_stats {
+    double  loss_sum;      /* sum over valid tokens of the per-token loss */
+    double  entropy_sum;   /* sum over valid tokens of the entropy (nats) */
+    int64_t n_valid;       /* valid (mask = 1) tokens */
+    int64_t n_clipped;     /* valid tokens whose gradient the clip removed */
+    int64_t n_nonfinite;   /* valid tokens with a non-finite log-prob, loss or entropy */
+    int64_t n_valid_rows;  /* rows with n_valid > 0 */
+} grpo_stats;
+
+const char* grpo_last_error(void);
+const char* grpo_version(void);
+
+/* ================================================================== plans */
+
+/* host.  Fixed mini/micro plan.  [P1] "The config surface" and "A worked
+ * example": batch is a positive multiple of group_size (else EINVAL);
+ * mini = 0 means the whole batch and micro = 0 one chunk per mini-batch;
+ * n_mini = batch / mini_rows and n_micro = mini_rows / micro_rows, each
+ * division exact (else EDIVISIBLE).  32/16/8 -> 2 x 2; 0/0 -> 1 x 1.
+ * Outputs are single int64 values. */
+int grpo_plan_fixed(int64_t batch, int64_t group_size, int64_t mini, int64_t micro,
+                    int64_t* n_mini, int64_t* n_micro, int64_t* mini_rows, int64_t* micro_rows);
+
+/* host.  Rows [row_begin, row_end) of chunk (i_mini, j_micro) of a fixed plan:
+ * contiguous, unshuffled slices in collected-batch order ([P1] "The core
+ * idea": the driver passes indices only).  EINVAL for an index out of range. */
+int grpo_plan_chunk(int64_t batch, int64_t mini_rows, int64_t micro_rows,
+                    int64_t i_mini, int64_t j_micro, int64_t* row_begin, int64_t* row_end);
+
+/* host.  Token-budget dynamic packing ([P3] section 3).  len[n_rows] are row
+ * token counts (>= 0).  A row longer than token_budget -> ETOOLONG.  Boxes
+ * start at max(1, ceil(sum(len) / budget)); workload w = proxy_div*L + L*L;
+ * rows are placed by decreasing w (ties: lower index first) into the box with
+ * the least workload so far (ties: lower box) among those that still fit; if
+ * a row fits nowhere, one more box is added and packing restarts.  Rows keep
+ * their original order inside a box.
+ * Outputs: *n_bins; bin_off[n_bins + 1] offsets into order; order[n_rows]
+ * (packed position -> original row); restore[n_rows] (original row -> packed
+ * position).  bin_off must hold cap_bins + 1 entries: if the packing needs
+ * more boxes, ECAPACITY is returned with *n_bins set to the number needed.
+ * n_rows = 0 gives n_bins = 0. */
+int grpo_plan_dynamic(const int64_t* len, int64_t n_rows, int64_t token_budget, int64_t proxy_div,
+                      int64_t cap_bins, int64_t* n_bins, int64_t* bin_off,
+                      int64_t* order, int64_t* restore);
+
+/* host.  Context-compaction rows ([P4] figure and opening paragraphs).
+ * rows_per_rollout[n_rollouts] (each >= 1, else EINVAL): segment rows per
+ * rollout, rollouts grouped G at a time.  n_groups * group_size must equal
+ * expected_rollouts and so must n_rollouts (else ECOUNT: the step raises
+ * unless it holds exactly the configured rollouts).  dynamic != 0 -> EINVAL
+ * (compaction runs with fixed batching only, [P4] "What it costs").
+ * Per group: its real rows rollout-major in segment order, then
+ * (-real) mod Q pad rows, each copying the group's first real row.
+ * Outputs per padded row (capacity cap_rows, else ECAPACITY with *n_rows set):
+ * row_rollout (-1 for a pad), row_seg (segment index, -1 for a pad), row_src
+ * (input row, numbering all segment rows rollout-major), row_is_pad; and
+ * group_pad[n_groups]. */
+int grpo_plan_compaction(const int32_t* rows_per_rollout, int64_t n_rollouts, int64_t n_groups,
+                         int64_t group_size, int64_t Q, int64_t expected_rollouts, int32_t dynamic,
+                         int64_t cap_rows, int64_t* n_rows, int32_t* row_rollout, int32_t* row_seg,
+                         int32_t* row_src, uint8_t* row_is_pad, int32_t* group_pad);
+
+/* host.  Prefix offsets of rows laid end to end: row_off[0] = 0,
+ * row_off[k+1] = row_off[k] + len[order ? order[k] : k].  Used for the packed
+ * (variable-length) layout, [P3] section 3. */
+int grpo_row_offsets(const int64_t* len, const int64_t* order, int64_t n_rows, int64_t* row_off);
+
+/* ============================================================== advantage */
+
+/* host.  One advantage per rollout, relative to its group of group_size
+ * consecutive rollouts ([P2] "Field Lineage", reward/log-prob/advantage;
+ * [P4] "Why the row count does not change the math", item 2).  The pages
+ * give no formula; this is A = (r - mean) / (std + eps) with the unbiased
+ * (G - 1) standard deviation, or A = r - mean when norm_by_std = 0; a group
+ * of one rollout has A = 0.  Accumulates in double.  n_rollouts must be a
+ * multiple of group_size (EINVAL). */
+int grpo_group_advantage(const float* reward, int64_t n_rollouts, int64_t group_size,
+                         float eps, int32_t norm_by_std, float* adv_rollout);
+
+/* host.  adv_row[r] = adv_rollout[row_rollout[r]], or 0 for a pad
+ * (row_rollout < 0) ([P4] item 2: copied to all rows of the rollout, pads 0).
+ * A row_rollout >= n_rollouts is EINVAL. */
+int grpo_rows_advantage(const float* adv_rollout, int64_t n_rollouts,
+                        const int32_t* row_rollout, int64_t n_rows, float* adv_row);
+
+/* ============================================================ device path */
+
+/* device.  *n_valid (device int64) = number of non-zero bytes of
+ * mask[n_tok]: N, the valid tokens of a step ([P1] "The hard part: deferred
+ * normalization"; [P3] section 5: the token mean divides by the summed loss
+ * mask; [P4] item 1: padding counts 0).  Overwrites *n_valid. */
+int grpo_count_valid(void* stream, const uint8_t* mask, int64_t n_tok, int64_t* n_valid);
+
+/* device.  tok_row[t] = the row r with row_off[r] <= t < row_off[r+1]
+ * (row_off: device int64 [n_rows + 1], non-decreasing), or -1 if none. */
+int grpo_tok_row(void* stream, const int64_t* row_off, int64_t n_rows, int64_t n_tok, int32_t* tok_row);
+
+/* device.  Ahead pass: per-token log-prob, logsumexp and entropy, forward
+ * only ([P1] "pi_old must be frozen across the window -- the ahead pass";
+ * [P2] "Field Lineage": the normal-mode recompute yields old log-probs and
+ * entropy).  logits: dtype, token t's row at logits + t*ld (ld >= V elements),
+ * [n_tok x V].  target int32 [n_tok]; mask uint8 [n_tok].  Outputs float
+ * [n_tok]: logp = z_y - lse, lse = log sum exp z, entropy = -sum p log p; 0 at
+ * mask-0 tokens.  lse and entropy may be NULL.  Reads V elements per valid
+ * token once and writes nothing V-sized. */
+int grpo_logprob_fwd(void* stream, int32_t dtype, const void* logits, int64_t ld, int64_t n_tok,
+                     int64_t V, const int32_t* target, const uint8_t* mask,
+                     float* logp, float* lse, float* entropy);
+
+/* Arguments of grpo_loss_fwd_bwd (all pointers are device pointers). */
+typedef struct grpo_loss_args {
+    int32_t struct_size;        /* = sizeof(grpo_loss_args) */
+    int32_t in_dtype;           /* grpo_dtype of logits */
+    int32_t out_dtype;          /* grpo_dtype of dlogits */
+    int32_t reserved0;          /* 0 */
+    const void* logits;         /* token t's V logits at logits + t*ld */
+    int64_t ld;                 /* row stride in elements, >= V */
+    int64_t n_tok;              /* token rows in this chunk (>= 0) */
+    int64_t V;                  /* vocabulary (>= 1) */
+    const int32_t* target;      /* [n_tok] next-token ids */
+    const uint8_t* mask;        /* [n_tok] 1 = policy token ([P2] response mask) */
+    const float* old_logp;      /* [n_tok] pi_old log-probs (ignored where mask = 0) */
+    const int32_t* tok_row;     /* [n_tok] row of each token within the chunk */
+    const float* adv_row;       /* [n_rows] advantage per row (0 for pads) */
+    const int64_t* row_off;     /* [n_rows + 1] token offsets of the rows (row stats) */
+    int64_t n_rows;             /* rows in this chunk (>= 1 when n_tok > 0) */
+    float eps_low, eps_high;    /* clip band [1 - eps_low, 1 + eps_high] */
+    float scale;                /* gradient factor: 1/max(N,1) for a known step N, 1 to defer */
+    int32_t reserved1;          /* 0 */
+    const int64_t* denom;       /* NULL, or device int64: coef is further divided by max(*denom, 1) */
+    void* dlogits;              /* out_dtype, token t at dlogits + t*ld_out; may equal logits
+                                   when the dtypes and strides match; NULL = no gradient */
+    int64_t ld_out;             /* row stride of dlogits in elements, >= V */
+    float* logp;                /* [n_tok] required */
+    float* lse;                 /* [n_tok] or NULL */
+    float* entropy;             /* [n_tok] required */
+    float* loss_tok;            /* [n_tok] required: per-token surrogate loss l_t */
+    uint8_t* tok_flags;         /* [n_tok] required: bit0 valid, bit1 clipped, bit2 non-finite */
+    grpo_stats* row_stats;      /* [n_rows] required */
+    grpo_stats* chunk_stats;    /* [1] required: rows summed in row order */
+} grpo_loss_args;
+
+/* device.  Fused forward and backward of the token-level GRPO loss over one
+ * micro-batch chunk.  Per valid token (mask = 1), reading the token's logits
+ * once:
+ *   lse = log sum_v exp z_v, logp = z_y - lse, H = -sum_v p_v log p_v,
+ *   rho = exp(logp - old_logp), A = adv_row[tok_row[t]],
+ *   l = -min(rho*A, clip(rho, 1-eps_low, 1+eps_high)*A),
+ *   g = 0 if (A > 0 and rho > 1+eps_high) or (A < 0 and rho < 1-eps_low) else 1,
+ *   coef = s * A * rho * g with s = scale (/ max(*denom, 1) when denom is set),
+ *   dlogits_v = coef * (p_v - [v == y]).
+ * Mask-0 tokens: outputs 0 and a zero dlogits row.
+ * [P1] "The hard part: deferred normalization" (token mean over N; chunk
+ * gradients add up to the step gradient, so scale = 1/N on every chunk makes
+ * the chunked gradient equal the un-chunked one token for token);
+ * [P1] "pi_old must be frozen" (ratio and epsilon clip);
+ * [P2] "Field Lineage" (response mask, advantage broadcast over the row);
+ * [P4] "Why the row count does not change the math" items 1-2 (pads: no
+ * valid tokens, advantage 0).
+ * Then row_stats[r] sums tokens row_off[r] .. row_off[r+1]-1 and
+ * chunk_stats sums the rows in row order; the reductions have a fixed order,
+ * so results are bit-for-bit reproducible and a row's stats do not depend on
+ * where the row sits in the chunk. */
+int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* args);
+
+/* ============================================================ accumulator */
+
+/* One optimizer-step window of n_micro chunks, caller-allocated, plain data.
+ * [P1] "The hard part: deferred normalization": divisors add up and the
+ * gradient is scaled once by 1/max(sum, 1); [P1] "Metric roll-up": the step
+ * loss is sum(loss_sum)/max(sum(n_valid), 1) and counts sum; [P1] "The
+ * poisoned-window countdown": a non-finite chunk at position j discards the
+ * window and the next n_micro - 1 - j calls are swallowed. */
+typedef struct grpo_accum {
+    int64_t n_micro;
+    int64_t pos;        /* chunks accumulated in the open window */
+    int64_t skip;       /* calls still to swallow */
+    int32_t done;       /* a completed window waits for grpo_accum_finalize */
+    int32_t reserved;
+    grpo_stats open;    /* sums of the open window */
+    grpo_stats closed;  /* sums of the completed window */
+} grpo_accum;
+
+typedef struct grpo_step_result {
+    double  loss;          /* sum(loss_sum) / max(N, 1) */
+    double  entropy;       /* sum(entropy_sum) / max(N, 1) */
+    double  grad_scale;    /* 1 / max(N, 1): apply to gradients accumulated with scale = 1 */
+    int64_t n_valid;       /* N */
+    int64_t n_valid_rows;
+    int64_t n_clipped;
+} grpo_step_result;
+
+/* host.  n_micro >= 1. */
+int grpo_accum_init(grpo_accum* acc, int64_t n_micro);
+/* host.  Adds one chunk's stats (host copy).  Returns GRPO_OK, GRPO_ENONFINITE
+ * (window discarded; zero your accumulated gradients), GRPO_ESKIPPED (call
+ * swallowed by the countdown) or GRPO_ESTATE (finalize the completed window
+ * first).  A chunk is non-finite when n_nonfinite > 0 or a sum is not finite. */
+int grpo_accum_add(grpo_accum* acc, const grpo_stats* chunk);
+/* host.  *stepped = 1 and *out filled when a window is complete (the window is
+ * then closed); *stepped = 0 otherwise. */
+int grpo_accum_finalize(grpo_accum* acc, grpo_step_result* out, int32_t* stepped);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRPO_H */

@@ -1,0 +1,202 @@
+"""GPU parity of the fused loss kernel, the forward-only pass and the small
+device helpers against the oracle, element by element, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import DEV, assert_tokens_match, make_chunk, rel_l2, run_gpu, run_oracle, to_f64
+from grpo_token_level_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+
+def _stats(ws):
+    return ops.stats_to_dicts(ws["chunk_stats"])[0], ops.stats_to_dicts(ws["row_stats"])
+
+
+def _check_stats(ws, ref, d):
+    chunk, rows = _stats(ws)
+    want_rows = oracle.row_stats(ref, d["row_off"].tolist())
+    for g, w in zip(rows, want_rows):
+        for k in ("n_valid", "n_valid_rows", "n_nonfinite"):
+            assert g[k] == w[k], k
+        assert g["loss_sum"] == pytest.approx(w["loss_sum"], rel=1e-4, abs=1e-4)
+    want = oracle.chunk_stats(ref, d["row_off"].tolist())
+    assert chunk["n_valid"] == want["n_valid"]
+    assert chunk["loss_sum"] == pytest.approx(sum(r["loss_sum"] for r in rows), rel=1e-12, abs=1e-12)
+
+
+# (V, in dtype, out dtype, n_tok): register paths (wave / 256 / 1024 threads
+# per row), the generic path (V or stride not a multiple of the vector),
+# ragged token counts around the 4-rows-per-block wave path.
+CASES = [
+    (1024, torch.float32, torch.float32, 203),
+    (1024, torch.float32, torch.bfloat16, 61),
+    (4096, torch.bfloat16, torch.bfloat16, 130),
+    (4096, torch.bfloat16, torch.float32, 67),
+    (16384, torch.bfloat16, torch.bfloat16, 37),
+    (32000, torch.bfloat16, torch.bfloat16, 21),
+    (151936, torch.bfloat16, torch.bfloat16, 9),
+    (151936, torch.bfloat16, torch.float32, 5),
+    (8, torch.float32, torch.float32, 33),
+    (1, torch.float32, torch.float32, 10),
+    (7, torch.bfloat16, torch.bfloat16, 17),
+    (1000, torch.bfloat16, torch.bfloat16, 23),
+    (50257, torch.bfloat16, torch.bfloat16, 11),
+    (200000, torch.bfloat16, torch.bfloat16, 5),
+]
+
+
+@pytest.mark.parametrize("V,din,dout,n", CASES)
+def test_loss_matches_oracle(V, din, dout, n):
+    print(f"loss parity V={V} in={din} out={dout} n={n}", flush=True)
+    d = make_chunk(n, V, din, seed=V + n, noise=0.4)
+    N = int(d["mask"].sum())
+    scale = 1.0 / max(N, 1)
+    ws = run_gpu(d, scale=scale, out_dtype=dout)
+    ref = run_oracle(d, scale)
+    assert_tokens_match(ws, ref, d)
+    _check_stats(ws, ref, d)
+
+
+@pytest.mark.parametrize("din", [torch.float32, torch.bfloat16])
+def test_padded_row_stride_and_inplace(din):
+    # logits rows padded to ld > V; then the same chunk updated in place
+    V, n = 1024, 45
+    d = make_chunk(n, V, din, seed=3, ld=1040)
+    scale = 0.01
+    ref = run_oracle(d, scale)
+    ws = run_gpu(d, scale=scale)
+    assert_tokens_match(ws, ref, d)
+    ws2 = run_gpu(d, scale=scale, dlogits="inplace")
+    assert torch.equal(ws2["dlogits"], ws["dlogits"])
+    assert torch.equal(d["logits"], ws["dlogits"])           # the logits buffer now holds dlogits
+
+
+def test_denominator_from_device_count():
+    d = make_chunk(300, 4096, torch.bfloat16, seed=4)
+    N = ops.count_valid(d["g"]["mask"])
+    assert int(N.item()) == int(d["mask"].sum())
+    a = run_gpu(d, scale=1.0, denom=N)
+    b = run_gpu(d, scale=1.0 / int(d["mask"].sum()))
+    ref = run_oracle(d, 1.0 / int(d["mask"].sum()))
+    assert_tokens_match(a, ref, d)
+    assert rel_l2(to_f64(a["dlogits"]), to_f64(b["dlogits"])) < 1e-6
+
+
+def test_all_masked_and_empty():
+    d = make_chunk(40, 1024, torch.float32, seed=5)
+    d["g"]["mask"].zero_()
+    d["mask"][:] = 0
+    ws = run_gpu(d, scale=1.0)
+    assert not ws["dlogits"].any() and not ws["logp"].any() and not ws["loss_tok"].any()
+    chunk, rows = _stats(ws)
+    assert chunk["n_valid"] == 0 and chunk["loss_sum"] == 0.0 and chunk["n_valid_rows"] == 0
+    # zero tokens: stats still written
+    e = make_chunk(0, 64, torch.float32, seed=6, n_rows=1, with_old=False)
+    ws = run_gpu(e, scale=1.0)
+    chunk, _ = _stats(ws)
+    assert chunk["n_valid"] == 0 and chunk["loss_sum"] == 0.0
+
+
+def test_bad_targets_and_nan_logits_are_flagged_not_read():
+    d = make_chunk(20, 1024, torch.float32, seed=7)
+    d["mask"][:] = 1
+    d["g"]["mask"].fill_(1)
+    d["target"][3] = 1024
+    d["target"][4] = -5
+    d["g"]["target"].copy_(torch.from_numpy(d["target"]))
+    d["logits"][9, 17] = float("nan")
+    d["z64"][9, 17] = np.nan
+    ws = run_gpu(d, scale=1.0)
+    flags = ws["tok_flags"].cpu().numpy()
+    assert set(np.nonzero(flags & 4)[0].tolist()) == {3, 4, 9}
+    chunk, _ = _stats(ws)
+    assert chunk["n_nonfinite"] == 3
+    acc = ops.Accumulator(2)
+    assert acc.add(chunk) == "NONFINITE"          # window of 2 poisoned at position 0
+    clean = dict(chunk, n_nonfinite=0, loss_sum=1.0, entropy_sum=1.0)
+    assert acc.add(clean) == "SKIPPED"            # the rest of the poisoned window
+    assert acc.add(clean) == "OK"                 # a fresh window
+
+
+def test_clip_quadrants_exercised():
+    d = make_chunk(400, 1024, torch.float32, seed=8, noise=0.6)
+    ref = run_oracle(d, 1.0)
+    ws = run_gpu(d, scale=1.0)
+    assert_tokens_match(ws, ref, d)
+    A = d["adv_row"][d["tok_row"]]
+    rho = np.exp(ref["logp"] - d["old"])
+    v = ref["valid"]
+    for cond in ((A > 0) & (rho > 1.2), (A > 0) & (rho < 0.8), (A < 0) & (rho > 1.2), (A < 0) & (rho < 0.8)):
+        assert (cond & v).sum() >= 5
+
+
+def test_asymmetric_clip():
+    d = make_chunk(200, 1024, torch.float32, seed=9, noise=0.5)
+    ref = run_oracle(d, 0.5, eps=(0.2, 0.28))
+    ws = run_gpu(d, scale=0.5, eps=(0.2, 0.28))
+    assert_tokens_match(ws, ref, d, eps=(0.2, 0.28))
+
+
+def test_runs_are_bit_identical():
+    d = make_chunk(64, 151936, torch.bfloat16, seed=10)
+    a = run_gpu(d, scale=0.001)
+    b = run_gpu(d, scale=0.001)
+    for k in ("dlogits", "logp", "entropy", "loss_tok", "row_stats", "chunk_stats"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_chunked_equals_unchunked_bit_exact():
+    # The same rows run as one chunk and as four: dlogits, per-token outputs and
+    # row stats are bit-identical (per-token scale, row-local reductions).
+    n_rows, T, V = 16, 24, 4096
+    d = make_chunk(n_rows * T, V, torch.bfloat16, seed=11, n_rows=2)
+    row_off = np.arange(0, n_rows * T + 1, T).astype(np.int64)
+    tok_row = np.repeat(np.arange(n_rows, dtype=np.int32), T)
+    adv = np.random.default_rng(1).normal(size=n_rows).astype(np.float32)
+    g = d["g"]
+    whole = ops.loss_fwd_bwd(d["logits"], g["target"], g["mask"], g["old"], torch.from_numpy(tok_row).to(DEV),
+                             torch.from_numpy(adv).to(DEV), torch.from_numpy(row_off).to(DEV), scale=1 / 377.0)
+    parts = []
+    for c in range(4):
+        a, b = c * 4 * T, (c + 1) * 4 * T
+        parts.append(ops.loss_fwd_bwd(d["logits"][a:b], g["target"][a:b], g["mask"][a:b], g["old"][a:b],
+                                      torch.from_numpy(tok_row[a:b] - 4 * c).to(DEV),
+                                      torch.from_numpy(adv[4 * c:4 * c + 4]).to(DEV),
+                                      torch.from_numpy(row_off[4 * c:4 * c + 5] - a).to(DEV), scale=1 / 377.0))
+    assert torch.equal(torch.cat([p["dlogits"] for p in parts]), whole["dlogits"])
+    for k in ("logp", "entropy", "loss_tok", "tok_flags"):
+        assert torch.equal(torch.cat([p[k] for p in parts]), whole[k]), k
+    assert torch.equal(torch.cat([p["row_stats"][:4] for p in parts]), whole["row_stats"][:n_rows])
+
+
+@pytest.mark.parametrize("V,dtype,n", [(1024, torch.float32, 130), (151936, torch.bfloat16, 7),
+                                       (1000, torch.bfloat16, 19), (4096, torch.bfloat16, 66)])
+def test_logprob_fwd_matches_oracle(V, dtype, n):
+    d = make_chunk(n, V, dtype, seed=12 + V, with_old=False)
+    logp, lse, ent = ops.logprob_fwd(d["logits"], d["g"]["target"], d["g"]["mask"])
+    ref = oracle.logprob_fwd(d["z64"], d["target"], d["mask"])
+    tol = 1e-5 if dtype == torch.float32 else 2e-3
+    assert np.max(np.abs(to_f64(logp) - ref["logp"])) <= tol
+    assert np.max(np.abs(to_f64(lse) - ref["lse"])) <= tol
+    assert np.max(np.abs(to_f64(ent) - ref["entropy"]) - 1e-5 * np.abs(ref["entropy"])) <= 1e-4
+    # the loss kernel's forward outputs are the same numbers
+    ws = run_gpu(make_chunk(n, V, dtype, seed=12 + V, with_old=False), scale=1.0, dlogits=None)
+    assert torch.equal(ws["logp"], logp) and torch.equal(ws["lse"], lse)
+
+
+def test_count_valid_and_tok_row():
+    rng = np.random.default_rng(13)
+    for n in (0, 1, 15, 16, 17, 1000, 131072 + 5):
+        m = (rng.random(n) < 0.6).astype(np.uint8) * rng.integers(1, 255, n).astype(np.uint8)
+        t = torch.from_numpy(m).to(DEV)
+        assert int(ops.count_valid(t).item()) == int((m != 0).sum())
+        if n > 3:   # unaligned start
+            assert int(ops.count_valid(t[3:]).item()) == int((m[3:] != 0).sum())
+    off = np.array([0, 0, 5, 9, 9, 20], np.int64)
+    tr = ops.tok_row(torch.from_numpy(off).to(DEV), 22).cpu().numpy()
+    want = [1] * 5 + [2] * 4 + [4] * 11 + [-1, -1]
+    assert tr.tolist() == want

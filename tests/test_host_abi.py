@@ -1,0 +1,213 @@
+"""CPU tests of libgrpo's host half through the C ABI: every declared symbol
+is exported, the ctypes structs match the C layout, and the host plans,
+advantages and accumulator agree with the oracle (plans bit-exact)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import PlanError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "grpo.h")
+
+C = pytest.importorskip("grpo_token_level_amd._capi")
+try:
+    C.lib()
+except ImportError as e:  # pragma: no cover - the driver builds before testing
+    pytest.skip(str(e), allow_module_level=True)
+from grpo_token_level_amd import ops  # noqa: E402
+from grpo_token_level_amd.ops import GrpoError  # noqa: E402
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(grpo_\w+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(C.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding declares a prototype for each of them
+    assert sorted(C.PROTOTYPES) == names
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "grpo.h"
+#define F(T, f) printf(#T "." #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("grpo_stats %zu\n", sizeof(grpo_stats));
+  printf("grpo_loss_args %zu\n", sizeof(grpo_loss_args));
+  printf("grpo_accum %zu\n", sizeof(grpo_accum));
+  printf("grpo_step_result %zu\n", sizeof(grpo_step_result));
+  F(grpo_loss_args, logits) F(grpo_loss_args, n_rows) F(grpo_loss_args, eps_low) F(grpo_loss_args, denom)
+  F(grpo_loss_args, dlogits) F(grpo_loss_args, chunk_stats) F(grpo_accum, open) F(grpo_accum, closed)
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines())
+    assert int(got["grpo_stats"]) == ctypes.sizeof(C.Stats) == C.STATS_BYTES
+    assert int(got["grpo_loss_args"]) == ctypes.sizeof(C.LossArgs)
+    assert int(got["grpo_accum"]) == ctypes.sizeof(C.Accum)
+    assert int(got["grpo_step_result"]) == ctypes.sizeof(C.StepResult)
+    for key, v in got.items():
+        if "." in key:
+            struct, field = key.split(".")
+            cls = {"grpo_loss_args": C.LossArgs, "grpo_accum": C.Accum}[struct]
+            assert getattr(cls, field).offset == int(v), key
+
+
+# ---------------------------------------------------------------- plans vs oracle
+
+def _kind(fn, *a, **k):
+    try:
+        return fn(*a, **k), None
+    except PlanError as e:
+        return None, e.kind
+    except GrpoError as e:
+        return None, e.kind
+    except ValueError:
+        return None, "EINVAL"
+
+
+def test_fixed_plan_matches_oracle():
+    rng = np.random.default_rng(0)
+    cases = [(32, 4, 16, 8), (32, 4, 0, 0), (30, 4, 0, 0), (64, 4, 0, 8), (128, 8, 64, 4), (32, 4, 12, 0),
+             (32, 4, 16, 5), (0, 4, 0, 0), (32, 0, 0, 0), (32, 4, -1, 0)]
+    for _ in range(300):
+        cases.append(tuple(int(x) for x in (rng.integers(0, 70), rng.integers(0, 9), rng.integers(0, 70), rng.integers(0, 40))))
+    for c in cases:
+        want, wk = _kind(oracle.plan_fixed, *c)
+        got, gk = _kind(ops.plan_fixed, *c)
+        assert (got, gk) == (want, wk), c
+        if want:
+            for i, j in oracle.train_calls(want):
+                assert ops.plan_chunk(c[0], want[2], want[3], i, j) == oracle.chunk_rows(want, i, j)
+
+
+def test_plan_chunk_rejects_out_of_range():
+    with pytest.raises(GrpoError) as e:
+        ops.plan_chunk(32, 16, 8, 2, 0)
+    assert e.value.kind == "EINVAL"
+
+
+def test_dynamic_plan_matches_oracle_bit_exact():
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        n = int(rng.integers(0, 60))
+        budget = int(rng.integers(8, 300))
+        lengths = rng.integers(0, budget + (1 if rng.random() < 0.9 else 40), size=n).tolist()
+        pd = int(rng.integers(1, 5000))
+        want, wk = _kind(oracle.plan_dynamic, lengths, budget, pd)
+        got, gk = _kind(ops.plan_dynamic, lengths, budget, pd)
+        assert gk == wk
+        if want:
+            assert got["n_bins"] == want["n_bins"]
+            assert got["bin_off"].tolist() == want["bin_off"]
+            assert got["order"].tolist() == want["order"]
+            assert got["restore"].tolist() == want["restore"]
+
+
+def test_dynamic_plan_on_the_lognormal_workload():
+    from synth import dynamic_lengths
+    for seed in range(3):
+        L = dynamic_lengths(seed=seed).tolist()
+        want = oracle.plan_dynamic(L, 16384, 4096)
+        got = ops.plan_dynamic(L, 16384, 4096)
+        assert got["order"].tolist() == want["order"] and got["bin_off"].tolist() == want["bin_off"]
+
+
+def test_dynamic_capacity_error_reports_need():
+    nb = ctypes.c_int64()
+    L = np.array([8] * 10, np.int64)
+    off = np.zeros(3, np.int64)
+    order = np.zeros(10, np.int64)
+    rest = np.zeros(10, np.int64)
+    code = C.lib().grpo_plan_dynamic(C.ptr64(L), 10, 8, 4, 2, ctypes.byref(nb), C.ptr64(off), C.ptr64(order), C.ptr64(rest))
+    assert code == -7 and nb.value == 10
+
+
+def test_compaction_plan_matches_oracle():
+    rng = np.random.default_rng(2)
+    cases = [([1, 3, 2, 5, 1, 1], 3, 2, 4, 6, False), ([1, 3, 2, 5, 1, 1], 3, 2, 4, 8, False),
+             ([1, 3, 2, 5], 3, 2, 4, 6, False), ([1, 0, 2, 5, 1, 1], 3, 2, 4, 6, False),
+             ([1, 3, 2, 5, 1, 1], 3, 2, 4, 6, True), ([1, 3, 2, 5, 1, 1], 3, 2, 0, 6, False)]
+    for _ in range(200):
+        G, ng, Q = int(rng.integers(1, 6)), int(rng.integers(1, 8)), int(rng.integers(1, 9))
+        seg = rng.integers(1, 6, size=ng * G).tolist()
+        cases.append((seg, ng, G, Q, ng * G, False))
+    for seg, ng, G, Q, exp, dyn in cases:
+        want, wk = _kind(oracle.plan_compaction, seg, ng, G, Q, exp, dynamic=dyn)
+        got, gk = _kind(ops.plan_compaction, seg, ng, G, Q, exp, dynamic=dyn)
+        assert gk == wk, (seg, ng, G, Q, exp, dyn)
+        if want:
+            for k in ("row_rollout", "row_seg", "row_src", "is_pad", "group_pad"):
+                assert got[k].tolist() == want[k], k
+            assert got["n_rows"] == want["n_rows"]
+
+
+def test_row_offsets():
+    L = np.array([3, 0, 5, 2])
+    assert ops.row_offsets(L).tolist() == [0, 3, 3, 8, 10]
+    assert ops.row_offsets(L, [2, 0, 3, 1]).tolist() == [0, 5, 8, 10, 10]
+
+
+# ---------------------------------------------------------------- advantage vs oracle
+
+def test_group_advantage_matches_oracle():
+    rng = np.random.default_rng(3)
+    for G in (1, 2, 4, 8):
+        for norm in (True, False):
+            r = (rng.random(8 * G) < 0.5).astype(np.float32) + rng.normal(0, 0.1, 8 * G).astype(np.float32)
+            got = ops.group_advantage(r, G, 1e-6, norm)
+            want = oracle.group_advantage(r.astype(np.float64), G, 1e-6, norm)
+            # host accumulates in double and rounds once to float32
+            assert np.allclose(got, want, rtol=2 ** -23, atol=1e-12)
+    with pytest.raises(GrpoError):
+        ops.group_advantage([1, 0, 1], 2)
+
+
+def test_rows_advantage_matches_oracle():
+    p = oracle.plan_compaction([1, 3, 2, 5, 1, 1], 3, 2, 4, 6)
+    A = np.array([1.0, -1.0, 0.5, -0.5, 2.0, -2.0], np.float32)
+    assert ops.rows_advantage(A, p["row_rollout"]).tolist() == oracle.rows_advantage(A, p["row_rollout"]).tolist()
+    with pytest.raises(GrpoError):
+        ops.rows_advantage(A, [0, 6])
+
+
+# ---------------------------------------------------------------- accumulator vs oracle
+
+def test_accumulator_matches_oracle_on_random_sequences():
+    rng = np.random.default_rng(4)
+    for _ in range(100):
+        n_micro = int(rng.integers(1, 6))
+        a, b = oracle.Accumulator(n_micro), ops.Accumulator(n_micro)
+        for _ in range(int(rng.integers(1, 40))):
+            if rng.random() < 0.3:
+                fa, fb = a.finalize(), b.finalize()
+                assert (fa is None) == (fb is None)
+                if fa:
+                    for k in fa:
+                        assert fb[k] == pytest.approx(fa[k], rel=1e-15, abs=0), k
+                continue
+            bad = rng.random() < 0.15
+            st = {"loss_sum": float("nan") if bad and rng.random() < 0.5 else float(rng.normal()),
+                  "entropy_sum": float(rng.random()), "n_valid": int(rng.integers(0, 50)),
+                  "n_clipped": int(rng.integers(0, 3)), "n_nonfinite": 1 if bad else 0,
+                  "n_valid_rows": int(rng.integers(0, 4))}
+            assert b.add(st) == a.add(st)

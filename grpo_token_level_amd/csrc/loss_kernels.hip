@@ -88,6 +88,20 @@ template <> struct In<GRPO_F32> {
     }
 };
 
+// 16-byte global store; GRPO_NT_STORES selects the non-temporal form
+// (dlogits are written once and not re-read by this kernel).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ void st16(T* p, const T& v) {
+#ifdef GRPO_NT_STORES
+    if constexpr (sizeof(T) == 16) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+    else __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), reinterpret_cast<u32x2*>(p));
+#else
+    *p = v;
+#endif
+}
+
 template <int DT> struct Out;
 template <> struct Out<GRPO_BF16> {
     static constexpr int BYTES = 2;
@@ -98,18 +112,18 @@ template <> struct Out<GRPO_BF16> {
             uint4 v;
             v.x = pack_bf16x2(d[0], d[1]); v.y = pack_bf16x2(d[2], d[3]);
             v.z = pack_bf16x2(d[4], d[5]); v.w = pack_bf16x2(d[6], d[7]);
-            *reinterpret_cast<uint4*>(p) = v;
+            st16(reinterpret_cast<uint4*>(p), v);
         } else {
             uint2 v;
             v.x = pack_bf16x2(d[0], d[1]); v.y = pack_bf16x2(d[2], d[3]);
-            *reinterpret_cast<uint2*>(p) = v;
+            st16(reinterpret_cast<uint2*>(p), v);
         }
     }
     template <int N>
     __device__ static __forceinline__ void zero(void* row, int e0) {
         uint16_t* p = reinterpret_cast<uint16_t*>(row) + e0;
-        if constexpr (N == 8) *reinterpret_cast<uint4*>(p) = make_uint4(0, 0, 0, 0);
-        else *reinterpret_cast<uint2*>(p) = make_uint2(0, 0);
+        if constexpr (N == 8) st16(reinterpret_cast<uint4*>(p), make_uint4(0, 0, 0, 0));
+        else st16(reinterpret_cast<uint2*>(p), make_uint2(0, 0));
     }
     __device__ static __forceinline__ void scalar(void* row, int64_t i, float d) {
         f32x2 v = {d, 0.0f};
@@ -122,14 +136,14 @@ template <> struct Out<GRPO_F32> {
     template <int N>
     __device__ static __forceinline__ void store(void* row, int e0, const float (&d)[N]) {
         float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(row) + e0);
-        p[0] = make_float4(d[0], d[1], d[2], d[3]);
-        if constexpr (N == 8) p[1] = make_float4(d[4], d[5], d[6], d[7]);
+        st16(p, make_float4(d[0], d[1], d[2], d[3]));
+        if constexpr (N == 8) st16(p + 1, make_float4(d[4], d[5], d[6], d[7]));
     }
     template <int N>
     __device__ static __forceinline__ void zero(void* row, int e0) {
         float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(row) + e0);
-        p[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if constexpr (N == 8) p[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        st16(p, make_float4(0.f, 0.f, 0.f, 0.f));
+        if constexpr (N == 8) st16(p + 1, make_float4(0.f, 0.f, 0.f, 0.f));
     }
     __device__ static __forceinline__ void scalar(void* row, int64_t i, float d) {
         reinterpret_cast<float*>(row)[i] = d;
@@ -489,22 +503,25 @@ __global__ __launch_bounds__(256) void tok_generic_kernel(const TokParams p) {
 
 // ---------------------------------------------------------------- statistics
 
-// One wave per row: lane j takes the row's tokens j, j+64, ...; fixed
-// butterfly.  A row's stats depend only on its own tokens.
+// One 256-thread block per row: thread j takes the row's tokens j, j+256, ...,
+// then a fixed tree over the block.  A row's stats depend only on its own
+// tokens (never on where the row sits in the chunk).
 __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ loss_tok,
                                                         const float* __restrict__ entropy,
                                                         const uint8_t* __restrict__ flags,
                                                         const int64_t* __restrict__ row_off, int64_t n_rows,
                                                         int64_t n_tok, grpo_stats* __restrict__ out) {
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    __shared__ double s_ls[4], s_es[4];
+    __shared__ long long s_nv[4], s_nc[4], s_nn[4];
+    const int64_t r = blockIdx.x;
+    const int i = threadIdx.x;
     if (r >= n_rows) return;
     int64_t b = row_off[r], e = row_off[r + 1];
     b = b < 0 ? 0 : (b > n_tok ? n_tok : b);
     e = e < b ? b : (e > n_tok ? n_tok : e);
     double ls = 0.0, es = 0.0;
     long long nv = 0, nc = 0, nn = 0;
-    for (int64_t t = b + lane; t < e; t += 64) {
+    for (int64_t t = b + i; t < e; t += 256) {
         const uint8_t f = flags[t];
         if (f & 1u) {
             ls += (double)loss_tok[t];
@@ -519,14 +536,19 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
     nv = wave_sum_i(nv);
     nc = wave_sum_i(nc);
     nn = wave_sum_i(nn);
-    if (lane == 0) {
+    const int w = i >> 6;
+    if ((i & 63) == 0) {
+        s_ls[w] = ls; s_es[w] = es; s_nv[w] = nv; s_nc[w] = nc; s_nn[w] = nn;
+    }
+    __syncthreads();
+    if (i == 0) {
         grpo_stats s;
-        s.loss_sum = ls;
-        s.entropy_sum = es;
-        s.n_valid = nv;
-        s.n_clipped = nc;
-        s.n_nonfinite = nn;
-        s.n_valid_rows = nv > 0 ? 1 : 0;
+        s.loss_sum = ((s_ls[0] + s_ls[1]) + s_ls[2]) + s_ls[3];
+        s.entropy_sum = ((s_es[0] + s_es[1]) + s_es[2]) + s_es[3];
+        s.n_valid = s_nv[0] + s_nv[1] + s_nv[2] + s_nv[3];
+        s.n_clipped = s_nc[0] + s_nc[1] + s_nc[2] + s_nc[3];
+        s.n_nonfinite = s_nn[0] + s_nn[1] + s_nn[2] + s_nn[3];
+        s.n_valid_rows = s.n_valid > 0 ? 1 : 0;
         out[r] = s;
     }
 }
@@ -703,7 +725,7 @@ extern "C" int grpo_logprob_fwd(void* stream, int32_t dtype, const void* logits,
     if (dtype != GRPO_F32 && dtype != GRPO_BF16) return fail(GRPO_EINVAL, "grpo_logprob_fwd: unknown dtype %d", dtype);
     if (n_tok < 0 || V < 1 || ld < V) return fail(GRPO_EINVAL, "grpo_logprob_fwd: need n_tok >= 0, V >= 1, ld >= V");
     if (n_tok > 0 && (!logits || !target || !mask || !logp)) return fail(GRPO_EINVAL, "grpo_logprob_fwd: NULL pointer");
-    if (n_tok > 0x7fffffffLL * 4) return fail(GRPO_EINVAL, "grpo_logprob_fwd: too many tokens for one launch");
+    if (n_tok > 0x7fffffffLL) return fail(GRPO_EINVAL, "grpo_logprob_fwd: too many tokens for one launch");
     TokParams p{};
     p.logits = logits; p.ld = ld; p.n_tok = n_tok; p.V = V;
     p.target = target; p.mask = mask;
@@ -725,7 +747,8 @@ extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
     if (a->n_tok < 0 || a->V < 1 || a->ld < a->V || a->n_rows < 0)
         return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: need n_tok >= 0, V >= 1, ld >= V, n_rows >= 0");
     if (a->n_tok > 0 && a->n_rows < 1) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: tokens without rows");
-    if (a->n_tok > 0x7fffffffLL) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: too many tokens for one launch");
+    if (a->n_tok > 0x7fffffffLL || a->n_rows > 0x7fffffffLL)
+        return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: too many tokens or rows for one launch");
     if (!a->chunk_stats || (a->n_rows > 0 && (!a->row_stats || !a->row_off)))
         return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: NULL stats pointer");
     if (a->n_tok > 0 && (!a->logits || !a->target || !a->mask || !a->old_logp || !a->tok_row || !a->adv_row ||
@@ -761,7 +784,7 @@ extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
     else e = launch_tok<GRPO_F32, GRPO_F32, true>(p, vec_ok, st);
     if (e != hipSuccess) return check_launch(e, "grpo_loss_fwd_bwd (token kernel)");
     if (a->n_rows > 0) {
-        hipLaunchKernelGGL(row_stats_kernel, dim3((unsigned)((a->n_rows + 3) / 4)), dim3(256), 0, st, a->loss_tok,
+        hipLaunchKernelGGL(row_stats_kernel, dim3((unsigned)a->n_rows), dim3(256), 0, st, a->loss_tok,
                            a->entropy, a->tok_flags, a->row_off, a->n_rows, a->n_tok, a->row_stats);
         e = hipGetLastError();
         if (e != hipSuccess) return check_launch(e, "grpo_loss_fwd_bwd (row stats)");

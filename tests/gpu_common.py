@@ -127,3 +127,83 @@ def assert_tokens_match(ws, ref, d, idx=None, check_dz=True, eps=(0.2, 0.2)):
         assert rel_l2(dz, want) <= 1e-3, rel_l2(dz, want)
         assert not dz[~valid[keep]].any()
     return int(differ.sum())
+
+
+def torch_logp(logits, target, block=512):
+    """Current log-probs from a plain PyTorch fp32 log-softmax (used only to
+    shape old log-probs as "current + small drift" for large inputs)."""
+    out = torch.empty(logits.shape[0], dtype=torch.float32, device=logits.device)
+    for a in range(0, logits.shape[0], block):
+        b = min(a + block, logits.shape[0])
+        lp = torch.log_softmax(logits[a:b].float(), dim=-1)
+        out[a:b] = lp.gather(1, target[a:b].long()[:, None])[:, 0]
+    return out
+
+
+def padded_on_gpu(workload, seed=0, **over):
+    """A padded workload resident on the GPU: logits drawn row by row from the
+    seeded streams, old log-probs = torch log-probs + the workload's noise."""
+    from synth import fill_normal_rows, padded_batch
+    b = padded_batch(workload, seed=seed, **over)
+    n_rows, T, V = b["n_rows"], b["T"], b["V"]
+    dt = torch.bfloat16 if b["dtype"] == "bf16" else torch.float32
+    logits = torch.empty((n_rows * T, V), dtype=dt, device=DEV)
+    fill_normal_rows(logits, range(n_rows), [r * T for r in range(n_rows)], [T] * n_rows, b["logit_std"], seed, workload)
+    G = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    target, mask = G(b["target"]), G(b["mask"])
+    old = (torch_logp(logits, target).double() + G(b["logratio_noise"])).float()
+    return b, logits, target, mask, old
+
+
+def oracle_tokens(logits, target, mask, old, adv_tok, scale, idx, eps=(0.2, 0.2)):
+    """Oracle outputs for the sampled token indices ``idx`` of a GPU batch."""
+    ii = torch.as_tensor(np.asarray(idx), device=DEV)
+    z = logits[ii].double().cpu().numpy()
+    return oracle.loss_fwd_bwd(z, target[ii].cpu().numpy(), mask[ii].cpu().numpy(),
+                               old[ii].double().cpu().numpy(), np.asarray(adv_tok, np.float64)[np.asarray(idx)],
+                               scale, eps[0], eps[1])
+
+
+def compare_sampled(out, ref, idx, old_np, dtype, dz_rows=None, eps=(0.2, 0.2)):
+    """Per-token outputs (dicts of full-length GPU tensors) at ``idx`` vs the
+    oracle dict ``ref``; ``dz_rows``: the kernel's dlogits rows at ``idx``."""
+    ii = torch.as_tensor(np.asarray(idx), device=DEV)
+    valid = ref["valid"]
+    flags = out["tok_flags"][ii].cpu().numpy()
+    assert np.array_equal((flags & 1).astype(bool), valid)
+    fin = valid & ~ref["nonfinite"]
+    logp = to_f64(out["logp"][ii])
+    assert np.all(np.abs(logp[fin] - ref["logp"][fin]) <= tol_logp(dtype)), np.max(np.abs(logp[fin] - ref["logp"][fin]))
+    ent = to_f64(out["entropy"][ii])
+    assert np.all(np.abs(ent[fin] - ref["entropy"][fin]) <= 1e-4 + 1e-5 * np.abs(ref["entropy"][fin]))
+    lt = to_f64(out["loss_tok"][ii])
+    assert np.all(np.abs(lt[fin] - ref["loss_tok"][fin]) <= 1e-4 * np.maximum(np.abs(ref["loss_tok"][fin]), 1e-3))
+    with np.errstate(over="ignore", invalid="ignore"):
+        rho = np.exp(ref["logp"] - old_np)
+    hi, lo = 1.0 + eps[1], 1.0 - eps[0]
+    edge = fin & ((np.abs(rho - hi) <= 1e-4 * hi) | (np.abs(rho - lo) <= 1e-4))
+    differ = ((flags >> 1) & 1).astype(bool) != (ref["clipped"] & valid)
+    assert not np.any(differ & ~edge)
+    if dz_rows is not None:
+        keep = ~differ
+        dz = to_f64(dz_rows)[keep]
+        want = ref["dz"][keep]
+        if dz_rows.dtype == torch.bfloat16:
+            want = oracle.round_to_bf16(want)
+        assert rel_l2(dz, want) <= 1e-3, rel_l2(dz, want)
+        assert not dz[~valid[keep]].any()
+
+
+def sample_tokens(mask_np, row_len, n_valid=24, n_masked=8, seed=0):
+    """Token indices to check one by one: first/last positions of rows, random
+    valid tokens, random masked tokens."""
+    rng = np.random.default_rng(seed)
+    v = np.nonzero(mask_np)[0]
+    m = np.nonzero(mask_np == 0)[0]
+    pick = list(rng.choice(v, size=min(n_valid, len(v)), replace=False))
+    if len(m):
+        pick += list(rng.choice(m, size=min(n_masked, len(m)), replace=False))
+    pick += [0, len(mask_np) - 1]
+    for r0 in np.cumsum(np.concatenate([[0], row_len]))[:-1][:4]:
+        pick.append(int(r0))
+    return np.unique(np.asarray(pick, np.int64))

@@ -57,6 +57,17 @@ class LossArgs(ctypes.Structure):
                 ("row_stats", _p), ("chunk_stats", _p)]
 
 
+class LmheadArgs(ctypes.Structure):
+    _fields_ = [("struct_size", _i32), ("reserved0", _i32), ("h", _p), ("ldh", _i64), ("W", _p), ("Wt", _p),
+                ("n_tok", _i64), ("H", _i64), ("V", _i64),
+                ("target", _p), ("mask", _p), ("old_logp", _p), ("tok_row", _p), ("adv_row", _p),
+                ("row_off", _p), ("n_rows", _i64),
+                ("eps_low", _f32), ("eps_high", _f32), ("scale", _f32), ("reserved1", _i32),
+                ("denom", _p), ("dh", _p), ("dW", _p),
+                ("logp", _p), ("lse", _p), ("entropy", _p), ("loss_tok", _p), ("tok_flags", _p),
+                ("row_stats", _p), ("chunk_stats", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class Accum(ctypes.Structure):
     _fields_ = [("n_micro", _i64), ("pos", _i64), ("skip", _i64), ("done", _i32), ("reserved", _i32),
                 ("open", Stats), ("closed", Stats)]
@@ -88,6 +99,9 @@ PROTOTYPES = {
     "grpo_tok_row": (ctypes.c_int, [_p, _p, _i64, _i64, _p]),
     "grpo_logprob_fwd": (ctypes.c_int, [_p, _i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "grpo_loss_fwd_bwd": (ctypes.c_int, [_p, ctypes.POINTER(LossArgs)]),
+    "grpo_transpose_bf16": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _i64]),
+    "grpo_lmhead_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64]),
+    "grpo_lmhead_fwd_bwd": (ctypes.c_int, [_p, ctypes.POINTER(LmheadArgs)]),
     "grpo_accum_init": (ctypes.c_int, [ctypes.POINTER(Accum), _i64]),
     "grpo_accum_add": (ctypes.c_int, [ctypes.POINTER(Accum), ctypes.POINTER(Stats)]),
     "grpo_accum_finalize": (ctypes.c_int, [ctypes.POINTER(Accum), ctypes.POINTER(StepResult),

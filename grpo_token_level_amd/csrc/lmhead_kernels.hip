@@ -1,0 +1,547 @@
+// LM-head variant of the token-level GRPO loss for gfx950: the logits
+// z = h W^T are produced by bf16 MFMA GEMMs tile by tile and consumed in the
+// GEMM epilogues, so no [tokens x V] logit or gradient matrix is ever held.
+//
+// Sources: [P1] "Sizing mini-batches and micro-batches" ("The problem": the
+// materialised log-softmax is the memory wall; "The hard part: deferred
+// normalization": chunk gradients add up to the step gradient); [P4] "How a
+// context-compaction step fits a variable number of rows into one batch"
+// (rows are micro-batched, padding rows are masked and add nothing).
+//
+// One call handles one micro-batch chunk of n tokens:
+//   pass 1  GEMM z = h W^T over the whole vocabulary; the epilogue reduces
+//           each 64-column slice of a token row to (max, sum e, sum e*t) and
+//           picks out the target logit.  A merge kernel combines the slices
+//           (fixed order) into logsumexp, entropy, log-prob, the surrogate and
+//           the gradient coefficient.
+//   pass 2  per vocabulary chunk of Vc columns: the GEMM recomputes z and its
+//           epilogue writes dz = coef*(softmax - onehot) in bf16 (row-major and
+//           transposed) into a bounded workspace; then dh (+)= dz W_c and
+//           dW_c += dz^T h, two more MFMA GEMMs with fp32 accumulation.
+// All products use one kernel shape, C[m,n] = sum_k A[m,k] B[n,k] with both
+// operands K-contiguous ("NT"): W for pass 1, W^T for dh, h^T and dz^T for dW.
+//
+// MFMA: v_mfma_f32_32x32x16_bf16.  A 256-thread block computes a 128x128 tile
+// (four waves, 64x64 each = 2x2 MFMA tiles), K in steps of 64 staged through
+// LDS with double buffering.  Lane layouts (checked on the device): operand
+// lane l holds row/column l%32 and k = (l/32)*8 .. +8; result lane l, register
+// i holds column l%32 and row (i/4)*8 + (l/32)*4 + i%4.  Blocks are mapped so
+// that each XCD works through a contiguous range of tiles, M fastest: the
+// tiles that share a W slice run together on one L2.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "common.h"
+#include "surrogate.h"
+
+using grpo::fail;
+using grpo::ok;
+using grpo_dev::kLn2;
+using grpo_dev::kLog2e;
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LDK = BK + 8;          // LDS row stride in bf16 (144 B): conflict-free 16-byte fragment reads
+constexpr int NTHREADS = 256;
+constexpr int NXCD = 8;
+constexpr int kVocabChunk = 16384;   // pass-2 vocabulary chunk (bounds the dz workspace)
+
+enum { EPI_STATS = 0, EPI_DZ = 1, EPI_ACC = 2 };
+
+struct GemmArgs {
+    const uint16_t* A;   // row m at A + m*lda, K contiguous
+    int64_t lda;
+    const uint16_t* B;   // row n at B + n*ldb, K contiguous
+    int64_t ldb;
+    int M, N, K;         // K % 8 == 0; rows >= M / >= N are read as zeros
+    int tiles_m, tiles_n;
+    // EPI_STATS
+    float4* part;        // part[m * n_parts + n/64] = {max, sum e, sum e*t, 0}
+    int n_parts;
+    const int32_t* target;
+    float* zy;           // zy[m] = z[m, target[m]]
+    // EPI_DZ
+    const float* c2;     // log2-domain logsumexp per token
+    const float* coef;   // gradient coefficient per token
+    int col0;            // vocabulary index of column 0 of this chunk
+    int m_out;           // rows [M, m_out) are written as zeros (K padding of dz^T)
+    uint16_t* dz;        // dz[m * ld_dz + n]
+    int64_t ld_dz;
+    uint16_t* dzT;       // dzT[n * ld_dzT + m]
+    int64_t ld_dzT;
+    // EPI_ACC
+    float* C;            // C[m * ldc + n] = (beta ? C : 0) + acc
+    int64_t ldc;
+    int beta;
+};
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+    f32x2 v = {x, 0.0f};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return (uint16_t)(__builtin_bit_cast(uint32_t, r) & 0xffffu);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Hardware dispatch sends block b to XCD b % 8; renumber so that XCD x owns a
+// contiguous range of logical tiles (a bijection for any block count).
+__device__ __forceinline__ int xcd_logical(int b, int nb) {
+    const int q = nb / NXCD, r = nb % NXCD;
+    const int x = b % NXCD, i = b / NXCD;
+    return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
+    // stage s: A tile at smem + s*(BM+BN)*LDK, B tile right after it
+    auto As = [&](int s) { return smem + s * (BM + BN) * LDK; };
+    auto Bs = [&](int s) { return smem + s * (BM + BN) * LDK + BM * LDK; };
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int logical = xcd_logical(blockIdx.x, g.tiles_m * g.tiles_n);
+    const int m0 = (logical % g.tiles_m) * BM, n0 = (logical / g.tiles_m) * BN;
+
+    // global -> register staging: 128 rows x 64 k per operand = 1024 16-byte
+    // vectors; thread t takes rows t/8 + 32j (j < 4), vector t%8 of the row
+    const int lrow = tid >> 3, lvec = (tid & 7) * 8;
+    uint4 ra[4], rb[4];
+    auto gload = [&](int k0) {
+        const int kk = k0 + lvec;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = m0 + lrow + 32 * j, n = n0 + lrow + 32 * j;
+            ra[j] = (m < g.M && kk < g.K) ? *reinterpret_cast<const uint4*>(g.A + (int64_t)m * g.lda + kk)
+                                          : make_uint4(0, 0, 0, 0);
+            rb[j] = (n < g.N && kk < g.K) ? *reinterpret_cast<const uint4*>(g.B + (int64_t)n * g.ldb + kk)
+                                          : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto sstore = [&](int s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<uint4*>(As(s) + (lrow + 32 * j) * LDK + lvec) = ra[j];
+            *reinterpret_cast<uint4*>(Bs(s) + (lrow + 32 * j) * LDK + lvec) = rb[j];
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+    const int nk = (g.K + BK - 1) / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    const int fr = lane & 31, fk = (lane >> 5) * 8;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int s = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 16) {
+            bf16x8 a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                a[i] = *reinterpret_cast<const bf16x8*>(As(s) + (wm * 64 + i * 32 + fr) * LDK + kk + fk);
+                b[i] = *reinterpret_cast<const bf16x8*>(Bs(s) + (wn * 64 + i * 32 + fr) * LDK + kk + fk);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) sstore(s ^ 1);
+        __syncthreads();
+    }
+
+    // result element (i, j, r): row wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
+    //                           column wn*64 + j*32 + lane%32
+    const int rq = (lane >> 5) * 4;
+    if constexpr (EPI == EPI_ACC) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int n = n0 + wn * 64 + j * 32 + fr;
+                if (n >= g.N) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + rq + (r & 3);
+                    if (m < g.M) {
+                        float* c = g.C + (int64_t)m * g.ldc + n;
+                        *c = g.beta ? *c + acc[i][j][r] : acc[i][j][r];
+                    }
+                }
+            }
+    } else if constexpr (EPI == EPI_DZ) {
+        float* s_c2 = reinterpret_cast<float*>(smem);
+        float* s_cf = s_c2 + BM;
+        int* s_y = reinterpret_cast<int*>(s_cf + BM);
+        if (tid < BM) {
+            const int m = m0 + tid;
+            const bool in = m < g.M;
+            s_c2[tid] = in ? g.c2[m] : 0.0f;
+            s_cf[tid] = in ? g.coef[m] : 0.0f;
+            s_y[tid] = in ? g.target[m] : -1;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int nl = n0 + wn * 64 + j * 32 + fr;   // column within the chunk
+                if (nl >= g.N) continue;
+                const int v = g.col0 + nl;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float d[4];
+                    const int mb = wm * 64 + i * 32 + q * 8 + rq;   // local row of element r = 4q
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int ml = mb + u;
+                        const float cf = s_cf[ml];
+                        float x = cf * __builtin_amdgcn_exp2f(fmaf(acc[i][j][q * 4 + u], kLog2e, -s_c2[ml]));
+                        if (s_y[ml] == v) x -= cf;
+                        d[u] = x;
+                    }
+                    const int m = m0 + mb;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (m + u < g.M) g.dz[(int64_t)(m + u) * g.ld_dz + nl] = to_bf16(d[u]);
+                    if (m + 3 < g.m_out) {
+                        uint2 pk;
+                        pk.x = pack2(d[0], d[1]);
+                        pk.y = pack2(d[2], d[3]);
+                        *reinterpret_cast<uint2*>(g.dzT + (int64_t)nl * g.ld_dzT + m) = pk;
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (m + u < g.m_out) g.dzT[(int64_t)nl * g.ld_dzT + m + u] = to_bf16(d[u]);
+                    }
+                }
+            }
+    } else {
+        // per wave, transpose the 64x64 tile through LDS so that lane r owns row r
+        float* T = reinterpret_cast<float*>(smem) + wave * 64 * 65;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    T[(i * 32 + (r >> 2) * 8 + rq + (r & 3)) * 65 + j * 32 + fr] = acc[i][j][r];
+        __syncthreads();
+        const int m = m0 + wm * 64 + lane;
+        const int nb = n0 + wn * 64;
+        const int ncols = g.N - nb < 64 ? g.N - nb : 64;
+        if (m < g.M && ncols > 0) {
+            const float* row = T + lane * 65;
+            float mx = -INFINITY;
+            for (int c = 0; c < ncols; ++c) mx = fmaxf(mx, row[c]);
+            const float cm = mx * kLog2e;
+            float se = 0.0f, sw = 0.0f;
+            for (int c = 0; c < ncols; ++c) {
+                const float t = fmaf(row[c], kLog2e, -cm);
+                const float e = __builtin_amdgcn_exp2f(t);
+                se += e;
+                sw = fmaf(e, t, sw);
+            }
+            g.part[(int64_t)m * g.n_parts + nb / 64] = make_float4(mx, se, sw, 0.0f);
+            const int y = g.target[m];
+            if (y >= nb && y < nb + ncols) g.zy[m] = row[y - nb];
+        }
+    }
+}
+
+// One wave per token: merge the token's slice partials in a fixed order,
+// then logsumexp, entropy, log-prob, surrogate and gradient coefficient.
+struct MergeArgs {
+    const float4* part;
+    int n_parts;
+    const float* zy;
+    int64_t n_tok;
+    int64_t V;
+    const int32_t* target;
+    const uint8_t* mask;
+    const float* old_logp;
+    const int32_t* tok_row;
+    const float* adv_row;
+    int64_t n_rows;
+    float eps_low, eps_high, scale;
+    const int64_t* denom;
+    float* c2;
+    float* coef;
+    float* logp;
+    float* lse;
+    float* entropy;
+    float* loss_tok;
+    uint8_t* tok_flags;
+};
+
+// (M, S, W): S = sum e^(z-M), W = sum e^(z-M) (z-M) log2(e), merged exactly
+__device__ __forceinline__ void merge_part(float& M, float& S, float& W, float m, float s, float w) {
+    if (s == 0.0f) return;
+    if (S == 0.0f) {
+        M = m;
+        S = s;
+        W = w;
+        return;
+    }
+    const float Mn = fmaxf(M, m);
+    const float d1 = (M - Mn) * kLog2e, d2 = (m - Mn) * kLog2e;
+    const float f1 = __builtin_amdgcn_exp2f(d1), f2 = __builtin_amdgcn_exp2f(d2);
+    const float Sn = S * f1 + s * f2;
+    W = f1 * fmaf(S, d1, W) + f2 * fmaf(s, d2, w);
+    S = Sn;
+    M = Mn;
+}
+
+__global__ __launch_bounds__(256) void lm_merge_kernel(const MergeArgs a) {
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (t >= a.n_tok) return;
+    if (a.mask[t] == 0) {
+        if (lane == 0) {
+            a.c2[t] = 0.0f;
+            a.coef[t] = 0.0f;
+            a.logp[t] = 0.0f;
+            if (a.lse) a.lse[t] = 0.0f;
+            a.entropy[t] = 0.0f;
+            a.loss_tok[t] = 0.0f;
+            a.tok_flags[t] = 0;
+        }
+        return;
+    }
+    float M = 0.0f, S = 0.0f, W = 0.0f;
+    for (int p = lane; p < a.n_parts; p += 64) {
+        const float4 q = a.part[t * a.n_parts + p];
+        merge_part(M, S, W, q.x, q.y, q.z);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(M, o), s2 = __shfl_xor(S, o), w2 = __shfl_xor(W, o);
+        // the same pair is merged on both lanes; order the operands so both
+        // lanes compute bit-identical results
+        float Ma = M, Sa = S, Wa = W, Mb = m2, Sb = s2, Wb = w2;
+        if ((lane & o) != 0) {
+            Ma = m2; Sa = s2; Wa = w2;
+            Mb = M; Sb = S; Wb = W;
+        }
+        merge_part(Ma, Sa, Wa, Mb, Sb, Wb);
+        M = Ma;
+        S = Sa;
+        W = Wa;
+    }
+    if (lane != 0) return;
+    const float log2s = log2f(S);
+    const float c2 = M * kLog2e + log2s;
+    const float lse = c2 * kLn2;
+    const int32_t y = a.target[t];
+    const bool ybad = (uint32_t)y >= (uint64_t)a.V;
+    const float logp = ybad ? __builtin_nanf("") : a.zy[t] - lse;
+    const float H = kLn2 * (log2s - W / S);
+    const int32_t row = a.tok_row[t];
+    const float A = ((uint32_t)row < (uint64_t)a.n_rows) ? a.adv_row[row] : __builtin_nanf("");
+    const grpo_dev::Surrogate sg = grpo_dev::surrogate(logp, H, a.old_logp[t], A, a.eps_low, a.eps_high,
+                                                       grpo_dev::step_scale(a.scale, a.denom));
+    a.c2[t] = c2;
+    a.coef[t] = sg.coef;
+    a.logp[t] = logp;
+    if (a.lse) a.lse[t] = lse;
+    a.entropy[t] = H;
+    a.loss_tok[t] = sg.loss;
+    a.tok_flags[t] = (uint8_t)(1u | (sg.clipped ? 2u : 0u) | (sg.bad ? 4u : 0u));
+}
+
+// dst[c * ld_dst + r] = src[r * ld_src + c] for r < rows, c < cols; columns
+// [rows, rows_pad) of dst are written as zeros.  64x64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t rows,
+                                                             int64_t cols, int64_t ld_src, uint16_t* __restrict__ dst,
+                                                             int64_t ld_dst, int64_t rows_pad) {
+    __shared__ uint16_t tile[64][66];
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int k = ty; k < 64; k += 4) {
+        const int64_t r = r0 + k, c = c0 + tx;
+        tile[k][tx] = (r < rows && c < cols) ? src[r * ld_src + c] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int k = ty; k < 64; k += 4) {
+        const int64_t c = c0 + k, r = r0 + tx;
+        if (c < cols && r < rows_pad) dst[c * ld_dst + r] = tile[tx][k];
+    }
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Workspace {
+    float4* part;
+    float* zy;
+    float* c2;
+    float* coef;
+    uint16_t* hT;
+    uint16_t* dz;
+    uint16_t* dzT;
+    size_t bytes;
+};
+
+Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V) {
+    const int64_t n_parts = (V + 63) / 64;
+    const int64_t n_pad = round_up(n_tok > 0 ? n_tok : 1, 8);
+    const int64_t vc = V < kVocabChunk ? V : kVocabChunk;
+    Workspace w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = (size_t)round_up((int64_t)(off + bytes), 256);
+        return reinterpret_cast<char*>(base) + at;
+    };
+    w.part = reinterpret_cast<float4*>(take((size_t)n_tok * n_parts * sizeof(float4)));
+    w.zy = reinterpret_cast<float*>(take((size_t)n_tok * 4));
+    w.c2 = reinterpret_cast<float*>(take((size_t)n_tok * 4));
+    w.coef = reinterpret_cast<float*>(take((size_t)n_tok * 4));
+    w.hT = reinterpret_cast<uint16_t*>(take((size_t)H * n_pad * 2));
+    w.dz = reinterpret_cast<uint16_t*>(take((size_t)n_tok * vc * 2));
+    w.dzT = reinterpret_cast<uint16_t*>(take((size_t)vc * n_pad * 2));
+    w.bytes = off;
+    return w;
+}
+
+template <int EPI>
+hipError_t launch_gemm(GemmArgs g, hipStream_t st) {
+    g.tiles_m = (g.M + BM - 1) / BM;
+    g.tiles_n = (g.N + BN - 1) / BN;
+    if (EPI == EPI_DZ) g.tiles_m = (g.m_out + BM - 1) / BM;
+    const long long nb = (long long)g.tiles_m * g.tiles_n;
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemm_nt_kernel<EPI>, dim3((unsigned)nb), dim3(NTHREADS), 0, st, g);
+    return hipGetLastError();
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int dev_fail(hipError_t e, const char* what) {
+    return fail(GRPO_EDEVICE, "grpo_lmhead_fwd_bwd (%s): %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V) {
+    if (n_tok < 0 || H <= 0 || V <= 0) return 0;
+    return carve(nullptr, n_tok, H, V).bytes;
+}
+
+extern "C" int grpo_transpose_bf16(void* stream, const void* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                   void* dst, int64_t ld_dst) {
+    if (rows < 0 || cols < 0 || ld_src < cols || ld_dst < rows || (rows > 0 && cols > 0 && (!src || !dst)))
+        return fail(GRPO_EINVAL, "grpo_transpose_bf16: bad arguments");
+    if (rows == 0 || cols == 0) return ok();
+    if ((rows + 63) / 64 > 65535 || (cols + 63) / 64 > 0x7fffffffLL)
+        return fail(GRPO_EINVAL, "grpo_transpose_bf16: too many rows for one launch");
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64)),
+                       dim3(256), 0, (hipStream_t)stream, (const uint16_t*)src, rows, cols, ld_src, (uint16_t*)dst,
+                       ld_dst, rows);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? ok() : fail(GRPO_EDEVICE, "grpo_transpose_bf16: %s", hipGetErrorString(e));
+}
+
+extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
+    if (!a) return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: NULL args");
+    if (a->struct_size != (int32_t)sizeof(grpo_lmhead_args))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: struct_size %d != %d", a->struct_size,
+                    (int)sizeof(grpo_lmhead_args));
+    const int64_t n = a->n_tok, H = a->H, V = a->V;
+    if (n < 0 || H <= 0 || V <= 0 || a->n_rows < 0 || (n > 0 && a->n_rows < 1))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: need n_tok >= 0, H > 0, V > 0, rows for the tokens");
+    if (H % 8 || V % 8 || a->ldh < H || a->ldh % 8)
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: H, V and ldh must be multiples of 8 (ldh >= H)");
+    if (n > (1 << 30) || V > (1 << 30) || H > (1 << 20))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: sizes beyond the kernels' 32-bit tile indexing");
+    if (!a->W || !a->Wt || !a->dW || !al16(a->W) || !al16(a->Wt))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: W, Wt and dW are required (W, Wt 16-byte aligned)");
+    if (!a->chunk_stats || (a->n_rows > 0 && (!a->row_stats || !a->row_off)))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: NULL stats pointer");
+    if (n > 0 && (!a->h || !al16(a->h) || !a->target || !a->mask || !a->old_logp || !a->tok_row || !a->adv_row ||
+                  !a->dh || !a->logp || !a->entropy || !a->loss_tok || !a->tok_flags))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: NULL or misaligned pointer");
+    if (!(a->eps_low >= 0.0f && a->eps_low <= 1.0f && a->eps_high >= 0.0f && std::isfinite(a->eps_high)) ||
+        !std::isfinite(a->scale))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: bad clip band or scale");
+    const size_t need = grpo_lmhead_workspace_size(n, H, V);
+    if (!a->workspace || a->workspace_bytes < need || !al16(a->workspace))
+        return fail(GRPO_ECAPACITY, "grpo_lmhead_fwd_bwd: workspace of %zu bytes needed (16-byte aligned)", need);
+    hipStream_t st = (hipStream_t)stream;
+    if (n == 0) return grpo::launch_stats(stream, a->loss_tok, a->entropy, a->tok_flags, a->row_off, a->n_rows, 0,
+                                          a->row_stats, a->chunk_stats);
+    const Workspace w = carve(a->workspace, n, H, V);
+    const int64_t n_pad = round_up(n, 8);
+    const int n_parts = (int)((V + 63) / 64);
+    const uint16_t* h = (const uint16_t*)a->h;
+    const uint16_t* W = (const uint16_t*)a->W;
+    const uint16_t* Wt = (const uint16_t*)a->Wt;
+    hipError_t e;
+
+    // h^T with zero columns up to n_pad (the K operand of dW's GEMM)
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((H + 63) / 64), (unsigned)((n_pad + 63) / 64)),
+                       dim3(256), 0, st, h, n, H, a->ldh, w.hT, n_pad, n_pad);
+    if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "transpose h");
+
+    // pass 1: slice partials of the log-softmax and the target logit
+    GemmArgs g{};
+    g.A = h; g.lda = a->ldh; g.B = W; g.ldb = H;
+    g.M = (int)n; g.N = (int)V; g.K = (int)H;
+    g.part = w.part; g.n_parts = n_parts; g.target = a->target; g.zy = w.zy;
+    if ((e = launch_gemm<EPI_STATS>(g, st)) != hipSuccess) return dev_fail(e, "pass 1");
+
+    MergeArgs mg{};
+    mg.part = w.part; mg.n_parts = n_parts; mg.zy = w.zy; mg.n_tok = n; mg.V = V;
+    mg.target = a->target; mg.mask = a->mask; mg.old_logp = a->old_logp; mg.tok_row = a->tok_row;
+    mg.adv_row = a->adv_row; mg.n_rows = a->n_rows; mg.eps_low = a->eps_low; mg.eps_high = a->eps_high;
+    mg.scale = a->scale; mg.denom = a->denom; mg.c2 = w.c2; mg.coef = w.coef; mg.logp = a->logp; mg.lse = a->lse;
+    mg.entropy = a->entropy; mg.loss_tok = a->loss_tok; mg.tok_flags = a->tok_flags;
+    hipLaunchKernelGGL(lm_merge_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, mg);
+    if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "merge");
+    const int rc = grpo::launch_stats(stream, a->loss_tok, a->entropy, a->tok_flags, a->row_off, a->n_rows, n,
+                                      a->row_stats, a->chunk_stats);
+    if (rc != GRPO_OK) return rc;
+
+    // pass 2: per vocabulary chunk, dz then dh (+)= dz W_c and dW_c += dz^T h
+    for (int64_t c0 = 0; c0 < V; c0 += kVocabChunk) {
+        const int vc = (int)(V - c0 < kVocabChunk ? V - c0 : kVocabChunk);
+        GemmArgs d{};
+        d.A = h; d.lda = a->ldh; d.B = W + c0 * H; d.ldb = H;
+        d.M = (int)n; d.N = vc; d.K = (int)H;
+        d.c2 = w.c2; d.coef = w.coef; d.target = a->target; d.col0 = (int)c0; d.m_out = (int)n_pad;
+        d.dz = w.dz; d.ld_dz = vc; d.dzT = w.dzT; d.ld_dzT = n_pad;
+        if ((e = launch_gemm<EPI_DZ>(d, st)) != hipSuccess) return dev_fail(e, "dz");
+
+        GemmArgs gh{};
+        gh.A = w.dz; gh.lda = vc; gh.B = Wt + c0; gh.ldb = V;
+        gh.M = (int)n; gh.N = (int)H; gh.K = vc;
+        gh.C = a->dh; gh.ldc = H; gh.beta = c0 > 0;
+        if ((e = launch_gemm<EPI_ACC>(gh, st)) != hipSuccess) return dev_fail(e, "dh");
+
+        GemmArgs gw{};
+        gw.A = w.dzT; gw.lda = n_pad; gw.B = w.hT; gw.ldb = n_pad;
+        gw.M = vc; gw.N = (int)H; gw.K = (int)n_pad;
+        gw.C = a->dW + c0 * H; gw.ldc = H; gw.beta = 1;
+        if ((e = launch_gemm<EPI_ACC>(gw, st)) != hipSuccess) return dev_fail(e, "dW");
+    }
+    return ok();
+}

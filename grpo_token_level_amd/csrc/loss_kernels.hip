@@ -36,14 +36,15 @@
 #include <cstdint>
 
 #include "common.h"
+#include "surrogate.h"
 
 using grpo::fail;
 using grpo::ok;
 
 namespace {
 
-constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kLn2 = 0.69314718055994530942f;
+using grpo_dev::kLn2;
+using grpo_dev::kLog2e;
 constexpr float kNegClampLog2 = -128.0f;   // below this 2^t is under every fp32 normal
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -235,25 +236,15 @@ __device__ __forceinline__ TokenResult token_tail(const TokParams& p, int64_t t,
     } else {
         const int32_t row = p.tok_row[t];
         const float A = ((uint32_t)row < (uint64_t)p.n_rows) ? p.adv_row[row] : __builtin_nanf("");
-        const float rho = expf(logp - p.old_logp[t]);
-        const float lo = 1.0f - p.eps_low, hi = 1.0f + p.eps_high;
-        const float s1 = rho * A;
-        const float s2 = fminf(fmaxf(rho, lo), hi) * A;
-        const float l = -fminf(s1, s2);
-        const bool clipped = (A > 0.0f && rho > hi) || (A < 0.0f && rho < lo);
-        float sc = p.scale;
-        if (p.denom) {
-            const int64_t n = *p.denom;
-            sc = (float)((double)p.scale / (double)(n > 1 ? n : 1));
-        }
-        const float coef = clipped ? 0.0f : sc * A * rho;
-        const bool bad = !(isfinite(logp) && isfinite(l) && isfinite(H));
+        const grpo_dev::Surrogate sg = grpo_dev::surrogate(logp, H, p.old_logp[t], A, p.eps_low, p.eps_high,
+                                                           grpo_dev::step_scale(p.scale, p.denom));
+        const float coef = sg.coef;
         if (write) {
             p.logp[t] = logp;
             if (p.lse) p.lse[t] = lse;
             p.entropy[t] = H;
-            p.loss_tok[t] = l;
-            p.tok_flags[t] = (uint8_t)(1u | (clipped ? 2u : 0u) | (bad ? 4u : 0u));
+            p.loss_tok[t] = sg.loss;
+            p.tok_flags[t] = (uint8_t)(1u | (sg.clipped ? 2u : 0u) | (sg.bad ? 4u : 0u));
         }
         r.coef = coef;
         return r;
@@ -702,6 +693,21 @@ int check_launch(hipError_t e, const char* what) {
 
 }  // namespace
 
+// Row stats then chunk stats for a chunk whose per-token outputs are written.
+int grpo::launch_stats(void* stream, const float* loss_tok, const float* entropy, const uint8_t* flags,
+                       const int64_t* row_off, int64_t n_rows, int64_t n_tok, grpo_stats* row_stats,
+                       grpo_stats* chunk_stats) {
+    hipStream_t st = (hipStream_t)stream;
+    if (n_rows > 0) {
+        hipLaunchKernelGGL(row_stats_kernel, dim3((unsigned)n_rows), dim3(256), 0, st, loss_tok, entropy, flags,
+                           row_off, n_rows, n_tok, row_stats);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return check_launch(e, "row stats");
+    }
+    hipLaunchKernelGGL(chunk_stats_kernel, dim3(1), dim3(256), 0, st, row_stats, n_rows, chunk_stats);
+    return check_launch(hipGetLastError(), "chunk stats");
+}
+
 // ---------------------------------------------------------------- C ABI
 
 extern "C" int grpo_count_valid(void* stream, const uint8_t* mask, int64_t n_tok, int64_t* n_valid) {
@@ -783,12 +789,6 @@ extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
     else if (dout == GRPO_BF16) e = launch_tok<GRPO_F32, GRPO_BF16, true>(p, vec_ok, st);
     else e = launch_tok<GRPO_F32, GRPO_F32, true>(p, vec_ok, st);
     if (e != hipSuccess) return check_launch(e, "grpo_loss_fwd_bwd (token kernel)");
-    if (a->n_rows > 0) {
-        hipLaunchKernelGGL(row_stats_kernel, dim3((unsigned)a->n_rows), dim3(256), 0, st, a->loss_tok,
-                           a->entropy, a->tok_flags, a->row_off, a->n_rows, a->n_tok, a->row_stats);
-        e = hipGetLastError();
-        if (e != hipSuccess) return check_launch(e, "grpo_loss_fwd_bwd (row stats)");
-    }
-    hipLaunchKernelGGL(chunk_stats_kernel, dim3(1), dim3(256), 0, st, a->row_stats, a->n_rows, a->chunk_stats);
-    return check_launch(hipGetLastError(), "grpo_loss_fwd_bwd (chunk stats)");
+    return grpo::launch_stats(stream, a->loss_tok, a->entropy, a->tok_flags, a->row_off, a->n_rows, a->n_tok,
+                              a->row_stats, a->chunk_stats);
 }

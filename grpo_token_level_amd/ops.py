@@ -268,3 +268,68 @@ def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, 
     C.check(C.lib().grpo_loss_fwd_bwd(_stream(), ctypes.byref(a)))
     ws["dlogits"] = dl
     return ws
+
+
+def transpose_bf16(x, out=None):
+    """bf16 [rows x cols] -> its transpose [cols x rows] (grpo_transpose_bf16)."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16:
+        raise ValueError("transpose_bf16 takes a bf16 matrix")
+    ld = _rows2d(x, "x")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((cols, rows), dtype=torch.bfloat16, device=x.device)
+    C.check(C.lib().grpo_transpose_bf16(_stream(), _dev(x, "x"), rows, cols, ld, _dev(out, "out"), _rows2d(out, "out")))
+    return out
+
+
+def lmhead_workspace_bytes(n_tok, H, V):
+    return int(C.lib().grpo_lmhead_workspace_size(n_tok, H, V))
+
+
+def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off, dW, *, scale=1.0, denom=None,
+                   eps_low=0.2, eps_high=0.2, dh=None, ws=None, workspace=None):
+    """Fused LM-head GRPO loss over one chunk (grpo_lmhead_fwd_bwd).
+
+    ``dW`` (fp32 [V x H]) is accumulated into; ``dh`` (fp32 [n_tok x H]) is
+    written.  Returns the per-token workspace dict with ``dh`` added."""
+    torch = _torch()
+    n, H = h.shape
+    V = W.shape[0]
+    n_rows = row_off.numel() - 1
+    if ws is None:
+        ws = loss_workspace(n, n_rows, h.device)
+    if dh is None:
+        dh = torch.empty((n, H), dtype=torch.float32, device=h.device)
+    if workspace is None:
+        workspace = torch.empty(max(lmhead_workspace_bytes(n, H, V), 1), dtype=torch.uint8, device=h.device)
+    for name, t in (("h", h), ("W", W), ("Wt", Wt), ("target", target), ("mask", mask), ("old_logp", old_logp),
+                    ("tok_row", tok_row_), ("adv_row", adv_row), ("row_off", row_off), ("dW", dW), ("dh", dh)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (libgrpo has no CPU path)")
+    a = C.LmheadArgs()
+    a.struct_size = ctypes.sizeof(C.LmheadArgs)
+    a.h = h.data_ptr() if n else None
+    a.ldh = _rows2d(h, "h")
+    a.W, a.Wt = W.data_ptr(), Wt.data_ptr()
+    a.n_tok, a.H, a.V = n, H, V
+    a.target = target.data_ptr() if n else None
+    a.mask = mask.data_ptr() if n else None
+    a.old_logp = old_logp.data_ptr() if n else None
+    a.tok_row = tok_row_.data_ptr() if n else None
+    a.adv_row = adv_row.data_ptr() if n_rows else None
+    a.row_off = row_off.data_ptr()
+    a.n_rows = n_rows
+    a.eps_low, a.eps_high, a.scale = eps_low, eps_high, scale
+    a.denom = denom.data_ptr() if denom is not None else None
+    a.dh = dh.data_ptr() if n else None
+    a.dW = dW.data_ptr()
+    for k in ("logp", "lse", "entropy", "loss_tok", "tok_flags", "row_stats", "chunk_stats"):
+        t = ws[k]
+        setattr(a, k, t.data_ptr() if t is not None else None)
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel()
+    C.check(C.lib().grpo_lmhead_fwd_bwd(_stream(), ctypes.byref(a)))
+    ws["dh"] = dh
+    ws["workspace"] = workspace
+    return ws

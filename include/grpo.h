@@ -221,6 +221,65 @@ typedef struct grpo_loss_args {
  * where the row sits in the chunk. */
 int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* args);
 
+/* ========================================================= LM-head variant */
+
+/* device.  dst[c * ld_dst + r] = src[r * ld_src + c] for a bf16 matrix of
+ * rows x cols (the transpose).  Used once per step to give the LM-head path W^T. */
+int grpo_transpose_bf16(void* stream, const void* src, int64_t rows, int64_t cols, int64_t ld_src,
+                        void* dst, int64_t ld_dst);
+
+/* Arguments of grpo_lmhead_fwd_bwd (all pointers are device pointers). */
+typedef struct grpo_lmhead_args {
+    int32_t struct_size;        /* = sizeof(grpo_lmhead_args) */
+    int32_t reserved0;          /* 0 */
+    const void* h;              /* bf16 [n_tok x H] hidden states, row stride ldh (16-byte aligned) */
+    int64_t ldh;                /* >= H, multiple of 8 */
+    const void* W;              /* bf16 [V x H] LM-head weight, rows contiguous (16-byte aligned) */
+    const void* Wt;             /* bf16 [H x V]: W transposed (grpo_transpose_bf16) */
+    int64_t n_tok, H, V;        /* H and V multiples of 8 */
+    const int32_t* target;      /* [n_tok] */
+    const uint8_t* mask;        /* [n_tok] 1 = policy token; pads and observations 0 */
+    const float* old_logp;      /* [n_tok] */
+    const int32_t* tok_row;     /* [n_tok] row of each token within the chunk */
+    const float* adv_row;       /* [n_rows] advantage per row (0 for pads) */
+    const int64_t* row_off;     /* [n_rows + 1] token offsets of the rows */
+    int64_t n_rows;
+    float eps_low, eps_high;    /* clip band */
+    float scale;                /* gradient factor (see grpo_loss_args) */
+    int32_t reserved1;          /* 0 */
+    const int64_t* denom;       /* NULL or device int64 N: factor further divided by max(N, 1) */
+    float* dh;                  /* fp32 [n_tok x H]: dL/dh, overwritten */
+    float* dW;                  /* fp32 [V x H]: dL/dW of this chunk is ADDED (accumulate over chunks) */
+    float* logp;                /* [n_tok] required */
+    float* lse;                 /* [n_tok] or NULL */
+    float* entropy;             /* [n_tok] required */
+    float* loss_tok;            /* [n_tok] required */
+    uint8_t* tok_flags;         /* [n_tok] required: bit0 valid, bit1 clipped, bit2 non-finite */
+    grpo_stats* row_stats;      /* [n_rows] required */
+    grpo_stats* chunk_stats;    /* [1] required */
+    void* workspace;            /* >= grpo_lmhead_workspace_size(n_tok, H, V) bytes, 16-byte aligned */
+    size_t workspace_bytes;
+} grpo_lmhead_args;
+
+/* host.  Workspace bytes grpo_lmhead_fwd_bwd needs for a chunk of n_tok tokens:
+ * per-token slice partials of the log-softmax (16 B per token per 64 vocabulary
+ * columns), h^T, and one vocabulary chunk of dz in two layouts (bf16).  It
+ * grows with n_tok * V / 4 and n_tok * 16384, never with n_tok * V * 2. */
+size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V);
+
+/* device.  The fused loss of grpo_loss_fwd_bwd with the logits produced by the
+ * LM head, z = h W^T, and the gradient pushed through it:
+ *   per valid token the same logp / entropy / surrogate / coef as
+ *   grpo_loss_fwd_bwd, dz = coef * (softmax(z) - onehot(y)),
+ *   dh = dz W (overwritten), dW += dz^T h (accumulated across chunks: [P1] "The
+ *   hard part: deferred normalization" -- chunk gradients add up to the step's).
+ * z and dz are formed tile by tile in registers by bf16 MFMA GEMMs (fp32
+ * accumulation) and never stored for the whole vocabulary; dz feeds the two
+ * gradient GEMMs in bf16, one vocabulary chunk at a time.  Masked tokens
+ * (pads, [P4] figure) get zero outputs and contribute nothing.  Row and chunk
+ * stats as in grpo_loss_fwd_bwd.  ECAPACITY if the workspace is too small. */
+int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* args);
+
 /* ============================================================ accumulator */
 
 /* One optimizer-step window of n_micro chunks, caller-allocated, plain data.

@@ -53,8 +53,10 @@ int main(void) {
   printf("grpo_loss_args %zu\n", sizeof(grpo_loss_args));
   printf("grpo_accum %zu\n", sizeof(grpo_accum));
   printf("grpo_step_result %zu\n", sizeof(grpo_step_result));
+  printf("grpo_lmhead_args %zu\n", sizeof(grpo_lmhead_args));
   F(grpo_loss_args, logits) F(grpo_loss_args, n_rows) F(grpo_loss_args, eps_low) F(grpo_loss_args, denom)
   F(grpo_loss_args, dlogits) F(grpo_loss_args, chunk_stats) F(grpo_accum, open) F(grpo_accum, closed)
+  F(grpo_lmhead_args, Wt) F(grpo_lmhead_args, n_rows) F(grpo_lmhead_args, denom) F(grpo_lmhead_args, workspace_bytes)
   return 0;
 }
 ''')
@@ -65,10 +67,11 @@ int main(void) {
     assert int(got["grpo_loss_args"]) == ctypes.sizeof(C.LossArgs)
     assert int(got["grpo_accum"]) == ctypes.sizeof(C.Accum)
     assert int(got["grpo_step_result"]) == ctypes.sizeof(C.StepResult)
+    assert int(got["grpo_lmhead_args"]) == ctypes.sizeof(C.LmheadArgs)
     for key, v in got.items():
         if "." in key:
             struct, field = key.split(".")
-            cls = {"grpo_loss_args": C.LossArgs, "grpo_accum": C.Accum}[struct]
+            cls = {"grpo_loss_args": C.LossArgs, "grpo_accum": C.Accum, "grpo_lmhead_args": C.LmheadArgs}[struct]
             assert getattr(cls, field).offset == int(v), key
 
 

@@ -1,18 +1,24 @@
 """Throughput of one token-level GRPO loss step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload qwen|long|tiny] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload qwen|long|tiny|dynamic|compact] [--gpus 1]
 
-A step is one pass of the hot path over one collected batch whose logits are
-already resident in HBM: the fixed mini/micro plan and the group advantages
-(host, libgrpo), the step's valid-token count N (device), then for every
-micro-batch chunk the fused log-softmax + clipped-surrogate forward/backward
-that reads the chunk's logits once and writes dlogits once (device), and the
-token-weighted roll-up of the chunk statistics (host accumulator).
+A step is one pass of the hot path over one collected batch whose inputs are
+already resident in HBM:
 
-Prints one JSON line: valid tokens/s, the dominant kernel's achieved HBM
-bandwidth against the 8 TB/s peak (algorithmic bytes over its launch time,
-timed with HIP events on the stream it runs on), and the CPU oracle's
-throughput on a bounded sample of the same workload.
+* padded workloads (qwen = default, long, tiny): the fixed mini/micro plan and
+  the group advantages (host, libgrpo), N per mini-batch (device), then per
+  micro-batch chunk the fused log-softmax + clipped-surrogate forward/backward
+  that reads the chunk's logits once and writes dlogits once (device), and the
+  token-weighted roll-up of the chunk statistics (host accumulator);
+* dynamic: the same with the token-budget packing plan (host) and its boxes;
+* compact: the context-compaction plan, advantages copied to segment rows,
+  W^T, then per 4-row chunk the fused LM-head loss (bf16 MFMA GEMMs) with dW
+  accumulated over the chunks.
+
+Prints one JSON line: valid tokens/s, the dominant kernel's achieved
+bandwidth (or MFMA rate) against the chip's published peak, measured with HIP
+events on the stream the kernels run on, and the CPU oracle's throughput on
+a bounded sample of the same workload.
 """
 
 import argparse
@@ -28,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "valid tokens/s, fused log-softmax+GRPO loss fwd/bwd; % of HBM peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 PER_TOKEN_SCALAR_READ = 4 + 4 + 4      # target, old log-prob, row index (valid tokens)
 PER_TOKEN_SCALAR_ALL = 1 + 4 * 4 + 1   # mask read; logp, lse, entropy, loss written; flags written
 
@@ -38,6 +45,11 @@ WORKLOAD_TEXT = {
             "mini 64 rows (2 optimizer steps), micro 4 rows -> 32 chunks",
     "tiny": "32 rows (8 prompts x group 4), lengths U{8..64} padded to 64, vocab 1024, fp32 logits ~N(0,2), "
             "~20% masked in spans, mini 16 / micro 8 -> 2x2 chunks",
+    "dynamic": "256 rows, lengths round(LogNormal(ln 512, 1.0)) clipped to [64, 8192], all valid, packed, "
+               "vocab 151936 bf16 ~N(0,3), token budget 16384 per micro-batch, proxy L + L^2/4096",
+    "compact": "8 prompts x group 4 rollouts, U{1..5} segment rows of U{256..1024} tokens, groups padded to a "
+               "multiple of Q=4 with masked copies, micro 4 rows, hidden 2048 bf16 ~N(0,1), "
+               "LM head [151936 x 2048] bf16 ~N(0,0.02)",
 }
 
 
@@ -55,124 +67,337 @@ def parse():
     return ap.parse_args()
 
 
-def build_batch(wl, seed, torch, ops):
-    """Resident synthetic batch for workload ``wl`` (logits generated on the GPU)."""
-    from synth import fill_normal_rows, padded_batch
-    b = padded_batch(wl, seed=seed)
-    n_rows, T, V = b["n_rows"], b["T"], b["V"]
-    dt = torch.bfloat16 if b["dtype"] == "bf16" else torch.float32
-    dev = "cuda"
-    n_tok = n_rows * T
-    logits = torch.empty((n_tok, V), dtype=dt, device=dev)
-    fill_normal_rows(logits, range(n_rows), [r * T for r in range(n_rows)], [T] * n_rows, b["logit_std"], seed, wl)
-    G = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
-    target, mask = G(b["target"]), G(b["mask"])
-    # pi_old: the ahead pass over the collected batch, then the log-ratio
-    # perturbation that stands in for the policy having moved since rollout
-    logp, _, _ = ops.logprob_fwd(logits, target, mask, want_lse=False, want_entropy=False)
-    old = (logp.double() + G(b["logratio_noise"])).float()
-    del logp
-    dlogits = torch.empty_like(logits)
-    return dict(b=b, logits=logits, target=target, mask=mask, old=old, dlogits=dlogits, dtype=dt)
+def _g(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
 
 
-class Step:
-    """One loss step over the resident batch; the same work every call."""
+class Timed:
+    """HIP-event brackets around the dominant launches of the timed steps."""
 
-    def __init__(self, data, torch, ops):
-        self.torch, self.ops, self.d = torch, ops, data
-        b = data["b"]
-        self.n_rows, self.T, self.V = b["n_rows"], b["T"], b["V"]
-        self.reward = b["reward"]
-        dev = "cuda"
-        n_mini, n_micro, mini_rows, micro_rows = ops.plan_fixed(self.n_rows, b["group"], b["mini"], b["micro"])
-        self.micro_rows = micro_rows
-        self.row_off = torch.arange(0, micro_rows * self.T + 1, self.T, dtype=torch.int64, device=dev)
-        self.tok_row = ops.tok_row(self.row_off, micro_rows * self.T)
-        self.ws = ops.loss_workspace(micro_rows * self.T, micro_rows, dev)
-        self.N = torch.empty(max(n_mini, 1), dtype=torch.int64, device=dev)
-        self.adv_host = torch.empty(self.n_rows, dtype=torch.float32).pin_memory()
-        self.adv_dev = torch.empty(self.n_rows, dtype=torch.float32, device=dev)
-        self.stats_dev = torch.empty((n_mini * n_micro, ops.STATS_BYTES), dtype=torch.uint8, device=dev)
+    def __init__(self, torch):
+        self.torch = torch
+        self.rec = []
+        self.on = False
+
+    def begin(self):
+        if not self.on:
+            return None
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def end(self, e0, units):
+        if e0 is None:
+            return
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.rec.append((e0, e1, units))
+
+    def totals(self):
+        ms = sum(a.elapsed_time(b) for a, b, _ in self.rec)
+        units = sum(u for _, _, u in self.rec)
+        return ms, units, len(self.rec)
+
+
+# ---------------------------------------------------------------- padded / dynamic: fused loss
+
+def chunk_bytes(mask_np, V, b_in, b_out):
+    """Algorithmic bytes of one fused launch: valid tokens read V*b_in and write
+    V*b_out, masked tokens write V*b_out (zeros), plus the per-token scalars."""
+    nv = int(mask_np.sum())
+    nm = len(mask_np) - nv
+    return nv * (V * (b_in + b_out) + PER_TOKEN_SCALAR_READ) + nm * V * b_out + len(mask_np) * PER_TOKEN_SCALAR_ALL
+
+
+class PaddedStep:
+    """Fixed-plan step over a right-padded batch."""
+
+    def __init__(self, wl, seed, torch, ops, timed):
+        from synth import fill_normal_rows, padded_batch
+        self.torch, self.ops, self.timed = torch, ops, timed
+        b = self.b = padded_batch(wl, seed=seed)
+        n_rows, T, V = b["n_rows"], b["T"], b["V"]
+        self.dt = torch.bfloat16 if b["dtype"] == "bf16" else torch.float32
+        n_tok = n_rows * T
+        self.logits = torch.empty((n_tok, V), dtype=self.dt, device="cuda")
+        fill_normal_rows(self.logits, range(n_rows), [r * T for r in range(n_rows)], [T] * n_rows, b["logit_std"],
+                         seed, wl)
+        self.target, self.mask = _g(torch, b["target"]), _g(torch, b["mask"])
+        # pi_old: the ahead pass over the collected batch, then the log-ratio
+        # perturbation that stands in for the policy having moved since rollout
+        logp, _, _ = ops.logprob_fwd(self.logits, self.target, self.mask, want_lse=False, want_entropy=False)
+        self.old = (logp.double() + _g(torch, b["logratio_noise"])).float()
+        del logp
+        self.dlogits = torch.empty_like(self.logits)
+        n_mini, n_micro, mini_rows, micro_rows = ops.plan_fixed(n_rows, b["group"], b["mini"], b["micro"])
+        self.row_off = torch.arange(0, micro_rows * T + 1, T, dtype=torch.int64, device="cuda")
+        self.tok_row = ops.tok_row(self.row_off, micro_rows * T)
+        self.ws = ops.loss_workspace(micro_rows * T, micro_rows, "cuda")
+        self.N = torch.empty(n_mini, dtype=torch.int64, device="cuda")
+        self.adv_host = torch.empty(n_rows, dtype=torch.float32).pin_memory()
+        self.adv_dev = torch.empty(n_rows, dtype=torch.float32, device="cuda")
+        self.stats_dev = torch.empty((n_mini * n_micro, ops.STATS_BYTES), dtype=torch.uint8, device="cuda")
         self.stats_host = torch.empty((n_mini * n_micro, ops.STATS_BYTES), dtype=torch.uint8).pin_memory()
-        self.events = []
+        b_in = 2 if self.dt == torch.bfloat16 else 4
+        self.chunk_units = {}
+        for i in range(n_mini):
+            for j in range(n_micro):
+                a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
+                self.chunk_units[(i, j)] = chunk_bytes(b["mask"][a * T:e * T], V, b_in, b_in)
+        self.n_valid = int(np.sum(b["mask"]))
+        self.logits_dtype = "bf16" if b_in == 2 else "fp32"
 
-    def __call__(self, record=False):
-        torch, ops, d = self.torch, self.ops, self.d
-        b = d["b"]
-        T = self.T
-        plan = ops.plan_fixed(self.n_rows, b["group"], b["mini"], b["micro"])
-        n_mini, n_micro, mini_rows, micro_rows = plan
-        adv = ops.group_advantage(self.reward, b["group"])            # one rollout per row here
-        self.adv_host.numpy()[:] = adv
+    def __call__(self):
+        torch, ops, b, T = self.torch, self.ops, self.b, self.b["T"]
+        n_rows = b["n_rows"]
+        n_mini, n_micro, mini_rows, micro_rows = ops.plan_fixed(n_rows, b["group"], b["mini"], b["micro"])
+        self.adv_host.numpy()[:] = ops.group_advantage(b["reward"], b["group"])    # one rollout per row
         self.adv_dev.copy_(self.adv_host, non_blocking=True)
-        results = []
         k = 0
         for i in range(n_mini):
-            r0 = i * mini_rows
-            ops.count_valid(d["mask"][r0 * T:(r0 + mini_rows) * T], out=self.N[i:i + 1])
+            ops.count_valid(self.mask[i * mini_rows * T:(i + 1) * mini_rows * T], out=self.N[i:i + 1])
             for j in range(n_micro):
-                a, e = ops.plan_chunk(self.n_rows, mini_rows, micro_rows, i, j)
+                a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
                 t0, t1 = a * T, e * T
-                if record:
-                    ev0 = torch.cuda.Event(enable_timing=True)
-                    ev1 = torch.cuda.Event(enable_timing=True)
-                    ev0.record()
                 self.ws["chunk_stats"] = self.stats_dev[k:k + 1]
-                ops.loss_fwd_bwd(d["logits"][t0:t1], d["target"][t0:t1], d["mask"][t0:t1], d["old"][t0:t1],
-                                 self.tok_row, self.adv_dev[a:e], self.row_off, scale=1.0,
-                                 denom=self.N[i:i + 1], dlogits=d["dlogits"][t0:t1], ws=self.ws)
-                if record:
-                    ev1.record()
-                    self.events.append((ev0, ev1, t0, t1))
+                ev = self.timed.begin()
+                ops.loss_fwd_bwd(self.logits[t0:t1], self.target[t0:t1], self.mask[t0:t1], self.old[t0:t1],
+                                 self.tok_row, self.adv_dev[a:e], self.row_off, scale=1.0, denom=self.N[i:i + 1],
+                                 dlogits=self.dlogits[t0:t1], ws=self.ws)
+                self.timed.end(ev, self.chunk_units[(i, j)])
                 k += 1
         self.stats_host.copy_(self.stats_dev, non_blocking=True)
         torch.cuda.current_stream().synchronize()
         stats = ops.stats_to_dicts(self.stats_host.numpy())
-        k = 0
+        out = []
         for i in range(n_mini):
             acc = ops.Accumulator(n_micro)
             for j in range(n_micro):
-                acc.add(stats[k])
-                k += 1
-            results.append(acc.finalize())
-        return results
+                acc.add(stats[i * n_micro + j])
+            out.append(acc.finalize())
+        return out
+
+    def copy_context(self):
+        """Plain device copy of one chunk's bytes, timed like the kernel."""
+        torch = self.torch
+        n = self.ws["logp"].numel()
+        src, dst = self.logits[:n], self.dlogits[:n]
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dst.copy_(src)
+        c0.record()
+        for _ in range(3):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        return 3 * 2 * src.numel() * src.element_size() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+    def sample(self, n):
+        """(z float64 [n, V], target, drift, advantage) of the first n valid tokens."""
+        torch, b = self.torch, self.b
+        idx = np.nonzero(b["mask"])[0][:n]
+        z = self.logits[torch.as_tensor(idx, device="cuda")].double().cpu().numpy()
+        adv = np.random.default_rng(1).normal(0, 1, b["n_rows"])[idx // b["T"]]
+        return z, b["target"][idx], b["logratio_noise"][idx], adv
 
 
-def algorithmic_bytes(mask_np, t0, t1, V, b_in, b_out):
-    m = mask_np[t0:t1]
-    nv = int(m.sum())
-    nm = (t1 - t0) - nv
-    return nv * (V * (b_in + b_out) + PER_TOKEN_SCALAR_READ) + nm * V * b_out + (t1 - t0) * PER_TOKEN_SCALAR_ALL
+class DynamicStep(PaddedStep):
+    """Token-budget packing: rows laid out box by box, one launch per box."""
+
+    def __init__(self, wl, seed, torch, ops, timed):
+        from synth import dynamic_batch, fill_normal_rows
+        self.torch, self.ops, self.timed = torch, ops, timed
+        b = self.b = dynamic_batch(seed=seed)
+        L = b["lengths"].astype(np.int64)
+        V = b["V"]
+        self.dt = torch.bfloat16
+        plan = ops.plan_dynamic(L, b["budget"], b["proxy_div"])
+        order = plan["order"]
+        offB = ops.row_offsets(L, order)
+        offA = np.concatenate([[0], np.cumsum(L)])
+        perm = np.concatenate([np.arange(offA[r], offA[r + 1]) for r in order])
+        n_tok = int(offA[-1])
+        self.logits = torch.empty((n_tok, V), dtype=self.dt, device="cuda")
+        fill_normal_rows(self.logits, order, offB[:-1], L[order], b["logit_std"], seed, "dynamic")
+        self.target = _g(torch, b["target"][perm])
+        self.mask = _g(torch, b["mask"][perm])
+        logp, _, _ = ops.logprob_fwd(self.logits, self.target, self.mask, want_lse=False, want_entropy=False)
+        self.old = (logp.double() + _g(torch, b["logratio_noise"][perm])).float()
+        del logp
+        self.dlogits = torch.empty_like(self.logits)
+        bin_tok = [int(offB[plan["bin_off"][k + 1]] - offB[plan["bin_off"][k]]) for k in range(plan["n_bins"])]
+        max_rows = int(np.max(np.diff(plan["bin_off"])))
+        self.ws = ops.loss_workspace(max(bin_tok), max_rows, "cuda")
+        self.tok_row = torch.empty(max(bin_tok), dtype=torch.int32, device="cuda")
+        self.N = torch.empty(1, dtype=torch.int64, device="cuda")
+        n_rows = len(L)
+        self.meta_host = torch.empty(n_rows + plan["n_bins"] + 8, dtype=torch.int64).pin_memory()
+        self.meta_dev = torch.empty(n_rows + plan["n_bins"] + 8, dtype=torch.int64, device="cuda")
+        self.adv_host = torch.empty(n_rows, dtype=torch.float32).pin_memory()
+        self.adv_dev = torch.empty(n_rows, dtype=torch.float32, device="cuda")
+        self.stats_dev = torch.empty((plan["n_bins"] + 8, ops.STATS_BYTES), dtype=torch.uint8, device="cuda")
+        self.stats_host = torch.empty((plan["n_bins"] + 8, ops.STATS_BYTES), dtype=torch.uint8).pin_memory()
+        self.mask_np = b["mask"][perm]
+        self.n_valid = int(np.sum(b["mask"]))
+        self.logits_dtype = "bf16"
+
+    def __call__(self):
+        torch, ops, b = self.torch, self.ops, self.b
+        L = b["lengths"].astype(np.int64)
+        n_rows = len(L)
+        plan = ops.plan_dynamic(L, b["budget"], b["proxy_div"])
+        order, bin_off = plan["order"], plan["bin_off"]
+        offB = ops.row_offsets(L, order)
+        # per box: its rows' token offsets relative to the box start
+        local = np.empty(n_rows + plan["n_bins"], np.int64)
+        starts = []
+        p = 0
+        for k in range(plan["n_bins"]):
+            a, e = int(bin_off[k]), int(bin_off[k + 1])
+            starts.append(p)
+            local[p:p + e - a + 1] = offB[a:e + 1] - offB[a]
+            p += e - a + 1
+        self.meta_host.numpy()[:p] = local[:p]
+        self.meta_dev[:p].copy_(self.meta_host[:p], non_blocking=True)
+        adv = ops.group_advantage(b["reward"], b["group"])
+        self.adv_host.numpy()[:] = adv[order]
+        self.adv_dev.copy_(self.adv_host, non_blocking=True)
+        ops.count_valid(self.mask, out=self.N)
+        for k in range(plan["n_bins"]):
+            a, e = int(bin_off[k]), int(bin_off[k + 1])
+            t0, t1 = int(offB[a]), int(offB[e])
+            ro = self.meta_dev[starts[k]:starts[k] + e - a + 1]
+            tr = ops.tok_row(ro, t1 - t0, out=self.tok_row[:t1 - t0])
+            ws = {kk: (v[:t1 - t0] if kk in ("logp", "lse", "entropy", "loss_tok", "tok_flags") else v)
+                  for kk, v in self.ws.items()}
+            ws["row_stats"] = self.ws["row_stats"][:e - a]
+            ws["chunk_stats"] = self.stats_dev[k:k + 1]
+            ev = self.timed.begin()
+            ops.loss_fwd_bwd(self.logits[t0:t1], self.target[t0:t1], self.mask[t0:t1], self.old[t0:t1], tr,
+                             self.adv_dev[a:e], ro, scale=1.0, denom=self.N, dlogits=self.dlogits[t0:t1], ws=ws)
+            self.timed.end(ev, chunk_bytes(self.mask_np[t0:t1], b["V"], 2, 2))
+        nb = plan["n_bins"]
+        self.stats_host[:nb].copy_(self.stats_dev[:nb], non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        acc = ops.Accumulator(nb)
+        for s in ops.stats_to_dicts(self.stats_host[:nb].numpy()):
+            acc.add(s)
+        return [acc.finalize()]
+
+    def sample(self, n):
+        torch = self.torch
+        idx = np.arange(min(n, self.logits.shape[0]))
+        z = self.logits[torch.as_tensor(idx, device="cuda")].double().cpu().numpy()
+        adv = np.random.default_rng(1).normal(0, 1, len(idx))
+        return z, self.target[:len(idx)].cpu().numpy(), np.zeros(len(idx)), adv
 
 
-def cpu_baseline(data, budget_s):
-    """The oracle, as it stands, on the first valid tokens of the batch until
-    ``budget_s`` seconds of compute have run (single process)."""
+# ---------------------------------------------------------------- compaction: fused LM head
+
+class CompactStep:
+    def __init__(self, wl, seed, torch, ops, timed):
+        from synth import compaction_batch
+        self.torch, self.ops, self.timed = torch, ops, timed
+        b = self.b = compaction_batch(seed=seed)
+        plan = ops.plan_compaction(b["rows_per_rollout"], b["n_groups"], b["group"], b["Q"],
+                                   b["n_groups"] * b["group"])
+        H, V = b["H"], b["V"]
+        seg_len = b["seg_len"]
+        seg_off = np.concatenate([[0], np.cumsum(seg_len)])
+        row_len = np.array([seg_len[s] for s in plan["row_src"]], np.int64)
+        self.off = np.concatenate([[0], np.cumsum(row_len)])
+        src_tok = np.concatenate([np.arange(seg_off[s], seg_off[s] + seg_len[s]) for s in plan["row_src"]])
+        n_tok = int(self.off[-1])
+        mask = np.repeat(1 - plan["is_pad"].astype(np.uint8), row_len).astype(np.uint8)
+        gen = torch.Generator(device="cuda").manual_seed(seed + 11)
+        self.W = (torch.randn((V, H), generator=gen, device="cuda") * b["w_std"]).to(torch.bfloat16)
+        h_seg = (torch.randn((int(seg_off[-1]), H), generator=gen, device="cuda") * b["h_std"]).to(torch.bfloat16)
+        self.h = h_seg[torch.as_tensor(src_tok, device="cuda")].contiguous()   # pads copy a real row
+        del h_seg
+        self.target = _g(torch, b["target"][src_tok])
+        self.mask = _g(torch, mask)
+        self.mask_np = mask
+        # pi_old from a plain fp32 recompute, 1024 tokens at a time, plus the drift
+        old = torch.empty(n_tok, dtype=torch.float32, device="cuda")
+        Wf = self.W.float()
+        for a in range(0, n_tok, 1024):
+            e = min(a + 1024, n_tok)
+            z = self.h[a:e].float() @ Wf.t()
+            old[a:e] = torch.log_softmax(z, -1).gather(1, self.target[a:e].long()[:, None])[:, 0]
+            del z
+        del Wf
+        self.old = old + _g(torch, b["logratio_noise"][src_tok]).float()
+        self.Wt = torch.empty((H, V), dtype=torch.bfloat16, device="cuda")
+        self.dW = torch.zeros((V, H), dtype=torch.float32, device="cuda")
+        self.dh = torch.empty((n_tok, H), dtype=torch.float32, device="cuda")
+        self.N = torch.empty(1, dtype=torch.int64, device="cuda")
+        self.chunks = [(a, min(a + b["micro"], plan["n_rows"])) for a in range(0, plan["n_rows"], b["micro"])]
+        max_tok = int(max(self.off[e] - self.off[a] for a, e in self.chunks))
+        self.workspace = torch.empty(ops.lmhead_workspace_bytes(max_tok, H, V), dtype=torch.uint8, device="cuda")
+        self.ws = ops.loss_workspace(max_tok, b["micro"], "cuda")
+        self.tok_row = torch.empty(max_tok, dtype=torch.int32, device="cuda")
+        self.row_off_dev = _g(torch, np.concatenate([self.off[a:e + 1] - self.off[a] for a, e in self.chunks]))
+        self.adv_host = torch.empty(plan["n_rows"], dtype=torch.float32).pin_memory()
+        self.adv_dev = torch.empty(plan["n_rows"], dtype=torch.float32, device="cuda")
+        self.stats_dev = torch.empty((len(self.chunks), ops.STATS_BYTES), dtype=torch.uint8, device="cuda")
+        self.stats_host = torch.empty((len(self.chunks), ops.STATS_BYTES), dtype=torch.uint8).pin_memory()
+        self.n_valid = int(mask.sum())
+        self.H, self.V = H, V
+        self.logits_dtype = "none (h and W bf16; logits never materialised)"
+
+    def __call__(self):
+        torch, ops, b = self.torch, self.ops, self.b
+        plan = ops.plan_compaction(b["rows_per_rollout"], b["n_groups"], b["group"], b["Q"],
+                                   b["n_groups"] * b["group"])
+        adv_roll = ops.group_advantage(b["reward"], b["group"])
+        self.adv_host.numpy()[:] = ops.rows_advantage(adv_roll, plan["row_rollout"])
+        self.adv_dev.copy_(self.adv_host, non_blocking=True)
+        self.dW.zero_()
+        ops.transpose_bf16(self.W, out=self.Wt)
+        ops.count_valid(self.mask, out=self.N)
+        ro_at = 0
+        for k, (a, e) in enumerate(self.chunks):
+            t0, t1 = int(self.off[a]), int(self.off[e])
+            ro = self.row_off_dev[ro_at:ro_at + e - a + 1]
+            ro_at += e - a + 1
+            tr = ops.tok_row(ro, t1 - t0, out=self.tok_row[:t1 - t0])
+            ws = {kk: (v[:t1 - t0] if kk in ("logp", "lse", "entropy", "loss_tok", "tok_flags") else v)
+                  for kk, v in self.ws.items()}
+            ws["row_stats"] = self.ws["row_stats"][:e - a]
+            ws["chunk_stats"] = self.stats_dev[k:k + 1]
+            ev = self.timed.begin()
+            ops.lmhead_fwd_bwd(self.h[t0:t1], self.W, self.Wt, self.target[t0:t1], self.mask[t0:t1],
+                               self.old[t0:t1], tr, self.adv_dev[a:e], ro, self.dW, denom=self.N,
+                               dh=self.dh[t0:t1], ws=ws, workspace=self.workspace)
+            self.timed.end(ev, 6.0 * self.V * self.H * int(self.mask_np[t0:t1].sum()))
+        self.stats_host.copy_(self.stats_dev, non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        acc = ops.Accumulator(len(self.chunks))
+        for s in ops.stats_to_dicts(self.stats_host.numpy()):
+            acc.add(s)
+        return [acc.finalize()]
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(step, budget_s):
+    """The oracle, as it stands, on the first valid tokens of the benched batch
+    until ``budget_s`` seconds of compute have run (one process)."""
     import oracle
-    torch = __import__("torch")
-    b = data["b"]
-    mask = b["mask"]
-    valid = np.nonzero(mask)[0]
-    rng = np.random.default_rng(1)
-    adv_rows = rng.normal(0, 1, b["n_rows"])
-    done, t_used = 0, 0.0
-    block = 16
-    pos = 0
-    while t_used < budget_s and pos < len(valid):
-        idx = valid[pos:pos + block]
-        pos += block
-        z = data["logits"][torch.as_tensor(idx, device="cuda")].double().cpu().numpy()
-        y = b["target"][idx]
-        m = np.ones(len(idx), np.uint8)
-        old = oracle.logprob_fwd(z, y, m)["logp"] + b["logratio_noise"][idx]
-        adv = adv_rows[idx // b["T"]]
+    done, t_used, pos = 0, 0.0, 0
+    z_all, y_all, drift, adv_all = step.sample(4096)
+    V = z_all.shape[1]
+    while t_used < budget_s and pos < len(y_all):
+        sl = slice(pos, pos + 16)
+        pos += 16
+        z, y = z_all[sl], y_all[sl]
+        m = np.ones(len(y), np.uint8)
+        old = oracle.logprob_fwd(z, y, m)["logp"] + drift[sl]
         t0 = time.perf_counter()
-        oracle.loss_fwd_bwd(z, y, m, old, adv, 1.0 / max(1, len(valid)))
+        oracle.loss_fwd_bwd(z, y, m, old, adv_all[sl], 1e-5)
         t_used += time.perf_counter() - t0
-        done += len(idx)
-    return {"value": done / t_used, "unit": "valid tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} valid tokens of the benched batch (V={b['V']}, float64 numpy, one process), "
+        done += len(y)
+    return {"value": round(done / t_used, 1), "unit": "valid tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} valid tokens of the benched batch (V={V}, float64 numpy, one process), "
                       f"{t_used:.1f} s of compute"}
 
 
@@ -189,69 +414,54 @@ def main():
         sys.exit(2)
     ops.version()                      # fails loudly if libgrpo.so is missing
     wl = args.workload
-    data = build_batch(wl, args.seed, torch, ops)
-    step = Step(data, torch, ops)
+    timed = Timed(torch)
+    cls = {"qwen": PaddedStep, "long": PaddedStep, "tiny": PaddedStep, "dynamic": DynamicStep,
+           "compact": CompactStep}[wl]
+    step = cls(wl, args.seed, torch, ops, timed)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    step.events.clear()
+    timed.on = True
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        res = step(record=True)
+        res = step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    b = data["b"]
-    n_valid = int(np.sum(b["mask"]))
     ms = 1e3 * wall / args.steps
-    value = n_valid / (wall / args.steps)
-    # dominant kernel: the fused loss launch per chunk (token kernel + two tiny
-    # stats reductions inside the same event pair)
-    b_in = 2 if data["dtype"] == torch.bfloat16 else 4
-    b_out = b_in
-    tot_bytes, tot_ms = 0, 0.0
-    for ev0, ev1, t0_, t1_ in step.events:
-        tot_ms += ev0.elapsed_time(ev1)
-        tot_bytes += algorithmic_bytes(b["mask"], t0_, t1_, b["V"], b_in, b_out)
-    launches = len(step.events)
-    achieved = (tot_bytes / launches) / (tot_ms / launches * 1e-3) / 1e9
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "valid tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{wl}: {WORKLOAD_TEXT[wl]}", "logits_dtype": "bf16" if b_in == 2 else "fp32",
-                   "rows": b["n_rows"], "T": b["T"], "V": b["V"], "valid_tokens": n_valid,
-                   "chunks_per_step": launches // args.steps, "step_loss": res[0]["loss"] if res[0] else None},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "tok_reg_kernel (fused loss fwd+bwd), per chunk launch",
-                     "algorithmic_bytes_per_launch": tot_bytes // launches,
-                     "avg_launch_ms": round(tot_ms / launches, 4)},
-    }
-    # context: a plain device-to-device copy of one chunk's bytes (read V*2 +
-    # write V*2 per token), timed the same way, after the timed region
-    t0_, t1_ = step.events[0][2], step.events[0][3]
-    src, dst = data["logits"][t0_:t1_], data["dlogits"][t0_:t1_]
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    dst.copy_(src)
-    c0.record()
-    for _ in range(3):
-        dst.copy_(src)
-    c1.record()
-    torch.cuda.synchronize()
-    out["roofline"]["device_copy_GBs"] = round(3 * 2 * src.numel() * src.element_size() / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)
-    if wl == "qwen":
-        from grpo_token_level_amd.prof_summary import load_traffic
-        rec = load_traffic(os.path.join(ROOT, "profiles", "fused_loss_qwen_pmc.txt"))
-        if rec is not None:
-            out["roofline"]["traffic"] = rec["traffic_bytes_per_launch"]
+    value = step.n_valid / (wall / args.steps)
+    tot_ms, units, launches = timed.totals()
+    cfg = {"workload": f"{wl}: {WORKLOAD_TEXT[wl]}", "logits_dtype": step.logits_dtype,
+           "valid_tokens": step.n_valid, "launches_per_step": launches // args.steps,
+           "step_loss": res[0]["loss"] if res and res[0] else None}
+    if wl == "compact":
+        achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "grpo_lmhead_fwd_bwd per 4-row chunk (bf16 MFMA GEMMs + epilogues)",
+                "algorithmic_flops_per_launch": int(units // launches), "avg_launch_ms": round(tot_ms / launches, 4)}
+    else:
+        achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "tok_reg_kernel (fused loss fwd+bwd) + row/chunk stats, per chunk launch",
+                "algorithmic_bytes_per_launch": int(units // launches), "avg_launch_ms": round(tot_ms / launches, 4)}
+        roof["device_copy_GBs"] = round(step.copy_context(), 1)
+        if wl == "qwen":
+            from grpo_token_level_amd.prof_summary import load_traffic
+            rec = load_traffic(os.path.join(ROOT, "profiles", "fused_loss_qwen_pmc.txt"))
+            if rec is not None:
+                roof["traffic"] = rec["traffic_bytes_per_launch"]
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "valid tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg, "roofline": roof}
     if args.copy_calibration:
         # known-size plain copy for the byte counters: 1 GiB read, 1 GiB written
         x = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
         y = torch.empty_like(x)
         torch.bitwise_not(x, out=y)
         torch.cuda.synchronize()
-    if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(data, args.cpu_seconds)
+    if args.cpu_seconds > 0 and hasattr(step, "sample"):
+        out["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

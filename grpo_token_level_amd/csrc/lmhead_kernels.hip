@@ -14,20 +14,26 @@
 //           picks out the target logit.  A merge kernel combines the slices
 //           (fixed order) into logsumexp, entropy, log-prob, the surrogate and
 //           the gradient coefficient.
-//   pass 2  per vocabulary chunk of Vc columns: the GEMM recomputes z and its
-//           epilogue writes dz = coef*(softmax - onehot) in bf16 (row-major and
-//           transposed) into a bounded workspace; then dh (+)= dz W_c and
-//           dW_c += dz^T h, two more MFMA GEMMs with fp32 accumulation.
+//   pass 2  per vocabulary chunk (equal chunks of at most 65536 columns): the
+//           GEMM recomputes z and its epilogue writes dz = coef*(softmax -
+//           onehot) in bf16 (row-major and transposed) into a bounded
+//           workspace; then dh (+)= dz W_c (split-K, one fp32 partial per
+//           split, summed in order at the end) and dW_c += dz^T h, two more
+//           MFMA GEMMs with fp32 accumulation.
 // All products use one kernel shape, C[m,n] = sum_k A[m,k] B[n,k] with both
 // operands K-contiguous ("NT"): W for pass 1, W^T for dh, h^T and dz^T for dW.
 //
-// MFMA: v_mfma_f32_32x32x16_bf16.  A 256-thread block computes a 128x128 tile
-// (four waves, 64x64 each = 2x2 MFMA tiles), K in steps of 64 staged through
-// LDS with double buffering.  Lane layouts (checked on the device): operand
-// lane l holds row/column l%32 and k = (l/32)*8 .. +8; result lane l, register
-// i holds column l%32 and row (i/4)*8 + (l/32)*4 + i%4.  Blocks are mapped so
-// that each XCD works through a contiguous range of tiles, M fastest: the
-// tiles that share a W slice run together on one L2.
+// MFMA: v_mfma_f32_32x32x16_bf16.  A 512-thread block computes a 256x256 tile
+// (eight waves in 4 x 2, each 64x128 = 2x4 MFMA tiles).  K advances 32 at a
+// time through a four-stage LDS ring (32 KiB per stage) filled by
+// global_load_lds (16 bytes per lane straight into LDS, no register
+// staging), three stages in flight; rows past the edge and k past the end
+// load from a zero page.  Lane layouts (checked on the device): operand lane
+// l holds row/column l%32 and k = (l/32)*8 .. +8; result lane l, register i
+// holds column l%32 and row (i/4)*8 + (l/32)*4 + i%4.  Blocks are mapped so
+// that each XCD works through a contiguous range of tiles, the index with
+// fewer tiles fastest: the tiles that share a slice of the larger operand (W in
+// pass 1, dz^T for dW) run together on one L2.
 
 #include <hip/hip_runtime.h>
 
@@ -49,11 +55,31 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDK = BK + 8;          // LDS row stride in bf16 (144 B): conflict-free 16-byte fragment reads
-constexpr int NTHREADS = 256;
+constexpr int BM = 256, BN = 256;    // block tile
+constexpr int BK = 32;               // k per LDS stage
+constexpr int NST = 4;               // LDS stages (ring)
+constexpr int PREF = 3;              // stages in flight ahead of the one being consumed
+constexpr int NTHREADS = 512;        // eight waves in 4 (M) x 2 (N), each owning a 64 x 128 sub-tile
+constexpr int WM = 64, WN = 128;     // wave tile
+constexpr int FM = WM / 32, FN = WN / 32;
+constexpr int ROWB = BK * 2;         // bytes of one tile row in one stage
+constexpr int OPB = BM * ROWB;       // bytes of one operand in one stage (16 KiB)
+constexpr int STB = 2 * OPB;         // bytes of one stage (32 KiB)
+constexpr int EPI_ROW = WN + 1;      // floats per row of a wave's epilogue buffer (row-wise reads)
+constexpr int EPI_ROW_Q = WN + 4;    // the same for 16-byte column-quad reads
+constexpr int EPIB = 8 * 32 * EPI_ROW_Q * 4;
+constexpr int SMEM = NST * STB > EPIB ? NST * STB : EPIB;
 constexpr int NXCD = 8;
-constexpr int kVocabChunk = 16384;   // pass-2 vocabulary chunk (bounds the dz workspace)
+constexpr int kVocabChunkMax = 65536;   // pass-2 vocabulary chunk bound (sizes the dz workspace)
+constexpr int kVocabChunkMin = 16384;
+constexpr int kDhSplitMax = 16;         // dh split-K partials (sizes the dh workspace)
+constexpr int kTokPad = 64;             // token count padding of h^T and dz^T rows (128-byte rows)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Source of the direct-to-LDS loads for rows beyond M / N and k beyond the
+// split: sixteen zero bytes (the loader zero-fills device globals).
+__device__ __attribute__((aligned(64))) uint16_t g_zero_page[32];
 
 enum { EPI_STATS = 0, EPI_DZ = 1, EPI_ACC = 2 };
 
@@ -64,6 +90,8 @@ struct GemmArgs {
     int64_t ldb;
     int M, N, K;         // K % 8 == 0; rows >= M / >= N are read as zeros
     int tiles_m, tiles_n;
+    int ksplit, kper;    // K range of split s: [s*kper, min(K, (s+1)*kper)), kper % BK == 0
+    int n_fast;          // tile order: N index fastest (else M fastest)
     // EPI_STATS
     float4* part;        // part[m * n_parts + n/64] = {max, sum e, sum e*t, 0}
     int n_parts;
@@ -79,8 +107,9 @@ struct GemmArgs {
     uint16_t* dzT;       // dzT[n * ld_dzT + m]
     int64_t ld_dzT;
     // EPI_ACC
-    float* C;            // C[m * ldc + n] = (beta ? C : 0) + acc
+    float* C;            // split s: (C + s*c_split)[m * ldc + n] = (beta ? that : 0) + acc
     int64_t ldc;
+    int64_t c_split;
     int beta;
 };
 
@@ -103,96 +132,149 @@ __device__ __forceinline__ int xcd_logical(int b, int nb) {
     return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// LDS rows are 64 bytes (four 16-byte k chunks); chunk c of row r is stored
+// at position c ^ swz(r), which spreads the 16-byte fragment reads of 32
+// consecutive rows over all banks.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their no-wait maxima)
+#define GRPO_VMCNT(n) (((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
 template <int EPI>
-__global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
-    // stage s: A tile at smem + s*(BM+BN)*LDK, B tile right after it
-    auto As = [&](int s) { return smem + s * (BM + BN) * LDK; };
-    auto Bs = [&](int s) { return smem + s * (BM + BN) * LDK + BM * LDK; };
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) {
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
-    const int logical = xcd_logical(blockIdx.x, g.tiles_m * g.tiles_n);
-    const int m0 = (logical % g.tiles_m) * BM, n0 = (logical / g.tiles_m) * BN;
+    const int nt = g.tiles_m * g.tiles_n;
+    const int logical = xcd_logical(blockIdx.x, nt * g.ksplit);
+    const int tile = logical % nt, split = logical / nt;
+    const int tm = g.n_fast ? tile / g.tiles_n : tile % g.tiles_m;
+    const int tn = g.n_fast ? tile % g.tiles_n : tile / g.tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int kbeg = split * g.kper;
+    const int kend = min(g.K, kbeg + g.kper);
+    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
-    // global -> register staging: 128 rows x 64 k per operand = 1024 16-byte
-    // vectors; thread t takes rows t/8 + 32j (j < 4), vector t%8 of the row
-    const int lrow = tid >> 3, lvec = (tid & 7) * 8;
-    uint4 ra[4], rb[4];
-    auto gload = [&](int k0) {
-        const int kk = k0 + lvec;
+    // Direct-to-LDS loads: one global_load_lds moves 64 lanes x 16 bytes to
+    // LDS base + 16*lane, i.e. 16 tile rows of 64 bytes.  Wave w fills rows
+    // (2w+q)*16 .. +16 of each operand (q < 2); lane l takes row (l/4) of
+    // those and stores k chunk (l%4) ^ swz(row) at LDS position l%4.
+    const int lr = lane >> 2, lp = lane & 3;
+    auto issue = [&](int kt) {
+        char* st = smem + (kt % NST) * STB;
+        const int k0 = kbeg + kt * BK;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m = m0 + lrow + 32 * j, n = n0 + lrow + 32 * j;
-            ra[j] = (m < g.M && kk < g.K) ? *reinterpret_cast<const uint4*>(g.A + (int64_t)m * g.lda + kk)
-                                          : make_uint4(0, 0, 0, 0);
-            rb[j] = (n < g.N && kk < g.K) ? *reinterpret_cast<const uint4*>(g.B + (int64_t)n * g.ldb + kk)
-                                          : make_uint4(0, 0, 0, 0);
+        for (int q = 0; q < 2; ++q) {
+            const int r = (wave * 2 + q) * 16 + lr;
+            const int k = k0 + ((lp ^ swz(r)) << 3);
+            const bool kin = k < kend;
+            const int ma = m0 + r, nb = n0 + r;
+            const uint16_t* ga = (ma < g.M && kin) ? g.A + (int64_t)ma * g.lda + k : g_zero_page;
+            const uint16_t* gb = (nb < g.N && kin) ? g.B + (int64_t)nb * g.ldb + k : g_zero_page;
+            __builtin_amdgcn_global_load_lds(ga, (lds_void*)(st + (wave * 2 + q) * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gb, (lds_void*)(st + OPB + (wave * 2 + q) * 1024), 16, 0, 0);
         }
     };
-    auto sstore = [&](int s) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<uint4*>(As(s) + (lrow + 32 * j) * LDK + lvec) = ra[j];
-            *reinterpret_cast<uint4*>(Bs(s) + (lrow + 32 * j) * LDK + lvec) = rb[j];
-        }
-    };
 
-    f32x16 acc[2][2];
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    const int nk = (g.K + BK - 1) / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    const int fr = lane & 31, fk = (lane >> 5) * 8;
+    const int fr = lane & 31, fh = lane >> 5;
+    for (int p = 0; p < PREF && p < nk; ++p) issue(p);
     for (int kt = 0; kt < nk; ++kt) {
-        const int s = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
+        // stage kt has landed once at most 4 loads per later stage are pending
+        const int later = min(PREF - 1, nk - 1 - kt);
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(GRPO_VMCNT(8));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(GRPO_VMCNT(4));
+        else __builtin_amdgcn_s_waitcnt(GRPO_VMCNT(0));
+        // every wave's share of stage kt is in LDS, and every wave is done
+        // reading stage kt-1, which the next issue overwrites
+        __syncthreads();
+        if (kt + PREF < nk) issue(kt + PREF);
+        const char* sa = smem + (kt % NST) * STB;
+        const char* sb = sa + OPB;
+        bf16x8 a[2][FM], b[2][FN];
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            bf16x8 a[2], b[2];
+        for (int h = 0; h < 2; ++h) {
+            const int c = h * 2 + fh;   // k chunk: lane half fh holds k = c*8 .. +8
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                a[i] = *reinterpret_cast<const bf16x8*>(As(s) + (wm * 64 + i * 32 + fr) * LDK + kk + fk);
-                b[i] = *reinterpret_cast<const bf16x8*>(Bs(s) + (wn * 64 + i * 32 + fr) * LDK + kk + fk);
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * WM + i * 32 + fr;
+                a[h][i] = *reinterpret_cast<const bf16x8*>(sa + r * ROWB + ((c ^ swz(r)) << 4));
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < FN; ++j) {
+                const int r = wn * WN + j * 32 + fr;
+                b[h][j] = *reinterpret_cast<const bf16x8*>(sb + r * ROWB + ((c ^ swz(r)) << 4));
+            }
         }
-        if (kt + 1 < nk) sstore(s ^ 1);
-        __syncthreads();
+        // all fragment reads before the first MFMA
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
     }
 
     // result element (i, j, r): row wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
-    //                           column wn*64 + j*32 + lane%32
-    const int rq = (lane >> 5) * 4;
+    //                           column wn*128 + j*32 + lane%32
+    const int rq = fh * 4;
     if constexpr (EPI == EPI_ACC) {
+        // per wave, 32 rows of the 64x128 tile at a time go through LDS; then
+        // lane l updates column quad l%32 of rows 2k + l/32 with 16-byte
+        // accesses (N % 4 == 0 and ldc % 4 == 0, so a quad is all in or all out)
+        float* Cs = g.C + (int64_t)split * g.c_split;
+        float* T = reinterpret_cast<float*>(smem) + wave * 32 * EPI_ROW_Q;
+        const int qc = lane & 31, rh = lane >> 5;
+        const int n = n0 + wn * WN + qc * 4;
+        __syncthreads();   // the stage buffers are reused
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FM; ++i) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int n = n0 + wn * 64 + j * 32 + fr;
-                if (n >= g.N) continue;
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + rq + (r & 3);
-                    if (m < g.M) {
-                        float* c = g.C + (int64_t)m * g.ldc + n;
-                        *c = g.beta ? *c + acc[i][j][r] : acc[i][j][r];
+                for (int r = 0; r < 16; ++r)
+                    T[((r >> 2) * 8 + rq + (r & 3)) * EPI_ROW_Q + j * 32 + fr] = acc[i][j][r];
+            __syncthreads();
+            if (n < g.N) {
+                const int mb = m0 + wm * WM + i * 32 + rh;
+                float4 v[16];
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    v[k] = *reinterpret_cast<const float4*>(T + (2 * k + rh) * EPI_ROW_Q + qc * 4);
+                if (g.beta) {
+                    float4 o[16];
+#pragma unroll
+                    for (int k = 0; k < 16; ++k)
+                        if (mb + 2 * k < g.M) o[k] = *reinterpret_cast<const float4*>(Cs + (int64_t)(mb + 2 * k) * g.ldc + n);
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) {
+                        v[k].x += o[k].x;
+                        v[k].y += o[k].y;
+                        v[k].z += o[k].z;
+                        v[k].w += o[k].w;
                     }
                 }
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    if (mb + 2 * k < g.M) *reinterpret_cast<float4*>(Cs + (int64_t)(mb + 2 * k) * g.ldc + n) = v[k];
             }
+            __syncthreads();
+        }
     } else if constexpr (EPI == EPI_DZ) {
         float* s_c2 = reinterpret_cast<float*>(smem);
         float* s_cf = s_c2 + BM;
         int* s_y = reinterpret_cast<int*>(s_cf + BM);
+        __syncthreads();   // the stage buffers are reused
         if (tid < BM) {
             const int m = m0 + tid;
             const bool in = m < g.M;
@@ -202,16 +284,16 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmArgs g) {
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int nl = n0 + wn * 64 + j * 32 + fr;   // column within the chunk
+            for (int j = 0; j < FN; ++j) {
+                const int nl = n0 + wn * WN + j * 32 + fr;   // column within the chunk
                 if (nl >= g.N) continue;
                 const int v = g.col0 + nl;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     float d[4];
-                    const int mb = wm * 64 + i * 32 + q * 8 + rq;   // local row of element r = 4q
+                    const int mb = wm * WM + i * 32 + q * 8 + rq;   // local row of element r = 4q
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int ml = mb + u;
@@ -237,36 +319,51 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmArgs g) {
                 }
             }
     } else {
-        // per wave, transpose the 64x64 tile through LDS so that lane r owns row r
-        float* T = reinterpret_cast<float*>(smem) + wave * 64 * 65;
+        // per wave, the 64x128 tile goes through LDS 32 rows at a time so that
+        // two lanes own one row (64 columns each)
+        float* T = reinterpret_cast<float*>(smem) + wave * 32 * EPI_ROW;
+        __syncthreads();   // the stage buffers are reused
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FM; ++i) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    T[(i * 32 + (r >> 2) * 8 + rq + (r & 3)) * 65 + j * 32 + fr] = acc[i][j][r];
-        __syncthreads();
-        const int m = m0 + wm * 64 + lane;
-        const int nb = n0 + wn * 64;
-        const int ncols = g.N - nb < 64 ? g.N - nb : 64;
-        if (m < g.M && ncols > 0) {
-            const float* row = T + lane * 65;
-            float mx = -INFINITY;
-            for (int c = 0; c < ncols; ++c) mx = fmaxf(mx, row[c]);
-            const float cm = mx * kLog2e;
-            float se = 0.0f, sw = 0.0f;
-            for (int c = 0; c < ncols; ++c) {
-                const float t = fmaf(row[c], kLog2e, -cm);
-                const float e = __builtin_amdgcn_exp2f(t);
-                se += e;
-                sw = fmaf(e, t, sw);
+                    T[((r >> 2) * 8 + rq + (r & 3)) * EPI_ROW + j * 32 + fr] = acc[i][j][r];
+            __syncthreads();
+            const int rr = lane >> 1, half = lane & 1;
+            const int m = m0 + wm * WM + i * 32 + rr;
+            const int nb = n0 + wn * WN + half * 64;
+            const int ncols = g.N - nb < 64 ? g.N - nb : 64;
+            if (m < g.M && ncols > 0) {
+                const float* row = T + rr * EPI_ROW + half * 64;
+                float mx = -INFINITY;
+                for (int c = 0; c < ncols; ++c) mx = fmaxf(mx, row[c]);
+                const float cm = mx * kLog2e;
+                float se = 0.0f, sw = 0.0f;
+                for (int c = 0; c < ncols; ++c) {
+                    const float t = fmaf(row[c], kLog2e, -cm);
+                    const float e = __builtin_amdgcn_exp2f(t);
+                    se += e;
+                    sw = fmaf(e, t, sw);
+                }
+                g.part[(int64_t)m * g.n_parts + nb / 64] = make_float4(mx, se, sw, 0.0f);
+                const int y = g.target[m];
+                if (y >= nb && y < nb + ncols) g.zy[m] = row[y - nb];
             }
-            g.part[(int64_t)m * g.n_parts + nb / 64] = make_float4(mx, se, sw, 0.0f);
-            const int y = g.target[m];
-            if (y >= nb && y < nb + ncols) g.zy[m] = row[y - nb];
+            __syncthreads();
         }
     }
+}
+
+// dst[i] = sum over s of parts[s * count + i], s in order
+__global__ __launch_bounds__(256) void sum_splits_kernel(float* __restrict__ dst, const float* __restrict__ parts,
+                                                         int nsplit, int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count) return;
+    float s = parts[i];
+    for (int k = 1; k < nsplit; ++k) s += parts[(int64_t)k * count + i];
+    dst[i] = s;
 }
 
 // One wave per token: merge the token's slice partials in a fixed order,
@@ -398,13 +495,54 @@ struct Workspace {
     uint16_t* hT;
     uint16_t* dz;
     uint16_t* dzT;
+    float* dh_part;
     size_t bytes;
 };
 
+// Pass 2 plan.  Every block of these GEMMs fills one compute unit, so a
+// launch of b blocks costs ceil(b / CUs) rounds of its per-block k-steps.
+// The vocabulary chunk width (a multiple of the tile width, at most
+// kVocabChunkMax) and the split count of dh = dz W_c (its output has only
+// ceil(n/256) x ceil(H/256) tiles, so its K range, the chunk's vocabulary, is
+// split; one partial per split, the same count for every chunk) are chosen
+// to minimise the summed rounds x k-steps of the dz, dh and dW launches.
+struct Pass2Plan {
+    int64_t chunk;
+    int nsplit;
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus) {
+    const int64_t n_pad = round_up(n, kTokPad);
+    const int64_t tm = cdiv(n, BM), th = cdiv(H, BN);
+    Pass2Plan best{V < kVocabChunkMax ? V : kVocabChunkMax, 1};
+    int64_t best_cost = -1;
+    const int64_t wmax = V < kVocabChunkMax ? round_up(V, BN) : kVocabChunkMax;
+    const int64_t wmin = wmax < kVocabChunkMin ? wmax : kVocabChunkMin;
+    for (int64_t w = wmin; w <= wmax; w += 2048 > wmax - wmin ? BN : 2048) {
+        for (int sp = 1; sp <= kDhSplitMax; ++sp) {
+            int64_t cost = 0;
+            for (int64_t c0 = 0; c0 < V; c0 += w) {
+                const int64_t vc = V - c0 < w ? V - c0 : w, tv = cdiv(vc, BN);
+                cost += cdiv(tm * tv, cus) * cdiv(H, BK);                              // dz
+                cost += cdiv(tv * th, cus) * cdiv(n_pad, BK);                          // dW
+                cost += cdiv(tm * th * sp, cus) * (round_up(cdiv(vc, sp), BK) / BK);   // dh
+            }
+            // a split must save at least 1 % to be worth its partial
+            if (best_cost < 0 || cost * 100 < best_cost * 99) {
+                best_cost = cost;
+                best = {w < V ? w : V, sp};
+            }
+        }
+    }
+    return best;
+}
+
 Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V) {
     const int64_t n_parts = (V + 63) / 64;
-    const int64_t n_pad = round_up(n_tok > 0 ? n_tok : 1, 8);
-    const int64_t vc = V < kVocabChunk ? V : kVocabChunk;
+    const int64_t n_pad = round_up(n_tok > 0 ? n_tok : 1, kTokPad);
+    const int64_t vc = V < kVocabChunkMax ? V : kVocabChunkMax;   // widest chunk any plan uses
     Workspace w{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -419,6 +557,7 @@ Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V) {
     w.hT = reinterpret_cast<uint16_t*>(take((size_t)H * n_pad * 2));
     w.dz = reinterpret_cast<uint16_t*>(take((size_t)n_tok * vc * 2));
     w.dzT = reinterpret_cast<uint16_t*>(take((size_t)vc * n_pad * 2));
+    w.dh_part = reinterpret_cast<float*>(take((size_t)kDhSplitMax * n_tok * H * 4));
     w.bytes = off;
     return w;
 }
@@ -428,7 +567,14 @@ hipError_t launch_gemm(GemmArgs g, hipStream_t st) {
     g.tiles_m = (g.M + BM - 1) / BM;
     g.tiles_n = (g.N + BN - 1) / BN;
     if (EPI == EPI_DZ) g.tiles_m = (g.m_out + BM - 1) / BM;
-    const long long nb = (long long)g.tiles_m * g.tiles_n;
+    // the index with fewer tiles varies fastest, so the blocks that read one
+    // tile of the larger operand are adjacent and share it in L2
+    g.n_fast = g.tiles_n < g.tiles_m;
+    if (g.ksplit < 1) {
+        g.ksplit = 1;
+        g.kper = g.K;
+    }
+    const long long nb = (long long)g.tiles_m * g.tiles_n * g.ksplit;
     if (nb == 0) return hipSuccess;
     hipLaunchKernelGGL(gemm_nt_kernel<EPI>, dim3((unsigned)nb), dim3(NTHREADS), 0, st, g);
     return hipGetLastError();
@@ -473,8 +619,8 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
         return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: H, V and ldh must be multiples of 8 (ldh >= H)");
     if (n > (1 << 30) || V > (1 << 30) || H > (1 << 20))
         return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: sizes beyond the kernels' 32-bit tile indexing");
-    if (!a->W || !a->Wt || !a->dW || !al16(a->W) || !al16(a->Wt))
-        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: W, Wt and dW are required (W, Wt 16-byte aligned)");
+    if (!a->W || !a->Wt || !a->dW || !al16(a->W) || !al16(a->Wt) || !al16(a->dW))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: W, Wt and dW are required (16-byte aligned)");
     if (!a->chunk_stats || (a->n_rows > 0 && (!a->row_stats || !a->row_off)))
         return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: NULL stats pointer");
     if (n > 0 && (!a->h || !al16(a->h) || !a->target || !a->mask || !a->old_logp || !a->tok_row || !a->adv_row ||
@@ -490,7 +636,7 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
     if (n == 0) return grpo::launch_stats(stream, a->loss_tok, a->entropy, a->tok_flags, a->row_off, a->n_rows, 0,
                                           a->row_stats, a->chunk_stats);
     const Workspace w = carve(a->workspace, n, H, V);
-    const int64_t n_pad = round_up(n, 8);
+    const int64_t n_pad = round_up(n, kTokPad);
     const int n_parts = (int)((V + 63) / 64);
     const uint16_t* h = (const uint16_t*)a->h;
     const uint16_t* W = (const uint16_t*)a->W;
@@ -522,8 +668,15 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
     if (rc != GRPO_OK) return rc;
 
     // pass 2: per vocabulary chunk, dz then dh (+)= dz W_c and dW_c += dz^T h
-    for (int64_t c0 = 0; c0 < V; c0 += kVocabChunk) {
-        const int vc = (int)(V - c0 < kVocabChunk ? V - c0 : kVocabChunk);
+    int dev = 0, cus = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess ||
+        (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return dev_fail(e, "device query");
+    const Pass2Plan plan = plan_pass2(n, H, V, cus > 0 ? cus : 1);
+    const int64_t chunk = plan.chunk;
+    const int nsplit = plan.nsplit;
+    for (int64_t c0 = 0; c0 < V; c0 += chunk) {
+        const int vc = (int)(V - c0 < chunk ? V - c0 : chunk);
         GemmArgs d{};
         d.A = h; d.lda = a->ldh; d.B = W + c0 * H; d.ldb = H;
         d.M = (int)n; d.N = vc; d.K = (int)H;
@@ -531,10 +684,14 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
         d.dz = w.dz; d.ld_dz = vc; d.dzT = w.dzT; d.ld_dzT = n_pad;
         if ((e = launch_gemm<EPI_DZ>(d, st)) != hipSuccess) return dev_fail(e, "dz");
 
+        // dh: the chunk's vocabulary range split nsplit ways, split s
+        // accumulating into its own partial (summed in order at the end)
         GemmArgs gh{};
         gh.A = w.dz; gh.lda = vc; gh.B = Wt + c0; gh.ldb = V;
         gh.M = (int)n; gh.N = (int)H; gh.K = vc;
-        gh.C = a->dh; gh.ldc = H; gh.beta = c0 > 0;
+        gh.ksplit = nsplit;
+        gh.kper = (int)round_up((vc + nsplit - 1) / nsplit, BK);
+        gh.C = w.dh_part; gh.ldc = H; gh.c_split = n * H; gh.beta = c0 > 0;
         if ((e = launch_gemm<EPI_ACC>(gh, st)) != hipSuccess) return dev_fail(e, "dh");
 
         GemmArgs gw{};
@@ -543,5 +700,8 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
         gw.C = a->dW + c0 * H; gw.ldc = H; gw.beta = 1;
         if ((e = launch_gemm<EPI_ACC>(gw, st)) != hipSuccess) return dev_fail(e, "dW");
     }
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n * H + 255) / 256)), dim3(256), 0, st, a->dh, w.dh_part,
+                       nsplit, n * H);
+    if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "dh splits");
     return ok();
 }

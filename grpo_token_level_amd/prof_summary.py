@@ -49,7 +49,7 @@ def stats(args):
                     rec = json.loads(line)
                     rf = rec["roofline"]
                     lines += ["", "the profiled bench run's own line (HIP events around each fused-loss call):",
-                              f"  avg_launch_ms {rf['avg_launch_ms']}  achieved {rf['achieved']} GB/s  "
+                              f"  avg_launch_ms {rf['avg_launch_ms']}  achieved {rf['achieved']} {rf['unit']}  "
                               f"ms_per_step {rec['ms_per_step']}  value {rec['value']} {rec['unit']}"]
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")

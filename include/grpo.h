@@ -235,7 +235,7 @@ typedef struct grpo_lmhead_args {
     const void* h;              /* bf16 [n_tok x H] hidden states, row stride ldh (16-byte aligned) */
     int64_t ldh;                /* >= H, multiple of 8 */
     const void* W;              /* bf16 [V x H] LM-head weight, rows contiguous (16-byte aligned) */
-    const void* Wt;             /* bf16 [H x V]: W transposed (grpo_transpose_bf16) */
+    const void* Wt;             /* bf16 [H x V]: W transposed (grpo_transpose_bf16), 16-byte aligned */
     int64_t n_tok, H, V;        /* H and V multiples of 8 */
     const int32_t* target;      /* [n_tok] */
     const uint8_t* mask;        /* [n_tok] 1 = policy token; pads and observations 0 */
@@ -249,7 +249,7 @@ typedef struct grpo_lmhead_args {
     int32_t reserved1;          /* 0 */
     const int64_t* denom;       /* NULL or device int64 N: factor further divided by max(N, 1) */
     float* dh;                  /* fp32 [n_tok x H]: dL/dh, overwritten */
-    float* dW;                  /* fp32 [V x H]: dL/dW of this chunk is ADDED (accumulate over chunks) */
+    float* dW;                  /* fp32 [V x H], 16-byte aligned: dL/dW of this chunk is ADDED (accumulate) */
     float* logp;                /* [n_tok] required */
     float* lse;                 /* [n_tok] or NULL */
     float* entropy;             /* [n_tok] required */
@@ -263,8 +263,9 @@ typedef struct grpo_lmhead_args {
 
 /* host.  Workspace bytes grpo_lmhead_fwd_bwd needs for a chunk of n_tok tokens:
  * per-token slice partials of the log-softmax (16 B per token per 64 vocabulary
- * columns), h^T, and one vocabulary chunk of dz in two layouts (bf16).  It
- * grows with n_tok * V / 4 and n_tok * 16384, never with n_tok * V * 2. */
+ * columns), h^T, one vocabulary chunk (at most 65536 columns) of dz in two
+ * layouts (bf16) and up to 16 fp32 split partials of dh.  It grows with
+ * n_tok * V / 4, n_tok * 262144 and n_tok * H * 64, never with n_tok * V * 2. */
 size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V);
 
 /* device.  The fused loss of grpo_loss_fwd_bwd with the logits produced by the

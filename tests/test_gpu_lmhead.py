@@ -1,6 +1,6 @@
 """GPU parity of the fused LM-head variant (grpo_lmhead_fwd_bwd) against the
 oracle: per-token outputs, dh and the accumulated dW, on ragged shapes
-(tokens, hidden size and vocabulary not multiples of the 128x128x64 tiles, a
+(tokens, hidden size and vocabulary not multiples of the 256x256x32 tiles, a
 vocabulary spanning several pass-2 chunks), plus the context-compaction
 workload at full size checked on sampled tokens and by properties.
 

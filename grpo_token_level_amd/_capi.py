@@ -29,14 +29,20 @@ class GrpoError(RuntimeError):
         super().__init__(f"{self.kind}: {msg}")
 
 
+KL_K1, KL_K2, KL_K3 = 1, 2, 3
+AGG_TOKEN_MEAN, AGG_SEQ_MEAN_TOKEN_SUM, AGG_SEQ_MEAN_TOKEN_MEAN = 0, 1, 2
+
+
 class Stats(ctypes.Structure):
     _fields_ = [("loss_sum", ctypes.c_double), ("entropy_sum", ctypes.c_double),
+                ("kl_sum", ctypes.c_double), ("obj_sum", ctypes.c_double),
                 ("n_valid", ctypes.c_int64), ("n_clipped", ctypes.c_int64),
                 ("n_nonfinite", ctypes.c_int64), ("n_valid_rows", ctypes.c_int64)]
 
 
-# numpy view of an array of grpo_stats (48 bytes each)
-STATS_DTYPE = np.dtype([("loss_sum", "<f8"), ("entropy_sum", "<f8"), ("n_valid", "<i8"),
+# numpy view of an array of grpo_stats (64 bytes each)
+STATS_DTYPE = np.dtype([("loss_sum", "<f8"), ("entropy_sum", "<f8"), ("kl_sum", "<f8"), ("obj_sum", "<f8"),
+                        ("n_valid", "<i8"),
                         ("n_clipped", "<i8"), ("n_nonfinite", "<i8"), ("n_valid_rows", "<i8")])
 STATS_BYTES = STATS_DTYPE.itemsize
 
@@ -54,7 +60,9 @@ class LossArgs(ctypes.Structure):
                 ("eps_low", _f32), ("eps_high", _f32), ("scale", _f32), ("reserved1", _i32),
                 ("denom", _p), ("dlogits", _p), ("ld_out", _i64),
                 ("logp", _p), ("lse", _p), ("entropy", _p), ("loss_tok", _p), ("tok_flags", _p),
-                ("row_stats", _p), ("chunk_stats", _p)]
+                ("row_stats", _p), ("chunk_stats", _p),
+                ("row_weight", _p), ("ref_logp", _p), ("kl_tok", _p),
+                ("ent_coef", _f32), ("kl_coef", _f32), ("kl_type", _i32), ("reserved2", _i32)]
 
 
 class LmheadArgs(ctypes.Structure):
@@ -65,7 +73,9 @@ class LmheadArgs(ctypes.Structure):
                 ("eps_low", _f32), ("eps_high", _f32), ("scale", _f32), ("reserved1", _i32),
                 ("denom", _p), ("dh", _p), ("dW", _p),
                 ("logp", _p), ("lse", _p), ("entropy", _p), ("loss_tok", _p), ("tok_flags", _p),
-                ("row_stats", _p), ("chunk_stats", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
+                ("row_stats", _p), ("chunk_stats", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+                ("row_weight", _p), ("ref_logp", _p), ("kl_tok", _p),
+                ("ent_coef", _f32), ("kl_coef", _f32), ("kl_type", _i32), ("reserved2", _i32)]
 
 
 class Accum(ctypes.Structure):
@@ -74,7 +84,8 @@ class Accum(ctypes.Structure):
 
 
 class StepResult(ctypes.Structure):
-    _fields_ = [("loss", ctypes.c_double), ("entropy", ctypes.c_double), ("grad_scale", ctypes.c_double),
+    _fields_ = [("loss", ctypes.c_double), ("entropy", ctypes.c_double), ("kl", ctypes.c_double),
+                ("obj_sum", ctypes.c_double), ("grad_scale", ctypes.c_double),
                 ("n_valid", _i64), ("n_valid_rows", _i64), ("n_clipped", _i64)]
 
 
@@ -96,6 +107,8 @@ PROTOTYPES = {
     "grpo_group_advantage": (ctypes.c_int, [_PF32, _i64, _i64, _f32, _i32, _PF32]),
     "grpo_rows_advantage": (ctypes.c_int, [_PF32, _i64, _P32, _i64, _PF32]),
     "grpo_count_valid": (ctypes.c_int, [_p, _p, _i64, _p]),
+    "grpo_count_rows": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _p]),
+    "grpo_row_weights": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p, _p]),
     "grpo_tok_row": (ctypes.c_int, [_p, _p, _i64, _i64, _p]),
     "grpo_logprob_fwd": (ctypes.c_int, [_p, _i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "grpo_loss_fwd_bwd": (ctypes.c_int, [_p, ctypes.POINTER(LossArgs)]),

@@ -302,6 +302,8 @@ void stats_zero(grpo_stats* s) { std::memset(s, 0, sizeof(*s)); }
 void stats_add(grpo_stats* a, const grpo_stats* b) {
     a->loss_sum += b->loss_sum;
     a->entropy_sum += b->entropy_sum;
+    a->kl_sum += b->kl_sum;
+    a->obj_sum += b->obj_sum;
     a->n_valid += b->n_valid;
     a->n_clipped += b->n_clipped;
     a->n_nonfinite += b->n_nonfinite;
@@ -325,7 +327,8 @@ extern "C" int grpo_accum_add(grpo_accum* acc, const grpo_stats* c) {
         --acc->skip;
         return fail(GRPO_ESKIPPED, "grpo_accum_add: call swallowed, %lld more to skip", (long long)acc->skip);
     }
-    if (c->n_nonfinite > 0 || !std::isfinite(c->loss_sum) || !std::isfinite(c->entropy_sum)) {
+    if (c->n_nonfinite > 0 || !std::isfinite(c->loss_sum) || !std::isfinite(c->entropy_sum) ||
+        !std::isfinite(c->kl_sum) || !std::isfinite(c->obj_sum)) {
         acc->skip = acc->n_micro - 1 - acc->pos;
         acc->pos = 0;
         stats_zero(&acc->open);
@@ -354,6 +357,8 @@ extern "C" int grpo_accum_finalize(grpo_accum* acc, grpo_step_result* out, int32
     const double denom = (double)std::max<int64_t>(s.n_valid, 1);
     out->loss = s.loss_sum / denom;
     out->entropy = s.entropy_sum / denom;
+    out->kl = s.kl_sum / denom;
+    out->obj_sum = s.obj_sum;
     out->grad_scale = 1.0 / denom;
     out->n_valid = s.n_valid;
     out->n_valid_rows = s.n_valid_rows;

@@ -100,6 +100,9 @@ struct GemmArgs {
     // EPI_DZ
     const float* c2;     // log2-domain logsumexp per token
     const float* coef;   // gradient coefficient per token
+    const float* ea;     // with the entropy bonus (bonus != 0): dz = p * (ea + eb * t) - coef * onehot,
+    const float* eb;     //   t = z*log2e - c2, per token
+    int bonus;
     int col0;            // vocabulary index of column 0 of this chunk
     int m_out;           // rows [M, m_out) are written as zeros (K padding of dz^T)
     uint16_t* dz;        // dz[m * ld_dz + n]
@@ -273,13 +276,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
     } else if constexpr (EPI == EPI_DZ) {
         float* s_c2 = reinterpret_cast<float*>(smem);
         float* s_cf = s_c2 + BM;
-        int* s_y = reinterpret_cast<int*>(s_cf + BM);
+        float* s_ea = s_cf + BM;
+        float* s_eb = s_ea + BM;
+        int* s_y = reinterpret_cast<int*>(s_eb + BM);
         __syncthreads();   // the stage buffers are reused
         if (tid < BM) {
             const int m = m0 + tid;
             const bool in = m < g.M;
             s_c2[tid] = in ? g.c2[m] : 0.0f;
             s_cf[tid] = in ? g.coef[m] : 0.0f;
+            s_ea[tid] = (in && g.bonus) ? g.ea[m] : 0.0f;
+            s_eb[tid] = (in && g.bonus) ? g.eb[m] : 0.0f;
             s_y[tid] = in ? g.target[m] : -1;
         }
         __syncthreads();
@@ -298,7 +305,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
                     for (int u = 0; u < 4; ++u) {
                         const int ml = mb + u;
                         const float cf = s_cf[ml];
-                        float x = cf * __builtin_amdgcn_exp2f(fmaf(acc[i][j][q * 4 + u], kLog2e, -s_c2[ml]));
+                        const float tt = fmaf(acc[i][j][q * 4 + u], kLog2e, -s_c2[ml]);
+                        const float pp = __builtin_amdgcn_exp2f(tt);
+                        float x;
+                        if (!g.bonus) x = cf * pp;
+                        else x = pp > 0.0f ? pp * fmaf(s_eb[ml], tt, s_ea[ml]) : 0.0f;
                         if (s_y[ml] == v) x -= cf;
                         d[u] = x;
                     }
@@ -384,11 +395,15 @@ struct MergeArgs {
     const int64_t* denom;
     float* c2;
     float* coef;
+    float* ea;
+    float* eb;
     float* logp;
     float* lse;
     float* entropy;
     float* loss_tok;
     uint8_t* tok_flags;
+    grpo_dev::Terms terms;
+    float* kl_tok;
 };
 
 // (M, S, W): S = sum e^(z-M), W = sum e^(z-M) (z-M) log2(e), merged exactly
@@ -417,6 +432,9 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const MergeArgs a) {
         if (lane == 0) {
             a.c2[t] = 0.0f;
             a.coef[t] = 0.0f;
+            a.ea[t] = 0.0f;
+            a.eb[t] = 0.0f;
+            if (a.kl_tok) a.kl_tok[t] = 0.0f;
             a.logp[t] = 0.0f;
             if (a.lse) a.lse[t] = 0.0f;
             a.entropy[t] = 0.0f;
@@ -455,10 +473,16 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const MergeArgs a) {
     const float H = kLn2 * (log2s - W / S);
     const int32_t row = a.tok_row[t];
     const float A = ((uint32_t)row < (uint64_t)a.n_rows) ? a.adv_row[row] : __builtin_nanf("");
-    const grpo_dev::Surrogate sg = grpo_dev::surrogate(logp, H, a.old_logp[t], A, a.eps_low, a.eps_high,
-                                                       grpo_dev::step_scale(a.scale, a.denom));
+    const float sf = grpo_dev::token_factor(grpo_dev::step_scale(a.scale, a.denom), a.terms.row_weight, row,
+                                            a.n_rows);
+    const grpo_dev::Surrogate sg = grpo_dev::surrogate(logp, H, a.old_logp[t], A, a.eps_low, a.eps_high, sf,
+                                                       a.terms, t);
+    const float e = a.terms.ent_coef * sf;
     a.c2[t] = c2;
     a.coef[t] = sg.coef;
+    a.ea[t] = fmaf(e, H, sg.coef);
+    a.eb[t] = e * kLn2;
+    if (a.kl_tok) a.kl_tok[t] = sg.kl;
     a.logp[t] = logp;
     if (a.lse) a.lse[t] = lse;
     a.entropy[t] = H;
@@ -492,6 +516,8 @@ struct Workspace {
     float* zy;
     float* c2;
     float* coef;
+    float* ea;
+    float* eb;
     uint16_t* hT;
     uint16_t* dz;
     uint16_t* dzT;
@@ -554,6 +580,8 @@ Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V) {
     w.zy = reinterpret_cast<float*>(take((size_t)n_tok * 4));
     w.c2 = reinterpret_cast<float*>(take((size_t)n_tok * 4));
     w.coef = reinterpret_cast<float*>(take((size_t)n_tok * 4));
+    w.ea = reinterpret_cast<float*>(take((size_t)n_tok * 4));
+    w.eb = reinterpret_cast<float*>(take((size_t)n_tok * 4));
     w.hT = reinterpret_cast<uint16_t*>(take((size_t)H * n_pad * 2));
     w.dz = reinterpret_cast<uint16_t*>(take((size_t)n_tok * vc * 2));
     w.dzT = reinterpret_cast<uint16_t*>(take((size_t)vc * n_pad * 2));
@@ -629,12 +657,19 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
     if (!(a->eps_low >= 0.0f && a->eps_low <= 1.0f && a->eps_high >= 0.0f && std::isfinite(a->eps_high)) ||
         !std::isfinite(a->scale))
         return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: bad clip band or scale");
+    {
+        const int rc = grpo::check_terms("grpo_lmhead_fwd_bwd", n, a->ref_logp, a->kl_tok, a->ent_coef, a->kl_coef,
+                                         a->kl_type);
+        if (rc != GRPO_OK) return rc;
+    }
     const size_t need = grpo_lmhead_workspace_size(n, H, V);
     if (!a->workspace || a->workspace_bytes < need || !al16(a->workspace))
         return fail(GRPO_ECAPACITY, "grpo_lmhead_fwd_bwd: workspace of %zu bytes needed (16-byte aligned)", need);
     hipStream_t st = (hipStream_t)stream;
-    if (n == 0) return grpo::launch_stats(stream, a->loss_tok, a->entropy, a->tok_flags, a->row_off, a->n_rows, 0,
-                                          a->row_stats, a->chunk_stats);
+    const grpo::ObjTerms obj{a->scale, a->denom, a->row_weight, a->ent_coef, a->ref_logp ? a->kl_coef : 0.0f};
+    float* kl_tok = a->ref_logp ? a->kl_tok : nullptr;
+    if (n == 0) return grpo::launch_stats(stream, a->loss_tok, a->entropy, kl_tok, a->tok_flags, a->row_off,
+                                          a->n_rows, 0, obj, a->row_stats, a->chunk_stats);
     const Workspace w = carve(a->workspace, n, H, V);
     const int64_t n_pad = round_up(n, kTokPad);
     const int n_parts = (int)((V + 63) / 64);
@@ -659,12 +694,15 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
     mg.part = w.part; mg.n_parts = n_parts; mg.zy = w.zy; mg.n_tok = n; mg.V = V;
     mg.target = a->target; mg.mask = a->mask; mg.old_logp = a->old_logp; mg.tok_row = a->tok_row;
     mg.adv_row = a->adv_row; mg.n_rows = a->n_rows; mg.eps_low = a->eps_low; mg.eps_high = a->eps_high;
-    mg.scale = a->scale; mg.denom = a->denom; mg.c2 = w.c2; mg.coef = w.coef; mg.logp = a->logp; mg.lse = a->lse;
+    mg.scale = a->scale; mg.denom = a->denom; mg.c2 = w.c2; mg.coef = w.coef; mg.ea = w.ea; mg.eb = w.eb;
+    mg.logp = a->logp; mg.lse = a->lse;
+    mg.terms = grpo_dev::Terms{a->row_weight, a->ref_logp, a->ent_coef, a->kl_coef, a->kl_type};
+    mg.kl_tok = kl_tok;
     mg.entropy = a->entropy; mg.loss_tok = a->loss_tok; mg.tok_flags = a->tok_flags;
     hipLaunchKernelGGL(lm_merge_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, mg);
     if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "merge");
-    const int rc = grpo::launch_stats(stream, a->loss_tok, a->entropy, a->tok_flags, a->row_off, a->n_rows, n,
-                                      a->row_stats, a->chunk_stats);
+    const int rc = grpo::launch_stats(stream, a->loss_tok, a->entropy, kl_tok, a->tok_flags, a->row_off, a->n_rows,
+                                      n, obj, a->row_stats, a->chunk_stats);
     if (rc != GRPO_OK) return rc;
 
     // pass 2: per vocabulary chunk, dz then dh (+)= dz W_c and dW_c += dz^T h
@@ -681,6 +719,7 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
         d.A = h; d.lda = a->ldh; d.B = W + c0 * H; d.ldb = H;
         d.M = (int)n; d.N = vc; d.K = (int)H;
         d.c2 = w.c2; d.coef = w.coef; d.target = a->target; d.col0 = (int)c0; d.m_out = (int)n_pad;
+        d.ea = w.ea; d.eb = w.eb; d.bonus = a->ent_coef != 0.0f;
         d.dz = w.dz; d.ld_dz = vc; d.dzT = w.dzT; d.ld_dzT = n_pad;
         if ((e = launch_gemm<EPI_DZ>(d, st)) != hipSuccess) return dev_fail(e, "dz");
 

@@ -207,6 +207,8 @@ struct TokParams {
     float* entropy;
     float* loss_tok;
     uint8_t* tok_flags;
+    grpo_dev::Terms terms;   // row weights, entropy bonus, KL
+    float* kl_tok;           // required when terms.ref_logp is set
 };
 
 // Per-token scalar tail shared by both kernels: from (max-shifted sums, z_y)
@@ -214,7 +216,9 @@ struct TokParams {
 // shift used for the sums, s = sum 2^t, w = sum 2^t * t.
 struct TokenResult {
     float c2;      // log2-domain logsumexp: p_v = 2^(z_v*log2e - c2)
-    float coef;    // dlogits_v = coef * (p_v - [v == y])
+    float coef;    // dlogits_v = p_v * (ea + eb * t_v) - coef * [v == y], t_v = z_v*log2e - c2
+    float ea;      // coef + e*H
+    float eb;      // e*ln2, e = ent_coef * s (0: dlogits_v = coef * (p_v - [v == y]))
 };
 
 template <bool GRAD>
@@ -225,7 +229,7 @@ __device__ __forceinline__ TokenResult token_tail(const TokParams& p, int64_t t,
     const float lse = c2 * kLn2;
     const float logp = ybad ? __builtin_nanf("") : zy - lse;
     const float H = kLn2 * (log2s - w / s);
-    TokenResult r{c2, 0.0f};
+    TokenResult r{c2, 0.0f, 0.0f, 0.0f};
     if constexpr (!GRAD) {
         if (write) {
             p.logp[t] = logp;
@@ -236,17 +240,26 @@ __device__ __forceinline__ TokenResult token_tail(const TokParams& p, int64_t t,
     } else {
         const int32_t row = p.tok_row[t];
         const float A = ((uint32_t)row < (uint64_t)p.n_rows) ? p.adv_row[row] : __builtin_nanf("");
-        const grpo_dev::Surrogate sg = grpo_dev::surrogate(logp, H, p.old_logp[t], A, p.eps_low, p.eps_high,
-                                                           grpo_dev::step_scale(p.scale, p.denom));
-        const float coef = sg.coef;
+        const float sf = grpo_dev::token_factor(grpo_dev::step_scale(p.scale, p.denom), p.terms.row_weight, row,
+                                                p.n_rows);
+        const grpo_dev::Surrogate sg = grpo_dev::surrogate(logp, H, p.old_logp[t], A, p.eps_low, p.eps_high, sf,
+                                                           p.terms, t);
         if (write) {
             p.logp[t] = logp;
             if (p.lse) p.lse[t] = lse;
             p.entropy[t] = H;
             p.loss_tok[t] = sg.loss;
+            if (p.kl_tok) p.kl_tok[t] = sg.kl;
             p.tok_flags[t] = (uint8_t)(1u | (sg.clipped ? 2u : 0u) | (sg.bad ? 4u : 0u));
         }
-        r.coef = coef;
+        r.coef = sg.coef;
+        if (p.terms.ent_coef != 0.0f) {
+            const float e = p.terms.ent_coef * sf;
+            r.ea = fmaf(e, H, sg.coef);
+            r.eb = e * kLn2;
+        } else {
+            r.ea = sg.coef;
+        }
         return r;
     }
 }
@@ -258,8 +271,16 @@ __device__ __forceinline__ void masked_outputs(const TokParams& p, int64_t t) {
     if (p.entropy) p.entropy[t] = 0.0f;
     if constexpr (GRAD) {
         p.loss_tok[t] = 0.0f;
+        if (p.kl_tok) p.kl_tok[t] = 0.0f;
         p.tok_flags[t] = 0;
     }
+}
+
+// dlogits value of one element with the entropy bonus on: p * (ea + eb * tt)
+// with p = 2^tt (an element with p = 0 contributes 0, also at z = -inf)
+__device__ __forceinline__ float dz_with_bonus(float tt, float ea, float eb) {
+    const float pp = __builtin_amdgcn_exp2f(tt);
+    return pp > 0.0f ? pp * fmaf(eb, tt, ea) : 0.0f;
 }
 
 // ---------------------------------------------------------------- register-resident kernel
@@ -389,7 +410,7 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     const TokenResult r = token_tail<GRAD>(p, t, c, s, w, zy, ybad, tid == 0);
     if constexpr (GRAD) {
         if (!orow) return;
-        if (r.coef == 0.0f) {   // zero advantage or clipped token: the gradient row is zero
+        if (r.coef == 0.0f && r.eb == 0.0f) {   // zero advantage or clipped, no bonus: the row is zero
 #pragma unroll
             for (int k = 0; k < NV; ++k) {
                 const int idx = k * TPR + tid;
@@ -405,8 +426,13 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
             float f[VEC];
             In<DTI>::unpack(x[k], f);
             float d[VEC];
+            if (r.eb == 0.0f) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) d[e] = r.coef * __builtin_amdgcn_exp2f(fmaf(f[e], kLog2e, -r.c2));
+                for (int e = 0; e < VEC; ++e) d[e] = r.coef * __builtin_amdgcn_exp2f(fmaf(f[e], kLog2e, -r.c2));
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) d[e] = dz_with_bonus(fmaf(f[e], kLog2e, -r.c2), r.ea, r.eb);
+            }
             if (idx == vy && !ybad) {
                 const int ey = y % VEC;
 #pragma unroll
@@ -484,9 +510,10 @@ __global__ __launch_bounds__(256) void tok_generic_kernel(const TokParams p) {
     if constexpr (GRAD) {
         if (!orow) return;
         for (int64_t v = tid; v < p.V; v += TPR) {
-            float d = r.coef * __builtin_amdgcn_exp2f(fmaf(In<DTI>::scalar(irow, v), kLog2e, -r.c2));
+            const float tt = fmaf(In<DTI>::scalar(irow, v), kLog2e, -r.c2);
+            float d = r.eb == 0.0f ? r.coef * __builtin_amdgcn_exp2f(tt) : dz_with_bonus(tt, r.ea, r.eb);
             if (v == y) d -= r.coef;
-            if (r.coef == 0.0f) d = 0.0f;
+            if (r.coef == 0.0f && r.eb == 0.0f) d = 0.0f;
             Out<DTO>::scalar(orow, v, d);
         }
     }
@@ -496,13 +523,17 @@ __global__ __launch_bounds__(256) void tok_generic_kernel(const TokParams p) {
 
 // One 256-thread block per row: thread j takes the row's tokens j, j+256, ...,
 // then a fixed tree over the block.  A row's stats depend only on its own
-// tokens (never on where the row sits in the chunk).
+// tokens (never on where the row sits in the chunk).  The row's objective
+// share is s_r * (sum l - ent_coef * sum H + kl_coef * sum KL), s_r being the
+// factor its tokens' gradients carried.
 __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ loss_tok,
                                                         const float* __restrict__ entropy,
+                                                        const float* __restrict__ kl_tok,
                                                         const uint8_t* __restrict__ flags,
                                                         const int64_t* __restrict__ row_off, int64_t n_rows,
-                                                        int64_t n_tok, grpo_stats* __restrict__ out) {
-    __shared__ double s_ls[4], s_es[4];
+                                                        int64_t n_tok, const grpo::ObjTerms obj,
+                                                        grpo_stats* __restrict__ out) {
+    __shared__ double s_ls[4], s_es[4], s_ks[4];
     __shared__ long long s_nv[4], s_nc[4], s_nn[4];
     const int64_t r = blockIdx.x;
     const int i = threadIdx.x;
@@ -510,13 +541,14 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
     int64_t b = row_off[r], e = row_off[r + 1];
     b = b < 0 ? 0 : (b > n_tok ? n_tok : b);
     e = e < b ? b : (e > n_tok ? n_tok : e);
-    double ls = 0.0, es = 0.0;
+    double ls = 0.0, es = 0.0, ks = 0.0;
     long long nv = 0, nc = 0, nn = 0;
     for (int64_t t = b + i; t < e; t += 256) {
         const uint8_t f = flags[t];
         if (f & 1u) {
             ls += (double)loss_tok[t];
             es += (double)entropy[t];
+            if (kl_tok) ks += (double)kl_tok[t];
             nv += 1;
             nc += (f >> 1) & 1u;
             nn += (f >> 2) & 1u;
@@ -524,22 +556,32 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
     }
     ls = wave_sum_d(ls);
     es = wave_sum_d(es);
+    ks = wave_sum_d(ks);
     nv = wave_sum_i(nv);
     nc = wave_sum_i(nc);
     nn = wave_sum_i(nn);
     const int w = i >> 6;
     if ((i & 63) == 0) {
-        s_ls[w] = ls; s_es[w] = es; s_nv[w] = nv; s_nc[w] = nc; s_nn[w] = nn;
+        s_ls[w] = ls; s_es[w] = es; s_ks[w] = ks; s_nv[w] = nv; s_nc[w] = nc; s_nn[w] = nn;
     }
     __syncthreads();
     if (i == 0) {
         grpo_stats s;
         s.loss_sum = ((s_ls[0] + s_ls[1]) + s_ls[2]) + s_ls[3];
         s.entropy_sum = ((s_es[0] + s_es[1]) + s_es[2]) + s_es[3];
+        s.kl_sum = ((s_ks[0] + s_ks[1]) + s_ks[2]) + s_ks[3];
         s.n_valid = s_nv[0] + s_nv[1] + s_nv[2] + s_nv[3];
         s.n_clipped = s_nc[0] + s_nc[1] + s_nc[2] + s_nc[3];
         s.n_nonfinite = s_nn[0] + s_nn[1] + s_nn[2] + s_nn[3];
         s.n_valid_rows = s.n_valid > 0 ? 1 : 0;
+        if (s.n_valid > 0) {
+            const float sr = grpo_dev::token_factor(grpo_dev::step_scale(obj.scale, obj.denom), obj.row_weight,
+                                                    (int32_t)r, n_rows);
+            s.obj_sum = (double)sr * ((s.loss_sum - (double)obj.ent_coef * s.entropy_sum) +
+                                      (double)obj.kl_coef * s.kl_sum);
+        } else {
+            s.obj_sum = 0.0;
+        }
         out[r] = s;
     }
 }
@@ -547,24 +589,28 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
 // One block: thread i sums rows i, i+256, ... in order, then a fixed tree.
 __global__ __launch_bounds__(256) void chunk_stats_kernel(const grpo_stats* __restrict__ rows, int64_t n_rows,
                                                           grpo_stats* __restrict__ out) {
-    __shared__ double s_ls[256], s_es[256];
+    __shared__ double s_ls[256], s_es[256], s_ks[256], s_os[256];
     __shared__ long long s_nv[256], s_nc[256], s_nn[256], s_nr[256];
     const int i = threadIdx.x;
-    double ls = 0.0, es = 0.0;
+    double ls = 0.0, es = 0.0, ks = 0.0, os = 0.0;
     long long nv = 0, nc = 0, nn = 0, nr = 0;
     for (int64_t r = i; r < n_rows; r += 256) {
         ls += rows[r].loss_sum;
         es += rows[r].entropy_sum;
+        ks += rows[r].kl_sum;
+        os += rows[r].obj_sum;
         nv += rows[r].n_valid;
         nc += rows[r].n_clipped;
         nn += rows[r].n_nonfinite;
         nr += rows[r].n_valid_rows;
     }
-    s_ls[i] = ls; s_es[i] = es; s_nv[i] = nv; s_nc[i] = nc; s_nn[i] = nn; s_nr[i] = nr;
+    s_ls[i] = ls; s_es[i] = es; s_ks[i] = ks; s_os[i] = os;
+    s_nv[i] = nv; s_nc[i] = nc; s_nn[i] = nn; s_nr[i] = nr;
     __syncthreads();
     for (int h = 128; h > 0; h >>= 1) {
         if (i < h) {
             s_ls[i] += s_ls[i + h]; s_es[i] += s_es[i + h];
+            s_ks[i] += s_ks[i + h]; s_os[i] += s_os[i + h];
             s_nv[i] += s_nv[i + h]; s_nc[i] += s_nc[i + h];
             s_nn[i] += s_nn[i + h]; s_nr[i] += s_nr[i + h];
         }
@@ -574,12 +620,65 @@ __global__ __launch_bounds__(256) void chunk_stats_kernel(const grpo_stats* __re
         grpo_stats s;
         s.loss_sum = s_ls[0];
         s.entropy_sum = s_es[0];
+        s.kl_sum = s_ks[0];
+        s.obj_sum = s_os[0];
         s.n_valid = s_nv[0];
         s.n_clipped = s_nc[0];
         s.n_nonfinite = s_nn[0];
         s.n_valid_rows = s_nr[0];
         *out = s;
     }
+}
+
+// Valid tokens of rows: one wave per row (lanes stride the row's tokens).
+__device__ __forceinline__ long long row_valid_count(const uint8_t* __restrict__ mask,
+                                                     const int64_t* __restrict__ row_off, int64_t r, int64_t n_tok,
+                                                     int lane) {
+    int64_t b = row_off[r], e = row_off[r + 1];
+    b = b < 0 ? 0 : (b > n_tok ? n_tok : b);
+    e = e < b ? b : (e > n_tok ? n_tok : e);
+    long long c = 0;
+    for (int64_t t = b + lane; t < e; t += 64) c += mask[t] != 0;
+    return wave_sum_i(c);
+}
+
+// B = rows holding a valid token: one 1024-thread block, wave w takes rows
+// w, w+16, ..., fixed-order total.
+__global__ __launch_bounds__(1024) void count_rows_kernel(const uint8_t* __restrict__ mask,
+                                                          const int64_t* __restrict__ row_off, int64_t n_rows,
+                                                          int64_t n_tok, int64_t* __restrict__ out) {
+    __shared__ long long s_part[16];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    long long c = 0;
+    for (int64_t r = wave; r < n_rows; r += 16) c += row_valid_count(mask, row_off, r, n_tok, lane) > 0 ? 1 : 0;
+    if (lane == 0) s_part[wave] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        long long tot = 0;
+        for (int k = 0; k < 16; ++k) tot += s_part[k];
+        *out = tot;
+    }
+}
+
+// Per-row aggregation weights, one wave per row.
+__global__ __launch_bounds__(256) void row_weights_kernel(const uint8_t* __restrict__ mask,
+                                                          const int64_t* __restrict__ row_off, int64_t n_rows,
+                                                          int64_t n_tok, int mode, const int64_t* __restrict__ n_seq,
+                                                          float* __restrict__ w_row) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= n_rows) return;
+    if (mode == GRPO_AGG_TOKEN_MEAN) {
+        if (lane == 0) w_row[r] = 1.0f;
+        return;
+    }
+    const long long B = *n_seq > 1 ? *n_seq : 1;
+    if (mode == GRPO_AGG_SEQ_MEAN_TOKEN_SUM) {
+        if (lane == 0) w_row[r] = (float)(1.0 / (double)B);
+        return;
+    }
+    const long long L = row_valid_count(mask, row_off, r, n_tok, lane);
+    if (lane == 0) w_row[r] = L > 0 ? (float)(1.0 / ((double)B * (double)L)) : 0.0f;
 }
 
 // N = number of non-zero mask bytes; one 1024-thread block, 16-byte loads
@@ -694,13 +793,13 @@ int check_launch(hipError_t e, const char* what) {
 }  // namespace
 
 // Row stats then chunk stats for a chunk whose per-token outputs are written.
-int grpo::launch_stats(void* stream, const float* loss_tok, const float* entropy, const uint8_t* flags,
-                       const int64_t* row_off, int64_t n_rows, int64_t n_tok, grpo_stats* row_stats,
-                       grpo_stats* chunk_stats) {
+int grpo::launch_stats(void* stream, const float* loss_tok, const float* entropy, const float* kl_tok,
+                       const uint8_t* flags, const int64_t* row_off, int64_t n_rows, int64_t n_tok,
+                       const ObjTerms& obj, grpo_stats* row_stats, grpo_stats* chunk_stats) {
     hipStream_t st = (hipStream_t)stream;
     if (n_rows > 0) {
-        hipLaunchKernelGGL(row_stats_kernel, dim3((unsigned)n_rows), dim3(256), 0, st, loss_tok, entropy, flags,
-                           row_off, n_rows, n_tok, row_stats);
+        hipLaunchKernelGGL(row_stats_kernel, dim3((unsigned)n_rows), dim3(256), 0, st, loss_tok, entropy, kl_tok,
+                           flags, row_off, n_rows, n_tok, obj, row_stats);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return check_launch(e, "row stats");
     }
@@ -714,6 +813,28 @@ extern "C" int grpo_count_valid(void* stream, const uint8_t* mask, int64_t n_tok
     if (n_tok < 0 || !n_valid || (n_tok > 0 && !mask)) return fail(GRPO_EINVAL, "grpo_count_valid: bad arguments");
     hipLaunchKernelGGL(count_valid_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, mask, n_tok, n_valid);
     return check_launch(hipGetLastError(), "grpo_count_valid");
+}
+
+extern "C" int grpo_count_rows(void* stream, const uint8_t* mask, const int64_t* row_off, int64_t n_rows,
+                               int64_t n_tok, int64_t* n_seq) {
+    if (n_rows < 0 || n_tok < 0 || !n_seq || !row_off || (n_tok > 0 && !mask))
+        return fail(GRPO_EINVAL, "grpo_count_rows: bad arguments");
+    hipLaunchKernelGGL(count_rows_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, mask, row_off, n_rows, n_tok,
+                       n_seq);
+    return check_launch(hipGetLastError(), "grpo_count_rows");
+}
+
+extern "C" int grpo_row_weights(void* stream, const uint8_t* mask, const int64_t* row_off, int64_t n_rows,
+                                int64_t n_tok, int32_t mode, const int64_t* n_seq, float* w_row) {
+    if (mode != GRPO_AGG_TOKEN_MEAN && mode != GRPO_AGG_SEQ_MEAN_TOKEN_SUM && mode != GRPO_AGG_SEQ_MEAN_TOKEN_MEAN)
+        return fail(GRPO_EINVAL, "grpo_row_weights: unknown aggregation mode %d", mode);
+    if (n_rows < 0 || n_tok < 0 || (n_rows > 0 && (!row_off || !w_row || !n_seq)) || (n_tok > 0 && !mask))
+        return fail(GRPO_EINVAL, "grpo_row_weights: bad arguments");
+    if (n_rows > 0x7fffffffLL * 4) return fail(GRPO_EINVAL, "grpo_row_weights: too many rows for one launch");
+    if (n_rows == 0) return ok();
+    hipLaunchKernelGGL(row_weights_kernel, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, (hipStream_t)stream,
+                       mask, row_off, n_rows, n_tok, (int)mode, n_seq, w_row);
+    return check_launch(hipGetLastError(), "grpo_row_weights");
 }
 
 extern "C" int grpo_tok_row(void* stream, const int64_t* row_off, int64_t n_rows, int64_t n_tok, int32_t* tok_row) {
@@ -763,6 +884,11 @@ extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
     if (!(a->eps_low >= 0.0f && a->eps_low <= 1.0f && a->eps_high >= 0.0f && std::isfinite(a->eps_high)))
         return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: need 0 <= eps_low <= 1 and finite eps_high >= 0");
     if (!std::isfinite(a->scale)) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: scale must be finite");
+    {
+        const int rc = grpo::check_terms("grpo_loss_fwd_bwd", a->n_tok, a->ref_logp, a->kl_tok, a->ent_coef,
+                                         a->kl_coef, a->kl_type);
+        if (rc != GRPO_OK) return rc;
+    }
     const int in_b = di == GRPO_BF16 ? 2 : 4, out_b = dout == GRPO_BF16 ? 2 : 4;
     if (a->dlogits && a->n_tok > 0) {
         if (a->ld_out < a->V) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: ld_out < V");
@@ -779,6 +905,8 @@ extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
     p.eps_low = a->eps_low; p.eps_high = a->eps_high; p.scale = a->scale; p.denom = a->denom;
     p.dlogits = a->dlogits; p.ld_out = a->ld_out;
     p.logp = a->logp; p.lse = a->lse; p.entropy = a->entropy; p.loss_tok = a->loss_tok; p.tok_flags = a->tok_flags;
+    p.terms = grpo_dev::Terms{a->row_weight, a->ref_logp, a->ent_coef, a->kl_coef, a->kl_type};
+    p.kl_tok = a->ref_logp ? a->kl_tok : nullptr;
     const int vec = di == GRPO_BF16 ? 8 : 4;
     bool vec_ok = aligned16(a->logits) && a->ld % vec == 0 && a->V % vec == 0;
     if (a->dlogits) vec_ok = vec_ok && aligned16(a->dlogits) && (a->ld_out * out_b) % 16 == 0 && ((int64_t)vec * out_b) % 8 == 0;
@@ -789,6 +917,19 @@ extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
     else if (dout == GRPO_BF16) e = launch_tok<GRPO_F32, GRPO_BF16, true>(p, vec_ok, st);
     else e = launch_tok<GRPO_F32, GRPO_F32, true>(p, vec_ok, st);
     if (e != hipSuccess) return check_launch(e, "grpo_loss_fwd_bwd (token kernel)");
-    return grpo::launch_stats(stream, a->loss_tok, a->entropy, a->tok_flags, a->row_off, a->n_rows, a->n_tok,
-                              a->row_stats, a->chunk_stats);
+    const grpo::ObjTerms obj{a->scale, a->denom, a->row_weight, a->ent_coef, a->ref_logp ? a->kl_coef : 0.0f};
+    return grpo::launch_stats(stream, a->loss_tok, a->entropy, p.kl_tok, a->tok_flags, a->row_off, a->n_rows,
+                              a->n_tok, obj, a->row_stats, a->chunk_stats);
+}
+
+// Shared argument checks of the extra terms.
+int grpo::check_terms(const char* who, int64_t n_tok, const float* ref_logp, const float* kl_tok, float ent_coef,
+                      float kl_coef, int32_t kl_type) {
+    if (!std::isfinite(ent_coef) || !std::isfinite(kl_coef))
+        return fail(GRPO_EINVAL, "%s: ent_coef and kl_coef must be finite", who);
+    if (kl_coef != 0.0f && !ref_logp) return fail(GRPO_EINVAL, "%s: kl_coef needs ref_logp", who);
+    if (ref_logp && kl_type != GRPO_KL_K1 && kl_type != GRPO_KL_K2 && kl_type != GRPO_KL_K3)
+        return fail(GRPO_EINVAL, "%s: unknown kl_type %d", who, kl_type);
+    if (ref_logp && n_tok > 0 && !kl_tok) return fail(GRPO_EINVAL, "%s: ref_logp needs a kl_tok output", who);
+    return ok();
 }

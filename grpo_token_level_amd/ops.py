@@ -111,7 +111,7 @@ class Accumulator:
         C.check(C.lib().grpo_accum_init(ctypes.byref(self._a), n_micro))
 
     def add(self, stats):
-        s = C.Stats(**{k: stats[k] for k in STATS_DTYPE.names})
+        s = C.Stats(**{k: stats.get(k, 0) for k in STATS_DTYPE.names})
         code = C.lib().grpo_accum_add(ctypes.byref(self._a), ctypes.byref(s))
         if code == 0:
             return "OK"
@@ -185,6 +185,28 @@ def count_valid(mask, out=None):
     return out
 
 
+def count_rows(mask, row_off, out=None):
+    """Device int64 [1] tensor: rows holding a valid token (grpo_count_rows)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(1, dtype=torch.int64, device=mask.device)
+    C.check(C.lib().grpo_count_rows(_stream(), _dev(mask, "mask"), _dev(row_off, "row_off"), row_off.numel() - 1,
+                                    mask.numel(), _dev(out, "out")))
+    return out
+
+
+def row_weights(mask, row_off, mode, n_seq, out=None):
+    """Per-row float32 gradient factors of an aggregation mode (grpo_row_weights);
+    ``n_seq`` is the device int64 count from count_rows over the mini-batch."""
+    torch = _torch()
+    n_rows = row_off.numel() - 1
+    if out is None:
+        out = torch.empty(max(n_rows, 1), dtype=torch.float32, device=mask.device)
+    C.check(C.lib().grpo_row_weights(_stream(), _dev(mask, "mask"), _dev(row_off, "row_off"), n_rows, mask.numel(),
+                                     mode, _dev(n_seq, "n_seq"), _dev(out, "w_row")))
+    return out
+
+
 def tok_row(row_off, n_tok, out=None):
     torch = _torch()
     if out is None:
@@ -213,18 +235,32 @@ def loss_workspace(n_tok, n_rows, device):
     torch = _torch()
     f = dict(dtype=torch.float32, device=device)
     return {"logp": torch.empty(n_tok, **f), "lse": torch.empty(n_tok, **f), "entropy": torch.empty(n_tok, **f),
-            "loss_tok": torch.empty(n_tok, **f),
+            "loss_tok": torch.empty(n_tok, **f), "kl_tok": torch.empty(n_tok, **f),
             "tok_flags": torch.empty(n_tok, dtype=torch.uint8, device=device),
             "row_stats": torch.empty((max(n_rows, 1), STATS_BYTES), dtype=torch.uint8, device=device),
             "chunk_stats": torch.empty((1, STATS_BYTES), dtype=torch.uint8, device=device)}
 
 
+def _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws):
+    for name, t in (("row_weight", row_weight), ("ref_logp", ref_logp)):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (libgrpo has no CPU path)")
+    a.row_weight = row_weight.data_ptr() if row_weight is not None else None
+    a.ref_logp = ref_logp.data_ptr() if ref_logp is not None else None
+    a.kl_tok = ws["kl_tok"].data_ptr() if ref_logp is not None else None
+    a.ent_coef, a.kl_coef, a.kl_type = ent_coef, kl_coef, kl_type
+
+
 def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, scale=1.0, denom=None,
-                 eps_low=0.2, eps_high=0.2, dlogits="new", out_dtype=None, ws=None):
+                 eps_low=0.2, eps_high=0.2, dlogits="new", out_dtype=None, ws=None, row_weight=None,
+                 ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3):
     """Fused GRPO loss forward/backward over one chunk (grpo_loss_fwd_bwd).
 
     ``dlogits``: "new" (allocate, dtype ``out_dtype`` or the logits dtype),
     "inplace" (overwrite ``logits``), None (no gradient), or a tensor.
+    ``row_weight`` / ``ref_logp`` / ``ent_coef`` / ``kl_coef`` / ``kl_type``:
+    the aggregation weights and extra terms (``ws["kl_tok"]`` receives the
+    per-token KL when ``ref_logp`` is given).
     Returns the workspace dict with ``dlogits`` added."""
     torch = _torch()
     ld = _rows2d(logits, "logits")
@@ -265,6 +301,7 @@ def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, 
                     ("tok_row", tok_row_), ("adv_row", adv_row), ("row_off", row_off)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor (libgrpo has no CPU path)")
+    _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws)
     C.check(C.lib().grpo_loss_fwd_bwd(_stream(), ctypes.byref(a)))
     ws["dlogits"] = dl
     return ws
@@ -288,7 +325,8 @@ def lmhead_workspace_bytes(n_tok, H, V):
 
 
 def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off, dW, *, scale=1.0, denom=None,
-                   eps_low=0.2, eps_high=0.2, dh=None, ws=None, workspace=None):
+                   eps_low=0.2, eps_high=0.2, dh=None, ws=None, workspace=None, row_weight=None,
+                   ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3):
     """Fused LM-head GRPO loss over one chunk (grpo_lmhead_fwd_bwd).
 
     ``dW`` (fp32 [V x H]) is accumulated into; ``dh`` (fp32 [n_tok x H]) is
@@ -329,6 +367,7 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
         setattr(a, k, t.data_ptr() if t is not None else None)
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel()
+    _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws)
     C.check(C.lib().grpo_lmhead_fwd_bwd(_stream(), ctypes.byref(a)))
     ws["dh"] = dh
     ws["workspace"] = workspace

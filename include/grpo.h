@@ -50,6 +50,23 @@ extern "C" {
 
 typedef enum grpo_dtype { GRPO_F32 = 0, GRPO_BF16 = 1 } grpo_dtype;
 
+/* Per-token KL estimators against a reference policy, d = ref_logp - logp
+ * (the pages name a KL loss but no estimator): k1 = -d, k2 = d^2/2,
+ * k3 = e^d - d - 1 (non-negative); no clamp. */
+#define GRPO_KL_K1 1
+#define GRPO_KL_K2 2
+#define GRPO_KL_K3 3
+
+/* Loss-aggregation modes ([P3] section 5: token-mean over the global valid
+ * token count N, sequence-level modes over the global batch size B):
+ *   token-mean           L = sum_t l_t / N
+ *   seq-mean-token-sum   L = sum_r sum_{t in r} l_t / B
+ *   seq-mean-token-mean  L = sum_r (sum_{t in r} l_t / L_r) / B
+ * with L_r the valid tokens of row r and B the rows holding a valid token. */
+#define GRPO_AGG_TOKEN_MEAN 0
+#define GRPO_AGG_SEQ_MEAN_TOKEN_SUM 1
+#define GRPO_AGG_SEQ_MEAN_TOKEN_MEAN 2
+
 /* Sums over a row or a chunk.  [P1] "Metric roll-up: token-weighted, not
  * averaged": losses are carried as sums with their token counts so that the
  * step loss is sum(loss_sum) / sum(n_valid); counts sum.  n_valid is the
@@ -59,6 +76,9 @@ typedef enum grpo_dtype { GRPO_F32 = 0, GRPO_BF16 = 1 } grpo_dtype;
 typedef struct grpo_stats {
     double  loss_sum;      /* sum over valid tokens of the per-token loss */
     double  entropy_sum;   /* sum over valid tokens of the entropy (nats) */
+    double  kl_sum;        /* sum over valid tokens of the KL estimate (0 without a reference) */
+    double  obj_sum;       /* sum over valid tokens of s_t (l_t - ent_coef H_t + kl_coef KL_t): the
+                              objective whose gradient the chunk wrote (s_t = the token's factor) */
     int64_t n_valid;       /* valid (mask = 1) tokens */
     int64_t n_clipped;     /* valid tokens whose gradient the clip removed */
     int64_t n_nonfinite;   /* valid tokens with a non-finite log-prob, loss or entropy */
@@ -149,6 +169,24 @@ int grpo_rows_advantage(const float* adv_rollout, int64_t n_rollouts,
  * mask; [P4] item 1: padding counts 0).  Overwrites *n_valid. */
 int grpo_count_valid(void* stream, const uint8_t* mask, int64_t n_tok, int64_t* n_valid);
 
+/* device.  *n_seq (device int64) = number of rows r holding at least one
+ * mask-1 token in [row_off[r], row_off[r+1]): B, the sequence count of the
+ * seq-level aggregation modes ([P3] section 5: they divide by the global
+ * batch size; masked padding rows, [P4] "Why the row count does not change
+ * the math", do not count).  row_off: device int64 [n_rows + 1],
+ * non-decreasing, within [0, n_tok].  Overwrites *n_seq. */
+int grpo_count_rows(void* stream, const uint8_t* mask, const int64_t* row_off, int64_t n_rows, int64_t n_tok,
+                    int64_t* n_seq);
+
+/* device.  Per-row gradient factors of an aggregation mode (GRPO_AGG_*),
+ * for grpo_loss_args.row_weight: token-mean 1 (the 1/N goes in scale or
+ * denom); seq-mean-token-sum 1/max(B, 1); seq-mean-token-mean
+ * 1/(max(B, 1) * L_r), 0 for a row without valid tokens.  B = *n_seq (device
+ * int64, grpo_count_rows over the whole mini-batch); L_r counted from mask
+ * over [row_off[r], row_off[r+1]).  w_row: device float [n_rows]. */
+int grpo_row_weights(void* stream, const uint8_t* mask, const int64_t* row_off, int64_t n_rows, int64_t n_tok,
+                     int32_t mode, const int64_t* n_seq, float* w_row);
+
 /* device.  tok_row[t] = the row r with row_off[r] <= t < row_off[r+1]
  * (row_off: device int64 [n_rows + 1], non-decreasing), or -1 if none. */
 int grpo_tok_row(void* stream, const int64_t* row_off, int64_t n_rows, int64_t n_tok, int32_t* tok_row);
@@ -196,6 +234,14 @@ typedef struct grpo_loss_args {
     uint8_t* tok_flags;         /* [n_tok] required: bit0 valid, bit1 clipped, bit2 non-finite */
     grpo_stats* row_stats;      /* [n_rows] required */
     grpo_stats* chunk_stats;    /* [1] required: rows summed in row order */
+    /* Extra terms ([P3] section 5: the policy, entropy and KL losses share one aggregation). */
+    const float* row_weight;    /* NULL (all 1) or [n_rows]: per-row factor of the token's gradient */
+    const float* ref_logp;      /* NULL or [n_tok]: reference-policy log-probs (KL term) */
+    float* kl_tok;              /* [n_tok], required when ref_logp is set: per-token KL estimate */
+    float ent_coef;             /* entropy bonus: the token's objective gains -ent_coef * H */
+    float kl_coef;              /* KL weight: the token's objective gains +kl_coef * KL (needs ref_logp) */
+    int32_t kl_type;            /* GRPO_KL_K1 / K2 / K3 (read when ref_logp is set) */
+    int32_t reserved2;          /* 0 */
 } grpo_loss_args;
 
 /* device.  Fused forward and backward of the token-level GRPO loss over one
@@ -205,8 +251,12 @@ typedef struct grpo_loss_args {
  *   rho = exp(logp - old_logp), A = adv_row[tok_row[t]],
  *   l = -min(rho*A, clip(rho, 1-eps_low, 1+eps_high)*A),
  *   g = 0 if (A > 0 and rho > 1+eps_high) or (A < 0 and rho < 1-eps_low) else 1,
- *   coef = s * A * rho * g with s = scale (/ max(*denom, 1) when denom is set),
- *   dlogits_v = coef * (p_v - [v == y]).
+ *   s = scale (/ max(*denom, 1) when denom is set) (* row_weight[row] when set),
+ *   KL, dKL/dlogp from ref_logp (GRPO_KL_*; 0 without ref_logp),
+ *   coef = s * (A * rho * g - kl_coef * dKL/dlogp),
+ *   dlogits_v = coef * (p_v - [v == y]) + ent_coef * s * p_v * (z_v - lse + H),
+ * the gradient of the token's objective s * (l - ent_coef * H + kl_coef * KL)
+ * (with ent_coef = kl_coef = 0 and no row weights: coef * (p_v - [v == y])).
  * Mask-0 tokens: outputs 0 and a zero dlogits row.
  * [P1] "The hard part: deferred normalization" (token mean over N; chunk
  * gradients add up to the step gradient, so scale = 1/N on every chunk makes
@@ -259,6 +309,13 @@ typedef struct grpo_lmhead_args {
     grpo_stats* chunk_stats;    /* [1] required */
     void* workspace;            /* >= grpo_lmhead_workspace_size(n_tok, H, V) bytes, 16-byte aligned */
     size_t workspace_bytes;
+    const float* row_weight;    /* extra terms exactly as in grpo_loss_args */
+    const float* ref_logp;
+    float* kl_tok;
+    float ent_coef;
+    float kl_coef;
+    int32_t kl_type;
+    int32_t reserved2;
 } grpo_lmhead_args;
 
 /* host.  Workspace bytes grpo_lmhead_fwd_bwd needs for a chunk of n_tok tokens:
@@ -302,6 +359,10 @@ typedef struct grpo_accum {
 typedef struct grpo_step_result {
     double  loss;          /* sum(loss_sum) / max(N, 1) */
     double  entropy;       /* sum(entropy_sum) / max(N, 1) */
+    double  kl;            /* sum(kl_sum) / max(N, 1) */
+    double  obj_sum;       /* sum(obj_sum): the step objective when the chunks carried the
+                              normalisation (global N or row weights); times grad_scale in
+                              the deferred token-mean mode (scale = 1) */
     double  grad_scale;    /* 1 / max(N, 1): apply to gradients accumulated with scale = 1 */
     int64_t n_valid;       /* N */
     int64_t n_valid_rows;

@@ -17,7 +17,7 @@ Sources (cited by title and section in every function):
 * [P2] "03 Data Protocol and Batch Lifecycle" -- verl source reading, field
   lifecycle of one GRPO update.
 * [P3] "22 - mini-batch, micro-batch and dynamic batch size" -- verl article on
-  the three batch levels and loss normalisation.
+  the three batch levels, loss normalisation and the aggregation modes.
 * [P4] "How a context-compaction step fits a variable number of rows into one
   batch" -- NeMo-RL context-compaction explainer.
 
@@ -35,7 +35,10 @@ from .plans import (PlanError, plan_fixed, chunk_rows, train_calls,
                     plan_dynamic, plan_compaction, compaction_micro_chunks)
 from .advantage import group_advantage, rows_advantage
 from .loss import (round_to_bf16, token_forward, surrogate, loss_fwd_bwd,
-                   logprob_fwd, chunk_stats, row_stats, valid_count)
+                   logprob_fwd, chunk_stats, row_stats, valid_count, kl_term,
+                   KL_K1, KL_K2, KL_K3, STAT_KEYS)
+from .agg import (AGG_TOKEN_MEAN, AGG_SEQ_MEAN_TOKEN_SUM, AGG_SEQ_MEAN_TOKEN_MEAN,
+                  row_valid_counts, count_rows, agg_loss, row_weights)
 from .accum import Accumulator, ACC_OK, ACC_NONFINITE, ACC_SKIPPED
 from .lmhead import lmhead_fwd_bwd
 
@@ -45,4 +48,7 @@ __all__ = [
     "rows_advantage", "round_to_bf16", "token_forward", "surrogate",
     "loss_fwd_bwd", "logprob_fwd", "chunk_stats", "row_stats", "valid_count",
     "Accumulator", "ACC_OK", "ACC_NONFINITE", "ACC_SKIPPED", "lmhead_fwd_bwd",
+    "kl_term", "KL_K1", "KL_K2", "KL_K3", "STAT_KEYS", "AGG_TOKEN_MEAN",
+    "AGG_SEQ_MEAN_TOKEN_SUM", "AGG_SEQ_MEAN_TOKEN_MEAN", "row_valid_counts",
+    "count_rows", "agg_loss", "row_weights",
 ]

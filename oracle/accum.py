@@ -9,7 +9,8 @@ ACC_NONFINITE = "NONFINITE"
 ACC_SKIPPED = "SKIPPED"
 ACC_STATE = "STATE"      # a completed window was not finalized before the next add
 
-_KEYS = ("loss_sum", "entropy_sum", "n_valid", "n_clipped", "n_valid_rows")
+_KEYS = ("loss_sum", "entropy_sum", "kl_sum", "obj_sum", "n_valid", "n_clipped", "n_valid_rows")
+_FLOAT_KEYS = ("loss_sum", "entropy_sum", "kl_sum", "obj_sum")
 
 
 class Accumulator:
@@ -26,8 +27,9 @@ class Accumulator:
     whole mini-batch is abandoned, not only the chunk.
 
     Reading: a chunk is non-finite when any valid token was (n_nonfinite > 0)
-    or its loss or entropy sum is not finite.  With an empty step
-    (sum of divisors 0) the loss is 0 and the gradient scale is 1.
+    or one of its loss, entropy, KL or objective sums is not finite.  With an
+    empty step (sum of divisors 0) the loss is 0 and the gradient scale is 1.
+    Stats dicts without ``kl_sum`` / ``obj_sum`` count them as 0.
     """
 
     def __init__(self, n_micro):
@@ -45,15 +47,14 @@ class Accumulator:
         if self.skip > 0:
             self.skip -= 1
             return ACC_SKIPPED
-        bad = (stats["n_nonfinite"] > 0 or not math.isfinite(stats["loss_sum"])
-               or not math.isfinite(stats["entropy_sum"]))
+        bad = stats["n_nonfinite"] > 0 or not all(math.isfinite(stats.get(k, 0.0)) for k in _FLOAT_KEYS)
         if bad:
             self.skip = self.n_micro - 1 - self.pos
             self.pos = 0
             self.sums = {k: 0 for k in _KEYS}
             return ACC_NONFINITE
         for k in _KEYS:
-            self.sums[k] += stats[k]
+            self.sums[k] += stats.get(k, 0)
         self.pos += 1
         if self.pos == self.n_micro:
             self.done = dict(self.sums)
@@ -63,8 +64,11 @@ class Accumulator:
 
     def finalize(self):
         """Close a completed window.  Returns ``None`` when no window is complete,
-        else a dict with the step loss, counts, mean entropy and the gradient
-        scale 1/max(N, 1)."""
+        else a dict with the step loss, counts, mean entropy and KL per valid
+        token, the gradient scale 1/max(N, 1) and ``obj_sum``, the window's sum
+        of the chunks' objective shares (the step objective itself when the
+        chunks carried the normalisation; times grad_scale in the deferred
+        token-mean mode)."""
         if self.done is None:
             return None
         d = self.done
@@ -72,4 +76,5 @@ class Accumulator:
         denom = max(d["n_valid"], 1)
         return {"loss": d["loss_sum"] / denom, "n_valid": d["n_valid"],
                 "n_valid_rows": d["n_valid_rows"], "n_clipped": d["n_clipped"],
-                "entropy": d["entropy_sum"] / denom, "grad_scale": 1.0 / denom}
+                "entropy": d["entropy_sum"] / denom, "kl": d["kl_sum"] / denom,
+                "obj_sum": d["obj_sum"], "grad_scale": 1.0 / denom}

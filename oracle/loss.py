@@ -94,8 +94,40 @@ def surrogate(logp, old_logp, A, eps_low, eps_high):
     return l, g, rho
 
 
+KL_K1, KL_K2, KL_K3 = 1, 2, 3
+
+
+def kl_term(logp, ref_logp, kind):
+    """Per-token estimate of KL(current || reference) from the sampled
+    token's two log-probs, and its derivative with respect to logp.
+
+    [P2] "Field Lineage": the reference worker writes ref_log_prob next to the
+    old log-probs.  [P3] section 5: the KL loss is aggregated like the policy
+    loss.
+
+    Reading (the pages name a KL loss but print no estimator): with
+    d = ref_logp - logp,
+      k1: KL = -d,             dKL/dlogp = 1
+      k2: KL = d^2 / 2,        dKL/dlogp = -d
+      k3: KL = e^d - d - 1,    dKL/dlogp = 1 - e^d
+    with no clamp (an overflow makes the token non-finite, as for the ratio).
+    Returns ``(KL, dKL/dlogp)``.
+    """
+    d = float(ref_logp) - float(logp)
+    if kind == KL_K1:
+        return -d, 1.0
+    if kind == KL_K2:
+        return 0.5 * d * d, -d
+    if kind == KL_K3:
+        with np.errstate(over="ignore"):
+            ed = float(np.exp(np.float64(d)))
+        return ed - d - 1.0, 1.0 - ed
+    raise ValueError(f"unknown KL estimator {kind}")
+
+
 def loss_fwd_bwd(logits, target, mask, old_logp, adv_tok, scale,
-                 eps_low=0.2, eps_high=0.2, want_dz=True):
+                 eps_low=0.2, eps_high=0.2, want_dz=True, w_tok=None,
+                 ent_coef=0.0, kl_coef=0.0, ref_logp=None, kl_type=KL_K3):
     """Fused forward and backward of the token-level GRPO loss over one chunk.
 
     ``logits`` [n_tok, V] (read as float64), ``target`` [n_tok] int,
@@ -115,13 +147,24 @@ def loss_fwd_bwd(logits, target, mask, old_logp, adv_tok, scale,
     (``surrogate``); coef = scale * A * rho * g; dz_v = coef * (p_v - [v == y]),
     which is d(scale * l)/dz_v.  Masked tokens: every output 0 and dz = 0.
 
+    Extra terms ([P3] section 5: the policy, entropy and KL losses share one
+    aggregation).  ``w_tok`` [n_tok] (default 1) multiplies each token's
+    factor, s_t = scale * w_tok[t] (the aggregation-mode weight of the token's
+    row, ``agg.row_weights``).  The token's objective is
+      obj_t = s_t * (l_t - ent_coef * H_t + kl_coef * KL_t)
+    (entropy as a bonus, KL from ``kl_term`` against ``ref_logp``), and dz is
+    its gradient:
+      dz_v = coef_t (p_v - [v == y]) + ent_coef s_t p_v (z_v - lse + H_t),
+      coef_t = s_t (A rho g - kl_coef dKL/dlogp),
+    using dlogp/dz_v = [v == y] - p_v and dH/dz_v = -p_v (z_v - lse + H).
+
     Returns a dict of float64 arrays: ``logp``, ``lse``, ``entropy``,
-    ``loss_tok``, ``coef``, ``clipped`` (bool, g == 0), ``valid`` (bool),
-    ``nonfinite`` (bool) and ``dz`` ([n_tok, V] or None).
+    ``loss_tok``, ``kl``, ``obj``, ``coef``, ``clipped`` (bool, g == 0),
+    ``valid`` (bool), ``nonfinite`` (bool) and ``dz`` ([n_tok, V] or None).
     """
     logits = np.asarray(logits)
     n, V = logits.shape
-    out = {k: np.zeros(n, dtype=np.float64) for k in ("logp", "lse", "entropy", "loss_tok", "coef")}
+    out = {k: np.zeros(n, dtype=np.float64) for k in ("logp", "lse", "entropy", "loss_tok", "kl", "obj", "coef")}
     out["clipped"] = np.zeros(n, dtype=bool)
     out["valid"] = np.zeros(n, dtype=bool)
     out["nonfinite"] = np.zeros(n, dtype=bool)
@@ -135,16 +178,24 @@ def loss_fwd_bwd(logits, target, mask, old_logp, adv_tok, scale,
         lse, logp, H, p = token_forward(z, y)
         A = float(adv_tok[t])
         l, g, rho = surrogate(logp, float(old_logp[t]), A, eps_low, eps_high)
-        coef = scale * A * rho * g
+        s = scale * (1.0 if w_tok is None else float(w_tok[t]))
+        kl, dkl = (0.0, 0.0) if ref_logp is None else kl_term(logp, float(ref_logp[t]), kl_type)
+        coef = s * (A * rho * g - kl_coef * dkl)
         out["logp"][t] = logp
         out["lse"][t] = lse
         out["entropy"][t] = H
         out["loss_tok"][t] = l
+        out["kl"][t] = kl
+        out["obj"][t] = s * (l - ent_coef * H + kl_coef * kl)
         out["coef"][t] = coef
         out["clipped"][t] = (g == 0)
-        out["nonfinite"][t] = not (math.isfinite(logp) and math.isfinite(l) and math.isfinite(H))
+        out["nonfinite"][t] = not (math.isfinite(logp) and math.isfinite(l) and math.isfinite(H)
+                                   and math.isfinite(kl))
         if want_dz:
             row = coef * p
+            if ent_coef != 0.0:
+                with np.errstate(invalid="ignore"):
+                    row = row + np.where(p > 0.0, ent_coef * s * p * (z - lse + H), 0.0)
             if 0 <= y < V:
                 row[y] -= coef
             dz[t] = row
@@ -191,14 +242,19 @@ def valid_count(mask):
     return n
 
 
+STAT_KEYS = ("loss_sum", "entropy_sum", "kl_sum", "obj_sum", "n_valid", "n_clipped", "n_nonfinite",
+             "n_valid_rows")
+
+
 def _stats_over(out, idx):
-    s = {"loss_sum": 0.0, "entropy_sum": 0.0, "n_valid": 0, "n_clipped": 0,
-         "n_nonfinite": 0, "n_valid_rows": 0}
+    s = {k: 0.0 if k.endswith("_sum") else 0 for k in STAT_KEYS}
     for t in idx:
         if not out["valid"][t]:
             continue
         s["loss_sum"] += float(out["loss_tok"][t])
         s["entropy_sum"] += float(out["entropy"][t])
+        s["kl_sum"] += float(out["kl"][t]) if "kl" in out else 0.0
+        s["obj_sum"] += float(out["obj"][t]) if "obj" in out else 0.0
         s["n_valid"] += 1
         s["n_clipped"] += 1 if out["clipped"][t] else 0
         s["n_nonfinite"] += 1 if out["nonfinite"][t] else 0
@@ -207,7 +263,7 @@ def _stats_over(out, idx):
 
 
 def row_stats(out, row_off):
-    """Per-row sums of loss and entropy and counts, tokens of row r being
+    """Per-row sums of loss, entropy, KL and objective and counts, tokens of row r being
     ``row_off[r]:row_off[r+1]``; ``n_valid_rows`` is 1 for a row holding a
     valid token.
 
@@ -222,14 +278,14 @@ def row_stats(out, row_off):
 
 def chunk_stats(out, row_off):
     """Chunk totals, summed over the rows in row order: loss_sum,
-    entropy_sum, n_valid (the chunk's divisor), n_clipped, n_nonfinite,
+    entropy_sum, kl_sum, obj_sum (the chunk's share of the aggregated
+    objective), n_valid (the chunk's divisor), n_clipped, n_nonfinite,
     n_valid_rows.  The reported chunk loss is loss_sum / max(n_valid, 1).
 
     [P1] "The hard part: deferred normalization" (the objective reports the
     divisor it used) and "Metric roll-up".
     """
-    tot = {"loss_sum": 0.0, "entropy_sum": 0.0, "n_valid": 0, "n_clipped": 0,
-           "n_nonfinite": 0, "n_valid_rows": 0}
+    tot = {k: 0.0 if k.endswith("_sum") else 0 for k in STAT_KEYS}
     for r in row_stats(out, row_off):
         for k in tot:
             tot[k] += r[k]

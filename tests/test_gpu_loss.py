@@ -117,7 +117,8 @@ def test_bad_targets_and_nan_logits_are_flagged_not_read():
     assert chunk["n_nonfinite"] == 3
     acc = ops.Accumulator(2)
     assert acc.add(chunk) == "NONFINITE"          # window of 2 poisoned at position 0
-    clean = dict(chunk, n_nonfinite=0, loss_sum=1.0, entropy_sum=1.0)
+    assert not np.isfinite(chunk["obj_sum"])       # the objective share carries the NaN too
+    clean = dict(chunk, n_nonfinite=0, loss_sum=1.0, entropy_sum=1.0, obj_sum=1.0)
     assert acc.add(clean) == "SKIPPED"            # the rest of the poisoned window
     assert acc.add(clean) == "OK"                 # a fresh window
 

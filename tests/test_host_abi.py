@@ -57,6 +57,10 @@ int main(void) {
   F(grpo_loss_args, logits) F(grpo_loss_args, n_rows) F(grpo_loss_args, eps_low) F(grpo_loss_args, denom)
   F(grpo_loss_args, dlogits) F(grpo_loss_args, chunk_stats) F(grpo_accum, open) F(grpo_accum, closed)
   F(grpo_lmhead_args, Wt) F(grpo_lmhead_args, n_rows) F(grpo_lmhead_args, denom) F(grpo_lmhead_args, workspace_bytes)
+  F(grpo_loss_args, row_weight) F(grpo_loss_args, kl_tok) F(grpo_loss_args, kl_type)
+  F(grpo_lmhead_args, row_weight) F(grpo_lmhead_args, ent_coef) F(grpo_lmhead_args, kl_type)
+  F(grpo_stats, kl_sum) F(grpo_stats, obj_sum) F(grpo_stats, n_valid_rows)
+  F(grpo_step_result, kl) F(grpo_step_result, obj_sum) F(grpo_step_result, n_clipped)
   return 0;
 }
 ''')
@@ -71,7 +75,8 @@ int main(void) {
     for key, v in got.items():
         if "." in key:
             struct, field = key.split(".")
-            cls = {"grpo_loss_args": C.LossArgs, "grpo_accum": C.Accum, "grpo_lmhead_args": C.LmheadArgs}[struct]
+            cls = {"grpo_loss_args": C.LossArgs, "grpo_accum": C.Accum, "grpo_lmhead_args": C.LmheadArgs,
+                   "grpo_stats": C.Stats, "grpo_step_result": C.StepResult}[struct]
             assert getattr(cls, field).offset == int(v), key
 
 
@@ -210,7 +215,9 @@ def test_accumulator_matches_oracle_on_random_sequences():
                 continue
             bad = rng.random() < 0.15
             st = {"loss_sum": float("nan") if bad and rng.random() < 0.5 else float(rng.normal()),
-                  "entropy_sum": float(rng.random()), "n_valid": int(rng.integers(0, 50)),
+                  "entropy_sum": float(rng.random()), "kl_sum": float(rng.random()),
+                  "obj_sum": float("inf") if bad and rng.random() < 0.3 else float(rng.normal()),
+                  "n_valid": int(rng.integers(0, 50)),
                   "n_clipped": int(rng.integers(0, 3)), "n_nonfinite": 1 if bad else 0,
                   "n_valid_rows": int(rng.integers(0, 4))}
             assert b.add(st) == a.add(st)

@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle sample (0 disables the cpu_baseline leg)")
+    ap.add_argument("--terms", action="store_true",
+                    help="padded workloads: seq-mean-token-mean aggregation with an entropy bonus (0.01) and a k3 "
+                         "KL term (0.05) against a reference log-prob (the step's extra-term variant)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     return ap.parse_args()
@@ -101,20 +104,26 @@ class Timed:
 
 # ---------------------------------------------------------------- padded / dynamic: fused loss
 
-def chunk_bytes(mask_np, V, b_in, b_out):
+def chunk_bytes(mask_np, V, b_in, b_out, extra_per_valid=0):
     """Algorithmic bytes of one fused launch: valid tokens read V*b_in and write
-    V*b_out, masked tokens write V*b_out (zeros), plus the per-token scalars."""
+    V*b_out, masked tokens write V*b_out (zeros), plus the per-token scalars
+    (``extra_per_valid``: the reference log-prob read and KL write of the
+    extra-term variant)."""
     nv = int(mask_np.sum())
     nm = len(mask_np) - nv
-    return nv * (V * (b_in + b_out) + PER_TOKEN_SCALAR_READ) + nm * V * b_out + len(mask_np) * PER_TOKEN_SCALAR_ALL
+    return (nv * (V * (b_in + b_out) + PER_TOKEN_SCALAR_READ + extra_per_valid) + nm * V * b_out
+            + len(mask_np) * PER_TOKEN_SCALAR_ALL)
 
 
 class PaddedStep:
     """Fixed-plan step over a right-padded batch."""
 
-    def __init__(self, wl, seed, torch, ops, timed):
+    ENT_COEF, KL_COEF = 0.01, 0.05
+
+    def __init__(self, wl, seed, torch, ops, timed, terms=False):
         from synth import fill_normal_rows, padded_batch
         self.torch, self.ops, self.timed = torch, ops, timed
+        self.terms = terms
         b = self.b = padded_batch(wl, seed=seed)
         n_rows, T, V = b["n_rows"], b["T"], b["V"]
         self.dt = torch.bfloat16 if b["dtype"] == "bf16" else torch.float32
@@ -127,10 +136,16 @@ class PaddedStep:
         # perturbation that stands in for the policy having moved since rollout
         logp, _, _ = ops.logprob_fwd(self.logits, self.target, self.mask, want_lse=False, want_entropy=False)
         self.old = (logp.double() + _g(torch, b["logratio_noise"])).float()
+        if terms:
+            # a reference policy a little further away: old log-probs plus the same noise again
+            self.ref = (self.old.double() + _g(torch, b["logratio_noise"])).float()
         del logp
         self.dlogits = torch.empty_like(self.logits)
         n_mini, n_micro, mini_rows, micro_rows = ops.plan_fixed(n_rows, b["group"], b["mini"], b["micro"])
         self.row_off = torch.arange(0, micro_rows * T + 1, T, dtype=torch.int64, device="cuda")
+        self.mini_off = torch.arange(0, mini_rows * T + 1, T, dtype=torch.int64, device="cuda")
+        self.n_seq = torch.empty(n_mini, dtype=torch.int64, device="cuda")
+        self.w_row = torch.empty(n_rows, dtype=torch.float32, device="cuda")
         self.tok_row = ops.tok_row(self.row_off, micro_rows * T)
         self.ws = ops.loss_workspace(micro_rows * T, micro_rows, "cuda")
         self.N = torch.empty(n_mini, dtype=torch.int64, device="cuda")
@@ -143,7 +158,7 @@ class PaddedStep:
         for i in range(n_mini):
             for j in range(n_micro):
                 a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
-                self.chunk_units[(i, j)] = chunk_bytes(b["mask"][a * T:e * T], V, b_in, b_in)
+                self.chunk_units[(i, j)] = chunk_bytes(b["mask"][a * T:e * T], V, b_in, b_in, 8 if terms else 0)
         self.n_valid = int(np.sum(b["mask"]))
         self.logits_dtype = "bf16" if b_in == 2 else "fp32"
 
@@ -155,15 +170,25 @@ class PaddedStep:
         self.adv_dev.copy_(self.adv_host, non_blocking=True)
         k = 0
         for i in range(n_mini):
-            ops.count_valid(self.mask[i * mini_rows * T:(i + 1) * mini_rows * T], out=self.N[i:i + 1])
+            mini_mask = self.mask[i * mini_rows * T:(i + 1) * mini_rows * T]
+            ops.count_valid(mini_mask, out=self.N[i:i + 1])
+            if self.terms:
+                ops.count_rows(mini_mask, self.mini_off, out=self.n_seq[i:i + 1])
+                ops.row_weights(mini_mask, self.mini_off, ops.C.AGG_SEQ_MEAN_TOKEN_MEAN, self.n_seq[i:i + 1],
+                                out=self.w_row[i * mini_rows:(i + 1) * mini_rows])
             for j in range(n_micro):
                 a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
                 t0, t1 = a * T, e * T
                 self.ws["chunk_stats"] = self.stats_dev[k:k + 1]
+                if self.terms:
+                    kw = dict(scale=1.0, row_weight=self.w_row[a:e], ref_logp=self.ref[t0:t1],
+                              ent_coef=self.ENT_COEF, kl_coef=self.KL_COEF, kl_type=ops.C.KL_K3)
+                else:
+                    kw = dict(scale=1.0, denom=self.N[i:i + 1])
                 ev = self.timed.begin()
                 ops.loss_fwd_bwd(self.logits[t0:t1], self.target[t0:t1], self.mask[t0:t1], self.old[t0:t1],
-                                 self.tok_row, self.adv_dev[a:e], self.row_off, scale=1.0, denom=self.N[i:i + 1],
-                                 dlogits=self.dlogits[t0:t1], ws=self.ws)
+                                 self.tok_row, self.adv_dev[a:e], self.row_off, dlogits=self.dlogits[t0:t1],
+                                 ws=self.ws, **kw)
                 self.timed.end(ev, self.chunk_units[(i, j)])
                 k += 1
         self.stats_host.copy_(self.stats_dev, non_blocking=True)
@@ -417,7 +442,10 @@ def main():
     timed = Timed(torch)
     cls = {"qwen": PaddedStep, "long": PaddedStep, "tiny": PaddedStep, "dynamic": DynamicStep,
            "compact": CompactStep}[wl]
-    step = cls(wl, args.seed, torch, ops, timed)
+    if args.terms and cls is not PaddedStep:
+        print("--terms applies to the padded workloads (qwen, long, tiny)", file=sys.stderr)
+        sys.exit(2)
+    step = cls(wl, args.seed, torch, ops, timed, terms=True) if args.terms else cls(wl, args.seed, torch, ops, timed)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -430,9 +458,13 @@ def main():
     ms = 1e3 * wall / args.steps
     value = step.n_valid / (wall / args.steps)
     tot_ms, units, launches = timed.totals()
-    cfg = {"workload": f"{wl}: {WORKLOAD_TEXT[wl]}", "logits_dtype": step.logits_dtype,
+    cfg = {"workload": f"{wl}: {WORKLOAD_TEXT[wl]}"
+                       + ("; seq-mean-token-mean aggregation, entropy bonus 0.01, k3 KL 0.05" if args.terms else ""),
+           "logits_dtype": step.logits_dtype,
            "valid_tokens": step.n_valid, "launches_per_step": launches // args.steps,
            "step_loss": res[0]["loss"] if res and res[0] else None}
+    if args.terms and res and res[0]:
+        cfg["step_objective"] = res[0]["obj_sum"]
     if wl == "compact":
         achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -446,7 +478,7 @@ def main():
                 "kernel": "tok_reg_kernel (fused loss fwd+bwd) + row/chunk stats, per chunk launch",
                 "algorithmic_bytes_per_launch": int(units // launches), "avg_launch_ms": round(tot_ms / launches, 4)}
         roof["device_copy_GBs"] = round(step.copy_context(), 1)
-        if wl == "qwen":
+        if wl == "qwen" and not args.terms:
             from grpo_token_level_amd.prof_summary import load_traffic
             rec = load_traffic(os.path.join(ROOT, "profiles", "fused_loss_qwen_pmc.txt"))
             if rec is not None:

@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--terms", action="store_true",
                     help="padded workloads: seq-mean-token-mean aggregation with an entropy bonus (0.01) and a k3 "
                          "KL term (0.05) against a reference log-prob (the step's extra-term variant)")
+    ap.add_argument("--ahead", action="store_true",
+                    help="padded workloads: when the batch drives more than one optimizer step, run the ahead "
+                         "pass (pi_old recorded per chunk into the old-log-prob cache) inside the timed step and "
+                         "train against the replayed records")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     return ap.parse_args()
@@ -120,10 +124,11 @@ class PaddedStep:
 
     ENT_COEF, KL_COEF = 0.01, 0.05
 
-    def __init__(self, wl, seed, torch, ops, timed, terms=False):
+    def __init__(self, wl, seed, torch, ops, timed, terms=False, ahead=False):
         from synth import fill_normal_rows, padded_batch
         self.torch, self.ops, self.timed = torch, ops, timed
         self.terms = terms
+        self.ahead_timed = Timed(torch)
         b = self.b = padded_batch(wl, seed=seed)
         n_rows, T, V = b["n_rows"], b["T"], b["V"]
         self.dt = torch.bfloat16 if b["dtype"] == "bf16" else torch.float32
@@ -161,6 +166,14 @@ class PaddedStep:
                 self.chunk_units[(i, j)] = chunk_bytes(b["mask"][a * T:e * T], V, b_in, b_in, 8 if terms else 0)
         self.n_valid = int(np.sum(b["mask"]))
         self.logits_dtype = "bf16" if b_in == 2 else "fp32"
+        # the ahead pass runs only where the gate asks for it (more than one optimizer step per batch)
+        self.ahead = ahead and ops.needs_ahead_pass(n_mini)
+        if self.ahead:
+            self.cache = ops.OldLogprobCache(n_mini * n_micro,
+                                             torch.empty(n_rows * T, dtype=torch.float32, device="cuda"))
+            self.ahead_units = {k: int(np.sum(b["mask"][ops.plan_chunk(n_rows, mini_rows, micro_rows, *k)[0] * T:
+                                                      ops.plan_chunk(n_rows, mini_rows, micro_rows, *k)[1] * T]))
+                                * V * b_in for k in self.chunk_units}
 
     def __call__(self):
         torch, ops, b, T = self.torch, self.ops, self.b, self.b["T"]
@@ -168,6 +181,15 @@ class PaddedStep:
         n_mini, n_micro, mini_rows, micro_rows = ops.plan_fixed(n_rows, b["group"], b["mini"], b["micro"])
         self.adv_host.numpy()[:] = ops.group_advantage(b["reward"], b["group"])    # one rollout per row
         self.adv_dev.copy_(self.adv_host, non_blocking=True)
+        if self.ahead:
+            # [P1] the ahead walk: pi_old of every chunk, recorded before training
+            self.cache.reset()
+            for i in range(n_mini):
+                for j in range(n_micro):
+                    a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
+                    ev = self.ahead_timed.begin()
+                    self.cache.record(self.logits[a * T:e * T], self.target[a * T:e * T], self.mask[a * T:e * T])
+                    self.ahead_timed.end(ev, self.ahead_units[(i, j)])
         k = 0
         for i in range(n_mini):
             mini_mask = self.mask[i * mini_rows * T:(i + 1) * mini_rows * T]
@@ -185,8 +207,9 @@ class PaddedStep:
                               ent_coef=self.ENT_COEF, kl_coef=self.KL_COEF, kl_type=ops.C.KL_K3)
                 else:
                     kw = dict(scale=1.0, denom=self.N[i:i + 1])
+                old = self.cache.replay(t1 - t0) if self.ahead else self.old[t0:t1]
                 ev = self.timed.begin()
-                ops.loss_fwd_bwd(self.logits[t0:t1], self.target[t0:t1], self.mask[t0:t1], self.old[t0:t1],
+                ops.loss_fwd_bwd(self.logits[t0:t1], self.target[t0:t1], self.mask[t0:t1], old,
                                  self.tok_row, self.adv_dev[a:e], self.row_off, dlogits=self.dlogits[t0:t1],
                                  ws=self.ws, **kw)
                 self.timed.end(ev, self.chunk_units[(i, j)])
@@ -442,14 +465,21 @@ def main():
     timed = Timed(torch)
     cls = {"qwen": PaddedStep, "long": PaddedStep, "tiny": PaddedStep, "dynamic": DynamicStep,
            "compact": CompactStep}[wl]
-    if args.terms and cls is not PaddedStep:
-        print("--terms applies to the padded workloads (qwen, long, tiny)", file=sys.stderr)
+    if (args.terms or args.ahead) and cls is not PaddedStep:
+        print("--terms and --ahead apply to the padded workloads (qwen, long, tiny)", file=sys.stderr)
         sys.exit(2)
-    step = cls(wl, args.seed, torch, ops, timed, terms=True) if args.terms else cls(wl, args.seed, torch, ops, timed)
+    extra = {}
+    if args.terms:
+        extra["terms"] = True
+    if args.ahead:
+        extra["ahead"] = True
+    step = cls(wl, args.seed, torch, ops, timed, **extra)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     timed.on = True
+    if getattr(step, "ahead", False):
+        step.ahead_timed.on = True
     t0 = time.perf_counter()
     for _ in range(args.steps):
         res = step()
@@ -459,12 +489,19 @@ def main():
     value = step.n_valid / (wall / args.steps)
     tot_ms, units, launches = timed.totals()
     cfg = {"workload": f"{wl}: {WORKLOAD_TEXT[wl]}"
-                       + ("; seq-mean-token-mean aggregation, entropy bonus 0.01, k3 KL 0.05" if args.terms else ""),
+                       + ("; seq-mean-token-mean aggregation, entropy bonus 0.01, k3 KL 0.05" if args.terms else "")
+                       + ("; ahead pass (pi_old cache) in the step" if args.ahead else ""),
            "logits_dtype": step.logits_dtype,
            "valid_tokens": step.n_valid, "launches_per_step": launches // args.steps,
            "step_loss": res[0]["loss"] if res and res[0] else None}
     if args.terms and res and res[0]:
         cfg["step_objective"] = res[0]["obj_sum"]
+    if args.ahead:
+        cfg["ahead_pass"] = bool(getattr(step, "ahead", False))
+        if cfg["ahead_pass"]:
+            a_ms, a_units, a_n = step.ahead_timed.totals()
+            cfg["ahead_ms_per_step"] = round(a_ms / args.steps, 4)
+            cfg["ahead_read_GBs"] = round(a_units / (a_ms * 1e-3) / 1e9, 1)
     if wl == "compact":
         achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -89,6 +89,22 @@ class StepResult(ctypes.Structure):
                 ("n_valid", _i64), ("n_valid_rows", _i64), ("n_clipped", _i64)]
 
 
+class OldCache(ctypes.Structure):
+    _fields_ = [("buf", _p), ("capacity", _i64), ("off", ctypes.POINTER(ctypes.c_int64)), ("n_calls", _i64),
+                ("recorded", _i64), ("replayed", _i64)]
+
+
+class ProbeStats(ctypes.Structure):
+    _fields_ = [("n_valid", _i64), ("n_moved", _i64), ("max_abs", ctypes.c_double)]
+
+
+class Probe(ctypes.Structure):
+    _fields_ = [("bound", ctypes.c_double), ("max_fraction", ctypes.c_double), ("done", _i32), ("passed", _i32)]
+
+
+PROBE_STRICT_BOUND = 0.05
+PROBE_STRICT_FRACTION = 0.0
+
 _P64 = ctypes.POINTER(ctypes.c_int64)
 _P32 = ctypes.POINTER(ctypes.c_int32)
 _PU8 = ctypes.POINTER(ctypes.c_uint8)
@@ -115,6 +131,16 @@ PROTOTYPES = {
     "grpo_transpose_bf16": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _i64]),
     "grpo_lmhead_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "grpo_lmhead_fwd_bwd": (ctypes.c_int, [_p, ctypes.POINTER(LmheadArgs)]),
+    "grpo_needs_ahead_pass": (ctypes.c_int32, [_i64, _i32, _i32]),
+    "grpo_old_cache_init": (ctypes.c_int, [ctypes.POINTER(OldCache), _p, _i64, _P64, _i64]),
+    "grpo_old_cache_reset": (ctypes.c_int, [ctypes.POINTER(OldCache)]),
+    "grpo_old_cache_record": (ctypes.c_int, [_p, ctypes.POINTER(OldCache), _i32, _p, _i64, _i64, _i64, _p, _p,
+                                             ctypes.POINTER(ctypes.c_void_p)]),
+    "grpo_old_cache_replay": (ctypes.c_int, [ctypes.POINTER(OldCache), _i64, ctypes.POINTER(ctypes.c_void_p)]),
+    "grpo_probe_compare": (ctypes.c_int, [_p, _p, _p, _p, _i64, _f32, _p]),
+    "grpo_probe_init": (ctypes.c_int, [ctypes.POINTER(Probe), ctypes.c_double, ctypes.c_double]),
+    "grpo_probe_finish": (ctypes.c_int, [ctypes.POINTER(Probe), ctypes.POINTER(ProbeStats),
+                                         ctypes.POINTER(ctypes.c_int32)]),
     "grpo_accum_init": (ctypes.c_int, [ctypes.POINTER(Accum), _i64]),
     "grpo_accum_add": (ctypes.c_int, [ctypes.POINTER(Accum), ctypes.POINTER(Stats)]),
     "grpo_accum_finalize": (ctypes.c_int, [ctypes.POINTER(Accum), ctypes.POINTER(StepResult),

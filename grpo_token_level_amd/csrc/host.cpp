@@ -368,3 +368,86 @@ extern "C" int grpo_accum_finalize(grpo_accum* acc, grpo_step_result* out, int32
     *stepped = 1;
     return ok();
 }
+
+// ---------------------------------------------------------------- frozen pi_old
+
+// [P1] "pi_old must be frozen across the window -- the ahead pass": the gate.
+extern "C" int32_t grpo_needs_ahead_pass(int64_t n_mini, int32_t use_rollout_logprobs,
+                                         int32_t consumes_old_logprobs) {
+    return (n_mini > 1 && !use_rollout_logprobs && consumes_old_logprobs) ? 1 : 0;
+}
+
+extern "C" int grpo_old_cache_init(grpo_old_cache* c, float* buf, int64_t capacity, int64_t* off, int64_t n_calls) {
+    if (!c || !off || n_calls < 1 || capacity < 0 || (capacity > 0 && !buf))
+        return fail(GRPO_EINVAL, "grpo_old_cache_init: need n_calls >= 1, capacity >= 0, buf and off");
+    c->buf = buf;
+    c->capacity = capacity;
+    c->off = off;
+    c->n_calls = n_calls;
+    return grpo_old_cache_reset(c);
+}
+
+extern "C" int grpo_old_cache_reset(grpo_old_cache* c) {
+    if (!c || !c->off || c->n_calls < 1) return fail(GRPO_EINVAL, "grpo_old_cache_reset: uninitialised cache");
+    c->recorded = 0;
+    c->replayed = 0;
+    c->off[0] = 0;
+    return ok();
+}
+
+// Record k is the chunk's forward-only log-probs, appended after record k-1.
+extern "C" int grpo_old_cache_record(void* stream, grpo_old_cache* c, int32_t dtype, const void* logits, int64_t ld,
+                                     int64_t n_tok, int64_t V, const int32_t* target, const uint8_t* mask,
+                                     float** slot) {
+    if (!c || !c->off || c->n_calls < 1 || n_tok < 0) return fail(GRPO_EINVAL, "grpo_old_cache_record: bad arguments");
+    if (c->replayed > 0) return fail(GRPO_ESTATE, "grpo_old_cache_record: replay has begun; reset for the next batch");
+    if (c->recorded >= c->n_calls)
+        return fail(GRPO_ESTATE, "grpo_old_cache_record: all %lld calls of the walk are recorded",
+                    (long long)c->n_calls);
+    const int64_t k = c->recorded, at = c->off[k];
+    if (at + n_tok > c->capacity)
+        return fail(GRPO_ECAPACITY, "grpo_old_cache_record: %lld floats needed, %lld available",
+                    (long long)(at + n_tok), (long long)c->capacity);
+    float* dst = c->buf ? c->buf + at : nullptr;
+    if (n_tok > 0) {
+        const int rc = grpo_logprob_fwd(stream, dtype, logits, ld, n_tok, V, target, mask, dst, nullptr, nullptr);
+        if (rc != GRPO_OK) return rc;
+    }
+    c->off[k + 1] = at + n_tok;
+    c->recorded = k + 1;
+    if (slot) *slot = dst;
+    return ok();
+}
+
+extern "C" int grpo_old_cache_replay(grpo_old_cache* c, int64_t n_tok, const float** old_logp) {
+    if (!c || !c->off || !old_logp) return fail(GRPO_EINVAL, "grpo_old_cache_replay: bad arguments");
+    const int64_t k = c->replayed;
+    if (k >= c->recorded)
+        return fail(GRPO_ESTATE, "grpo_old_cache_replay: call %lld was not recorded", (long long)k);
+    const int64_t have = c->off[k + 1] - c->off[k];
+    if (have != n_tok)
+        return fail(GRPO_EINVAL, "grpo_old_cache_replay: call %lld has %lld tokens, record has %lld (walks diverged)",
+                    (long long)k, (long long)n_tok, (long long)have);
+    *old_logp = c->buf ? c->buf + c->off[k] : nullptr;
+    c->replayed = k + 1;
+    return ok();
+}
+
+extern "C" int grpo_probe_init(grpo_probe* p, double bound, double max_fraction) {
+    if (!p || !(bound >= 0.0) || !(max_fraction >= 0.0 && max_fraction <= 1.0))
+        return fail(GRPO_EINVAL, "grpo_probe_init: need bound >= 0 and 0 <= max_fraction <= 1");
+    p->bound = bound;
+    p->max_fraction = max_fraction;
+    p->done = 0;
+    p->passed = 0;
+    return ok();
+}
+
+extern "C" int grpo_probe_finish(grpo_probe* p, const grpo_probe_stats* s, int32_t* passed) {
+    if (!p || !s || !passed) return fail(GRPO_EINVAL, "grpo_probe_finish: NULL argument");
+    if (p->done) return fail(GRPO_ESTATE, "grpo_probe_finish: the probe runs once per run");
+    p->done = 1;
+    p->passed = (double)s->n_moved <= p->max_fraction * (double)s->n_valid ? 1 : 0;
+    *passed = p->passed;
+    return ok();
+}

@@ -714,6 +714,48 @@ __global__ __launch_bounds__(1024) void count_valid_kernel(const uint8_t* __rest
     }
 }
 
+// Determinism probe: over mask-1 tokens, count those whose two log-probs
+// differ by more than `bound` (or are not finite) and take the largest
+// difference.  One 1024-thread block, fixed-order totals.
+__global__ __launch_bounds__(1024) void probe_compare_kernel(const float* __restrict__ a, const float* __restrict__ b,
+                                                             const uint8_t* __restrict__ mask, int64_t n, float bound,
+                                                             grpo_probe_stats* __restrict__ out) {
+    __shared__ long long s_nv[16], s_nm[16];
+    __shared__ float s_mx[16];
+    const int i = threadIdx.x;
+    long long nv = 0, nm = 0;
+    float mx = 0.0f;
+    for (int64_t t = i; t < n; t += 1024) {
+        if (!mask[t]) continue;
+        const float d = fabsf(a[t] - b[t]);
+        nv += 1;
+        nm += (d <= bound) ? 0 : 1;
+        mx = fmaxf(mx, isfinite(d) ? d : INFINITY);
+    }
+    nv = wave_sum_i(nv);
+    nm = wave_sum_i(nm);
+    mx = wave_max(mx);
+    if ((i & 63) == 0) {
+        s_nv[i >> 6] = nv;
+        s_nm[i >> 6] = nm;
+        s_mx[i >> 6] = mx;
+    }
+    __syncthreads();
+    if (i == 0) {
+        grpo_probe_stats r;
+        r.n_valid = 0;
+        r.n_moved = 0;
+        float m = 0.0f;
+        for (int k = 0; k < 16; ++k) {
+            r.n_valid += s_nv[k];
+            r.n_moved += s_nm[k];
+            m = fmaxf(m, s_mx[k]);
+        }
+        r.max_abs = (double)m;
+        *out = r;
+    }
+}
+
 __global__ __launch_bounds__(256) void tok_row_kernel(const int64_t* __restrict__ row_off, int64_t n_rows,
                                                       int64_t n_tok, int32_t* __restrict__ tok_row) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -835,6 +877,15 @@ extern "C" int grpo_row_weights(void* stream, const uint8_t* mask, const int64_t
     hipLaunchKernelGGL(row_weights_kernel, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, (hipStream_t)stream,
                        mask, row_off, n_rows, n_tok, (int)mode, n_seq, w_row);
     return check_launch(hipGetLastError(), "grpo_row_weights");
+}
+
+extern "C" int grpo_probe_compare(void* stream, const float* recorded, const float* rescored, const uint8_t* mask,
+                                  int64_t n_tok, float bound, grpo_probe_stats* out) {
+    if (n_tok < 0 || !out || (n_tok > 0 && (!recorded || !rescored || !mask)) || !(bound >= 0.0f))
+        return fail(GRPO_EINVAL, "grpo_probe_compare: bad arguments");
+    hipLaunchKernelGGL(probe_compare_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, recorded, rescored, mask,
+                       n_tok, bound, out);
+    return check_launch(hipGetLastError(), "grpo_probe_compare");
 }
 
 extern "C" int grpo_tok_row(void* stream, const int64_t* row_off, int64_t n_rows, int64_t n_tok, int32_t* tok_row) {

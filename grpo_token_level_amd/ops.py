@@ -132,6 +132,94 @@ class Accumulator:
         return {k: getattr(r, k) for k, _ in C.StepResult._fields_}
 
 
+def needs_ahead_pass(n_mini, use_rollout_logprobs=False, consumes_old_logprobs=True):
+    return bool(C.lib().grpo_needs_ahead_pass(n_mini, 1 if use_rollout_logprobs else 0,
+                                              1 if consumes_old_logprobs else 0))
+
+
+class OldLogprobCache:
+    """grpo_old_cache: pi_old records of one collected batch keyed by call
+    order, in a caller-owned device buffer (a float32 torch tensor)."""
+
+    def __init__(self, n_calls, buf):
+        torch = _torch()
+        if buf.dtype != torch.float32 or not buf.is_cuda or not buf.is_contiguous():
+            raise ValueError("buf must be a contiguous float32 GPU tensor")
+        self.buf = buf
+        self.off = np.zeros(n_calls + 1, np.int64)
+        self.c = C.OldCache()
+        C.check(C.lib().grpo_old_cache_init(ctypes.byref(self.c), ctypes.c_void_p(buf.data_ptr()), buf.numel(),
+                                            C.ptr64(self.off), n_calls))
+
+    def reset(self):
+        C.check(C.lib().grpo_old_cache_reset(ctypes.byref(self.c)))
+
+    def _view(self, addr, n):
+        start = (addr - self.buf.data_ptr()) // 4 if n else 0
+        return self.buf[start:start + n]
+
+    def record(self, logits, target, mask):
+        """Ahead pass of one chunk into the next record; returns its view."""
+        ld = _rows2d(logits, "logits")
+        n, V = logits.shape
+        slot = ctypes.c_void_p()
+        C.check(C.lib().grpo_old_cache_record(_stream(), ctypes.byref(self.c), _dtype_code(logits),
+                                              _dev(logits, "logits"), ld, n, V, _dev(target, "target"),
+                                              _dev(mask, "mask"), ctypes.byref(slot)))
+        return self._view(slot.value or 0, n)
+
+    def replay(self, n_tok):
+        """pi_old of the next training call (a view of the buffer)."""
+        ptr = ctypes.c_void_p()
+        C.check(C.lib().grpo_old_cache_replay(ctypes.byref(self.c), n_tok, ctypes.byref(ptr)))
+        return self._view(ptr.value or 0, n_tok)
+
+    @property
+    def recorded(self):
+        return self.c.recorded
+
+    @property
+    def replayed(self):
+        return self.c.replayed
+
+
+PROBE_STATS_BYTES = ctypes.sizeof(C.ProbeStats)
+
+
+def probe_compare(recorded, rescored, mask, bound=C.PROBE_STRICT_BOUND, out=None):
+    """Device compare of two log-prob arrays -> uint8 device tensor holding a
+    grpo_probe_stats (see probe_stats)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(PROBE_STATS_BYTES, dtype=torch.uint8, device=recorded.device)
+    C.check(C.lib().grpo_probe_compare(_stream(), _dev(recorded, "recorded"), _dev(rescored, "rescored"),
+                                       _dev(mask, "mask"), mask.numel(), bound, _dev(out, "out")))
+    return out
+
+
+def probe_stats(raw):
+    b = raw.cpu().numpy().tobytes() if hasattr(raw, "cpu") else bytes(raw)
+    s = C.ProbeStats.from_buffer_copy(b)
+    return {"n_valid": s.n_valid, "n_moved": s.n_moved, "max_abs": s.max_abs}
+
+
+class Probe:
+    """grpo_probe: the one-shot determinism screen of a run."""
+
+    def __init__(self, bound=C.PROBE_STRICT_BOUND, max_fraction=C.PROBE_STRICT_FRACTION):
+        self.p = C.Probe()
+        C.check(C.lib().grpo_probe_init(ctypes.byref(self.p), bound, max_fraction))
+
+    def due(self):
+        return not self.p.done
+
+    def finish(self, stats):
+        s = C.ProbeStats(stats["n_valid"], stats["n_moved"], stats["max_abs"])
+        passed = ctypes.c_int32()
+        C.check(C.lib().grpo_probe_finish(ctypes.byref(self.p), ctypes.byref(s), ctypes.byref(passed)))
+        return bool(passed.value)
+
+
 def stats_to_dicts(raw):
     """uint8 bytes of a grpo_stats array (numpy or torch) -> list of dicts."""
     if hasattr(raw, "cpu"):

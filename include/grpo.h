@@ -338,6 +338,82 @@ size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V);
  * stats as in grpo_loss_fwd_bwd.  ECAPACITY if the workspace is too small. */
 int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* args);
 
+/* ===================================================== frozen pi_old (ahead pass) */
+
+/* host.  [P1] "pi_old must be frozen across the window -- the ahead pass":
+ * with n_mini > 1 optimizer steps per collected batch, pi_old recomputed from
+ * the current policy makes every ratio 1 and the clip never binds, so the
+ * whole (mini, micro) product is walked once before training and pi_old is
+ * recorded per chunk.  Returns 1 when that pass is needed: n_mini > 1, the
+ * loss does not use the rollout's own log-probs, and the objective consumes
+ * old log-probs; else 0 (n_mini = 1 always skips it). */
+int32_t grpo_needs_ahead_pass(int64_t n_mini, int32_t use_rollout_logprobs, int32_t consumes_old_logprobs);
+
+/* The pi_old records of one collected batch, keyed by call order ([P1]: both
+ * walks visit the chunks in the same order, so training call k pairs with
+ * ahead call k).  Plain data, caller-allocated; buf (device) and off (host)
+ * are caller-owned.  Not thread-safe: one walk per cache. */
+typedef struct grpo_old_cache {
+    float* buf;         /* device float [capacity]: the records end to end */
+    int64_t capacity;   /* floats in buf */
+    int64_t* off;       /* host int64 [n_calls + 1]: record k is buf[off[k] .. off[k+1]) */
+    int64_t n_calls;    /* calls in one walk */
+    int64_t recorded;   /* records made */
+    int64_t replayed;   /* training calls served */
+} grpo_old_cache;
+
+/* host.  n_calls >= 1, capacity >= 0, buf and off non-NULL (EINVAL). */
+int grpo_old_cache_init(grpo_old_cache* c, float* buf, int64_t capacity, int64_t* off, int64_t n_calls);
+/* host.  Empties the cache for the next collected batch. */
+int grpo_old_cache_reset(grpo_old_cache* c);
+/* device.  Records the next call: the forward-only log-prob pass
+ * (grpo_logprob_fwd, same arguments) of the chunk into buf + off[k], k =
+ * c->recorded; *slot (if slot is non-NULL) receives that device address.
+ * ESTATE when all n_calls are recorded or a replay has begun (reset first);
+ * ECAPACITY when the record does not fit in buf. */
+int grpo_old_cache_record(void* stream, grpo_old_cache* c, int32_t dtype, const void* logits, int64_t ld,
+                          int64_t n_tok, int64_t V, const int32_t* target, const uint8_t* mask, float** slot);
+/* host.  pi_old of the next training call: *old_logp = buf + off[k], k =
+ * c->replayed (device float [n_tok], as grpo_loss_args.old_logp).  ESTATE if
+ * call k was not recorded; EINVAL if n_tok differs from record k's token
+ * count (the training walk diverged from the ahead walk). */
+int grpo_old_cache_replay(grpo_old_cache* c, int64_t n_tok, const float** old_logp);
+
+/* The determinism probe ([P1], same section): on the first ahead chunk of a
+ * run, the chunk re-scored in training mode is compared with its record at
+ * unchanged weights; the gate is on the fraction of tokens whose log-prob
+ * moved past a per-token bound, under the tolerance the model declares
+ * (bound, largest moved fraction); the strict default is 0.05 nats on any
+ * token.  It runs once per run. */
+#define GRPO_PROBE_STRICT_BOUND 0.05
+#define GRPO_PROBE_STRICT_FRACTION 0.0
+
+typedef struct grpo_probe_stats {
+    int64_t n_valid;    /* mask-1 tokens compared */
+    int64_t n_moved;    /* of those, |recorded - rescored| > bound (float32) or not finite */
+    double max_abs;     /* largest |recorded - rescored| (infinity if one is not finite) */
+} grpo_probe_stats;
+
+/* device.  Compares two per-token log-prob arrays (device float [n_tok])
+ * over mask-1 tokens into *out (device grpo_probe_stats); fixed-order
+ * reduction.  Overwrites *out. */
+int grpo_probe_compare(void* stream, const float* recorded, const float* rescored, const uint8_t* mask,
+                       int64_t n_tok, float bound, grpo_probe_stats* out);
+
+typedef struct grpo_probe {
+    double bound;        /* per-token bound (nats) */
+    double max_fraction; /* largest allowed moved fraction */
+    int32_t done;        /* the probe has run */
+    int32_t passed;      /* its verdict */
+} grpo_probe;
+
+/* host.  bound >= 0, 0 <= max_fraction <= 1 (EINVAL). */
+int grpo_probe_init(grpo_probe* p, double bound, double max_fraction);
+/* host.  Takes the verdict from a host copy of the compare's stats:
+ * *passed = (n_moved <= max_fraction * n_valid).  ESTATE on a second call
+ * (the probe is one-shot). */
+int grpo_probe_finish(grpo_probe* p, const grpo_probe_stats* stats, int32_t* passed);
+
 /* ============================================================ accumulator */
 
 /* One optimizer-step window of n_micro chunks, caller-allocated, plain data.

@@ -41,6 +41,8 @@ from .agg import (AGG_TOKEN_MEAN, AGG_SEQ_MEAN_TOKEN_SUM, AGG_SEQ_MEAN_TOKEN_MEA
                   row_valid_counts, count_rows, agg_loss, row_weights)
 from .accum import Accumulator, ACC_OK, ACC_NONFINITE, ACC_SKIPPED
 from .lmhead import lmhead_fwd_bwd
+from .cache import (CacheError, needs_ahead_pass, OldLogprobCache, probe_compare, Probe,
+                    PROBE_STRICT_BOUND, PROBE_STRICT_FRACTION)
 
 __all__ = [
     "PlanError", "plan_fixed", "chunk_rows", "train_calls", "plan_dynamic",
@@ -50,5 +52,6 @@ __all__ = [
     "Accumulator", "ACC_OK", "ACC_NONFINITE", "ACC_SKIPPED", "lmhead_fwd_bwd",
     "kl_term", "KL_K1", "KL_K2", "KL_K3", "STAT_KEYS", "AGG_TOKEN_MEAN",
     "AGG_SEQ_MEAN_TOKEN_SUM", "AGG_SEQ_MEAN_TOKEN_MEAN", "row_valid_counts",
-    "count_rows", "agg_loss", "row_weights",
+    "count_rows", "agg_loss", "row_weights", "CacheError", "needs_ahead_pass",
+    "OldLogprobCache", "probe_compare", "Probe", "PROBE_STRICT_BOUND", "PROBE_STRICT_FRACTION",
 ]

@@ -221,3 +221,52 @@ def test_accumulator_matches_oracle_on_random_sequences():
                   "n_clipped": int(rng.integers(0, 3)), "n_nonfinite": 1 if bad else 0,
                   "n_valid_rows": int(rng.integers(0, 4))}
             assert b.add(st) == a.add(st)
+
+
+# ---------------------------------------------------------------- ahead pass, cache, probe (host parts)
+
+def test_ahead_pass_gate_matches_oracle():
+    for n_mini in (0, 1, 2, 7):
+        for rollout in (False, True):
+            for consumes in (False, True):
+                assert ops.needs_ahead_pass(n_mini, rollout, consumes) == oracle.needs_ahead_pass(n_mini, rollout,
+                                                                                                  consumes)
+
+
+def test_probe_verdict_matches_oracle():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        bound, frac = float(rng.random() * 0.1), float(rng.choice([0.0, 0.05, 0.1, 0.5, 1.0]))
+        n_valid = int(rng.integers(0, 100))
+        n_moved = int(rng.integers(0, n_valid + 1))
+        a, b = ops.Probe(bound, frac), oracle.Probe(bound, frac)
+        st = {"n_valid": n_valid, "n_moved": n_moved, "max_abs": 0.0}
+        assert a.finish(st) == b.finish(n_valid, n_moved)
+        with pytest.raises(GrpoError) as e:
+            a.finish(st)
+        assert e.value.kind == "ESTATE"
+    with pytest.raises(GrpoError):
+        ops.Probe(-1.0, 0.0)
+    with pytest.raises(GrpoError):
+        ops.Probe(0.05, 1.5)
+
+
+def test_old_cache_state_machine_without_device_work():
+    # zero-token records never launch a kernel, so the bookkeeping runs on the CPU
+    c = C.OldCache()
+    off = np.zeros(4, np.int64)
+    L = C.lib()
+    assert L.grpo_old_cache_init(ctypes.byref(c), None, 0, C.ptr64(off), 3) == 0
+    ptr = ctypes.c_void_p()
+    assert L.grpo_old_cache_replay(ctypes.byref(c), 0, ctypes.byref(ptr)) == -9          # nothing recorded
+    for _ in range(3):
+        assert L.grpo_old_cache_record(None, ctypes.byref(c), 1, None, 8, 0, 8, None, None, None) == 0
+    assert L.grpo_old_cache_record(None, ctypes.byref(c), 1, None, 8, 0, 8, None, None, None) == -9  # walk complete
+    assert L.grpo_old_cache_replay(ctypes.byref(c), 5, ctypes.byref(ptr)) == -1          # token count differs
+    assert L.grpo_old_cache_replay(ctypes.byref(c), 0, ctypes.byref(ptr)) == 0
+    assert L.grpo_old_cache_record(None, ctypes.byref(c), 1, None, 8, 0, 8, None, None, None) == -9  # replay began
+    assert L.grpo_old_cache_reset(ctypes.byref(c)) == 0 and c.recorded == 0 and c.replayed == 0
+    # a record that does not fit is refused before any launch
+    assert L.grpo_old_cache_record(None, ctypes.byref(c), 1, ctypes.c_void_p(16), 8, 4, 8, ctypes.c_void_p(16),
+                                   ctypes.c_void_p(16), None) == -7
+    assert L.grpo_old_cache_init(ctypes.byref(c), None, 0, C.ptr64(off), 0) == -1

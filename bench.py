@@ -69,6 +69,11 @@ def parse():
                     help="padded workloads: when the batch drives more than one optimizer step, run the ahead "
                          "pass (pi_old recorded per chunk into the old-log-prob cache) inside the timed step and "
                          "train against the replayed records")
+    ap.add_argument("--epochs", type=int, default=1,
+                    help="padded workloads: inner epochs (mu) over the collected batch in one timed step")
+    ap.add_argument("--shuffle", action="store_true",
+                    help="padded workloads: reshuffle the rows every epoch (seeded); chunks read the batch through "
+                         "tok_src")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     return ap.parse_args()
@@ -120,11 +125,14 @@ def chunk_bytes(mask_np, V, b_in, b_out, extra_per_valid=0):
 
 
 class PaddedStep:
-    """Fixed-plan step over a right-padded batch."""
+    """Fixed-plan step over a right-padded batch: mu inner epochs (1 by
+    default) of n_mini optimizer windows of n_micro chunks, optionally
+    reshuffled per epoch (the chunks then read the batch through tok_src),
+    optionally with the ahead pass and the extra loss terms."""
 
     ENT_COEF, KL_COEF = 0.01, 0.05
 
-    def __init__(self, wl, seed, torch, ops, timed, terms=False, ahead=False):
+    def __init__(self, wl, seed, torch, ops, timed, terms=False, ahead=False, epochs=1, shuffle=False):
         from synth import fill_normal_rows, padded_batch
         self.torch, self.ops, self.timed = torch, ops, timed
         self.terms = terms
@@ -146,34 +154,49 @@ class PaddedStep:
             self.ref = (self.old.double() + _g(torch, b["logratio_noise"])).float()
         del logp
         self.dlogits = torch.empty_like(self.logits)
-        n_mini, n_micro, mini_rows, micro_rows = ops.plan_fixed(n_rows, b["group"], b["mini"], b["micro"])
+        ep = ops.plan_epochs(n_rows, b["group"], b["mini"], b["micro"], mu=epochs, shuffle=shuffle, seed=seed + 1)
+        self.ep, self.mu, self.shuffle = ep, epochs, shuffle
+        n_mini, n_micro, mini_rows, micro_rows = ep["n_mini"], ep["n_micro"], ep["mini_rows"], ep["micro_rows"]
+        self.perm_dev = _g(torch, ep["perm"])
+        self.batch_off = torch.arange(0, n_tok + 1, T, dtype=torch.int64, device="cuda")
         self.row_off = torch.arange(0, micro_rows * T + 1, T, dtype=torch.int64, device="cuda")
         self.mini_off = torch.arange(0, mini_rows * T + 1, T, dtype=torch.int64, device="cuda")
         self.n_seq = torch.empty(n_mini, dtype=torch.int64, device="cuda")
-        self.w_row = torch.empty(n_rows, dtype=torch.float32, device="cuda")
+        self.w_row = torch.empty(mini_rows, dtype=torch.float32, device="cuda")
         self.tok_row = ops.tok_row(self.row_off, micro_rows * T)
         self.ws = ops.loss_workspace(micro_rows * T, micro_rows, "cuda")
         self.N = torch.empty(n_mini, dtype=torch.int64, device="cuda")
         self.adv_host = torch.empty(n_rows, dtype=torch.float32).pin_memory()
         self.adv_dev = torch.empty(n_rows, dtype=torch.float32, device="cuda")
-        self.stats_dev = torch.empty((n_mini * n_micro, ops.STATS_BYTES), dtype=torch.uint8, device="cuda")
-        self.stats_host = torch.empty((n_mini * n_micro, ops.STATS_BYTES), dtype=torch.uint8).pin_memory()
+        if shuffle:
+            self.mini_src = torch.empty(mini_rows * T, dtype=torch.int64, device="cuda")
+            self.mini_mask = torch.empty(mini_rows * T, dtype=torch.uint8, device="cuda")
+            self.tok_src = torch.empty(micro_rows * T, dtype=torch.int64, device="cuda")
+            self.adv_chunk = torch.empty(micro_rows, dtype=torch.float32, device="cuda")
+        n_calls = epochs * n_mini * n_micro
+        self.stats_dev = torch.empty((n_calls, ops.STATS_BYTES), dtype=torch.uint8, device="cuda")
+        self.stats_host = torch.empty((n_calls, ops.STATS_BYTES), dtype=torch.uint8).pin_memory()
         b_in = 2 if self.dt == torch.bfloat16 else 4
         self.chunk_units = {}
-        for i in range(n_mini):
-            for j in range(n_micro):
-                a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
-                self.chunk_units[(i, j)] = chunk_bytes(b["mask"][a * T:e * T], V, b_in, b_in, 8 if terms else 0)
-        self.n_valid = int(np.sum(b["mask"]))
+        for e in range(epochs):
+            for i in range(n_mini):
+                for j in range(n_micro):
+                    rows = ep["perm"][e][i * mini_rows + j * micro_rows:][:micro_rows]
+                    m = np.concatenate([b["mask"][r * T:(r + 1) * T] for r in rows])
+                    self.chunk_units[(e, i, j)] = chunk_bytes(m, V, b_in, b_in, 8 if terms else 0)
+        self.n_valid = int(np.sum(b["mask"])) * epochs
         self.logits_dtype = "bf16" if b_in == 2 else "fp32"
-        # the ahead pass runs only where the gate asks for it (more than one optimizer step per batch)
-        self.ahead = ahead and ops.needs_ahead_pass(n_mini)
+        # the ahead pass runs only where the gate asks for it (more than one
+        # optimizer step per collected batch: n_mini windows per epoch, mu epochs)
+        self.ahead = ahead and ops.needs_ahead_pass(n_mini * epochs)
         if self.ahead:
             self.cache = ops.OldLogprobCache(n_mini * n_micro,
                                              torch.empty(n_rows * T, dtype=torch.float32, device="cuda"))
-            self.ahead_units = {k: int(np.sum(b["mask"][ops.plan_chunk(n_rows, mini_rows, micro_rows, *k)[0] * T:
-                                                      ops.plan_chunk(n_rows, mini_rows, micro_rows, *k)[1] * T]))
-                                * V * b_in for k in self.chunk_units}
+            self.ahead_units = {}
+            for i in range(n_mini):
+                for j in range(n_micro):
+                    a, e_ = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
+                    self.ahead_units[(i, j)] = int(np.sum(b["mask"][a * T:e_ * T])) * V * b_in
 
     def __call__(self):
         torch, ops, b, T = self.torch, self.ops, self.b, self.b["T"]
@@ -182,7 +205,7 @@ class PaddedStep:
         self.adv_host.numpy()[:] = ops.group_advantage(b["reward"], b["group"])    # one rollout per row
         self.adv_dev.copy_(self.adv_host, non_blocking=True)
         if self.ahead:
-            # [P1] the ahead walk: pi_old of every chunk, recorded before training
+            # [P1] the ahead walk: pi_old of every chunk, recorded before training (batch order)
             self.cache.reset()
             for i in range(n_mini):
                 for j in range(n_micro):
@@ -191,37 +214,59 @@ class PaddedStep:
                     self.cache.record(self.logits[a * T:e * T], self.target[a * T:e * T], self.mask[a * T:e * T])
                     self.ahead_timed.end(ev, self.ahead_units[(i, j)])
         k = 0
-        for i in range(n_mini):
-            mini_mask = self.mask[i * mini_rows * T:(i + 1) * mini_rows * T]
-            ops.count_valid(mini_mask, out=self.N[i:i + 1])
-            if self.terms:
-                ops.count_rows(mini_mask, self.mini_off, out=self.n_seq[i:i + 1])
-                ops.row_weights(mini_mask, self.mini_off, ops.C.AGG_SEQ_MEAN_TOKEN_MEAN, self.n_seq[i:i + 1],
-                                out=self.w_row[i * mini_rows:(i + 1) * mini_rows])
-            for j in range(n_micro):
-                a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
-                t0, t1 = a * T, e * T
-                self.ws["chunk_stats"] = self.stats_dev[k:k + 1]
-                if self.terms:
-                    kw = dict(scale=1.0, row_weight=self.w_row[a:e], ref_logp=self.ref[t0:t1],
-                              ent_coef=self.ENT_COEF, kl_coef=self.KL_COEF, kl_type=ops.C.KL_K3)
+        for ep in range(self.mu):
+            if self.ahead and not self.shuffle and ep > 0:
+                self.cache.rewind()                      # the next epoch replays the records in order
+            for i in range(n_mini):
+                if self.shuffle:
+                    rows_mini = self.perm_dev[ep, i * mini_rows:(i + 1) * mini_rows]
+                    ops.chunk_tok_src(self.batch_off, rows_mini, self.mini_off, out=self.mini_src)
+                    mini_mask = ops.gather(self.mask, self.mini_src, out=self.mini_mask)
                 else:
-                    kw = dict(scale=1.0, denom=self.N[i:i + 1])
-                old = self.cache.replay(t1 - t0) if self.ahead else self.old[t0:t1]
-                ev = self.timed.begin()
-                ops.loss_fwd_bwd(self.logits[t0:t1], self.target[t0:t1], self.mask[t0:t1], old,
-                                 self.tok_row, self.adv_dev[a:e], self.row_off, dlogits=self.dlogits[t0:t1],
-                                 ws=self.ws, **kw)
-                self.timed.end(ev, self.chunk_units[(i, j)])
-                k += 1
+                    mini_mask = self.mask[i * mini_rows * T:(i + 1) * mini_rows * T]
+                ops.count_valid(mini_mask, out=self.N[i:i + 1])
+                if self.terms:
+                    ops.count_rows(mini_mask, self.mini_off, out=self.n_seq[i:i + 1])
+                    ops.row_weights(mini_mask, self.mini_off, ops.C.AGG_SEQ_MEAN_TOKEN_MEAN, self.n_seq[i:i + 1],
+                                    out=self.w_row)
+                for j in range(n_micro):
+                    r0 = j * micro_rows                      # the chunk's rows within the mini-batch
+                    self.ws["chunk_stats"] = self.stats_dev[k:k + 1]
+                    if self.terms:
+                        kw = dict(scale=1.0, row_weight=self.w_row[r0:r0 + micro_rows],
+                                  ent_coef=self.ENT_COEF, kl_coef=self.KL_COEF, kl_type=ops.C.KL_K3)
+                    else:
+                        kw = dict(scale=1.0, denom=self.N[i:i + 1])
+                    if self.shuffle:
+                        rows = self.perm_dev[ep, i * mini_rows + r0:i * mini_rows + r0 + micro_rows]
+                        ops.chunk_tok_src(self.batch_off, rows, self.row_off, out=self.tok_src)
+                        ops.gather(self.adv_dev, rows, out=self.adv_chunk)
+                        old = self.cache.buf if self.ahead else self.old
+                        if self.terms:
+                            kw["ref_logp"] = self.ref
+                        ev = self.timed.begin()
+                        ops.loss_fwd_bwd(self.logits, self.target, self.mask, old, self.tok_row, self.adv_chunk,
+                                         self.row_off, dlogits=self.dlogits, ws=self.ws, tok_src=self.tok_src, **kw)
+                    else:
+                        a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
+                        t0, t1 = a * T, e * T
+                        old = self.cache.replay(t1 - t0) if self.ahead else self.old[t0:t1]
+                        if self.terms:
+                            kw["ref_logp"] = self.ref[t0:t1]
+                        ev = self.timed.begin()
+                        ops.loss_fwd_bwd(self.logits[t0:t1], self.target[t0:t1], self.mask[t0:t1], old,
+                                         self.tok_row, self.adv_dev[a:e], self.row_off, dlogits=self.dlogits[t0:t1],
+                                         ws=self.ws, **kw)
+                    self.timed.end(ev, self.chunk_units[(ep, i, j)])
+                    k += 1
         self.stats_host.copy_(self.stats_dev, non_blocking=True)
         torch.cuda.current_stream().synchronize()
         stats = ops.stats_to_dicts(self.stats_host.numpy())
         out = []
-        for i in range(n_mini):
+        for w in range(self.mu * n_mini):
             acc = ops.Accumulator(n_micro)
             for j in range(n_micro):
-                acc.add(stats[i * n_micro + j])
+                acc.add(stats[w * n_micro + j])
             out.append(acc.finalize())
         return out
 
@@ -465,14 +510,18 @@ def main():
     timed = Timed(torch)
     cls = {"qwen": PaddedStep, "long": PaddedStep, "tiny": PaddedStep, "dynamic": DynamicStep,
            "compact": CompactStep}[wl]
-    if (args.terms or args.ahead) and cls is not PaddedStep:
-        print("--terms and --ahead apply to the padded workloads (qwen, long, tiny)", file=sys.stderr)
+    if (args.terms or args.ahead or args.epochs != 1 or args.shuffle) and cls is not PaddedStep:
+        print("--terms, --ahead, --epochs and --shuffle apply to the padded workloads (qwen, long, tiny)",
+              file=sys.stderr)
         sys.exit(2)
     extra = {}
     if args.terms:
         extra["terms"] = True
     if args.ahead:
         extra["ahead"] = True
+    if args.epochs != 1 or args.shuffle:
+        extra["epochs"] = args.epochs
+        extra["shuffle"] = args.shuffle
     step = cls(wl, args.seed, torch, ops, timed, **extra)
     for _ in range(args.warmup):
         step()
@@ -490,7 +539,9 @@ def main():
     tot_ms, units, launches = timed.totals()
     cfg = {"workload": f"{wl}: {WORKLOAD_TEXT[wl]}"
                        + ("; seq-mean-token-mean aggregation, entropy bonus 0.01, k3 KL 0.05" if args.terms else "")
-                       + ("; ahead pass (pi_old cache) in the step" if args.ahead else ""),
+                       + ("; ahead pass (pi_old cache) in the step" if args.ahead else "")
+                       + (f"; {args.epochs} inner epochs" if args.epochs != 1 else "")
+                       + ("; rows reshuffled every epoch (seeded)" if args.shuffle else ""),
            "logits_dtype": step.logits_dtype,
            "valid_tokens": step.n_valid, "launches_per_step": launches // args.steps,
            "step_loss": res[0]["loss"] if res and res[0] else None}
@@ -515,7 +566,7 @@ def main():
                 "kernel": "tok_reg_kernel (fused loss fwd+bwd) + row/chunk stats, per chunk launch",
                 "algorithmic_bytes_per_launch": int(units // launches), "avg_launch_ms": round(tot_ms / launches, 4)}
         roof["device_copy_GBs"] = round(step.copy_context(), 1)
-        if wl == "qwen" and not args.terms:
+        if wl == "qwen" and not (args.terms or args.ahead or args.epochs != 1 or args.shuffle):
             from grpo_token_level_amd.prof_summary import load_traffic
             rec = load_traffic(os.path.join(ROOT, "profiles", "fused_loss_qwen_pmc.txt"))
             if rec is not None:

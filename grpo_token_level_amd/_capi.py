@@ -62,7 +62,8 @@ class LossArgs(ctypes.Structure):
                 ("logp", _p), ("lse", _p), ("entropy", _p), ("loss_tok", _p), ("tok_flags", _p),
                 ("row_stats", _p), ("chunk_stats", _p),
                 ("row_weight", _p), ("ref_logp", _p), ("kl_tok", _p),
-                ("ent_coef", _f32), ("kl_coef", _f32), ("kl_type", _i32), ("reserved2", _i32)]
+                ("ent_coef", _f32), ("kl_coef", _f32), ("kl_type", _i32), ("reserved2", _i32),
+                ("tok_src", _p), ("n_src", _i64)]
 
 
 class LmheadArgs(ctypes.Structure):
@@ -117,6 +118,8 @@ PROTOTYPES = {
     "grpo_plan_fixed": (ctypes.c_int, [_i64, _i64, _i64, _i64, _P64, _P64, _P64, _P64]),
     "grpo_plan_chunk": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64, _P64, _P64]),
     "grpo_plan_dynamic": (ctypes.c_int, [_P64, _i64, _i64, _i64, _i64, _P64, _P64, _P64, _P64]),
+    "grpo_plan_epochs": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64, _i32, ctypes.c_uint64, _P64, _P64, _P64, _P64,
+                                        _P64]),
     "grpo_plan_compaction": (ctypes.c_int, [_P32, _i64, _i64, _i64, _i64, _i64, _i32, _i64, _P64,
                                             _P32, _P32, _P32, _PU8, _P32]),
     "grpo_row_offsets": (ctypes.c_int, [_P64, _P64, _i64, _P64]),
@@ -126,6 +129,8 @@ PROTOTYPES = {
     "grpo_count_rows": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _p]),
     "grpo_row_weights": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p, _p]),
     "grpo_tok_row": (ctypes.c_int, [_p, _p, _i64, _i64, _p]),
+    "grpo_chunk_tok_src": (ctypes.c_int, [_p, _p, _i64, _p, _i64, _p, _i64, _p]),
+    "grpo_gather": (ctypes.c_int, [_p, _p, _i64, _p, _i64, _i64, _p]),
     "grpo_logprob_fwd": (ctypes.c_int, [_p, _i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "grpo_loss_fwd_bwd": (ctypes.c_int, [_p, ctypes.POINTER(LossArgs)]),
     "grpo_transpose_bf16": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _i64]),
@@ -134,6 +139,7 @@ PROTOTYPES = {
     "grpo_needs_ahead_pass": (ctypes.c_int32, [_i64, _i32, _i32]),
     "grpo_old_cache_init": (ctypes.c_int, [ctypes.POINTER(OldCache), _p, _i64, _P64, _i64]),
     "grpo_old_cache_reset": (ctypes.c_int, [ctypes.POINTER(OldCache)]),
+    "grpo_old_cache_rewind": (ctypes.c_int, [ctypes.POINTER(OldCache)]),
     "grpo_old_cache_record": (ctypes.c_int, [_p, ctypes.POINTER(OldCache), _i32, _p, _i64, _i64, _i64, _p, _p,
                                              ctypes.POINTER(ctypes.c_void_p)]),
     "grpo_old_cache_replay": (ctypes.c_int, [ctypes.POINTER(OldCache), _i64, ctypes.POINTER(ctypes.c_void_p)]),

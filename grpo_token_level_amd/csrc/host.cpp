@@ -76,6 +76,51 @@ extern "C" int grpo_plan_fixed(int64_t batch, int64_t group_size, int64_t mini, 
     return ok();
 }
 
+namespace {
+// splitmix64 (Steele, Lea and Flood, OOPSLA 2014): the state advances by the
+// golden-ratio increment; each output is the state through two
+// xor-shift-multiply rounds and a final xor-shift.
+struct SplitMix64 {
+    uint64_t state;
+    uint64_t next() {
+        state += 0x9E3779B97F4A7C15ull;
+        uint64_t z = state;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        return z ^ (z >> 31);
+    }
+};
+}  // namespace
+
+// [P3] section 1: epochs of the mini-batch iterator, reshuffled with a seed.
+// One generator stream, consumed epoch after epoch; the Fisher-Yates shuffle
+// (Knuth, Algorithm P) swaps item i with item (draw mod (i + 1)) for i from
+// the last down to 1.
+extern "C" int grpo_plan_epochs(int64_t batch, int64_t group_size, int64_t mini, int64_t micro, int64_t mu,
+                                int32_t shuffle, uint64_t seed, int64_t* n_mini, int64_t* n_micro,
+                                int64_t* mini_rows, int64_t* micro_rows, int64_t* perm) {
+    if (mu < 1) return fail(GRPO_EINVAL, "grpo_plan_epochs: mu (epochs) must be >= 1");
+    if (!perm) return fail(GRPO_EINVAL, "grpo_plan_epochs: NULL perm");
+    int64_t a, b, c, d;
+    const int rc = grpo_plan_fixed(batch, group_size, mini, micro, &a, &b, &c, &d);
+    if (rc != GRPO_OK) return rc;
+    SplitMix64 g{seed};
+    for (int64_t e = 0; e < mu; ++e) {
+        int64_t* p = perm + e * batch;
+        for (int64_t i = 0; i < batch; ++i) p[i] = i;
+        if (!shuffle) continue;
+        for (int64_t i = batch - 1; i >= 1; --i) {
+            const int64_t j = (int64_t)(g.next() % (uint64_t)(i + 1));
+            std::swap(p[i], p[j]);
+        }
+    }
+    *n_mini = a;
+    *n_micro = b;
+    *mini_rows = c;
+    *micro_rows = d;
+    return ok();
+}
+
 // [P1] "The core idea": chunk (i, j) is the j-th micro slice of the i-th mini
 // slice; the driver only ever names the indices.
 extern "C" int grpo_plan_chunk(int64_t batch, int64_t mini_rows, int64_t micro_rows, int64_t i_mini,
@@ -416,6 +461,16 @@ extern "C" int grpo_old_cache_record(void* stream, grpo_old_cache* c, int32_t dt
     c->off[k + 1] = at + n_tok;
     c->recorded = k + 1;
     if (slot) *slot = dst;
+    return ok();
+}
+
+// Inner epochs without a shuffle visit the chunks in the same order again:
+// the records are replayed from call 0.
+extern "C" int grpo_old_cache_rewind(grpo_old_cache* c) {
+    if (!c || !c->off || c->n_calls < 1) return fail(GRPO_EINVAL, "grpo_old_cache_rewind: uninitialised cache");
+    if (c->recorded != c->n_calls || c->replayed != c->n_calls)
+        return fail(GRPO_ESTATE, "grpo_old_cache_rewind: needs a complete recorded and replayed walk");
+    c->replayed = 0;
     return ok();
 }
 

@@ -209,7 +209,17 @@ struct TokParams {
     uint8_t* tok_flags;
     grpo_dev::Terms terms;   // row weights, entropy bonus, KL
     float* kl_tok;           // required when terms.ref_logp is set
+    const int64_t* tok_src;  // NULL, or the batch token row behind chunk token t
+    int64_t n_src;
 };
+
+// Batch row of chunk token t (t itself without a source map); -1 when the
+// map points outside the batch.
+__device__ __forceinline__ int64_t token_source(const TokParams& p, int64_t t) {
+    if (!p.tok_src) return t;
+    const int64_t s = p.tok_src[t];
+    return (uint64_t)s < (uint64_t)p.n_src ? s : -1;
+}
 
 // Per-token scalar tail shared by both kernels: from (max-shifted sums, z_y)
 // to logp / entropy / surrogate / gradient coefficient.  c = the log2-domain
@@ -222,8 +232,8 @@ struct TokenResult {
 };
 
 template <bool GRAD>
-__device__ __forceinline__ TokenResult token_tail(const TokParams& p, int64_t t, float c, float s, float w,
-                                                  float zy, bool ybad, bool write) {
+__device__ __forceinline__ TokenResult token_tail(const TokParams& p, int64_t t, int64_t src, float c, float s,
+                                                  float w, float zy, bool ybad, bool write) {
     const float log2s = log2f(s);
     const float c2 = c + log2s;
     const float lse = c2 * kLn2;
@@ -242,8 +252,8 @@ __device__ __forceinline__ TokenResult token_tail(const TokParams& p, int64_t t,
         const float A = ((uint32_t)row < (uint64_t)p.n_rows) ? p.adv_row[row] : __builtin_nanf("");
         const float sf = grpo_dev::token_factor(grpo_dev::step_scale(p.scale, p.denom), p.terms.row_weight, row,
                                                 p.n_rows);
-        const grpo_dev::Surrogate sg = grpo_dev::surrogate(logp, H, p.old_logp[t], A, p.eps_low, p.eps_high, sf,
-                                                           p.terms, t);
+        const grpo_dev::Surrogate sg = grpo_dev::surrogate(logp, H, p.old_logp[src], A, p.eps_low, p.eps_high, sf,
+                                                           p.terms, src);
         if (write) {
             p.logp[t] = logp;
             if (p.lse) p.lse[t] = lse;
@@ -276,6 +286,20 @@ __device__ __forceinline__ void masked_outputs(const TokParams& p, int64_t t) {
     }
 }
 
+// A chunk token whose source index is outside the batch: nothing V-sized is
+// touched; the token is reported valid and non-finite, which poisons the window.
+template <bool GRAD>
+__device__ __forceinline__ void bad_source_outputs(const TokParams& p, int64_t t) {
+    p.logp[t] = __builtin_nanf("");
+    if (p.lse) p.lse[t] = 0.0f;
+    if (p.entropy) p.entropy[t] = 0.0f;
+    if constexpr (GRAD) {
+        p.loss_tok[t] = 0.0f;
+        if (p.kl_tok) p.kl_tok[t] = 0.0f;
+        p.tok_flags[t] = 1u | 4u;
+    }
+}
+
 // dlogits value of one element with the entropy bonus on: p * (ea + eb * tt)
 // with p = 2^tt (an element with p = 0 contributes 0, also at z = -inf)
 __device__ __forceinline__ float dz_with_bonus(float tt, float ea, float eb) {
@@ -299,12 +323,17 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     if (t >= p.n_tok) return;   // wave-uniform (RPB > 1) or block-uniform (RPB == 1)
 
     const int nvec = (int)(p.V / VEC);   // the register path only runs for V / VEC <= TPR * NV
+    const int64_t src = token_source(p, t);
+    if (src < 0) {
+        if (tid == 0) bad_source_outputs<GRAD>(p, t);
+        return;
+    }
     void* orow = nullptr;
     if constexpr (GRAD) {
-        if (p.dlogits) orow = reinterpret_cast<char*>(p.dlogits) + t * p.ld_out * Out<DTO>::BYTES;
+        if (p.dlogits) orow = reinterpret_cast<char*>(p.dlogits) + src * p.ld_out * Out<DTO>::BYTES;
     }
 
-    if (p.mask[t] == 0) {
+    if (p.mask[src] == 0) {
         if (tid == 0) masked_outputs<GRAD>(p, t);
         if constexpr (GRAD) {
             if (orow) {
@@ -318,12 +347,12 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         return;
     }
 
-    const char* irow = reinterpret_cast<const char*>(p.logits) + t * p.ld * In<DTI>::BYTES;
+    const char* irow = reinterpret_cast<const char*>(p.logits) + src * p.ld * In<DTI>::BYTES;
     const uint4* vrow = reinterpret_cast<const uint4*>(irow);
 
     // Target logit: read by the one lane that owns element y (it alone later
     // writes dlogits[y], so an in-place update stays ordered).
-    const int32_t y = p.target[t];
+    const int32_t y = p.target[src];
     const bool ybad = (uint32_t)y >= (uint64_t)p.V;
     const int vy = ybad ? 0 : y / VEC;
     const int own_tid = vy % TPR;
@@ -407,7 +436,7 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         }
     }
 
-    const TokenResult r = token_tail<GRAD>(p, t, c, s, w, zy, ybad, tid == 0);
+    const TokenResult r = token_tail<GRAD>(p, t, src, c, s, w, zy, ybad, tid == 0);
     if constexpr (GRAD) {
         if (!orow) return;
         if (r.coef == 0.0f && r.eb == 0.0f) {   // zero advantage or clipped, no bonus: the row is zero
@@ -455,11 +484,16 @@ __global__ __launch_bounds__(256) void tok_generic_kernel(const TokParams p) {
     const int64_t t = blockIdx.x;
     if (t >= p.n_tok) return;
     const int tid = threadIdx.x;
+    const int64_t src = token_source(p, t);
+    if (src < 0) {
+        if (tid == 0) bad_source_outputs<GRAD>(p, t);
+        return;
+    }
     void* orow = nullptr;
     if constexpr (GRAD) {
-        if (p.dlogits) orow = reinterpret_cast<char*>(p.dlogits) + t * p.ld_out * Out<DTO>::BYTES;
+        if (p.dlogits) orow = reinterpret_cast<char*>(p.dlogits) + src * p.ld_out * Out<DTO>::BYTES;
     }
-    if (p.mask[t] == 0) {
+    if (p.mask[src] == 0) {
         if (tid == 0) masked_outputs<GRAD>(p, t);
         if constexpr (GRAD) {
             if (orow)
@@ -467,8 +501,8 @@ __global__ __launch_bounds__(256) void tok_generic_kernel(const TokParams p) {
         }
         return;
     }
-    const char* irow = reinterpret_cast<const char*>(p.logits) + t * p.ld * In<DTI>::BYTES;
-    const int32_t y = p.target[t];
+    const char* irow = reinterpret_cast<const char*>(p.logits) + src * p.ld * In<DTI>::BYTES;
+    const int32_t y = p.target[src];
     const bool ybad = (uint32_t)y >= (uint64_t)p.V;
     __shared__ float s_max[WPR];
     __shared__ float s_sum[WPR][2];
@@ -506,7 +540,7 @@ __global__ __launch_bounds__(256) void tok_generic_kernel(const TokParams p) {
         s += s_sum[i][0];
         w += s_sum[i][1];
     }
-    const TokenResult r = token_tail<GRAD>(p, t, c, s, w, zy, ybad, tid == 0);
+    const TokenResult r = token_tail<GRAD>(p, t, src, c, s, w, zy, ybad, tid == 0);
     if constexpr (GRAD) {
         if (!orow) return;
         for (int64_t v = tid; v < p.V; v += TPR) {
@@ -756,6 +790,40 @@ __global__ __launch_bounds__(1024) void probe_compare_kernel(const float* __rest
     }
 }
 
+// tok_src of a chunk made of batch rows laid end to end (binary search of
+// the chunk's row offsets per token).
+__global__ __launch_bounds__(256) void chunk_tok_src_kernel(const int64_t* __restrict__ src_row_off,
+                                                            int64_t n_src_rows, const int64_t* __restrict__ rows,
+                                                            int64_t n_rows, const int64_t* __restrict__ dst_row_off,
+                                                            int64_t n_tok, int64_t* __restrict__ tok_src) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n_tok) return;
+    if (n_rows <= 0 || dst_row_off[0] > t) {
+        tok_src[t] = -1;
+        return;
+    }
+    int64_t lo = 0, hi = n_rows;
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (dst_row_off[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    const int64_t r = rows[lo];
+    tok_src[t] = (t < dst_row_off[lo + 1] && (uint64_t)r < (uint64_t)n_src_rows)
+                     ? src_row_off[r] + (t - dst_row_off[lo])
+                     : -1;
+}
+
+// dst[k] = src[idx[k]] for elements of EB bytes; out-of-range indices give 0.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ src, int64_t n_src,
+                                                     const int64_t* __restrict__ idx, int64_t n, T* __restrict__ dst) {
+    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (k >= n) return;
+    const int64_t i = idx[k];
+    dst[k] = (uint64_t)i < (uint64_t)n_src ? src[i] : T(0);
+}
+
 __global__ __launch_bounds__(256) void tok_row_kernel(const int64_t* __restrict__ row_off, int64_t n_rows,
                                                       int64_t n_tok, int32_t* __restrict__ tok_row) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -888,6 +956,36 @@ extern "C" int grpo_probe_compare(void* stream, const float* recorded, const flo
     return check_launch(hipGetLastError(), "grpo_probe_compare");
 }
 
+extern "C" int grpo_chunk_tok_src(void* stream, const int64_t* src_row_off, int64_t n_src_rows, const int64_t* rows,
+                                  int64_t n_rows, const int64_t* dst_row_off, int64_t n_tok, int64_t* tok_src) {
+    if (n_tok < 0 || n_rows < 0 || n_src_rows < 0 ||
+        (n_tok > 0 && (!tok_src || !dst_row_off || (n_rows > 0 && (!rows || !src_row_off)))))
+        return fail(GRPO_EINVAL, "grpo_chunk_tok_src: bad arguments");
+    if (n_tok == 0) return ok();
+    if ((n_tok + 255) / 256 > 0x7fffffffLL) return fail(GRPO_EINVAL, "grpo_chunk_tok_src: too many tokens");
+    hipLaunchKernelGGL(chunk_tok_src_kernel, dim3((unsigned)((n_tok + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, src_row_off, n_src_rows, rows, n_rows, dst_row_off, n_tok, tok_src);
+    return check_launch(hipGetLastError(), "grpo_chunk_tok_src");
+}
+
+extern "C" int grpo_gather(void* stream, const void* src, int64_t n_src, const int64_t* idx, int64_t n,
+                           int64_t elem_bytes, void* dst) {
+    if (n < 0 || n_src < 0 || (n > 0 && (!idx || !dst || (n_src > 0 && !src))))
+        return fail(GRPO_EINVAL, "grpo_gather: bad arguments");
+    if (n == 0) return ok();
+    if ((n + 255) / 256 > 0x7fffffffLL) return fail(GRPO_EINVAL, "grpo_gather: too many elements");
+    const dim3 g((unsigned)((n + 255) / 256)), b(256);
+    hipStream_t st = (hipStream_t)stream;
+    switch (elem_bytes) {
+        case 1: hipLaunchKernelGGL(gather_kernel<uint8_t>, g, b, 0, st, (const uint8_t*)src, n_src, idx, n, (uint8_t*)dst); break;
+        case 2: hipLaunchKernelGGL(gather_kernel<uint16_t>, g, b, 0, st, (const uint16_t*)src, n_src, idx, n, (uint16_t*)dst); break;
+        case 4: hipLaunchKernelGGL(gather_kernel<uint32_t>, g, b, 0, st, (const uint32_t*)src, n_src, idx, n, (uint32_t*)dst); break;
+        case 8: hipLaunchKernelGGL(gather_kernel<uint64_t>, g, b, 0, st, (const uint64_t*)src, n_src, idx, n, (uint64_t*)dst); break;
+        default: return fail(GRPO_EINVAL, "grpo_gather: elem_bytes must be 1, 2, 4 or 8");
+    }
+    return check_launch(hipGetLastError(), "grpo_gather");
+}
+
 extern "C" int grpo_tok_row(void* stream, const int64_t* row_off, int64_t n_rows, int64_t n_tok, int32_t* tok_row) {
     if (n_tok < 0 || n_rows < 0 || (n_tok > 0 && (!tok_row || !row_off)))
         return fail(GRPO_EINVAL, "grpo_tok_row: bad arguments");
@@ -941,10 +1039,13 @@ extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
         if (rc != GRPO_OK) return rc;
     }
     const int in_b = di == GRPO_BF16 ? 2 : 4, out_b = dout == GRPO_BF16 ? 2 : 4;
+    if (a->tok_src && a->n_src < 1) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: tok_src needs n_src >= 1");
     if (a->dlogits && a->n_tok > 0) {
         if (a->ld_out < a->V) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: ld_out < V");
-        const uintptr_t i0 = (uintptr_t)a->logits, i1 = i0 + (uintptr_t)((a->n_tok - 1) * a->ld + a->V) * in_b;
-        const uintptr_t o0 = (uintptr_t)a->dlogits, o1 = o0 + (uintptr_t)((a->n_tok - 1) * a->ld_out + a->V) * out_b;
+        // rows that may be touched: the chunk's own, or every batch row behind tok_src
+        const int64_t span = a->tok_src ? a->n_src : a->n_tok;
+        const uintptr_t i0 = (uintptr_t)a->logits, i1 = i0 + (uintptr_t)((span - 1) * a->ld + a->V) * in_b;
+        const uintptr_t o0 = (uintptr_t)a->dlogits, o1 = o0 + (uintptr_t)((span - 1) * a->ld_out + a->V) * out_b;
         const bool overlap = o0 < i1 && i0 < o1;
         if (overlap && !(o0 == i0 && di == dout && a->ld == a->ld_out))
             return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: dlogits overlaps logits without being the same buffer");
@@ -958,6 +1059,8 @@ extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
     p.logp = a->logp; p.lse = a->lse; p.entropy = a->entropy; p.loss_tok = a->loss_tok; p.tok_flags = a->tok_flags;
     p.terms = grpo_dev::Terms{a->row_weight, a->ref_logp, a->ent_coef, a->kl_coef, a->kl_type};
     p.kl_tok = a->ref_logp ? a->kl_tok : nullptr;
+    p.tok_src = a->tok_src;
+    p.n_src = a->n_src;
     const int vec = di == GRPO_BF16 ? 8 : 4;
     bool vec_ok = aligned16(a->logits) && a->ld % vec == 0 && a->V % vec == 0;
     if (a->dlogits) vec_ok = vec_ok && aligned16(a->dlogits) && (a->ld_out * out_b) % 16 == 0 && ((int64_t)vec * out_b) % 8 == 0;

@@ -34,6 +34,17 @@ def plan_chunk(batch, mini_rows, micro_rows, i_mini, j_micro):
     return b.value, e.value
 
 
+def plan_epochs(batch, group_size, mini=0, micro=0, mu=1, shuffle=False, seed=0):
+    """Inner epochs with an optional seeded shuffle -> dict(n_mini, n_micro,
+    mini_rows, micro_rows, mu, perm [mu x batch] int64).  See grpo_plan_epochs."""
+    o = [ctypes.c_int64() for _ in range(4)]
+    perm = np.zeros(max(mu, 1) * max(batch, 1), np.int64)
+    C.check(C.lib().grpo_plan_epochs(batch, group_size, mini, micro, mu, 1 if shuffle else 0, seed & (2 ** 64 - 1),
+                                     *[ctypes.byref(x) for x in o], C.ptr64(perm)))
+    return {"n_mini": o[0].value, "n_micro": o[1].value, "mini_rows": o[2].value, "micro_rows": o[3].value,
+            "mu": mu, "perm": perm[:mu * batch].reshape(mu, batch)}
+
+
 def plan_dynamic(lengths, token_budget, proxy_div=4096):
     """Token-budget packing -> dict(n_bins, bin_off, order, restore) (int64 arrays)."""
     L = np.ascontiguousarray(lengths, dtype=np.int64)
@@ -168,6 +179,10 @@ class OldLogprobCache:
                                               _dev(mask, "mask"), ctypes.byref(slot)))
         return self._view(slot.value or 0, n)
 
+    def rewind(self):
+        """Replay the records again from call 0 (the next unshuffled epoch)."""
+        C.check(C.lib().grpo_old_cache_rewind(ctypes.byref(self.c)))
+
     def replay(self, n_tok):
         """pi_old of the next training call (a view of the buffer)."""
         ptr = ctypes.c_void_p()
@@ -295,6 +310,29 @@ def row_weights(mask, row_off, mode, n_seq, out=None):
     return out
 
 
+def chunk_tok_src(src_row_off, rows, dst_row_off, out=None):
+    """Batch token index of each token of a chunk of batch ``rows`` (device
+    int64 tensors), grpo_chunk_tok_src."""
+    torch = _torch()
+    n_tok = int(dst_row_off[-1].item()) if out is None else out.numel()
+    if out is None:
+        out = torch.empty(max(n_tok, 1), dtype=torch.int64, device=rows.device)
+    C.check(C.lib().grpo_chunk_tok_src(_stream(), _dev(src_row_off, "src_row_off"), src_row_off.numel() - 1,
+                                       _dev(rows, "rows"), rows.numel(), _dev(dst_row_off, "dst_row_off"), n_tok,
+                                       _dev(out, "tok_src")))
+    return out[:n_tok]
+
+
+def gather(src, idx, out=None):
+    """dst[k] = src[idx[k]] on the device (grpo_gather); 1-, 2-, 4- or 8-byte elements."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(idx.numel(), dtype=src.dtype, device=src.device)
+    C.check(C.lib().grpo_gather(_stream(), _dev(src, "src"), src.numel(), _dev(idx, "idx"), idx.numel(),
+                                src.element_size(), _dev(out, "dst")))
+    return out
+
+
 def tok_row(row_off, n_tok, out=None):
     torch = _torch()
     if out is None:
@@ -341,7 +379,7 @@ def _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws):
 
 def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, scale=1.0, denom=None,
                  eps_low=0.2, eps_high=0.2, dlogits="new", out_dtype=None, ws=None, row_weight=None,
-                 ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3):
+                 ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3, tok_src=None):
     """Fused GRPO loss forward/backward over one chunk (grpo_loss_fwd_bwd).
 
     ``dlogits``: "new" (allocate, dtype ``out_dtype`` or the logits dtype),
@@ -349,15 +387,20 @@ def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, 
     ``row_weight`` / ``ref_logp`` / ``ent_coef`` / ``kl_coef`` / ``kl_type``:
     the aggregation weights and extra terms (``ws["kl_tok"]`` receives the
     per-token KL when ``ref_logp`` is given).
+    ``tok_src``: a chunk of batch rows in any order -- ``logits``,
+    ``target``, ``mask``, ``old_logp``, ``ref_logp`` and ``dlogits`` are then
+    the whole batch's, read and written at tok_src[t]; the chunk's token count
+    is tok_src's length.
     Returns the workspace dict with ``dlogits`` added."""
     torch = _torch()
     ld = _rows2d(logits, "logits")
-    n, V = logits.shape
+    n_src, V = logits.shape
+    n = tok_src.numel() if tok_src is not None else n_src
     n_rows = row_off.numel() - 1
     if ws is None:
         ws = loss_workspace(n, n_rows, logits.device)
     if isinstance(dlogits, str) and dlogits == "new":
-        dl = torch.empty((n, V), dtype=out_dtype or logits.dtype, device=logits.device)
+        dl = torch.empty((n_src, V), dtype=out_dtype or logits.dtype, device=logits.device)
     elif isinstance(dlogits, str) and dlogits == "inplace":
         dl = logits
     else:
@@ -390,6 +433,11 @@ def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, 
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor (libgrpo has no CPU path)")
     _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws)
+    if tok_src is not None:
+        if not tok_src.is_cuda or tok_src.dtype != torch.int64:
+            raise ValueError("tok_src must be an int64 GPU tensor")
+        a.tok_src = tok_src.data_ptr() if n else None
+        a.n_src = n_src
     C.check(C.lib().grpo_loss_fwd_bwd(_stream(), ctypes.byref(a)))
     ws["dlogits"] = dl
     return ws

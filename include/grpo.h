@@ -105,6 +105,22 @@ int grpo_plan_fixed(int64_t batch, int64_t group_size, int64_t mini, int64_t mic
 int grpo_plan_chunk(int64_t batch, int64_t mini_rows, int64_t micro_rows,
                     int64_t i_mini, int64_t j_micro, int64_t* row_begin, int64_t* row_end);
 
+/* host.  Inner epochs over one collected batch with an optional seeded
+ * shuffle ([P3] section 1: each update gets the mini-batch size, the number
+ * of epochs and a shuffle flag with a data-loader seed, and the iterator
+ * yields the mini-batches again each epoch; [P1] "What's not done", item 2:
+ * inner epochs reuse the frozen pi_old of the ahead pass unchanged).  The
+ * levels are sized as grpo_plan_fixed (same errors); mu >= 1 (EINVAL).
+ * perm[mu * batch]: epoch e visits rows perm[e*batch .. e*batch + batch) in
+ * order -- the identity without shuffle, else the Fisher-Yates permutation
+ * (for i = batch-1 down to 1 swap items i and draw mod (i+1)) driven by one
+ * splitmix64 stream seeded with `seed` (Steele, Lea and Flood 2014) consumed
+ * epoch after epoch.  Chunk (e, i, j) is rows
+ * perm[e*batch + i*mini_rows + j*micro_rows ..  + micro_rows). */
+int grpo_plan_epochs(int64_t batch, int64_t group_size, int64_t mini, int64_t micro, int64_t mu, int32_t shuffle,
+                     uint64_t seed, int64_t* n_mini, int64_t* n_micro, int64_t* mini_rows, int64_t* micro_rows,
+                     int64_t* perm);
+
 /* host.  Token-budget dynamic packing ([P3] section 3).  len[n_rows] are row
  * token counts (>= 0).  A row longer than token_budget -> ETOOLONG.  Boxes
  * start at max(1, ceil(sum(len) / budget)); workload w = proxy_div*L + L*L;
@@ -187,6 +203,24 @@ int grpo_count_rows(void* stream, const uint8_t* mask, const int64_t* row_off, i
 int grpo_row_weights(void* stream, const uint8_t* mask, const int64_t* row_off, int64_t n_rows, int64_t n_tok,
                      int32_t mode, const int64_t* n_seq, float* w_row);
 
+/* device.  Chunk resolution from indices ([P1] "The core idea": the driver
+ * passes indices only): tok_src[t] = src_row_off[rows[r]] + (t - dst_row_off[r])
+ * for dst_row_off[r] <= t < dst_row_off[r+1], i.e. the batch token index of
+ * every token of a chunk made of batch rows `rows` laid end to end.
+ * src_row_off: device int64 [n_src_rows + 1] (batch layout); rows: device
+ * int64 [n_rows] in [0, n_src_rows); dst_row_off: device int64 [n_rows + 1],
+ * dst_row_off[r+1] - dst_row_off[r] = that row's length.  A row index out of
+ * range gives -1 for its tokens. */
+int grpo_chunk_tok_src(void* stream, const int64_t* src_row_off, int64_t n_src_rows, const int64_t* rows,
+                       int64_t n_rows, const int64_t* dst_row_off, int64_t n_tok, int64_t* tok_src);
+
+/* device.  dst[k] = src[idx[k]] for k < n, elements of elem_bytes (1, 2, 4
+ * or 8) bytes: per-row or per-token values of a chunk whose rows sit anywhere
+ * in the batch (advantages, aggregation weights, cached pi_old).  idx[k]
+ * outside [0, n_src) writes zero bytes. */
+int grpo_gather(void* stream, const void* src, int64_t n_src, const int64_t* idx, int64_t n, int64_t elem_bytes,
+                void* dst);
+
 /* device.  tok_row[t] = the row r with row_off[r] <= t < row_off[r+1]
  * (row_off: device int64 [n_rows + 1], non-decreasing), or -1 if none. */
 int grpo_tok_row(void* stream, const int64_t* row_off, int64_t n_rows, int64_t n_tok, int32_t* tok_row);
@@ -242,6 +276,14 @@ typedef struct grpo_loss_args {
     float kl_coef;              /* KL weight: the token's objective gains +kl_coef * KL (needs ref_logp) */
     int32_t kl_type;            /* GRPO_KL_K1 / K2 / K3 (read when ref_logp is set) */
     int32_t reserved2;          /* 0 */
+    /* Chunks of batch rows in any order (shuffled epochs) without copies. */
+    const int64_t* tok_src;     /* NULL, or [n_tok] (grpo_chunk_tok_src): token t's logits, dlogits, target,
+                                   mask, old_logp and ref_logp are those of batch token tok_src[t]; the
+                                   per-token outputs, tok_row, adv_row, row_weight, row_off and the stats stay
+                                   chunk-local.  Entries must be distinct when dlogits is written. */
+    int64_t n_src;              /* batch token rows behind logits / dlogits / the per-token inputs when
+                                   tok_src is set (a tok_src[t] outside [0, n_src) makes token t non-finite,
+                                   with no V-sized access) */
 } grpo_loss_args;
 
 /* device.  Fused forward and backward of the token-level GRPO loss over one
@@ -373,6 +415,12 @@ int grpo_old_cache_reset(grpo_old_cache* c);
  * ECAPACITY when the record does not fit in buf. */
 int grpo_old_cache_record(void* stream, grpo_old_cache* c, int32_t dtype, const void* logits, int64_t ld,
                           int64_t n_tok, int64_t V, const int32_t* target, const uint8_t* mask, float** slot);
+/* host.  After a complete walk was recorded and replayed, starts the next
+ * inner epoch's replay from call 0 (same order: unshuffled epochs reuse the
+ * records by call order).  ESTATE otherwise.  A shuffled epoch reads pi_old
+ * per token instead: with the ahead walk in batch order, buf holds the whole
+ * batch's pi_old in batch token order, and grpo_loss_args.tok_src selects it. */
+int grpo_old_cache_rewind(grpo_old_cache* c);
 /* host.  pi_old of the next training call: *old_logp = buf + off[k], k =
  * c->replayed (device float [n_tok], as grpo_loss_args.old_logp).  ESTATE if
  * call k was not recorded; EINVAL if n_tok differs from record k's token

@@ -32,7 +32,9 @@ parity unpinned, because the pages name no algorithm).
 """
 
 from .plans import (PlanError, plan_fixed, chunk_rows, train_calls,
-                    plan_dynamic, plan_compaction, compaction_micro_chunks)
+                    plan_dynamic, plan_compaction, compaction_micro_chunks,
+                    splitmix64_stream, fisher_yates, plan_epochs, epoch_chunk_rows,
+                    epoch_train_calls)
 from .advantage import group_advantage, rows_advantage
 from .loss import (round_to_bf16, token_forward, surrogate, loss_fwd_bwd,
                    logprob_fwd, chunk_stats, row_stats, valid_count, kl_term,
@@ -42,7 +44,7 @@ from .agg import (AGG_TOKEN_MEAN, AGG_SEQ_MEAN_TOKEN_SUM, AGG_SEQ_MEAN_TOKEN_MEA
 from .accum import Accumulator, ACC_OK, ACC_NONFINITE, ACC_SKIPPED
 from .lmhead import lmhead_fwd_bwd
 from .cache import (CacheError, needs_ahead_pass, OldLogprobCache, probe_compare, Probe,
-                    PROBE_STRICT_BOUND, PROBE_STRICT_FRACTION)
+                    PROBE_STRICT_BOUND, PROBE_STRICT_FRACTION, gather, chunk_token_sources)
 
 __all__ = [
     "PlanError", "plan_fixed", "chunk_rows", "train_calls", "plan_dynamic",
@@ -54,4 +56,6 @@ __all__ = [
     "AGG_SEQ_MEAN_TOKEN_SUM", "AGG_SEQ_MEAN_TOKEN_MEAN", "row_valid_counts",
     "count_rows", "agg_loss", "row_weights", "CacheError", "needs_ahead_pass",
     "OldLogprobCache", "probe_compare", "Probe", "PROBE_STRICT_BOUND", "PROBE_STRICT_FRACTION",
+    "splitmix64_stream", "fisher_yates", "plan_epochs", "epoch_chunk_rows", "epoch_train_calls",
+    "gather", "chunk_token_sources",
 ]

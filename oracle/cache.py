@@ -77,6 +77,14 @@ class OldLogprobCache:
         self.used += n
         return len(self.records) - 1
 
+    def rewind(self):
+        """Start the next inner epoch's replay from call 0 ([P1] "What's not
+        done", item 2: inner epochs reuse the frozen pi_old unchanged); only
+        after a complete walk was recorded and replayed."""
+        if not (len(self.records) == self.n_calls and self.replayed == self.n_calls):
+            raise CacheError("ESTATE", "rewind needs a complete recorded and replayed walk")
+        self.replayed = 0
+
     def replay(self, n_tok):
         k = self.replayed
         if k >= len(self.records):
@@ -85,6 +93,23 @@ class OldLogprobCache:
             raise CacheError("EINVAL", "the training walk diverged from the ahead walk (token count)")
         self.replayed += 1
         return self.records[k]
+
+
+def gather(src, idx):
+    """dst[k] = src[idx[k]]: the per-token (or per-row) values of a chunk whose
+    rows sit anywhere in the batch ([P1] "The core idea": the driver passes
+    indices only and the chunk is resolved from them)."""
+    return [src[i] for i in idx]
+
+
+def chunk_token_sources(src_row_off, rows):
+    """Batch token index of every token of a chunk made of ``rows`` (in
+    order): row r's tokens src_row_off[r] .. src_row_off[r+1]-1, rows end to
+    end."""
+    out = []
+    for r in rows:
+        out.extend(range(src_row_off[r], src_row_off[r + 1]))
+    return out
 
 
 def probe_compare(recorded, rescored, mask, bound):

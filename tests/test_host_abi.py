@@ -270,3 +270,38 @@ def test_old_cache_state_machine_without_device_work():
     assert L.grpo_old_cache_record(None, ctypes.byref(c), 1, ctypes.c_void_p(16), 8, 4, 8, ctypes.c_void_p(16),
                                    ctypes.c_void_p(16), None) == -7
     assert L.grpo_old_cache_init(ctypes.byref(c), None, 0, C.ptr64(off), 0) == -1
+
+
+def test_epoch_plan_matches_oracle_bit_exact():
+    rng = np.random.default_rng(6)
+    cases = [(32, 4, 16, 8, 3, True, 7), (32, 4, 16, 8, 2, False, 7), (8, 2, 4, 2, 1, True, 0),
+             (1, 1, 0, 0, 4, True, 2 ** 64 - 1), (30, 3, 10, 5, 2, True, 12345)]
+    for _ in range(60):
+        G = int(rng.integers(1, 5))
+        B = G * int(rng.integers(1, 20))
+        cases.append((B, G, 0, 0, int(rng.integers(1, 4)), bool(rng.integers(0, 2)), int(rng.integers(0, 2 ** 63))))
+    for B, G, mini, micro, mu, sh, seed in cases:
+        want = oracle.plan_epochs(B, G, mini, micro, mu, sh, seed)
+        got = ops.plan_epochs(B, G, mini, micro, mu, sh, seed)
+        for k in ("n_mini", "n_micro", "mini_rows", "micro_rows"):
+            assert got[k] == want[k]
+        assert got["perm"].tolist() == want["perm"], (B, mu, sh, seed)
+    for bad in ((32, 4, 16, 8, 0, True, 1), (32, 4, 12, 0, 2, True, 1), (0, 4, 0, 0, 1, False, 1)):
+        w, wk = _kind(oracle.plan_epochs, *bad)
+        g, gk = _kind(ops.plan_epochs, *bad)
+        assert gk == wk, bad
+
+
+def test_old_cache_rewind_without_device_work():
+    c = C.OldCache()
+    off = np.zeros(3, np.int64)
+    L = C.lib()
+    assert L.grpo_old_cache_init(ctypes.byref(c), None, 0, C.ptr64(off), 2) == 0
+    for _ in range(2):
+        assert L.grpo_old_cache_record(None, ctypes.byref(c), 1, None, 8, 0, 8, None, None, None) == 0
+    assert L.grpo_old_cache_rewind(ctypes.byref(c)) == -9          # not replayed yet
+    ptr = ctypes.c_void_p()
+    for _ in range(2):
+        assert L.grpo_old_cache_replay(ctypes.byref(c), 0, ctypes.byref(ptr)) == 0
+    assert L.grpo_old_cache_rewind(ctypes.byref(c)) == 0 and c.replayed == 0
+    assert L.grpo_old_cache_replay(ctypes.byref(c), 0, ctypes.byref(ptr)) == 0

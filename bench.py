@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--shuffle", action="store_true",
                     help="padded workloads: reshuffle the rows every epoch (seeded); chunks read the batch through "
                          "tok_src")
+    ap.add_argument("--cpu-pool-seconds", type=float, default=8.0,
+                    help="wall seconds of the oracle over a process pool (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     return ap.parse_args()
@@ -284,10 +286,10 @@ class PaddedStep:
         torch.cuda.synchronize()
         return 3 * 2 * src.numel() * src.element_size() / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
-    def sample(self, n):
-        """(z float64 [n, V], target, drift, advantage) of the first n valid tokens."""
+    def sample(self, n, start=0):
+        """(z float64 [n, V], target, drift, advantage) of valid tokens start .. start+n."""
         torch, b = self.torch, self.b
-        idx = np.nonzero(b["mask"])[0][:n]
+        idx = np.nonzero(b["mask"])[0][start:start + n]
         z = self.logits[torch.as_tensor(idx, device="cuda")].double().cpu().numpy()
         adv = np.random.default_rng(1).normal(0, 1, b["n_rows"])[idx // b["T"]]
         return z, b["target"][idx], b["logratio_noise"][idx], adv
@@ -376,9 +378,9 @@ class DynamicStep(PaddedStep):
             acc.add(s)
         return [acc.finalize()]
 
-    def sample(self, n):
+    def sample(self, n, start=0):
         torch = self.torch
-        idx = np.arange(min(n, self.logits.shape[0]))
+        idx = np.arange(start, min(start + n, self.logits.shape[0]))
         z = self.logits[torch.as_tensor(idx, device="cuda")].double().cpu().numpy()
         adv = np.random.default_rng(1).normal(0, 1, len(idx))
         return z, self.target[:len(idx)].cpu().numpy(), np.zeros(len(idx)), adv
@@ -472,26 +474,91 @@ class CompactStep:
 
 # ---------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(step, budget_s):
-    """The oracle, as it stands, on the first valid tokens of the benched batch
-    until ``budget_s`` seconds of compute have run (one process)."""
+def _oracle_block(z, y, drift, adv):
+    """The oracle on one block of tokens; returns (tokens, seconds of compute)."""
     import oracle
+    m = np.ones(len(y), np.uint8)
+    old = oracle.logprob_fwd(z, y, m)["logp"] + drift
+    t0 = time.perf_counter()
+    oracle.loss_fwd_bwd(z, y, m, old, adv, 1e-5)
+    return len(y), time.perf_counter() - t0
+
+
+_SHM = {}
+
+
+def _oracle_pool_worker(args):
+    """One pool task: tokens [a, b) of the shared float64 logits block."""
+    from multiprocessing import shared_memory
+    name, shape, a, b, y, drift, adv = args
+    if name not in _SHM:
+        for old in list(_SHM):
+            _SHM.pop(old).close()
+        _SHM[name] = shared_memory.SharedMemory(name=name)
+    z = np.ndarray(shape, dtype=np.float64, buffer=_SHM[name].buf)
+    return _oracle_block(z[a:b], y, drift, adv)
+
+
+def cpu_baseline(step, budget_s, block=1024):
+    """The oracle, as it stands, on the benched batch's valid tokens, streamed
+    to the host 1024 at a time (float64), until ``budget_s`` seconds of
+    compute have run (one process)."""
     done, t_used, pos = 0, 0.0, 0
-    z_all, y_all, drift, adv_all = step.sample(4096)
-    V = z_all.shape[1]
-    while t_used < budget_s and pos < len(y_all):
-        sl = slice(pos, pos + 16)
-        pos += 16
-        z, y = z_all[sl], y_all[sl]
-        m = np.ones(len(y), np.uint8)
-        old = oracle.logprob_fwd(z, y, m)["logp"] + drift[sl]
-        t0 = time.perf_counter()
-        oracle.loss_fwd_bwd(z, y, m, old, adv_all[sl], 1e-5)
-        t_used += time.perf_counter() - t0
-        done += len(y)
+    V = None
+    while t_used < budget_s:
+        z_all, y_all, drift, adv_all = step.sample(block, pos)
+        if len(y_all) == 0:
+            break
+        V = z_all.shape[1]
+        for a in range(0, len(y_all), 16):
+            n, dt = _oracle_block(z_all[a:a + 16], y_all[a:a + 16], drift[a:a + 16], adv_all[a:a + 16])
+            done += n
+            t_used += dt
+            if t_used >= budget_s:
+                break
+        pos += block
+        del z_all
     return {"value": round(done / t_used, 1), "unit": "valid tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} valid tokens of the benched batch (V={V}, float64 numpy, one process), "
+            "sample": f"the first {done} valid tokens of the benched batch (V={V}, float64 numpy, one process), "
                       f"{t_used:.1f} s of compute"}
+
+
+def cpu_baseline_pool(step, budget_s, block=1024):
+    """The same oracle over a multiprocessing pool on the cores this process
+    may run on (at most 16), blocks of 16 tokens per task; wall time of the
+    pool's compute.  Spawned workers: they never touch the GPU."""
+    import multiprocessing as mp
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    done, wall, pos = 0, 0.0, 0
+    ctx = mp.get_context("spawn")
+    from multiprocessing import shared_memory
+    with ctx.Pool(cores) as pool:
+        while wall < budget_s:
+            z_all, y_all, drift, adv_all = step.sample(block, pos)
+            if len(y_all) == 0:
+                break
+            shm = shared_memory.SharedMemory(create=True, size=z_all.nbytes)
+            try:
+                np.ndarray(z_all.shape, dtype=np.float64, buffer=shm.buf)[:] = z_all
+                tasks = [(shm.name, z_all.shape, a, a + 16, y_all[a:a + 16], drift[a:a + 16], adv_all[a:a + 16])
+                         for a in range(0, len(y_all), 16)]
+                t0 = time.perf_counter()
+                done += sum(n for n, _ in pool.map(_oracle_pool_worker, tasks))
+                wall += time.perf_counter() - t0
+            finally:
+                shm.close()
+                shm.unlink()
+            pos += block
+            del z_all
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(done / wall, 1), "unit": "valid tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} valid tokens of the benched batch, blocks of 1024 in shared memory, 16-token "
+                      f"tasks over a {cores}-process pool, {wall:.1f} s wall" + (f" ({model})" if model else "")}
 
 
 def main():
@@ -582,6 +649,8 @@ def main():
         torch.cuda.synchronize()
     if args.cpu_seconds > 0 and hasattr(step, "sample"):
         out["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
+        if args.cpu_pool_seconds > 0:
+            out["cpu_baseline_pool"] = cpu_baseline_pool(step, args.cpu_pool_seconds)
     print(json.dumps(out), flush=True)
 
 

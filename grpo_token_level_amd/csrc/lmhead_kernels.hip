@@ -24,11 +24,11 @@
 // operands K-contiguous ("NT"): W for pass 1, W^T for dh, h^T and dz^T for dW.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16.  A 512-thread block computes a 256x256 tile
-// (eight waves in 4 x 2, each 64x128 = 2x4 MFMA tiles).  K advances 32 at a
-// time through a four-stage LDS ring (32 KiB per stage) filled by
-// global_load_lds (16 bytes per lane straight into LDS, no register
-// staging), three stages in flight; rows past the edge and k past the end
-// load from a zero page.  Lane layouts (checked on the device): operand lane
+// (eight waves in 4 x 2, each 64x128 = 2x4 MFMA tiles).  K advances 64 at a
+// time through two LDS stages of 64 KiB (one loading while the other feeds
+// the MFMAs), filled by global_load_lds (16 bytes per lane straight into
+// LDS, no register staging; a tile row is one 128-byte line per stage); rows
+// past the edge and k past the end load from a zero page.  Lane layouts (checked on the device): operand lane
 // l holds row/column l%32 and k = (l/32)*8 .. +8; result lane l, register i
 // holds column l%32 and row (i/4)*8 + (l/32)*4 + i%4.  Blocks are mapped so
 // that each XCD works through a contiguous range of tiles, the index with
@@ -56,15 +56,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256, BN = 256;    // block tile
-constexpr int BK = 32;               // k per LDS stage
-constexpr int NST = 4;               // LDS stages (ring)
-constexpr int PREF = 3;              // stages in flight ahead of the one being consumed
+constexpr int BK = 64;               // k per LDS stage (one 128-byte line per tile row)
+constexpr int NST = 2;               // LDS stages: one loading while the other is consumed
 constexpr int NTHREADS = 512;        // eight waves in 4 (M) x 2 (N), each owning a 64 x 128 sub-tile
 constexpr int WM = 64, WN = 128;     // wave tile
 constexpr int FM = WM / 32, FN = WN / 32;
 constexpr int ROWB = BK * 2;         // bytes of one tile row in one stage
-constexpr int OPB = BM * ROWB;       // bytes of one operand in one stage (16 KiB)
-constexpr int STB = 2 * OPB;         // bytes of one stage (32 KiB)
+constexpr int OPB = BM * ROWB;       // bytes of one operand in one stage (32 KiB)
+constexpr int STB = 2 * OPB;         // bytes of one stage (64 KiB)
 constexpr int EPI_ROW = WN + 1;      // floats per row of a wave's epilogue buffer (row-wise reads)
 constexpr int EPI_ROW_Q = WN + 4;    // the same for 16-byte column-quad reads
 constexpr int EPIB = 8 * 32 * EPI_ROW_Q * 4;
@@ -135,10 +134,10 @@ __device__ __forceinline__ int xcd_logical(int b, int nb) {
     return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
-// LDS rows are 64 bytes (four 16-byte k chunks); chunk c of row r is stored
-// at position c ^ swz(r), which spreads the 16-byte fragment reads of 32
+// LDS rows are 128 bytes (eight 16-byte k chunks); chunk c of row r is
+// stored at position c ^ swz(r), which spreads the 16-byte fragment reads of
 // consecutive rows over all banks.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
@@ -162,23 +161,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
     // Direct-to-LDS loads: one global_load_lds moves 64 lanes x 16 bytes to
-    // LDS base + 16*lane, i.e. 16 tile rows of 64 bytes.  Wave w fills rows
-    // (2w+q)*16 .. +16 of each operand (q < 2); lane l takes row (l/4) of
-    // those and stores k chunk (l%4) ^ swz(row) at LDS position l%4.
-    const int lr = lane >> 2, lp = lane & 3;
+    // LDS base + 16*lane, i.e. 8 tile rows of 128 bytes.  Wave w fills rows
+    // (4w+q)*8 .. +8 of each operand (q < 4); lane l takes row (l/8) of those
+    // and stores k chunk (l%8) ^ swz(row) at LDS position l%8.
+    const int lr = lane >> 3, lp = lane & 7;
     auto issue = [&](int kt) {
         char* st = smem + (kt % NST) * STB;
         const int k0 = kbeg + kt * BK;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int r = (wave * 2 + q) * 16 + lr;
+        for (int q = 0; q < 4; ++q) {
+            const int r = (wave * 4 + q) * 8 + lr;
             const int k = k0 + ((lp ^ swz(r)) << 3);
             const bool kin = k < kend;
             const int ma = m0 + r, nb = n0 + r;
             const uint16_t* ga = (ma < g.M && kin) ? g.A + (int64_t)ma * g.lda + k : g_zero_page;
             const uint16_t* gb = (nb < g.N && kin) ? g.B + (int64_t)nb * g.ldb + k : g_zero_page;
-            __builtin_amdgcn_global_load_lds(ga, (lds_void*)(st + (wave * 2 + q) * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(gb, (lds_void*)(st + OPB + (wave * 2 + q) * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(ga, (lds_void*)(st + (wave * 4 + q) * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gb, (lds_void*)(st + OPB + (wave * 4 + q) * 1024), 16, 0, 0);
         }
     };
 
@@ -189,43 +188,44 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
     const int fr = lane & 31, fh = lane >> 5;
-    for (int p = 0; p < PREF && p < nk; ++p) issue(p);
+    if (nk > 0) issue(0);
     for (int kt = 0; kt < nk; ++kt) {
-        // stage kt has landed once at most 4 loads per later stage are pending
-        const int later = min(PREF - 1, nk - 1 - kt);
-        if (later >= 2) __builtin_amdgcn_s_waitcnt(GRPO_VMCNT(8));
-        else if (later == 1) __builtin_amdgcn_s_waitcnt(GRPO_VMCNT(4));
-        else __builtin_amdgcn_s_waitcnt(GRPO_VMCNT(0));
+        // this wave's loads of stage kt have landed
+        __builtin_amdgcn_s_waitcnt(GRPO_VMCNT(0));
         // every wave's share of stage kt is in LDS, and every wave is done
         // reading stage kt-1, which the next issue overwrites
         __syncthreads();
-        if (kt + PREF < nk) issue(kt + PREF);
+        if (kt + 1 < nk) issue(kt + 1);
         const char* sa = smem + (kt % NST) * STB;
         const char* sb = sa + OPB;
-        bf16x8 a[2][FM], b[2][FN];
+        // the stage's 64 k in two halves of two 16-k MFMA steps each
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int c = h * 2 + fh;   // k chunk: lane half fh holds k = c*8 .. +8
+        for (int half = 0; half < 2; ++half) {
+            bf16x8 a[2][FM], b[2][FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int r = wm * WM + i * 32 + fr;
-                a[h][i] = *reinterpret_cast<const bf16x8*>(sa + r * ROWB + ((c ^ swz(r)) << 4));
+            for (int h = 0; h < 2; ++h) {
+                const int c = (half * 2 + h) * 2 + fh;   // k chunk: lane half fh holds k = c*8 .. +8
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int r = wm * WM + i * 32 + fr;
+                    a[h][i] = *reinterpret_cast<const bf16x8*>(sa + r * ROWB + ((c ^ swz(r)) << 4));
+                }
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int r = wn * WN + j * 32 + fr;
+                    b[h][j] = *reinterpret_cast<const bf16x8*>(sb + r * ROWB + ((c ^ swz(r)) << 4));
+                }
             }
+            // all fragment reads of the half before its first MFMA
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int r = wn * WN + j * 32 + fr;
-                b[h][j] = *reinterpret_cast<const bf16x8*>(sb + r * ROWB + ((c ^ swz(r)) << 4));
-            }
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
         }
-        // all fragment reads before the first MFMA
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
     }
 
     // result element (i, j, r): row wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,

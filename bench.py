@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--replicate", type=int, default=1,
                     help="tiny workload: the same row shape and distributions replicated R times as one batch in "
                          "one launch (the HBM reading of the launch-bound workload)")
+    ap.add_argument("--graph", action="store_true",
+                    help="padded workloads: capture the step's device work in a HIP graph once and replay it "
+                         "(the launch-bound tiny step); the roofline then uses graph replay time / launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     return ap.parse_args()
@@ -103,17 +106,17 @@ class Timed:
         e.record()
         return e
 
-    def end(self, e0, units):
+    def end(self, e0, units, launches=1):
         if e0 is None:
             return
         e1 = self.torch.cuda.Event(enable_timing=True)
         e1.record()
-        self.rec.append((e0, e1, units))
+        self.rec.append((e0, e1, units, launches))
 
     def totals(self):
-        ms = sum(a.elapsed_time(b) for a, b, _ in self.rec)
-        units = sum(u for _, _, u in self.rec)
-        return ms, units, len(self.rec)
+        ms = sum(a.elapsed_time(b) for a, b, _, _ in self.rec)
+        units = sum(u for _, _, u, _ in self.rec)
+        return ms, units, sum(n for _, _, _, n in self.rec)
 
 
 # ---------------------------------------------------------------- padded / dynamic: fused loss
@@ -137,10 +140,12 @@ class PaddedStep:
 
     ENT_COEF, KL_COEF = 0.01, 0.05
 
-    def __init__(self, wl, seed, torch, ops, timed, terms=False, ahead=False, epochs=1, shuffle=False, over=None):
+    def __init__(self, wl, seed, torch, ops, timed, terms=False, ahead=False, epochs=1, shuffle=False, over=None,
+                 graph=False):
         from synth import fill_normal_rows, padded_batch
         self.torch, self.ops, self.timed = torch, ops, timed
         self.terms = terms
+        self.graph, self.graph_obj = graph, None
         self.ahead_timed = Timed(torch)
         b = self.b = padded_batch(wl, seed=seed, **(over or {}))
         n_rows, T, V = b["n_rows"], b["T"], b["V"]
@@ -191,6 +196,8 @@ class PaddedStep:
                     self.chunk_units[(e, i, j)] = chunk_bytes(m, V, b_in, b_in, 8 if terms else 0)
         self.n_valid = int(np.sum(b["mask"])) * epochs
         self.logits_dtype = "bf16" if b_in == 2 else "fp32"
+        self.graph_units = sum(self.chunk_units.values())
+        self.graph_launches = len(self.chunk_units)
         # the ahead pass runs only where the gate asks for it (more than one
         # optimizer step per collected batch: n_mini windows per epoch, mu epochs)
         self.ahead = ahead and ops.needs_ahead_pass(n_mini * epochs)
@@ -204,11 +211,32 @@ class PaddedStep:
                     self.ahead_units[(i, j)] = int(np.sum(b["mask"][a * T:e_ * T])) * V * b_in
 
     def __call__(self):
+        self._host_prep()
+        if not self.graph:
+            self._device()
+        elif self.graph_obj is None:
+            # first call: run eagerly (warm-up), then capture the device work once
+            self._device()
+            self.torch.cuda.synchronize()
+            self.graph_obj = self.torch.cuda.CUDAGraph()
+            with self.torch.cuda.graph(self.graph_obj):
+                self._device()
+            self.torch.cuda.synchronize()
+        else:
+            ev = self.timed.begin()
+            self.graph_obj.replay()
+            self.timed.end(ev, self.graph_units, self.graph_launches)
+        return self._finish()
+
+    def _host_prep(self):
+        b = self.b
+        self.adv_host.numpy()[:] = self.ops.group_advantage(b["reward"], b["group"])    # one rollout per row
+        self.adv_dev.copy_(self.adv_host, non_blocking=True)
+
+    def _device(self):
         torch, ops, b, T = self.torch, self.ops, self.b, self.b["T"]
         n_rows = b["n_rows"]
         n_mini, n_micro, mini_rows, micro_rows = ops.plan_fixed(n_rows, b["group"], b["mini"], b["micro"])
-        self.adv_host.numpy()[:] = ops.group_advantage(b["reward"], b["group"])    # one rollout per row
-        self.adv_dev.copy_(self.adv_host, non_blocking=True)
         if self.ahead:
             # [P1] the ahead walk: pi_old of every chunk, recorded before training (batch order)
             self.cache.reset()
@@ -264,6 +292,10 @@ class PaddedStep:
                                          ws=self.ws, **kw)
                     self.timed.end(ev, self.chunk_units[(ep, i, j)])
                     k += 1
+
+    def _finish(self):
+        torch, ops, b = self.torch, self.ops, self.b
+        n_mini, n_micro, _, _ = ops.plan_fixed(b["n_rows"], b["group"], b["mini"], b["micro"])
         self.stats_host.copy_(self.stats_dev, non_blocking=True)
         torch.cuda.current_stream().synchronize()
         stats = ops.stats_to_dicts(self.stats_host.numpy())
@@ -586,8 +618,8 @@ def main():
     timed = Timed(torch)
     cls = {"qwen": PaddedStep, "long": PaddedStep, "tiny": PaddedStep, "dynamic": DynamicStep,
            "compact": CompactStep}[wl]
-    if (args.terms or args.ahead or args.epochs != 1 or args.shuffle) and cls is not PaddedStep:
-        print("--terms, --ahead, --epochs and --shuffle apply to the padded workloads (qwen, long, tiny)",
+    if (args.terms or args.ahead or args.epochs != 1 or args.shuffle or args.graph) and cls is not PaddedStep:
+        print("--terms, --ahead, --epochs, --shuffle and --graph apply to the padded workloads (qwen, long, tiny)",
               file=sys.stderr)
         sys.exit(2)
     extra = {}
@@ -598,6 +630,12 @@ def main():
     if args.epochs != 1 or args.shuffle:
         extra["epochs"] = args.epochs
         extra["shuffle"] = args.shuffle
+    if args.graph:
+        if args.ahead:
+            print("--graph does not combine with --ahead (the cache's host bookkeeping runs per call)",
+                  file=sys.stderr)
+            sys.exit(2)
+        extra["graph"] = True
     if args.replicate != 1:
         if wl != "tiny":
             print("--replicate applies to the tiny workload", file=sys.stderr)
@@ -630,7 +668,8 @@ def main():
                        + ("; ahead pass (pi_old cache) in the step" if args.ahead else "")
                        + (f"; {args.epochs} inner epochs" if args.epochs != 1 else "")
                        + ("; rows reshuffled every epoch (seeded)" if args.shuffle else "")
-                       + (f"; replicated x{args.replicate} as one batch, one launch" if args.replicate != 1 else ""),
+                       + (f"; replicated x{args.replicate} as one batch, one launch" if args.replicate != 1 else "")
+                       + ("; device work replayed from a HIP graph" if args.graph else ""),
            "logits_dtype": step.logits_dtype,
            "valid_tokens": step.n_valid, "launches_per_step": launches // args.steps,
            "step_loss": res[0]["loss"] if res and res[0] else None}
@@ -652,7 +691,8 @@ def main():
         achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "tok_reg_kernel (fused loss fwd+bwd) + row/chunk stats, per chunk launch",
+                "kernel": "tok_reg_kernel (fused loss fwd+bwd) + row/chunk stats, per chunk launch"
+                          + ("; graph replay time divided by the chunk launches" if args.graph else ""),
                 "algorithmic_bytes_per_launch": int(units // launches), "avg_launch_ms": round(tot_ms / launches, 4)}
         roof["device_copy_GBs"] = round(step.copy_context(), 1)
         if wl == "qwen" and not (args.terms or args.ahead or args.epochs != 1 or args.shuffle):

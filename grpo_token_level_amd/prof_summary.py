@@ -104,6 +104,46 @@ def load_traffic(path, kernel_source=KERNEL_SOURCE):
     return None
 
 
+def mfma(args):
+    """MFMA busy share and bf16 MFMA work per kernel from one --pmc run of
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16 and GRBM_GUI_ACTIVE.
+    The CSV holds each counter summed over the XCD instances, so the GPU-busy
+    cycles of a dispatch are GRBM_GUI_ACTIVE / n_xcd; busy share =
+    sum(MFMA busy cycles) / (GPU-busy cycles * SIMDs); bf16 MFMA flops =
+    MOPS * 512."""
+    per = {}
+    for r in _rows(args.csv):
+        name = r["Kernel_Name"]
+        if args.needle not in name:
+            continue
+        key = name.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
+        d = per.setdefault(key, {})
+        disp = d.setdefault(r["Dispatch_Id"], {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        disp[r["Counter_Name"]] = float(r["Counter_Value"])
+    lines = [f"# rocprofv3 MFMA counters: {args.title}", "", "command:", f"  {args.cmd}", "",
+             f"busy share = sum(SQ_VALU_MFMA_BUSY_CYCLES) / ((GRBM_GUI_ACTIVE / {args.n_xcd}) * {args.simds} SIMDs); "
+             "bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512", "",
+             f"{'kernel':40s} {'dispatches':>10s} {'avg_us':>9s} {'MFMA busy %':>12s} {'MFMA TFLOP':>11s} "
+             f"{'TFLOP/s':>9s}"]
+    tot_busy = tot_active = tot_flop = tot_ns = 0.0
+    for key, d in sorted(per.items()):
+        busy = sum(x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for x in d.values())
+        active = sum(x.get("GRBM_GUI_ACTIVE", 0.0) for x in d.values()) / args.n_xcd
+        flop = sum(x.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for x in d.values()) * 512
+        ns = sum(x["ns"] for x in d.values())
+        tot_busy += busy
+        tot_active += active
+        tot_flop += flop
+        tot_ns += ns
+        lines.append(f"{key[:40]:40s} {len(d):10d} {ns / len(d) / 1e3:9.1f} {100 * busy / (active * args.simds):12.1f} "
+                     f"{flop / 1e12:11.2f} {flop / (ns * 1e-9) / 1e12:9.1f}")
+    if per:
+        lines.append(f"{'all of the above':40s} {'':10s} {'':9s} {100 * tot_busy / (tot_active * args.simds):12.1f} "
+                     f"{tot_flop / 1e12:11.2f} {tot_flop / (tot_ns * 1e-9) / 1e12:9.1f}")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -121,8 +161,16 @@ def main():
     p.add_argument("--cmd", required=True)
     p.add_argument("--kernel", default="tok_reg_kernel<1, 1, 1024, 19, true>")
     p.add_argument("--workload", default="qwen")
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
+    m.add_argument("out")
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--title", default="")
+    m.add_argument("--needle", default="gemm_nt_kernel", help="keep kernels whose name contains this")
+    m.add_argument("--n-xcd", type=int, default=8)
+    m.add_argument("--simds", type=int, default=1024, help="SIMDs on the chip (256 CUs x 4)")
     a = ap.parse_args()
-    stats(a) if a.mode == "stats" else pmc(a)
+    {"stats": stats, "pmc": pmc, "mfma": mfma}[a.mode](a)
 
 
 if __name__ == "__main__":

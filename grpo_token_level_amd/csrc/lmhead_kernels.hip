@@ -8,7 +8,11 @@
 // context-compaction step fits a variable number of rows into one batch"
 // (rows are micro-batched, padding rows are masked and add nothing).
 //
-// One call handles one micro-batch chunk of n tokens:
+// One call handles one micro-batch chunk of n tokens.  Masked tokens (pads,
+// observations) contribute nothing, so a one-block kernel first lists the
+// chunk's valid tokens on the device (index map + count); every GEMM below
+// runs over those rows only.  Grids are sized for all n tokens and tiles past
+// the device count exit at once, so the host never waits for the count.
 //   pass 1  GEMM z = h W^T over the whole vocabulary; the epilogue reduces
 //           each 64-column slice of a token row to (max, sum e, sum e*t) and
 //           picks out the target logit.  A merge kernel combines the slices
@@ -73,6 +77,7 @@ constexpr int kVocabChunkMax = 65536;   // pass-2 vocabulary chunk bound (sizes 
 constexpr int kVocabChunkMin = 16384;
 constexpr int kDhSplitMax = 16;         // dh split-K partials (sizes the dh workspace)
 constexpr int kTokPad = 64;             // token count padding of h^T and dz^T rows (128-byte rows)
+constexpr int64_t kMaxTokens = 65535LL * 64;   // tokens per call (the h^T transpose grid's y extent)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -83,11 +88,18 @@ __device__ __attribute__((aligned(64))) uint16_t g_zero_page[32];
 enum { EPI_STATS = 0, EPI_DZ = 1, EPI_ACC = 2 };
 
 struct GemmArgs {
-    const uint16_t* A;   // row m at A + m*lda, K contiguous
+    const uint16_t* A;   // row m at A + m*lda (A + a_rows[m]*lda with a row map), K contiguous
     int64_t lda;
     const uint16_t* B;   // row n at B + n*ldb, K contiguous
     int64_t ldb;
     int M, N, K;         // K % 8 == 0; rows >= M / >= N are read as zeros
+    // Valid-token compaction (NULL = off).  The grid is sized for the host
+    // bounds M / K; the device count *m_dev (rows, <= M) or the device count
+    // *k_dev rounded up to kTokPad (K, <= K) takes their place in the kernel,
+    // and tiles past it exit at once.
+    const int32_t* a_rows;   // A row (and target index) of row m
+    const int32_t* m_dev;
+    const int32_t* k_dev;
     int tiles_m, tiles_n;
     int ksplit, kper;    // K range of split s: [s*kper, min(K, (s+1)*kper)), kper % BK == 0
     int n_fast;          // tile order: N index fastest (else M fastest)
@@ -96,14 +108,15 @@ struct GemmArgs {
     int n_parts;
     const int32_t* target;
     float* zy;           // zy[m] = z[m, target[m]]
-    // EPI_DZ
+    // EPI_DZ (per-token arrays indexed by row m; target by the A row)
     const float* c2;     // log2-domain logsumexp per token
     const float* coef;   // gradient coefficient per token
     const float* ea;     // with the entropy bonus (bonus != 0): dz = p * (ea + eb * t) - coef * onehot,
     const float* eb;     //   t = z*log2e - c2, per token
     int bonus;
     int col0;            // vocabulary index of column 0 of this chunk
-    int m_out;           // rows [M, m_out) are written as zeros (K padding of dz^T)
+    int m_out;           // rows [M, m_out) are written as zeros (K padding of dz^T);
+                         // with m_dev, m_out = *m_dev rounded up to kTokPad
     uint16_t* dz;        // dz[m * ld_dz + n]
     int64_t ld_dz;
     uint16_t* dzT;       // dzT[n * ld_dzT + m]
@@ -156,15 +169,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
     const int tm = g.n_fast ? tile / g.tiles_n : tile % g.tiles_m;
     const int tn = g.n_fast ? tile % g.tiles_n : tile / g.tiles_m;
     const int m0 = tm * BM, n0 = tn * BN;
+    const int M = g.m_dev ? min(g.M, *g.m_dev) : g.M;
+    const int m_out = g.m_dev ? min(g.m_out, (M + kTokPad - 1) / kTokPad * kTokPad) : g.m_out;
+    const int K = g.k_dev ? min(g.K, (*g.k_dev + kTokPad - 1) / kTokPad * kTokPad) : g.K;
+    // tiles past the valid rows; an accumulation with an empty K range leaves C as it is
+    if (m0 >= (EPI == EPI_DZ ? m_out : M)) return;
     const int kbeg = split * g.kper;
-    const int kend = min(g.K, kbeg + g.kper);
+    const int kend = min(K, kbeg + g.kper);
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+    if (EPI == EPI_ACC && nk == 0 && g.beta) return;
 
     // Direct-to-LDS loads: one global_load_lds moves 64 lanes x 16 bytes to
     // LDS base + 16*lane, i.e. 8 tile rows of 128 bytes.  Wave w fills rows
     // (4w+q)*8 .. +8 of each operand (q < 4); lane l takes row (l/8) of those
     // and stores k chunk (l%8) ^ swz(row) at LDS position l%8.
     const int lr = lane >> 3, lp = lane & 7;
+    int64_t aoff[4];   // element offset of this lane's A rows, -1 past the valid rows
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int ma = m0 + (wave * 4 + q) * 8 + lr;
+        aoff[q] = ma < M ? (int64_t)(g.a_rows ? g.a_rows[ma] : ma) * g.lda : -1;
+    }
     auto issue = [&](int kt) {
         char* st = smem + (kt % NST) * STB;
         const int k0 = kbeg + kt * BK;
@@ -173,8 +198,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
             const int r = (wave * 4 + q) * 8 + lr;
             const int k = k0 + ((lp ^ swz(r)) << 3);
             const bool kin = k < kend;
-            const int ma = m0 + r, nb = n0 + r;
-            const uint16_t* ga = (ma < g.M && kin) ? g.A + (int64_t)ma * g.lda + k : g_zero_page;
+            const int nb = n0 + r;
+            const uint16_t* ga = (aoff[q] >= 0 && kin) ? g.A + aoff[q] + k : g_zero_page;
             const uint16_t* gb = (nb < g.N && kin) ? g.B + (int64_t)nb * g.ldb + k : g_zero_page;
             __builtin_amdgcn_global_load_lds(ga, (lds_void*)(st + (wave * 4 + q) * 1024), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(gb, (lds_void*)(st + OPB + (wave * 4 + q) * 1024), 16, 0, 0);
@@ -258,7 +283,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
                     float4 o[16];
 #pragma unroll
                     for (int k = 0; k < 16; ++k)
-                        if (mb + 2 * k < g.M) o[k] = *reinterpret_cast<const float4*>(Cs + (int64_t)(mb + 2 * k) * g.ldc + n);
+                        if (mb + 2 * k < M) o[k] = *reinterpret_cast<const float4*>(Cs + (int64_t)(mb + 2 * k) * g.ldc + n);
 #pragma unroll
                     for (int k = 0; k < 16; ++k) {
                         v[k].x += o[k].x;
@@ -269,7 +294,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
                 }
 #pragma unroll
                 for (int k = 0; k < 16; ++k)
-                    if (mb + 2 * k < g.M) *reinterpret_cast<float4*>(Cs + (int64_t)(mb + 2 * k) * g.ldc + n) = v[k];
+                    if (mb + 2 * k < M) *reinterpret_cast<float4*>(Cs + (int64_t)(mb + 2 * k) * g.ldc + n) = v[k];
             }
             __syncthreads();
         }
@@ -282,12 +307,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
         __syncthreads();   // the stage buffers are reused
         if (tid < BM) {
             const int m = m0 + tid;
-            const bool in = m < g.M;
+            const bool in = m < M;
             s_c2[tid] = in ? g.c2[m] : 0.0f;
             s_cf[tid] = in ? g.coef[m] : 0.0f;
             s_ea[tid] = (in && g.bonus) ? g.ea[m] : 0.0f;
             s_eb[tid] = (in && g.bonus) ? g.eb[m] : 0.0f;
-            s_y[tid] = in ? g.target[m] : -1;
+            s_y[tid] = in ? g.target[g.a_rows ? g.a_rows[m] : m] : -1;
         }
         __syncthreads();
 #pragma unroll
@@ -316,8 +341,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
                     const int m = m0 + mb;
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        if (m + u < g.M) g.dz[(int64_t)(m + u) * g.ld_dz + nl] = to_bf16(d[u]);
-                    if (m + 3 < g.m_out) {
+                        if (m + u < M) g.dz[(int64_t)(m + u) * g.ld_dz + nl] = to_bf16(d[u]);
+                    if (m + 3 < m_out) {
                         uint2 pk;
                         pk.x = pack2(d[0], d[1]);
                         pk.y = pack2(d[2], d[3]);
@@ -325,7 +350,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
                     } else {
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
-                            if (m + u < g.m_out) g.dzT[(int64_t)nl * g.ld_dzT + m + u] = to_bf16(d[u]);
+                            if (m + u < m_out) g.dzT[(int64_t)nl * g.ld_dzT + m + u] = to_bf16(d[u]);
                     }
                 }
             }
@@ -346,7 +371,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
             const int m = m0 + wm * WM + i * 32 + rr;
             const int nb = n0 + wn * WN + half * 64;
             const int ncols = g.N - nb < 64 ? g.N - nb : 64;
-            if (m < g.M && ncols > 0) {
+            if (m < M && ncols > 0) {
                 const float* row = T + rr * EPI_ROW + half * 64;
                 float mx = -INFINITY;
                 for (int c = 0; c < ncols; ++c) mx = fmaxf(mx, row[c]);
@@ -359,7 +384,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
                     sw = fmaf(e, t, sw);
                 }
                 g.part[(int64_t)m * g.n_parts + nb / 64] = make_float4(mx, se, sw, 0.0f);
-                const int y = g.target[m];
+                const int y = g.target[g.a_rows ? g.a_rows[m] : m];
                 if (y >= nb && y < nb + ncols) g.zy[m] = row[y - nb];
             }
             __syncthreads();
@@ -367,22 +392,79 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
     }
 }
 
-// dst[i] = sum over s of parts[s * count + i], s in order
-__global__ __launch_bounds__(256) void sum_splits_kernel(float* __restrict__ dst, const float* __restrict__ parts,
-                                                         int nsplit, int64_t count) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= count) return;
-    float s = parts[i];
-    for (int k = 1; k < nsplit; ++k) s += parts[(int64_t)k * count + i];
-    dst[i] = s;
+// dh row t (H floats) = sum over s, in order, of the partials of t's compact
+// row inv[t]; a masked token (inv[t] < 0) gets a zero row.  Block (x, y):
+// columns [256x, 256x + 256) of tokens y, y + gridDim.y, ...
+__global__ __launch_bounds__(256) void sum_splits_kernel(float* __restrict__ dst, int64_t ld_dst,
+                                                         const float* __restrict__ parts, int nsplit, int64_t c_split,
+                                                         const int32_t* __restrict__ inv, int64_t n, int64_t H) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= H) return;
+    for (int64_t t = blockIdx.y; t < n; t += gridDim.y) {
+        const int32_t j = inv[t];
+        float s = 0.0f;
+        if (j >= 0) {
+            const float* p = parts + (int64_t)j * H + c;
+            s = p[0];
+            for (int k = 1; k < nsplit; ++k) s += p[(int64_t)k * c_split];
+        }
+        dst[t * ld_dst + c] = s;
+    }
+}
+
+// Valid-token compaction of one chunk: vidx[j] = position of the j-th token
+// with mask != 0 (in order), inv[t] = its compact index or -1, count[0] = the
+// number of valid tokens.  One block, four tokens per thread per pass.
+__global__ __launch_bounds__(1024) void compact_tokens_kernel(const uint8_t* __restrict__ mask, int64_t n,
+                                                              int32_t* __restrict__ vidx, int32_t* __restrict__ inv,
+                                                              int32_t* __restrict__ count) {
+    __shared__ int s_wave[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    int base = 0;
+    for (int64_t t0 = 0; t0 < n; t0 += 4096) {
+        const int64_t t = t0 + (int64_t)tid * 4;
+        int v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = (t + u < n && mask[t + u] != 0) ? 1 : 0;
+        // valid tokens of the lower lanes of this wave, then of this lane's lower slots
+        int pre = 0, mine = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint64_t b = __ballot(v[u]);
+            pre += __popcll(b & below);
+            mine += __popcll(b);
+        }
+        if (lane == 0) s_wave[wave] = mine;
+        __syncthreads();
+        int off = base, tot = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            off += w < wave ? s_wave[w] : 0;
+            tot += s_wave[w];
+        }
+        int j = off + pre;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (t + u < n) {
+                inv[t + u] = v[u] ? j : -1;
+                if (v[u]) vidx[j] = (int32_t)(t + u);
+            }
+            j += v[u];
+        }
+        base += tot;
+        __syncthreads();   // s_wave is rewritten by the next pass
+    }
+    if (tid == 0) count[0] = base;
 }
 
 // One wave per token: merge the token's slice partials in a fixed order,
 // then logsumexp, entropy, log-prob, surrogate and gradient coefficient.
 struct MergeArgs {
-    const float4* part;
+    const float4* part;   // part, zy, c2, coef, ea, eb: at the token's compact index inv[t]
     int n_parts;
     const float* zy;
+    const int32_t* inv;
     int64_t n_tok;
     int64_t V;
     const int32_t* target;
@@ -428,12 +510,9 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const MergeArgs a) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (t >= a.n_tok) return;
-    if (a.mask[t] == 0) {
+    const int32_t j = a.inv[t];   // -1 exactly when mask[t] == 0
+    if (j < 0) {
         if (lane == 0) {
-            a.c2[t] = 0.0f;
-            a.coef[t] = 0.0f;
-            a.ea[t] = 0.0f;
-            a.eb[t] = 0.0f;
             if (a.kl_tok) a.kl_tok[t] = 0.0f;
             a.logp[t] = 0.0f;
             if (a.lse) a.lse[t] = 0.0f;
@@ -445,7 +524,7 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const MergeArgs a) {
     }
     float M = 0.0f, S = 0.0f, W = 0.0f;
     for (int p = lane; p < a.n_parts; p += 64) {
-        const float4 q = a.part[t * a.n_parts + p];
+        const float4 q = a.part[(int64_t)j * a.n_parts + p];
         merge_part(M, S, W, q.x, q.y, q.z);
     }
 #pragma unroll
@@ -469,7 +548,7 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const MergeArgs a) {
     const float lse = c2 * kLn2;
     const int32_t y = a.target[t];
     const bool ybad = (uint32_t)y >= (uint64_t)a.V;
-    const float logp = ybad ? __builtin_nanf("") : a.zy[t] - lse;
+    const float logp = ybad ? __builtin_nanf("") : a.zy[j] - lse;
     const float H = kLn2 * (log2s - W / S);
     const int32_t row = a.tok_row[t];
     const float A = ((uint32_t)row < (uint64_t)a.n_rows) ? a.adv_row[row] : __builtin_nanf("");
@@ -478,10 +557,10 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const MergeArgs a) {
     const grpo_dev::Surrogate sg = grpo_dev::surrogate(logp, H, a.old_logp[t], A, a.eps_low, a.eps_high, sf,
                                                        a.terms, t);
     const float e = a.terms.ent_coef * sf;
-    a.c2[t] = c2;
-    a.coef[t] = sg.coef;
-    a.ea[t] = fmaf(e, H, sg.coef);
-    a.eb[t] = e * kLn2;
+    a.c2[j] = c2;
+    a.coef[j] = sg.coef;
+    a.ea[j] = fmaf(e, H, sg.coef);
+    a.eb[j] = e * kLn2;
     if (a.kl_tok) a.kl_tok[t] = sg.kl;
     a.logp[t] = logp;
     if (a.lse) a.lse[t] = lse;
@@ -490,17 +569,22 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const MergeArgs a) {
     a.tok_flags[t] = (uint8_t)(1u | (sg.clipped ? 2u : 0u) | (sg.bad ? 4u : 0u));
 }
 
-// dst[c * ld_dst + r] = src[r * ld_src + c] for r < rows, c < cols; columns
-// [rows, rows_pad) of dst are written as zeros.  64x64 tiles through LDS.
+// dst[c * ld_dst + r] = src[row(r) * ld_src + c] for r < rows, c < cols, with
+// row(r) = rmap ? rmap[r] : r and rows = min(rows, *rcount) when rcount is
+// set; columns [rows, rows_pad) of dst are written as zeros.  64x64 tiles
+// through LDS.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t rows,
                                                              int64_t cols, int64_t ld_src, uint16_t* __restrict__ dst,
-                                                             int64_t ld_dst, int64_t rows_pad) {
+                                                             int64_t ld_dst, int64_t rows_pad,
+                                                             const int32_t* __restrict__ rmap,
+                                                             const int32_t* __restrict__ rcount) {
     __shared__ uint16_t tile[64][66];
     const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    if (rcount && *rcount < rows) rows = *rcount;
     for (int k = ty; k < 64; k += 4) {
         const int64_t r = r0 + k, c = c0 + tx;
-        tile[k][tx] = (r < rows && c < cols) ? src[r * ld_src + c] : (uint16_t)0;
+        tile[k][tx] = (r < rows && c < cols) ? src[(rmap ? (int64_t)rmap[r] : r) * ld_src + c] : (uint16_t)0;
     }
     __syncthreads();
     for (int k = ty; k < 64; k += 4) {
@@ -522,6 +606,9 @@ struct Workspace {
     uint16_t* dz;
     uint16_t* dzT;
     float* dh_part;
+    int32_t* vidx;    // valid-token compaction of the chunk
+    int32_t* inv;
+    int32_t* count;   // number of valid tokens
     size_t bytes;
 };
 
@@ -586,6 +673,9 @@ Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V) {
     w.dz = reinterpret_cast<uint16_t*>(take((size_t)n_tok * vc * 2));
     w.dzT = reinterpret_cast<uint16_t*>(take((size_t)vc * n_pad * 2));
     w.dh_part = reinterpret_cast<float*>(take((size_t)kDhSplitMax * n_tok * H * 4));
+    w.vidx = reinterpret_cast<int32_t*>(take((size_t)n_tok * 4));
+    w.inv = reinterpret_cast<int32_t*>(take((size_t)n_tok * 4));
+    w.count = reinterpret_cast<int32_t*>(take(4));
     w.bytes = off;
     return w;
 }
@@ -630,7 +720,7 @@ extern "C" int grpo_transpose_bf16(void* stream, const void* src, int64_t rows, 
         return fail(GRPO_EINVAL, "grpo_transpose_bf16: too many rows for one launch");
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64)),
                        dim3(256), 0, (hipStream_t)stream, (const uint16_t*)src, rows, cols, ld_src, (uint16_t*)dst,
-                       ld_dst, rows);
+                       ld_dst, rows, nullptr, nullptr);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? ok() : fail(GRPO_EDEVICE, "grpo_transpose_bf16: %s", hipGetErrorString(e));
 }
@@ -645,8 +735,9 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
         return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: need n_tok >= 0, H > 0, V > 0, rows for the tokens");
     if (H % 8 || V % 8 || a->ldh < H || a->ldh % 8)
         return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: H, V and ldh must be multiples of 8 (ldh >= H)");
-    if (n > (1 << 30) || V > (1 << 30) || H > (1 << 20))
-        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: sizes beyond the kernels' 32-bit tile indexing");
+    if (n > kMaxTokens || V > (1 << 30) || H > (1 << 20))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: n_tok above %lld or sizes beyond the kernels' 32-bit tile "
+                    "indexing", (long long)kMaxTokens);
     if (!a->W || !a->Wt || !a->dW || !al16(a->W) || !al16(a->Wt) || !al16(a->dW))
         return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: W, Wt and dW are required (16-byte aligned)");
     if (!a->chunk_stats || (a->n_rows > 0 && (!a->row_stats || !a->row_off)))
@@ -678,20 +769,28 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
     const uint16_t* Wt = (const uint16_t*)a->Wt;
     hipError_t e;
 
-    // h^T with zero columns up to n_pad (the K operand of dW's GEMM)
+    // Masked tokens add nothing to any product (their dz rows are zero), so
+    // the GEMMs run over the chunk's valid tokens only: vidx lists them in
+    // order, inv maps a token to its compact index, count holds how many.
+    // Grids stay sized for all n tokens; the kernels read the count.
+    hipLaunchKernelGGL(compact_tokens_kernel, dim3(1), dim3(1024), 0, st, a->mask, n, w.vidx, w.inv, w.count);
+    if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "compaction");
+
+    // h^T of the valid tokens, zero columns up to n_pad (the K operand of dW's GEMM)
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((H + 63) / 64), (unsigned)((n_pad + 63) / 64)),
-                       dim3(256), 0, st, h, n, H, a->ldh, w.hT, n_pad, n_pad);
+                       dim3(256), 0, st, h, n, H, a->ldh, w.hT, n_pad, n_pad, w.vidx, w.count);
     if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "transpose h");
 
     // pass 1: slice partials of the log-softmax and the target logit
     GemmArgs g{};
     g.A = h; g.lda = a->ldh; g.B = W; g.ldb = H;
     g.M = (int)n; g.N = (int)V; g.K = (int)H;
+    g.a_rows = w.vidx; g.m_dev = w.count;
     g.part = w.part; g.n_parts = n_parts; g.target = a->target; g.zy = w.zy;
     if ((e = launch_gemm<EPI_STATS>(g, st)) != hipSuccess) return dev_fail(e, "pass 1");
 
     MergeArgs mg{};
-    mg.part = w.part; mg.n_parts = n_parts; mg.zy = w.zy; mg.n_tok = n; mg.V = V;
+    mg.part = w.part; mg.n_parts = n_parts; mg.zy = w.zy; mg.inv = w.inv; mg.n_tok = n; mg.V = V;
     mg.target = a->target; mg.mask = a->mask; mg.old_logp = a->old_logp; mg.tok_row = a->tok_row;
     mg.adv_row = a->adv_row; mg.n_rows = a->n_rows; mg.eps_low = a->eps_low; mg.eps_high = a->eps_high;
     mg.scale = a->scale; mg.denom = a->denom; mg.c2 = w.c2; mg.coef = w.coef; mg.ea = w.ea; mg.eb = w.eb;
@@ -718,6 +817,7 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
         GemmArgs d{};
         d.A = h; d.lda = a->ldh; d.B = W + c0 * H; d.ldb = H;
         d.M = (int)n; d.N = vc; d.K = (int)H;
+        d.a_rows = w.vidx; d.m_dev = w.count;
         d.c2 = w.c2; d.coef = w.coef; d.target = a->target; d.col0 = (int)c0; d.m_out = (int)n_pad;
         d.ea = w.ea; d.eb = w.eb; d.bonus = a->ent_coef != 0.0f;
         d.dz = w.dz; d.ld_dz = vc; d.dzT = w.dzT; d.ld_dzT = n_pad;
@@ -728,6 +828,7 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
         GemmArgs gh{};
         gh.A = w.dz; gh.lda = vc; gh.B = Wt + c0; gh.ldb = V;
         gh.M = (int)n; gh.N = (int)H; gh.K = vc;
+        gh.m_dev = w.count;
         gh.ksplit = nsplit;
         gh.kper = (int)round_up((vc + nsplit - 1) / nsplit, BK);
         gh.C = w.dh_part; gh.ldc = H; gh.c_split = n * H; gh.beta = c0 > 0;
@@ -736,11 +837,12 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
         GemmArgs gw{};
         gw.A = w.dzT; gw.lda = n_pad; gw.B = w.hT; gw.ldb = n_pad;
         gw.M = vc; gw.N = (int)H; gw.K = (int)n_pad;
+        gw.k_dev = w.count;
         gw.C = a->dW + c0 * H; gw.ldc = H; gw.beta = 1;
         if ((e = launch_gemm<EPI_ACC>(gw, st)) != hipSuccess) return dev_fail(e, "dW");
     }
-    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n * H + 255) / 256)), dim3(256), 0, st, a->dh, w.dh_part,
-                       nsplit, n * H);
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((H + 255) / 256), (unsigned)(n < 65535 ? n : 65535)),
+                       dim3(256), 0, st, a->dh, H, w.dh_part, nsplit, n * H, w.inv, n, H);
     if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "dh splits");
     return ok();
 }

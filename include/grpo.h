@@ -328,7 +328,7 @@ typedef struct grpo_lmhead_args {
     int64_t ldh;                /* >= H, multiple of 8 */
     const void* W;              /* bf16 [V x H] LM-head weight, rows contiguous (16-byte aligned) */
     const void* Wt;             /* bf16 [H x V]: W transposed (grpo_transpose_bf16), 16-byte aligned */
-    int64_t n_tok, H, V;        /* H and V multiples of 8 */
+    int64_t n_tok, H, V;        /* n_tok <= 4194240 (65535 x 64); H and V multiples of 8 */
     const int32_t* target;      /* [n_tok] */
     const uint8_t* mask;        /* [n_tok] 1 = policy token; pads and observations 0 */
     const float* old_logp;      /* [n_tok] */
@@ -363,8 +363,9 @@ typedef struct grpo_lmhead_args {
 /* host.  Workspace bytes grpo_lmhead_fwd_bwd needs for a chunk of n_tok tokens:
  * per-token slice partials of the log-softmax (16 B per token per 64 vocabulary
  * columns), h^T, one vocabulary chunk (at most 65536 columns) of dz in two
- * layouts (bf16) and up to 16 fp32 split partials of dh.  It grows with
- * n_tok * V / 4, n_tok * 262144 and n_tok * H * 64, never with n_tok * V * 2. */
+ * layouts (bf16), up to 16 fp32 split partials of dh and the chunk's
+ * valid-token index maps.  It grows with n_tok * V / 4, n_tok * 262144 and
+ * n_tok * H * 64, never with n_tok * V * 2. */
 size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V);
 
 /* device.  The fused loss of grpo_loss_fwd_bwd with the logits produced by the
@@ -376,8 +377,11 @@ size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V);
  * z and dz are formed tile by tile in registers by bf16 MFMA GEMMs (fp32
  * accumulation) and never stored for the whole vocabulary; dz feeds the two
  * gradient GEMMs in bf16, one vocabulary chunk at a time.  Masked tokens
- * (pads, [P4] figure) get zero outputs and contribute nothing.  Row and chunk
- * stats as in grpo_loss_fwd_bwd.  ECAPACITY if the workspace is too small. */
+ * (pads, [P4] figure; observations, [P2] "Field Lineage") get zero outputs and
+ * contribute nothing; the GEMMs skip them: the chunk's valid tokens are listed
+ * on the device first and only their rows are multiplied (the host never
+ * waits for the count).  Row and chunk stats as in grpo_loss_fwd_bwd.
+ * ECAPACITY if the workspace is too small. */
 int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* args);
 
 /* ===================================================== frozen pi_old (ahead pass) */

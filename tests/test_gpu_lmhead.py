@@ -142,6 +142,51 @@ def test_lmhead_equals_materialised_path():
     assert rel_l2(to_f64(ws["dh"]), dz @ c["W64"]) <= TOL_GRAD
 
 
+@pytest.mark.parametrize("pattern", ["blocks", "sparse"])
+def test_lmhead_skips_masked_tokens(pattern):
+    # The GEMMs run over the valid tokens only (listed on the device): a chunk
+    # spanning three 256-row tiles whose masked tokens come in long runs or
+    # leave only one token in eight, against the oracle; dh rows of masked
+    # tokens are zero and dW (pre-filled) gains exactly the valid tokens' share.
+    n, H, V = 700, 128, 2000
+    c = _case(n, H, V, seed=31 if pattern == "blocks" else 32, masked_frac=0.0)
+    m = np.zeros(n, np.uint8)
+    if pattern == "blocks":
+        m[40:170] = 1
+        m[300:310] = 1
+        m[650:] = 1
+    else:
+        m[::8] = 1
+    c["mask"] = m
+    c["g"]["mask"] = torch.from_numpy(m).to(DEV)
+    N = int(m.sum())
+    base = torch.randn((V, H), generator=torch.Generator(device="cpu").manual_seed(3)).to(DEV) * 1e-3
+    dW = base.clone()
+    ws = _run(c, dW, 1.0 / N)
+    torch.cuda.synchronize()
+    ref = oracle.lmhead_fwd_bwd(c["h64"], c["W64"], c["target"], m, c["old"].astype(np.float64),
+                                c["adv"].astype(np.float64)[c["tok_row"]], 1.0 / N)
+    _check(ws, dW - base, ref, c, ref["dW"])
+    assert ops.stats_to_dicts(ws["chunk_stats"])[0]["n_valid"] == N
+
+
+def test_lmhead_all_masked_chunk():
+    # no valid token: every GEMM tile exits, dW keeps its bits, outputs are zero
+    n, H, V = 300, 64, 1000
+    c = _case(n, H, V, seed=33)
+    c["mask"] = np.zeros(n, np.uint8)
+    c["g"]["mask"] = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    dW = torch.randn((V, H), generator=torch.Generator(device="cpu").manual_seed(4)).to(DEV)
+    before = dW.clone()
+    ws = _run(c, dW, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(dW, before)
+    for k in ("dh", "logp", "entropy", "loss_tok", "tok_flags"):
+        assert not ws[k].any(), k
+    st = ops.stats_to_dicts(ws["chunk_stats"])[0]
+    assert st["n_valid"] == 0 and st["loss_sum"] == 0.0
+
+
 def test_lmhead_rejects_small_workspace_and_bad_shapes():
     c = _case(8, 64, 256, seed=1)
     Wt = ops.transpose_bf16(c["W"])

@@ -111,17 +111,19 @@ __device__ __forceinline__ void st16_nt(T* p, const T& v) {
 template <int DT> struct Out;
 template <> struct Out<GRPO_BF16> {
     static constexpr int BYTES = 2;
+    // neg: every stored value negated (sign bits flipped after rounding)
     template <int N>
-    __device__ static __forceinline__ void store(void* row, int e0, const float (&d)[N]) {
+    __device__ static __forceinline__ void store(void* row, int e0, const float (&d)[N], bool neg = false) {
         uint16_t* p = reinterpret_cast<uint16_t*>(row) + e0;
+        const uint32_t sg = neg ? 0x80008000u : 0u;
         if constexpr (N == 8) {
             uint4 v;
-            v.x = pack_bf16x2(d[0], d[1]); v.y = pack_bf16x2(d[2], d[3]);
-            v.z = pack_bf16x2(d[4], d[5]); v.w = pack_bf16x2(d[6], d[7]);
+            v.x = pack_bf16x2(d[0], d[1]) ^ sg; v.y = pack_bf16x2(d[2], d[3]) ^ sg;
+            v.z = pack_bf16x2(d[4], d[5]) ^ sg; v.w = pack_bf16x2(d[6], d[7]) ^ sg;
             st16(reinterpret_cast<uint4*>(p), v);
         } else {
             uint2 v;
-            v.x = pack_bf16x2(d[0], d[1]); v.y = pack_bf16x2(d[2], d[3]);
+            v.x = pack_bf16x2(d[0], d[1]) ^ sg; v.y = pack_bf16x2(d[2], d[3]) ^ sg;
             st16(reinterpret_cast<uint2*>(p), v);
         }
     }
@@ -140,10 +142,14 @@ template <> struct Out<GRPO_BF16> {
 template <> struct Out<GRPO_F32> {
     static constexpr int BYTES = 4;
     template <int N>
-    __device__ static __forceinline__ void store(void* row, int e0, const float (&d)[N]) {
-        float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(row) + e0);
-        st16(p, make_float4(d[0], d[1], d[2], d[3]));
-        if constexpr (N == 8) st16(p + 1, make_float4(d[4], d[5], d[6], d[7]));
+    __device__ static __forceinline__ void store(void* row, int e0, const float (&d)[N], bool neg = false) {
+        uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<float*>(row) + e0);
+        const uint32_t sg = neg ? 0x80000000u : 0u;
+        st16(p, make_uint4(__float_as_uint(d[0]) ^ sg, __float_as_uint(d[1]) ^ sg, __float_as_uint(d[2]) ^ sg,
+                           __float_as_uint(d[3]) ^ sg));
+        if constexpr (N == 8)
+            st16(p + 1, make_uint4(__float_as_uint(d[4]) ^ sg, __float_as_uint(d[5]) ^ sg,
+                                   __float_as_uint(d[6]) ^ sg, __float_as_uint(d[7]) ^ sg));
     }
     template <int N>
     __device__ static __forceinline__ void zero(void* row, int e0) {
@@ -178,6 +184,110 @@ __device__ __forceinline__ long long wave_sum_i(long long x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
     return x;
+}
+
+// (c, s, w) of two parts of a row merged exactly, where a part's s = sum 2^t
+// and w = sum 2^t * t with t = z*log2(e) - c: relative to C = max(c, c2),
+// s = s 2^(c-C) + s2 2^(c2-C) and w = sum over both of 2^(c_i-C) (w_i +
+// (c_i-C) s_i).  An empty part (s = 0) leaves the other as it is.
+__device__ __forceinline__ void merge3(float& c, float& s, float& w, float c2, float s2, float w2) {
+    if (s2 == 0.0f) return;
+    if (s == 0.0f) {
+        c = c2;
+        s = s2;
+        w = w2;
+        return;
+    }
+    const float C = fmaxf(c, c2);
+    const float d1 = c - C, d2 = c2 - C;
+    const float f1 = __builtin_amdgcn_exp2f(d1), f2 = __builtin_amdgcn_exp2f(d2);
+    const float S = fmaf(s, f1, s2 * f2);
+    w = fmaf(f1, fmaf(s, d1, w), f2 * fmaf(s2, d2, w2));
+    s = S;
+    c = C;
+}
+
+// Butterfly over the lanes of a wave with stride o >= 1 down to 1, starting
+// at `from`: both lanes of a pair merge (lower lane's part, upper lane's
+// part), so every lane ends with the same bits.
+__device__ __forceinline__ void butterfly3(float& c, float& s, float& w, int lane, int from) {
+#pragma unroll
+    for (int o = from; o > 0; o >>= 1) {
+        float c2 = __shfl_xor(c, o), s2 = __shfl_xor(s, o), w2 = __shfl_xor(w, o);
+        if (lane & o) {
+            const float tc = c, ts = s, tw = w;
+            c = c2; s = s2; w = w2;
+            c2 = tc; s2 = ts; w2 = tw;
+        }
+        merge3(c, s, w, c2, s2, w2);
+    }
+}
+
+// The row's (c, s, w) on every thread of the TPR threads of a row: wave
+// butterfly, then the WPR wave parts through LDS, merged by a butterfly over
+// the first WPR lanes of every wave (the same fixed tree everywhere).
+template <int WPR>
+__device__ __forceinline__ void block_merge(float& c, float& s, float& w, int tid, float (*s_part)[3]) {
+    const int lane = tid & 63;
+    butterfly3(c, s, w, lane, 32);
+    if constexpr (WPR > 1) {
+        if (lane == 0) {
+            s_part[tid >> 6][0] = c;
+            s_part[tid >> 6][1] = s;
+            s_part[tid >> 6][2] = w;
+        }
+        __syncthreads();
+        c = -INFINITY;
+        s = 0.0f;
+        w = 0.0f;
+        if (lane < WPR) {
+            c = s_part[lane][0];
+            s = s_part[lane][1];
+            w = s_part[lane][2];
+        }
+        butterfly3(c, s, w, lane, WPR / 2);
+        c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c)));
+        s = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s)));
+        w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w)));
+    }
+}
+
+// Row maximum and row sums on every thread (wave butterfly, then the wave
+// parts through LDS in wave order); the LDS buffer may still be being read
+// by an earlier helper, hence the leading barrier.
+template <int WPR>
+__device__ __forceinline__ float block_max(float m, int tid, float (*s_part)[3]) {
+    m = wave_max(m);
+    if constexpr (WPR > 1) {
+        __syncthreads();
+        if ((tid & 63) == 0) s_part[tid >> 6][0] = m;
+        __syncthreads();
+        m = s_part[0][0];
+#pragma unroll
+        for (int i = 1; i < WPR; ++i) m = fmaxf(m, s_part[i][0]);
+    }
+    return m;
+}
+
+template <int WPR>
+__device__ __forceinline__ void block_sum2(float& s, float& w, int tid, float (*s_part)[3]) {
+    s = wave_sum(s);
+    w = wave_sum(w);
+    if constexpr (WPR > 1) {
+        __syncthreads();
+        if ((tid & 63) == 0) {
+            s_part[tid >> 6][1] = s;
+            s_part[tid >> 6][2] = w;
+        }
+        __syncthreads();
+        s = s_part[0][1];
+        w = s_part[0][2];
+#pragma unroll
+        for (int i = 1; i < WPR; ++i) {
+            s += s_part[i][1];
+            w += s_part[i][2];
+        }
+    }
 }
 
 // An empty asm that claims to rewrite the register-resident row: the unpacked
@@ -364,81 +474,90 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     float zy_mine = 0.0f;
     if (!ybad && tid == own_tid) zy_mine = In<DTI>::scalar(irow, y);
 
-    // Lanes past the row end load the last vector again (in bounds) and then
-    // hold -inf, which no sweep can see: it loses every max, adds 2^-inf = 0.
+    // Lanes past the row end load the last vector again (in bounds); the
+    // sweeps skip those elements.
     uint4 x[NV];
-    constexpr uint32_t NEG = In<DTI>::NEG_INF2;
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int idx = k * TPR + tid;
-        const bool in = idx < nvec;
-        const uint4 v = vrow[in ? idx : nvec - 1];
-        x[k].x = in ? v.x : NEG;
-        x[k].y = in ? v.y : NEG;
-        x[k].z = in ? v.z : NEG;
-        x[k].w = in ? v.w : NEG;
-    }
+    for (int k = 0; k < NV; ++k) x[k] = vrow[min(k * TPR + tid, nvec - 1)];
 
-    // sweep 1: max
-    float m = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        float f[VEC];
-        In<DTI>::unpack(x[k], f);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) m = fmaxf(m, f[e]);
-    }
-    m = wave_max(m);
-
-    [[maybe_unused]] __shared__ float s_max[WPR];
-    [[maybe_unused]] __shared__ float s_sum[WPR][2];
+    [[maybe_unused]] __shared__ float s_part[WPR][3];
     [[maybe_unused]] __shared__ float s_zy;
     float zy;
     if constexpr (WPR == 1) {
         zy = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zy_mine), own_tid));
     } else {
-        const int wave = tid >> 6;
-        if ((tid & 63) == 0) s_max[wave] = m;
-        if (tid == own_tid) s_zy = zy_mine;
-        __syncthreads();
-        m = s_max[0];
-#pragma unroll
-        for (int i = 1; i < WPR; ++i) m = fmaxf(m, s_max[i]);
-        zy = s_zy;
+        if (tid == own_tid) s_zy = zy_mine;   // read after the first barrier below
     }
 
-    // sweep 2: s = sum 2^t, w = sum 2^t * t
+    // One sweep: each lane sums 2^t and 2^t * t, t = z*log2(e) - c, with its
+    // own shift c = log2(e) * (largest element of its first vector); the
+    // lanes' (c, s, w) are then merged exactly.  Any shift near the lane's
+    // maximum keeps the sums in range; a row where they overflow or turn NaN
+    // (a -inf or NaN logit, a spread of more than ~80 nats within one lane)
+    // takes the exact max-shifted sweeps instead.
+    float c = -INFINITY, s = 0.0f, w = 0.0f;   // an empty lane: s = 0
+    if (tid < nvec) {
+        float f[VEC];
+        In<DTI>::unpack(x[0], f);
+        float m0 = f[0];
+#pragma unroll
+        for (int e = 1; e < VEC; ++e) m0 = fmaxf(m0, f[e]);
+        c = m0 * kLog2e;
+        if (!isfinite(c)) c = 0.0f;
+    }
     opaque_regs(x);
-    const float c = m * kLog2e;
-    float s = 0.0f, w = 0.0f;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-        float f[VEC];
-        In<DTI>::unpack(x[k], f);
+        if (k * TPR + tid < nvec) {
+            float f[VEC];
+            In<DTI>::unpack(x[k], f);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float tt = fmaf(f[e], kLog2e, -c);
-            const float ee = __builtin_amdgcn_exp2f(tt);
-            s += ee;
-            w = fmaf(ee, fmaxf(tt, kNegClampLog2), w);
+            for (int e = 0; e < VEC; ++e) {
+                const float tt = fmaf(f[e], kLog2e, -c);
+                const float ee = __builtin_amdgcn_exp2f(tt);
+                s += ee;
+                w = fmaf(ee, tt, w);
+            }
         }
     }
-    s = wave_sum(s);
-    w = wave_sum(w);
-    if constexpr (WPR > 1) {
-        const int wave = tid >> 6;
-        if ((tid & 63) == 0) {
-            s_sum[wave][0] = s;
-            s_sum[wave][1] = w;
-        }
-        __syncthreads();
-        s = s_sum[0][0];
-        w = s_sum[0][1];
+    block_merge<WPR>(c, s, w, tid, s_part);
+    if constexpr (WPR > 1) zy = s_zy;
+
+    if (!(isfinite(s) && isfinite(w))) {
+        // exact sweeps: shift by the row maximum, clamp t so that 2^t * t of
+        // a -inf logit is 0 (block-uniform branch: s and w are the same on
+        // every lane)
+        opaque_regs(x);
+        float m = -INFINITY;
 #pragma unroll
-        for (int i = 1; i < WPR; ++i) {
-            s += s_sum[i][0];
-            w += s_sum[i][1];
+        for (int k = 0; k < NV; ++k) {
+            if (k * TPR + tid < nvec) {
+                float f[VEC];
+                In<DTI>::unpack(x[k], f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) m = fmaxf(m, f[e]);
+            }
         }
+        m = block_max<WPR>(m, tid, s_part);
+        c = m * kLog2e;
+        s = 0.0f;
+        w = 0.0f;
+        opaque_regs(x);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            if (k * TPR + tid < nvec) {
+                float f[VEC];
+                In<DTI>::unpack(x[k], f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float tt = fmaf(f[e], kLog2e, -c);
+                    const float ee = __builtin_amdgcn_exp2f(tt);
+                    s += ee;
+                    w = fmaf(ee, fmaxf(tt, kNegClampLog2), w);
+                }
+            }
+        }
+        block_sum2<WPR>(s, w, tid, s_part);
     }
 
     const TokenResult r = token_tail<GRAD>(p, t, src, c, s, w, zy, ybad, tid == 0);
@@ -452,28 +571,41 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
             }
             return;
         }
-        // sweep 3: dz = coef * p, minus coef at the target
+        // sweep 3: dz = coef * p, minus coef at the target.  Without the
+        // bonus, coef is folded into the exponent: |coef| p_v = 2^(z_v log2(e)
+        // - (c2 - log2|coef|)), and its sign goes onto the stored bits.  The
+        // target element is rewritten by the lane that owns it from
+        // coef * p_y - coef.
         opaque_regs(x);
+        const int ky = vy / TPR, ey = ybad ? -1 : y % VEC;
+        const float c3 = r.c2 - log2f(fabsf(r.coef));
+        const bool neg = r.coef < 0.0f;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = k * TPR + tid;
-            float f[VEC];
-            In<DTI>::unpack(x[k], f);
-            float d[VEC];
-            if (r.eb == 0.0f) {
+            if (idx < nvec) {
+                float f[VEC];
+                In<DTI>::unpack(x[k], f);
+                float d[VEC];
+                if (r.eb == 0.0f) {
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) d[e] = r.coef * __builtin_amdgcn_exp2f(fmaf(f[e], kLog2e, -r.c2));
-            } else {
+                    for (int e = 0; e < VEC; ++e) d[e] = __builtin_amdgcn_exp2f(fmaf(f[e], kLog2e, -c3));
+                } else {
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) d[e] = dz_with_bonus(fmaf(f[e], kLog2e, -r.c2), r.ea, r.eb);
+                    for (int e = 0; e < VEC; ++e) d[e] = dz_with_bonus(fmaf(f[e], kLog2e, -r.c2), r.ea, r.eb);
+                }
+                if (k == ky && idx == vy) {
+                    const float tty = fmaf(zy, kLog2e, -r.c2);
+                    const float dy = r.eb == 0.0f ? fmaf(r.coef, __builtin_amdgcn_exp2f(tty), -r.coef)
+                                                  : dz_with_bonus(tty, r.ea, r.eb) - r.coef;
+                    // stored with the sign flip applied to the whole vector below
+                    const float dys = (r.eb == 0.0f && neg) ? -dy : dy;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        if (e == ey) d[e] = dys;
+                }
+                Out<DTO>::template store<VEC>(orow, idx * VEC, d, r.eb == 0.0f && neg);
             }
-            if (idx == vy && !ybad) {
-                const int ey = y % VEC;
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    if (e == ey) d[e] -= r.coef;
-            }
-            if (idx < nvec) Out<DTO>::template store<VEC>(orow, idx * VEC, d);
         }
     }
 }

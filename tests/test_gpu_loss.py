@@ -123,6 +123,49 @@ def test_bad_targets_and_nan_logits_are_flagged_not_read():
     assert acc.add(clean) == "OK"                 # a fresh window
 
 
+# first: elements held by the first vector of every lane of a row (lanes per
+# row x elements per 16-byte vector on that kernel path)
+@pytest.mark.parametrize("V,dtype,first", [(151936, torch.bfloat16, 8192), (16384, torch.bfloat16, 2048),
+                                           (4096, torch.bfloat16, 512), (1024, torch.float32, 256)])
+def test_special_rows(V, dtype, first):
+    # Rows the one-sweep sums cannot take and that go through the exact
+    # max-shifted sweeps instead: scattered -inf logits, the whole first
+    # vector of every lane at -inf, a logit ~150 nats above the rest of its
+    # lane, a -inf target logit; plus a constant row and a row shifted down.
+    print(f"special rows V={V} {dtype}", flush=True)
+    n = 8
+    d = make_chunk(n, V, dtype, seed=40 + V, masked_frac=0.0, n_rows=2)
+    z = d["logits"].float().cpu()
+    rng = np.random.default_rng(V)
+    z[1, rng.choice(V, V // 100, replace=False)] = float("-inf")
+    z[2, :first] = float("-inf")
+    z[3, V // 2 + 3] = 150.0
+    z[4].fill_(0.5)
+    z[5] -= 30.0
+    z[6, int(d["target"][6])] = float("-inf")
+    for r in (1, 2):
+        if not np.isfinite(z[r, int(d["target"][r])]):
+            d["target"][r] = int(np.nonzero(np.isfinite(z[r].numpy()))[0][-1])
+    zz = z.to(dtype)
+    d["logits"].copy_(zz.to(DEV))
+    d["z64"] = zz.double().numpy()
+    d["g"]["target"].copy_(torch.from_numpy(d["target"]))
+    lp = oracle.logprob_fwd(d["z64"], d["target"], np.ones(n, np.uint8))["logp"]
+    with np.errstate(invalid="ignore"):
+        d["old"] = np.where(np.isfinite(lp), lp + 0.05, 0.0).astype(np.float32)
+    d["g"]["old"].copy_(torch.from_numpy(d["old"]))
+    ws = run_gpu(d, scale=0.1)
+    ref = run_oracle(d, 0.1)
+    assert ref["nonfinite"].tolist() == [False] * 6 + [True, False]
+    assert_tokens_match(ws, ref, d)
+    f_logp, f_lse, f_ent = ops.logprob_fwd(d["logits"], d["g"]["target"], d["g"]["mask"])
+    assert torch.equal(f_logp, ws["logp"]) and torch.equal(f_ent, ws["entropy"])
+    fwd = oracle.logprob_fwd(d["z64"], d["target"], d["mask"])
+    fin = np.isfinite(fwd["logp"])
+    assert np.max(np.abs(to_f64(f_logp)[fin] - fwd["logp"][fin])) <= (1e-5 if dtype == torch.float32 else 2e-3)
+    assert np.max(np.abs(to_f64(f_lse) - fwd["lse"])) <= (1e-5 if dtype == torch.float32 else 2e-3)
+
+
 def test_clip_quadrants_exercised():
     d = make_chunk(400, 1024, torch.float32, seed=8, noise=0.6)
     ref = run_oracle(d, 1.0)

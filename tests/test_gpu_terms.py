@@ -50,11 +50,15 @@ def _oracle_terms(d, mode, ent, kap, kind, scale):
 
 
 def _check_stats(ws, ref, d):
+    # Row sums of signed terms (the k1 estimate, the objective) can cancel,
+    # so the bound scales with the row's sum of magnitudes, as for the chunk.
     rows = ops.stats_to_dicts(ws["row_stats"])
-    want = oracle.row_stats(ref, d["row_off"].tolist())
-    for g, w in zip(rows, want):
-        for k in ("kl_sum", "obj_sum"):
-            assert g[k] == pytest.approx(w[k], rel=1e-4, abs=1e-6), (k, g[k], w[k])
+    off = d["row_off"].tolist()
+    want = oracle.row_stats(ref, off)
+    for r, (g, w) in enumerate(zip(rows, want)):
+        for k, per_tok in (("kl_sum", ref["kl"]), ("obj_sum", ref["obj"])):
+            mag = float(np.sum(np.abs(per_tok[off[r]:off[r + 1]])))
+            assert abs(g[k] - w[k]) <= 1e-4 * mag + 1e-9, (k, g[k], w[k], mag)
         assert g["n_valid"] == w["n_valid"]
     ch = ops.stats_to_dicts(ws["chunk_stats"])[0]
     cw = oracle.chunk_stats(ref, d["row_off"].tolist())

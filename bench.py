@@ -314,18 +314,29 @@ class PaddedStep:
         return f"warm: a step touches {ws / 1e6:.1f} MB of logits and dlogits, within the 256 MB last-level cache"
 
     def copy_context(self):
-        """Plain device copy of one chunk's bytes, timed like the kernel."""
-        torch = self.torch
+        """The library's streaming copy (grpo_stream_probe) of one chunk's bytes,
+        timed like the kernel: the bandwidth a plain copy of the same bytes gets."""
+        return self._stream_rate(self.ops.STREAM_COPY)
+
+    def read_context(self):
+        """The same for a plain read of one chunk's logits (the ahead pass's yardstick)."""
+        return self._stream_rate(self.ops.STREAM_READ)
+
+    def _stream_rate(self, mode):
+        torch, ops = self.torch, self.ops
         n = self.ws["logp"].numel()
-        src, dst = self.logits[:n], self.dlogits[:n]
+        src = self.logits[:n]
+        dst = self.dlogits[:n] if mode == ops.STREAM_COPY else None
+        nbytes = src.numel() * src.element_size()
+        dst = ops.stream_probe(mode, src, dst, nbytes)
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        dst.copy_(src)
         c0.record()
         for _ in range(3):
-            dst.copy_(src)
+            ops.stream_probe(mode, src, dst, nbytes)
         c1.record()
         torch.cuda.synchronize()
-        return 3 * 2 * src.numel() * src.element_size() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        moved = nbytes * (2 if mode == ops.STREAM_COPY else 1)
+        return 3 * moved / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
     def sample(self, n, start=0):
         """(z float64 [n, V], target, drift, advantage) of valid tokens start .. start+n."""
@@ -681,6 +692,7 @@ def main():
             a_ms, a_units, a_n = step.ahead_timed.totals()
             cfg["ahead_ms_per_step"] = round(a_ms / args.steps, 4)
             cfg["ahead_read_GBs"] = round(a_units / (a_ms * 1e-3) / 1e9, 1)
+            cfg["device_read_GBs"] = round(step.read_context(), 1)
     if wl == "compact":
         achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -31,6 +31,7 @@ class GrpoError(RuntimeError):
 
 KL_K1, KL_K2, KL_K3 = 1, 2, 3
 AGG_TOKEN_MEAN, AGG_SEQ_MEAN_TOKEN_SUM, AGG_SEQ_MEAN_TOKEN_MEAN = 0, 1, 2
+STREAM_COPY, STREAM_READ, STREAM_FILL = 0, 1, 2
 
 
 class Stats(ctypes.Structure):
@@ -151,6 +152,7 @@ PROTOTYPES = {
     "grpo_accum_add": (ctypes.c_int, [ctypes.POINTER(Accum), ctypes.POINTER(Stats)]),
     "grpo_accum_finalize": (ctypes.c_int, [ctypes.POINTER(Accum), ctypes.POINTER(StepResult),
                                            ctypes.POINTER(ctypes.c_int32)]),
+    "grpo_stream_probe": (ctypes.c_int, [_p, _i32, _p, _p, _i64]),
 }
 
 _lib = None

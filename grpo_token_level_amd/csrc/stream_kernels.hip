@@ -1,0 +1,85 @@
+// Streaming yardsticks for measurement: a plain 16-byte copy, read and fill
+// of one buffer, with the access pattern that sustains the most bandwidth
+// here (many small blocks, four 16-byte vectors in flight per lane, no
+// reuse).  They carry none of the method's arithmetic; the benchmark times
+// them beside the loss kernels to place those against what the memory
+// system delivers for the same bytes.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.h"
+
+using grpo::fail;
+using grpo::ok;
+
+namespace {
+
+constexpr int kLanes = 256;
+constexpr int kPerLane = 4;
+constexpr int64_t kPerBlock = (int64_t)kLanes * kPerLane;   // 16-byte vectors per block
+
+// Block b covers vectors [b*1024, b*1024 + 1024); lane l takes l, l+256, ...
+__global__ __launch_bounds__(kLanes) void stream_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                             int64_t n) {
+    const int64_t base = (int64_t)blockIdx.x * kPerBlock + threadIdx.x;
+    uint4 v[kPerLane];
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u)
+        if (base + u * kLanes < n) v[u] = src[base + u * kLanes];
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u)
+        if (base + u * kLanes < n) dst[base + u * kLanes] = v[u];
+}
+
+// Reads every byte; the xor of the data is written to out[0] only if it
+// equals a value no caller is expected to produce, so the loads are kept and
+// nothing is written in practice.
+__global__ __launch_bounds__(kLanes) void stream_read_kernel(const uint4* __restrict__ src, uint32_t* __restrict__ out,
+                                                             int64_t n) {
+    const int64_t base = (int64_t)blockIdx.x * kPerBlock + threadIdx.x;
+    uint32_t acc = 0;
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u)
+        if (base + u * kLanes < n) {
+            const uint4 v = src[base + u * kLanes];
+            acc ^= v.x ^ v.y ^ v.z ^ v.w;
+        }
+    if (acc == 0x9e3779b9u) out[0] = acc;
+}
+
+__global__ __launch_bounds__(kLanes) void stream_fill_kernel(uint4* __restrict__ dst, int64_t n) {
+    const int64_t base = (int64_t)blockIdx.x * kPerBlock + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u)
+        if (base + u * kLanes < n) dst[base + u * kLanes] = make_uint4(0, 0, 0, 0);
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int grpo_stream_probe(void* stream, int32_t mode, const void* src, void* dst, int64_t bytes) {
+    if (mode != GRPO_STREAM_COPY && mode != GRPO_STREAM_READ && mode != GRPO_STREAM_FILL)
+        return fail(GRPO_EINVAL, "grpo_stream_probe: unknown mode %d", mode);
+    if (bytes < 0 || bytes % 16) return fail(GRPO_EINVAL, "grpo_stream_probe: bytes must be a multiple of 16");
+    const bool need_src = mode != GRPO_STREAM_FILL;
+    if ((need_src && (!src || !al16(src))) || !dst || !al16(dst))
+        return fail(GRPO_EINVAL, "grpo_stream_probe: NULL or misaligned pointer (16 bytes)");
+    const int64_t n = bytes / 16;
+    if (n == 0) return ok();
+    const int64_t blocks = (n + kPerBlock - 1) / kPerBlock;
+    if (blocks > 0x7fffffffLL) return fail(GRPO_EINVAL, "grpo_stream_probe: too many bytes for one launch");
+    hipStream_t st = (hipStream_t)stream;
+    if (mode == GRPO_STREAM_COPY)
+        hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(kLanes), 0, st, (const uint4*)src,
+                           (uint4*)dst, n);
+    else if (mode == GRPO_STREAM_READ)
+        hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(kLanes), 0, st, (const uint4*)src,
+                           (uint32_t*)dst, n);
+    else
+        hipLaunchKernelGGL(stream_fill_kernel, dim3((unsigned)blocks), dim3(kLanes), 0, st, (uint4*)dst, n);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? ok() : fail(GRPO_EDEVICE, "grpo_stream_probe: %s", hipGetErrorString(e));
+}

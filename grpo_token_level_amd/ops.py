@@ -12,6 +12,7 @@ import numpy as np
 
 from . import _capi as C
 from ._capi import GrpoError, STATS_DTYPE, STATS_BYTES  # noqa: F401  (re-exported)
+from ._capi import STREAM_COPY, STREAM_READ, STREAM_FILL  # noqa: F401  (re-exported)
 
 # ---------------------------------------------------------------- host calls
 
@@ -277,6 +278,28 @@ def _rows2d(x, name):
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError(f"{name} must be 2-D with unit stride along the vocabulary")
     return x.stride(0)
+
+
+def stream_probe(mode, src=None, dst=None, nbytes=None):
+    """The measurement yardstick (grpo_stream_probe): a plain copy
+    (STREAM_COPY, src -> dst), read (STREAM_READ, src; dst is 16 bytes of
+    scratch) or zero fill (STREAM_FILL, dst) of ``nbytes`` bytes (default: the
+    whole src, or dst for a fill).  Returns dst."""
+    torch = _torch()
+    if mode == C.STREAM_READ and dst is None:
+        dst = torch.empty(16, dtype=torch.uint8, device=src.device)
+    if mode not in (C.STREAM_COPY, C.STREAM_READ, C.STREAM_FILL):
+        raise ValueError(f"unknown stream mode {mode}")
+    size = lambda t: t.numel() * t.element_size()  # noqa: E731
+    if nbytes is None:
+        nbytes = size(dst if mode == C.STREAM_FILL else src)
+    for t, name, need in ((src, "src", nbytes if mode != C.STREAM_FILL else 0),
+                          (dst, "dst", 16 if mode == C.STREAM_READ else nbytes)):
+        if need and (t is None or not t.is_cuda or not t.is_contiguous() or size(t) < need):
+            raise ValueError(f"{name} must be a contiguous GPU tensor of at least {need} bytes")
+    C.check(C.lib().grpo_stream_probe(_stream(), mode, ctypes.c_void_p(src.data_ptr()) if src is not None else None,
+                                      ctypes.c_void_p(dst.data_ptr()), nbytes))
+    return dst
 
 
 def count_valid(mask, out=None):

@@ -508,6 +508,20 @@ int grpo_accum_add(grpo_accum* acc, const grpo_stats* chunk);
  * then closed); *stepped = 0 otherwise. */
 int grpo_accum_finalize(grpo_accum* acc, grpo_step_result* out, int32_t* stepped);
 
+/* ===================================================== measurement yardstick */
+
+/* Not part of the method: a plain streaming pass over one buffer that the
+ * benchmark times beside the loss kernels, so that their bandwidth can be
+ * read against what the memory system delivers for a copy, a read or a write
+ * of the same bytes (and that calibrates byte counters with a known size). */
+#define GRPO_STREAM_COPY 0   /* dst[0, bytes) = src[0, bytes) */
+#define GRPO_STREAM_READ 1   /* reads src[0, bytes); dst: 16 bytes of scratch, in practice untouched */
+#define GRPO_STREAM_FILL 2   /* dst[0, bytes) = 0; src unused (may be NULL) */
+
+/* device.  bytes a multiple of 16 and pointers 16-byte aligned, else EINVAL;
+ * for a copy the ranges must not overlap.  Enqueued on `stream`. */
+int grpo_stream_probe(void* stream, int32_t mode, const void* src, void* dst, int64_t bytes);
+
 #ifdef __cplusplus
 }
 #endif

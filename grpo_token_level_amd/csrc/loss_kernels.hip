@@ -422,6 +422,20 @@ __device__ __forceinline__ float dz_with_bonus(float tt, float ea, float eb) {
     return pp > 0.0f ? pp * fmaf(eb, tt, ea) : 0.0f;
 }
 
+// Block -> token group.  Hardware dispatch sends block b to XCD b % 8; the
+// groups are dealt to the XCDs in runs of 16 consecutive groups instead of one
+// by one, so that a mask pattern with a short period in token order (valid
+// and masked tokens alternating, say) does not put all the valid tokens on
+// half of the XCDs.  A bijection on [0, nb): blocks below the largest
+// multiple of 8 x 16 are permuted, the rest map to themselves.
+__device__ __forceinline__ uint32_t xcd_runs(uint32_t b, uint32_t nb) {
+    constexpr uint32_t kXcd = 8, kRun = 16;
+    const uint32_t full = nb / (kXcd * kRun) * (kXcd * kRun);
+    if (b >= full) return b;
+    const uint32_t x = b % kXcd, j = b / kXcd;
+    return ((j / kRun) * kXcd + x) * kRun + j % kRun;
+}
+
 // ---------------------------------------------------------------- register-resident kernel
 //
 // TPR threads per token row, NV 16-byte vectors per thread.  TPR == 64: four
@@ -434,7 +448,7 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     constexpr int RPB = TPR == 64 ? 4 : 1;
     const int lrow = RPB == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int tid = RPB == 1 ? (int)threadIdx.x : (int)(threadIdx.x & 63);
-    const int64_t t = (int64_t)blockIdx.x * RPB + lrow;
+    const int64_t t = (int64_t)xcd_runs(blockIdx.x, gridDim.x) * RPB + lrow;
     if (t >= p.n_tok) return;   // wave-uniform (RPB > 1) or block-uniform (RPB == 1)
 
     const int nvec = (int)(p.V / VEC);   // the register path only runs for V / VEC <= TPR * NV

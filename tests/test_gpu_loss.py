@@ -166,6 +166,22 @@ def test_special_rows(V, dtype, first):
     assert np.max(np.abs(to_f64(f_lse) - fwd["lse"])) <= (1e-5 if dtype == torch.float32 else 2e-3)
 
 
+@pytest.mark.parametrize("V,n", [(16384, 300), (4096, 1100)])
+def test_many_blocks_with_a_periodic_mask(V, n):
+    # More blocks than one run of 8 x 16 (the block -> token deal over the
+    # XCDs permutes them) plus a ragged tail, with valid and masked tokens
+    # alternating: every token is processed exactly once, as the oracle says.
+    print(f"periodic mask V={V} n={n}", flush=True)
+    d = make_chunk(n, V, torch.bfloat16, seed=50 + n, masked_frac=0.0, n_rows=7)
+    d["mask"][1::2] = 0
+    d["g"]["mask"].copy_(torch.from_numpy(d["mask"]))
+    N = int(d["mask"].sum())
+    ws = run_gpu(d, scale=1.0 / N)
+    ref = run_oracle(d, 1.0 / N)
+    assert_tokens_match(ws, ref, d)
+    _check_stats(ws, ref, d)
+
+
 def test_clip_quadrants_exercised():
     d = make_chunk(400, 1024, torch.float32, seed=8, noise=0.6)
     ref = run_oracle(d, 1.0)

@@ -1,6 +1,9 @@
-// Host half of libgrpo: batch plans, group advantages and the step
-// accumulator.  Pure functions of their arguments; no allocation beyond small
-// stack/heap temporaries of the dynamic packer; no HIP calls.
+// Host half of libgrpo: batch plans (fixed, epochs, dynamic packing,
+// compaction), group advantages, the step accumulator, the frozen pi_old
+// cache bookkeeping and the probe verdict.  Pure functions of their arguments
+// (no allocation beyond small temporaries of the dynamic packer); the only
+// device work is the forward pass a cache record enqueues through
+// grpo_logprob_fwd.
 //
 // Sources: [P1] "Sizing mini-batches and micro-batches"; [P2] "03 Data
 // Protocol and Batch Lifecycle"; [P3] "22 - mini-batch, micro-batch and
@@ -230,11 +233,9 @@ extern "C" int grpo_plan_compaction(const int32_t* rows_per_rollout, int64_t n_r
     if (n_rollouts != expected_rollouts)
         return fail(GRPO_ECOUNT, "grpo_plan_compaction: the step holds %lld rollouts, %lld configured",
                     (long long)n_rollouts, (long long)expected_rollouts);
-    int64_t total = 0;
     for (int64_t r = 0; r < n_rollouts; ++r) {
         if (rows_per_rollout[r] < 1)
             return fail(GRPO_EINVAL, "grpo_plan_compaction: rollout %lld has no rows", (long long)r);
-        total += rows_per_rollout[r];
     }
     int64_t need = 0;
     for (int64_t g = 0; g < n_groups; ++g) {
@@ -249,7 +250,6 @@ extern "C" int grpo_plan_compaction(const int32_t* rows_per_rollout, int64_t n_r
     }
     if (!row_rollout || !row_seg || !row_src || !row_is_pad || !group_pad)
         return fail(GRPO_EINVAL, "grpo_plan_compaction: NULL output");
-    (void)total;
     int64_t out = 0, src = 0;
     for (int64_t g = 0; g < n_groups; ++g) {
         const int64_t first = src;

@@ -618,7 +618,12 @@ struct Workspace {
 // kVocabChunkMax) and the split count of dh = dz W_c (its output has only
 // ceil(n/256) x ceil(H/256) tiles, so its K range, the chunk's vocabulary, is
 // split; one partial per split, the same count for every chunk) are chosen
-// to minimise the summed rounds x k-steps of the dz, dh and dW launches.
+// to minimise the summed rounds x k-steps of the dz, dh and dW launches plus
+// the HBM time of the dh partials: each split's n x H fp32 partial is written
+// by the first chunk, read and rewritten by every later one and read once by
+// the final sum (2 x chunks x splits partials moved), converted to k-step
+// units with the measured rates (a 256 x 256 x 64 block step takes ~2 us at
+// ~1 PFLOP/s; HBM moves ~5 bytes per ns).
 struct Pass2Plan {
     int64_t chunk;
     int nsplit;
@@ -627,23 +632,27 @@ struct Pass2Plan {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus) {
+    constexpr double kKstepUs = 2.0, kHbmBytesPerUs = 5.0e6;
     const int64_t n_pad = round_up(n, kTokPad);
     const int64_t tm = cdiv(n, BM), th = cdiv(H, BN);
     Pass2Plan best{V < kVocabChunkMax ? V : kVocabChunkMax, 1};
-    int64_t best_cost = -1;
+    double best_cost = -1.0;
     const int64_t wmax = V < kVocabChunkMax ? round_up(V, BN) : kVocabChunkMax;
     const int64_t wmin = wmax < kVocabChunkMin ? wmax : kVocabChunkMin;
     for (int64_t w = wmin; w <= wmax; w += 2048 > wmax - wmin ? BN : 2048) {
         for (int sp = 1; sp <= kDhSplitMax; ++sp) {
-            int64_t cost = 0;
+            int64_t steps = 0, chunks = 0;
             for (int64_t c0 = 0; c0 < V; c0 += w) {
                 const int64_t vc = V - c0 < w ? V - c0 : w, tv = cdiv(vc, BN);
-                cost += cdiv(tm * tv, cus) * cdiv(H, BK);                              // dz
-                cost += cdiv(tv * th, cus) * cdiv(n_pad, BK);                          // dW
-                cost += cdiv(tm * th * sp, cus) * (round_up(cdiv(vc, sp), BK) / BK);   // dh
+                steps += cdiv(tm * tv, cus) * cdiv(H, BK);                              // dz
+                steps += cdiv(tv * th, cus) * cdiv(n_pad, BK);                          // dW
+                steps += cdiv(tm * th * sp, cus) * (round_up(cdiv(vc, sp), BK) / BK);   // dh
+                ++chunks;
             }
+            const double partial_bytes = 2.0 * (double)chunks * sp * (double)n * (double)H * 4.0;
+            const double cost = (double)steps + partial_bytes / (kHbmBytesPerUs * kKstepUs);
             // a split must save at least 1 % to be worth its partial
-            if (best_cost < 0 || cost * 100 < best_cost * 99) {
+            if (best_cost < 0.0 || cost * 100.0 < best_cost * 99.0) {
                 best_cost = cost;
                 best = {w < V ? w : V, sp};
             }

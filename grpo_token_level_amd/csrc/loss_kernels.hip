@@ -436,13 +436,90 @@ __device__ __forceinline__ uint32_t xcd_runs(uint32_t b, uint32_t nb) {
     return ((j / kRun) * kXcd + x) * kRun + j % kRun;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate: at most n vector-memory operations of this wave still
+// outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt not waited on)
+#define GRPO_LOSS_VMCNT(n) (((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// Per-vector steps of the sweeps, shared by the register-resident vectors and
+// the ones held in LDS.
+template <int DTI>
+__device__ __forceinline__ void sweep_sums(const uint4& v, float c, float& s, float& w) {
+    constexpr int VEC = In<DTI>::VEC;
+    float f[VEC];
+    In<DTI>::unpack(v, f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        const float tt = fmaf(f[e], kLog2e, -c);
+        const float ee = __builtin_amdgcn_exp2f(tt);
+        s += ee;
+        w = fmaf(ee, tt, w);
+    }
+}
+
+template <int DTI>
+__device__ __forceinline__ void sweep_max(const uint4& v, float& m) {
+    constexpr int VEC = In<DTI>::VEC;
+    float f[VEC];
+    In<DTI>::unpack(v, f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) m = fmaxf(m, f[e]);
+}
+
+template <int DTI>
+__device__ __forceinline__ void sweep_sums_clamped(const uint4& v, float c, float& s, float& w) {
+    constexpr int VEC = In<DTI>::VEC;
+    float f[VEC];
+    In<DTI>::unpack(v, f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        const float tt = fmaf(f[e], kLog2e, -c);
+        const float ee = __builtin_amdgcn_exp2f(tt);
+        s += ee;
+        w = fmaf(ee, fmaxf(tt, kNegClampLog2), w);
+    }
+}
+
+// dz of one vector (element index idx*VEC..), stored; `own_y`: this vector
+// holds the target, element ey, whose value the caller passes as zy.
+template <int DTI, int DTO>
+__device__ __forceinline__ void sweep_dz(void* orow, int idx, const uint4& v, const TokenResult& r, float c3, bool neg,
+                                         bool own_y, int ey, float zy) {
+    constexpr int VEC = In<DTI>::VEC;
+    float f[VEC];
+    In<DTI>::unpack(v, f);
+    float d[VEC];
+    if (r.eb == 0.0f) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d[e] = __builtin_amdgcn_exp2f(fmaf(f[e], kLog2e, -c3));
+    } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d[e] = dz_with_bonus(fmaf(f[e], kLog2e, -r.c2), r.ea, r.eb);
+    }
+    if (own_y) {
+        const float tty = fmaf(zy, kLog2e, -r.c2);
+        const float dy = r.eb == 0.0f ? fmaf(r.coef, __builtin_amdgcn_exp2f(tty), -r.coef)
+                                      : dz_with_bonus(tty, r.ea, r.eb) - r.coef;
+        // stored with the sign flip applied to the whole vector below
+        const float dys = (r.eb == 0.0f && neg) ? -dy : dy;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            if (e == ey) d[e] = dys;
+    }
+    Out<DTO>::template store<VEC>(orow, idx * VEC, d, r.eb == 0.0f && neg);
+}
+
 // ---------------------------------------------------------------- register-resident kernel
 //
-// TPR threads per token row, NV 16-byte vectors per thread.  TPR == 64: four
-// token rows per 256-thread block, one wave each, wave-only reductions.
-// TPR > 64: one row per block, cross-wave reduction through LDS.
-template <int DTI, int DTO, int TPR, int NV, bool GRAD>
+// TPR threads per token row, NV 16-byte vectors per thread in registers and
+// NL more in LDS (filled by direct-to-LDS loads issued with the register
+// loads, so a row that outgrows the register file is still read once).
+// TPR == 64: four token rows per 256-thread block, one wave each, wave-only
+// reductions.  TPR > 64: one row per block, cross-wave reduction through LDS.
+template <int DTI, int DTO, int TPR, int NV, bool GRAD, int NL = 0>
 __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const TokParams p) {
+    static_assert(NL == 0 || TPR == 1024, "LDS-held vectors are for the one-row-per-block path");
     constexpr int VEC = In<DTI>::VEC;
     constexpr int WPR = TPR / 64;
     constexpr int RPB = TPR == 64 ? 4 : 1;
@@ -451,7 +528,7 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     const int64_t t = (int64_t)xcd_runs(blockIdx.x, gridDim.x) * RPB + lrow;
     if (t >= p.n_tok) return;   // wave-uniform (RPB > 1) or block-uniform (RPB == 1)
 
-    const int nvec = (int)(p.V / VEC);   // the register path only runs for V / VEC <= TPR * NV
+    const int nvec = (int)(p.V / VEC);   // the register path only runs for V / VEC <= TPR * (NV + NL)
     const int64_t src = token_source(p, t);
     if (src < 0) {
         if (tid == 0) bad_source_outputs<GRAD>(p, t);
@@ -467,7 +544,7 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         if constexpr (GRAD) {
             if (orow) {
 #pragma unroll
-                for (int k = 0; k < NV; ++k) {
+                for (int k = 0; k < NV + NL; ++k) {
                     const int idx = k * TPR + tid;
                     if (idx < nvec) Out<DTO>::template zero<VEC>(orow, idx * VEC);
                 }
@@ -493,6 +570,17 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     uint4 x[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) x[k] = vrow[min(k * TPR + tid, nvec - 1)];
+    // Vectors NV .. NV+NL-1 of each lane go straight to LDS: one
+    // global_load_lds moves the wave's 64 lanes x 16 bytes to base + 16 * lane,
+    // so lane tid's vector j sits at s_tail[j * TPR + tid].
+    [[maybe_unused]] __shared__ uint4 s_tail[NL > 0 ? NL * TPR : 1];
+    if constexpr (NL > 0) {
+        const int wave = tid >> 6;
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+            __builtin_amdgcn_global_load_lds(vrow + min((NV + j) * TPR + tid, nvec - 1),
+                                             (lds_void*)(s_tail + j * TPR + wave * 64), 16, 0, 0);
+    }
 
     [[maybe_unused]] __shared__ float s_part[WPR][3];
     [[maybe_unused]] __shared__ float s_zy;
@@ -521,18 +609,15 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     }
     opaque_regs(x);
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        if (k * TPR + tid < nvec) {
-            float f[VEC];
-            In<DTI>::unpack(x[k], f);
+    for (int k = 0; k < NV; ++k)
+        if (k * TPR + tid < nvec) sweep_sums<DTI>(x[k], c, s, w);
+    if constexpr (NL > 0) {
+        // this wave's direct-to-LDS loads have landed (each lane reads only
+        // the 16 bytes its own wave's load wrote)
+        __builtin_amdgcn_s_waitcnt(GRPO_LOSS_VMCNT(0));
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float tt = fmaf(f[e], kLog2e, -c);
-                const float ee = __builtin_amdgcn_exp2f(tt);
-                s += ee;
-                w = fmaf(ee, tt, w);
-            }
-        }
+        for (int j = 0; j < NL; ++j)
+            if ((NV + j) * TPR + tid < nvec) sweep_sums<DTI>(s_tail[j * TPR + tid], c, s, w);
     }
     block_merge<WPR>(c, s, w, tid, s_part);
     if constexpr (WPR > 1) zy = s_zy;
@@ -544,33 +629,22 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         opaque_regs(x);
         float m = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            if (k * TPR + tid < nvec) {
-                float f[VEC];
-                In<DTI>::unpack(x[k], f);
+        for (int k = 0; k < NV; ++k)
+            if (k * TPR + tid < nvec) sweep_max<DTI>(x[k], m);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) m = fmaxf(m, f[e]);
-            }
-        }
+        for (int j = 0; j < NL; ++j)
+            if ((NV + j) * TPR + tid < nvec) sweep_max<DTI>(s_tail[j * TPR + tid], m);
         m = block_max<WPR>(m, tid, s_part);
         c = m * kLog2e;
         s = 0.0f;
         w = 0.0f;
         opaque_regs(x);
 #pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            if (k * TPR + tid < nvec) {
-                float f[VEC];
-                In<DTI>::unpack(x[k], f);
+        for (int k = 0; k < NV; ++k)
+            if (k * TPR + tid < nvec) sweep_sums_clamped<DTI>(x[k], c, s, w);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const float tt = fmaf(f[e], kLog2e, -c);
-                    const float ee = __builtin_amdgcn_exp2f(tt);
-                    s += ee;
-                    w = fmaf(ee, fmaxf(tt, kNegClampLog2), w);
-                }
-            }
-        }
+        for (int j = 0; j < NL; ++j)
+            if ((NV + j) * TPR + tid < nvec) sweep_sums_clamped<DTI>(s_tail[j * TPR + tid], c, s, w);
         block_sum2<WPR>(s, w, tid, s_part);
     }
 
@@ -579,7 +653,7 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         if (!orow) return;
         if (r.coef == 0.0f && r.eb == 0.0f) {   // zero advantage or clipped, no bonus: the row is zero
 #pragma unroll
-            for (int k = 0; k < NV; ++k) {
+            for (int k = 0; k < NV + NL; ++k) {
                 const int idx = k * TPR + tid;
                 if (idx < nvec) Out<DTO>::template zero<VEC>(orow, idx * VEC);
             }
@@ -591,35 +665,19 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         // target element is rewritten by the lane that owns it from
         // coef * p_y - coef.
         opaque_regs(x);
-        const int ky = vy / TPR, ey = ybad ? -1 : y % VEC;
+        const int ky = ybad ? -1 : vy / TPR, ey = ybad ? -1 : y % VEC;   // ky: block-uniform
         const float c3 = r.c2 - log2f(fabsf(r.coef));
         const bool neg = r.coef < 0.0f;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = k * TPR + tid;
-            if (idx < nvec) {
-                float f[VEC];
-                In<DTI>::unpack(x[k], f);
-                float d[VEC];
-                if (r.eb == 0.0f) {
+            if (idx < nvec) sweep_dz<DTI, DTO>(orow, idx, x[k], r, c3, neg, k == ky && idx == vy, ey, zy);
+        }
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) d[e] = __builtin_amdgcn_exp2f(fmaf(f[e], kLog2e, -c3));
-                } else {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) d[e] = dz_with_bonus(fmaf(f[e], kLog2e, -r.c2), r.ea, r.eb);
-                }
-                if (k == ky && idx == vy) {
-                    const float tty = fmaf(zy, kLog2e, -r.c2);
-                    const float dy = r.eb == 0.0f ? fmaf(r.coef, __builtin_amdgcn_exp2f(tty), -r.coef)
-                                                  : dz_with_bonus(tty, r.ea, r.eb) - r.coef;
-                    // stored with the sign flip applied to the whole vector below
-                    const float dys = (r.eb == 0.0f && neg) ? -dy : dy;
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        if (e == ey) d[e] = dys;
-                }
-                Out<DTO>::template store<VEC>(orow, idx * VEC, d, r.eb == 0.0f && neg);
-            }
+        for (int j = 0; j < NL; ++j) {
+            const int idx = (NV + j) * TPR + tid;
+            if (idx < nvec)
+                sweep_dz<DTI, DTO>(orow, idx, s_tail[j * TPR + tid], r, c3, neg, NV + j == ky && idx == vy, ey, zy);
         }
     }
 }
@@ -998,36 +1056,41 @@ __global__ __launch_bounds__(256) void tok_row_kernel(const int64_t* __restrict_
 struct RegCfg {
     int tpr;
     int nv;
+    int nl;   // 16-byte vectors per thread held in LDS
 };
 
 // Register-resident configurations, in order of preference; the first whose
-// capacity tpr * nv covers the row's 16-byte vectors is used.
+// capacity tpr * (nv + nl) covers the row's 16-byte vectors is used.
 // NV stops at 19: at 1024 threads a lane has 128 VGPRs, and 19 vectors (76
-// VGPRs of row data) is the most that compiles without spilling.
-constexpr RegCfg kRegCfgs[] = {{64, 1}, {64, 2}, {64, 4}, {64, 8}, {256, 4}, {256, 8},
-                               {1024, 4}, {1024, 8}, {1024, 12}, {1024, 16}, {1024, 19}};
+// VGPRs of row data) is the most that compiles without spilling.  The last
+// configuration adds 9 vectors per lane in LDS (144 KiB of the CU's 160 KiB):
+// rows up to 229 376 bf16 / 114 688 fp32 logits are still read once.
+constexpr RegCfg kRegCfgs[] = {{64, 1, 0},    {64, 2, 0},    {64, 4, 0},     {64, 8, 0},
+                               {256, 4, 0},   {256, 8, 0},   {1024, 4, 0},   {1024, 8, 0},
+                               {1024, 12, 0}, {1024, 16, 0}, {1024, 19, 0},  {1024, 19, 9}};
 
 template <int DTI, int DTO, bool GRAD>
 hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st) {
     const int rpb = c.tpr == 64 ? 4 : 1;
     const dim3 grid((unsigned)((p.n_tok + rpb - 1) / rpb));
     const dim3 block(c.tpr == 64 ? 256 : c.tpr);
-#define GRPO_REG_CASE(TPR_, NV_)                                                                  \
-    if (c.tpr == TPR_ && c.nv == NV_) {                                                           \
-        hipLaunchKernelGGL((tok_reg_kernel<DTI, DTO, TPR_, NV_, GRAD>), grid, block, 0, st, p); \
-        return hipGetLastError();                                                                 \
+#define GRPO_REG_CASE(TPR_, NV_, NL_)                                                                  \
+    if (c.tpr == TPR_ && c.nv == NV_ && c.nl == NL_) {                                                 \
+        hipLaunchKernelGGL((tok_reg_kernel<DTI, DTO, TPR_, NV_, GRAD, NL_>), grid, block, 0, st, p); \
+        return hipGetLastError();                                                                      \
     }
-    GRPO_REG_CASE(64, 1)
-    GRPO_REG_CASE(64, 2)
-    GRPO_REG_CASE(64, 4)
-    GRPO_REG_CASE(64, 8)
-    GRPO_REG_CASE(256, 4)
-    GRPO_REG_CASE(256, 8)
-    GRPO_REG_CASE(1024, 4)
-    GRPO_REG_CASE(1024, 8)
-    GRPO_REG_CASE(1024, 12)
-    GRPO_REG_CASE(1024, 16)
-    GRPO_REG_CASE(1024, 19)
+    GRPO_REG_CASE(64, 1, 0)
+    GRPO_REG_CASE(64, 2, 0)
+    GRPO_REG_CASE(64, 4, 0)
+    GRPO_REG_CASE(64, 8, 0)
+    GRPO_REG_CASE(256, 4, 0)
+    GRPO_REG_CASE(256, 8, 0)
+    GRPO_REG_CASE(1024, 4, 0)
+    GRPO_REG_CASE(1024, 8, 0)
+    GRPO_REG_CASE(1024, 12, 0)
+    GRPO_REG_CASE(1024, 16, 0)
+    GRPO_REG_CASE(1024, 19, 0)
+    GRPO_REG_CASE(1024, 19, 9)
 #undef GRPO_REG_CASE
     return hipErrorInvalidValue;
 }
@@ -1038,7 +1101,7 @@ hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st) {
     if (vec_ok) {
         const int64_t nvec = p.V / In<DTI>::VEC;
         for (const RegCfg& c : kRegCfgs)
-            if ((int64_t)c.tpr * c.nv >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st);
+            if ((int64_t)c.tpr * (c.nv + c.nl) >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st);
     }
     hipLaunchKernelGGL((tok_generic_kernel<DTI, DTO, GRAD>), dim3((unsigned)p.n_tok), dim3(256), 0, st, p);
     return hipGetLastError();

@@ -46,6 +46,13 @@ CASES = [
     (1000, torch.bfloat16, torch.bfloat16, 23),
     (50257, torch.bfloat16, torch.bfloat16, 11),
     (200000, torch.bfloat16, torch.bfloat16, 5),
+    # rows past the register file: the tail of each lane's vectors in LDS
+    (155656, torch.bfloat16, torch.bfloat16, 5),
+    (202048, torch.bfloat16, torch.bfloat16, 6),
+    (229376, torch.bfloat16, torch.float32, 3),
+    (100000, torch.float32, torch.float32, 4),
+    # one vector past that capacity: the generic kernel
+    (229384, torch.bfloat16, torch.bfloat16, 3),
 ]
 
 
@@ -61,11 +68,12 @@ def test_loss_matches_oracle(V, din, dout, n):
     _check_stats(ws, ref, d)
 
 
-@pytest.mark.parametrize("din", [torch.float32, torch.bfloat16])
-def test_padded_row_stride_and_inplace(din):
+@pytest.mark.parametrize("din,V,ld,n", [(torch.float32, 1024, 1040, 45), (torch.bfloat16, 1024, 1040, 45),
+                                        (torch.bfloat16, 202048, 202064, 4)])
+def test_padded_row_stride_and_inplace(din, V, ld, n):
     # logits rows padded to ld > V; then the same chunk updated in place
-    V, n = 1024, 45
-    d = make_chunk(n, V, din, seed=3, ld=1040)
+    # (the last case holds part of each row in LDS)
+    d = make_chunk(n, V, din, seed=3, ld=ld)
     scale = 0.01
     ref = run_oracle(d, scale)
     ws = run_gpu(d, scale=scale)
@@ -126,7 +134,8 @@ def test_bad_targets_and_nan_logits_are_flagged_not_read():
 # first: elements held by the first vector of every lane of a row (lanes per
 # row x elements per 16-byte vector on that kernel path)
 @pytest.mark.parametrize("V,dtype,first", [(151936, torch.bfloat16, 8192), (16384, torch.bfloat16, 2048),
-                                           (4096, torch.bfloat16, 512), (1024, torch.float32, 256)])
+                                           (4096, torch.bfloat16, 512), (1024, torch.float32, 256),
+                                           (202048, torch.bfloat16, 8192)])
 def test_special_rows(V, dtype, first):
     # Rows the one-sweep sums cannot take and that go through the exact
     # max-shifted sweeps instead: scattered -inf logits, the whole first
@@ -234,7 +243,8 @@ def test_chunked_equals_unchunked_bit_exact():
 
 
 @pytest.mark.parametrize("V,dtype,n", [(1024, torch.float32, 130), (151936, torch.bfloat16, 7),
-                                       (1000, torch.bfloat16, 19), (4096, torch.bfloat16, 66)])
+                                       (1000, torch.bfloat16, 19), (4096, torch.bfloat16, 66),
+                                       (202048, torch.bfloat16, 5), (100000, torch.float32, 4)])
 def test_logprob_fwd_matches_oracle(V, dtype, n):
     d = make_chunk(n, V, dtype, seed=12 + V, with_old=False)
     logp, lse, ent = ops.logprob_fwd(d["logits"], d["g"]["target"], d["g"]["mask"])

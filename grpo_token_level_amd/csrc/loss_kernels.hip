@@ -113,7 +113,7 @@ template <> struct Out<GRPO_BF16> {
     static constexpr int BYTES = 2;
     // neg: every stored value negated (sign bits flipped after rounding)
     template <int N>
-    __device__ static __forceinline__ void store(void* row, int e0, const float (&d)[N], bool neg = false) {
+    __device__ static __forceinline__ void store(void* row, int64_t e0, const float (&d)[N], bool neg = false) {
         uint16_t* p = reinterpret_cast<uint16_t*>(row) + e0;
         const uint32_t sg = neg ? 0x80008000u : 0u;
         if constexpr (N == 8) {
@@ -128,7 +128,7 @@ template <> struct Out<GRPO_BF16> {
         }
     }
     template <int N>
-    __device__ static __forceinline__ void zero(void* row, int e0) {
+    __device__ static __forceinline__ void zero(void* row, int64_t e0) {
         uint16_t* p = reinterpret_cast<uint16_t*>(row) + e0;
         if constexpr (N == 8) st16_nt(reinterpret_cast<uint4*>(p), make_uint4(0, 0, 0, 0));
         else st16_nt(reinterpret_cast<uint2*>(p), make_uint2(0, 0));
@@ -142,7 +142,7 @@ template <> struct Out<GRPO_BF16> {
 template <> struct Out<GRPO_F32> {
     static constexpr int BYTES = 4;
     template <int N>
-    __device__ static __forceinline__ void store(void* row, int e0, const float (&d)[N], bool neg = false) {
+    __device__ static __forceinline__ void store(void* row, int64_t e0, const float (&d)[N], bool neg = false) {
         uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<float*>(row) + e0);
         const uint32_t sg = neg ? 0x80000000u : 0u;
         st16(p, make_uint4(__float_as_uint(d[0]) ^ sg, __float_as_uint(d[1]) ^ sg, __float_as_uint(d[2]) ^ sg,
@@ -152,7 +152,7 @@ template <> struct Out<GRPO_F32> {
                                    __float_as_uint(d[6]) ^ sg, __float_as_uint(d[7]) ^ sg));
     }
     template <int N>
-    __device__ static __forceinline__ void zero(void* row, int e0) {
+    __device__ static __forceinline__ void zero(void* row, int64_t e0) {
         float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(row) + e0);
         st16_nt(p, make_float4(0.f, 0.f, 0.f, 0.f));
         if constexpr (N == 8) st16_nt(p + 1, make_float4(0.f, 0.f, 0.f, 0.f));
@@ -484,8 +484,8 @@ __device__ __forceinline__ void sweep_sums_clamped(const uint4& v, float c, floa
 // dz of one vector (element index idx*VEC..), stored; `own_y`: this vector
 // holds the target, element ey, whose value the caller passes as zy.
 template <int DTI, int DTO>
-__device__ __forceinline__ void sweep_dz(void* orow, int idx, const uint4& v, const TokenResult& r, float c3, bool neg,
-                                         bool own_y, int ey, float zy) {
+__device__ __forceinline__ void sweep_dz(void* orow, int64_t idx, const uint4& v, const TokenResult& r, float c3,
+                                         bool neg, bool own_y, int ey, float zy) {
     constexpr int VEC = In<DTI>::VEC;
     float f[VEC];
     In<DTI>::unpack(v, f);
@@ -682,14 +682,80 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     }
 }
 
-// ---------------------------------------------------------------- generic streaming kernel
+// ---------------------------------------------------------------- streaming kernel
 //
-// Any stride, alignment or vocabulary size: 256 threads per token, element
-// loads, three passes over the row in memory.
+// Rows the register/LDS path cannot take: V beyond its capacity, or a stride,
+// base or V that leaves rows off 16-byte alignment.  256 threads per token
+// stream the row from memory: 16-byte vectors over its aligned interior,
+// single elements for the head before the first 16-byte boundary and the tail
+// after the last whole vector.  The sums use the register path's per-lane
+// shift and exact merge (the exact max-shifted sweeps when they overflow);
+// the dz pass streams the row again, so a token costs two reads and one write
+// of the row.  Interior vectors of dz are 16-byte (8-byte) stores when the
+// output row shares the input row's alignment, single elements otherwise.
+
+constexpr int kStreamTPR = 256;
+constexpr int kStreamUnroll = 4;   // vectors in flight per lane
+
+// Elements before the row's first 16-byte boundary (at most V), the whole
+// 16-byte vectors after them, and the first element after those vectors.
+struct RowGeom {
+    int64_t hh;
+    int64_t nvi;
+    int64_t t0;
+};
+
+template <int BYTES, int VEC>
+__device__ __forceinline__ RowGeom row_geom(const void* row, int64_t V) {
+    const int64_t h = (int64_t)((16u - (uint32_t)(reinterpret_cast<uintptr_t>(row) & 15u)) & 15u) / BYTES;
+    RowGeom g;
+    g.hh = h < V ? h : V;
+    g.nvi = (V - g.hh) / VEC;
+    g.t0 = g.hh + g.nvi * VEC;
+    return g;
+}
+
+// a zero row of V output elements, whatever the row's alignment
+template <int DTO>
+__device__ __forceinline__ void zero_row_stream(void* orow, int64_t V, int tid) {
+    constexpr int OVEC = 16 / Out<DTO>::BYTES;   // output elements per 16-byte store
+    const RowGeom g = row_geom<Out<DTO>::BYTES, OVEC>(orow, V);
+    if (tid < g.hh) Out<DTO>::scalar(orow, tid, 0.0f);
+    uint4* v = reinterpret_cast<uint4*>(reinterpret_cast<char*>(orow) + g.hh * Out<DTO>::BYTES);
+    for (int64_t i = tid; i < g.nvi; i += kStreamTPR) st16_nt(v + i, make_uint4(0, 0, 0, 0));
+    if (g.t0 + tid < V) Out<DTO>::scalar(orow, g.t0 + tid, 0.0f);
+}
+
+// 2^t and 2^t t sums of one element
+__device__ __forceinline__ void elem_sums(float z, float c, float& s, float& w) {
+    const float tt = fmaf(z, kLog2e, -c);
+    const float ee = __builtin_amdgcn_exp2f(tt);
+    s += ee;
+    w = fmaf(ee, tt, w);
+}
+
+__device__ __forceinline__ void elem_sums_clamped(float z, float c, float& s, float& w) {
+    const float tt = fmaf(z, kLog2e, -c);
+    const float ee = __builtin_amdgcn_exp2f(tt);
+    s += ee;
+    w = fmaf(ee, fmaxf(tt, kNegClampLog2), w);
+}
+
+// dlogits value of element z (true value, sign applied); own_y: this is the target
+__device__ __forceinline__ float elem_dz(float z, const TokenResult& r, float c3, bool neg, bool own_y) {
+    const float tt = fmaf(z, kLog2e, -r.c2);
+    if (own_y) {
+        return r.eb == 0.0f ? fmaf(r.coef, __builtin_amdgcn_exp2f(tt), -r.coef) : dz_with_bonus(tt, r.ea, r.eb) - r.coef;
+    }
+    if (r.eb != 0.0f) return dz_with_bonus(tt, r.ea, r.eb);
+    const float d = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -c3));
+    return neg ? -d : d;
+}
+
 template <int DTI, int DTO, bool GRAD>
-__global__ __launch_bounds__(256) void tok_generic_kernel(const TokParams p) {
-    constexpr int TPR = 256;
-    constexpr int WPR = TPR / 64;
+__global__ __launch_bounds__(kStreamTPR) void tok_stream_kernel(const TokParams p) {
+    constexpr int TPR = kStreamTPR, WPR = TPR / 64, U = kStreamUnroll;
+    constexpr int VEC = In<DTI>::VEC;
     const int64_t t = blockIdx.x;
     if (t >= p.n_tok) return;
     const int tid = threadIdx.x;
@@ -698,6 +764,7 @@ __global__ __launch_bounds__(256) void tok_generic_kernel(const TokParams p) {
         if (tid == 0) bad_source_outputs<GRAD>(p, t);
         return;
     }
+    const int64_t V = p.V;
     void* orow = nullptr;
     if constexpr (GRAD) {
         if (p.dlogits) orow = reinterpret_cast<char*>(p.dlogits) + src * p.ld_out * Out<DTO>::BYTES;
@@ -705,60 +772,110 @@ __global__ __launch_bounds__(256) void tok_generic_kernel(const TokParams p) {
     if (p.mask[src] == 0) {
         if (tid == 0) masked_outputs<GRAD>(p, t);
         if constexpr (GRAD) {
-            if (orow)
-                for (int64_t v = tid; v < p.V; v += TPR) Out<DTO>::scalar(orow, v, 0.0f);
+            if (orow) zero_row_stream<DTO>(orow, V, tid);
         }
         return;
     }
     const char* irow = reinterpret_cast<const char*>(p.logits) + src * p.ld * In<DTI>::BYTES;
+    const RowGeom g = row_geom<In<DTI>::BYTES, VEC>(irow, V);
+    const uint4* vin = reinterpret_cast<const uint4*>(irow + g.hh * In<DTI>::BYTES);
     const int32_t y = p.target[src];
-    const bool ybad = (uint32_t)y >= (uint64_t)p.V;
-    __shared__ float s_max[WPR];
-    __shared__ float s_sum[WPR][2];
+    const bool ybad = (uint32_t)y >= (uint64_t)V;
+    __shared__ float s_part[WPR][3];
     __shared__ float s_zy;
-    if (tid == 0) s_zy = ybad ? 0.0f : In<DTI>::scalar(irow, y);
+    if (tid == 0) s_zy = ybad ? 0.0f : In<DTI>::scalar(irow, y);   // read after the merge's barrier
 
-    float m = -INFINITY;
-    for (int64_t v = tid; v < p.V; v += TPR) m = fmaxf(m, In<DTI>::scalar(irow, v));
-    m = wave_max(m);
-    const int wave = tid >> 6;
-    if ((tid & 63) == 0) s_max[wave] = m;
-    __syncthreads();
-    m = s_max[0];
-    for (int i = 1; i < WPR; ++i) m = fmaxf(m, s_max[i]);
+    // the lane's shift: its first interior vector, else its head or tail element
+    float c = -INFINITY, s = 0.0f, w = 0.0f;
+    {
+        float m0 = -INFINITY;
+        bool any = true;
+        if (tid < g.nvi) {
+            sweep_max<DTI>(vin[tid], m0);
+        } else if (tid < g.hh) {
+            m0 = In<DTI>::scalar(irow, tid);
+        } else if (g.t0 + tid < V) {
+            m0 = In<DTI>::scalar(irow, g.t0 + tid);
+        } else {
+            any = false;
+        }
+        if (any) {
+            c = m0 * kLog2e;
+            if (!isfinite(c)) c = 0.0f;
+        }
+    }
+    if (tid < g.hh) elem_sums(In<DTI>::scalar(irow, tid), c, s, w);
+    for (int64_t i0 = tid; i0 < g.nvi; i0 += (int64_t)TPR * U) {
+        uint4 q[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = i0 + (int64_t)u * TPR;
+            if (i < g.nvi) q[u] = vin[i];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + (int64_t)u * TPR < g.nvi) sweep_sums<DTI>(q[u], c, s, w);
+    }
+    if (g.t0 + tid < V) elem_sums(In<DTI>::scalar(irow, g.t0 + tid), c, s, w);
+    block_merge<WPR>(c, s, w, tid, s_part);
     const float zy = s_zy;
 
-    const float c = m * kLog2e;
-    float s = 0.0f, w = 0.0f;
-    for (int64_t v = tid; v < p.V; v += TPR) {
-        const float tt = fmaf(In<DTI>::scalar(irow, v), kLog2e, -c);
-        const float ee = __builtin_amdgcn_exp2f(tt);
-        s += ee;
-        w = fmaf(ee, fmaxf(tt, kNegClampLog2), w);
+    if (!(isfinite(s) && isfinite(w))) {
+        // exact sweeps, streamed again (block-uniform branch)
+        float m = -INFINITY;
+        if (tid < g.hh) m = fmaxf(m, In<DTI>::scalar(irow, tid));
+        for (int64_t i = tid; i < g.nvi; i += TPR) sweep_max<DTI>(vin[i], m);
+        if (g.t0 + tid < V) m = fmaxf(m, In<DTI>::scalar(irow, g.t0 + tid));
+        m = block_max<WPR>(m, tid, s_part);
+        c = m * kLog2e;
+        s = 0.0f;
+        w = 0.0f;
+        if (tid < g.hh) elem_sums_clamped(In<DTI>::scalar(irow, tid), c, s, w);
+        for (int64_t i = tid; i < g.nvi; i += TPR) sweep_sums_clamped<DTI>(vin[i], c, s, w);
+        if (g.t0 + tid < V) elem_sums_clamped(In<DTI>::scalar(irow, g.t0 + tid), c, s, w);
+        block_sum2<WPR>(s, w, tid, s_part);
     }
-    s = wave_sum(s);
-    w = wave_sum(w);
-    if ((tid & 63) == 0) {
-        s_sum[wave][0] = s;
-        s_sum[wave][1] = w;
-    }
-    __syncthreads();
-    s = s_sum[0][0];
-    w = s_sum[0][1];
-    for (int i = 1; i < WPR; ++i) {
-        s += s_sum[i][0];
-        w += s_sum[i][1];
-    }
+
     const TokenResult r = token_tail<GRAD>(p, t, src, c, s, w, zy, ybad, tid == 0);
     if constexpr (GRAD) {
         if (!orow) return;
-        for (int64_t v = tid; v < p.V; v += TPR) {
-            const float tt = fmaf(In<DTI>::scalar(irow, v), kLog2e, -r.c2);
-            float d = r.eb == 0.0f ? r.coef * __builtin_amdgcn_exp2f(tt) : dz_with_bonus(tt, r.ea, r.eb);
-            if (v == y) d -= r.coef;
-            if (r.coef == 0.0f && r.eb == 0.0f) d = 0.0f;
-            Out<DTO>::scalar(orow, v, d);
+        if (r.coef == 0.0f && r.eb == 0.0f) {   // zero advantage or clipped, no bonus: the row is zero
+            zero_row_stream<DTO>(orow, V, tid);
+            return;
         }
+        const float c3 = r.c2 - log2f(fabsf(r.coef));
+        const bool neg = r.coef < 0.0f;
+        if (tid < g.hh) Out<DTO>::scalar(orow, tid, elem_dz(In<DTI>::scalar(irow, tid), r, c3, neg, tid == y));
+        // output vectors line up with input vectors when the output row shares the input row's phase
+        char* ovec = reinterpret_cast<char*>(orow) + g.hh * Out<DTO>::BYTES;
+        constexpr int OALIGN = VEC * Out<DTO>::BYTES >= 16 ? 16 : 8;
+        const bool oaligned = (reinterpret_cast<uintptr_t>(ovec) & (OALIGN - 1)) == 0;
+        for (int64_t i0 = tid; i0 < g.nvi; i0 += (int64_t)TPR * U) {
+            uint4 q[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + (int64_t)u * TPR;
+                if (i < g.nvi) q[u] = vin[i];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + (int64_t)u * TPR;
+                if (i >= g.nvi) continue;
+                const int64_t e0 = g.hh + i * VEC;   // first element of the vector
+                const bool own_y = !ybad && (int64_t)y >= e0 && (int64_t)y < e0 + VEC;
+                const int ey = own_y ? (int)(y - e0) : -1;
+                if (oaligned) {
+                    sweep_dz<DTI, DTO>(ovec, i, q[u], r, c3, neg, own_y, ey, zy);   // elements i*VEC.. of ovec
+                } else {
+                    float f[VEC];
+                    In<DTI>::unpack(q[u], f);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) Out<DTO>::scalar(orow, e0 + e, elem_dz(f[e], r, c3, neg, e == ey));
+                }
+            }
+        }
+        if (g.t0 + tid < V)
+            Out<DTO>::scalar(orow, g.t0 + tid, elem_dz(In<DTI>::scalar(irow, g.t0 + tid), r, c3, neg, g.t0 + tid == y));
     }
 }
 
@@ -1103,7 +1220,7 @@ hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st) {
         for (const RegCfg& c : kRegCfgs)
             if ((int64_t)c.tpr * (c.nv + c.nl) >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st);
     }
-    hipLaunchKernelGGL((tok_generic_kernel<DTI, DTO, GRAD>), dim3((unsigned)p.n_tok), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((tok_stream_kernel<DTI, DTO, GRAD>), dim3((unsigned)p.n_tok), dim3(kStreamTPR), 0, st, p);
     return hipGetLastError();
 }
 

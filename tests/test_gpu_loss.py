@@ -51,8 +51,12 @@ CASES = [
     (202048, torch.bfloat16, torch.bfloat16, 6),
     (229376, torch.bfloat16, torch.float32, 3),
     (100000, torch.float32, torch.float32, 4),
-    # one vector past that capacity: the generic kernel
+    # one vector past that capacity, a 256k vocabulary, rows off 16-byte
+    # alignment with an output of another phase: the streaming kernel
     (229384, torch.bfloat16, torch.bfloat16, 3),
+    (256000, torch.bfloat16, torch.bfloat16, 3),
+    (50257, torch.bfloat16, torch.float32, 9),
+    (1003, torch.float32, torch.bfloat16, 31),
 ]
 
 
@@ -69,10 +73,11 @@ def test_loss_matches_oracle(V, din, dout, n):
 
 
 @pytest.mark.parametrize("din,V,ld,n", [(torch.float32, 1024, 1040, 45), (torch.bfloat16, 1024, 1040, 45),
-                                        (torch.bfloat16, 202048, 202064, 4)])
+                                        (torch.bfloat16, 202048, 202064, 4), (torch.bfloat16, 50257, 50263, 9)])
 def test_padded_row_stride_and_inplace(din, V, ld, n):
     # logits rows padded to ld > V; then the same chunk updated in place
-    # (the last case holds part of each row in LDS)
+    # (202048: part of each row in LDS; 50257 with an odd stride: rows of
+    # every alignment phase through the streaming kernel)
     d = make_chunk(n, V, din, seed=3, ld=ld)
     scale = 0.01
     ref = run_oracle(d, scale)
@@ -135,7 +140,8 @@ def test_bad_targets_and_nan_logits_are_flagged_not_read():
 # row x elements per 16-byte vector on that kernel path)
 @pytest.mark.parametrize("V,dtype,first", [(151936, torch.bfloat16, 8192), (16384, torch.bfloat16, 2048),
                                            (4096, torch.bfloat16, 512), (1024, torch.float32, 256),
-                                           (202048, torch.bfloat16, 8192)])
+                                           (202048, torch.bfloat16, 8192), (256000, torch.bfloat16, 2056),
+                                           (50257, torch.bfloat16, 2056)])
 def test_special_rows(V, dtype, first):
     # Rows the one-sweep sums cannot take and that go through the exact
     # max-shifted sweeps instead: scattered -inf logits, the whole first
@@ -153,7 +159,7 @@ def test_special_rows(V, dtype, first):
     z[5] -= 30.0
     z[6, int(d["target"][6])] = float("-inf")
     for r in (1, 2):
-        if not np.isfinite(z[r, int(d["target"][r])]):
+        if not np.isfinite(float(z[r, int(d["target"][r])])):
             d["target"][r] = int(np.nonzero(np.isfinite(z[r].numpy()))[0][-1])
     zz = z.to(dtype)
     d["logits"].copy_(zz.to(DEV))
@@ -244,7 +250,8 @@ def test_chunked_equals_unchunked_bit_exact():
 
 @pytest.mark.parametrize("V,dtype,n", [(1024, torch.float32, 130), (151936, torch.bfloat16, 7),
                                        (1000, torch.bfloat16, 19), (4096, torch.bfloat16, 66),
-                                       (202048, torch.bfloat16, 5), (100000, torch.float32, 4)])
+                                       (202048, torch.bfloat16, 5), (100000, torch.float32, 4),
+                                       (50257, torch.bfloat16, 6), (256000, torch.bfloat16, 3)])
 def test_logprob_fwd_matches_oracle(V, dtype, n):
     d = make_chunk(n, V, dtype, seed=12 + V, with_old=False)
     logp, lse, ent = ops.logprob_fwd(d["logits"], d["g"]["target"], d["g"]["mask"])

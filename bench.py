@@ -76,6 +76,10 @@ def parse():
                          "tok_src")
     ap.add_argument("--cpu-pool-seconds", type=float, default=8.0,
                     help="wall seconds of the oracle over a process pool (0: skip)")
+    ap.add_argument("--vocab", type=int, default=0,
+                    help="padded workloads: vocabulary size in place of the workload's own (rows past the register "
+                         "file take the LDS-tail configuration, beyond 229 376 or off 16-byte alignment the "
+                         "streaming kernel)")
     ap.add_argument("--replicate", type=int, default=1,
                     help="tiny workload: the same row shape and distributions replicated R times as one batch in "
                          "one launch (the HBM reading of the launch-bound workload)")
@@ -149,6 +153,7 @@ class PaddedStep:
         self.ahead_timed = Timed(torch)
         b = self.b = padded_batch(wl, seed=seed, **(over or {}))
         n_rows, T, V = b["n_rows"], b["T"], b["V"]
+        self.V = V
         self.dt = torch.bfloat16 if b["dtype"] == "bf16" else torch.float32
         n_tok = n_rows * T
         self.logits = torch.empty((n_tok, V), dtype=self.dt, device="cuda")
@@ -355,7 +360,7 @@ class DynamicStep(PaddedStep):
         self.torch, self.ops, self.timed = torch, ops, timed
         b = self.b = dynamic_batch(seed=seed)
         L = b["lengths"].astype(np.int64)
-        V = b["V"]
+        V = self.V = b["V"]
         self.dt = torch.bfloat16
         plan = ops.plan_dynamic(L, b["budget"], b["proxy_div"])
         order = plan["order"]
@@ -613,6 +618,18 @@ def cpu_baseline_pool(step, budget_s, block=1024):
                       f"tasks over a {cores}-process pool, {wall:.1f} s wall" + (f" ({model})" if model else "")}
 
 
+def fused_kernel_label(V, dtype):
+    """Which fused-loss kernel a contiguous [tokens x V] chunk of this dtype takes
+    (the library's dispatch: 1024 threads x 19 register vectors, plus 9 LDS
+    vectors per lane past that, else the streaming kernel)."""
+    vec = 8 if dtype == "bf16" else 4
+    if V % vec:
+        return "tok_stream_kernel"
+    if V // vec <= 1024 * 19:
+        return "tok_reg_kernel"
+    return "tok_reg_kernel (LDS tail)" if V // vec <= 1024 * 28 else "tok_stream_kernel"
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -653,6 +670,11 @@ def main():
             sys.exit(2)
         from synth import WORKLOADS
         extra["over"] = dict(n_prompts=WORKLOADS["tiny"]["n_prompts"] * args.replicate, mini=0, micro=0)
+    if args.vocab:
+        if cls is not PaddedStep or args.vocab < 1:
+            print("--vocab applies to the padded workloads (qwen, long, tiny) and must be positive", file=sys.stderr)
+            sys.exit(2)
+        extra.setdefault("over", {})["V"] = args.vocab
     step = cls(wl, args.seed, torch, ops, timed, **extra)
     for _ in range(args.warmup):
         step()
@@ -680,7 +702,8 @@ def main():
                        + (f"; {args.epochs} inner epochs" if args.epochs != 1 else "")
                        + ("; rows reshuffled every epoch (seeded)" if args.shuffle else "")
                        + (f"; replicated x{args.replicate} as one batch, one launch" if args.replicate != 1 else "")
-                       + ("; device work replayed from a HIP graph" if args.graph else ""),
+                       + ("; device work replayed from a HIP graph" if args.graph else "")
+                       + (f"; vocabulary {args.vocab} in place of the workload's" if args.vocab else ""),
            "logits_dtype": step.logits_dtype,
            "valid_tokens": step.n_valid, "launches_per_step": launches // args.steps,
            "step_loss": res[0]["loss"] if res and res[0] else None}
@@ -703,11 +726,11 @@ def main():
         achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "tok_reg_kernel (fused loss fwd+bwd) + row/chunk stats, per chunk launch"
-                          + ("; graph replay time divided by the chunk launches" if args.graph else ""),
+                "kernel": fused_kernel_label(step.V, step.logits_dtype) + " (fused loss fwd+bwd) + row/chunk stats, "
+                          "per chunk launch" + ("; graph replay time divided by the chunk launches" if args.graph else ""),
                 "algorithmic_bytes_per_launch": int(units // launches), "avg_launch_ms": round(tot_ms / launches, 4)}
         roof["device_copy_GBs"] = round(step.copy_context(), 1)
-        if wl == "qwen" and not (args.terms or args.ahead or args.epochs != 1 or args.shuffle):
+        if wl == "qwen" and not (args.terms or args.ahead or args.epochs != 1 or args.shuffle or args.vocab):
             from grpo_token_level_amd.prof_summary import load_traffic
             rec = load_traffic(os.path.join(ROOT, "profiles", "fused_loss_qwen_pmc.txt"))
             if rec is not None:

@@ -172,12 +172,12 @@ class OldLogprobCache:
 
     def record(self, logits, target, mask):
         """Ahead pass of one chunk into the next record; returns its view."""
-        ld = _rows2d(logits, "logits")
         n, V = logits.shape
+        ld = _matrix(logits, "logits", n, V)
         slot = ctypes.c_void_p()
         C.check(C.lib().grpo_old_cache_record(_stream(), ctypes.byref(self.c), _dtype_code(logits),
-                                              _dev(logits, "logits"), ld, n, V, _dev(target, "target"),
-                                              _dev(mask, "mask"), ctypes.byref(slot)))
+                                              logits.data_ptr(), ld, n, V, _need(target, "target", "int32", n),
+                                              _need(mask, "mask", "byte", n), ctypes.byref(slot)))
         return self._view(slot.value or 0, n)
 
     def rewind(self):
@@ -208,8 +208,10 @@ def probe_compare(recorded, rescored, mask, bound=C.PROBE_STRICT_BOUND, out=None
     torch = _torch()
     if out is None:
         out = torch.empty(PROBE_STATS_BYTES, dtype=torch.uint8, device=recorded.device)
-    C.check(C.lib().grpo_probe_compare(_stream(), _dev(recorded, "recorded"), _dev(rescored, "rescored"),
-                                       _dev(mask, "mask"), mask.numel(), bound, _dev(out, "out")))
+    n = mask.numel()
+    C.check(C.lib().grpo_probe_compare(_stream(), _need(recorded, "recorded", "float32", n),
+                                       _need(rescored, "rescored", "float32", n), _need(mask, "mask", "byte", n),
+                                       n, bound, _need(out, "out", "byte", PROBE_STATS_BYTES)))
     return out
 
 
@@ -251,14 +253,42 @@ def _torch():
     return torch
 
 
-def _dev(t, name):
+def _need(t, name, dtype, n, optional=False):
+    """Device address of ``t``: a contiguous GPU tensor of element type
+    ``dtype`` ("int32", "int64", "float32", "bfloat16", or "byte" for uint8 or
+    bool) holding at least ``n`` elements; None for an absent optional one.
+    libgrpo sees only addresses, so every length it will read or write is
+    checked here, before the call."""
     if t is None:
-        return None
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (libgrpo has no CPU path)")
-    if not t.is_contiguous() and t.dim() == 1:
+    kind = str(t.dtype).removeprefix("torch.")
+    if kind not in (("uint8", "bool") if dtype == "byte" else (dtype,)):
+        raise ValueError(f"{name} must hold {dtype} elements, not {kind}")
+    if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements; the call uses {n}")
+    return t.data_ptr()
+
+
+def _matrix(t, name, rows, cols, dtypes=("bfloat16", "float32"), dense=False):
+    """Row stride of a GPU matrix of at least ``rows`` rows and exactly
+    ``cols`` columns with unit stride along a row (``dense``: no row padding)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libgrpo has no CPU path)")
+    kind = str(t.dtype).removeprefix("torch.")
+    if kind not in dtypes:
+        raise ValueError(f"{name} must hold {' or '.join(dtypes)} elements, not {kind}")
+    ld = _rows2d(t, name)
+    if t.shape[0] < rows or t.shape[1] != cols:
+        raise ValueError(f"{name} is {tuple(t.shape)}; the call needs at least {rows} rows of {cols}")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ld
 
 
 def _stream():
@@ -307,7 +337,8 @@ def count_valid(mask, out=None):
     torch = _torch()
     if out is None:
         out = torch.empty(1, dtype=torch.int64, device=mask.device)
-    C.check(C.lib().grpo_count_valid(_stream(), _dev(mask, "mask"), mask.numel(), _dev(out, "out")))
+    C.check(C.lib().grpo_count_valid(_stream(), _need(mask, "mask", "byte", 0), mask.numel(),
+                                     _need(out, "out", "int64", 1)))
     return out
 
 
@@ -316,8 +347,8 @@ def count_rows(mask, row_off, out=None):
     torch = _torch()
     if out is None:
         out = torch.empty(1, dtype=torch.int64, device=mask.device)
-    C.check(C.lib().grpo_count_rows(_stream(), _dev(mask, "mask"), _dev(row_off, "row_off"), row_off.numel() - 1,
-                                    mask.numel(), _dev(out, "out")))
+    C.check(C.lib().grpo_count_rows(_stream(), _need(mask, "mask", "byte", 0), _need(row_off, "row_off", "int64", 1),
+                                    row_off.numel() - 1, mask.numel(), _need(out, "out", "int64", 1)))
     return out
 
 
@@ -328,8 +359,9 @@ def row_weights(mask, row_off, mode, n_seq, out=None):
     n_rows = row_off.numel() - 1
     if out is None:
         out = torch.empty(max(n_rows, 1), dtype=torch.float32, device=mask.device)
-    C.check(C.lib().grpo_row_weights(_stream(), _dev(mask, "mask"), _dev(row_off, "row_off"), n_rows, mask.numel(),
-                                     mode, _dev(n_seq, "n_seq"), _dev(out, "w_row")))
+    C.check(C.lib().grpo_row_weights(_stream(), _need(mask, "mask", "byte", 0), _need(row_off, "row_off", "int64", 1),
+                                     n_rows, mask.numel(), mode, _need(n_seq, "n_seq", "int64", 1),
+                                     _need(out, "w_row", "float32", n_rows)))
     return out
 
 
@@ -340,9 +372,10 @@ def chunk_tok_src(src_row_off, rows, dst_row_off, out=None):
     n_tok = int(dst_row_off[-1].item()) if out is None else out.numel()
     if out is None:
         out = torch.empty(max(n_tok, 1), dtype=torch.int64, device=rows.device)
-    C.check(C.lib().grpo_chunk_tok_src(_stream(), _dev(src_row_off, "src_row_off"), src_row_off.numel() - 1,
-                                       _dev(rows, "rows"), rows.numel(), _dev(dst_row_off, "dst_row_off"), n_tok,
-                                       _dev(out, "tok_src")))
+    C.check(C.lib().grpo_chunk_tok_src(_stream(), _need(src_row_off, "src_row_off", "int64", 1),
+                                       src_row_off.numel() - 1, _need(rows, "rows", "int64", 0), rows.numel(),
+                                       _need(dst_row_off, "dst_row_off", "int64", rows.numel() + 1), n_tok,
+                                       _need(out, "tok_src", "int64", n_tok)))
     return out[:n_tok]
 
 
@@ -351,8 +384,12 @@ def gather(src, idx, out=None):
     torch = _torch()
     if out is None:
         out = torch.empty(idx.numel(), dtype=src.dtype, device=src.device)
-    C.check(C.lib().grpo_gather(_stream(), _dev(src, "src"), src.numel(), _dev(idx, "idx"), idx.numel(),
-                                src.element_size(), _dev(out, "dst")))
+    if out.dtype != src.dtype:
+        raise ValueError(f"out must hold {src.dtype} elements like src, not {out.dtype}")
+    kind = str(src.dtype).removeprefix("torch.")
+    C.check(C.lib().grpo_gather(_stream(), _need(src, "src", kind, 0), src.numel(),
+                                _need(idx, "idx", "int64", 0), idx.numel(), src.element_size(),
+                                _need(out, "dst", kind, idx.numel())))
     return out
 
 
@@ -360,22 +397,23 @@ def tok_row(row_off, n_tok, out=None):
     torch = _torch()
     if out is None:
         out = torch.empty(n_tok, dtype=torch.int32, device=row_off.device)
-    C.check(C.lib().grpo_tok_row(_stream(), _dev(row_off, "row_off"), row_off.numel() - 1, n_tok,
-                                 _dev(out, "tok_row")))
+    C.check(C.lib().grpo_tok_row(_stream(), _need(row_off, "row_off", "int64", 1), row_off.numel() - 1, n_tok,
+                                 _need(out, "tok_row", "int32", n_tok)))
     return out
 
 
 def logprob_fwd(logits, target, mask, want_lse=True, want_entropy=True):
     """Forward-only per-token (logp, lse, entropy) float32 tensors."""
     torch = _torch()
-    ld = _rows2d(logits, "logits")
     n, V = logits.shape
+    ld = _matrix(logits, "logits", n, V)
     logp = torch.empty(n, dtype=torch.float32, device=logits.device)
     lse = torch.empty_like(logp) if want_lse else None
     ent = torch.empty_like(logp) if want_entropy else None
-    C.check(C.lib().grpo_logprob_fwd(_stream(), _dtype_code(logits), _dev(logits, "logits"), ld, n, V,
-                                     _dev(target, "target"), _dev(mask, "mask"), _dev(logp, "logp"),
-                                     _dev(lse, "lse"), _dev(ent, "entropy")))
+    C.check(C.lib().grpo_logprob_fwd(_stream(), _dtype_code(logits), logits.data_ptr(), ld, n, V,
+                                     _need(target, "target", "int32", n), _need(mask, "mask", "byte", n),
+                                     logp.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                     ent.data_ptr() if ent is not None else None))
     return logp, lse, ent
 
 
@@ -390,14 +428,36 @@ def loss_workspace(n_tok, n_rows, device):
             "chunk_stats": torch.empty((1, STATS_BYTES), dtype=torch.uint8, device=device)}
 
 
-def _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws):
-    for name, t in (("row_weight", row_weight), ("ref_logp", ref_logp)):
-        if t is not None and not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor (libgrpo has no CPU path)")
-    a.row_weight = row_weight.data_ptr() if row_weight is not None else None
-    a.ref_logp = ref_logp.data_ptr() if ref_logp is not None else None
-    a.kl_tok = ws["kl_tok"].data_ptr() if ref_logp is not None else None
+def _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws, n_rows, n_tok, n_src):
+    a.row_weight = _need(row_weight, "row_weight", "float32", n_rows, optional=True)
+    a.ref_logp = _need(ref_logp, "ref_logp", "float32", n_src, optional=True)
+    a.kl_tok = _need(ws.get("kl_tok"), "kl_tok", "float32", n_tok) if ref_logp is not None else None
     a.ent_coef, a.kl_coef, a.kl_type = ent_coef, kl_coef, kl_type
+
+
+def _set_common(a, target, mask, old_logp, tok_row_, adv_row, row_off, denom, ws, n, n_src):
+    """The per-token inputs (``n_src`` tokens behind them), the chunk-local row
+    arrays and the per-token / per-row outputs shared by both loss calls."""
+    n_rows = row_off.numel() - 1
+    a.target = _need(target, "target", "int32", n_src)
+    a.mask = _need(mask, "mask", "byte", n_src)
+    a.old_logp = _need(old_logp, "old_logp", "float32", n_src)
+    a.tok_row = _need(tok_row_, "tok_row", "int32", n)
+    a.adv_row = _need(adv_row, "adv_row", "float32", n_rows)
+    a.row_off = _need(row_off, "row_off", "int64", 1)
+    a.n_rows = n_rows
+    a.denom = _need(denom, "denom", "int64", 1, optional=True)
+    for k in ("logp", "entropy", "loss_tok"):
+        setattr(a, k, _need(ws.get(k), k, "float32", n))
+    a.lse = _need(ws.get("lse"), "lse", "float32", n, optional=True)
+    a.tok_flags = _need(ws.get("tok_flags"), "tok_flags", "byte", n)
+    a.row_stats = _need(ws.get("row_stats"), "row_stats", "byte", n_rows * STATS_BYTES)
+    a.chunk_stats = _need(ws.get("chunk_stats"), "chunk_stats", "byte", STATS_BYTES)
+    if not n:                       # nothing per token is touched
+        a.target = a.mask = a.old_logp = a.tok_row = None
+        a.logp = a.lse = a.entropy = a.loss_tok = a.tok_flags = None
+    if not n_rows:
+        a.adv_row = None
 
 
 def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, scale=1.0, denom=None,
@@ -414,11 +474,18 @@ def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, 
     ``target``, ``mask``, ``old_logp``, ``ref_logp`` and ``dlogits`` are then
     the whole batch's, read and written at tok_src[t]; the chunk's token count
     is tok_src's length.
+    Every tensor's device, element type and length are checked against what
+    the call will touch before anything is launched (ValueError).
     Returns the workspace dict with ``dlogits`` added."""
     torch = _torch()
-    ld = _rows2d(logits, "logits")
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [tokens x V]")
     n_src, V = logits.shape
-    n = tok_src.numel() if tok_src is not None else n_src
+    ld = _matrix(logits, "logits", n_src, V)
+    n = n_src
+    if tok_src is not None:
+        _need(tok_src, "tok_src", "int64", 0)
+        n = tok_src.numel()
     n_rows = row_off.numel() - 1
     if ws is None:
         ws = loss_workspace(n, n_rows, logits.device)
@@ -434,31 +501,13 @@ def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, 
     a.out_dtype = _dtype_code(dl) if dl is not None else a.in_dtype
     a.logits = logits.data_ptr() if n else None
     a.ld, a.n_tok, a.V = ld, n, V
-    a.target = target.data_ptr() if n else None
-    a.mask = mask.data_ptr() if n else None
-    a.old_logp = old_logp.data_ptr() if n else None
-    a.tok_row = tok_row_.data_ptr() if n else None
-    a.adv_row = adv_row.data_ptr() if n_rows else None
-    a.row_off = row_off.data_ptr()
-    a.n_rows = n_rows
+    _set_common(a, target, mask, old_logp, tok_row_, adv_row, row_off, denom, ws, n, n_src)
     a.eps_low, a.eps_high, a.scale = eps_low, eps_high, scale
-    a.denom = denom.data_ptr() if denom is not None else None
     if dl is not None:
+        a.ld_out = _matrix(dl, "dlogits", n_src, V)
         a.dlogits = dl.data_ptr() if n else None
-        a.ld_out = _rows2d(dl, "dlogits")
-    for k in ("logp", "lse", "entropy", "loss_tok", "tok_flags", "row_stats", "chunk_stats"):
-        t = ws[k]
-        if t is not None and not t.is_cuda:
-            raise ValueError(f"{k} must be a GPU tensor")
-        setattr(a, k, t.data_ptr() if t is not None else None)
-    for name, t in (("logits", logits), ("target", target), ("mask", mask), ("old_logp", old_logp),
-                    ("tok_row", tok_row_), ("adv_row", adv_row), ("row_off", row_off)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor (libgrpo has no CPU path)")
-    _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws)
+    _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws, n_rows, n, n_src)
     if tok_src is not None:
-        if not tok_src.is_cuda or tok_src.dtype != torch.int64:
-            raise ValueError("tok_src must be an int64 GPU tensor")
         a.tok_src = tok_src.data_ptr() if n else None
         a.n_src = n_src
     C.check(C.lib().grpo_loss_fwd_bwd(_stream(), ctypes.byref(a)))
@@ -471,11 +520,12 @@ def transpose_bf16(x, out=None):
     torch = _torch()
     if x.dtype != torch.bfloat16:
         raise ValueError("transpose_bf16 takes a bf16 matrix")
-    ld = _rows2d(x, "x")
     rows, cols = x.shape
+    ld = _matrix(x, "x", rows, cols, ("bfloat16",))
     if out is None:
         out = torch.empty((cols, rows), dtype=torch.bfloat16, device=x.device)
-    C.check(C.lib().grpo_transpose_bf16(_stream(), _dev(x, "x"), rows, cols, ld, _dev(out, "out"), _rows2d(out, "out")))
+    ld_out = _matrix(out, "out", cols, rows, ("bfloat16",))
+    C.check(C.lib().grpo_transpose_bf16(_stream(), x.data_ptr(), rows, cols, ld, out.data_ptr(), ld_out))
     return out
 
 
@@ -489,8 +539,11 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
     """Fused LM-head GRPO loss over one chunk (grpo_lmhead_fwd_bwd).
 
     ``dW`` (fp32 [V x H]) is accumulated into; ``dh`` (fp32 [n_tok x H]) is
-    written.  Returns the per-token workspace dict with ``dh`` added."""
+    written.  Shapes, element types and lengths are checked before the call
+    (ValueError).  Returns the per-token workspace dict with ``dh`` added."""
     torch = _torch()
+    if h.dim() != 2 or W.dim() != 2:
+        raise ValueError("h and W must be 2-D")
     n, H = h.shape
     V = W.shape[0]
     n_rows = row_off.numel() - 1
@@ -500,33 +553,29 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
         dh = torch.empty((n, H), dtype=torch.float32, device=h.device)
     if workspace is None:
         workspace = torch.empty(max(lmhead_workspace_bytes(n, H, V), 1), dtype=torch.uint8, device=h.device)
-    for name, t in (("h", h), ("W", W), ("Wt", Wt), ("target", target), ("mask", mask), ("old_logp", old_logp),
-                    ("tok_row", tok_row_), ("adv_row", adv_row), ("row_off", row_off), ("dW", dW), ("dh", dh)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor (libgrpo has no CPU path)")
     a = C.LmheadArgs()
     a.struct_size = ctypes.sizeof(C.LmheadArgs)
+    a.ldh = _matrix(h, "h", n, H, ("bfloat16",))
     a.h = h.data_ptr() if n else None
-    a.ldh = _rows2d(h, "h")
+    _matrix(W, "W", V, H, ("bfloat16",), dense=True)
+    _matrix(Wt, "Wt", H, V, ("bfloat16",), dense=True)
+    if W.shape[0] != V or Wt.shape[0] != H:
+        raise ValueError(f"W must be [{V} x {H}] and Wt [{H} x {V}]")
     a.W, a.Wt = W.data_ptr(), Wt.data_ptr()
     a.n_tok, a.H, a.V = n, H, V
-    a.target = target.data_ptr() if n else None
-    a.mask = mask.data_ptr() if n else None
-    a.old_logp = old_logp.data_ptr() if n else None
-    a.tok_row = tok_row_.data_ptr() if n else None
-    a.adv_row = adv_row.data_ptr() if n_rows else None
-    a.row_off = row_off.data_ptr()
-    a.n_rows = n_rows
+    _set_common(a, target, mask, old_logp, tok_row_, adv_row, row_off, denom, ws, n, n)
     a.eps_low, a.eps_high, a.scale = eps_low, eps_high, scale
-    a.denom = denom.data_ptr() if denom is not None else None
+    _matrix(dh, "dh", n, H, ("float32",), dense=True)
     a.dh = dh.data_ptr() if n else None
+    _matrix(dW, "dW", V, H, ("float32",), dense=True)
+    if dW.shape[0] != V:
+        raise ValueError(f"dW must be [{V} x {H}]")
     a.dW = dW.data_ptr()
-    for k in ("logp", "lse", "entropy", "loss_tok", "tok_flags", "row_stats", "chunk_stats"):
-        t = ws[k]
-        setattr(a, k, t.data_ptr() if t is not None else None)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
     a.workspace = workspace.data_ptr()
-    a.workspace_bytes = workspace.numel()
-    _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws)
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws, n_rows, n, n)
     C.check(C.lib().grpo_lmhead_fwd_bwd(_stream(), ctypes.byref(a)))
     ws["dh"] = dh
     ws["workspace"] = workspace

@@ -126,6 +126,7 @@ struct GemmArgs {
     int64_t ldc;
     int64_t c_split;
     int beta;
+    const uint16_t* zero;   // device address of g_zero_page (set by launch_gemm)
 };
 
 __device__ __forceinline__ uint16_t to_bf16(float x) {
@@ -148,9 +149,12 @@ __device__ __forceinline__ int xcd_logical(int b, int nb) {
 }
 
 // LDS rows are 128 bytes (eight 16-byte k chunks); chunk c of row r is
-// stored at position c ^ swz(r), which spreads the 16-byte fragment reads of
-// consecutive rows over all banks.
-__device__ __forceinline__ int swz(int r) { return r & 7; }
+// stored at position c ^ swz(r).  A 16-byte LDS read serves 16 lanes per
+// pass over 64 banks (256 bytes), i.e. two 128-byte rows: the eight rows of
+// one parity among 16 consecutive rows must take eight different positions,
+// and so must any eight consecutive rows (measured: the plain r & 7 pattern
+// left two-way conflicts on every fragment read).
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
@@ -185,11 +189,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
     // and stores k chunk (l%8) ^ swz(row) at LDS position l%8.
     const int lr = lane >> 3, lp = lane & 7;
     int64_t aoff[4];   // element offset of this lane's A rows, -1 past the valid rows
+    int arow[4];
+    if (g.a_rows) {
+        // four independent loads (index clamped; M >= 1 past the exit above)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int ma = m0 + (wave * 4 + q) * 8 + lr;
-        aoff[q] = ma < M ? (int64_t)(g.a_rows ? g.a_rows[ma] : ma) * g.lda : -1;
+        for (int q = 0; q < 4; ++q) arow[q] = g.a_rows[min(m0 + (wave * 4 + q) * 8 + lr, M - 1)];
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) arow[q] = m0 + (wave * 4 + q) * 8 + lr;
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        aoff[q] = m0 + (wave * 4 + q) * 8 + lr < M ? (int64_t)arow[q] * g.lda : -1;
     auto issue = [&](int kt) {
         char* st = smem + (kt % NST) * STB;
         const int k0 = kbeg + kt * BK;
@@ -199,8 +210,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
             const int k = k0 + ((lp ^ swz(r)) << 3);
             const bool kin = k < kend;
             const int nb = n0 + r;
-            const uint16_t* ga = (aoff[q] >= 0 && kin) ? g.A + aoff[q] + k : g_zero_page;
-            const uint16_t* gb = (nb < g.N && kin) ? g.B + (int64_t)nb * g.ldb + k : g_zero_page;
+            const uint16_t* ga = (aoff[q] >= 0 && kin) ? g.A + aoff[q] + k : g.zero;
+            const uint16_t* gb = (nb < g.N && kin) ? g.B + (int64_t)nb * g.ldb + k : g.zero;
             __builtin_amdgcn_global_load_lds(ga, (lds_void*)(st + (wave * 4 + q) * 1024), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(gb, (lds_void*)(st + OPB + (wave * 4 + q) * 1024), 16, 0, 0);
         }
@@ -703,6 +714,10 @@ hipError_t launch_gemm(GemmArgs g, hipStream_t st) {
     }
     const long long nb = (long long)g.tiles_m * g.tiles_n * g.ksplit;
     if (nb == 0) return hipSuccess;
+    // the zero page's address as an argument: taken from the symbol in the
+    // loop, it was reloaded from memory after every barrier
+    hipError_t e = hipGetSymbolAddress((void**)&g.zero, HIP_SYMBOL(g_zero_page));
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gemm_nt_kernel<EPI>, dim3((unsigned)nb), dim3(NTHREADS), 0, st, g);
     return hipGetLastError();
 }

@@ -881,11 +881,12 @@ __global__ __launch_bounds__(kStreamTPR) void tok_stream_kernel(const TokParams 
 
 // ---------------------------------------------------------------- statistics
 
-// One 256-thread block per row: thread j takes the row's tokens j, j+256, ...,
-// then a fixed tree over the block.  A row's stats depend only on its own
-// tokens (never on where the row sits in the chunk).  The row's objective
-// share is s_r * (sum l - ent_coef * sum H + kl_coef * sum KL), s_r being the
-// factor its tokens' gradients carried.
+// One 256-thread block per row: thread j takes the row's tokens j, j+256, ...
+// (eight per pass, every load of a pass issued before its adds, the adds in
+// token order), then a fixed tree over the block.  A row's stats depend only
+// on its own tokens (never on where the row sits in the chunk).  The row's
+// objective share is s_r * (sum l - ent_coef * sum H + kl_coef * sum KL), s_r
+// being the factor its tokens' gradients carried.
 __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ loss_tok,
                                                         const float* __restrict__ entropy,
                                                         const float* __restrict__ kl_tok,
@@ -901,17 +902,36 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
     int64_t b = row_off[r], e = row_off[r + 1];
     b = b < 0 ? 0 : (b > n_tok ? n_tok : b);
     e = e < b ? b : (e > n_tok ? n_tok : e);
+    const float* kp = kl_tok ? kl_tok : loss_tok;   // read either way, added only with a KL term
     double ls = 0.0, es = 0.0, ks = 0.0;
     long long nv = 0, nc = 0, nn = 0;
-    for (int64_t t = b + i; t < e; t += 256) {
-        const uint8_t f = flags[t];
-        if (f & 1u) {
-            ls += (double)loss_tok[t];
-            es += (double)entropy[t];
-            if (kl_tok) ks += (double)kl_tok[t];
-            nv += 1;
-            nc += (f >> 1) & 1u;
-            nn += (f >> 2) & 1u;
+    constexpr int U = 8;
+    for (int64_t t0 = b + i; t0 < e; t0 += 256 * U) {
+        uint8_t f[U];
+        float l[U], h[U], k[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // past the row end the loads read token t0 (in bounds) and the
+            // flag is cleared, so no load waits behind a branch
+            const int64_t t = t0 + (int64_t)u * 256;
+            const bool in = t < e;
+            const int64_t tc = in ? t : t0;
+            const uint8_t fl = flags[tc];
+            f[u] = in ? fl : (uint8_t)0;
+            l[u] = loss_tok[tc];
+            h[u] = entropy[tc];
+            k[u] = kp[tc];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (f[u] & 1u) {
+                ls += (double)l[u];
+                es += (double)h[u];
+                if (kl_tok) ks += (double)k[u];
+                nv += 1;
+                nc += (f[u] >> 1) & 1u;
+                nn += (f[u] >> 2) & 1u;
+            }
         }
     }
     ls = wave_sum_d(ls);

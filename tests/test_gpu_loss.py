@@ -248,6 +248,39 @@ def test_chunked_equals_unchunked_bit_exact():
     assert torch.equal(torch.cat([p["row_stats"][:4] for p in parts]), whole["row_stats"][:n_rows])
 
 
+@pytest.mark.parametrize("n_rows", [1, 15, 16, 17, 40])
+def test_row_stats_independent_of_the_chunk(n_rows):
+    """A row's stats are the same bits whether the row is reduced alone or
+    inside a chunk of n_rows rows (ragged lengths, an empty row, a short last
+    row); the chunk's stats match the oracle."""
+    rng = np.random.default_rng(40 + n_rows)
+    lens = [int(x) for x in rng.integers(5, 40, n_rows)]
+    if n_rows > 2:
+        lens[1] = 0
+        lens[-1] = 3
+    n_tok = sum(lens)
+    d = make_chunk(n_tok, 1024, torch.float32, seed=50 + n_rows, n_rows=1)
+    row_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    d["row_off"] = row_off
+    d["tok_row"] = np.repeat(np.arange(n_rows, dtype=np.int32), lens)
+    d["adv_row"] = rng.normal(0, 1, n_rows).astype(np.float32)
+    for k in ("row_off", "tok_row", "adv_row"):
+        d["g"][k] = torch.from_numpy(d[k]).to(DEV)
+    scale = 1.0 / 97.0
+    whole = run_gpu(d, scale=scale)
+    ref = run_oracle(d, scale)
+    assert_tokens_match(whole, ref, d)
+    _check_stats(whole, ref, d)
+    g = d["g"]
+    for r in range(n_rows):
+        a, b = int(row_off[r]), int(row_off[r + 1])
+        one = ops.loss_fwd_bwd(d["logits"][a:b], g["target"][a:b], g["mask"][a:b], g["old"][a:b],
+                               torch.zeros(b - a, dtype=torch.int32, device=DEV), g["adv_row"][r:r + 1],
+                               torch.tensor([0, b - a], dtype=torch.int64, device=DEV), scale=scale)
+        assert torch.equal(one["row_stats"][0], whole["row_stats"][r]), r
+        assert torch.equal(one["loss_tok"], whole["loss_tok"][a:b]), r
+
+
 @pytest.mark.parametrize("V,dtype,n", [(1024, torch.float32, 130), (151936, torch.bfloat16, 7),
                                        (1000, torch.bfloat16, 19), (4096, torch.bfloat16, 66),
                                        (202048, torch.bfloat16, 5), (100000, torch.float32, 4),

@@ -68,8 +68,7 @@ constexpr int FM = WM / 32, FN = WN / 32;
 constexpr int ROWB = BK * 2;         // bytes of one tile row in one stage
 constexpr int OPB = BM * ROWB;       // bytes of one operand in one stage (32 KiB)
 constexpr int STB = 2 * OPB;         // bytes of one stage (64 KiB)
-constexpr int EPI_ROW = WN + 1;      // floats per row of a wave's epilogue buffer (row-wise reads)
-constexpr int EPI_ROW_Q = WN + 4;    // the same for 16-byte column-quad reads
+constexpr int EPI_ROW_Q = WN + 4;    // floats per row of a wave's epilogue buffer (16-byte reads)
 constexpr int EPIB = 8 * 32 * EPI_ROW_Q * 4;
 constexpr int SMEM = NST * STB > EPIB ? NST * STB : EPIB;
 constexpr int NXCD = 8;
@@ -190,13 +189,39 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
     const int lr = lane >> 3, lp = lane & 7;
     int64_t aoff[4];   // element offset of this lane's A rows, -1 past the valid rows
     int arow[4];
+    // the epilogue's per-row values are loaded here, so that their latency
+    // hides behind the main loop: STATS the target of this lane's result rows
+    // (row l%32 of each 32-row block), DZ the per-token factors of row tid
+    int ep_y[FM];
+    float ep_c2 = 0.0f, ep_cf = 0.0f, ep_ea = 0.0f, ep_eb = 0.0f;
+    int ep_yd = -1;
     if (g.a_rows) {
-        // four independent loads (index clamped; M >= 1 past the exit above)
+        // independent loads (index clamped; M >= 1 past the exit above), one wait
 #pragma unroll
         for (int q = 0; q < 4; ++q) arow[q] = g.a_rows[min(m0 + (wave * 4 + q) * 8 + lr, M - 1)];
     } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) arow[q] = m0 + (wave * 4 + q) * 8 + lr;
+    }
+    if constexpr (EPI == EPI_STATS) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + wm * WM + i * 32 + (lane & 31);
+            ep_y[i] = m < M ? g.target[g.a_rows ? g.a_rows[m] : m] : -1;
+        }
+    } else if constexpr (EPI == EPI_DZ) {
+        if (tid < BM) {
+            const int m = m0 + tid;
+            if (m < M) {
+                ep_c2 = g.c2[m];
+                ep_cf = g.coef[m];
+                if (g.bonus) {
+                    ep_ea = g.ea[m];
+                    ep_eb = g.eb[m];
+                }
+                ep_yd = g.target[g.a_rows ? g.a_rows[m] : m];
+            }
+        }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -317,13 +342,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
         int* s_y = reinterpret_cast<int*>(s_eb + BM);
         __syncthreads();   // the stage buffers are reused
         if (tid < BM) {
-            const int m = m0 + tid;
-            const bool in = m < M;
-            s_c2[tid] = in ? g.c2[m] : 0.0f;
-            s_cf[tid] = in ? g.coef[m] : 0.0f;
-            s_ea[tid] = (in && g.bonus) ? g.ea[m] : 0.0f;
-            s_eb[tid] = (in && g.bonus) ? g.eb[m] : 0.0f;
-            s_y[tid] = in ? g.target[g.a_rows ? g.a_rows[m] : m] : -1;
+            s_c2[tid] = ep_c2;
+            s_cf[tid] = ep_cf;
+            s_ea[tid] = ep_ea;
+            s_eb[tid] = ep_eb;
+            s_y[tid] = ep_yd;
         }
         __syncthreads();
 #pragma unroll
@@ -366,9 +389,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
                 }
             }
     } else {
-        // per wave, the 64x128 tile goes through LDS 32 rows at a time so that
-        // two lanes own one row (64 columns each)
-        float* T = reinterpret_cast<float*>(smem) + wave * 32 * EPI_ROW;
+        // per wave, the 64x128 tile goes through LDS 32 rows at a time; lane l
+        // owns row l%32, columns (l/32)*64 .. +64 (rows 528 bytes apart, so the
+        // 16 lanes of one 16-byte read pass hit 16 different bank groups)
+        float* T = reinterpret_cast<float*>(smem) + wave * 32 * EPI_ROW_Q;
         __syncthreads();   // the stage buffers are reused
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -376,26 +400,49 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    T[((r >> 2) * 8 + rq + (r & 3)) * EPI_ROW + j * 32 + fr] = acc[i][j][r];
+                    T[((r >> 2) * 8 + rq + (r & 3)) * EPI_ROW_Q + j * 32 + fr] = acc[i][j][r];
             __syncthreads();
-            const int rr = lane >> 1, half = lane & 1;
+            const int rr = lane & 31, half = lane >> 5;
             const int m = m0 + wm * WM + i * 32 + rr;
             const int nb = n0 + wn * WN + half * 64;
             const int ncols = g.N - nb < 64 ? g.N - nb : 64;
             if (m < M && ncols > 0) {
-                const float* row = T + rr * EPI_ROW + half * 64;
-                float mx = -INFINITY;
-                for (int c = 0; c < ncols; ++c) mx = fmaxf(mx, row[c]);
-                const float cm = mx * kLog2e;
-                float se = 0.0f, sw = 0.0f;
-                for (int c = 0; c < ncols; ++c) {
-                    const float t = fmaf(row[c], kLog2e, -cm);
-                    const float e = __builtin_amdgcn_exp2f(t);
-                    se += e;
-                    sw = fmaf(e, t, sw);
+                const float* row = T + rr * EPI_ROW_Q + half * 64;
+                float mx = -INFINITY, se = 0.0f, sw = 0.0f;
+                if (ncols == 64) {
+                    // the whole slice in registers: 16 reads of 16 bytes, then
+                    // the max and the sums in column order
+                    float v[64];
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) {
+                        const float4 q = *reinterpret_cast<const float4*>(row + c * 4);
+                        v[4 * c] = q.x;
+                        v[4 * c + 1] = q.y;
+                        v[4 * c + 2] = q.z;
+                        v[4 * c + 3] = q.w;
+                    }
+#pragma unroll
+                    for (int c = 0; c < 64; ++c) mx = fmaxf(mx, v[c]);
+                    const float cm = mx * kLog2e;
+#pragma unroll
+                    for (int c = 0; c < 64; ++c) {
+                        const float t = fmaf(v[c], kLog2e, -cm);
+                        const float e = __builtin_amdgcn_exp2f(t);
+                        se += e;
+                        sw = fmaf(e, t, sw);
+                    }
+                } else {
+                    for (int c = 0; c < ncols; ++c) mx = fmaxf(mx, row[c]);
+                    const float cm = mx * kLog2e;
+                    for (int c = 0; c < ncols; ++c) {
+                        const float t = fmaf(row[c], kLog2e, -cm);
+                        const float e = __builtin_amdgcn_exp2f(t);
+                        se += e;
+                        sw = fmaf(e, t, sw);
+                    }
                 }
                 g.part[(int64_t)m * g.n_parts + nb / 64] = make_float4(mx, se, sw, 0.0f);
-                const int y = g.target[g.a_rows ? g.a_rows[m] : m];
+                const int y = ep_y[i];
                 if (y >= nb && y < nb + ncols) g.zy[m] = row[y - nb];
             }
             __syncthreads();

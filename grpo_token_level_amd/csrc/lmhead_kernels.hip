@@ -71,6 +71,11 @@ constexpr int STB = 2 * OPB;         // bytes of one stage (64 KiB)
 constexpr int EPI_ROW_Q = WN + 4;    // floats per row of a wave's epilogue buffer (16-byte reads)
 constexpr int EPIB = 8 * 32 * EPI_ROW_Q * 4;
 constexpr int SMEM = NST * STB > EPIB ? NST * STB : EPIB;
+constexpr int DZT_ROWB = 64 * 2 + 8;  // bytes per column of a wave's dz^T staging (64 tokens + 8: conflict-free writes)
+constexpr int DZT_OFF = 8192;         // the staging follows the per-token factors
+constexpr int DZR_ROWB = WN * 2 + 16; // bytes per token row of a wave's dz staging (128 columns + 16)
+constexpr int DZ_WAVEB = 64 * DZR_ROWB > WN * DZT_ROWB ? 64 * DZR_ROWB : WN * DZT_ROWB;   // one buffer, used twice
+constexpr int SMEM_DZ = DZT_OFF + 8 * DZ_WAVEB > SMEM ? DZT_OFF + 8 * DZ_WAVEB : SMEM;
 constexpr int NXCD = 8;
 constexpr int kVocabChunkMax = 65536;   // pass-2 vocabulary chunk bound (sizes the dz workspace)
 constexpr int kVocabChunkMin = 16384;
@@ -162,7 +167,7 @@ __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 template <int EPI>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) {
-    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+    __shared__ __attribute__((aligned(1024))) char smem[EPI == EPI_DZ ? SMEM_DZ : SMEM];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
@@ -340,6 +345,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
         float* s_ea = s_cf + BM;
         float* s_eb = s_ea + BM;
         int* s_y = reinterpret_cast<int*>(s_eb + BM);
+        char* tcol = smem + DZT_OFF + wave * DZ_WAVEB;   // [column][token] bf16 of this wave, then [token][column]
+        uint32_t dpk[FM][FN][4][2] = {};   // the wave's dz values, bf16 pairs (tokens 4q+rq+{0,1}, {2,3})
         __syncthreads();   // the stage buffers are reused
         if (tid < BM) {
             s_c2[tid] = ep_c2;
@@ -373,21 +380,61 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
                         d[u] = x;
                     }
                     const int m = m0 + mb;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (m + u < M) g.dz[(int64_t)(m + u) * g.ld_dz + nl] = to_bf16(d[u]);
-                    if (m + 3 < m_out) {
-                        uint2 pk;
-                        pk.x = pack2(d[0], d[1]);
-                        pk.y = pack2(d[2], d[3]);
-                        *reinterpret_cast<uint2*>(g.dzT + (int64_t)nl * g.ld_dzT + m) = pk;
-                    } else {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            if (m + u < m_out) g.dzT[(int64_t)nl * g.ld_dzT + m + u] = to_bf16(d[u]);
-                    }
+                    // dz and dz^T go out through LDS: column j*32+fr of the
+                    // wave, tokens mb-wm*WM .. +4 (8 bytes)
+                    uint2 pk;
+                    pk.x = pack2(d[0], d[1]);
+                    pk.y = pack2(d[2], d[3]);
+                    dpk[i][j][q][0] = pk.x;
+                    dpk[i][j][q][1] = pk.y;
+                    *reinterpret_cast<uint2*>(tcol + (j * 32 + fr) * DZT_ROWB + (mb - wm * WM) * 2) = pk;
                 }
             }
+        // each dz^T row segment of the wave (its 64 tokens, 128 bytes) by 8
+        // lanes with 16-byte stores; the wave reads only what it wrote
+        const int mg = m0 + wm * WM;
+#pragma unroll
+        for (int it = 0; it < WN / 8; ++it) {
+            const int nloc = it * 8 + (lane >> 3), c = lane & 7;
+            const int nl = n0 + wn * WN + nloc;
+            const int m = mg + c * 8;
+            if (nl < g.N && m < m_out) {
+                const char* src = tcol + nloc * DZT_ROWB + c * 16;
+                const uint2 lo = *reinterpret_cast<const uint2*>(src);
+                const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+                *reinterpret_cast<uint4*>(g.dzT + (int64_t)nl * g.ld_dzT + m) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+        }
+        // then the same buffer as [token][column]: 2-byte writes of the kept
+        // values (columns past N were never computed: dpk holds zeros there,
+        // and those columns are not stored), then each token row segment of
+        // the wave (128 columns, 256 bytes) by 16 lanes with 16-byte stores
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int ml = i * 32 + q * 8 + rq;
+                    char* dst = tcol + ml * DZR_ROWB + (j * 32 + fr) * 2;
+                    const uint32_t a = dpk[i][j][q][0], b = dpk[i][j][q][1];
+                    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(a & 0xffffu);
+                    *reinterpret_cast<uint16_t*>(dst + DZR_ROWB) = (uint16_t)(a >> 16);
+                    *reinterpret_cast<uint16_t*>(dst + 2 * DZR_ROWB) = (uint16_t)(b & 0xffffu);
+                    *reinterpret_cast<uint16_t*>(dst + 3 * DZR_ROWB) = (uint16_t)(b >> 16);
+                }
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int ml = it * 4 + (lane >> 4), c = lane & 15;
+            const int m = mg + ml;
+            const int nl = n0 + wn * WN + c * 8;
+            if (m < M && nl < g.N) {
+                const char* src = tcol + ml * DZR_ROWB + c * 16;
+                const uint2 lo = *reinterpret_cast<const uint2*>(src);
+                const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+                *reinterpret_cast<uint4*>(g.dz + (int64_t)m * g.ld_dz + nl) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+        }
     } else {
         // per wave, the 64x128 tile goes through LDS 32 rows at a time; lane l
         // owns row l%32, columns (l/32)*64 .. +64 (rows 528 bytes apart, so the

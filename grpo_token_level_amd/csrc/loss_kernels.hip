@@ -695,7 +695,7 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
 // output row shares the input row's alignment, single elements otherwise.
 
 constexpr int kStreamTPR = 256;
-constexpr int kStreamUnroll = 4;   // vectors in flight per lane
+constexpr int kStreamUnroll = 4;   // vectors in flight per lane (gradient path; the forward-only path keeps 8)
 
 // Elements before the row's first 16-byte boundary (at most V), the whole
 // 16-byte vectors after them, and the first element after those vectors.
@@ -754,7 +754,7 @@ __device__ __forceinline__ float elem_dz(float z, const TokenResult& r, float c3
 
 template <int DTI, int DTO, bool GRAD>
 __global__ __launch_bounds__(kStreamTPR) void tok_stream_kernel(const TokParams p) {
-    constexpr int TPR = kStreamTPR, WPR = TPR / 64, U = kStreamUnroll;
+    constexpr int TPR = kStreamTPR, WPR = TPR / 64, U = GRAD ? kStreamUnroll : 2 * kStreamUnroll;
     constexpr int VEC = In<DTI>::VEC;
     const int64_t t = blockIdx.x;
     if (t >= p.n_tok) return;
@@ -806,11 +806,19 @@ __global__ __launch_bounds__(kStreamTPR) void tok_stream_kernel(const TokParams 
     }
     if (tid < g.hh) elem_sums(In<DTI>::scalar(irow, tid), c, s, w);
     for (int64_t i0 = tid; i0 < g.nvi; i0 += (int64_t)TPR * U) {
+        // every load of the pass issued before the sums: past the row's end
+        // a lane reads vector i0 again (in bounds) and skips it.  Without a
+        // gradient sweep the row is read once, so the loads carry the
+        // non-temporal hint (measured: 6.5-7.0 TB/s read against 5.6-5.9 with
+        // the row held in registers); with one, the second read may still
+        // find the row in the last-level cache.
         uint4 q[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = i0 + (int64_t)u * TPR;
-            if (i < g.nvi) q[u] = vin[i];
+            const int64_t ic = i < g.nvi ? i : i0;
+            if constexpr (GRAD) q[u] = vin[ic];
+            else q[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vin) + ic));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -1235,7 +1243,11 @@ hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st) {
 template <int DTI, int DTO, bool GRAD>
 hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st) {
     if (p.n_tok == 0) return hipSuccess;
-    if (vec_ok) {
+    // Forward only, rows past 1024 vectors stream: the row need not stay on
+    // chip, and many 256-thread blocks per CU keep more reads in flight than
+    // one row-resident block (V = 16 384 .. 202 048 bf16: 6.2-7.0 TB/s against
+    // 4.4-5.9 for the register kernel; at 8192 the register kernel is ahead).
+    if (vec_ok && (GRAD || p.V / In<DTI>::VEC <= 1024)) {
         const int64_t nvec = p.V / In<DTI>::VEC;
         for (const RegCfg& c : kRegCfgs)
             if ((int64_t)c.tpr * (c.nv + c.nl) >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st);

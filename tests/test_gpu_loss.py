@@ -12,6 +12,16 @@ from grpo_token_level_amd import ops
 pytestmark = pytest.mark.gpu
 
 
+def assert_same_up_to_sum_order(a, b):
+    """The forward-only pass streams rows past 1024 vectors in another lane
+    partition than the fused kernel, so their outputs agree to rounding (a
+    few float32 ulps), with the same non-finite entries."""
+    a, b = to_f64(a), to_f64(b)
+    fa, fb = np.isfinite(a), np.isfinite(b)
+    assert np.array_equal(fa, fb) and np.array_equal(a[~fa], b[~fb])
+    assert np.all(np.abs(a[fa] - b[fb]) <= 2e-6 * np.maximum(1.0, np.abs(b[fb])))
+
+
 def _stats(ws):
     return ops.stats_to_dicts(ws["chunk_stats"])[0], ops.stats_to_dicts(ws["row_stats"])
 
@@ -174,7 +184,8 @@ def test_special_rows(V, dtype, first):
     assert ref["nonfinite"].tolist() == [False] * 6 + [True, False]
     assert_tokens_match(ws, ref, d)
     f_logp, f_lse, f_ent = ops.logprob_fwd(d["logits"], d["g"]["target"], d["g"]["mask"])
-    assert torch.equal(f_logp, ws["logp"]) and torch.equal(f_ent, ws["entropy"])
+    assert_same_up_to_sum_order(f_logp, ws["logp"])
+    assert_same_up_to_sum_order(f_ent, ws["entropy"])
     fwd = oracle.logprob_fwd(d["z64"], d["target"], d["mask"])
     fin = np.isfinite(fwd["logp"])
     assert np.max(np.abs(to_f64(f_logp)[fin] - fwd["logp"][fin])) <= (1e-5 if dtype == torch.float32 else 2e-3)
@@ -293,9 +304,10 @@ def test_logprob_fwd_matches_oracle(V, dtype, n):
     assert np.max(np.abs(to_f64(logp) - ref["logp"])) <= tol
     assert np.max(np.abs(to_f64(lse) - ref["lse"])) <= tol
     assert np.max(np.abs(to_f64(ent) - ref["entropy"]) - 1e-5 * np.abs(ref["entropy"])) <= 1e-4
-    # the loss kernel's forward outputs are the same numbers
+    # the loss kernel's forward outputs are the same numbers up to the order of the sums
     ws = run_gpu(make_chunk(n, V, dtype, seed=12 + V, with_old=False), scale=1.0, dlogits=None)
-    assert torch.equal(ws["logp"], logp) and torch.equal(ws["lse"], lse)
+    assert_same_up_to_sum_order(ws["logp"], logp)
+    assert_same_up_to_sum_order(ws["lse"], lse)
 
 
 def test_count_valid_and_tok_row():

@@ -10,21 +10,24 @@
 // the math").
 //
 // Design (HBM-bound streaming, no MFMA: there is no contraction here).
-// One token row of V logits is read from HBM exactly once into registers:
+// The fused loss reads a token's row of V logits from HBM once and keeps it
+// on chip until its gradient row is written (tok_reg_kernel):
 //   * large V (e.g. 151936 bf16 = 297 KiB): one 1024-thread workgroup per
-//     token; each lane holds NV 16-byte vectors (NV = 19 -> 76 VGPRs).
+//     token; each lane holds NV 16-byte vectors (NV = 19 -> 76 VGPRs), and
+//     past that 9 more per lane in LDS (rows up to 229376 bf16).
 //     Reductions: wave64 butterfly, then the 16 wave partials through LDS in a
 //     fixed order.
 //   * small V (<= 4096 bf16 / 2048 fp32): one wave64 per token, four tokens
 //     per 256-thread workgroup, no LDS and no barrier at all.
-// Three sweeps over the registers: max; sum of 2^t and sum of 2^t * t with
-// t = z*log2(e) - max*log2(e) (one FMA + v_exp_f32 per element); then the write
-// of dz = coef * 2^(z*log2(e) - lse*log2(e)) minus coef at the target.  The
-// logits are never re-read, dlogits are written once with 16-byte stores, so
-// the kernel moves V*(in + out) bytes per valid token and V*out per masked one.
-// Rows whose stride or base is not 16-byte aligned, or whose V exceeds what the
-// register file holds, take a generic kernel that streams the row three times
-// from memory (correct for any layout, slower).
+// One sweep over the row forms sum 2^t and sum 2^t * t with a per-lane shift
+// (t = z*log2(e) - c) and merges the lanes exactly; a second writes
+// dz = coef * 2^(z*log2(e) - lse*log2(e)) minus coef at the target.  So the
+// kernel moves V*(in + out) bytes per valid token and V*out per masked one.
+// Rows off 16-byte alignment, or past what registers and LDS hold, take
+// tok_stream_kernel: 256 threads per token, the row streamed once for the sums
+// and once more for dz.  The forward-only pass keeps no row on chip: rows past
+// 1024 vectors take tok_stream_kernel's single sum sweep, shorter ones
+// tok_reg_kernel.
 //
 // Every reduction has a fixed order, nothing uses floating-point atomics, so
 // results are bit-for-bit reproducible and a token's outputs depend only on

@@ -310,6 +310,53 @@ def test_logprob_fwd_matches_oracle(V, dtype, n):
     assert_same_up_to_sum_order(ws["lse"], lse)
 
 
+def _random_shapes(count=24, seed=2024):
+    """Seeded shapes across every dispatch path: V in [1, 262 144], half
+    log-uniform up to 4096 and half uniform above (the wave, 256- and
+    1024-thread register paths, the LDS tail, the streaming kernel), both
+    input dtypes, padded row strides, in-place and mixed-precision outputs,
+    ragged token counts."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(count):
+        if k % 2:
+            V = int(rng.integers(4097, 262145))
+        else:
+            V = max(1, int(np.exp(rng.uniform(0.0, np.log(4096.0)))))
+        din = torch.float32 if rng.random() < 0.4 else torch.bfloat16
+        n = int(rng.integers(1, 9)) if V > 60000 else int(rng.integers(1, 40))
+        pad = int(rng.integers(0, 14)) if rng.random() < 0.5 else 0
+        mode = ("inplace", "new_other", "new_same")[int(rng.integers(0, 3))]
+        out.append((k, V, din, n, pad, mode))
+    return out
+
+
+@pytest.mark.parametrize("k,V,din,n,pad,mode", _random_shapes())
+def test_random_shapes_match_oracle(k, V, din, n, pad, mode):
+    d = make_chunk(n, V, din, seed=300 + k, ld=V + pad)
+    dout = din
+    if mode == "new_other":
+        dout = torch.float32 if din == torch.bfloat16 else torch.bfloat16
+    ref = run_oracle(d, 1.0 / 50.0)
+    if mode == "inplace":
+        ws = ops.loss_fwd_bwd(d["logits"], d["g"]["target"], d["g"]["mask"],
+                              d["g"]["old"], d["g"]["tok_row"], d["g"]["adv_row"], d["g"]["row_off"],
+                              scale=1.0 / 50.0, dlogits="inplace")
+    else:
+        ws = run_gpu(d, scale=1.0 / 50.0, out_dtype=dout)
+    assert_tokens_match(ws, ref, d)
+    _check_stats(ws, ref, d)
+    if mode != "inplace":
+        # the forward-only pass on the same (untouched) logits
+        logp, lse, ent = ops.logprob_fwd(d["logits"], d["g"]["target"], d["g"]["mask"])
+        fwd = oracle.logprob_fwd(d["z64"], d["target"], d["mask"])
+        fin = np.isfinite(fwd["logp"])
+        tol = 1e-5 if din == torch.float32 else 2e-3
+        assert np.max(np.abs(to_f64(logp)[fin] - fwd["logp"][fin]), initial=0.0) <= tol
+        assert np.max(np.abs(to_f64(lse) - fwd["lse"]), initial=0.0) <= tol
+        assert_same_up_to_sum_order(logp, ws["logp"])
+
+
 def test_count_valid_and_tok_row():
     rng = np.random.default_rng(13)
     for n in (0, 1, 15, 16, 17, 1000, 131072 + 5):

@@ -22,6 +22,7 @@ a bounded sample of the same workload.
 """
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -676,6 +677,14 @@ def main():
             sys.exit(2)
         extra.setdefault("over", {})["V"] = args.vocab
     step = cls(wl, args.seed, torch, ops, timed, **extra)
+    # A full garbage collection walks every tracked Python object, most of them
+    # torch's own (~170 k): tens of milliseconds on one host thread.  Inside the
+    # timed steps such a pause can fall between a launch's start event and the
+    # launch itself while the GPU has drained its queue, and the idle time would
+    # be booked to that launch.  The set-up's objects are collected once and
+    # frozen out of later collections; the steps' own garbage is still collected.
+    gc.collect()
+    gc.freeze()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -297,10 +297,13 @@ __device__ __forceinline__ void block_sum2(float& s, float& w, int tid, float (*
 // floats of one sweep cannot then be kept alive into the next sweep (that
 // would double the row's register footprint and spill); each sweep re-derives
 // them from the packed registers with one ALU op per element.
+__device__ __forceinline__ void opaque_vec(uint4& x) {
+    asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+}
 template <int NV>
 __device__ __forceinline__ void opaque_regs(uint4 (&x)[NV]) {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) asm volatile("" : "+v"(x[k].x), "+v"(x[k].y), "+v"(x[k].z), "+v"(x[k].w));
+    for (int k = 0; k < NV; ++k) opaque_vec(x[k]);
 }
 
 // ---------------------------------------------------------------- parameters
@@ -610,10 +613,15 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         c = m0 * kLog2e;
         if (!isfinite(c)) c = 0.0f;
     }
-    opaque_regs(x);
+    // Each vector is fenced on its own just before its sums: a fence over the
+    // whole array would make every wave wait for all of its loads before the
+    // first sum, while per vector the sweep follows the loads as they land.
 #pragma unroll
     for (int k = 0; k < NV; ++k)
-        if (k * TPR + tid < nvec) sweep_sums<DTI>(x[k], c, s, w);
+        if (k * TPR + tid < nvec) {
+            opaque_vec(x[k]);
+            sweep_sums<DTI>(x[k], c, s, w);
+        }
     if constexpr (NL > 0) {
         // this wave's direct-to-LDS loads have landed (each lane reads only
         // the 16 bytes its own wave's load wrote)

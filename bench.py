@@ -622,13 +622,18 @@ def cpu_baseline_pool(step, budget_s, block=1024):
 def fused_kernel_label(V, dtype):
     """Which fused-loss kernel a contiguous [tokens x V] chunk of this dtype takes
     (the library's dispatch: 1024 threads x 19 register vectors, plus 9 LDS
-    vectors per lane past that, else the streaming kernel)."""
+    vectors per lane past that, plus up to 4 vectors per lane read in both
+    sweeps for bf16, else the streaming kernel)."""
     vec = 8 if dtype == "bf16" else 4
     if V % vec:
         return "tok_stream_kernel"
     if V // vec <= 1024 * 19:
         return "tok_reg_kernel"
-    return "tok_reg_kernel (LDS tail)" if V // vec <= 1024 * 28 else "tok_stream_kernel"
+    if V // vec <= 1024 * 28:
+        return "tok_reg_kernel (LDS tail)"
+    if dtype == "bf16" and V // vec <= 1024 * 32:
+        return "tok_reg_kernel (LDS tail, part of the row read twice)"
+    return "tok_stream_kernel"
 
 
 def main():

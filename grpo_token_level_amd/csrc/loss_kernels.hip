@@ -521,11 +521,15 @@ __device__ __forceinline__ void sweep_dz(void* orow, int64_t idx, const uint4& v
 // TPR threads per token row, NV 16-byte vectors per thread in registers and
 // NL more in LDS (filled by direct-to-LDS loads issued with the register
 // loads, so a row that outgrows the register file is still read once).
+// NG more per thread, past what registers and LDS hold, are read from memory
+// in each of the two sweeps, two at a time: only that part of the row is read
+// twice.
 // TPR == 64: four token rows per 256-thread block, one wave each, wave-only
 // reductions.  TPR > 64: one row per block, cross-wave reduction through LDS.
-template <int DTI, int DTO, int TPR, int NV, bool GRAD, int NL = 0>
+template <int DTI, int DTO, int TPR, int NV, bool GRAD, int NL = 0, int NG = 0>
 __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const TokParams p) {
     static_assert(NL == 0 || TPR == 1024, "LDS-held vectors are for the one-row-per-block path");
+    static_assert(NG == 0 || (NL > 0 && NG % 2 == 0), "re-read vectors follow the LDS-held ones, in pairs");
     constexpr int VEC = In<DTI>::VEC;
     constexpr int WPR = TPR / 64;
     constexpr int RPB = TPR == 64 ? 4 : 1;
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     const int64_t t = (int64_t)xcd_runs(blockIdx.x, gridDim.x) * RPB + lrow;
     if (t >= p.n_tok) return;   // wave-uniform (RPB > 1) or block-uniform (RPB == 1)
 
-    const int nvec = (int)(p.V / VEC);   // the register path only runs for V / VEC <= TPR * (NV + NL)
+    const int nvec = (int)(p.V / VEC);   // the register path only runs for V / VEC <= TPR * (NV + NL + NG)
     const int64_t src = token_source(p, t);
     if (src < 0) {
         if (tid == 0) bad_source_outputs<GRAD>(p, t);
@@ -550,7 +554,7 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         if constexpr (GRAD) {
             if (orow) {
 #pragma unroll
-                for (int k = 0; k < NV + NL; ++k) {
+                for (int k = 0; k < NV + NL + NG; ++k) {
                     const int idx = k * TPR + tid;
                     if (idx < nvec) Out<DTO>::template zero<VEC>(orow, idx * VEC);
                 }
@@ -630,6 +634,14 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         for (int j = 0; j < NL; ++j)
             if ((NV + j) * TPR + tid < nvec) sweep_sums<DTI>(s_tail[j * TPR + tid], c, s, w);
     }
+    // the vectors past registers and LDS (clamped loads stay in the row)
+#pragma unroll
+    for (int g = 0; g < NG; g += 2) {
+        const int i0 = (NV + NL + g) * TPR + tid, i1 = i0 + TPR;
+        const uint4 a = vrow[min(i0, nvec - 1)], b = vrow[min(i1, nvec - 1)];
+        if (i0 < nvec) sweep_sums<DTI>(a, c, s, w);
+        if (i1 < nvec) sweep_sums<DTI>(b, c, s, w);
+    }
     block_merge<WPR>(c, s, w, tid, s_part);
     if constexpr (WPR > 1) zy = s_zy;
 
@@ -645,6 +657,11 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
 #pragma unroll
         for (int j = 0; j < NL; ++j)
             if ((NV + j) * TPR + tid < nvec) sweep_max<DTI>(s_tail[j * TPR + tid], m);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int i = (NV + NL + g) * TPR + tid;
+            if (i < nvec) sweep_max<DTI>(vrow[i], m);
+        }
         m = block_max<WPR>(m, tid, s_part);
         c = m * kLog2e;
         s = 0.0f;
@@ -656,6 +673,11 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
 #pragma unroll
         for (int j = 0; j < NL; ++j)
             if ((NV + j) * TPR + tid < nvec) sweep_sums_clamped<DTI>(s_tail[j * TPR + tid], c, s, w);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int i = (NV + NL + g) * TPR + tid;
+            if (i < nvec) sweep_sums_clamped<DTI>(vrow[i], c, s, w);
+        }
         block_sum2<WPR>(s, w, tid, s_part);
     }
 
@@ -664,7 +686,7 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         if (!orow) return;
         if (r.coef == 0.0f && r.eb == 0.0f) {   // zero advantage or clipped, no bonus: the row is zero
 #pragma unroll
-            for (int k = 0; k < NV + NL; ++k) {
+            for (int k = 0; k < NV + NL + NG; ++k) {
                 const int idx = k * TPR + tid;
                 if (idx < nvec) Out<DTO>::template zero<VEC>(orow, idx * VEC);
             }
@@ -689,6 +711,15 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
             const int idx = (NV + j) * TPR + tid;
             if (idx < nvec)
                 sweep_dz<DTI, DTO>(orow, idx, s_tail[j * TPR + tid], r, c3, neg, NV + j == ky && idx == vy, ey, zy);
+        }
+        // the re-read vectors: each is read and then written by the same lane,
+        // so an in-place update stays ordered
+#pragma unroll
+        for (int g = 0; g < NG; g += 2) {
+            const int i0 = (NV + NL + g) * TPR + tid, i1 = i0 + TPR;
+            const uint4 a = vrow[min(i0, nvec - 1)], b = vrow[min(i1, nvec - 1)];
+            if (i0 < nvec) sweep_dz<DTI, DTO>(orow, i0, a, r, c3, neg, NV + NL + g == ky && i0 == vy, ey, zy);
+            if (i1 < nvec) sweep_dz<DTI, DTO>(orow, i1, b, r, c3, neg, NV + NL + g + 1 == ky && i1 == vy, ey, zy);
         }
     }
 }
@@ -1213,6 +1244,7 @@ struct RegCfg {
     int tpr;
     int nv;
     int nl;   // 16-byte vectors per thread held in LDS
+    int ng;   // 16-byte vectors per thread read in both sweeps
 };
 
 // Register-resident configurations, in order of preference; the first whose
@@ -1220,33 +1252,38 @@ struct RegCfg {
 // NV stops at 19: at 1024 threads a lane has 128 VGPRs, and 19 vectors (76
 // VGPRs of row data) is the most that compiles without spilling.  The last
 // configuration adds 9 vectors per lane in LDS (144 KiB of the CU's 160 KiB):
-// rows up to 229 376 bf16 / 114 688 fp32 logits are still read once.
-constexpr RegCfg kRegCfgs[] = {{64, 1, 0},    {64, 2, 0},    {64, 4, 0},     {64, 8, 0},
-                               {256, 4, 0},   {256, 8, 0},   {1024, 4, 0},   {1024, 8, 0},
-                               {1024, 12, 0}, {1024, 16, 0}, {1024, 19, 0},  {1024, 19, 9}};
+// rows up to 229 376 bf16 / 114 688 fp32 logits are still read once.  The
+// last one reads up to 4 more vectors per lane from memory in each sweep, so
+// bf16 rows up to 262 144 logits read at most 1/8 of the row twice (gradient
+// path; with fp32 logits that variant would spill, and such rows stream).
+constexpr RegCfg kRegCfgs[] = {{64, 1, 0, 0},    {64, 2, 0, 0},   {64, 4, 0, 0},    {64, 8, 0, 0},
+                               {256, 4, 0, 0},   {256, 8, 0, 0},  {1024, 4, 0, 0},  {1024, 8, 0, 0},
+                               {1024, 12, 0, 0}, {1024, 16, 0, 0}, {1024, 19, 0, 0}, {1024, 19, 9, 0},
+                               {1024, 19, 9, 4}};
 
 template <int DTI, int DTO, bool GRAD>
 hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st) {
     const int rpb = c.tpr == 64 ? 4 : 1;
     const dim3 grid((unsigned)((p.n_tok + rpb - 1) / rpb));
     const dim3 block(c.tpr == 64 ? 256 : c.tpr);
-#define GRPO_REG_CASE(TPR_, NV_, NL_)                                                                  \
-    if (c.tpr == TPR_ && c.nv == NV_ && c.nl == NL_) {                                                 \
-        hipLaunchKernelGGL((tok_reg_kernel<DTI, DTO, TPR_, NV_, GRAD, NL_>), grid, block, 0, st, p); \
-        return hipGetLastError();                                                                      \
+#define GRPO_REG_CASE(TPR_, NV_, NL_, NG_)                                                                  \
+    if (c.tpr == TPR_ && c.nv == NV_ && c.nl == NL_ && c.ng == NG_) {                                       \
+        hipLaunchKernelGGL((tok_reg_kernel<DTI, DTO, TPR_, NV_, GRAD, NL_, NG_>), grid, block, 0, st, p); \
+        return hipGetLastError();                                                                           \
     }
-    GRPO_REG_CASE(64, 1, 0)
-    GRPO_REG_CASE(64, 2, 0)
-    GRPO_REG_CASE(64, 4, 0)
-    GRPO_REG_CASE(64, 8, 0)
-    GRPO_REG_CASE(256, 4, 0)
-    GRPO_REG_CASE(256, 8, 0)
-    GRPO_REG_CASE(1024, 4, 0)
-    GRPO_REG_CASE(1024, 8, 0)
-    GRPO_REG_CASE(1024, 12, 0)
-    GRPO_REG_CASE(1024, 16, 0)
-    GRPO_REG_CASE(1024, 19, 0)
-    GRPO_REG_CASE(1024, 19, 9)
+    GRPO_REG_CASE(64, 1, 0, 0)
+    GRPO_REG_CASE(64, 2, 0, 0)
+    GRPO_REG_CASE(64, 4, 0, 0)
+    GRPO_REG_CASE(64, 8, 0, 0)
+    GRPO_REG_CASE(256, 4, 0, 0)
+    GRPO_REG_CASE(256, 8, 0, 0)
+    GRPO_REG_CASE(1024, 4, 0, 0)
+    GRPO_REG_CASE(1024, 8, 0, 0)
+    GRPO_REG_CASE(1024, 12, 0, 0)
+    GRPO_REG_CASE(1024, 16, 0, 0)
+    GRPO_REG_CASE(1024, 19, 0, 0)
+    GRPO_REG_CASE(1024, 19, 9, 0)
+    if constexpr (GRAD && DTI == GRPO_BF16) GRPO_REG_CASE(1024, 19, 9, 4)
 #undef GRPO_REG_CASE
     return hipErrorInvalidValue;
 }
@@ -1260,8 +1297,10 @@ hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st) {
     // 4.4-5.9 for the register kernel; at 8192 the register kernel is ahead).
     if (vec_ok && (GRAD || p.V / In<DTI>::VEC <= 1024)) {
         const int64_t nvec = p.V / In<DTI>::VEC;
-        for (const RegCfg& c : kRegCfgs)
-            if ((int64_t)c.tpr * (c.nv + c.nl) >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st);
+        for (const RegCfg& c : kRegCfgs) {
+            if (c.ng > 0 && !(GRAD && DTI == GRPO_BF16)) continue;
+            if ((int64_t)c.tpr * (c.nv + c.nl + c.ng) >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st);
+        }
     }
     hipLaunchKernelGGL((tok_stream_kernel<DTI, DTO, GRAD>), dim3((unsigned)p.n_tok), dim3(kStreamTPR), 0, st, p);
     return hipGetLastError();

@@ -61,10 +61,17 @@ CASES = [
     (202048, torch.bfloat16, torch.bfloat16, 6),
     (229376, torch.bfloat16, torch.float32, 3),
     (100000, torch.float32, torch.float32, 4),
-    # one vector past that capacity, a 256k vocabulary, rows off 16-byte
-    # alignment with an output of another phase: the streaming kernel
+    # past registers and LDS: up to 4 more vectors per lane read in both
+    # sweeps (one vector past the LDS capacity, a 256k vocabulary, the full
+    # capacity of 262 144)
     (229384, torch.bfloat16, torch.bfloat16, 3),
     (256000, torch.bfloat16, torch.bfloat16, 3),
+    (256000, torch.bfloat16, torch.float32, 2),
+    (262144, torch.bfloat16, torch.bfloat16, 3),
+    # one vector past that, fp32 rows past the LDS capacity, rows off 16-byte
+    # alignment with an output of another phase: the streaming kernel
+    (262152, torch.bfloat16, torch.bfloat16, 2),
+    (114696, torch.float32, torch.float32, 2),
     (50257, torch.bfloat16, torch.float32, 9),
     (1003, torch.float32, torch.bfloat16, 31),
 ]
@@ -83,11 +90,13 @@ def test_loss_matches_oracle(V, din, dout, n):
 
 
 @pytest.mark.parametrize("din,V,ld,n", [(torch.float32, 1024, 1040, 45), (torch.bfloat16, 1024, 1040, 45),
-                                        (torch.bfloat16, 202048, 202064, 4), (torch.bfloat16, 50257, 50263, 9)])
+                                        (torch.bfloat16, 202048, 202064, 4), (torch.bfloat16, 256000, 256016, 3),
+                                        (torch.bfloat16, 50257, 50263, 9)])
 def test_padded_row_stride_and_inplace(din, V, ld, n):
     # logits rows padded to ld > V; then the same chunk updated in place
-    # (202048: part of each row in LDS; 50257 with an odd stride: rows of
-    # every alignment phase through the streaming kernel)
+    # (202048: part of each row in LDS; 256000: part read again in the
+    # gradient sweep; 50257 with an odd stride: rows of every alignment phase
+    # through the streaming kernel)
     d = make_chunk(n, V, din, seed=3, ld=ld)
     scale = 0.01
     ref = run_oracle(d, scale)
@@ -150,8 +159,8 @@ def test_bad_targets_and_nan_logits_are_flagged_not_read():
 # row x elements per 16-byte vector on that kernel path)
 @pytest.mark.parametrize("V,dtype,first", [(151936, torch.bfloat16, 8192), (16384, torch.bfloat16, 2048),
                                            (4096, torch.bfloat16, 512), (1024, torch.float32, 256),
-                                           (202048, torch.bfloat16, 8192), (256000, torch.bfloat16, 2056),
-                                           (50257, torch.bfloat16, 2056)])
+                                           (202048, torch.bfloat16, 8192), (256000, torch.bfloat16, 8192),
+                                           (262152, torch.bfloat16, 2056), (50257, torch.bfloat16, 2056)])
 def test_special_rows(V, dtype, first):
     # Rows the one-sweep sums cannot take and that go through the exact
     # max-shifted sweeps instead: scattered -inf logits, the whole first

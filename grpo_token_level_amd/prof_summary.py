@@ -3,7 +3,7 @@
 
     python -m grpo_token_level_amd.prof_summary stats KERNEL_STATS_CSV OUT.txt --cmd "..."
     python -m grpo_token_level_amd.prof_summary pmc FETCH_CSV WRITE_CSV OUT.txt --cmd "..." \
-        [--kernel "tok_reg_kernel<1, 1, 1024, 19, true, 0>"]
+        [--kernel "tok_reg_kernel<1, 1, 1024, 19, true, 0, 0>"]
 
 ``pmc`` calibrates the two TCC byte counters with the plain copy the bench
 runs under ``--copy-calibration`` (a 1 GiB int32 bitwise-not: 1 GiB read,
@@ -159,7 +159,7 @@ def main():
     p.add_argument("write")
     p.add_argument("out")
     p.add_argument("--cmd", required=True)
-    p.add_argument("--kernel", default="tok_reg_kernel<1, 1, 1024, 19, true, 0>")
+    p.add_argument("--kernel", default="tok_reg_kernel<1, 1, 1024, 19, true, 0, 0>")
     p.add_argument("--workload", default="qwen")
     m = sub.add_parser("mfma")
     m.add_argument("csv")

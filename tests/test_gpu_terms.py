@@ -127,9 +127,11 @@ def test_terms_on_the_generic_path():
     _check_stats(ws, ref, d)
 
 
-def test_full_vocabulary_with_terms():
-    # V = 151936 bf16: the 1024-thread register path with the bonus sweep
-    d = _with_ref(make_chunk(12, 151936, torch.bfloat16, seed=9, n_rows=3, logit_std=3.0, noise=0.3), seed=9)
+@pytest.mark.parametrize("V", [151936, 256000])
+def test_full_vocabulary_with_terms(V):
+    # the 1024-thread register path with the bonus sweep (256000: the part of
+    # each row past registers and LDS is read again in that sweep)
+    d = _with_ref(make_chunk(12, V, torch.bfloat16, seed=9, n_rows=3, logit_std=3.0, noise=0.3), seed=9)
     _, w = _weights(d, AGG_SEQ_MEAN_TOKEN_SUM)
     g = d["g"]
     ws = ops.loss_fwd_bwd(d["logits"], g["target"], g["mask"], g["old"], g["tok_row"], g["adv_row"], g["row_off"],

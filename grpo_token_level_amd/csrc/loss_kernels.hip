@@ -14,7 +14,8 @@
 // on chip until its gradient row is written (tok_reg_kernel):
 //   * large V (e.g. 151936 bf16 = 297 KiB): one 1024-thread workgroup per
 //     token; each lane holds NV 16-byte vectors (NV = 19 -> 76 VGPRs), and
-//     past that 9 more per lane in LDS (rows up to 229376 bf16).
+//     past that 9 more per lane in LDS (rows up to 229376 bf16).  bf16 rows up
+//     to 262144 read the up to 4 vectors per lane past that in both sweeps.
 //     Reductions: wave64 butterfly, then the 16 wave partials through LDS in a
 //     fixed order.
 //   * small V (<= 4096 bf16 / 2048 fp32): one wave64 per token, four tokens

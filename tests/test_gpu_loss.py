@@ -48,6 +48,10 @@ CASES = [
     (4096, torch.bfloat16, torch.float32, 67),
     (16384, torch.bfloat16, torch.bfloat16, 37),
     (32000, torch.bfloat16, torch.bfloat16, 21),
+    # 256-thread blocks with 16 and 24 vectors per lane
+    (24576, torch.bfloat16, torch.float32, 7),
+    (40960, torch.bfloat16, torch.bfloat16, 9),
+    (20000, torch.float32, torch.float32, 6),
     (151936, torch.bfloat16, torch.bfloat16, 9),
     (151936, torch.bfloat16, torch.float32, 5),
     (8, torch.float32, torch.float32, 33),
@@ -160,7 +164,8 @@ def test_bad_targets_and_nan_logits_are_flagged_not_read():
 @pytest.mark.parametrize("V,dtype,first", [(151936, torch.bfloat16, 8192), (16384, torch.bfloat16, 2048),
                                            (4096, torch.bfloat16, 512), (1024, torch.float32, 256),
                                            (202048, torch.bfloat16, 8192), (256000, torch.bfloat16, 8192),
-                                           (262152, torch.bfloat16, 2056), (50257, torch.bfloat16, 2056)])
+                                           (262152, torch.bfloat16, 2056), (50257, torch.bfloat16, 2056),
+                                           (40960, torch.bfloat16, 2048)])
 def test_special_rows(V, dtype, first):
     # Rows the one-sweep sums cannot take and that go through the exact
     # max-shifted sweeps instead: scattered -inf logits, the whole first

@@ -320,28 +320,31 @@ class PaddedStep:
         return f"warm: a step touches {ws / 1e6:.1f} MB of logits and dlogits, within the 256 MB last-level cache"
 
     def copy_context(self):
-        """The library's streaming copy (grpo_stream_probe) of one chunk's bytes,
-        timed like the kernel: the bandwidth a plain copy of the same bytes gets."""
-        return self._stream_rate(self.ops.STREAM_COPY)
+        """The yardstick's streaming copy of one chunk's bytes, timed like the
+        kernel: the bandwidth a plain copy of the same bytes gets."""
+        import yardstick
+        return self._stream_rate(yardstick.COPY)
 
     def read_context(self):
         """The same for a plain read of one chunk's logits (the ahead pass's yardstick)."""
-        return self._stream_rate(self.ops.STREAM_READ)
+        import yardstick
+        return self._stream_rate(yardstick.READ)
 
     def _stream_rate(self, mode):
-        torch, ops = self.torch, self.ops
+        import yardstick
+        torch = self.torch
         n = self.ws["logp"].numel()
         src = self.logits[:n]
-        dst = self.dlogits[:n] if mode == ops.STREAM_COPY else None
+        dst = self.dlogits[:n] if mode == yardstick.COPY else None
         nbytes = src.numel() * src.element_size()
-        dst = ops.stream_probe(mode, src, dst, nbytes)
+        dst = yardstick.stream(mode, src, dst, nbytes)
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record()
         for _ in range(3):
-            ops.stream_probe(mode, src, dst, nbytes)
+            yardstick.stream(mode, src, dst, nbytes)
         c1.record()
         torch.cuda.synchronize()
-        moved = nbytes * (2 if mode == ops.STREAM_COPY else 1)
+        moved = nbytes * (2 if mode == yardstick.COPY else 1)
         return 3 * moved / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
     def sample(self, n, start=0):
@@ -745,7 +748,7 @@ def main():
                 "algorithmic_bytes_per_launch": int(units // launches), "avg_launch_ms": round(tot_ms / launches, 4)}
         roof["device_copy_GBs"] = round(step.copy_context(), 1)
         if wl == "qwen" and not (args.terms or args.ahead or args.epochs != 1 or args.shuffle or args.vocab):
-            from grpo_token_level_amd.prof_summary import load_traffic
+            from yardstick.prof_summary import load_traffic
             rec = load_traffic(os.path.join(ROOT, "profiles", "fused_loss_qwen_pmc.txt"))
             if rec is not None:
                 roof["traffic"] = rec["traffic_bytes_per_launch"]

@@ -11,7 +11,9 @@ import os
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgrpo.so")
+# GRPO_LIB names another build of the same ABI (the host-only sanitizer build).
+LIB_PATH = os.environ.get("GRPO_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgrpo.so")
+HOST_ONLY = os.path.basename(LIB_PATH) == "libgrpo_host_san.so"
 
 GRPO_F32 = 0
 GRPO_BF16 = 1
@@ -31,7 +33,6 @@ class GrpoError(RuntimeError):
 
 KL_K1, KL_K2, KL_K3 = 1, 2, 3
 AGG_TOKEN_MEAN, AGG_SEQ_MEAN_TOKEN_SUM, AGG_SEQ_MEAN_TOKEN_MEAN = 0, 1, 2
-STREAM_COPY, STREAM_READ, STREAM_FILL = 0, 1, 2
 
 
 class Stats(ctypes.Structure):
@@ -80,9 +81,11 @@ class LmheadArgs(ctypes.Structure):
                 ("ent_coef", _f32), ("kl_coef", _f32), ("kl_type", _i32), ("reserved2", _i32)]
 
 
-class Accum(ctypes.Structure):
-    _fields_ = [("n_micro", _i64), ("pos", _i64), ("skip", _i64), ("done", _i32), ("reserved", _i32),
-                ("open", Stats), ("closed", Stats)]
+class TracePlan(ctypes.Structure):
+    _fields_ = [("struct_size", _i32), ("dtype", _i32), ("stage", ctypes.c_char_p), ("n_rows", _i64), ("T", _i64),
+                ("V", _i64), ("row_len", _p), ("row_valid", _p), ("row_uid", _p), ("row_traj", _p),
+                ("row_seg", _p), ("row_is_pad", _p), ("n_calls", _i64), ("call_off", _p), ("call_rows", _p),
+                ("call_step", _p)]
 
 
 class StepResult(ctypes.Structure):
@@ -124,6 +127,8 @@ PROTOTYPES = {
     "grpo_plan_compaction": (ctypes.c_int, [_P32, _i64, _i64, _i64, _i64, _i64, _i32, _i64, _P64,
                                             _P32, _P32, _P32, _PU8, _P32]),
     "grpo_row_offsets": (ctypes.c_int, [_P64, _P64, _i64, _P64]),
+    "grpo_plan_trace": (ctypes.c_int, [ctypes.POINTER(TracePlan), ctypes.c_char_p, ctypes.c_size_t,
+                                       ctypes.POINTER(ctypes.c_size_t)]),
     "grpo_group_advantage": (ctypes.c_int, [_PF32, _i64, _i64, _f32, _i32, _PF32]),
     "grpo_rows_advantage": (ctypes.c_int, [_PF32, _i64, _P32, _i64, _PF32]),
     "grpo_count_valid": (ctypes.c_int, [_p, _p, _i64, _p]),
@@ -148,11 +153,11 @@ PROTOTYPES = {
     "grpo_probe_init": (ctypes.c_int, [ctypes.POINTER(Probe), ctypes.c_double, ctypes.c_double]),
     "grpo_probe_finish": (ctypes.c_int, [ctypes.POINTER(Probe), ctypes.POINTER(ProbeStats),
                                          ctypes.POINTER(ctypes.c_int32)]),
-    "grpo_accum_init": (ctypes.c_int, [ctypes.POINTER(Accum), _i64]),
-    "grpo_accum_add": (ctypes.c_int, [ctypes.POINTER(Accum), ctypes.POINTER(Stats)]),
-    "grpo_accum_finalize": (ctypes.c_int, [ctypes.POINTER(Accum), ctypes.POINTER(StepResult),
+    "grpo_accum_size": (ctypes.c_size_t, []),
+    "grpo_accum_init": (ctypes.c_int, [_p, _i64]),
+    "grpo_accum_add": (ctypes.c_int, [_p, ctypes.POINTER(Stats)]),
+    "grpo_accum_finalize": (ctypes.c_int, [_p, ctypes.POINTER(StepResult),
                                            ctypes.POINTER(ctypes.c_int32)]),
-    "grpo_stream_probe": (ctypes.c_int, [_p, _i32, _p, _p, _i64]),
 }
 
 _lib = None
@@ -166,6 +171,8 @@ def lib():
             raise ImportError(f"{LIB_PATH} is missing: build it with `python -m grpo_token_level_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in PROTOTYPES.items():
+            if HOST_ONLY and not hasattr(L, name):
+                continue
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args

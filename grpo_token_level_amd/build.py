@@ -1,6 +1,12 @@
 """Builds libgrpo.so (host C++ + gfx950 HIP kernels) in-tree.
 
-    python -m grpo_token_level_amd.build [-v]
+    python -m grpo_token_level_amd.build [-v] [--sanitize]
+
+``--sanitize`` builds instead ``libgrpo_host_san.so``: the host half only
+(plans, advantages, accumulator, pi_old cache bookkeeping, probe verdict,
+trace dump) under AddressSanitizer and UndefinedBehaviorSanitizer, with the
+one device call the host half makes stubbed out.  Load it with the ASan
+runtime preloaded (``sanitizer_env``).
 
 Objects go to ``_build/`` at the repository root; the shared library is
 written next to this file so that it travels with the source tree.
@@ -18,11 +24,14 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgrpo.so")
+SAN_LIB = os.path.join(PKG, "libgrpo_host_san.so")
+SAN_FLAGS = ["-O1", "-g", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-fno-omit-frame-pointer",
+             "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of the generated code.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
-             "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics", "-Wall", "-Wno-unused-result"]
+             "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-result"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 
@@ -69,5 +78,29 @@ def build(verbose=False):
     return LIB
 
 
+def build_sanitized(verbose=False):
+    """The host-only library under ASan + UBSan (g++; no GPU code in it)."""
+    srcs = [s for s in sources() if s.endswith(".cpp")] + [os.path.join(CSRC, "sanitize", "device_stub.cpp")]
+    tmp = SAN_LIB + ".tmp"
+    _run(["g++", *SAN_FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp], verbose)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
+def sanitizer_env(base=None):
+    """Environment for a process that loads libgrpo_host_san.so: the ASan
+    runtime preloaded (ahead of anything already preloaded), leak checks off
+    (the interpreter keeps objects alive at exit), every report fatal."""
+    env = dict(os.environ if base is None else base)
+    asan = subprocess.run(["g++", "-print-file-name=libasan.so"], stdout=subprocess.PIPE, text=True).stdout.strip()
+    pre = env.get("LD_PRELOAD", "")
+    env["LD_PRELOAD"] = asan + (":" + pre if pre else "")
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1:halt_on_error=1"
+    env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1"
+    env["GRPO_LIB"] = SAN_LIB
+    return env
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv[1:]))
+    args = sys.argv[1:]
+    print(build_sanitized(verbose="-v" in args) if "--sanitize" in args else build(verbose="-v" in args))

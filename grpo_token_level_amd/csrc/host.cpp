@@ -342,7 +342,22 @@ extern "C" int grpo_rows_advantage(const float* adv_rollout, int64_t n_rollouts,
 
 // ---------------------------------------------------------------- accumulator
 
+// The window state behind the opaque grpo_accum handle.
+struct grpo_accum {
+    uint64_t magic;     // kAccumMagic once grpo_accum_init has run
+    int64_t n_micro;
+    int64_t pos;        // chunks accumulated in the open window
+    int64_t skip;       // calls still to swallow
+    int32_t done;       // a completed window waits for grpo_accum_finalize
+    int32_t reserved;
+    grpo_stats open;    // sums of the open window
+    grpo_stats closed;  // sums of the completed window
+};
+
 namespace {
+constexpr uint64_t kAccumMagic = 0x6772706f61636331ull;
+bool accum_ready(const grpo_accum* a) { return a && a->magic == kAccumMagic && a->n_micro >= 1; }
+
 void stats_zero(grpo_stats* s) { std::memset(s, 0, sizeof(*s)); }
 void stats_add(grpo_stats* a, const grpo_stats* b) {
     a->loss_sum += b->loss_sum;
@@ -356,9 +371,12 @@ void stats_add(grpo_stats* a, const grpo_stats* b) {
 }
 }  // namespace
 
+extern "C" size_t grpo_accum_size(void) { return sizeof(grpo_accum); }
+
 extern "C" int grpo_accum_init(grpo_accum* acc, int64_t n_micro) {
     if (!acc || n_micro < 1) return fail(GRPO_EINVAL, "grpo_accum_init: n_micro must be >= 1");
     std::memset(acc, 0, sizeof(*acc));
+    acc->magic = kAccumMagic;
     acc->n_micro = n_micro;
     return ok();
 }
@@ -366,7 +384,7 @@ extern "C" int grpo_accum_init(grpo_accum* acc, int64_t n_micro) {
 // [P1] "The poisoned-window countdown": on a non-finite chunk the window is
 // discarded and exactly the remaining chunks of that window are swallowed.
 extern "C" int grpo_accum_add(grpo_accum* acc, const grpo_stats* c) {
-    if (!acc || !c || acc->n_micro < 1) return fail(GRPO_EINVAL, "grpo_accum_add: bad arguments");
+    if (!accum_ready(acc) || !c) return fail(GRPO_EINVAL, "grpo_accum_add: NULL or unprepared argument");
     if (acc->done) return fail(GRPO_ESTATE, "grpo_accum_add: finalize the completed window first");
     if (acc->skip > 0) {
         --acc->skip;
@@ -393,7 +411,8 @@ extern "C" int grpo_accum_add(grpo_accum* acc, const grpo_stats* c) {
 // [P1] "Metric roll-up": token-weighted loss, summed counts; "The hard part":
 // one gradient scale 1/max(sum of divisors, 1).
 extern "C" int grpo_accum_finalize(grpo_accum* acc, grpo_step_result* out, int32_t* stepped) {
-    if (!acc || !out || !stepped) return fail(GRPO_EINVAL, "grpo_accum_finalize: NULL argument");
+    if (!accum_ready(acc) || !out || !stepped)
+        return fail(GRPO_EINVAL, "grpo_accum_finalize: NULL or unprepared argument");
     if (!acc->done) {
         *stepped = 0;
         return ok();

@@ -12,7 +12,6 @@ import numpy as np
 
 from . import _capi as C
 from ._capi import GrpoError, STATS_DTYPE, STATS_BYTES  # noqa: F401  (re-exported)
-from ._capi import STREAM_COPY, STREAM_READ, STREAM_FILL  # noqa: F401  (re-exported)
 
 # ---------------------------------------------------------------- host calls
 
@@ -98,6 +97,36 @@ def row_offsets(lengths, order=None):
     return off
 
 
+def plan_trace(stage, calls, call_step, row_len, row_valid, row_uid, row_traj, V, T=0, dtype="bf16",
+               row_seg=None, row_is_pad=None):
+    """Trace of a plan (grpo_plan_trace) -> list of dicts, one per JSON line.
+
+    ``calls``: the rows of each training call in visiting order (a list of
+    int sequences); ``call_step``: the optimizer step of each call; per-row
+    arrays over the batch's rows."""
+    import json
+    n_rows = len(row_len)
+    a64 = lambda x: np.ascontiguousarray(x, dtype=np.int64)  # noqa: E731
+    a32 = lambda x: np.ascontiguousarray(x, dtype=np.int32)  # noqa: E731
+    off = a64(np.concatenate([[0], np.cumsum([len(c) for c in calls])]))
+    rows = a64(np.concatenate([np.asarray(c, np.int64) for c in calls]) if calls else np.zeros(0))
+    keep = [a64(row_len), a64(row_valid), a32(row_uid), a32(row_traj), a64(call_step), off, rows]
+    seg = a32(row_seg) if row_seg is not None else None
+    pad = np.ascontiguousarray(row_is_pad, dtype=np.uint8) if row_is_pad is not None else None
+    vp = lambda x: x.ctypes.data if x is not None and x.size else None  # noqa: E731
+    plan = C.TracePlan(struct_size=ctypes.sizeof(C.TracePlan), dtype=C.GRPO_BF16 if dtype == "bf16" else C.GRPO_F32,
+                       stage=stage.encode(), n_rows=n_rows, T=T, V=V, row_len=vp(keep[0]), row_valid=vp(keep[1]),
+                       row_uid=vp(keep[2]), row_traj=vp(keep[3]), row_seg=vp(seg), row_is_pad=vp(pad),
+                       n_calls=len(calls), call_off=vp(off), call_rows=vp(rows), call_step=vp(keep[4]))
+    need = ctypes.c_size_t()
+    code = C.lib().grpo_plan_trace(ctypes.byref(plan), None, 0, ctypes.byref(need))
+    if code != -7:
+        C.check(code)
+    buf = ctypes.create_string_buffer(need.value)
+    C.check(C.lib().grpo_plan_trace(ctypes.byref(plan), buf, need.value, ctypes.byref(need)))
+    return [json.loads(line) for line in buf.value.decode().splitlines()]
+
+
 def group_advantage(reward, group_size, eps=1e-6, norm_by_std=True):
     r = np.ascontiguousarray(reward, dtype=np.float32)
     out = np.zeros(max(r.shape[0], 1), np.float32)
@@ -119,12 +148,13 @@ class Accumulator:
     'SKIPPED'; finalize() returns a dict or None."""
 
     def __init__(self, n_micro):
-        self._a = C.Accum()
-        C.check(C.lib().grpo_accum_init(ctypes.byref(self._a), n_micro))
+        n = int(C.lib().grpo_accum_size())
+        self._a = (ctypes.c_int64 * ((n + 7) // 8))()     # opaque bytes, 8-byte aligned
+        C.check(C.lib().grpo_accum_init(self._a, n_micro))
 
     def add(self, stats):
         s = C.Stats(**{k: stats.get(k, 0) for k in STATS_DTYPE.names})
-        code = C.lib().grpo_accum_add(ctypes.byref(self._a), ctypes.byref(s))
+        code = C.lib().grpo_accum_add(self._a, ctypes.byref(s))
         if code == 0:
             return "OK"
         if code == -5:
@@ -138,7 +168,7 @@ class Accumulator:
     def finalize(self):
         r = C.StepResult()
         stepped = ctypes.c_int32()
-        C.check(C.lib().grpo_accum_finalize(ctypes.byref(self._a), ctypes.byref(r), ctypes.byref(stepped)))
+        C.check(C.lib().grpo_accum_finalize(self._a, ctypes.byref(r), ctypes.byref(stepped)))
         if not stepped.value:
             return None
         return {k: getattr(r, k) for k, _ in C.StepResult._fields_}
@@ -308,28 +338,6 @@ def _rows2d(x, name):
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError(f"{name} must be 2-D with unit stride along the vocabulary")
     return x.stride(0)
-
-
-def stream_probe(mode, src=None, dst=None, nbytes=None):
-    """The measurement yardstick (grpo_stream_probe): a plain copy
-    (STREAM_COPY, src -> dst), read (STREAM_READ, src; dst is 16 bytes of
-    scratch) or zero fill (STREAM_FILL, dst) of ``nbytes`` bytes (default: the
-    whole src, or dst for a fill).  Returns dst."""
-    torch = _torch()
-    if mode == C.STREAM_READ and dst is None:
-        dst = torch.empty(16, dtype=torch.uint8, device=src.device)
-    if mode not in (C.STREAM_COPY, C.STREAM_READ, C.STREAM_FILL):
-        raise ValueError(f"unknown stream mode {mode}")
-    size = lambda t: t.numel() * t.element_size()  # noqa: E731
-    if nbytes is None:
-        nbytes = size(dst if mode == C.STREAM_FILL else src)
-    for t, name, need in ((src, "src", nbytes if mode != C.STREAM_FILL else 0),
-                          (dst, "dst", 16 if mode == C.STREAM_READ else nbytes)):
-        if need and (t is None or not t.is_cuda or not t.is_contiguous() or size(t) < need):
-            raise ValueError(f"{name} must be a contiguous GPU tensor of at least {need} bytes")
-    C.check(C.lib().grpo_stream_probe(_stream(), mode, ctypes.c_void_p(src.data_ptr()) if src is not None else None,
-                                      ctypes.c_void_p(dst.data_ptr()), nbytes))
-    return dst
 
 
 def count_valid(mask, out=None):

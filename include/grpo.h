@@ -159,6 +159,50 @@ int grpo_plan_compaction(const int32_t* rows_per_rollout, int64_t n_rollouts, in
  * (variable-length) layout, [P3] section 3. */
 int grpo_row_offsets(const int64_t* len, const int64_t* order, int64_t n_rows, int64_t* row_off);
 
+/* ================================================================== plan trace */
+
+/* One plan, as the chunks a training walk visits, for the trace dump.
+ * [P2] "Trace Entry" lists what a minimal trace records per row of a group:
+ * stage, field, producer and consumer, shape or nested length, dtype and
+ * device, valid length, response_mask.sum(), uid and trajectory key, the
+ * global step, and is_padding.  All pointers are host pointers. */
+typedef struct grpo_trace_plan {
+    int32_t struct_size;        /* = sizeof(grpo_trace_plan) */
+    int32_t dtype;              /* grpo_dtype of the logits the chunks read */
+    const char* stage;          /* label of the plan ([A-Za-z0-9_.-], 1..63 characters) */
+    int64_t n_rows;             /* rows of the collected batch (after compaction: segment and pad rows) */
+    int64_t T;                  /* padded positions per row, or 0 for a packed (nested) layout */
+    int64_t V;                  /* vocabulary: a row's logits are [len x V] */
+    const int64_t* row_len;     /* [n_rows] positions of the row (its nested length; <= T when padded) */
+    const int64_t* row_valid;   /* [n_rows] response_mask.sum() of the row (<= row_len) */
+    const int32_t* row_uid;     /* [n_rows] group (prompt uid) of the row, >= 0 */
+    const int32_t* row_traj;    /* [n_rows] rollout (trajectory key) of the row; >= 0, or -1 on a pad row */
+    const int32_t* row_seg;     /* NULL or [n_rows] segment index within the rollout (compaction); -1 on a pad */
+    const uint8_t* row_is_pad;  /* NULL (no pads) or [n_rows] 1 = padding row */
+    int64_t n_calls;            /* training calls (chunks) in visiting order */
+    const int64_t* call_off;    /* [n_calls + 1] offsets into call_rows, non-decreasing from 0 */
+    const int64_t* call_rows;   /* rows of each call, in the order the chunk lays them out */
+    const int64_t* call_step;   /* [n_calls] optimizer step (global mini-batch index) of each call */
+} grpo_trace_plan;
+
+/* host.  Writes the trace of a plan as JSON lines into buf: for every call k,
+ * one object per row it holds,
+ *   {"stage", "call", "step", "pos", "row", "uid", "traj", "seg", "field",
+ *    "producer", "consumer", "shape", "dtype", "device", "len", "valid",
+ *    "is_padding"}
+ * ("pos" = the row's place in the chunk, "shape" = [len, V] nested or [T, V]
+ * padded, "field" = "logits", producer "policy forward", consumer
+ * "grpo_loss_fwd_bwd"; "traj" and "seg" are null on a pad row that names no
+ * rollout), then one summary object per call
+ *   {"stage", "call", "step", "summary": true, "rows", "pads", "positions",
+ *    "valid"}.
+ * Each line ends with '\n' and the text with a terminating NUL.  Checks: rows
+ * in range, lengths and counts consistent (valid <= len, len <= T when
+ * padded), EINVAL otherwise.  *need receives the bytes the text takes
+ * (NUL included); if cap < *need the result is ECAPACITY and buf is untouched. */
+int grpo_plan_trace(const grpo_trace_plan* plan, char* buf, size_t cap, size_t* need);
+
+
 /* ============================================================== advantage */
 
 /* host.  One advantage per rollout, relative to its group of group_size
@@ -474,15 +518,12 @@ int grpo_probe_finish(grpo_probe* p, const grpo_probe_stats* stats, int32_t* pas
  * loss is sum(loss_sum)/max(sum(n_valid), 1) and counts sum; [P1] "The
  * poisoned-window countdown": a non-finite chunk at position j discards the
  * window and the next n_micro - 1 - j calls are swallowed. */
-typedef struct grpo_accum {
-    int64_t n_micro;
-    int64_t pos;        /* chunks accumulated in the open window */
-    int64_t skip;       /* calls still to swallow */
-    int32_t done;       /* a completed window waits for grpo_accum_finalize */
-    int32_t reserved;
-    grpo_stats open;    /* sums of the open window */
-    grpo_stats closed;  /* sums of the completed window */
-} grpo_accum;
+typedef struct grpo_accum grpo_accum;   /* opaque: the caller provides grpo_accum_size() bytes,
+                                           aligned to 8, and grpo_accum_init prepares them */
+
+/* host.  Bytes of one accumulator (a small constant; no pointers inside, so a
+ * copy of the bytes is a copy of the state). */
+size_t grpo_accum_size(void);
 
 typedef struct grpo_step_result {
     double  loss;          /* sum(loss_sum) / max(N, 1) */
@@ -497,7 +538,9 @@ typedef struct grpo_step_result {
     int64_t n_clipped;
 } grpo_step_result;
 
-/* host.  n_micro >= 1. */
+/* host.  Prepares acc (grpo_accum_size() bytes) for windows of n_micro >= 1
+ * chunks.  Every other accum call refuses (EINVAL) a buffer that was not
+ * prepared. */
 int grpo_accum_init(grpo_accum* acc, int64_t n_micro);
 /* host.  Adds one chunk's stats (host copy).  Returns GRPO_OK, GRPO_ENONFINITE
  * (window discarded; zero your accumulated gradients), GRPO_ESKIPPED (call
@@ -507,20 +550,6 @@ int grpo_accum_add(grpo_accum* acc, const grpo_stats* chunk);
 /* host.  *stepped = 1 and *out filled when a window is complete (the window is
  * then closed); *stepped = 0 otherwise. */
 int grpo_accum_finalize(grpo_accum* acc, grpo_step_result* out, int32_t* stepped);
-
-/* ===================================================== measurement yardstick */
-
-/* Not part of the method: a plain streaming pass over one buffer that the
- * benchmark times beside the loss kernels, so that their bandwidth can be
- * read against what the memory system delivers for a copy, a read or a write
- * of the same bytes (and that calibrates byte counters with a known size). */
-#define GRPO_STREAM_COPY 0   /* dst[0, bytes) = src[0, bytes) */
-#define GRPO_STREAM_READ 1   /* reads src[0, bytes); dst: 16 bytes of scratch, in practice untouched */
-#define GRPO_STREAM_FILL 2   /* dst[0, bytes) = 0; src unused (may be NULL) */
-
-/* device.  bytes a multiple of 16 and pointers 16-byte aligned, else EINVAL;
- * for a copy the ranges must not overlap.  Enqueued on `stream`. */
-int grpo_stream_probe(void* stream, int32_t mode, const void* src, void* dst, int64_t bytes);
 
 #ifdef __cplusplus
 }

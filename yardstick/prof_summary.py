@@ -1,8 +1,8 @@
 """Turns rocprofv3 CSV output into the short text summaries kept under
 ``profiles/``.
 
-    python -m grpo_token_level_amd.prof_summary stats KERNEL_STATS_CSV OUT.txt --cmd "..."
-    python -m grpo_token_level_amd.prof_summary pmc FETCH_CSV WRITE_CSV OUT.txt --cmd "..." \
+    python -m yardstick.prof_summary stats KERNEL_STATS_CSV OUT.txt --cmd "..."
+    python -m yardstick.prof_summary pmc FETCH_CSV WRITE_CSV OUT.txt --cmd "..." \
         [--kernel "tok_reg_kernel<1, 1, 1024, 19, true, 0, 0>"]
 
 ``pmc`` calibrates the two TCC byte counters with the plain copy the bench
@@ -19,8 +19,8 @@ import hashlib
 import json
 import os
 
-PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(PKG, "csrc", "loss_kernels.hip")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCE = os.path.join(ROOT, "grpo_token_level_amd", "csrc", "loss_kernels.hip")
 CALIB_KERNEL = "bitwise_not_kernel"
 CALIB_BYTES = 1 << 30
 

@@ -9,11 +9,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdio>
 
-#include "common.h"
-
-using grpo::fail;
-using grpo::ok;
+enum { YS_COPY = 0, YS_READ = 1, YS_FILL = 2 };
 
 namespace {
 
@@ -61,28 +59,42 @@ __global__ __launch_bounds__(kLanes) void stream_fill_kernel(u32x4* __restrict__
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+thread_local char g_err[256] = "";
+
+int fail(int code, const char* msg) {
+    std::snprintf(g_err, sizeof(g_err), "%s", msg);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return 0;
+}
+
 }  // namespace
 
-extern "C" int grpo_stream_probe(void* stream, int32_t mode, const void* src, void* dst, int64_t bytes) {
-    if (mode != GRPO_STREAM_COPY && mode != GRPO_STREAM_READ && mode != GRPO_STREAM_FILL)
-        return fail(GRPO_EINVAL, "grpo_stream_probe: unknown mode %d", mode);
-    if (bytes < 0 || bytes % 16) return fail(GRPO_EINVAL, "grpo_stream_probe: bytes must be a multiple of 16");
-    const bool need_src = mode != GRPO_STREAM_FILL;
+extern "C" const char* ys_last_error(void) { return g_err; }
+
+extern "C" int ys_stream(void* stream, int32_t mode, const void* src, void* dst, int64_t bytes) {
+    if (mode != YS_COPY && mode != YS_READ && mode != YS_FILL)
+        return fail(-1, "ys_stream: unknown mode");
+    if (bytes < 0 || bytes % 16) return fail(-1, "ys_stream: bytes must be a multiple of 16");
+    const bool need_src = mode != YS_FILL;
     if ((need_src && (!src || !al16(src))) || !dst || !al16(dst))
-        return fail(GRPO_EINVAL, "grpo_stream_probe: NULL or misaligned pointer (16 bytes)");
+        return fail(-1, "ys_stream: NULL or misaligned pointer (16 bytes)");
     const int64_t n = bytes / 16;
     if (n == 0) return ok();
     const int64_t blocks = (n + kPerBlock - 1) / kPerBlock;
-    if (blocks > 0x7fffffffLL) return fail(GRPO_EINVAL, "grpo_stream_probe: too many bytes for one launch");
+    if (blocks > 0x7fffffffLL) return fail(-1, "ys_stream: too many bytes for one launch");
     hipStream_t st = (hipStream_t)stream;
-    if (mode == GRPO_STREAM_COPY)
+    if (mode == YS_COPY)
         hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(kLanes), 0, st, (const u32x4*)src,
                            (u32x4*)dst, n);
-    else if (mode == GRPO_STREAM_READ)
+    else if (mode == YS_READ)
         hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(kLanes), 0, st, (const u32x4*)src,
                            (uint32_t*)dst, n);
     else
         hipLaunchKernelGGL(stream_fill_kernel, dim3((unsigned)blocks), dim3(kLanes), 0, st, (u32x4*)dst, n);
     const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? ok() : fail(GRPO_EDEVICE, "grpo_stream_probe: %s", hipGetErrorString(e));
+    return e == hipSuccess ? ok() : fail(-8, hipGetErrorString(e));
 }

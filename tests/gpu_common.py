@@ -2,11 +2,17 @@
 seeded generators, run the oracle on the same values, and compare within the
 stated tolerances.
 
-Tolerances (the target's):
+Tolerances (the target's), applied token by token:
   * token log-prob: abs <= 1e-5 for fp32 logits, <= 2e-3 for bf16 logits;
-  * loss: |dL| <= 1e-4 * max(|L|, sum|l_t| / N) (relative, guarded near 0);
-  * dlogits: relative L2 <= 1e-3 against the oracle rounded once to the
-    output dtype (bf16 storage alone is ~1.7e-3 off float64);
+  * loss: |dl_t| <= 1e-4 |l_t| per token, and for a chunk's sum
+    |dL| <= 1e-4 * max(|L|, sum|l_t| / N) (relative, guarded near 0);
+  * dlogits, per token: every element within one bf16 ulp of the oracle
+    rounded once to bf16 (bf16 output; bf16 storage alone is ~1.7e-3 off
+    float64) or within 1e-5 relative (fp32 output), absolute floor at the
+    fp32 normal minimum, plus the float32 cancellation allowance of elements
+    that are differences; the non-target elements no further from the exact
+    row than the once-rounded oracle plus 1e-3 of the row's norm
+    (check_dz_rows);
   * entropy (no stated bound): abs <= 1e-4 + 1e-5 * H, from fp32 sums over V;
   * plans, counts, flags: exact.
 """
@@ -84,49 +90,177 @@ def run_gpu(d, scale=1.0, denom=None, eps=(0.2, 0.2), dlogits="new", out_dtype=N
                             dlogits=dlogits, out_dtype=out_dtype)
 
 
-def assert_tokens_match(ws, ref, d, idx=None, check_dz=True, eps=(0.2, 0.2)):
-    """Per-token outputs and dlogits vs the oracle (``idx``: token subset).
+FP32_NORMAL_MIN = 2.0 ** -126
 
-    The clip decision is a float comparison taken in float32 by the kernel
-    and in float64 by the oracle; a token whose ratio lies within 1e-4
-    (relative) of a clip edge may fall either way.  Such tokens, when the two
-    sides disagree, are left out of the flag and dlogits comparisons (their
-    loss is continuous across the edge and stays in); any other disagreement
-    fails."""
-    sel_np = np.arange(d["z64"].shape[0]) if idx is None else np.asarray(idx)
-    sel = torch.as_tensor(sel_np, device=DEV)
-    dtype = d["dtype"]
+
+def bf16_ulp(x):
+    """Spacing of the bf16 grid at |x| (8 significant bits): 2^(e-7) for
+    2^e <= |x| < 2^(e+1); 2^-133 in the subnormal range."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(ax)                       # ax = m 2^e, 0.5 <= m < 1
+    return np.exp2(np.maximum(e - 8, -133).astype(np.float64))
+
+
+def check_dz_rows(dz, want, target, valid, check, out_bf16, coef, mag=None, extra=None, label=""):
+    """dlogits rows of the compared tokens against the oracle, token by token.
+
+    ``dz``: the kernel's rows (float64 [n, V]); ``want``: the oracle's exact
+    rows; ``check``: tokens whose values are compared (valid, finite, and with
+    the same clip decision on both sides).  Masked tokens must be exactly zero.
+
+    Per element: within one bf16 ulp of the oracle rounded once to bf16 (bf16
+    output), or within 1e-5 relative (fp32 output), with an absolute floor at
+    the fp32 normal minimum.  Where an element is a difference of larger
+    summands, 1e-5 of the summands' magnitude ``mag`` is added (the float32
+    cancellation error): by default ``mag`` = |dz_v| + |coef| [v = y] (the
+    target element coef (p_y - 1)); with extra terms the caller passes it
+    (KL: coef itself is a difference; entropy bonus: p_v (z_v - lse + H)).
+    ``extra`` (absolute, per element) carries what an input error does to the
+    element: with a KL term, the kernel's log-prob error moves coef through
+    dKL/dlogp, and the caller passes that movement times (p_v + [v = y]).
+
+    Per token, over the non-target elements (the target element carries most
+    of a row's norm): the distance of the kernel's row to the exact row is at
+    most that of the exact row rounded once to the output dtype, plus 1e-3 of
+    the row's norm.  (A 1-ulp disagreement on one dominant element of a short
+    row is an unavoidable consequence of rounding a float32 result that lies
+    within 1e-6 of a rounding midpoint; it leaves the row as close to the
+    exact one as the once-rounded oracle.)"""
+    n, V = dz.shape
+    assert not dz[~valid].any(), f"{label}: a masked token has a non-zero dlogits row"
+    if not check.any():
+        return
+    got = dz[check]
+    exact = want[check]
+    tg = np.asarray(target)[check].astype(np.int64)
+    inr = (tg >= 0) & (tg < V)
+    if mag is None:
+        m = np.abs(exact)
+        m[np.nonzero(inr)[0], tg[inr]] += np.abs(np.asarray(coef, np.float64)[check][inr])
+    else:
+        m = mag[check]
+    if out_bf16:
+        ref = oracle.round_to_bf16(exact)
+        bound = np.maximum(bf16_ulp(ref), FP32_NORMAL_MIN) + 1e-5 * m
+    else:
+        ref = exact
+        bound = 1e-5 * np.maximum(m, np.abs(ref)) + FP32_NORMAL_MIN
+    if extra is not None:
+        bound = bound + extra[check]
+    err = np.abs(got - ref)
+    bad = err > bound
+    if bad.any():
+        t, v = np.argwhere(bad)[0]
+        tok = np.nonzero(check)[0][t]
+        raise AssertionError(f"{label}: {int(bad.sum())} elements outside the bound; first token {tok} v {v}: "
+                             f"got {got[t, v]!r} want {ref[t, v]!r} bound {bound[t, v]!r}")
+    off = np.ones_like(got, dtype=bool)
+    off[np.nonzero(inr)[0], tg[inr]] = False
+    norm = lambda x: np.sqrt(np.sum(np.where(off, x * x, 0.0), axis=1))  # noqa: E731
+    excess = norm(got - exact) - norm(ref - exact) - 1e-3 * norm(exact)
+    worst = int(np.argmax(excess))
+    assert excess[worst] <= 0.0, (f"{label}: token {np.nonzero(check)[0][worst]}: non-target distance to the exact "
+                                  f"row exceeds the once-rounded oracle's by {excess[worst]!r} beyond 1e-3 of its norm")
+
+
+def check_tokens(out, ref, idx, old_np, in_dtype, dz_rows=None, eps=(0.2, 0.2), logp_tol=None, label="",
+                 mag=None, extra=None):
+    """Per-token outputs (dict of full-length GPU tensors) at token indices
+    ``idx`` against the oracle dict ``ref`` (arrays over ``idx``), one token at
+    a time:
+
+    * flags: valid and non-finite exactly; the clip decision exactly except
+      where the ratio lies within 1e-4 (relative) of a clip edge, since the
+      kernel decides in float32 and the oracle in float64 -- such tokens may
+      fall either way and are then left out of the dlogits comparison (their
+      loss is continuous across the edge and stays in);
+    * logp: abs <= 1e-5 (fp32 logits) / 2e-3 (bf16 logits); entropy:
+      abs <= 1e-4 + 1e-5 H; loss: |dl_t| <= 1e-4 |l_t| (the relative bound with
+      the near-zero guard of a single token); masked tokens: all zeros;
+    * dlogits rows (``dz_rows``, the kernel's rows at ``idx``): check_dz_rows.
+
+    Returns the number of clip-edge tokens whose decision differed."""
+    idx = np.asarray(idx)
+    ii = torch.as_tensor(idx, device=DEV)
+    tol = logp_tol if logp_tol is not None else tol_logp(in_dtype)
     valid = ref["valid"]
-    logp = to_f64(ws["logp"][sel])
-    ent = to_f64(ws["entropy"][sel])
-    lt = to_f64(ws["loss_tok"][sel])
-    flags = ws["tok_flags"][sel].cpu().numpy()
-    assert np.array_equal((flags & 1).astype(bool), valid)
-    assert np.array_equal(((flags >> 2) & 1).astype(bool), ref["nonfinite"])
+    flags = out["tok_flags"][ii].cpu().numpy()
+    assert np.array_equal((flags & 1).astype(bool), valid), label
+    assert np.array_equal(((flags >> 2) & 1).astype(bool), ref["nonfinite"]), label
     fin = valid & ~ref["nonfinite"]
+    logp = to_f64(out["logp"][ii])
+    ent = to_f64(out["entropy"][ii])
+    lt = to_f64(out["loss_tok"][ii])
+    d_logp = np.abs(logp[fin] - ref["logp"][fin])
+    assert np.all(d_logp <= tol), (label, float(np.max(d_logp)))
+    d_ent = np.abs(ent[fin] - ref["entropy"][fin])
+    assert np.all(d_ent <= 1e-4 + 1e-5 * np.abs(ref["entropy"][fin])), (label, float(np.max(d_ent)))
+    d_l = np.abs(lt[fin] - ref["loss_tok"][fin])
+    assert np.all(d_l <= 1e-4 * np.abs(ref["loss_tok"][fin])), (label, float(np.max(d_l - 1e-4 * np.abs(
+        ref["loss_tok"][fin]))))
+    assert not logp[~valid].any() and not lt[~valid].any() and not ent[~valid].any(), label
     with np.errstate(over="ignore", invalid="ignore"):
-        rho = np.exp(ref["logp"] - d["old"].astype(np.float64)[sel_np])
+        rho = np.exp(ref["logp"] - np.asarray(old_np, np.float64))
     hi, lo = 1.0 + eps[1], 1.0 - eps[0]
     edge = fin & ((np.abs(rho - hi) <= 1e-4 * hi) | (np.abs(rho - lo) <= 1e-4))
     gclip = ((flags >> 1) & 1).astype(bool)
     differ = gclip != (ref["clipped"] & valid)
-    assert not np.any(differ & ~edge), np.nonzero(differ & ~edge)
-    keep = ~differ
-    assert np.all(np.abs(logp[fin] - ref["logp"][fin]) <= tol_logp(dtype)), np.max(np.abs(logp[fin] - ref["logp"][fin]))
-    assert np.all(np.abs(ent[fin] - ref["entropy"][fin]) <= 1e-4 + 1e-5 * np.abs(ref["entropy"][fin]))
-    assert np.all(logp[~valid] == 0) and np.all(lt[~valid] == 0) and np.all(ent[~valid] == 0)
-    # loss (as a sum over the chunk): |dL| <= 1e-4 * max(|L|, sum |l_t|)
+    assert not np.any(differ & ~edge), (label, np.nonzero(differ & ~edge))
+    if dz_rows is not None:
+        want = ref["dz"]
+        check_dz_rows(to_f64(dz_rows), want, ref["_target"], valid, fin & ~differ, dz_rows.dtype == torch.bfloat16,
+                      ref["coef"], mag=mag, extra=extra, label=label)
+    return int(differ.sum())
+
+
+def summand_magnitude(z64, ref, target, coef_mag, s_tok=None, ent_coef=0.0):
+    """Magnitude of the summands that form each dz element (float64 [n, V]):
+    coef_mag_t (p_v + [v = y]) plus, with an entropy bonus,
+    |ent_coef s_t| p_v (|z_v - lse| + H).  ``coef_mag``: per token, the summed
+    magnitudes of the terms of coef (|s A rho g| + |s kl_coef dKL/dlogp|)."""
+    lse = ref["lse"][:, None]
+    n, V = z64.shape
+    with np.errstate(invalid="ignore", over="ignore"):
+        fin = np.isfinite(z64)
+        p = np.where(fin, np.exp(np.where(fin, z64, 0.0) - lse), 0.0)
+        mag = np.asarray(coef_mag, np.float64)[:, None] * p
+        tg = np.asarray(target).astype(np.int64)
+        inr = (tg >= 0) & (tg < V)
+        mag[np.nonzero(inr)[0], tg[inr]] += np.asarray(coef_mag, np.float64)[inr]
+        if ent_coef:
+            mag += np.abs(ent_coef * np.asarray(s_tok, np.float64))[:, None] * p * (
+                np.where(fin, np.abs(np.where(fin, z64, 0.0) - lse), 0.0) + np.abs(ref["entropy"])[:, None])
+    mag[~ref["valid"]] = 0.0
+    return mag
+
+
+def assert_tokens_match(ws, ref, d, idx=None, check_dz=True, eps=(0.2, 0.2), coef_mag=None, s_tok=None,
+                        ent_coef=0.0, coef_err=None):
+    """Per-token outputs and dlogits of a chunk (``make_chunk``) vs the oracle,
+    token by token (``idx``: a token subset); see check_tokens.  With extra
+    terms, ``coef_mag`` is each token's |s A rho g| + |s kl_coef dKL/dlogp|,
+    ``s_tok`` its factor, ``ent_coef`` the entropy-bonus weight and
+    ``coef_err`` the movement of coef that the kernel's log-prob error
+    causes (per token)."""
+    sel = np.arange(d["z64"].shape[0]) if idx is None else np.asarray(idx)
+    ref = dict(ref, _target=d["target"][sel])
+    dz = ws.get("dlogits") if check_dz else None
+    dz_rows = dz[torch.as_tensor(sel, device=DEV)] if dz is not None else None
+    mag = extra = None
+    if dz_rows is not None and (coef_mag is not None or ent_coef):
+        cm = np.abs(ref["coef"]) if coef_mag is None else np.asarray(coef_mag)[sel]
+        mag = summand_magnitude(d["z64"][sel], ref, d["target"][sel], cm, None if s_tok is None else
+                                np.asarray(s_tok)[sel], ent_coef)
+    if dz_rows is not None and coef_err is not None:
+        extra = summand_magnitude(d["z64"][sel], ref, d["target"][sel], np.asarray(coef_err)[sel])
+    differ = check_tokens(ws, ref, sel, d["old"][sel], d["dtype"], dz_rows=dz_rows, eps=eps, mag=mag, extra=extra)
+    # the chunk's loss as a sum, with the guarded relative bound
+    fin = ref["valid"] & ~ref["nonfinite"]
+    lt = to_f64(ws["loss_tok"][torch.as_tensor(sel, device=DEV)])
     L_ref = float(np.sum(ref["loss_tok"][fin]))
     bound = 1e-4 * max(abs(L_ref), float(np.sum(np.abs(ref["loss_tok"][fin]))))
     assert abs(float(np.sum(lt[fin])) - L_ref) <= max(bound, 1e-12)
-    if check_dz and ws.get("dlogits") is not None:
-        dz = to_f64(ws["dlogits"][sel])[keep]
-        want = ref["dz"][keep]
-        if ws["dlogits"].dtype == torch.bfloat16:
-            want = oracle.round_to_bf16(want)
-        assert rel_l2(dz, want) <= 1e-3, rel_l2(dz, want)
-        assert not dz[~valid[keep]].any()
-    return int(differ.sum())
+    return differ
 
 
 def torch_logp(logits, target, block=512):
@@ -164,34 +298,15 @@ def oracle_tokens(logits, target, mask, old, adv_tok, scale, idx, eps=(0.2, 0.2)
                                scale, eps[0], eps[1])
 
 
-def compare_sampled(out, ref, idx, old_np, dtype, dz_rows=None, eps=(0.2, 0.2)):
+def compare_sampled(out, ref, idx, old_np, dtype, dz_rows=None, eps=(0.2, 0.2), target=None, logp_tol=None):
     """Per-token outputs (dicts of full-length GPU tensors) at ``idx`` vs the
-    oracle dict ``ref``; ``dz_rows``: the kernel's dlogits rows at ``idx``."""
-    ii = torch.as_tensor(np.asarray(idx), device=DEV)
-    valid = ref["valid"]
-    flags = out["tok_flags"][ii].cpu().numpy()
-    assert np.array_equal((flags & 1).astype(bool), valid)
-    fin = valid & ~ref["nonfinite"]
-    logp = to_f64(out["logp"][ii])
-    assert np.all(np.abs(logp[fin] - ref["logp"][fin]) <= tol_logp(dtype)), np.max(np.abs(logp[fin] - ref["logp"][fin]))
-    ent = to_f64(out["entropy"][ii])
-    assert np.all(np.abs(ent[fin] - ref["entropy"][fin]) <= 1e-4 + 1e-5 * np.abs(ref["entropy"][fin]))
-    lt = to_f64(out["loss_tok"][ii])
-    assert np.all(np.abs(lt[fin] - ref["loss_tok"][fin]) <= 1e-4 * np.maximum(np.abs(ref["loss_tok"][fin]), 1e-3))
-    with np.errstate(over="ignore", invalid="ignore"):
-        rho = np.exp(ref["logp"] - old_np)
-    hi, lo = 1.0 + eps[1], 1.0 - eps[0]
-    edge = fin & ((np.abs(rho - hi) <= 1e-4 * hi) | (np.abs(rho - lo) <= 1e-4))
-    differ = ((flags >> 1) & 1).astype(bool) != (ref["clipped"] & valid)
-    assert not np.any(differ & ~edge)
-    if dz_rows is not None:
-        keep = ~differ
-        dz = to_f64(dz_rows)[keep]
-        want = ref["dz"][keep]
-        if dz_rows.dtype == torch.bfloat16:
-            want = oracle.round_to_bf16(want)
-        assert rel_l2(dz, want) <= 1e-3, rel_l2(dz, want)
-        assert not dz[~valid[keep]].any()
+    oracle dict ``ref``; ``dz_rows``: the kernel's dlogits rows at ``idx``
+    (``target``: the targets at ``idx``, needed with dz_rows).  See
+    check_tokens."""
+    if dz_rows is not None and target is None:
+        raise ValueError("compare_sampled: the targets at idx are needed to compare dlogits rows")
+    ref = dict(ref, _target=np.asarray(target) if target is not None else None)
+    return check_tokens(out, ref, idx, old_np, dtype, dz_rows=dz_rows, eps=eps, logp_tol=logp_tol)
 
 
 def sample_tokens(mask_np, row_len, n_valid=24, n_masked=8, seed=0):

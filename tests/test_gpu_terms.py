@@ -4,7 +4,10 @@ row-weight kernels, the fused loss on both kernel paths and dtypes, the
 LM-head variant, chunk invariance of the seq-level modes, and the identity
 of the plain path when the terms are off.
 
-Tolerances as for the fused loss; KL per token abs <= 1e-5 (fp32 logits)
+Tolerances as for the fused loss, with two allowances in the dlogits
+element bound: the float32 cancellation between the terms that form an
+element, and the movement of coef that the kernel's log-prob error causes
+through the ratio and dKL/dlogp; KL per token abs <= 1e-5 (fp32 logits)
 or 2e-4 (bf16: the log-prob error times |dKL/dlogp| <= ~0.5 here); row
 weights relative 2^-23 (one float32 rounding of 1/(B L)); objective and KL
 sums relative 1e-4 of the sum of magnitudes."""
@@ -47,6 +50,41 @@ def _oracle_terms(d, mode, ent, kap, kind, scale):
     return oracle.loss_fwd_bwd(d["z64"], d["target"], d["mask"], d["old"].astype(np.float64), adv_tok, scale,
                                w_tok=w_tok, ent_coef=ent, kl_coef=kap, ref_logp=d["ref"].astype(np.float64),
                                kl_type=kind)
+
+
+def _s_tok(d, mode, scale):
+    """Each token's factor: scale times its row's aggregation weight."""
+    off = d["row_off"].tolist()
+    B = oracle.count_rows(d["mask"], off)
+    return scale * np.repeat(np.asarray(oracle.row_weights(d["mask"], off, mode, B), np.float64), np.diff(off))
+
+
+def _coef_mag(d, ref, mode, scale, kap, kind):
+    """|s A rho g| + |s kl_coef dKL/dlogp| per token: the two terms of coef,
+    whose float32 difference the dz bound allows for."""
+    s = _s_tok(d, mode, scale)
+    A = d["adv_row"].astype(np.float64)[d["tok_row"]]
+    with np.errstate(over="ignore", invalid="ignore"):
+        rho = np.where(ref["valid"], np.exp(ref["logp"] - d["old"].astype(np.float64)), 0.0)
+    g = np.where(ref["clipped"], 0.0, 1.0)
+    dkl = np.array([oracle.kl_term(lp, r, kind)[1] for lp, r in zip(ref["logp"], d["ref"].astype(np.float64))])
+    return np.abs(s) * (np.abs(A * rho * g) + np.abs(kap * dkl))
+
+
+def _coef_err(d, ref, ws, mode, scale, kap, kind):
+    """How far coef moves when logp carries the kernel's own log-prob error
+    (measured per token, which the logp bound limits): |d coef / d logp| =
+    |s| (|A rho g| + |kl_coef d2KL/dlogp2|) with d2KL/dlogp2 = 0, 1, e^d for
+    k1, k2, k3 (d = ref - logp), times that error plus float32 rounding."""
+    s = _s_tok(d, mode, scale)
+    A = d["adv_row"].astype(np.float64)[d["tok_row"]]
+    with np.errstate(over="ignore", invalid="ignore"):
+        rho = np.where(ref["valid"], np.exp(ref["logp"] - d["old"].astype(np.float64)), 0.0)
+        dd = d["ref"].astype(np.float64) - ref["logp"]
+        k2 = {KL_K1: 0.0 * dd, KL_K2: np.ones_like(dd), KL_K3: np.exp(dd)}[kind]
+    g = np.where(ref["clipped"], 0.0, 1.0)
+    dlogp = np.abs(to_f64(ws["logp"]) - ref["logp"]) + 2.0 ** -20 * (1.0 + np.abs(ref["logp"]))
+    return np.where(ref["valid"], np.abs(s) * (np.abs(A * rho * g) + np.abs(kap * k2)) * dlogp, 0.0)
 
 
 def _check_stats(ws, ref, d):
@@ -104,7 +142,8 @@ def test_terms_match_oracle(dtype, out_dtype, mode, ent, kap, kind):
                           kl_coef=kap, kl_type=kind)
     torch.cuda.synchronize()
     ref = _oracle_terms(d, mode, ent, kap, kind, scale)
-    assert_tokens_match(ws, ref, d)
+    assert_tokens_match(ws, ref, d, coef_mag=_coef_mag(d, ref, mode, scale, kap, kind), s_tok=_s_tok(d, mode, scale),
+                        ent_coef=ent, coef_err=_coef_err(d, ref, ws, mode, scale, kap, kind))
     valid = ref["valid"]
     kl = to_f64(ws["kl_tok"])
     tol = 1e-5 if dtype == torch.float32 else 2e-4
@@ -123,7 +162,9 @@ def test_terms_on_the_generic_path():
                           kl_coef=0.1, kl_type=KL_K3)
     torch.cuda.synchronize()
     ref = _oracle_terms(d, AGG_SEQ_MEAN_TOKEN_MEAN, 0.03, 0.1, KL_K3, 1.0)
-    assert_tokens_match(ws, ref, d)
+    assert_tokens_match(ws, ref, d, coef_mag=_coef_mag(d, ref, AGG_SEQ_MEAN_TOKEN_MEAN, 1.0, 0.1, KL_K3),
+                        s_tok=_s_tok(d, AGG_SEQ_MEAN_TOKEN_MEAN, 1.0), ent_coef=0.03,
+                        coef_err=_coef_err(d, ref, ws, AGG_SEQ_MEAN_TOKEN_MEAN, 1.0, 0.1, KL_K3))
     _check_stats(ws, ref, d)
 
 
@@ -138,7 +179,9 @@ def test_full_vocabulary_with_terms(V):
                           scale=1.0, row_weight=w, ref_logp=g["ref"], ent_coef=0.01, kl_coef=0.05, kl_type=KL_K3)
     torch.cuda.synchronize()
     ref = _oracle_terms(d, AGG_SEQ_MEAN_TOKEN_SUM, 0.01, 0.05, KL_K3, 1.0)
-    assert_tokens_match(ws, ref, d)
+    assert_tokens_match(ws, ref, d, coef_mag=_coef_mag(d, ref, AGG_SEQ_MEAN_TOKEN_SUM, 1.0, 0.05, KL_K3),
+                        s_tok=_s_tok(d, AGG_SEQ_MEAN_TOKEN_SUM, 1.0), ent_coef=0.01,
+                        coef_err=_coef_err(d, ref, ws, AGG_SEQ_MEAN_TOKEN_SUM, 1.0, 0.05, KL_K3))
     _check_stats(ws, ref, d)
 
 

@@ -1,14 +1,24 @@
 """GPU parity on the pages' workload shapes, through the C ABI:
 
 * tiny   : the whole 2 x 2 step (plans, N per mini-batch, advantages, four
-           fused launches, accumulator) against the oracle, every token;
-* qwen   : one full step in the launch configuration bench.py times, checked
-           on sampled tokens one by one plus size-independent properties;
-* long   : micro-chunked (16 x 4 rows) == un-chunked (64 rows), bit for bit,
-           at full size;
+           fused launches, accumulator) against the oracle, every token and
+           every dlogits element;
+* qwen   : one full step in the launch configuration bench.py times; every
+           valid token's log-prob, entropy, loss and flags against the oracle
+           (a pool of CPU processes), dlogits of 256 sampled valid tokens
+           element by element, every masked row exactly zero;
+* long   : the whole 128-row batch; mini-batch 0 micro-chunked (16 x 4 rows)
+           == un-chunked (64 rows), bit for bit; every token against the
+           oracle, dlogits of 256 sampled tokens;
 * dynamic: token-budget packing restored to the original order == fixed
-           8-row micro-batches, bit for bit, at full size (in-place dlogits),
-           plus a small instance checked against the oracle on every token.
+           8-row micro-batches, bit for bit, at full size (in-place dlogits);
+           every token against the oracle, dlogits of 256 sampled tokens; a
+           small instance checked on every element;
+* pages  : the pages' own 256-sequence x 2048-token batch at group 8 (P1
+           "Prerequisite: reproducibility": it does not fit un-chunked, and
+           completes micro-batched), in place (159 GB of bf16 logits), mini 64
+           / micro 4: chunked == un-chunked on mini-batch 0 bit for bit,
+           sampled tokens against the oracle.
 """
 
 import gc
@@ -18,9 +28,9 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import (DEV, compare_sampled, oracle_tokens, padded_on_gpu, rel_l2, sample_tokens, to_f64,
-                        torch_logp)
+from gpu_common import (DEV, compare_sampled, oracle_tokens, padded_on_gpu, sample_tokens, to_f64, torch_logp)
 from grpo_token_level_amd import ops
+from oracle_pool import OraclePool
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +38,10 @@ pytestmark = pytest.mark.gpu
 def _free():
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def _say(msg):
+    print(msg, flush=True)
 
 
 def _outputs(n_tok, n_rows):
@@ -75,10 +89,46 @@ def _padded_step(b, logits, target, mask, old, dlogits):
                 chunk_stats=ops.stats_to_dicts(stats))
 
 
+def _every_token(P, out, logits, target_np, mask_np, old, adv_tok, scale_tok, dtype, label):
+    """Every valid token's forward outputs against the oracle (run on the pool
+    over the logits as they are now), and every masked token's outputs zero.
+    ``scale_tok``: the gradient factor of each token (1/N of its mini-batch)."""
+    idx = np.nonzero(mask_np)[0]
+    old_np = old.double().cpu().numpy()
+    _say(f"{label}: oracle over {len(idx)} valid tokens on {P.n} processes")
+    ref = {}
+    for s in np.unique(scale_tok[idx]):
+        part = idx[scale_tok[idx] == s]
+        r = P.forward(logits, part, target_np[part], mask_np[part], old_np[part], adv_tok[part], float(s))
+        for k, v in r.items():
+            ref.setdefault(k, np.zeros(len(idx), v.dtype))[np.searchsorted(idx, part)] = v
+    compare_sampled(out, ref, idx, old_np[idx], dtype)
+    m = torch.from_numpy(mask_np == 0).to(DEV)
+    for k in ("logp", "entropy", "loss_tok", "tok_flags"):
+        assert not out[k][m].any(), f"{label}: {k} non-zero on a masked token"
+    _say(f"{label}: every token matches")
+
+
+def _masked_rows_zero(dl, mask, label, block=4096):
+    bad = torch.zeros((), dtype=torch.bool, device=DEV)
+    for a in range(0, dl.shape[0], block):
+        e = min(a + block, dl.shape[0])
+        m = mask[a:e] == 0
+        if bool(m.any()):
+            bad |= (dl[a:e][m] != 0).any()
+    assert not bool(bad), f"{label}: a masked token has a non-zero dlogits row"
+
+
+def _dz_sample(mask_np, n, seed):
+    rng = np.random.default_rng(seed)
+    v = np.nonzero(mask_np)[0]
+    return np.sort(rng.choice(v, size=min(n, len(v)), replace=False))
+
+
 # ------------------------------------------------------------------ tiny: every token
 
 def test_tiny_step_end_to_end():
-    print("tiny workload end to end", flush=True)
+    _say("tiny workload end to end")
     b, logits, target, mask, old = padded_on_gpu("tiny", seed=0)
     dl = torch.empty_like(logits)
     r = _padded_step(b, logits, target, mask, old, dl)
@@ -101,7 +151,8 @@ def test_tiny_step_end_to_end():
             t = slice(a * T, e * T)
             ref = oracle.loss_fwd_bwd(z64[t], b["target"][t], b["mask"][t], old64[t], adv_tok[t], 1.0 / max(N, 1))
             idx = np.arange(a * T, e * T)
-            compare_sampled(r["out"], ref, idx, old64[t], torch.float32, dz_rows=dl[a * T:e * T])
+            compare_sampled(r["out"], ref, idx, old64[t], torch.float32, dz_rows=dl[a * T:e * T],
+                            target=b["target"][t])
             ost = oracle.chunk_stats(ref, list(range(0, (e - a) * T + 1, T)))
             gst = r["chunk_stats"][k]
             assert gst["n_valid"] == ost["n_valid"] and gst["n_valid_rows"] == ost["n_valid_rows"]
@@ -115,10 +166,11 @@ def test_tiny_step_end_to_end():
     _free()
 
 
-# ------------------------------------------------------------------ qwen: the benched step
+# ------------------------------------------------------------------ qwen: the benched step, every token
 
-def test_qwen_step_sampled_and_properties():
-    print("qwen workload full step", flush=True)
+@pytest.mark.timeout(900)
+def test_qwen_step_every_token():
+    _say("qwen workload full step")
     b, logits, target, mask, old = padded_on_gpu("qwen", seed=0)
     dl = torch.empty_like(logits)
     r = _padded_step(b, logits, target, mask, old, dl)
@@ -128,25 +180,17 @@ def test_qwen_step_sampled_and_properties():
     assert sum(s["n_valid"] for s in r["chunk_stats"]) == N
     rows = ops.stats_to_dicts(r["out"]["row_stats"])
     assert [x["n_valid"] for x in rows] == b["lengths"].tolist()
-    # sampled tokens one by one against the oracle
-    idx = sample_tokens(b["mask"], [T] * n_rows, n_valid=40, n_masked=10, seed=1)
     adv_tok = np.repeat(r["adv"].astype(np.float64), T)
+    with OraclePool() as P:
+        _every_token(P, r["out"], logits, b["target"], b["mask"], old, adv_tok, np.full(n_rows * T, 1.0 / N),
+                     torch.bfloat16, "qwen")
+    # dlogits of 256 valid tokens and 16 masked ones, element by element
+    idx = np.union1d(_dz_sample(b["mask"], 256, 1), sample_tokens(b["mask"], [T] * n_rows, 0, 16, seed=1))
     ref = oracle_tokens(logits, target, mask, old, adv_tok, 1.0 / N, idx)
-    compare_sampled(r["out"], ref, idx, old[torch.as_tensor(idx, device=DEV)].double().cpu().numpy(),
-                    torch.bfloat16, dz_rows=dl[torch.as_tensor(idx, device=DEV)])
-    # at every token: sum_v dz_v = 0 up to bf16 storage (|err| <= ~2^-8 |coef|),
-    # masked rows are exactly zero
-    coef_bound = torch.zeros(n_rows * T, dtype=torch.float32, device=DEV)
-    masked_nonzero = torch.zeros((), dtype=torch.bool, device=DEV)
-    for a in range(0, n_rows * T, 4096):
-        e = min(a + 4096, n_rows * T)
-        blk = dl[a:e].float()
-        s = blk.sum(dim=1)
-        amax = blk.abs().amax(dim=1)
-        coef_bound[a:e] = (s.abs() - 5e-3 * amax)
-        masked_nonzero |= ((amax > 0) & (mask[a:e] == 0)).any()
-    assert float(coef_bound.max()) <= 1e-9
-    assert not bool(masked_nonzero)
+    ii = torch.as_tensor(idx, device=DEV)
+    compare_sampled(r["out"], ref, idx, old[ii].double().cpu().numpy(), torch.bfloat16, dz_rows=dl[ii],
+                    target=b["target"][idx])
+    _masked_rows_zero(dl, mask, "qwen")
     # step loss: token-weighted roll-up equals the sum of per-row partials / N
     acc = ops.Accumulator(r["plan"][1])
     for s in r["chunk_stats"]:
@@ -157,46 +201,66 @@ def test_qwen_step_sampled_and_properties():
     _free()
 
 
-# ------------------------------------------------------------------ long: chunked == un-chunked
+# ------------------------------------------------------------------ long: chunked == un-chunked, every token
 
-def test_long_chunked_equals_unchunked_full_size():
-    print("long workload: one mini-batch chunked vs un-chunked", flush=True)
-    b, logits, target, mask, old = padded_on_gpu("long", seed=0, n_prompts=8)   # the first mini-batch: 64 rows
+@pytest.mark.timeout(900)
+def test_long_full_size_chunked_equals_unchunked_every_token():
+    _say("long workload: 128 rows, mini-batch 0 chunked vs un-chunked")
+    b, logits, target, mask, old = padded_on_gpu("long", seed=0)
     T, n_rows = b["T"], b["n_rows"]
-    assert n_rows == 64
+    assert n_rows == 128
+    n_mini, n_micro, mini_rows, micro_rows = ops.plan_fixed(n_rows, b["group"], b["mini"], b["micro"])
+    assert (n_mini, n_micro, micro_rows) == (2, 16, 4)
     adv = torch.from_numpy(ops.group_advantage(b["reward"], b["group"])).to(DEV)
-    N = ops.count_valid(mask)
-    assert int(N.item()) == n_rows * T
-    whole = _outputs(n_rows * T, n_rows)
-    dl_whole = torch.empty_like(logits)
-    cs = torch.empty((17, ops.STATS_BYTES), dtype=torch.uint8, device=DEV)
-    _run_chunk(logits, target, mask, old, adv, whole, 0, n_rows * T, 0, [T] * n_rows, N, dl_whole, cs[16:17])
+    half = mini_rows * T
+    Ns = [ops.count_valid(mask[i * half:(i + 1) * half]) for i in range(n_mini)]
+    assert [int(x.item()) for x in Ns] == [half, half]
+    # mini-batch 0 as one call of 64 rows
+    whole = _outputs(half, mini_rows)
+    dl_whole = torch.empty((half, b["V"]), dtype=logits.dtype, device=DEV)
+    cs = torch.empty((n_mini * n_micro + 1, ops.STATS_BYTES), dtype=torch.uint8, device=DEV)
+    _run_chunk(logits, target, mask, old, adv, whole, 0, half, 0, [T] * mini_rows, Ns[0], dl_whole, cs[-1:])
+    # the whole step in micro-chunks (mini-batch 1's dlogits reuse one buffer)
     parts = _outputs(n_rows * T, n_rows)
-    dl_parts = torch.empty_like(logits)
-    for c in range(16):
-        a, e = c * 4, (c + 1) * 4
-        _run_chunk(logits, target, mask, old, adv, parts, a * T, e * T, a, [T] * 4, N, dl_parts[a * T:e * T],
-                   cs[c:c + 1])
+    dl_parts = torch.empty((half, b["V"]), dtype=logits.dtype, device=DEV)
+    k = 0
+    for i in range(n_mini):
+        if i == 1:
+            torch.cuda.synchronize()
+            assert torch.equal(dl_parts, dl_whole)
+            _say("long: mini-batch 0 chunked == un-chunked, bit for bit")
+            sample0 = _dz_sample(np.ones(half, np.uint8), 128, 2)
+            dz0 = dl_parts[torch.as_tensor(sample0, device=DEV)].clone()
+        for j in range(n_micro):
+            a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
+            _run_chunk(logits, target, mask, old, adv, parts, a * T, e * T, a, [T] * (e - a), Ns[i],
+                       dl_parts[(a - i * mini_rows) * T:(e - i * mini_rows) * T], cs[k:k + 1])
+            k += 1
     torch.cuda.synchronize()
-    assert torch.equal(dl_parts, dl_whole)
-    for k in ("logp", "entropy", "loss_tok", "tok_flags", "row_stats"):
-        assert torch.equal(parts[k], whole[k]), k
+    for key in ("logp", "entropy", "loss_tok", "tok_flags"):
+        assert torch.equal(parts[key][:half], whole[key]), key
+    assert torch.equal(parts["row_stats"][:mini_rows], whole["row_stats"])
     st = ops.stats_to_dicts(cs)
-    assert sum(s["n_valid"] for s in st[:16]) == st[16]["n_valid"] == n_rows * T
-    assert sum(s["loss_sum"] for s in st[:16]) == pytest.approx(st[16]["loss_sum"], rel=1e-12)
-    # and the values themselves, on sampled tokens
-    idx = sample_tokens(b["mask"], [T] * n_rows, n_valid=24, n_masked=0, seed=2)
+    assert sum(s["n_valid"] for s in st[:n_micro]) == st[-1]["n_valid"] == half
+    assert sum(s["loss_sum"] for s in st[:n_micro]) == pytest.approx(st[-1]["loss_sum"], rel=1e-12)
     adv_tok = np.repeat(adv.cpu().numpy().astype(np.float64), T)
-    ref = oracle_tokens(logits, target, mask, old, adv_tok, 1.0 / (n_rows * T), idx)
-    compare_sampled(whole, ref, idx, old[torch.as_tensor(idx, device=DEV)].double().cpu().numpy(), torch.bfloat16,
-                    dz_rows=dl_whole[torch.as_tensor(idx, device=DEV)])
+    with OraclePool() as P:
+        _every_token(P, parts, logits, b["target"], b["mask"], old, adv_tok, np.full(n_rows * T, 1.0 / half),
+                     torch.bfloat16, "long")
+    # dlogits of 128 sampled tokens of each mini-batch, element by element
+    sample1 = _dz_sample(np.ones(half, np.uint8), 128, 3)
+    for i, (smp, rows) in enumerate(((sample0, dz0), (sample1, dl_parts[torch.as_tensor(sample1, device=DEV)]))):
+        idx = smp + i * half
+        ref = oracle_tokens(logits, target, mask, old, adv_tok, 1.0 / half, idx)
+        compare_sampled(parts, ref, idx, old[torch.as_tensor(idx, device=DEV)].double().cpu().numpy(),
+                        torch.bfloat16, dz_rows=rows, target=b["target"][idx])
     del logits, dl_whole, dl_parts
     _free()
 
 
 # ------------------------------------------------------------------ dynamic: restored == fixed micro
 
-def _dynamic_case(b, V, dtype, budget, proxy_div, fixed_micro, inplace, check_oracle_all, seed):
+def _dynamic_case(b, V, dtype, budget, proxy_div, fixed_micro, inplace, every_token, seed, P=None):
     from synth import fill_normal_rows
     L = b["lengths"].astype(np.int64)
     n_rows = len(L)
@@ -211,11 +275,8 @@ def _dynamic_case(b, V, dtype, budget, proxy_div, fixed_micro, inplace, check_or
     fill_normal_rows(logA, range(n_rows), offA[:-1], L, b["logit_std"], seed, "dynamic")
     old = (torch_logp(logA, target).double() + G(b["logratio_noise"])).float()
     N = ops.count_valid(mask)
-    # oracle inputs are copied out before any in-place update
-    if check_oracle_all:
-        idx = np.arange(n_tok)
-    else:
-        idx = sample_tokens(b["mask"], L, n_valid=24, n_masked=0, seed=seed)
+    # dlogits checks: the sampled tokens' logits are copied out before any in-place update
+    idx = np.arange(n_tok) if (every_token and P is None) else _dz_sample(b["mask"], 256, seed)
     ii = torch.as_tensor(idx, device=DEV)
     z_check = logA[ii].double().cpu().numpy()
     old_check = old[ii].double().cpu().numpy()
@@ -267,9 +328,17 @@ def _dynamic_case(b, V, dtype, budget, proxy_div, fixed_micro, inplace, check_or
     assert LA == LB
     adv_tok = np.repeat(adv.astype(np.float64), L)
     ref = oracle.loss_fwd_bwd(z_check, b["target"][idx], b["mask"][idx], old_check, adv_tok[idx], 1.0 / n_tok)
-    compare_sampled(outA, ref, idx, old_check, dtype, dz_rows=dlA[ii])
-    if check_oracle_all:
+    compare_sampled(outA, ref, idx, old_check, dtype, dz_rows=dlA[ii], target=b["target"][idx])
+    if every_token and P is None:
         assert LA == pytest.approx(float(np.sum(ref["loss_tok"])), rel=1e-4)
+    if every_token and P is not None:
+        if inplace:       # the logits buffer now holds dlogits: draw the same logits again
+            fill_normal_rows(logB, range(n_rows), offA[:-1], L, b["logit_std"], seed, "dynamic")
+            src = logB
+        else:
+            src = logA
+        _every_token(P, outA, src, b["target"], b["mask"], old, adv_tok, np.full(n_tok, 1.0 / n_tok), dtype,
+                     "dynamic")
     return plan, logA, logB
 
 
@@ -277,17 +346,86 @@ def test_dynamic_small_every_token_vs_oracle():
     from synth import dynamic_batch
     b = dynamic_batch(seed=3, n_rows=48, median=24, sigma=1.0, len_lo=2, len_hi=200, V=2048)
     plan, *_ = _dynamic_case(b, 2048, torch.float32, budget=256, proxy_div=64, fixed_micro=8, inplace=False,
-                             check_oracle_all=True, seed=3)
+                             every_token=True, seed=3)
     assert plan["n_bins"] >= 3
     _free()
 
 
-def test_dynamic_full_size_restored_equals_fixed_micro():
-    print("dynamic workload at full size (in place)", flush=True)
+@pytest.mark.timeout(900)
+def test_dynamic_full_size_restored_equals_fixed_micro_every_token():
+    _say("dynamic workload at full size (in place)")
     from synth import dynamic_batch
     b = dynamic_batch(seed=0)
-    plan, logA, logB = _dynamic_case(b, b["V"], torch.bfloat16, budget=b["budget"], proxy_div=b["proxy_div"],
-                                     fixed_micro=b["fixed_micro"], inplace=True, check_oracle_all=False, seed=0)
+    with OraclePool() as P:
+        plan, logA, logB = _dynamic_case(b, b["V"], torch.bfloat16, budget=b["budget"], proxy_div=b["proxy_div"],
+                                         fixed_micro=b["fixed_micro"], inplace=True, every_token=True, seed=0, P=P)
     assert plan["n_bins"] >= int(np.ceil(b["lengths"].sum() / b["budget"]))
     del logA, logB
+    _free()
+
+
+# ------------------------------------------------------------------ the pages' 256 x 2048 batch
+
+@pytest.mark.timeout(900)
+def test_pages_batch_256_by_2048_in_place():
+    """256 sequences x 2048 tokens at group 8, vocabulary 151936 bf16, updated
+    in place: 159 GB of logits, which an un-chunked log-softmax could not
+    hold beside its own float32 copy.  mini 64 rows (four optimizer steps),
+    micro 4 rows: 64 fused launches."""
+    from synth import fill_normal_rows, padded_batch
+    _say("pages batch: 256 x 2048 x 151936 bf16, in place")
+    b = padded_batch("long", seed=5, n_prompts=32)
+    n_rows, T, V = b["n_rows"], b["T"], b["V"]
+    assert (n_rows, T, b["group"]) == (256, 2048, 8)
+    n_tok = n_rows * T
+    logits = torch.empty((n_tok, V), dtype=torch.bfloat16, device=DEV)
+    fill_normal_rows(logits, range(n_rows), [r * T for r in range(n_rows)], [T] * n_rows, b["logit_std"], 5, "long")
+    G = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    target, mask = G(b["target"]), G(b["mask"])
+    old = (torch_logp(logits, target).double() + G(b["logratio_noise"])).float()
+    n_mini, n_micro, mini_rows, micro_rows = ops.plan_fixed(n_rows, b["group"], b["mini"], b["micro"])
+    assert (n_mini, n_micro, mini_rows, micro_rows) == (4, 16, 64, 4)
+    adv = G(ops.group_advantage(b["reward"], b["group"]))
+    half = mini_rows * T
+    # tokens checked against the oracle: logits copied out before the in-place update
+    idx = np.sort(np.concatenate([_dz_sample(np.ones(n_tok, np.uint8), 256, 6), [0, half - 1, half, n_tok - 1]]))
+    idx = np.unique(idx)
+    ii = torch.as_tensor(idx, device=DEV)
+    z_check = logits[ii].double().cpu().numpy()
+    out = _outputs(n_tok, n_rows)
+    stats = torch.empty((n_mini * n_micro, ops.STATS_BYTES), dtype=torch.uint8, device=DEV)
+    Ns = []
+    k = 0
+    for i in range(n_mini):
+        Ns.append(ops.count_valid(mask[i * half:(i + 1) * half]))
+        for j in range(n_micro):
+            a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
+            _run_chunk(logits, target, mask, old, adv, out, a * T, e * T, a, [T] * (e - a), Ns[i],
+                       logits[a * T:e * T], stats[k:k + 1])
+            k += 1
+    torch.cuda.synchronize()
+    _say("pages batch: 64 in-place launches done")
+    assert [int(x.item()) for x in Ns] == [half] * 4
+    st = ops.stats_to_dicts(stats)
+    assert sum(s["n_valid"] for s in st) == n_tok and sum(s["n_nonfinite"] for s in st) == 0
+    # mini-batch 0 un-chunked: the same rows drawn again, one launch of 64 rows, in place
+    again = torch.empty((half, V), dtype=torch.bfloat16, device=DEV)
+    fill_normal_rows(again, range(mini_rows), [r * T for r in range(mini_rows)], [T] * mini_rows, b["logit_std"], 5,
+                     "long")
+    whole = _outputs(half, mini_rows)
+    cs = torch.empty((1, ops.STATS_BYTES), dtype=torch.uint8, device=DEV)
+    _run_chunk(again, target, mask, old, adv, whole, 0, half, 0, [T] * mini_rows, Ns[0], again, cs)
+    torch.cuda.synchronize()
+    assert torch.equal(again, logits[:half])
+    for key in ("logp", "entropy", "loss_tok", "tok_flags"):
+        assert torch.equal(whole[key], out[key][:half]), key
+    assert sum(s["loss_sum"] for s in st[:n_micro]) == pytest.approx(ops.stats_to_dicts(cs)[0]["loss_sum"], rel=1e-12)
+    _say("pages batch: mini-batch 0 chunked == un-chunked, bit for bit")
+    del again
+    adv_tok = np.repeat(adv.cpu().numpy().astype(np.float64), T)
+    ref = oracle.loss_fwd_bwd(z_check, b["target"][idx], b["mask"][idx], old[ii].double().cpu().numpy(),
+                              adv_tok[idx], 1.0 / half)
+    compare_sampled(out, ref, idx, old[ii].double().cpu().numpy(), torch.bfloat16, dz_rows=logits[ii],
+                    target=b["target"][idx])
+    del logits
     _free()

@@ -107,6 +107,8 @@ class Probe(ctypes.Structure):
     _fields_ = [("bound", ctypes.c_double), ("max_fraction", ctypes.c_double), ("done", _i32), ("passed", _i32)]
 
 
+LMHEAD_NOALLOC_SCRATCH_BYTES = 256 << 20
+
 PROBE_STRICT_BOUND = 0.05
 PROBE_STRICT_FRACTION = 0.0
 
@@ -142,6 +144,7 @@ PROTOTYPES = {
     "grpo_transpose_bf16": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _i64]),
     "grpo_lmhead_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "grpo_lmhead_fwd_bwd": (ctypes.c_int, [_p, ctypes.POINTER(LmheadArgs)]),
+    "grpo_lmhead_fwd_bwd_noalloc": (ctypes.c_int, [_p, ctypes.POINTER(LmheadArgs)]),
     "grpo_needs_ahead_pass": (ctypes.c_int32, [_i64, _i32, _i32]),
     "grpo_old_cache_init": (ctypes.c_int, [ctypes.POINTER(OldCache), _p, _i64, _P64, _i64]),
     "grpo_old_cache_reset": (ctypes.c_int, [ctypes.POINTER(OldCache)]),

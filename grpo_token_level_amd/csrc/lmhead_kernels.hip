@@ -43,6 +43,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "common.h"
 #include "surrogate.h"
@@ -732,20 +733,25 @@ struct Workspace {
 struct Pass2Plan {
     int64_t chunk;
     int nsplit;
+    double cost;
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus) {
+// chunk_cap (a multiple of BN) and split_cap bound the plan to a smaller
+// workspace (the no-allocation entry point's fixed scratch).
+Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus, int64_t chunk_cap = kVocabChunkMax,
+                     int split_cap = kDhSplitMax) {
     constexpr double kKstepUs = 2.0, kHbmBytesPerUs = 5.0e6;
     const int64_t n_pad = round_up(n, kTokPad);
     const int64_t tm = cdiv(n, BM), th = cdiv(H, BN);
-    Pass2Plan best{V < kVocabChunkMax ? V : kVocabChunkMax, 1};
+    const int64_t wcap = chunk_cap < kVocabChunkMax ? chunk_cap : kVocabChunkMax;
+    Pass2Plan best{V < wcap ? V : wcap, 1, -1.0};
     double best_cost = -1.0;
-    const int64_t wmax = V < kVocabChunkMax ? round_up(V, BN) : kVocabChunkMax;
+    const int64_t wmax = V < wcap ? round_up(V, BN) : wcap;
     const int64_t wmin = wmax < kVocabChunkMin ? wmax : kVocabChunkMin;
     for (int64_t w = wmin; w <= wmax; w += 2048 > wmax - wmin ? BN : 2048) {
-        for (int sp = 1; sp <= kDhSplitMax; ++sp) {
+        for (int sp = 1; sp <= split_cap; ++sp) {
             int64_t steps = 0, chunks = 0;
             for (int64_t c0 = 0; c0 < V; c0 += w) {
                 const int64_t vc = V - c0 < w ? V - c0 : w, tv = cdiv(vc, BN);
@@ -759,17 +765,18 @@ Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus) {
             // a split must save at least 1 % to be worth its partial
             if (best_cost < 0.0 || cost * 100.0 < best_cost * 99.0) {
                 best_cost = cost;
-                best = {w < V ? w : V, sp};
+                best = {w < V ? w : V, sp, cost};
             }
         }
     }
     return best;
 }
 
-Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V) {
+Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V, int64_t chunk_cap = kVocabChunkMax,
+                int split_cap = kDhSplitMax) {
     const int64_t n_parts = (V + 63) / 64;
     const int64_t n_pad = round_up(n_tok > 0 ? n_tok : 1, kTokPad);
-    const int64_t vc = V < kVocabChunkMax ? V : kVocabChunkMax;   // widest chunk any plan uses
+    const int64_t vc = V < chunk_cap ? V : chunk_cap;   // widest chunk any plan within the caps uses
     Workspace w{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -786,7 +793,7 @@ Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V) {
     w.hT = reinterpret_cast<uint16_t*>(take((size_t)H * n_pad * 2));
     w.dz = reinterpret_cast<uint16_t*>(take((size_t)n_tok * vc * 2));
     w.dzT = reinterpret_cast<uint16_t*>(take((size_t)vc * n_pad * 2));
-    w.dh_part = reinterpret_cast<float*>(take((size_t)kDhSplitMax * n_tok * H * 4));
+    w.dh_part = reinterpret_cast<float*>(take((size_t)split_cap * n_tok * H * 4));
     w.vidx = reinterpret_cast<int32_t*>(take((size_t)n_tok * 4));
     w.inv = reinterpret_cast<int32_t*>(take((size_t)n_tok * 4));
     w.count = reinterpret_cast<int32_t*>(take(4));
@@ -843,7 +850,83 @@ extern "C" int grpo_transpose_bf16(void* stream, const void* src, int64_t rows, 
     return e == hipSuccess ? ok() : fail(GRPO_EDEVICE, "grpo_transpose_bf16: %s", hipGetErrorString(e));
 }
 
+namespace {
+
+// The scratch of grpo_lmhead_fwd_bwd_noalloc: one array per device, held by
+// the loaded library until the process ends.  On the host `scratch` names a
+// stand-in, not device memory: kernels get the address from
+// hipGetSymbolAddress, taken once per device (scratch_ptr).
+constexpr size_t kStaticScratchBytes = (size_t)GRPO_LMHEAD_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (looked up once per
+// device, with that device current).
+int scratch_ptr(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GRPO_EDEVICE, "grpo_lmhead_fwd_bwd_noalloc: hipGetDevice: %s",
+                                     hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GRPO_EDEVICE, "grpo_lmhead_fwd_bwd_noalloc: device %d beyond the %d this build tracks", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GRPO_EDEVICE, "grpo_lmhead_fwd_bwd_noalloc: hipGetSymbolAddress(scratch): %s",
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GRPO_OK;
+}
+
+// Caps (vocabulary chunk width, dh splits) whose workspace fits `cap` bytes,
+// the cheapest such plan by plan_pass2's cost; chunk 0 when none fits.
+Pass2Plan plan_within(int64_t n, int64_t H, int64_t V, int64_t cus, size_t cap, int64_t* chunk_cap,
+                      int* split_cap) {
+    Pass2Plan best{0, 0, -1.0};
+    *chunk_cap = 0;
+    *split_cap = 0;
+    for (int sp = kDhSplitMax; sp >= 1; sp = sp > 1 ? sp / 2 : 0) {
+        // the widest chunk (a multiple of BN) whose workspace fits, by bisection
+        int64_t lo = 0, hi = kVocabChunkMax / BN;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) / 2;
+            if (carve(nullptr, n, H, V, mid * BN, sp).bytes <= cap) lo = mid;
+            else hi = mid - 1;
+        }
+        if (lo == 0) continue;
+        const Pass2Plan p = plan_pass2(n, H, V, cus, lo * BN, sp);
+        if (best.cost < 0.0 || p.cost < best.cost) {
+            best = p;
+            *chunk_cap = lo * BN;
+            *split_cap = sp;
+        }
+    }
+    return best;
+}
+
+int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc);
+
+}  // namespace
+
 extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
+    return lmhead_run(stream, a, false);
+}
+
+extern "C" int grpo_lmhead_fwd_bwd_noalloc(void* stream, const grpo_lmhead_args* a) {
+    return lmhead_run(stream, a, true);
+}
+
+namespace {
+
+int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
     if (!a) return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: NULL args");
     if (a->struct_size != (int32_t)sizeof(grpo_lmhead_args))
         return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: struct_size %d != %d", a->struct_size,
@@ -871,21 +954,43 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
                                          a->kl_type);
         if (rc != GRPO_OK) return rc;
     }
-    const size_t need = grpo_lmhead_workspace_size(n, H, V);
-    if (!a->workspace || a->workspace_bytes < need || !al16(a->workspace))
-        return fail(GRPO_ECAPACITY, "grpo_lmhead_fwd_bwd: workspace of %zu bytes needed (16-byte aligned)", need);
+    int dev = 0, cus = 0;
+    hipError_t e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess ||
+        (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return dev_fail(e, "device query");
+    if (cus < 1) cus = 1;
+    void* wsp = a->workspace;
+    int64_t chunk_cap = kVocabChunkMax;
+    int split_cap = kDhSplitMax;
+    Pass2Plan plan{};
+    if (noalloc) {
+        // the library's own scratch; the caller's workspace fields are ignored
+        plan = plan_within(n, H, V, cus, kStaticScratchBytes, &chunk_cap, &split_cap);
+        if (chunk_cap == 0)
+            return fail(GRPO_ECAPACITY, "grpo_lmhead_fwd_bwd_noalloc: %lld tokens at H %lld, V %lld need %zu bytes of "
+                        "scratch even with the narrowest plan; the fixed scratch holds %zu",
+                        (long long)n, (long long)H, (long long)V, carve(nullptr, n, H, V, BN, 1).bytes,
+                        kStaticScratchBytes);
+        const int rc = scratch_ptr(&wsp);
+        if (rc != GRPO_OK) return rc;
+    } else {
+        const size_t need = grpo_lmhead_workspace_size(n, H, V);
+        if (!a->workspace || a->workspace_bytes < need || !al16(a->workspace))
+            return fail(GRPO_ECAPACITY, "grpo_lmhead_fwd_bwd: workspace of %zu bytes needed (16-byte aligned)", need);
+        plan = plan_pass2(n, H, V, cus);
+    }
     hipStream_t st = (hipStream_t)stream;
     const grpo::ObjTerms obj{a->scale, a->denom, a->row_weight, a->ent_coef, a->ref_logp ? a->kl_coef : 0.0f};
     float* kl_tok = a->ref_logp ? a->kl_tok : nullptr;
     if (n == 0) return grpo::launch_stats(stream, a->loss_tok, a->entropy, kl_tok, a->tok_flags, a->row_off,
                                           a->n_rows, 0, obj, a->row_stats, a->chunk_stats);
-    const Workspace w = carve(a->workspace, n, H, V);
+    const Workspace w = carve(wsp, n, H, V, chunk_cap, split_cap);
     const int64_t n_pad = round_up(n, kTokPad);
     const int n_parts = (int)((V + 63) / 64);
     const uint16_t* h = (const uint16_t*)a->h;
     const uint16_t* W = (const uint16_t*)a->W;
     const uint16_t* Wt = (const uint16_t*)a->Wt;
-    hipError_t e;
 
     // Masked tokens add nothing to any product (their dz rows are zero), so
     // the GEMMs run over the chunk's valid tokens only: vidx lists them in
@@ -923,11 +1028,6 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
     if (rc != GRPO_OK) return rc;
 
     // pass 2: per vocabulary chunk, dz then dh (+)= dz W_c and dW_c += dz^T h
-    int dev = 0, cus = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess ||
-        (e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-        return dev_fail(e, "device query");
-    const Pass2Plan plan = plan_pass2(n, H, V, cus > 0 ? cus : 1);
     const int64_t chunk = plan.chunk;
     const int nsplit = plan.nsplit;
     for (int64_t c0 = 0; c0 < V; c0 += chunk) {
@@ -964,3 +1064,5 @@ extern "C" int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* a) {
     if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "dh splits");
     return ok();
 }
+
+}  // namespace

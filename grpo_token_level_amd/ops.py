@@ -543,12 +543,15 @@ def lmhead_workspace_bytes(n_tok, H, V):
 
 def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off, dW, *, scale=1.0, denom=None,
                    eps_low=0.2, eps_high=0.2, dh=None, ws=None, workspace=None, row_weight=None,
-                   ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3):
+                   ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3, noalloc=False):
     """Fused LM-head GRPO loss over one chunk (grpo_lmhead_fwd_bwd).
 
     ``dW`` (fp32 [V x H]) is accumulated into; ``dh`` (fp32 [n_tok x H]) is
     written.  Shapes, element types and lengths are checked before the call
-    (ValueError).  Returns the per-token workspace dict with ``dh`` added."""
+    (ValueError).  Returns the per-token workspace dict with ``dh`` added.
+    ``noalloc``: call grpo_lmhead_fwd_bwd_noalloc, which uses the library's
+    fixed scratch (no workspace is passed; the caller still provides every
+    input and output)."""
     torch = _torch()
     if h.dim() != 2 or W.dim() != 2:
         raise ValueError("h and W must be 2-D")
@@ -559,7 +562,7 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
         ws = loss_workspace(n, n_rows, h.device)
     if dh is None:
         dh = torch.empty((n, H), dtype=torch.float32, device=h.device)
-    if workspace is None:
+    if workspace is None and not noalloc:
         workspace = torch.empty(max(lmhead_workspace_bytes(n, H, V), 1), dtype=torch.uint8, device=h.device)
     a = C.LmheadArgs()
     a.struct_size = ctypes.sizeof(C.LmheadArgs)
@@ -579,12 +582,18 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
     if dW.shape[0] != V:
         raise ValueError(f"dW must be [{V} x {H}]")
     a.dW = dW.data_ptr()
-    if not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous GPU tensor")
-    a.workspace = workspace.data_ptr()
-    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc calls take no workspace")
+        a.workspace, a.workspace_bytes = None, 0
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
     _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws, n_rows, n, n)
-    C.check(C.lib().grpo_lmhead_fwd_bwd(_stream(), ctypes.byref(a)))
+    entry = C.lib().grpo_lmhead_fwd_bwd_noalloc if noalloc else C.lib().grpo_lmhead_fwd_bwd
+    C.check(entry(_stream(), ctypes.byref(a)))
     ws["dh"] = dh
     ws["workspace"] = workspace
     return ws

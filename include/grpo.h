@@ -428,6 +428,26 @@ size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V);
  * ECAPACITY if the workspace is too small. */
 int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* args);
 
+/* Bytes of the fixed device scratch behind grpo_lmhead_fwd_bwd_noalloc. */
+#define GRPO_LMHEAD_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/* device.  grpo_lmhead_fwd_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, but its scratch lives in a fixed
+ * 256 MiB array that the library holds on every GPU it runs on until the
+ * process ends, so the call allocates nothing and args->workspace /
+ * workspace_bytes are ignored.  The vocabulary chunk width and the dh split
+ * count are chosen to fit that scratch (narrower than the workspace path may
+ * use when the chunk is large, so dh and dW can differ from
+ * grpo_lmhead_fwd_bwd in summation order, not in what they compute).  A chunk
+ * whose narrowest plan still needs more than
+ * GRPO_LMHEAD_NOALLOC_SCRATCH_BYTES (grpo_lmhead_workspace_size's per-token
+ * parts grow with n_tok * V / 4 and n_tok * H) returns GRPO_ECAPACITY with
+ * the size it needs.  Nothing in the scratch has to start at zero.  All calls
+ * on one GPU share that GPU's scratch: calls that overlap on one GPU (two
+ * streams, or two threads) race and must be serialised by the caller. */
+int grpo_lmhead_fwd_bwd_noalloc(void* stream, const grpo_lmhead_args* args);
+
 /* ===================================================== frozen pi_old (ahead pass) */
 
 /* host.  [P1] "pi_old must be frozen across the window -- the ahead pass":

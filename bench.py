@@ -1,11 +1,12 @@
 """Throughput of one token-level GRPO loss step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload qwen|long|tiny|dynamic|compact] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload long|qwen|tiny|dynamic|compact] [--gpus 1]
 
 A step is one pass of the hot path over one collected batch whose inputs are
 already resident in HBM:
 
-* padded workloads (qwen = default, long, tiny): the fixed mini/micro plan and
+* padded workloads (long = default: the largest configuration, 128 rows x
+  2048 tokens at group 8; qwen; tiny): the fixed mini/micro plan and
   the group advantages (host, libgrpo), N per mini-batch (device), then per
   micro-batch chunk the fused log-softmax + clipped-surrogate forward/backward
   that reads the chunk's logits once and writes dlogits once (device), and the
@@ -59,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="long", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle sample (0 disables the cpu_baseline leg)")
@@ -180,7 +181,12 @@ class PaddedStep:
         self.n_seq = torch.empty(n_mini, dtype=torch.int64, device="cuda")
         self.w_row = torch.empty(mini_rows, dtype=torch.float32, device="cuda")
         self.tok_row = ops.tok_row(self.row_off, micro_rows * T)
-        self.ws = ops.loss_workspace(micro_rows * T, micro_rows, "cuda")
+        # per-token outputs of a whole mini-batch: the chunks write views of it
+        # with their row reductions deferred, and one grpo_loss_stats call per
+        # optimizer window reduces every row of the window
+        self.ws = ops.loss_workspace(mini_rows * T, mini_rows, "cuda")
+        self.mini_rows, self.micro_rows, self.n_micro = mini_rows, micro_rows, n_micro
+        self.chunk_tokens = micro_rows * T
         self.N = torch.empty(n_mini, dtype=torch.int64, device="cuda")
         self.adv_host = torch.empty(n_rows, dtype=torch.float32).pin_memory()
         self.adv_dev = torch.empty(n_rows, dtype=torch.float32, device="cuda")
@@ -189,9 +195,10 @@ class PaddedStep:
             self.mini_mask = torch.empty(mini_rows * T, dtype=torch.uint8, device="cuda")
             self.tok_src = torch.empty(micro_rows * T, dtype=torch.int64, device="cuda")
             self.adv_chunk = torch.empty(micro_rows, dtype=torch.float32, device="cuda")
-        n_calls = epochs * n_mini * n_micro
-        self.stats_dev = torch.empty((n_calls, ops.STATS_BYTES), dtype=torch.uint8, device="cuda")
-        self.stats_host = torch.empty((n_calls, ops.STATS_BYTES), dtype=torch.uint8).pin_memory()
+        n_win = epochs * n_mini
+        self.stats_dev = torch.empty((n_win * mini_rows, ops.STATS_BYTES), dtype=torch.uint8, device="cuda")
+        self.stats_host = torch.empty((n_win * mini_rows, ops.STATS_BYTES), dtype=torch.uint8).pin_memory()
+        self.win_stats = torch.empty((n_win, ops.STATS_BYTES), dtype=torch.uint8, device="cuda")
         b_in = 2 if self.dt == torch.bfloat16 else 4
         self.chunk_units = {}
         for e in range(epochs):
@@ -268,9 +275,11 @@ class PaddedStep:
                     ops.count_rows(mini_mask, self.mini_off, out=self.n_seq[i:i + 1])
                     ops.row_weights(mini_mask, self.mini_off, ops.C.AGG_SEQ_MEAN_TOKEN_MEAN, self.n_seq[i:i + 1],
                                     out=self.w_row)
+                w = ep * n_mini + i
                 for j in range(n_micro):
                     r0 = j * micro_rows                      # the chunk's rows within the mini-batch
-                    self.ws["chunk_stats"] = self.stats_dev[k:k + 1]
+                    view = {key: self.ws[key][r0 * T:(r0 + micro_rows) * T]
+                            for key in ("logp", "lse", "entropy", "loss_tok", "kl_tok", "tok_flags")}
                     if self.terms:
                         kw = dict(scale=1.0, row_weight=self.w_row[r0:r0 + micro_rows],
                                   ent_coef=self.ENT_COEF, kl_coef=self.KL_COEF, kl_type=ops.C.KL_K3)
@@ -285,7 +294,8 @@ class PaddedStep:
                             kw["ref_logp"] = self.ref
                         ev = self.timed.begin()
                         ops.loss_fwd_bwd(self.logits, self.target, self.mask, old, self.tok_row, self.adv_chunk,
-                                         self.row_off, dlogits=self.dlogits, ws=self.ws, tok_src=self.tok_src, **kw)
+                                         self.row_off, dlogits=self.dlogits, ws=view, tok_src=self.tok_src,
+                                         defer_stats=True, **kw)
                     else:
                         a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
                         t0, t1 = a * T, e * T
@@ -295,21 +305,30 @@ class PaddedStep:
                         ev = self.timed.begin()
                         ops.loss_fwd_bwd(self.logits[t0:t1], self.target[t0:t1], self.mask[t0:t1], old,
                                          self.tok_row, self.adv_dev[a:e], self.row_off, dlogits=self.dlogits[t0:t1],
-                                         ws=self.ws, **kw)
+                                         ws=view, defer_stats=True, **kw)
                     self.timed.end(ev, self.chunk_units[(ep, i, j)])
                     k += 1
+                # the window's row reductions in one call (rows in mini-batch order)
+                self.ws["row_stats"] = self.stats_dev[w * mini_rows:(w + 1) * mini_rows]
+                self.ws["chunk_stats"] = self.win_stats[w:w + 1]
+                if self.terms:
+                    ops.loss_stats(self.ws, self.mini_off, scale=1.0, row_weight=self.w_row, with_kl=True,
+                                   ent_coef=self.ENT_COEF, kl_coef=self.KL_COEF)
+                else:
+                    ops.loss_stats(self.ws, self.mini_off, scale=1.0, denom=self.N[i:i + 1])
 
     def _finish(self):
         torch, ops, b = self.torch, self.ops, self.b
         n_mini, n_micro, _, _ = ops.plan_fixed(b["n_rows"], b["group"], b["mini"], b["micro"])
         self.stats_host.copy_(self.stats_dev, non_blocking=True)
         torch.cuda.current_stream().synchronize()
-        stats = ops.stats_to_dicts(self.stats_host.numpy())
+        base = self.stats_host.data_ptr()
+        m, u, sb = self.mini_rows, self.micro_rows, ops.STATS_BYTES
         out = []
         for w in range(self.mu * n_mini):
             acc = ops.Accumulator(n_micro)
-            for j in range(n_micro):
-                acc.add(stats[w * n_micro + j])
+            for j in range(n_micro):              # a chunk's stats: the sum of its rows'
+                acc.add_rows_at(base + (w * m + j * u) * sb, u)
             out.append(acc.finalize())
         return out
 
@@ -333,7 +352,7 @@ class PaddedStep:
     def _stream_rate(self, mode):
         import yardstick
         torch = self.torch
-        n = self.ws["logp"].numel()
+        n = self.chunk_tokens
         src = self.logits[:n]
         dst = self.dlogits[:n] if mode == yardstick.COPY else None
         nbytes = src.numel() * src.element_size()
@@ -381,8 +400,11 @@ class DynamicStep(PaddedStep):
         del logp
         self.dlogits = torch.empty_like(self.logits)
         bin_tok = [int(offB[plan["bin_off"][k + 1]] - offB[plan["bin_off"][k]]) for k in range(plan["n_bins"])]
-        max_rows = int(np.max(np.diff(plan["bin_off"])))
-        self.ws = ops.loss_workspace(max(bin_tok), max_rows, "cuda")
+        # per-token outputs of the whole batch (one optimizer window): the boxes
+        # write views of it with their row reductions deferred, then one
+        # grpo_loss_stats call reduces every row (packed order)
+        self.ws = ops.loss_workspace(n_tok, len(L), "cuda")
+        self.chunk_tokens = max(bin_tok)
         self.tok_row = torch.empty(max(bin_tok), dtype=torch.int32, device="cuda")
         self.N = torch.empty(1, dtype=torch.int64, device="cuda")
         n_rows = len(L)
@@ -390,8 +412,11 @@ class DynamicStep(PaddedStep):
         self.meta_dev = torch.empty(n_rows + plan["n_bins"] + 8, dtype=torch.int64, device="cuda")
         self.adv_host = torch.empty(n_rows, dtype=torch.float32).pin_memory()
         self.adv_dev = torch.empty(n_rows, dtype=torch.float32, device="cuda")
-        self.stats_dev = torch.empty((plan["n_bins"] + 8, ops.STATS_BYTES), dtype=torch.uint8, device="cuda")
-        self.stats_host = torch.empty((plan["n_bins"] + 8, ops.STATS_BYTES), dtype=torch.uint8).pin_memory()
+        self.stats_dev = torch.empty((n_rows, ops.STATS_BYTES), dtype=torch.uint8, device="cuda")
+        self.stats_host = torch.empty((n_rows, ops.STATS_BYTES), dtype=torch.uint8).pin_memory()
+        self.win_stats = torch.empty((1, ops.STATS_BYTES), dtype=torch.uint8, device="cuda")
+        self.offB_host = torch.empty(n_rows + 1, dtype=torch.int64).pin_memory()
+        self.offB_dev = torch.empty(n_rows + 1, dtype=torch.int64, device="cuda")
         self.mask_np = b["mask"][perm]
         self.n_valid = int(np.sum(b["mask"]))
         self.logits_dtype = "bf16"
@@ -417,26 +442,30 @@ class DynamicStep(PaddedStep):
         adv = ops.group_advantage(b["reward"], b["group"])
         self.adv_host.numpy()[:] = adv[order]
         self.adv_dev.copy_(self.adv_host, non_blocking=True)
+        self.offB_host.numpy()[:] = offB
+        self.offB_dev.copy_(self.offB_host, non_blocking=True)
         ops.count_valid(self.mask, out=self.N)
         for k in range(plan["n_bins"]):
             a, e = int(bin_off[k]), int(bin_off[k + 1])
             t0, t1 = int(offB[a]), int(offB[e])
             ro = self.meta_dev[starts[k]:starts[k] + e - a + 1]
             tr = ops.tok_row(ro, t1 - t0, out=self.tok_row[:t1 - t0])
-            ws = {kk: (v[:t1 - t0] if kk in ("logp", "lse", "entropy", "loss_tok", "tok_flags") else v)
-                  for kk, v in self.ws.items()}
-            ws["row_stats"] = self.ws["row_stats"][:e - a]
-            ws["chunk_stats"] = self.stats_dev[k:k + 1]
+            ws = {kk: self.ws[kk][t0:t1] for kk in ("logp", "lse", "entropy", "loss_tok", "kl_tok", "tok_flags")}
             ev = self.timed.begin()
             ops.loss_fwd_bwd(self.logits[t0:t1], self.target[t0:t1], self.mask[t0:t1], self.old[t0:t1], tr,
-                             self.adv_dev[a:e], ro, scale=1.0, denom=self.N, dlogits=self.dlogits[t0:t1], ws=ws)
+                             self.adv_dev[a:e], ro, scale=1.0, denom=self.N, dlogits=self.dlogits[t0:t1], ws=ws,
+                             defer_stats=True)
             self.timed.end(ev, chunk_bytes(self.mask_np[t0:t1], b["V"], 2, 2))
-        nb = plan["n_bins"]
-        self.stats_host[:nb].copy_(self.stats_dev[:nb], non_blocking=True)
+        self.ws["row_stats"] = self.stats_dev
+        self.ws["chunk_stats"] = self.win_stats
+        ops.loss_stats(self.ws, self.offB_dev, scale=1.0, denom=self.N)
+        self.stats_host.copy_(self.stats_dev, non_blocking=True)
         torch.cuda.current_stream().synchronize()
+        raw = self.stats_host.numpy()
+        nb = plan["n_bins"]
         acc = ops.Accumulator(nb)
-        for s in ops.stats_to_dicts(self.stats_host[:nb].numpy()):
-            acc.add(s)
+        for k in range(nb):                       # a box's stats: the sum of its rows'
+            acc.add_rows(raw, int(bin_off[k]), int(bin_off[k + 1] - bin_off[k]))
         return [acc.finalize()]
 
     def sample(self, n, start=0):
@@ -743,13 +772,15 @@ def main():
         achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": fused_kernel_label(step.V, step.logits_dtype) + " (fused loss fwd+bwd) + row/chunk stats, "
-                          "per chunk launch" + ("; graph replay time divided by the chunk launches" if args.graph else ""),
+                "kernel": fused_kernel_label(step.V, step.logits_dtype) + " (fused loss fwd+bwd), per chunk launch; "
+                          "the row and chunk reductions run once per optimizer window, outside these windows"
+                          + ("; graph replay time (reductions included) divided by the chunk launches"
+                             if args.graph else ""),
                 "algorithmic_bytes_per_launch": int(units // launches), "avg_launch_ms": round(tot_ms / launches, 4)}
         roof["device_copy_GBs"] = round(step.copy_context(), 1)
-        if wl == "qwen" and not (args.terms or args.ahead or args.epochs != 1 or args.shuffle or args.vocab):
+        if wl in ("qwen", "long") and not (args.terms or args.ahead or args.epochs != 1 or args.shuffle or args.vocab):
             from yardstick.prof_summary import load_traffic
-            rec = load_traffic(os.path.join(ROOT, "profiles", "fused_loss_qwen_pmc.txt"))
+            rec = load_traffic(os.path.join(ROOT, "profiles", f"fused_loss_{wl}_pmc.txt"))
             if rec is not None:
                 roof["traffic"] = rec["traffic_bytes_per_launch"]
     cfg["llc"] = step.llc_note() if hasattr(step, "llc_note") else None

@@ -32,6 +32,7 @@ class GrpoError(RuntimeError):
 
 
 KL_K1, KL_K2, KL_K3 = 1, 2, 3
+LOSS_DEFER_STATS = 1
 AGG_TOKEN_MEAN, AGG_SEQ_MEAN_TOKEN_SUM, AGG_SEQ_MEAN_TOKEN_MEAN = 0, 1, 2
 
 
@@ -59,7 +60,7 @@ class LossArgs(ctypes.Structure):
                 ("logits", _p), ("ld", _i64), ("n_tok", _i64), ("V", _i64),
                 ("target", _p), ("mask", _p), ("old_logp", _p), ("tok_row", _p), ("adv_row", _p),
                 ("row_off", _p), ("n_rows", _i64),
-                ("eps_low", _f32), ("eps_high", _f32), ("scale", _f32), ("reserved1", _i32),
+                ("eps_low", _f32), ("eps_high", _f32), ("scale", _f32), ("flags", _i32),
                 ("denom", _p), ("dlogits", _p), ("ld_out", _i64),
                 ("logp", _p), ("lse", _p), ("entropy", _p), ("loss_tok", _p), ("tok_flags", _p),
                 ("row_stats", _p), ("chunk_stats", _p),
@@ -141,6 +142,8 @@ PROTOTYPES = {
     "grpo_gather": (ctypes.c_int, [_p, _p, _i64, _p, _i64, _i64, _p]),
     "grpo_logprob_fwd": (ctypes.c_int, [_p, _i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "grpo_loss_fwd_bwd": (ctypes.c_int, [_p, ctypes.POINTER(LossArgs)]),
+    "grpo_loss_stats": (ctypes.c_int, [_p, ctypes.POINTER(LossArgs)]),
+    "grpo_stats_sum": (ctypes.c_int, [_p, _i64, ctypes.POINTER(Stats)]),
     "grpo_transpose_bf16": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _i64]),
     "grpo_lmhead_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "grpo_lmhead_fwd_bwd": (ctypes.c_int, [_p, ctypes.POINTER(LmheadArgs)]),

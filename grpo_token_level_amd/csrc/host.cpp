@@ -371,6 +371,15 @@ void stats_add(grpo_stats* a, const grpo_stats* b) {
 }
 }  // namespace
 
+extern "C" int grpo_stats_sum(const grpo_stats* rows, int64_t n, grpo_stats* out) {
+    if (n < 0 || !out || (n > 0 && !rows)) return fail(GRPO_EINVAL, "grpo_stats_sum: bad arguments");
+    grpo_stats s;
+    stats_zero(&s);
+    for (int64_t r = 0; r < n; ++r) stats_add(&s, rows + r);
+    *out = s;
+    return ok();
+}
+
 extern "C" size_t grpo_accum_size(void) { return sizeof(grpo_accum); }
 
 extern "C" int grpo_accum_init(grpo_accum* acc, int64_t n_micro) {

@@ -1444,7 +1444,9 @@ extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
     if (a->n_tok > 0 && a->n_rows < 1) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: tokens without rows");
     if (a->n_tok > 0x7fffffffLL || a->n_rows > 0x7fffffffLL)
         return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: too many tokens or rows for one launch");
-    if (!a->chunk_stats || (a->n_rows > 0 && (!a->row_stats || !a->row_off)))
+    if (a->flags & ~GRPO_LOSS_DEFER_STATS) return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: unknown flags %d", a->flags);
+    const bool defer = (a->flags & GRPO_LOSS_DEFER_STATS) != 0;
+    if (!defer && (!a->chunk_stats || (a->n_rows > 0 && (!a->row_stats || !a->row_off))))
         return fail(GRPO_EINVAL, "grpo_loss_fwd_bwd: NULL stats pointer");
     if (a->n_tok > 0 && (!a->logits || !a->target || !a->mask || !a->old_logp || !a->tok_row || !a->adv_row ||
                          !a->logp || !a->entropy || !a->loss_tok || !a->tok_flags))
@@ -1490,9 +1492,29 @@ extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
     else if (dout == GRPO_BF16) e = launch_tok<GRPO_F32, GRPO_BF16, true>(p, vec_ok, st);
     else e = launch_tok<GRPO_F32, GRPO_F32, true>(p, vec_ok, st);
     if (e != hipSuccess) return check_launch(e, "grpo_loss_fwd_bwd (token kernel)");
+    if (defer) return ok();
     const grpo::ObjTerms obj{a->scale, a->denom, a->row_weight, a->ent_coef, a->ref_logp ? a->kl_coef : 0.0f};
     return grpo::launch_stats(stream, a->loss_tok, a->entropy, p.kl_tok, a->tok_flags, a->row_off, a->n_rows,
                               a->n_tok, obj, a->row_stats, a->chunk_stats);
+}
+
+extern "C" int grpo_loss_stats(void* stream, const grpo_loss_args* a) {
+    if (!a) return fail(GRPO_EINVAL, "grpo_loss_stats: NULL args");
+    if (a->struct_size != (int32_t)sizeof(grpo_loss_args))
+        return fail(GRPO_EINVAL, "grpo_loss_stats: struct_size %d != %d", a->struct_size, (int)sizeof(grpo_loss_args));
+    if (a->n_tok < 0 || a->n_rows < 0 || (a->n_tok > 0 && a->n_rows < 1))
+        return fail(GRPO_EINVAL, "grpo_loss_stats: need n_tok >= 0 and rows for the tokens");
+    if (a->n_tok > 0x7fffffffLL || a->n_rows > 0x7fffffffLL)
+        return fail(GRPO_EINVAL, "grpo_loss_stats: too many tokens or rows for one launch");
+    if (!a->chunk_stats || (a->n_rows > 0 && (!a->row_stats || !a->row_off)))
+        return fail(GRPO_EINVAL, "grpo_loss_stats: NULL stats pointer");
+    if (a->n_tok > 0 && (!a->entropy || !a->loss_tok || !a->tok_flags || (a->ref_logp && !a->kl_tok)))
+        return fail(GRPO_EINVAL, "grpo_loss_stats: NULL per-token output");
+    if (!std::isfinite(a->scale) || !std::isfinite(a->ent_coef) || !std::isfinite(a->kl_coef))
+        return fail(GRPO_EINVAL, "grpo_loss_stats: scale, ent_coef and kl_coef must be finite");
+    const grpo::ObjTerms obj{a->scale, a->denom, a->row_weight, a->ent_coef, a->ref_logp ? a->kl_coef : 0.0f};
+    return grpo::launch_stats(stream, a->loss_tok, a->entropy, a->ref_logp ? a->kl_tok : nullptr, a->tok_flags,
+                              a->row_off, a->n_rows, a->n_tok, obj, a->row_stats, a->chunk_stats);
 }
 
 // Shared argument checks of the extra terms.

@@ -148,13 +148,39 @@ class Accumulator:
     'SKIPPED'; finalize() returns a dict or None."""
 
     def __init__(self, n_micro):
-        n = int(C.lib().grpo_accum_size())
+        self._L = C.lib()
+        n = int(self._L.grpo_accum_size())
         self._a = (ctypes.c_int64 * ((n + 7) // 8))()     # opaque bytes, 8-byte aligned
-        C.check(C.lib().grpo_accum_init(self._a, n_micro))
+        self._s = C.Stats()
+        self._s_ref = ctypes.byref(self._s)
+        C.check(self._L.grpo_accum_init(self._a, n_micro))
 
     def add(self, stats):
         s = C.Stats(**{k: stats.get(k, 0) for k in STATS_DTYPE.names})
-        code = C.lib().grpo_accum_add(self._a, ctypes.byref(s))
+        return self._add(s)
+
+    def add_rows(self, raw, start, n):
+        """Adds one chunk given as rows start .. start+n of a host array of
+        grpo_stats (uint8 bytes, STATS_BYTES per row): the rows are summed in
+        order by grpo_stats_sum, no Python arithmetic."""
+        if not isinstance(raw, np.ndarray) or not raw.flags.c_contiguous or raw.dtype != np.uint8:
+            raise ValueError("raw must be a C-contiguous uint8 array of grpo_stats")
+        if start < 0 or n < 0 or (start + n) * STATS_BYTES > raw.nbytes:
+            raise ValueError("rows outside the stats array")
+        return self.add_rows_at(raw.ctypes.data + start * STATS_BYTES, n)
+
+    def add_rows_at(self, addr, n):
+        """add_rows on n grpo_stats at host address ``addr`` (the caller keeps
+        them alive and in bounds)."""
+        C.check(self._L.grpo_stats_sum(addr, n, self._s_ref))
+        return self._add_ref()
+
+    def _add(self, s):
+        ctypes.memmove(ctypes.byref(self._s), ctypes.byref(s), ctypes.sizeof(C.Stats))
+        return self._add_ref()
+
+    def _add_ref(self):
+        code = self._L.grpo_accum_add(self._a, self._s_ref)
         if code == 0:
             return "OK"
         if code == -5:
@@ -443,9 +469,10 @@ def _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws, n_rows, 
     a.ent_coef, a.kl_coef, a.kl_type = ent_coef, kl_coef, kl_type
 
 
-def _set_common(a, target, mask, old_logp, tok_row_, adv_row, row_off, denom, ws, n, n_src):
+def _set_common(a, target, mask, old_logp, tok_row_, adv_row, row_off, denom, ws, n, n_src, stats=True):
     """The per-token inputs (``n_src`` tokens behind them), the chunk-local row
-    arrays and the per-token / per-row outputs shared by both loss calls."""
+    arrays and the per-token / per-row outputs shared by both loss calls
+    (``stats`` False: the row and chunk reductions are deferred)."""
     n_rows = row_off.numel() - 1
     a.target = _need(target, "target", "int32", n_src)
     a.mask = _need(mask, "mask", "byte", n_src)
@@ -459,8 +486,9 @@ def _set_common(a, target, mask, old_logp, tok_row_, adv_row, row_off, denom, ws
         setattr(a, k, _need(ws.get(k), k, "float32", n))
     a.lse = _need(ws.get("lse"), "lse", "float32", n, optional=True)
     a.tok_flags = _need(ws.get("tok_flags"), "tok_flags", "byte", n)
-    a.row_stats = _need(ws.get("row_stats"), "row_stats", "byte", n_rows * STATS_BYTES)
-    a.chunk_stats = _need(ws.get("chunk_stats"), "chunk_stats", "byte", STATS_BYTES)
+    if stats:
+        a.row_stats = _need(ws.get("row_stats"), "row_stats", "byte", n_rows * STATS_BYTES)
+        a.chunk_stats = _need(ws.get("chunk_stats"), "chunk_stats", "byte", STATS_BYTES)
     if not n:                       # nothing per token is touched
         a.target = a.mask = a.old_logp = a.tok_row = None
         a.logp = a.lse = a.entropy = a.loss_tok = a.tok_flags = None
@@ -470,8 +498,11 @@ def _set_common(a, target, mask, old_logp, tok_row_, adv_row, row_off, denom, ws
 
 def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, scale=1.0, denom=None,
                  eps_low=0.2, eps_high=0.2, dlogits="new", out_dtype=None, ws=None, row_weight=None,
-                 ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3, tok_src=None):
+                 ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3, tok_src=None, defer_stats=False):
     """Fused GRPO loss forward/backward over one chunk (grpo_loss_fwd_bwd).
+
+    ``defer_stats``: leave the row and chunk reductions to a later
+    ``loss_stats`` call (GRPO_LOSS_DEFER_STATS).
 
     ``dlogits``: "new" (allocate, dtype ``out_dtype`` or the logits dtype),
     "inplace" (overwrite ``logits``), None (no gradient), or a tensor.
@@ -509,7 +540,8 @@ def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, 
     a.out_dtype = _dtype_code(dl) if dl is not None else a.in_dtype
     a.logits = logits.data_ptr() if n else None
     a.ld, a.n_tok, a.V = ld, n, V
-    _set_common(a, target, mask, old_logp, tok_row_, adv_row, row_off, denom, ws, n, n_src)
+    _set_common(a, target, mask, old_logp, tok_row_, adv_row, row_off, denom, ws, n, n_src, stats=not defer_stats)
+    a.flags = C.LOSS_DEFER_STATS if defer_stats else 0
     a.eps_low, a.eps_high, a.scale = eps_low, eps_high, scale
     if dl is not None:
         a.ld_out = _matrix(dl, "dlogits", n_src, V)
@@ -521,6 +553,43 @@ def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, 
     C.check(C.lib().grpo_loss_fwd_bwd(_stream(), ctypes.byref(a)))
     ws["dlogits"] = dl
     return ws
+
+
+def loss_stats(ws, row_off, *, scale=1.0, denom=None, row_weight=None, with_kl=False, ent_coef=0.0, kl_coef=0.0):
+    """Row and chunk reductions (grpo_loss_stats) over the per-token outputs in
+    ``ws`` (loss_tok, entropy, tok_flags, and kl_tok with ``with_kl``) of the
+    rows ``row_off``, into ws["row_stats"] and ws["chunk_stats"]; the factor
+    fields are the ones the tokens were computed with."""
+    n_rows = row_off.numel() - 1
+    n = ws["loss_tok"].numel()
+    a = C.LossArgs()
+    a.struct_size = ctypes.sizeof(C.LossArgs)
+    a.n_tok, a.n_rows = n, n_rows
+    a.row_off = _need(row_off, "row_off", "int64", n_rows + 1)
+    for k in ("entropy", "loss_tok"):
+        setattr(a, k, _need(ws.get(k), k, "float32", n))
+    a.tok_flags = _need(ws.get("tok_flags"), "tok_flags", "byte", n)
+    a.row_stats = _need(ws.get("row_stats"), "row_stats", "byte", n_rows * STATS_BYTES)
+    a.chunk_stats = _need(ws.get("chunk_stats"), "chunk_stats", "byte", STATS_BYTES)
+    a.denom = _need(denom, "denom", "int64", 1, optional=True)
+    a.row_weight = _need(row_weight, "row_weight", "float32", n_rows, optional=True)
+    if with_kl:
+        a.kl_tok = _need(ws.get("kl_tok"), "kl_tok", "float32", n)
+        a.ref_logp = a.kl_tok          # marks the KL term as present; not read
+    a.scale, a.ent_coef, a.kl_coef = scale, ent_coef, kl_coef
+    C.check(C.lib().grpo_loss_stats(_stream(), ctypes.byref(a)))
+    return ws
+
+
+def stats_sum(rows):
+    """Sum of grpo_stats dicts in order (grpo_stats_sum) -> dict."""
+    n = len(rows)
+    arr = (C.Stats * max(n, 1))()
+    for i, r in enumerate(rows):
+        arr[i] = C.Stats(**{k: r.get(k, 0) for k in STATS_DTYPE.names})
+    out = C.Stats()
+    C.check(C.lib().grpo_stats_sum(ctypes.addressof(arr), n, ctypes.byref(out)))
+    return {k: (float(getattr(out, k)) if k.endswith("_sum") else int(getattr(out, k))) for k in STATS_DTYPE.names}
 
 
 def transpose_bf16(x, out=None):

@@ -281,6 +281,11 @@ int grpo_logprob_fwd(void* stream, int32_t dtype, const void* logits, int64_t ld
                      int64_t V, const int32_t* target, const uint8_t* mask,
                      float* logp, float* lse, float* entropy);
 
+/* grpo_loss_args.flags: leave the row and chunk reductions to a later
+ * grpo_loss_stats call (row_off, row_stats and chunk_stats are then not read
+ * and may be NULL), so that one reduction can serve several chunks. */
+#define GRPO_LOSS_DEFER_STATS 1
+
 /* Arguments of grpo_loss_fwd_bwd (all pointers are device pointers). */
 typedef struct grpo_loss_args {
     int32_t struct_size;        /* = sizeof(grpo_loss_args) */
@@ -300,7 +305,7 @@ typedef struct grpo_loss_args {
     int64_t n_rows;             /* rows in this chunk (>= 1 when n_tok > 0) */
     float eps_low, eps_high;    /* clip band [1 - eps_low, 1 + eps_high] */
     float scale;                /* gradient factor: 1/max(N,1) for a known step N, 1 to defer */
-    int32_t reserved1;          /* 0 */
+    int32_t flags;              /* 0, or GRPO_LOSS_DEFER_STATS */
     const int64_t* denom;       /* NULL, or device int64: coef is further divided by max(*denom, 1) */
     void* dlogits;              /* out_dtype, token t at dlogits + t*ld_out; may equal logits
                                    when the dtypes and strides match; NULL = no gradient */
@@ -356,6 +361,23 @@ typedef struct grpo_loss_args {
  * so results are bit-for-bit reproducible and a row's stats do not depend on
  * where the row sits in the chunk. */
 int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* args);
+
+/* device.  The row and chunk reductions of grpo_loss_fwd_bwd on their own,
+ * over the per-token outputs (loss_tok, entropy, kl_tok when ref_logp is set,
+ * tok_flags) of args->n_tok tokens in args->n_rows rows (row_off), with the
+ * gradient factor fields (scale, denom, row_weight, ent_coef, kl_coef) that
+ * the tokens were computed with: row_stats[r] and chunk_stats exactly as
+ * grpo_loss_fwd_bwd would write them for a chunk of those rows.  Use after
+ * calls made with GRPO_LOSS_DEFER_STATS: the rows of several chunks of one
+ * optimizer step can be reduced by one call ([P1] "Metric roll-up": rows
+ * carry sums and counts, so a chunk's stats are the sum of its rows',
+ * grpo_stats_sum).  The other fields of args are not read. */
+int grpo_loss_stats(void* stream, const grpo_loss_args* args);
+
+/* host.  out = the sum of rows[0 .. n) added in index order (float64 sums,
+ * integer counts): a chunk's stats from its rows' (n >= 0; n = 0 gives
+ * zeros). */
+int grpo_stats_sum(const grpo_stats* rows, int64_t n, grpo_stats* out);
 
 /* ========================================================= LM-head variant */
 

@@ -383,3 +383,49 @@ def test_count_valid_and_tok_row():
     tr = ops.tok_row(torch.from_numpy(off).to(DEV), 22).cpu().numpy()
     want = [1] * 5 + [2] * 4 + [4] * 11 + [-1, -1]
     assert tr.tolist() == want
+
+
+def test_deferred_stats_over_several_chunks():
+    # Four chunks with the reductions deferred, then one grpo_loss_stats over
+    # all their rows: every per-token output and dlogits row is the same as
+    # with per-chunk reductions, each row's stats are the same bits, and a
+    # chunk's stats are the sum of its rows' (grpo_stats_sum).
+    n_rows, T, V = 16, 48, 4096
+    d = make_chunk(n_rows * T, V, torch.bfloat16, seed=14, n_rows=2, masked_frac=0.3)
+    row_off = np.arange(0, n_rows * T + 1, T).astype(np.int64)
+    tok_row = np.repeat(np.arange(n_rows, dtype=np.int32), T)
+    adv = np.random.default_rng(2).normal(size=n_rows).astype(np.float32)
+    g = d["g"]
+    G = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    ws = ops.loss_workspace(n_rows * T, n_rows, DEV)
+    dl_def = torch.empty_like(d["logits"])
+    per_chunk = []
+    for c in range(4):
+        a, b = c * 4 * T, (c + 1) * 4 * T
+        view = {k: ws[k][a:b] for k in ("logp", "lse", "entropy", "loss_tok", "kl_tok", "tok_flags")}
+        ops.loss_fwd_bwd(d["logits"][a:b], g["target"][a:b], g["mask"][a:b], g["old"][a:b],
+                         G(tok_row[a:b] - 4 * c), G(adv[4 * c:4 * c + 4]), G(row_off[4 * c:4 * c + 5] - a),
+                         scale=1 / 500.0, dlogits=dl_def[a:b], ws=view, defer_stats=True)
+        per_chunk.append(ops.loss_fwd_bwd(d["logits"][a:b], g["target"][a:b], g["mask"][a:b], g["old"][a:b],
+                                          G(tok_row[a:b] - 4 * c), G(adv[4 * c:4 * c + 4]),
+                                          G(row_off[4 * c:4 * c + 5] - a), scale=1 / 500.0))
+    ops.loss_stats(ws, G(row_off), scale=1 / 500.0)
+    torch.cuda.synchronize()
+    assert torch.equal(dl_def, torch.cat([p["dlogits"] for p in per_chunk]))
+    for k in ("logp", "entropy", "loss_tok", "tok_flags"):
+        assert torch.equal(ws[k], torch.cat([p[k] for p in per_chunk])), k
+    assert torch.equal(ws["row_stats"], torch.cat([p["row_stats"][:4] for p in per_chunk]))
+    rows = ops.stats_to_dicts(ws["row_stats"])
+    for c, p in enumerate(per_chunk):
+        want = ops.stats_to_dicts(p["chunk_stats"])[0]
+        got = ops.stats_sum(rows[4 * c:4 * c + 4])
+        for k in want:
+            assert got[k] == pytest.approx(want[k], rel=1e-12, abs=1e-12), k
+    whole = ops.stats_to_dicts(ws["chunk_stats"])[0]
+    assert whole["n_valid"] == int(d["mask"].sum())
+    assert whole["loss_sum"] == pytest.approx(sum(r["loss_sum"] for r in rows), rel=1e-12)
+    ref = oracle.loss_fwd_bwd(d["z64"], d["target"], d["mask"], d["old"].astype(np.float64),
+                              adv.astype(np.float64)[tok_row], 1 / 500.0, want_dz=False)
+    want_rows = oracle.row_stats(ref, row_off.tolist())
+    for r, (gr, wr) in enumerate(zip(rows, want_rows)):
+        assert gr["n_valid"] == wr["n_valid"] and gr["loss_sum"] == pytest.approx(wr["loss_sum"], rel=1e-4, abs=1e-6)

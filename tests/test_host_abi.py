@@ -242,6 +242,20 @@ def test_accumulator_is_opaque_and_refuses_unprepared_bytes():
         assert stepped.value == 1 and r.n_valid == 3 and r.loss == 0.5
 
 
+def test_stats_sum_adds_rows_in_order():
+    rng = np.random.default_rng(9)
+    for n in (0, 1, 7, 300):
+        rows = [{"loss_sum": float(rng.normal()), "entropy_sum": float(rng.random()), "kl_sum": float(rng.normal()),
+                 "obj_sum": float(rng.normal()), "n_valid": int(rng.integers(0, 100)),
+                 "n_clipped": int(rng.integers(0, 3)), "n_nonfinite": int(rng.integers(0, 2)),
+                 "n_valid_rows": int(rng.integers(0, 2))} for _ in range(n)]
+        want = {k: 0.0 if k.endswith("_sum") else 0 for k in oracle.STAT_KEYS}
+        for r in rows:                               # the oracle's chunk roll-up: rows in row order
+            for k in want:
+                want[k] += r[k]
+        assert ops.stats_sum(rows) == want
+
+
 # ---------------------------------------------------------------- ahead pass, cache, probe (host parts)
 
 def test_ahead_pass_gate_matches_oracle():

@@ -64,6 +64,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// The same for -lo and -hi, the negation taken by the instruction's source
+// modifiers (no separate sign flip).
+__device__ __forceinline__ uint32_t pack_bf16x2_neg(float lo, float hi) {
+    uint32_t r;
+    asm("v_cvt_pk_bf16_f32 %0, -%1, -%2" : "=v"(r) : "v"(lo), "v"(hi));
+    return r;
+}
+
 // ---------------------------------------------------------------- dtype traits
 
 template <int DT> struct In;
@@ -122,8 +130,13 @@ template <> struct Out<GRPO_BF16> {
         const uint32_t sg = neg ? 0x80008000u : 0u;
         if constexpr (N == 8) {
             uint4 v;
-            v.x = pack_bf16x2(d[0], d[1]) ^ sg; v.y = pack_bf16x2(d[2], d[3]) ^ sg;
-            v.z = pack_bf16x2(d[4], d[5]) ^ sg; v.w = pack_bf16x2(d[6], d[7]) ^ sg;
+            if (neg) {   // (uniform per token) the sign rides on the conversion
+                v.x = pack_bf16x2_neg(d[0], d[1]); v.y = pack_bf16x2_neg(d[2], d[3]);
+                v.z = pack_bf16x2_neg(d[4], d[5]); v.w = pack_bf16x2_neg(d[6], d[7]);
+            } else {
+                v.x = pack_bf16x2(d[0], d[1]); v.y = pack_bf16x2(d[2], d[3]);
+                v.z = pack_bf16x2(d[4], d[5]); v.w = pack_bf16x2(d[6], d[7]);
+            }
             st16(reinterpret_cast<uint4*>(p), v);
         } else {
             uint2 v;
@@ -695,23 +708,19 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         }
         // sweep 3: dz = coef * p, minus coef at the target.  Without the
         // bonus, coef is folded into the exponent: |coef| p_v = 2^(z_v log2(e)
-        // - (c2 - log2|coef|)), and its sign goes onto the stored bits.  The
-        // target element is rewritten by the lane that owns it from
-        // coef * p_y - coef.
+        // - (c2 - log2|coef|)), and its sign goes onto the stored bits.
         opaque_regs(x);
-        const int ky = ybad ? -1 : vy / TPR, ey = ybad ? -1 : y % VEC;   // ky: block-uniform
         const float c3 = r.c2 - log2f(fabsf(r.coef));
         const bool neg = r.coef < 0.0f;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = k * TPR + tid;
-            if (idx < nvec) sweep_dz<DTI, DTO>(orow, idx, x[k], r, c3, neg, k == ky && idx == vy, ey, zy);
+            if (idx < nvec) sweep_dz<DTI, DTO>(orow, idx, x[k], r, c3, neg, false, -1, 0.0f);
         }
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             const int idx = (NV + j) * TPR + tid;
-            if (idx < nvec)
-                sweep_dz<DTI, DTO>(orow, idx, s_tail[j * TPR + tid], r, c3, neg, NV + j == ky && idx == vy, ey, zy);
+            if (idx < nvec) sweep_dz<DTI, DTO>(orow, idx, s_tail[j * TPR + tid], r, c3, neg, false, -1, 0.0f);
         }
         // the re-read vectors: each is read and then written by the same lane,
         // so an in-place update stays ordered
@@ -719,8 +728,17 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         for (int g = 0; g < NG; g += 2) {
             const int i0 = (NV + NL + g) * TPR + tid, i1 = i0 + TPR;
             const uint4 a = vrow[min(i0, nvec - 1)], b = vrow[min(i1, nvec - 1)];
-            if (i0 < nvec) sweep_dz<DTI, DTO>(orow, i0, a, r, c3, neg, NV + NL + g == ky && i0 == vy, ey, zy);
-            if (i1 < nvec) sweep_dz<DTI, DTO>(orow, i1, b, r, c3, neg, NV + NL + g + 1 == ky && i1 == vy, ey, zy);
+            if (i0 < nvec) sweep_dz<DTI, DTO>(orow, i0, a, r, c3, neg, false, -1, 0.0f);
+            if (i1 < nvec) sweep_dz<DTI, DTO>(orow, i1, b, r, c3, neg, false, -1, 0.0f);
+        }
+        // The target element, coef * p_y - coef: rewritten by the lane that
+        // owns it, after (program order) its own store of the vector holding
+        // it; no vector of the sweep needs a test for the target.
+        if (!ybad && tid == own_tid) {
+            const float tty = fmaf(zy, kLog2e, -r.c2);
+            const float dy = r.eb == 0.0f ? fmaf(r.coef, __builtin_amdgcn_exp2f(tty), -r.coef)
+                                          : dz_with_bonus(tty, r.ea, r.eb) - r.coef;
+            Out<DTO>::scalar(orow, y, dy);
         }
     }
 }

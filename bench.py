@@ -655,10 +655,13 @@ def fused_kernel_label(V, dtype):
     """Which fused-loss kernel a contiguous [tokens x V] chunk of this dtype takes
     (the library's dispatch: 1024 threads x 19 register vectors, plus 9 LDS
     vectors per lane past that, plus up to 4 vectors per lane read in both
-    sweeps for bf16, else the streaming kernel)."""
+    sweeps for bf16, else the streaming kernel; rows off 16-byte alignment,
+    whose dlogits rows here share their phase, take the register kernel over
+    the aligned vectors covering them, at most V / vec + 1 of them)."""
     vec = 8 if dtype == "bf16" else 4
     if V % vec:
-        return "tok_stream_kernel"
+        nvec = (V + 2 * vec - 2) // vec
+        return "tok_reg_kernel (rows off alignment)" if nvec <= 1024 * 19 else "tok_stream_kernel"
     if V // vec <= 1024 * 19:
         return "tok_reg_kernel"
     if V // vec <= 1024 * 28:

@@ -501,6 +501,59 @@ __device__ __forceinline__ void sweep_sums_clamped(const uint4& v, float c, floa
     }
 }
 
+// Rows off 16-byte alignment (register kernel, MIS): the row is read through
+// the aligned vectors that cover it, and the first and last of those hold
+// elements outside the row.  For such a vector, elements e with
+// elo <= e < ehi belong to the row (element e of vector idx is row element
+// idx*VEC + e - hb); these helpers take only those.
+template <int DTI>
+__device__ __forceinline__ void sweep_sums_part(const uint4& v, int elo, int ehi, float c, float& s, float& w,
+                                                bool clamp) {
+    constexpr int VEC = In<DTI>::VEC;
+    float f[VEC];
+    In<DTI>::unpack(v, f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        if (e >= elo && e < ehi) {
+            const float tt = fmaf(f[e], kLog2e, -c);
+            const float ee = __builtin_amdgcn_exp2f(tt);
+            s += ee;
+            w = fmaf(ee, clamp ? fmaxf(tt, kNegClampLog2) : tt, w);
+        }
+}
+
+template <int DTI>
+__device__ __forceinline__ void sweep_max_part(const uint4& v, int elo, int ehi, float& m) {
+    constexpr int VEC = In<DTI>::VEC;
+    float f[VEC];
+    In<DTI>::unpack(v, f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        if (e >= elo && e < ehi) m = fmaxf(m, f[e]);
+}
+
+// dz of the row's elements in a partial vector, stored one element at a time
+// (the vector's other elements belong to neighbouring rows: never written)
+template <int DTI, int DTO>
+__device__ __forceinline__ void dz_part(void* orow, int64_t e0, const uint4& v, const TokenResult& r, float c3,
+                                        bool neg, int elo, int ehi) {
+    constexpr int VEC = In<DTI>::VEC;
+    float f[VEC];
+    In<DTI>::unpack(v, f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        if (e >= elo && e < ehi) {
+            float d;
+            if (r.eb == 0.0f) {
+                d = __builtin_amdgcn_exp2f(fmaf(f[e], kLog2e, -c3));
+                d = neg ? -d : d;
+            } else {
+                d = dz_with_bonus(fmaf(f[e], kLog2e, -r.c2), r.ea, r.eb);
+            }
+            Out<DTO>::scalar(orow, e0 + e, d);
+        }
+}
+
 // dz of one vector (element index idx*VEC..), stored; `own_y`: this vector
 // holds the target, element ey, whose value the caller passes as zy.
 template <int DTI, int DTO>
@@ -530,6 +583,29 @@ __device__ __forceinline__ void sweep_dz(void* orow, int64_t idx, const uint4& v
     Out<DTO>::template store<VEC>(orow, idx * VEC, d, r.eb == 0.0f && neg);
 }
 
+// A zero dlogits row for the register kernel: whole vectors with 16-byte
+// non-temporal stores; with MIS the row's elements of the first and last
+// (partial) vectors one at a time.
+template <int DTO, int VEC, int TPR, int NK, bool MIS>
+__device__ __forceinline__ void zero_row(void* orow, int tid, int ilo, unsigned nwhole, int hb, int nvec, int64_t V) {
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        const int idx = k * TPR + tid;
+        if ((unsigned)(idx - ilo) < nwhole) Out<DTO>::template zero<VEC>(orow, (int64_t)idx * VEC - hb);
+    }
+    if constexpr (MIS) {
+        const int last = nvec - 1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int idx = h == 0 ? 0 : last;
+            if ((h == 0 || last > 0) && tid == idx % TPR) {
+                const int e0 = idx * VEC - hb;
+                for (int e = e0 < 0 ? 0 : e0; e < e0 + VEC && e < (int)V; ++e) Out<DTO>::scalar(orow, e, 0.0f);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- register-resident kernel
 //
 // TPR threads per token row, NV 16-byte vectors per thread in registers and
@@ -540,10 +616,11 @@ __device__ __forceinline__ void sweep_dz(void* orow, int64_t idx, const uint4& v
 // twice.
 // TPR == 64: four token rows per 256-thread block, one wave each, wave-only
 // reductions.  TPR > 64: one row per block, cross-wave reduction through LDS.
-template <int DTI, int DTO, int TPR, int NV, bool GRAD, int NL = 0, int NG = 0>
+template <int DTI, int DTO, int TPR, int NV, bool GRAD, int NL = 0, int NG = 0, bool MIS = false>
 __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const TokParams p) {
     static_assert(NL == 0 || TPR == 1024, "LDS-held vectors are for the one-row-per-block path");
     static_assert(NG == 0 || (NL > 0 && NG % 2 == 0), "re-read vectors follow the LDS-held ones, in pairs");
+    static_assert(!MIS || (NL == 0 && NG == 0 && GRAD), "rows off alignment: registers only, gradient path");
     constexpr int VEC = In<DTI>::VEC;
     constexpr int WPR = TPR / 64;
     constexpr int RPB = TPR == 64 ? 4 : 1;
@@ -552,39 +629,54 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     const int64_t t = (int64_t)xcd_runs(blockIdx.x, gridDim.x) * RPB + lrow;
     if (t >= p.n_tok) return;   // wave-uniform (RPB > 1) or block-uniform (RPB == 1)
 
-    const int nvec = (int)(p.V / VEC);   // the register path only runs for V / VEC <= TPR * (NV + NL + NG)
     const int64_t src = token_source(p, t);
     if (src < 0) {
         if (tid == 0) bad_source_outputs<GRAD>(p, t);
         return;
     }
+    const char* irow = reinterpret_cast<const char*>(p.logits) + src * p.ld * In<DTI>::BYTES;
+    // Row geometry.  Aligned rows: vectors 0 .. nvec-1 of the row.  MIS: the
+    // 16-byte-aligned vectors covering the row, vector i holding row elements
+    // i*VEC - hb .. +VEC; the first and the last hold elements outside the
+    // row and are taken one element at a time; [ilo, ihi) are whole.  The
+    // output row has the input row's alignment phase (the dispatch checks it).
+    // An aligned vector holding one element of the row lies in the same
+    // 16-byte granule, so in the same page, as that element: its other bytes
+    // are read (and ignored), never written.
+    // The register path only runs for nvec <= TPR * (NV + NL + NG).
+    int hb = 0, nvec, ilo = 0, ihi;
+    const uint4* vrow;
+    if constexpr (MIS) {
+        const uintptr_t ia = reinterpret_cast<uintptr_t>(irow);
+        hb = (int)((ia & 15u) / In<DTI>::BYTES);
+        vrow = reinterpret_cast<const uint4*>(ia - (ia & 15u));
+        nvec = (int)((p.V + hb + VEC - 1) / VEC);
+        ilo = 1;
+        ihi = nvec - 1;
+    } else {
+        vrow = reinterpret_cast<const uint4*>(irow);
+        nvec = (int)(p.V / VEC);
+        ihi = nvec;
+    }
+    // whole vector idx: (unsigned)(idx - ilo) < nwhole
+    const unsigned nwhole = ihi > ilo ? (unsigned)(ihi - ilo) : 0u;
     void* orow = nullptr;
     if constexpr (GRAD) {
         if (p.dlogits) orow = reinterpret_cast<char*>(p.dlogits) + src * p.ld_out * Out<DTO>::BYTES;
     }
-
     if (p.mask[src] == 0) {
         if (tid == 0) masked_outputs<GRAD>(p, t);
         if constexpr (GRAD) {
-            if (orow) {
-#pragma unroll
-                for (int k = 0; k < NV + NL + NG; ++k) {
-                    const int idx = k * TPR + tid;
-                    if (idx < nvec) Out<DTO>::template zero<VEC>(orow, idx * VEC);
-                }
-            }
+            if (orow) zero_row<DTO, VEC, TPR, NV + NL + NG, MIS>(orow, tid, ilo, nwhole, hb, nvec, p.V);
         }
         return;
     }
-
-    const char* irow = reinterpret_cast<const char*>(p.logits) + src * p.ld * In<DTI>::BYTES;
-    const uint4* vrow = reinterpret_cast<const uint4*>(irow);
 
     // Target logit: read by the one lane that owns element y (it alone later
     // writes dlogits[y], so an in-place update stays ordered).
     const int32_t y = p.target[src];
     const bool ybad = (uint32_t)y >= (uint64_t)p.V;
-    const int vy = ybad ? 0 : y / VEC;
+    const int vy = ybad ? 0 : (y + hb) / VEC;
     const int own_tid = vy % TPR;
     float zy_mine = 0.0f;
     if (!ybad && tid == own_tid) zy_mine = In<DTI>::scalar(irow, y);
@@ -622,12 +714,24 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     // (a -inf or NaN logit, a spread of more than ~80 nats within one lane)
     // takes the exact max-shifted sweeps instead.
     float c = -INFINITY, s = 0.0f, w = 0.0f;   // an empty lane: s = 0
+    // MIS: the last (partial) vector is vector klast of lane llast
+    [[maybe_unused]] const int klast = (nvec - 1) / TPR, llast = (nvec - 1) % TPR;
     if (tid < nvec) {
         float f[VEC];
         In<DTI>::unpack(x[0], f);
-        float m0 = f[0];
+        float m0;
+        if constexpr (MIS) {
+            // lane tid's first vector is vector tid: only the row's elements
+            const int elo = hb - tid * VEC, ehi = (int)p.V + hb - tid * VEC;
+            m0 = -INFINITY;
 #pragma unroll
-        for (int e = 1; e < VEC; ++e) m0 = fmaxf(m0, f[e]);
+            for (int e = 0; e < VEC; ++e)
+                if (e >= elo && e < ehi) m0 = fmaxf(m0, f[e]);
+        } else {
+            m0 = f[0];
+#pragma unroll
+            for (int e = 1; e < VEC; ++e) m0 = fmaxf(m0, f[e]);
+        }
         c = m0 * kLog2e;
         if (!isfinite(c)) c = 0.0f;
     }
@@ -635,11 +739,19 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     // whole array would make every wave wait for all of its loads before the
     // first sum, while per vector the sweep follows the loads as they land.
 #pragma unroll
-    for (int k = 0; k < NV; ++k)
-        if (k * TPR + tid < nvec) {
+    for (int k = 0; k < NV; ++k) {
+        const int idx = k * TPR + tid;
+        if ((unsigned)(idx - ilo) < nwhole) {
             opaque_vec(x[k]);
             sweep_sums<DTI>(x[k], c, s, w);
         }
+        if constexpr (MIS) {
+            if ((k == 0 && tid == 0) || (k == klast && tid == llast && nvec > 1)) {
+                opaque_vec(x[k]);
+                sweep_sums_part<DTI>(x[k], hb - idx * VEC, (int)p.V + hb - idx * VEC, c, s, w, false);
+            }
+        }
+    }
     if constexpr (NL > 0) {
         // this wave's direct-to-LDS loads have landed (each lane reads only
         // the 16 bytes its own wave's load wrote)
@@ -666,8 +778,14 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         opaque_regs(x);
         float m = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < NV; ++k)
-            if (k * TPR + tid < nvec) sweep_max<DTI>(x[k], m);
+        for (int k = 0; k < NV; ++k) {
+            const int idx = k * TPR + tid;
+            if ((unsigned)(idx - ilo) < nwhole) sweep_max<DTI>(x[k], m);
+            if constexpr (MIS) {
+                if ((k == 0 && tid == 0) || (k == klast && tid == llast && nvec > 1))
+                    sweep_max_part<DTI>(x[k], hb - idx * VEC, (int)p.V + hb - idx * VEC, m);
+            }
+        }
 #pragma unroll
         for (int j = 0; j < NL; ++j)
             if ((NV + j) * TPR + tid < nvec) sweep_max<DTI>(s_tail[j * TPR + tid], m);
@@ -682,8 +800,14 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         w = 0.0f;
         opaque_regs(x);
 #pragma unroll
-        for (int k = 0; k < NV; ++k)
-            if (k * TPR + tid < nvec) sweep_sums_clamped<DTI>(x[k], c, s, w);
+        for (int k = 0; k < NV; ++k) {
+            const int idx = k * TPR + tid;
+            if ((unsigned)(idx - ilo) < nwhole) sweep_sums_clamped<DTI>(x[k], c, s, w);
+            if constexpr (MIS) {
+                if ((k == 0 && tid == 0) || (k == klast && tid == llast && nvec > 1))
+                    sweep_sums_part<DTI>(x[k], hb - idx * VEC, (int)p.V + hb - idx * VEC, c, s, w, true);
+            }
+        }
 #pragma unroll
         for (int j = 0; j < NL; ++j)
             if ((NV + j) * TPR + tid < nvec) sweep_sums_clamped<DTI>(s_tail[j * TPR + tid], c, s, w);
@@ -699,11 +823,7 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     if constexpr (GRAD) {
         if (!orow) return;
         if (r.coef == 0.0f && r.eb == 0.0f) {   // zero advantage or clipped, no bonus: the row is zero
-#pragma unroll
-            for (int k = 0; k < NV + NL + NG; ++k) {
-                const int idx = k * TPR + tid;
-                if (idx < nvec) Out<DTO>::template zero<VEC>(orow, idx * VEC);
-            }
+            zero_row<DTO, VEC, TPR, NV + NL + NG, MIS>(orow, tid, ilo, nwhole, hb, nvec, p.V);
             return;
         }
         // sweep 3: dz = coef * p, minus coef at the target.  Without the
@@ -712,10 +832,17 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
         opaque_regs(x);
         const float c3 = r.c2 - log2f(fabsf(r.coef));
         const bool neg = r.coef < 0.0f;
+        // whole vector idx starts at row element idx*VEC - hb
+        void* ovec = reinterpret_cast<char*>(orow) - (int64_t)hb * Out<DTO>::BYTES;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = k * TPR + tid;
-            if (idx < nvec) sweep_dz<DTI, DTO>(orow, idx, x[k], r, c3, neg, false, -1, 0.0f);
+            if ((unsigned)(idx - ilo) < nwhole) sweep_dz<DTI, DTO>(ovec, idx, x[k], r, c3, neg, false, -1, 0.0f);
+            if constexpr (MIS) {
+                if ((k == 0 && tid == 0) || (k == klast && tid == llast && nvec > 1))
+                    dz_part<DTI, DTO>(orow, (int64_t)idx * VEC - hb, x[k], r, c3, neg, hb - idx * VEC,
+                                      (int)p.V + hb - idx * VEC);
+            }
         }
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
@@ -745,8 +872,9 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
 
 // ---------------------------------------------------------------- streaming kernel
 //
-// Rows the register/LDS path cannot take: V beyond its capacity, or a stride,
-// base or V that leaves rows off 16-byte alignment.  256 threads per token
+// Rows the register/LDS path cannot take: V beyond its capacity, or rows off
+// 16-byte alignment whose dlogits rows have another dtype or another
+// alignment phase.  256 threads per token
 // stream the row from memory: 16-byte vectors over its aligned interior,
 // single elements for the head before the first 16-byte boundary and the tail
 // after the last whole vector.  The sums use the register path's per-lane
@@ -1285,10 +1413,33 @@ constexpr RegCfg kRegCfgs[] = {{64, 1, 0, 0},    {64, 2, 0, 0},   {64, 4, 0, 0},
                                {1024, 19, 9, 4}};
 
 template <int DTI, int DTO, bool GRAD>
-hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st) {
+hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st, bool mis = false) {
     const int rpb = c.tpr == 64 ? 4 : 1;
     const dim3 grid((unsigned)((p.n_tok + rpb - 1) / rpb));
     const dim3 block(c.tpr == 64 ? 256 : c.tpr);
+    if constexpr (GRAD && DTI == DTO) {
+        if (mis) {
+#define GRPO_MIS_CASE(TPR_, NV_)                                                                                 \
+            if (c.tpr == TPR_ && c.nv == NV_ && c.nl == 0 && c.ng == 0) {                                        \
+                hipLaunchKernelGGL((tok_reg_kernel<DTI, DTO, TPR_, NV_, GRAD, 0, 0, true>), grid, block, 0, st, p); \
+                return hipGetLastError();                                                                        \
+            }
+            GRPO_MIS_CASE(64, 1)
+            GRPO_MIS_CASE(64, 2)
+            GRPO_MIS_CASE(64, 4)
+            GRPO_MIS_CASE(64, 8)
+            GRPO_MIS_CASE(256, 4)
+            GRPO_MIS_CASE(256, 8)
+            GRPO_MIS_CASE(256, 16)
+            GRPO_MIS_CASE(256, 24)
+            GRPO_MIS_CASE(1024, 8)
+            GRPO_MIS_CASE(1024, 12)
+            GRPO_MIS_CASE(1024, 16)
+            GRPO_MIS_CASE(1024, 19)
+#undef GRPO_MIS_CASE
+            return hipErrorInvalidValue;
+        }
+    }
 #define GRPO_REG_CASE(TPR_, NV_, NL_, NG_)                                                                  \
     if (c.tpr == TPR_ && c.nv == NV_ && c.nl == NL_ && c.ng == NG_) {                                       \
         hipLaunchKernelGGL((tok_reg_kernel<DTI, DTO, TPR_, NV_, GRAD, NL_, NG_>), grid, block, 0, st, p); \
@@ -1313,7 +1464,7 @@ hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st) {
 }
 
 template <int DTI, int DTO, bool GRAD>
-hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st) {
+hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st, bool mis_ok = false) {
     if (p.n_tok == 0) return hipSuccess;
     // Forward only, rows past 1024 vectors stream: the row need not stay on
     // chip, and many 256-thread blocks per CU keep more reads in flight than
@@ -1324,6 +1475,17 @@ hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st) {
         for (const RegCfg& c : kRegCfgs) {
             if (c.ng > 0 && !(GRAD && DTI == GRPO_BF16)) continue;
             if ((int64_t)c.tpr * (c.nv + c.nl + c.ng) >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st);
+        }
+    }
+    // Rows off 16-byte alignment whose gradient rows share their alignment
+    // phase (in place, or the same dtype, stride and base phase): the register
+    // kernel over the aligned vectors that cover each row, the row still read
+    // once.  A row spans at most V / VEC + 1 such vectors.
+    if (GRAD && DTI == DTO && !vec_ok && mis_ok) {
+        const int64_t nvec = (p.V + 2 * In<DTI>::VEC - 2) / In<DTI>::VEC;
+        for (const RegCfg& c : kRegCfgs) {
+            if (c.nl > 0 || c.ng > 0) continue;
+            if ((int64_t)c.tpr * c.nv >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st, true);
         }
     }
     hipLaunchKernelGGL((tok_stream_kernel<DTI, DTO, GRAD>), dim3((unsigned)p.n_tok), dim3(kStreamTPR), 0, st, p);
@@ -1503,12 +1665,17 @@ extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {
     const int vec = di == GRPO_BF16 ? 8 : 4;
     bool vec_ok = aligned16(a->logits) && a->ld % vec == 0 && a->V % vec == 0;
     if (a->dlogits) vec_ok = vec_ok && aligned16(a->dlogits) && (a->ld_out * out_b) % 16 == 0 && ((int64_t)vec * out_b) % 8 == 0;
+    // rows off alignment, each gradient row in its logits row's alignment phase
+    // (every row: same base phase and the same stride in bytes modulo 16)
+    const bool mis_ok = di == dout && (reinterpret_cast<uintptr_t>(a->logits) % in_b) == 0 &&
+                        (!a->dlogits || ((reinterpret_cast<uintptr_t>(a->dlogits) - reinterpret_cast<uintptr_t>(a->logits)) % 16 == 0 &&
+                                         ((a->ld_out - a->ld) * in_b) % 16 == 0));
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
-    if (di == GRPO_BF16 && dout == GRPO_BF16) e = launch_tok<GRPO_BF16, GRPO_BF16, true>(p, vec_ok, st);
+    if (di == GRPO_BF16 && dout == GRPO_BF16) e = launch_tok<GRPO_BF16, GRPO_BF16, true>(p, vec_ok, st, mis_ok);
     else if (di == GRPO_BF16) e = launch_tok<GRPO_BF16, GRPO_F32, true>(p, vec_ok, st);
     else if (dout == GRPO_BF16) e = launch_tok<GRPO_F32, GRPO_BF16, true>(p, vec_ok, st);
-    else e = launch_tok<GRPO_F32, GRPO_F32, true>(p, vec_ok, st);
+    else e = launch_tok<GRPO_F32, GRPO_F32, true>(p, vec_ok, st, mis_ok);
     if (e != hipSuccess) return check_launch(e, "grpo_loss_fwd_bwd (token kernel)");
     if (defer) return ok();
     const grpo::ObjTerms obj{a->scale, a->denom, a->row_weight, a->ent_coef, a->ref_logp ? a->kl_coef : 0.0f};

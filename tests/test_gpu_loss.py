@@ -58,7 +58,13 @@ CASES = [
     (1, torch.float32, torch.float32, 10),
     (7, torch.bfloat16, torch.bfloat16, 17),
     (1000, torch.bfloat16, torch.bfloat16, 23),
+    # rows off 16-byte alignment (V and the row stride odd), dlogits in the
+    # same phase: the register kernel over the aligned vectors covering each
+    # row (256 threads x 16, 1024 x 8, 1024 x 19 vectors; fp32 256 x 24)
     (50257, torch.bfloat16, torch.bfloat16, 11),
+    (32001, torch.bfloat16, torch.bfloat16, 13),
+    (151939, torch.bfloat16, torch.bfloat16, 5),
+    (20001, torch.float32, torch.float32, 6),
     (200000, torch.bfloat16, torch.bfloat16, 5),
     # rows past the register file: the tail of each lane's vectors in LDS
     (155656, torch.bfloat16, torch.bfloat16, 5),
@@ -97,18 +103,28 @@ def test_loss_matches_oracle(V, din, dout, n):
                                         (torch.bfloat16, 202048, 202064, 4), (torch.bfloat16, 256000, 256016, 3),
                                         (torch.bfloat16, 50257, 50263, 9)])
 def test_padded_row_stride_and_inplace(din, V, ld, n):
-    # logits rows padded to ld > V; then the same chunk updated in place
+    # logits rows padded to ld > V: dlogits into a contiguous tensor, into one
+    # with the logits' stride, then the same chunk updated in place
     # (202048: part of each row in LDS; 256000: part read again in the
-    # gradient sweep; 50257 with an odd stride: rows of every alignment phase
-    # through the streaming kernel)
+    # gradient sweep; 50257 with an odd stride: rows of every alignment phase,
+    # the contiguous output in another phase than its logits row -> the
+    # streaming kernel, the strided and in-place ones in the same phase ->
+    # the register kernel over aligned vectors)
     d = make_chunk(n, V, din, seed=3, ld=ld)
     scale = 0.01
     ref = run_oracle(d, scale)
     ws = run_gpu(d, scale=scale)
     assert_tokens_match(ws, ref, d)
+    strided = torch.full((n, ld), 7.0, dtype=din, device=DEV)
+    ws1 = run_gpu(d, scale=scale, dlogits=strided[:, :V])
+    assert_tokens_match(ws1, ref, d)
+    assert torch.all(strided[:, V:] == 7.0)                  # the padding columns are never written
     ws2 = run_gpu(d, scale=scale, dlogits="inplace")
-    assert torch.equal(ws2["dlogits"], ws["dlogits"])
-    assert torch.equal(d["logits"], ws["dlogits"])           # the logits buffer now holds dlogits
+    assert_tokens_match(ws2, ref, d)
+    assert torch.equal(ws2["dlogits"], ws1["dlogits"])
+    if V % 8 == 0:
+        assert torch.equal(ws2["dlogits"], ws["dlogits"])
+    assert torch.equal(d["logits"], ws2["dlogits"])          # the logits buffer now holds dlogits
 
 
 def test_denominator_from_device_count():
@@ -164,7 +180,8 @@ def test_bad_targets_and_nan_logits_are_flagged_not_read():
 @pytest.mark.parametrize("V,dtype,first", [(151936, torch.bfloat16, 8192), (16384, torch.bfloat16, 2048),
                                            (4096, torch.bfloat16, 512), (1024, torch.float32, 256),
                                            (202048, torch.bfloat16, 8192), (256000, torch.bfloat16, 8192),
-                                           (262152, torch.bfloat16, 2056), (50257, torch.bfloat16, 2056),
+                                           (262152, torch.bfloat16, 2056), (50257, torch.bfloat16, 8192),
+                                           (32001, torch.bfloat16, 2048),
                                            (40960, torch.bfloat16, 2048)])
 def test_special_rows(V, dtype, first):
     # Rows the one-sweep sums cannot take and that go through the exact

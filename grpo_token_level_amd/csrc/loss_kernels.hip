@@ -1407,10 +1407,10 @@ struct RegCfg {
 // last one reads up to 4 more vectors per lane from memory in each sweep, so
 // bf16 rows up to 262 144 logits read at most 1/8 of the row twice (gradient
 // path; with fp32 logits that variant would spill, and such rows stream).
-constexpr RegCfg kRegCfgs[] = {{64, 1, 0, 0},    {64, 2, 0, 0},   {64, 4, 0, 0},    {64, 8, 0, 0},
-                               {256, 4, 0, 0},   {256, 8, 0, 0},  {256, 16, 0, 0},  {256, 24, 0, 0}, {1024, 8, 0, 0},
-                               {1024, 12, 0, 0}, {1024, 16, 0, 0}, {1024, 19, 0, 0}, {1024, 19, 9, 0},
-                               {1024, 19, 9, 4}};
+constexpr RegCfg kRegCfgs[] = {{64, 1, 0, 0},    {64, 2, 0, 0},    {64, 4, 0, 0},    {64, 8, 0, 0},
+                               {256, 4, 0, 0},   {256, 8, 0, 0},   {256, 16, 0, 0},  {512, 12, 0, 0},
+                               {256, 24, 0, 0},  {512, 16, 0, 0},  {1024, 8, 0, 0},  {1024, 12, 0, 0},
+                               {1024, 16, 0, 0}, {1024, 19, 0, 0}, {1024, 19, 9, 0}, {1024, 19, 9, 4}};
 
 template <int DTI, int DTO, bool GRAD>
 hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st, bool mis = false) {
@@ -1432,6 +1432,8 @@ hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st, bool 
             GRPO_MIS_CASE(256, 8)
             GRPO_MIS_CASE(256, 16)
             GRPO_MIS_CASE(256, 24)
+            GRPO_MIS_CASE(512, 12)
+            GRPO_MIS_CASE(512, 16)
             GRPO_MIS_CASE(1024, 8)
             GRPO_MIS_CASE(1024, 12)
             GRPO_MIS_CASE(1024, 16)
@@ -1453,6 +1455,8 @@ hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st, bool 
     GRPO_REG_CASE(256, 8, 0, 0)
     GRPO_REG_CASE(256, 16, 0, 0)
     GRPO_REG_CASE(256, 24, 0, 0)
+    GRPO_REG_CASE(512, 12, 0, 0)
+    GRPO_REG_CASE(512, 16, 0, 0)
     GRPO_REG_CASE(1024, 8, 0, 0)
     GRPO_REG_CASE(1024, 12, 0, 0)
     GRPO_REG_CASE(1024, 16, 0, 0)

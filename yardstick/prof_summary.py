@@ -83,10 +83,23 @@ def pmc(args):
              f"{args.kernel}, {len(kf)} launches:",
              f"  FETCH_SIZE {fetch:.1f} KiB/launch -> {fetch / f_fetch * 1024 / 1e9:.4f} GB read",
              f"  WRITE_SIZE {write:.1f} KiB/launch -> {write / f_write * 1024 / 1e9:.4f} GB written",
-             f"  traffic {traffic / 1e9:.4f} GB/launch", "",
-             "TRAFFIC_JSON " + json.dumps(rec)]
+             f"  traffic {traffic / 1e9:.4f} GB/launch", ""]
+    algo = _bench_algorithmic_bytes(args.bench_log) if args.bench_log else None
+    if algo:
+        rec["algorithmic_bytes_per_launch"] = algo
+        lines += [f"algorithmic bytes per launch (the profiled bench run's own line): {algo / 1e9:.4f} GB",
+                  f"  traffic / algorithmic = {traffic / algo:.4f}", ""]
+    lines.append("TRAFFIC_JSON " + json.dumps(rec))
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
+
+
+def _bench_algorithmic_bytes(path):
+    with open(path) as f:
+        for line in f:
+            if line.startswith("{") and '"roofline"' in line:
+                return json.loads(line)["roofline"].get("algorithmic_bytes_per_launch")
+    return None
 
 
 def load_traffic(path, kernel_source=KERNEL_SOURCE):
@@ -159,8 +172,9 @@ def main():
     p.add_argument("write")
     p.add_argument("out")
     p.add_argument("--cmd", required=True)
-    p.add_argument("--kernel", default="tok_reg_kernel<1, 1, 1024, 19, true, 0, 0>")
+    p.add_argument("--kernel", default="tok_reg_kernel<1, 1, 1024, 19, true, 0, 0, false>")
     p.add_argument("--workload", default="qwen")
+    p.add_argument("--bench-log", default=None, help="stdout of one of the profiled bench.py runs")
     m = sub.add_parser("mfma")
     m.add_argument("csv")
     m.add_argument("out")

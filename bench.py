@@ -88,6 +88,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="padded workloads: capture the step's device work in a HIP graph once and replay it "
                          "(the launch-bound tiny step); the roofline then uses graph replay time / launches")
+    ap.add_argument("--keep-z", action="store_true",
+                    help="compact workload: the LM head keeps each chunk's fp32 logits for pass 2 "
+                         "(GRPO_LMHEAD_KEEP_Z: one [tokens x V] matrix per chunk in place of the recompute)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     return ap.parse_args()
@@ -479,7 +482,7 @@ class DynamicStep(PaddedStep):
 # ---------------------------------------------------------------- compaction: fused LM head
 
 class CompactStep:
-    def __init__(self, wl, seed, torch, ops, timed):
+    def __init__(self, wl, seed, torch, ops, timed, keep_z=False):
         from synth import compaction_batch
         self.torch, self.ops, self.timed = torch, ops, timed
         b = self.b = compaction_batch(seed=seed)
@@ -517,7 +520,9 @@ class CompactStep:
         self.N = torch.empty(1, dtype=torch.int64, device="cuda")
         self.chunks = [(a, min(a + b["micro"], plan["n_rows"])) for a in range(0, plan["n_rows"], b["micro"])]
         max_tok = int(max(self.off[e] - self.off[a] for a, e in self.chunks))
-        self.workspace = torch.empty(ops.lmhead_workspace_bytes(max_tok, H, V), dtype=torch.uint8, device="cuda")
+        self.keep_z = keep_z
+        self.workspace = torch.empty(ops.lmhead_workspace_bytes(max_tok, H, V, keep_z), dtype=torch.uint8,
+                                     device="cuda")
         self.ws = ops.loss_workspace(max_tok, b["micro"], "cuda")
         self.tok_row = torch.empty(max_tok, dtype=torch.int32, device="cuda")
         self.row_off_dev = _g(torch, np.concatenate([self.off[a:e + 1] - self.off[a] for a, e in self.chunks]))
@@ -527,7 +532,8 @@ class CompactStep:
         self.stats_host = torch.empty((len(self.chunks), ops.STATS_BYTES), dtype=torch.uint8).pin_memory()
         self.n_valid = int(mask.sum())
         self.H, self.V = H, V
-        self.logits_dtype = "none (h and W bf16; logits never materialised)"
+        self.logits_dtype = ("fp32 logits of one chunk kept for pass 2 (GRPO_LMHEAD_KEEP_Z)" if keep_z else
+                             "none (h and W bf16; logits never materialised)")
 
     def __call__(self):
         torch, ops, b = self.torch, self.ops, self.b
@@ -552,7 +558,7 @@ class CompactStep:
             ev = self.timed.begin()
             ops.lmhead_fwd_bwd(self.h[t0:t1], self.W, self.Wt, self.target[t0:t1], self.mask[t0:t1],
                                self.old[t0:t1], tr, self.adv_dev[a:e], ro, self.dW, denom=self.N,
-                               dh=self.dh[t0:t1], ws=ws, workspace=self.workspace)
+                               dh=self.dh[t0:t1], ws=ws, workspace=self.workspace, keep_z=self.keep_z)
             self.timed.end(ev, 6.0 * self.V * self.H * int(self.mask_np[t0:t1].sum()))
         self.stats_host.copy_(self.stats_dev, non_blocking=True)
         torch.cuda.current_stream().synchronize()
@@ -711,6 +717,11 @@ def main():
             sys.exit(2)
         from synth import WORKLOADS
         extra["over"] = dict(n_prompts=WORKLOADS["tiny"]["n_prompts"] * args.replicate, mini=0, micro=0)
+    if args.keep_z:
+        if cls is not CompactStep:
+            print("--keep-z applies to the compact workload", file=sys.stderr)
+            sys.exit(2)
+        extra["keep_z"] = True
     if args.vocab:
         if cls is not PaddedStep or args.vocab < 1:
             print("--vocab applies to the padded workloads (qwen, long, tiny) and must be positive", file=sys.stderr)
@@ -769,7 +780,9 @@ def main():
         achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "grpo_lmhead_fwd_bwd per 4-row chunk (bf16 MFMA GEMMs + epilogues)",
+                "kernel": "grpo_lmhead_fwd_bwd per 4-row chunk (bf16 MFMA GEMMs + epilogues"
+                          + ("; pass 2 from the kept fp32 logits)" if getattr(step, "keep_z", False) else
+                             "; pass 2 recomputes the logits)"),
                 "algorithmic_flops_per_launch": int(units // launches), "avg_launch_ms": round(tot_ms / launches, 4)}
     else:
         achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e9

@@ -74,7 +74,7 @@ class LmheadArgs(ctypes.Structure):
                 ("n_tok", _i64), ("H", _i64), ("V", _i64),
                 ("target", _p), ("mask", _p), ("old_logp", _p), ("tok_row", _p), ("adv_row", _p),
                 ("row_off", _p), ("n_rows", _i64),
-                ("eps_low", _f32), ("eps_high", _f32), ("scale", _f32), ("reserved1", _i32),
+                ("eps_low", _f32), ("eps_high", _f32), ("scale", _f32), ("flags", _i32),
                 ("denom", _p), ("dh", _p), ("dW", _p),
                 ("logp", _p), ("lse", _p), ("entropy", _p), ("loss_tok", _p), ("tok_flags", _p),
                 ("row_stats", _p), ("chunk_stats", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
@@ -108,6 +108,7 @@ class Probe(ctypes.Structure):
     _fields_ = [("bound", ctypes.c_double), ("max_fraction", ctypes.c_double), ("done", _i32), ("passed", _i32)]
 
 
+LMHEAD_KEEP_Z = 1
 LMHEAD_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 PROBE_STRICT_BOUND = 0.05
@@ -146,6 +147,7 @@ PROTOTYPES = {
     "grpo_stats_sum": (ctypes.c_int, [_p, _i64, ctypes.POINTER(Stats)]),
     "grpo_transpose_bf16": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, _p, _i64]),
     "grpo_lmhead_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64]),
+    "grpo_lmhead_workspace_size_flags": (ctypes.c_size_t, [_i64, _i64, _i64, _i32]),
     "grpo_lmhead_fwd_bwd": (ctypes.c_int, [_p, ctypes.POINTER(LmheadArgs)]),
     "grpo_lmhead_fwd_bwd_noalloc": (ctypes.c_int, [_p, ctypes.POINTER(LmheadArgs)]),
     "grpo_needs_ahead_pass": (ctypes.c_int32, [_i64, _i32, _i32]),

@@ -18,12 +18,17 @@
 //           picks out the target logit.  A merge kernel combines the slices
 //           (fixed order) into logsumexp, entropy, log-prob, the surrogate and
 //           the gradient coefficient.
-//   pass 2  per vocabulary chunk (equal chunks of at most 65536 columns): the
-//           GEMM recomputes z and its epilogue writes dz = coef*(softmax -
-//           onehot) in bf16 (row-major and transposed) into a bounded
-//           workspace; then dh (+)= dz W_c (split-K, one fp32 partial per
-//           split, summed in order at the end) and dW_c += dz^T h, two more
-//           MFMA GEMMs with fp32 accumulation.
+//           With a caller workspace the epilogue also stores z (fp32) of
+//           the valid tokens.
+//   pass 2  per vocabulary chunk: dz = coef*(softmax - onehot) in bf16
+//           (row-major and transposed) into the workspace, from the stored z
+//           by an elementwise kernel, or (the fixed-scratch entry point, in
+//           chunks of at most 65536 columns) by a GEMM that recomputes z and
+//           forms dz in its epilogue; both take the same arithmetic on the
+//           same fp32 z, so dz has the same bits either way.  Then dh (+)=
+//           dz W_c (split-K, one fp32 partial per split, summed in order at
+//           the end) and dW_c += dz^T h, two more MFMA GEMMs with fp32
+//           accumulation.
 // All products use one kernel shape, C[m,n] = sum_k A[m,k] B[n,k] with both
 // operands K-contiguous ("NT"): W for pass 1, W^T for dh, h^T and dz^T for dW.
 //
@@ -56,6 +61,7 @@ using grpo_dev::kLog2e;
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -113,6 +119,8 @@ struct GemmArgs {
     int n_parts;
     const int32_t* target;
     float* zy;           // zy[m] = z[m, target[m]]
+    float* zst;          // NULL, or z itself: zst[m * ld_zst + n] (fp32, for pass 2 without a recompute)
+    int64_t ld_zst;
     // EPI_DZ (per-token arrays indexed by row m; target by the A row)
     const float* c2;     // log2-domain logsumexp per token
     const float* coef;   // gradient coefficient per token
@@ -493,8 +501,115 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
                 const int y = ep_y[i];
                 if (y >= nb && y < nb + ncols) g.zy[m] = row[y - nb];
             }
+            if (g.zst) {
+                // z itself, from the same staged rows: lane l writes column
+                // quad l%32 of rows 2k + l/32 (two 512-byte row segments per
+                // store; N % 4 == 0, so a quad is all in or all out), with
+                // the non-temporal hint: z is read back only after the pass
+                const int qc = lane & 31, rh = lane >> 5;
+                const int n = n0 + wn * WN + qc * 4;
+                const int mb = m0 + wm * WM + i * 32 + rh;
+                if (n < g.N) {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k)
+                        if (mb + 2 * k < M)
+                            __builtin_nontemporal_store(
+                                *reinterpret_cast<const f32x4*>(T + (2 * k + rh) * EPI_ROW_Q + qc * 4),
+                                reinterpret_cast<f32x4*>(g.zst + (int64_t)(mb + 2 * k) * g.ld_zst + n));
+                }
+            }
             __syncthreads();
         }
+    }
+}
+
+// dz of one vocabulary chunk from the stored z (pass 2 without a recompute):
+// the dz epilogue's arithmetic on the same fp32 values, so the same bits.
+// Block: 64 compact token rows x 128 chunk columns, 256 threads; wave w
+// reads rows w*16 + 2k + l/32 (k < 8), column quad l%32, as 512-byte row
+// segments.  dz goes out row-major (8-byte stores), dz^T through LDS as
+// 128-byte token segments; rows [count, round_up(count, 64)) of dz^T are
+// written as zeros (the K padding of the dW GEMM).
+struct DzArgs {
+    const float* z;        // z[m * ld_z + col0 + c]
+    int64_t ld_z;
+    int col0, vc;          // chunk start, width (vc % 4 == 0)
+    const int32_t* count;  // valid tokens (compact rows)
+    const int32_t* vidx;   // token of compact row m
+    const int32_t* target;
+    const float* c2;
+    const float* coef;
+    const float* ea;
+    const float* eb;
+    int bonus;
+    uint16_t* dz;          // dz[m * ld_dz + c]
+    int64_t ld_dz;
+    uint16_t* dzT;         // dzT[c * ld_dzT + m]
+    int64_t ld_dzT;
+};
+
+__global__ __launch_bounds__(256) void dz_from_z_kernel(const DzArgs a) {
+    constexpr int TR = 64, TC = 128, TROW = TR * 2 + 16;   // dz^T staging: [column][token] bf16, padded rows
+    __shared__ __attribute__((aligned(16))) char s_t[TC * TROW];
+    __shared__ float s_c2[TR], s_cf[TR], s_ea[TR], s_eb[TR];
+    __shared__ int s_y[TR];
+    const int cnt = *a.count;
+    const int m0 = blockIdx.y * TR, n0 = blockIdx.x * TC;
+    if (m0 >= (cnt + kTokPad - 1) / kTokPad * kTokPad) return;   // block-uniform
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (tid < TR) {
+        const int m = m0 + tid;
+        const bool in = m < cnt;
+        s_c2[tid] = in ? a.c2[m] : 0.0f;
+        s_cf[tid] = in ? a.coef[m] : 0.0f;
+        s_ea[tid] = in && a.bonus ? a.ea[m] : 0.0f;
+        s_eb[tid] = in && a.bonus ? a.eb[m] : 0.0f;
+        s_y[tid] = in ? a.target[a.vidx[m]] : -1;
+    }
+    __syncthreads();
+    const int qc = lane & 31, rh = lane >> 5;
+    const int c = n0 + qc * 4;          // chunk column of this lane's quad
+    const bool cin = c < a.vc;
+    float4 zv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int ml = wave * 16 + 2 * k + rh, m = m0 + ml;
+        zv[k] = (cin && m < cnt) ? *reinterpret_cast<const float4*>(a.z + (int64_t)m * a.ld_z + a.col0 + c)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int ml = wave * 16 + 2 * k + rh, m = m0 + ml;
+        const float zz[4] = {zv[k].x, zv[k].y, zv[k].z, zv[k].w};
+        float d[4];
+        const float cf = s_cf[ml], c2 = s_c2[ml];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float tt = fmaf(zz[u], kLog2e, -c2);
+            const float pp = __builtin_amdgcn_exp2f(tt);
+            float x;
+            if (!a.bonus) x = cf * pp;
+            else x = pp > 0.0f ? pp * fmaf(s_eb[ml], tt, s_ea[ml]) : 0.0f;
+            if (s_y[ml] == a.col0 + c + u) x -= cf;
+            d[u] = m < cnt ? x : 0.0f;
+        }
+        const uint32_t lo = pack2(d[0], d[1]), hi = pack2(d[2], d[3]);
+        if (cin && m < cnt) *reinterpret_cast<uint2*>(a.dz + (int64_t)m * a.ld_dz + c) = make_uint2(lo, hi);
+        uint16_t* col = reinterpret_cast<uint16_t*>(s_t + (qc * 4) * TROW) + ml;
+        col[0] = (uint16_t)(lo & 0xffffu);
+        col[TROW / 2] = (uint16_t)(lo >> 16);
+        col[TROW] = (uint16_t)(hi & 0xffffu);
+        col[3 * TROW / 2] = (uint16_t)(hi >> 16);
+    }
+    __syncthreads();
+    // dz^T: 128 columns x 8 chunks of 16 bytes (8 tokens each)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int piece = it * 256 + tid, cl = piece >> 3, ch = piece & 7;
+        const int cc = n0 + cl;
+        if (cc < a.vc)
+            *reinterpret_cast<uint4*>(a.dzT + (int64_t)cc * a.ld_dzT + m0 + ch * 8) =
+                *reinterpret_cast<const uint4*>(s_t + cl * TROW + ch * 16);
     }
 }
 
@@ -709,6 +824,7 @@ struct Workspace {
     float* ea;
     float* eb;
     uint16_t* hT;
+    float* z;         // pass 1's z of the valid tokens [n x V] (NULL: pass 2 recomputes it)
     uint16_t* dz;
     uint16_t* dzT;
     float* dh_part;
@@ -741,11 +857,11 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // chunk_cap (a multiple of BN) and split_cap bound the plan to a smaller
 // workspace (the no-allocation entry point's fixed scratch).
 Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus, int64_t chunk_cap = kVocabChunkMax,
-                     int split_cap = kDhSplitMax) {
+                     int split_cap = kDhSplitMax, bool stash = false) {
     constexpr double kKstepUs = 2.0, kHbmBytesPerUs = 5.0e6;
     const int64_t n_pad = round_up(n, kTokPad);
     const int64_t tm = cdiv(n, BM), th = cdiv(H, BN);
-    const int64_t wcap = chunk_cap < kVocabChunkMax ? chunk_cap : kVocabChunkMax;
+    const int64_t wcap = chunk_cap;
     Pass2Plan best{V < wcap ? V : wcap, 1, -1.0};
     double best_cost = -1.0;
     const int64_t wmax = V < wcap ? round_up(V, BN) : wcap;
@@ -755,7 +871,7 @@ Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus, int64_t chunk
             int64_t steps = 0, chunks = 0;
             for (int64_t c0 = 0; c0 < V; c0 += w) {
                 const int64_t vc = V - c0 < w ? V - c0 : w, tv = cdiv(vc, BN);
-                steps += cdiv(tm * tv, cus) * cdiv(H, BK);                              // dz
+                if (!stash) steps += cdiv(tm * tv, cus) * cdiv(H, BK);                  // dz (recomputed)
                 steps += cdiv(tv * th, cus) * cdiv(n_pad, BK);                          // dW
                 steps += cdiv(tm * th * sp, cus) * (round_up(cdiv(vc, sp), BK) / BK);   // dh
                 ++chunks;
@@ -773,7 +889,7 @@ Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus, int64_t chunk
 }
 
 Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V, int64_t chunk_cap = kVocabChunkMax,
-                int split_cap = kDhSplitMax) {
+                int split_cap = kDhSplitMax, bool stash = false) {
     const int64_t n_parts = (V + 63) / 64;
     const int64_t n_pad = round_up(n_tok > 0 ? n_tok : 1, kTokPad);
     const int64_t vc = V < chunk_cap ? V : chunk_cap;   // widest chunk any plan within the caps uses
@@ -791,6 +907,7 @@ Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V, int64_t chunk_c
     w.ea = reinterpret_cast<float*>(take((size_t)n_tok * 4));
     w.eb = reinterpret_cast<float*>(take((size_t)n_tok * 4));
     w.hT = reinterpret_cast<uint16_t*>(take((size_t)H * n_pad * 2));
+    w.z = stash ? reinterpret_cast<float*>(take((size_t)n_tok * V * 4)) : nullptr;
     w.dz = reinterpret_cast<uint16_t*>(take((size_t)n_tok * vc * 2));
     w.dzT = reinterpret_cast<uint16_t*>(take((size_t)vc * n_pad * 2));
     w.dh_part = reinterpret_cast<float*>(take((size_t)split_cap * n_tok * H * 4));
@@ -829,11 +946,20 @@ int dev_fail(hipError_t e, const char* what) {
     return fail(GRPO_EDEVICE, "grpo_lmhead_fwd_bwd (%s): %s", what, hipGetErrorString(e));
 }
 
+// With GRPO_LMHEAD_KEEP_Z pass 1 keeps z (fp32) and pass 2 reads it back
+// instead of recomputing it; the vocabulary chunk may then span all of V.
+int64_t stash_chunk_cap(int64_t V) { return round_up(V, BN); }
+
 }  // namespace
 
-extern "C" size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V) {
-    if (n_tok < 0 || H <= 0 || V <= 0) return 0;
+extern "C" size_t grpo_lmhead_workspace_size_flags(int64_t n_tok, int64_t H, int64_t V, int32_t flags) {
+    if (n_tok < 0 || H <= 0 || V <= 0 || (flags & ~GRPO_LMHEAD_KEEP_Z)) return 0;
+    if (flags & GRPO_LMHEAD_KEEP_Z) return carve(nullptr, n_tok, H, V, stash_chunk_cap(V), kDhSplitMax, true).bytes;
     return carve(nullptr, n_tok, H, V).bytes;
+}
+
+extern "C" size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V) {
+    return grpo_lmhead_workspace_size_flags(n_tok, H, V, 0);
 }
 
 extern "C" int grpo_transpose_bf16(void* stream, const void* src, int64_t rows, int64_t cols, int64_t ld_src,
@@ -954,6 +1080,11 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
                                          a->kl_type);
         if (rc != GRPO_OK) return rc;
     }
+    if (a->flags & ~GRPO_LMHEAD_KEEP_Z) return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: unknown flags %d", a->flags);
+    const bool stash = (a->flags & GRPO_LMHEAD_KEEP_Z) != 0;
+    if (stash && noalloc)
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd_noalloc: GRPO_LMHEAD_KEEP_Z needs a caller workspace (the "
+                    "chunk's logits do not fit the fixed scratch)");
     int dev = 0, cus = 0;
     hipError_t e;
     if ((e = hipGetDevice(&dev)) != hipSuccess ||
@@ -975,17 +1106,18 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
         const int rc = scratch_ptr(&wsp);
         if (rc != GRPO_OK) return rc;
     } else {
-        const size_t need = grpo_lmhead_workspace_size(n, H, V);
+        const size_t need = grpo_lmhead_workspace_size_flags(n, H, V, a->flags);
         if (!a->workspace || a->workspace_bytes < need || !al16(a->workspace))
             return fail(GRPO_ECAPACITY, "grpo_lmhead_fwd_bwd: workspace of %zu bytes needed (16-byte aligned)", need);
-        plan = plan_pass2(n, H, V, cus);
+        if (stash) chunk_cap = stash_chunk_cap(V);
+        plan = plan_pass2(n, H, V, cus, chunk_cap, split_cap, stash);
     }
     hipStream_t st = (hipStream_t)stream;
     const grpo::ObjTerms obj{a->scale, a->denom, a->row_weight, a->ent_coef, a->ref_logp ? a->kl_coef : 0.0f};
     float* kl_tok = a->ref_logp ? a->kl_tok : nullptr;
     if (n == 0) return grpo::launch_stats(stream, a->loss_tok, a->entropy, kl_tok, a->tok_flags, a->row_off,
                                           a->n_rows, 0, obj, a->row_stats, a->chunk_stats);
-    const Workspace w = carve(wsp, n, H, V, chunk_cap, split_cap);
+    const Workspace w = carve(wsp, n, H, V, chunk_cap, split_cap, stash);
     const int64_t n_pad = round_up(n, kTokPad);
     const int n_parts = (int)((V + 63) / 64);
     const uint16_t* h = (const uint16_t*)a->h;
@@ -1010,6 +1142,7 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
     g.M = (int)n; g.N = (int)V; g.K = (int)H;
     g.a_rows = w.vidx; g.m_dev = w.count;
     g.part = w.part; g.n_parts = n_parts; g.target = a->target; g.zy = w.zy;
+    g.zst = w.z; g.ld_zst = V;
     if ((e = launch_gemm<EPI_STATS>(g, st)) != hipSuccess) return dev_fail(e, "pass 1");
 
     MergeArgs mg{};
@@ -1032,14 +1165,25 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
     const int nsplit = plan.nsplit;
     for (int64_t c0 = 0; c0 < V; c0 += chunk) {
         const int vc = (int)(V - c0 < chunk ? V - c0 : chunk);
-        GemmArgs d{};
-        d.A = h; d.lda = a->ldh; d.B = W + c0 * H; d.ldb = H;
-        d.M = (int)n; d.N = vc; d.K = (int)H;
-        d.a_rows = w.vidx; d.m_dev = w.count;
-        d.c2 = w.c2; d.coef = w.coef; d.target = a->target; d.col0 = (int)c0; d.m_out = (int)n_pad;
-        d.ea = w.ea; d.eb = w.eb; d.bonus = a->ent_coef != 0.0f;
-        d.dz = w.dz; d.ld_dz = vc; d.dzT = w.dzT; d.ld_dzT = n_pad;
-        if ((e = launch_gemm<EPI_DZ>(d, st)) != hipSuccess) return dev_fail(e, "dz");
+        if (stash) {
+            DzArgs d{};
+            d.z = w.z; d.ld_z = V; d.col0 = (int)c0; d.vc = vc;
+            d.count = w.count; d.vidx = w.vidx; d.target = a->target;
+            d.c2 = w.c2; d.coef = w.coef; d.ea = w.ea; d.eb = w.eb; d.bonus = a->ent_coef != 0.0f;
+            d.dz = w.dz; d.ld_dz = vc; d.dzT = w.dzT; d.ld_dzT = n_pad;
+            hipLaunchKernelGGL(dz_from_z_kernel, dim3((unsigned)((vc + 127) / 128), (unsigned)(n_pad / 64)),
+                               dim3(256), 0, st, d);
+            if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "dz");
+        } else {
+            GemmArgs d{};
+            d.A = h; d.lda = a->ldh; d.B = W + c0 * H; d.ldb = H;
+            d.M = (int)n; d.N = vc; d.K = (int)H;
+            d.a_rows = w.vidx; d.m_dev = w.count;
+            d.c2 = w.c2; d.coef = w.coef; d.target = a->target; d.col0 = (int)c0; d.m_out = (int)n_pad;
+            d.ea = w.ea; d.eb = w.eb; d.bonus = a->ent_coef != 0.0f;
+            d.dz = w.dz; d.ld_dz = vc; d.dzT = w.dzT; d.ld_dzT = n_pad;
+            if ((e = launch_gemm<EPI_DZ>(d, st)) != hipSuccess) return dev_fail(e, "dz");
+        }
 
         // dh: the chunk's vocabulary range split nsplit ways, split s
         // accumulating into its own partial (summed in order at the end)

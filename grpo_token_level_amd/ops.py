@@ -606,13 +606,15 @@ def transpose_bf16(x, out=None):
     return out
 
 
-def lmhead_workspace_bytes(n_tok, H, V):
+def lmhead_workspace_bytes(n_tok, H, V, keep_z=False):
+    if keep_z:
+        return int(C.lib().grpo_lmhead_workspace_size_flags(n_tok, H, V, C.LMHEAD_KEEP_Z))
     return int(C.lib().grpo_lmhead_workspace_size(n_tok, H, V))
 
 
 def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off, dW, *, scale=1.0, denom=None,
                    eps_low=0.2, eps_high=0.2, dh=None, ws=None, workspace=None, row_weight=None,
-                   ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3, noalloc=False):
+                   ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3, noalloc=False, keep_z=False):
     """Fused LM-head GRPO loss over one chunk (grpo_lmhead_fwd_bwd).
 
     ``dW`` (fp32 [V x H]) is accumulated into; ``dh`` (fp32 [n_tok x H]) is
@@ -620,7 +622,9 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
     (ValueError).  Returns the per-token workspace dict with ``dh`` added.
     ``noalloc``: call grpo_lmhead_fwd_bwd_noalloc, which uses the library's
     fixed scratch (no workspace is passed; the caller still provides every
-    input and output)."""
+    input and output).  ``keep_z``: GRPO_LMHEAD_KEEP_Z (pass 1 keeps the
+    chunk's fp32 logits in the workspace and pass 2 reads them back instead
+    of recomputing them)."""
     torch = _torch()
     if h.dim() != 2 or W.dim() != 2:
         raise ValueError("h and W must be 2-D")
@@ -632,9 +636,11 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
     if dh is None:
         dh = torch.empty((n, H), dtype=torch.float32, device=h.device)
     if workspace is None and not noalloc:
-        workspace = torch.empty(max(lmhead_workspace_bytes(n, H, V), 1), dtype=torch.uint8, device=h.device)
+        workspace = torch.empty(max(lmhead_workspace_bytes(n, H, V, keep_z), 1), dtype=torch.uint8,
+                                device=h.device)
     a = C.LmheadArgs()
     a.struct_size = ctypes.sizeof(C.LmheadArgs)
+    a.flags = C.LMHEAD_KEEP_Z if keep_z else 0
     a.ldh = _matrix(h, "h", n, H, ("bfloat16",))
     a.h = h.data_ptr() if n else None
     _matrix(W, "W", V, H, ("bfloat16",), dense=True)

@@ -404,7 +404,7 @@ typedef struct grpo_lmhead_args {
     int64_t n_rows;
     float eps_low, eps_high;    /* clip band */
     float scale;                /* gradient factor (see grpo_loss_args) */
-    int32_t reserved1;          /* 0 */
+    int32_t flags;              /* 0, or GRPO_LMHEAD_KEEP_Z */
     const int64_t* denom;       /* NULL or device int64 N: factor further divided by max(N, 1) */
     float* dh;                  /* fp32 [n_tok x H]: dL/dh, overwritten */
     float* dW;                  /* fp32 [V x H], 16-byte aligned: dL/dW of this chunk is ADDED (accumulate) */
@@ -415,7 +415,7 @@ typedef struct grpo_lmhead_args {
     uint8_t* tok_flags;         /* [n_tok] required: bit0 valid, bit1 clipped, bit2 non-finite */
     grpo_stats* row_stats;      /* [n_rows] required */
     grpo_stats* chunk_stats;    /* [1] required */
-    void* workspace;            /* >= grpo_lmhead_workspace_size(n_tok, H, V) bytes, 16-byte aligned */
+    void* workspace;            /* >= grpo_lmhead_workspace_size_flags(n_tok, H, V, flags) bytes, 16-byte aligned */
     size_t workspace_bytes;
     const float* row_weight;    /* extra terms exactly as in grpo_loss_args */
     const float* ref_logp;
@@ -426,13 +426,27 @@ typedef struct grpo_lmhead_args {
     int32_t reserved2;
 } grpo_lmhead_args;
 
-/* host.  Workspace bytes grpo_lmhead_fwd_bwd needs for a chunk of n_tok tokens:
- * per-token slice partials of the log-softmax (16 B per token per 64 vocabulary
- * columns), h^T, one vocabulary chunk (at most 65536 columns) of dz in two
- * layouts (bf16), up to 16 fp32 split partials of dh and the chunk's
- * valid-token index maps.  It grows with n_tok * V / 4, n_tok * 262144 and
- * n_tok * H * 64, never with n_tok * V * 2. */
+/* grpo_lmhead_args.flags: keep the chunk's logits.  Pass 1 stores z (fp32,
+ * [valid tokens x V]) in the workspace and pass 2 forms dz from it with an
+ * elementwise kernel instead of a second GEMM over h W^T (same dz bits, about
+ * 13 % less time at the compaction workload's sizes), at the price of holding
+ * 4 * n_tok * V bytes more: the chunk's [tokens x V] logits, which the default
+ * path never holds.  Not available with grpo_lmhead_fwd_bwd_noalloc. */
+#define GRPO_LMHEAD_KEEP_Z 1
+
+/* host.  Workspace bytes grpo_lmhead_fwd_bwd needs for a chunk of n_tok tokens
+ * without flags: per-token slice partials of the log-softmax (16 B per token
+ * per 64 vocabulary columns), h^T, one vocabulary chunk (at most 65536
+ * columns) of dz in two layouts (bf16), up to 16 fp32 split partials of dh and
+ * the chunk's valid-token index maps.  It grows with n_tok * V / 4,
+ * n_tok * 262144 and n_tok * H * 64, never with n_tok * V * 2. */
 size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V);
+
+/* host.  The same for the given flags.  With GRPO_LMHEAD_KEEP_Z: plus the
+ * fp32 logits (4 * n_tok * V), and dz in two layouts for up to the whole
+ * vocabulary (4 * n_tok * V) in place of one 65536-column chunk.  0 for
+ * unknown flags or bad sizes. */
+size_t grpo_lmhead_workspace_size_flags(int64_t n_tok, int64_t H, int64_t V, int32_t flags);
 
 /* device.  The fused loss of grpo_loss_fwd_bwd with the logits produced by the
  * LM head, z = h W^T, and the gradient pushed through it:
@@ -441,13 +455,14 @@ size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V);
  *   dh = dz W (overwritten), dW += dz^T h (accumulated across chunks: [P1] "The
  *   hard part: deferred normalization" -- chunk gradients add up to the step's).
  * z and dz are formed tile by tile in registers by bf16 MFMA GEMMs (fp32
- * accumulation) and never stored for the whole vocabulary; dz feeds the two
- * gradient GEMMs in bf16, one vocabulary chunk at a time.  Masked tokens
+ * accumulation) and never stored for the whole vocabulary (unless flags holds
+ * GRPO_LMHEAD_KEEP_Z); dz feeds the two gradient GEMMs in bf16, one
+ * vocabulary chunk at a time.  Masked tokens
  * (pads, [P4] figure; observations, [P2] "Field Lineage") get zero outputs and
  * contribute nothing; the GEMMs skip them: the chunk's valid tokens are listed
  * on the device first and only their rows are multiplied (the host never
  * waits for the count).  Row and chunk stats as in grpo_loss_fwd_bwd.
- * ECAPACITY if the workspace is too small. */
+ * ECAPACITY if the workspace is too small; EINVAL for unknown flags. */
 int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* args);
 
 /* Bytes of the fixed device scratch behind grpo_lmhead_fwd_bwd_noalloc. */
@@ -467,7 +482,9 @@ int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* args);
  * parts grow with n_tok * V / 4 and n_tok * H) returns GRPO_ECAPACITY with
  * the size it needs.  Nothing in the scratch has to start at zero.  All calls
  * on one GPU share that GPU's scratch: calls that overlap on one GPU (two
- * streams, or two threads) race and must be serialised by the caller. */
+ * streams, or two threads) race and must be serialised by the caller.
+ * flags must be 0 (EINVAL for GRPO_LMHEAD_KEEP_Z: the logits do not fit the
+ * scratch). */
 int grpo_lmhead_fwd_bwd_noalloc(void* stream, const grpo_lmhead_args* args);
 
 /* ===================================================== frozen pi_old (ahead pass) */

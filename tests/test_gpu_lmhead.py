@@ -54,12 +54,12 @@ def _case(n, H, V, seed, h_std=1.0, w_std=0.05, noise=0.3, masked_frac=0.2, n_ro
                                         ("tok_row", tok_row), ("row_off", row_off))})
 
 
-def _run(c, dW, scale, Wt=None, eps=(0.2, 0.2)):
+def _run(c, dW, scale, Wt=None, eps=(0.2, 0.2), keep_z=False):
     if Wt is None:
         Wt = ops.transpose_bf16(c["W"])
     g = c["g"]
     return ops.lmhead_fwd_bwd(c["h"], c["W"], Wt, g["target"], g["mask"], g["old"], g["tok_row"], g["adv"],
-                              g["row_off"], dW, scale=scale, eps_low=eps[0], eps_high=eps[1])
+                              g["row_off"], dW, scale=scale, eps_low=eps[0], eps_high=eps[1], keep_z=keep_z)
 
 
 GRAD_ROW = 2.0 ** -8 + 2.0 ** -12
@@ -102,14 +102,16 @@ def _check(ws, dW, ref, c, dW_ref, dz_ref=None):
 # ragged shapes: tokens, hidden size and vocabulary off the 256 x 256 tiles;
 # several 256-wide dW / dh tile columns (H = 512, 768); a vocabulary spanning
 # two pass-2 chunks of 65536 columns
+# (each with the logits kept for pass 2, GRPO_LMHEAD_KEEP_Z, and without)
+@pytest.mark.parametrize("keep_z", [False, True])
 @pytest.mark.parametrize("n,H,V", [(1, 64, 256), (37, 64, 1000), (130, 96, 520), (300, 128, 16520),
                                    (257, 256, 4096), (300, 768, 5000), (213, 512, 70000)])
-def test_lmhead_matches_oracle(n, H, V):
-    print(f"lmhead parity n={n} H={H} V={V}", flush=True)
+def test_lmhead_matches_oracle(n, H, V, keep_z):
+    print(f"lmhead parity n={n} H={H} V={V} keep_z={keep_z}", flush=True)
     c = _case(n, H, V, seed=n + H + V)
     N = max(1, int(c["mask"].sum()))
     dW = torch.zeros((V, H), dtype=torch.float32, device=DEV)
-    ws = _run(c, dW, 1.0 / N)
+    ws = _run(c, dW, 1.0 / N, keep_z=keep_z)
     torch.cuda.synchronize()
     ref = oracle.lmhead_fwd_bwd(c["h64"], c["W64"], c["target"], c["mask"], c["old"].astype(np.float64),
                                 c["adv"].astype(np.float64)[c["tok_row"]], 1.0 / N)
@@ -143,6 +145,41 @@ def test_lmhead_accumulates_dW_over_chunks():
                                 1.0 / N)
     assert rel_l2(to_f64(dW), ref["dW"]) <= TOL_GRAD
     assert rel_l2(to_f64(torch.cat(dhs)), ref["dh"]) <= TOL_GRAD
+
+
+@pytest.mark.parametrize("n,H,V,bonus", [(700, 256, 70000, 0.0), (513, 512, 20000, 0.01)])
+def test_keep_z_equals_the_recompute(n, H, V, bonus):
+    # Pass 2 from the stored logits forms dz with the recomputing GEMM's
+    # arithmetic on the same fp32 z: per-token outputs and dW (each dW element
+    # one GEMM tile over the tokens in the same order) are equal bit for bit;
+    # dh sums the same bf16 products split over the vocabulary another way,
+    # so its rows agree to float32 summation order.  With the entropy bonus
+    # (dz = p (ea + eb t)) as well.
+    print(f"keep_z vs recompute n={n} H={H} V={V} bonus={bonus}", flush=True)
+    c = _case(n, H, V, seed=90 + n)
+    N = max(1, int(c["mask"].sum()))
+    Wt = ops.transpose_bf16(c["W"])
+    out = []
+    for keep in (False, True):
+        dW = torch.zeros((V, H), dtype=torch.float32, device=DEV)
+        g = c["g"]
+        ws = ops.lmhead_fwd_bwd(c["h"], c["W"], Wt, g["target"], g["mask"], g["old"], g["tok_row"], g["adv"],
+                                g["row_off"], dW, scale=1.0 / N, ent_coef=bonus, keep_z=keep)
+        out.append((ws, dW))
+    torch.cuda.synchronize()
+    (wa, dWa), (wb, dWb) = out
+    for k in ("logp", "lse", "entropy", "loss_tok", "tok_flags", "row_stats", "chunk_stats"):
+        assert torch.equal(wa[k], wb[k]), k
+    assert torch.equal(dWa, dWb)
+    a, b = to_f64(wa["dh"]), to_f64(wb["dh"])
+    err = np.sqrt(np.sum((a - b) ** 2, axis=1))
+    assert np.all(err <= 1e-5 * np.sqrt(np.sum(a * a, axis=1)) + 1e-30), float(np.max(err))
+    # the fixed-scratch entry point cannot keep the logits
+    with pytest.raises(ops.GrpoError) as e:
+        g = c["g"]
+        ops.lmhead_fwd_bwd(c["h"], c["W"], Wt, g["target"], g["mask"], g["old"], g["tok_row"], g["adv"],
+                           g["row_off"], dWa, scale=1.0 / N, noalloc=True, keep_z=True)
+    assert e.value.kind == "EINVAL"
 
 
 def test_lmhead_equals_materialised_path():
@@ -328,7 +365,21 @@ def test_compaction_workload_full_size_sampled():
     dh1 = torch.empty((n_c, H), dtype=torch.float32, device=DEV)
     ws1 = ops.lmhead_fwd_bwd(h[t0:t1], W, Wt, tgt_d[t0:t1], mask_d[t0:t1], old[t0:t1], ops.tok_row(ro, n_c),
                              G(adv_row[a:e]), ro, dW1, denom=N, dh=dh1, workspace=workspace)
+    # the same chunk with its logits kept for pass 2 (GRPO_LMHEAD_KEEP_Z): dz
+    # has the same bits, so dW has; dh agrees to float32 summation order
+    del workspace
+    dW1k = torch.zeros((V, H), dtype=torch.float32, device=DEV)
+    dh1k = torch.empty((n_c, H), dtype=torch.float32, device=DEV)
+    ws1k = ops.lmhead_fwd_bwd(h[t0:t1], W, Wt, tgt_d[t0:t1], mask_d[t0:t1], old[t0:t1], ops.tok_row(ro, n_c),
+                              G(adv_row[a:e]), ro, dW1k, denom=N, dh=dh1k, keep_z=True)
     torch.cuda.synchronize()
+    assert torch.equal(dW1k, dW1)
+    for key in ("logp", "entropy", "loss_tok", "tok_flags"):
+        assert torch.equal(ws1k[key], ws1[key]), key
+    dka, dkb = to_f64(dh1), to_f64(dh1k)
+    assert np.all(np.sqrt(np.sum((dka - dkb) ** 2, axis=1)) <= 1e-5 * np.sqrt(np.sum(dka * dka, axis=1)) + 1e-30)
+    del dW1k, dh1k, ws1k, dka, dkb
+    torch.cuda.empty_cache()
     h_c = h[t0:t1].float().cpu().numpy()
     Wf32 = W.float().cpu().numpy()
     z = h_c @ Wf32.T

@@ -59,6 +59,7 @@ int main(void) {
   F(grpo_lmhead_args, Wt) F(grpo_lmhead_args, n_rows) F(grpo_lmhead_args, denom) F(grpo_lmhead_args, workspace_bytes)
   F(grpo_loss_args, row_weight) F(grpo_loss_args, kl_tok) F(grpo_loss_args, kl_type)
   F(grpo_lmhead_args, row_weight) F(grpo_lmhead_args, ent_coef) F(grpo_lmhead_args, kl_type)
+  F(grpo_lmhead_args, flags)
   F(grpo_stats, kl_sum) F(grpo_stats, obj_sum) F(grpo_stats, n_valid_rows)
   F(grpo_step_result, kl) F(grpo_step_result, obj_sum) F(grpo_step_result, n_clipped)
   return 0;
@@ -338,3 +339,25 @@ def test_old_cache_rewind_without_device_work():
         assert L.grpo_old_cache_replay(ctypes.byref(c), 0, ctypes.byref(ptr)) == 0
     assert L.grpo_old_cache_rewind(ctypes.byref(c)) == 0 and c.replayed == 0
     assert L.grpo_old_cache_replay(ctypes.byref(c), 0, ctypes.byref(ptr)) == 0
+
+
+@pytest.mark.skipif(C.HOST_ONLY, reason="the host-only sanitizer build carries no device entry points")
+def test_lmhead_workspace_sizes():
+    # The default path never holds a [tokens x V] matrix: past one
+    # 65536-column chunk its workspace grows with the vocabulary only by the
+    # log-softmax slice partials (16 bytes per token per 64 columns);
+    # GRPO_LMHEAD_KEEP_Z adds the fp32 logits and dz over the whole
+    # vocabulary (8 bytes per token and column).
+    L = C.lib()
+    n, H, V = 2700, 2048, 151936
+    base = L.grpo_lmhead_workspace_size(n, H, V)
+    assert base == L.grpo_lmhead_workspace_size_flags(n, H, V, 0)
+    grow = L.grpo_lmhead_workspace_size(n, H, 2 * V) - base
+    assert grow <= n * V // 4 + 4096
+    keep = L.grpo_lmhead_workspace_size_flags(n, H, V, C.LMHEAD_KEEP_Z)
+    assert keep >= base + 8 * n * V - 4 * n * 65536
+    grow_keep = L.grpo_lmhead_workspace_size_flags(n, H, 2 * V, C.LMHEAD_KEEP_Z) - keep
+    assert grow_keep >= 8 * n * V
+    assert L.grpo_lmhead_workspace_size_flags(n, H, V, 2) == 0           # unknown flag
+    assert L.grpo_lmhead_workspace_size_flags(-1, H, V, 0) == 0
+    assert L.grpo_lmhead_workspace_size_flags(0, H, V, C.LMHEAD_KEEP_Z) > 0

@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--terms", action="store_true",
                     help="padded workloads: seq-mean-token-mean aggregation with an entropy bonus (0.01) and a k3 "
                          "KL term (0.05) against a reference log-prob (the step's extra-term variant)")
+    ap.add_argument("--paired", action="store_true",
+                    help="with --ahead: record pi_old with the paired forward pass (the fused loss's lane "
+                         "partition: the ratio is exactly 1 on unchanged logits)")
     ap.add_argument("--ahead", action="store_true",
                     help="padded workloads: when the batch drives more than one optimizer step, run the ahead "
                          "pass (pi_old recorded per chunk into the old-log-prob cache) inside the timed step and "
@@ -149,8 +152,8 @@ class PaddedStep:
 
     ENT_COEF, KL_COEF = 0.01, 0.05
 
-    def __init__(self, wl, seed, torch, ops, timed, terms=False, ahead=False, epochs=1, shuffle=False, over=None,
-                 graph=False):
+    def __init__(self, wl, seed, torch, ops, timed, terms=False, ahead=False, paired=False, epochs=1, shuffle=False,
+                 over=None, graph=False):
         from synth import fill_normal_rows, padded_batch
         self.torch, self.ops, self.timed = torch, ops, timed
         self.terms = terms
@@ -217,6 +220,7 @@ class PaddedStep:
         # the ahead pass runs only where the gate asks for it (more than one
         # optimizer step per collected batch: n_mini windows per epoch, mu epochs)
         self.ahead = ahead and ops.needs_ahead_pass(n_mini * epochs)
+        self.paired = paired
         if self.ahead:
             self.cache = ops.OldLogprobCache(n_mini * n_micro,
                                              torch.empty(n_rows * T, dtype=torch.float32, device="cuda"))
@@ -260,7 +264,8 @@ class PaddedStep:
                 for j in range(n_micro):
                     a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
                     ev = self.ahead_timed.begin()
-                    self.cache.record(self.logits[a * T:e * T], self.target[a * T:e * T], self.mask[a * T:e * T])
+                    self.cache.record(self.logits[a * T:e * T], self.target[a * T:e * T], self.mask[a * T:e * T],
+                                      paired=self.paired)
                     self.ahead_timed.end(ev, self.ahead_units[(i, j)])
         k = 0
         for ep in range(self.mu):
@@ -702,6 +707,11 @@ def main():
         extra["terms"] = True
     if args.ahead:
         extra["ahead"] = True
+    if args.paired:
+        if not args.ahead:
+            print("--paired applies to --ahead", file=sys.stderr)
+            sys.exit(2)
+        extra["paired"] = True
     if args.epochs != 1 or args.shuffle:
         extra["epochs"] = args.epochs
         extra["shuffle"] = args.shuffle
@@ -776,6 +786,7 @@ def main():
             cfg["ahead_ms_per_step"] = round(a_ms / args.steps, 4)
             cfg["ahead_read_GBs"] = round(a_units / (a_ms * 1e-3) / 1e9, 1)
             cfg["device_read_GBs"] = round(step.read_context(), 1)
+            cfg["ahead_paired"] = bool(getattr(step, "paired", False))
     if wl == "compact":
         achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

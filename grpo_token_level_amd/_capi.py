@@ -142,6 +142,7 @@ PROTOTYPES = {
     "grpo_chunk_tok_src": (ctypes.c_int, [_p, _p, _i64, _p, _i64, _p, _i64, _p]),
     "grpo_gather": (ctypes.c_int, [_p, _p, _i64, _p, _i64, _i64, _p]),
     "grpo_logprob_fwd": (ctypes.c_int, [_p, _i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    "grpo_logprob_fwd_paired": (ctypes.c_int, [_p, _i32, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "grpo_loss_fwd_bwd": (ctypes.c_int, [_p, ctypes.POINTER(LossArgs)]),
     "grpo_loss_stats": (ctypes.c_int, [_p, ctypes.POINTER(LossArgs)]),
     "grpo_stats_sum": (ctypes.c_int, [_p, _i64, ctypes.POINTER(Stats)]),
@@ -155,6 +156,8 @@ PROTOTYPES = {
     "grpo_old_cache_reset": (ctypes.c_int, [ctypes.POINTER(OldCache)]),
     "grpo_old_cache_rewind": (ctypes.c_int, [ctypes.POINTER(OldCache)]),
     "grpo_old_cache_record": (ctypes.c_int, [_p, ctypes.POINTER(OldCache), _i32, _p, _i64, _i64, _i64, _p, _p,
+                                             ctypes.POINTER(ctypes.c_void_p)]),
+    "grpo_old_cache_record_paired": (ctypes.c_int, [_p, ctypes.POINTER(OldCache), _i32, _p, _i64, _i64, _i64, _p, _p,
                                              ctypes.POINTER(ctypes.c_void_p)]),
     "grpo_old_cache_replay": (ctypes.c_int, [ctypes.POINTER(OldCache), _i64, ctypes.POINTER(ctypes.c_void_p)]),
     "grpo_probe_compare": (ctypes.c_int, [_p, _p, _p, _p, _i64, _f32, _p]),

@@ -469,9 +469,10 @@ extern "C" int grpo_old_cache_reset(grpo_old_cache* c) {
 }
 
 // Record k is the chunk's forward-only log-probs, appended after record k-1.
-extern "C" int grpo_old_cache_record(void* stream, grpo_old_cache* c, int32_t dtype, const void* logits, int64_t ld,
-                                     int64_t n_tok, int64_t V, const int32_t* target, const uint8_t* mask,
-                                     float** slot) {
+namespace {
+
+int old_cache_record(bool paired, void* stream, grpo_old_cache* c, int32_t dtype, const void* logits, int64_t ld,
+                     int64_t n_tok, int64_t V, const int32_t* target, const uint8_t* mask, float** slot) {
     if (!c || !c->off || c->n_calls < 1 || n_tok < 0) return fail(GRPO_EINVAL, "grpo_old_cache_record: bad arguments");
     if (c->replayed > 0) return fail(GRPO_ESTATE, "grpo_old_cache_record: replay has begun; reset for the next batch");
     if (c->recorded >= c->n_calls)
@@ -483,13 +484,30 @@ extern "C" int grpo_old_cache_record(void* stream, grpo_old_cache* c, int32_t dt
                     (long long)(at + n_tok), (long long)c->capacity);
     float* dst = c->buf ? c->buf + at : nullptr;
     if (n_tok > 0) {
-        const int rc = grpo_logprob_fwd(stream, dtype, logits, ld, n_tok, V, target, mask, dst, nullptr, nullptr);
+        const int rc = paired ? grpo_logprob_fwd_paired(stream, dtype, logits, ld, n_tok, V, target, mask, dst,
+                                                        nullptr, nullptr)
+                              : grpo_logprob_fwd(stream, dtype, logits, ld, n_tok, V, target, mask, dst, nullptr,
+                                                 nullptr);
         if (rc != GRPO_OK) return rc;
     }
     c->off[k + 1] = at + n_tok;
     c->recorded = k + 1;
     if (slot) *slot = dst;
     return ok();
+}
+
+}  // namespace
+
+extern "C" int grpo_old_cache_record(void* stream, grpo_old_cache* c, int32_t dtype, const void* logits, int64_t ld,
+                                     int64_t n_tok, int64_t V, const int32_t* target, const uint8_t* mask,
+                                     float** slot) {
+    return old_cache_record(false, stream, c, dtype, logits, ld, n_tok, V, target, mask, slot);
+}
+
+extern "C" int grpo_old_cache_record_paired(void* stream, grpo_old_cache* c, int32_t dtype, const void* logits,
+                                            int64_t ld, int64_t n_tok, int64_t V, const int32_t* target,
+                                            const uint8_t* mask, float** slot) {
+    return old_cache_record(true, stream, c, dtype, logits, ld, n_tok, V, target, mask, slot);
 }
 
 // Inner epochs without a shuffle visit the chunks in the same order again:

@@ -620,7 +620,7 @@ template <int DTI, int DTO, int TPR, int NV, bool GRAD, int NL = 0, int NG = 0, 
 __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const TokParams p) {
     static_assert(NL == 0 || TPR == 1024, "LDS-held vectors are for the one-row-per-block path");
     static_assert(NG == 0 || (NL > 0 && NG % 2 == 0), "re-read vectors follow the LDS-held ones, in pairs");
-    static_assert(!MIS || (NL == 0 && NG == 0 && GRAD), "rows off alignment: registers only, gradient path");
+    static_assert(!MIS || (NL == 0 && NG == 0), "rows off alignment: registers only");
     constexpr int VEC = In<DTI>::VEC;
     constexpr int WPR = TPR / 64;
     constexpr int RPB = TPR == 64 ? 4 : 1;
@@ -1417,7 +1417,7 @@ hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st, bool 
     const int rpb = c.tpr == 64 ? 4 : 1;
     const dim3 grid((unsigned)((p.n_tok + rpb - 1) / rpb));
     const dim3 block(c.tpr == 64 ? 256 : c.tpr);
-    if constexpr (GRAD && DTI == DTO) {
+    if constexpr (DTI == DTO) {
         if (mis) {
 #define GRPO_MIS_CASE(TPR_, NV_)                                                                                 \
             if (c.tpr == TPR_ && c.nv == NV_ && c.nl == 0 && c.ng == 0) {                                        \
@@ -1462,22 +1462,25 @@ hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st, bool 
     GRPO_REG_CASE(1024, 16, 0, 0)
     GRPO_REG_CASE(1024, 19, 0, 0)
     GRPO_REG_CASE(1024, 19, 9, 0)
-    if constexpr (GRAD && DTI == GRPO_BF16) GRPO_REG_CASE(1024, 19, 9, 4)
+    if constexpr (DTI == GRPO_BF16) GRPO_REG_CASE(1024, 19, 9, 4)
 #undef GRPO_REG_CASE
     return hipErrorInvalidValue;
 }
 
 template <int DTI, int DTO, bool GRAD>
-hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st, bool mis_ok = false) {
+hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st, bool mis_ok = false, bool paired = false) {
     if (p.n_tok == 0) return hipSuccess;
     // Forward only, rows past 1024 vectors stream: the row need not stay on
     // chip, and many 256-thread blocks per CU keep more reads in flight than
     // one row-resident block (V = 16 384 .. 202 048 bf16: 6.2-7.0 TB/s against
     // 4.4-5.9 for the register kernel; at 8192 the register kernel is ahead).
-    if (vec_ok && (GRAD || p.V / In<DTI>::VEC <= 1024)) {
+    // `paired` (forward only): the gradient path's choice of kernel shape, so
+    // that the sums run in the same lane partition and order as the fused loss.
+    const bool as_grad = GRAD || paired;
+    if (vec_ok && (as_grad || p.V / In<DTI>::VEC <= 1024)) {
         const int64_t nvec = p.V / In<DTI>::VEC;
         for (const RegCfg& c : kRegCfgs) {
-            if (c.ng > 0 && !(GRAD && DTI == GRPO_BF16)) continue;
+            if (c.ng > 0 && !(as_grad && DTI == GRPO_BF16)) continue;
             if ((int64_t)c.tpr * (c.nv + c.nl + c.ng) >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st);
         }
     }
@@ -1485,7 +1488,7 @@ hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st, bool mis_
     // phase (in place, or the same dtype, stride and base phase): the register
     // kernel over the aligned vectors that cover each row, the row still read
     // once.  A row spans at most V / VEC + 1 such vectors.
-    if (GRAD && DTI == DTO && !vec_ok && mis_ok) {
+    if (as_grad && DTI == DTO && !vec_ok && mis_ok) {
         const int64_t nvec = (p.V + 2 * In<DTI>::VEC - 2) / In<DTI>::VEC;
         for (const RegCfg& c : kRegCfgs) {
             if (c.nl > 0 || c.ng > 0) continue;
@@ -1598,22 +1601,45 @@ extern "C" int grpo_tok_row(void* stream, const int64_t* row_off, int64_t n_rows
     return check_launch(hipGetLastError(), "grpo_tok_row");
 }
 
-extern "C" int grpo_logprob_fwd(void* stream, int32_t dtype, const void* logits, int64_t ld, int64_t n_tok,
-                                int64_t V, const int32_t* target, const uint8_t* mask, float* logp, float* lse,
-                                float* entropy) {
-    if (dtype != GRPO_F32 && dtype != GRPO_BF16) return fail(GRPO_EINVAL, "grpo_logprob_fwd: unknown dtype %d", dtype);
-    if (n_tok < 0 || V < 1 || ld < V) return fail(GRPO_EINVAL, "grpo_logprob_fwd: need n_tok >= 0, V >= 1, ld >= V");
-    if (n_tok > 0 && (!logits || !target || !mask || !logp)) return fail(GRPO_EINVAL, "grpo_logprob_fwd: NULL pointer");
-    if (n_tok > 0x7fffffffLL) return fail(GRPO_EINVAL, "grpo_logprob_fwd: too many tokens for one launch");
+namespace {
+
+int logprob_fwd(const char* who, bool paired, void* stream, int32_t dtype, const void* logits, int64_t ld,
+                int64_t n_tok, int64_t V, const int32_t* target, const uint8_t* mask, float* logp, float* lse,
+                float* entropy) {
+    if (dtype != GRPO_F32 && dtype != GRPO_BF16) return fail(GRPO_EINVAL, "%s: unknown dtype %d", who, dtype);
+    if (n_tok < 0 || V < 1 || ld < V) return fail(GRPO_EINVAL, "%s: need n_tok >= 0, V >= 1, ld >= V", who);
+    if (n_tok > 0 && (!logits || !target || !mask || !logp)) return fail(GRPO_EINVAL, "%s: NULL pointer", who);
+    if (n_tok > 0x7fffffffLL) return fail(GRPO_EINVAL, "%s: too many tokens for one launch", who);
     TokParams p{};
     p.logits = logits; p.ld = ld; p.n_tok = n_tok; p.V = V;
     p.target = target; p.mask = mask;
     p.logp = logp; p.lse = lse; p.entropy = entropy;
     const int vec = dtype == GRPO_BF16 ? 8 : 4;
+    const int in_b = dtype == GRPO_BF16 ? 2 : 4;
     const bool vec_ok = aligned16(logits) && ld % vec == 0 && V % vec == 0;
-    hipError_t e = dtype == GRPO_BF16 ? launch_tok<GRPO_BF16, GRPO_BF16, false>(p, vec_ok, (hipStream_t)stream)
-                                      : launch_tok<GRPO_F32, GRPO_F32, false>(p, vec_ok, (hipStream_t)stream);
-    return check_launch(e, "grpo_logprob_fwd");
+    // rows off alignment: the fused loss keeps them in registers when its
+    // dlogits rows share their phase (in place), which the paired pass assumes
+    const bool mis_ok = paired && (reinterpret_cast<uintptr_t>(logits) % in_b) == 0;
+    hipError_t e = dtype == GRPO_BF16
+                       ? launch_tok<GRPO_BF16, GRPO_BF16, false>(p, vec_ok, (hipStream_t)stream, mis_ok, paired)
+                       : launch_tok<GRPO_F32, GRPO_F32, false>(p, vec_ok, (hipStream_t)stream, mis_ok, paired);
+    return check_launch(e, who);
+}
+
+}  // namespace
+
+extern "C" int grpo_logprob_fwd(void* stream, int32_t dtype, const void* logits, int64_t ld, int64_t n_tok,
+                                int64_t V, const int32_t* target, const uint8_t* mask, float* logp, float* lse,
+                                float* entropy) {
+    return logprob_fwd("grpo_logprob_fwd", false, stream, dtype, logits, ld, n_tok, V, target, mask, logp, lse,
+                       entropy);
+}
+
+extern "C" int grpo_logprob_fwd_paired(void* stream, int32_t dtype, const void* logits, int64_t ld, int64_t n_tok,
+                                       int64_t V, const int32_t* target, const uint8_t* mask, float* logp,
+                                       float* lse, float* entropy) {
+    return logprob_fwd("grpo_logprob_fwd_paired", true, stream, dtype, logits, ld, n_tok, V, target, mask, logp,
+                       lse, entropy);
 }
 
 extern "C" int grpo_loss_fwd_bwd(void* stream, const grpo_loss_args* a) {

@@ -226,12 +226,15 @@ class OldLogprobCache:
         start = (addr - self.buf.data_ptr()) // 4 if n else 0
         return self.buf[start:start + n]
 
-    def record(self, logits, target, mask):
-        """Ahead pass of one chunk into the next record; returns its view."""
+    def record(self, logits, target, mask, paired=False):
+        """Ahead pass of one chunk into the next record; returns its view.
+        ``paired``: grpo_old_cache_record_paired (the record equals the fused
+        loss's log-probs bit for bit on unchanged logits)."""
         n, V = logits.shape
         ld = _matrix(logits, "logits", n, V)
         slot = ctypes.c_void_p()
-        C.check(C.lib().grpo_old_cache_record(_stream(), ctypes.byref(self.c), _dtype_code(logits),
+        entry = C.lib().grpo_old_cache_record_paired if paired else C.lib().grpo_old_cache_record
+        C.check(entry(_stream(), ctypes.byref(self.c), _dtype_code(logits),
                                               logits.data_ptr(), ld, n, V, _need(target, "target", "int32", n),
                                               _need(mask, "mask", "byte", n), ctypes.byref(slot)))
         return self._view(slot.value or 0, n)
@@ -436,15 +439,25 @@ def tok_row(row_off, n_tok, out=None):
     return out
 
 
-def logprob_fwd(logits, target, mask, want_lse=True, want_entropy=True):
-    """Forward-only per-token (logp, lse, entropy) float32 tensors."""
+def logprob_fwd(logits, target, mask, want_lse=True, want_entropy=True, paired=False, out=None):
+    """Forward-only per-token (logp, lse, entropy) float32 tensors.
+
+    ``paired``: grpo_logprob_fwd_paired, whose sums run in the fused loss's
+    lane partition, so the results equal loss_fwd_bwd's bit for bit where the
+    fused loss keeps the row on chip.  ``out``: a float32 tensor of n_tok
+    elements that receives logp (for instance a slice of a pi_old cache)."""
     torch = _torch()
     n, V = logits.shape
     ld = _matrix(logits, "logits", n, V)
-    logp = torch.empty(n, dtype=torch.float32, device=logits.device)
-    lse = torch.empty_like(logp) if want_lse else None
-    ent = torch.empty_like(logp) if want_entropy else None
-    C.check(C.lib().grpo_logprob_fwd(_stream(), _dtype_code(logits), logits.data_ptr(), ld, n, V,
+    if out is not None:
+        _need(out, "out", "float32", n)
+        logp = out
+    else:
+        logp = torch.empty(n, dtype=torch.float32, device=logits.device)
+    lse = torch.empty(n, dtype=torch.float32, device=logits.device) if want_lse else None
+    ent = torch.empty(n, dtype=torch.float32, device=logits.device) if want_entropy else None
+    entry = C.lib().grpo_logprob_fwd_paired if paired else C.lib().grpo_logprob_fwd
+    C.check(entry(_stream(), _dtype_code(logits), logits.data_ptr(), ld, n, V,
                                      _need(target, "target", "int32", n), _need(mask, "mask", "byte", n),
                                      logp.data_ptr(), lse.data_ptr() if lse is not None else None,
                                      ent.data_ptr() if ent is not None else None))

@@ -281,6 +281,24 @@ int grpo_logprob_fwd(void* stream, int32_t dtype, const void* logits, int64_t ld
                      int64_t V, const int32_t* target, const uint8_t* mask,
                      float* logp, float* lse, float* entropy);
 
+/* device.  grpo_logprob_fwd whose sums run in the lane partition and order of
+ * grpo_loss_fwd_bwd, so that logp, lse and entropy equal the fused loss's bit
+ * for bit on the same logits: a pi_old recorded by this pass at unchanged
+ * weights gives the ratio exactly 1 in the first training call ([P1] "pi_old
+ * must be frozen across the window": the ratio of the current policy to its
+ * detached copy).  It takes the fused loss's kernel shapes: the row held on
+ * chip (registers, then LDS, then for bf16 a part re-read) up to 262 144 bf16
+ * or 114 688 fp32 logits, and rows off 16-byte alignment on chip as the fused
+ * loss does when its dlogits rows share their phase (in place).  Where the
+ * fused loss streams (longer rows, or misaligned rows with dlogits in another
+ * phase or dtype) the two agree to float32 summation order only.  Slower than
+ * grpo_logprob_fwd for rows past 1024 vectors (the row on chip instead of
+ * streamed: 5.7 against 6.6 TB/s at V = 151 936 bf16).  Arguments, outputs and
+ * errors as grpo_logprob_fwd. */
+int grpo_logprob_fwd_paired(void* stream, int32_t dtype, const void* logits, int64_t ld, int64_t n_tok,
+                            int64_t V, const int32_t* target, const uint8_t* mask, float* logp, float* lse,
+                            float* entropy);
+
 /* grpo_loss_args.flags: leave the row and chunk reductions to a later
  * grpo_loss_stats call (row_off, row_stats and chunk_stats are then not read
  * and may be NULL), so that one reduction can serve several chunks. */
@@ -522,6 +540,13 @@ int grpo_old_cache_reset(grpo_old_cache* c);
  * ECAPACITY when the record does not fit in buf. */
 int grpo_old_cache_record(void* stream, grpo_old_cache* c, int32_t dtype, const void* logits, int64_t ld,
                           int64_t n_tok, int64_t V, const int32_t* target, const uint8_t* mask, float** slot);
+/* device.  grpo_old_cache_record with the record made by
+ * grpo_logprob_fwd_paired: replayed into grpo_loss_fwd_bwd on logits that
+ * have not changed since, the ratio is exactly 1 (on the rows
+ * grpo_logprob_fwd_paired covers). */
+int grpo_old_cache_record_paired(void* stream, grpo_old_cache* c, int32_t dtype, const void* logits, int64_t ld,
+                                 int64_t n_tok, int64_t V, const int32_t* target, const uint8_t* mask,
+                                 float** slot);
 /* host.  After a complete walk was recorded and replayed, starts the next
  * inner epoch's replay from call 0 (same order: unshuffled epochs reuse the
  * records by call order).  ESTATE otherwise.  A shuffled epoch reads pi_old

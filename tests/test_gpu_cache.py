@@ -150,3 +150,34 @@ def test_frozen_pi_old_makes_the_clip_bind_on_the_gpu():
             assert r["cache"] == 0
         else:
             assert r["cache"] >= 20, r
+
+
+def test_paired_record_gives_the_ratio_exactly_one_on_long_rows():
+    # Rows of V = 151 936 bf16 (past 1024 vectors, where the plain forward pass
+    # streams): pi_old recorded with grpo_old_cache_record_paired and replayed
+    # into the fused loss on unchanged logits gives log-ratio 0 on every valid
+    # token, so rho = 1 exactly, nothing clips and each token's surrogate loss is -A
+    # ([P1] "pi_old must be frozen across the window": the ratio of the policy
+    # to its detached copy).  The plain record agrees to float32 summation order.
+    n_rows, T, V = 4, 48, 151936
+    z, y, mask = _batch(n_rows, T, V, torch.bfloat16, seed=21, std=3.0)
+    zg, yg, mg = z.to(DEV), torch.from_numpy(y).to(DEV), torch.from_numpy(mask).to(DEV)
+    n = n_rows * T
+    adv = torch.tensor([1.0, -1.0, 0.5, -0.25], dtype=torch.float32, device=DEV)
+    row_off = torch.arange(0, n + 1, T, dtype=torch.int64, device=DEV)
+    tok_row = ops.tok_row(row_off, n)
+    recs = {}
+    for paired in (False, True):
+        cache = ops.OldLogprobCache(1, torch.empty(n, dtype=torch.float32, device=DEV))
+        cache.record(zg, yg, mg, paired=paired)
+        recs[paired] = cache.replay(n).clone()
+    s = 1.0 / float(mask.sum())
+    ws = ops.loss_fwd_bwd(zg, yg, mg, recs[True], tok_row, adv, row_off, scale=s)
+    torch.cuda.synchronize()
+    v = torch.from_numpy(mask.astype(bool)).to(DEV)
+    assert torch.equal(ws["logp"][v], recs[True][v])
+    assert ops.stats_to_dicts(ws["chunk_stats"])[0]["n_clipped"] == 0
+    want = -adv[tok_row.long()]
+    assert torch.equal(ws["loss_tok"][v], want[v])
+    diff = (recs[False] - recs[True]).abs()[v]
+    assert float(diff.max()) <= 2e-5

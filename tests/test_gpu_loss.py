@@ -446,3 +446,31 @@ def test_deferred_stats_over_several_chunks():
     want_rows = oracle.row_stats(ref, row_off.tolist())
     for r, (gr, wr) in enumerate(zip(rows, want_rows)):
         assert gr["n_valid"] == wr["n_valid"] and gr["loss_sum"] == pytest.approx(wr["loss_sum"], rel=1e-4, abs=1e-6)
+
+
+# (V, dtype, ld, in place): kernel shapes of the fused loss -- one wave per
+# row, 512 x 12, 1024 x 19, the LDS tail, the re-read part (bf16), fp32 past
+# the register file, and rows off 16-byte alignment updated in place
+@pytest.mark.parametrize("V,dtype,ld,inplace", [(1024, torch.float32, 1024, False),
+                                                (40960, torch.bfloat16, 40960, False),
+                                                (151936, torch.bfloat16, 151936, False),
+                                                (202048, torch.bfloat16, 202048, False),
+                                                (256000, torch.bfloat16, 256000, False),
+                                                (100000, torch.float32, 100000, False),
+                                                (50257, torch.bfloat16, 50257, True),
+                                                (32001, torch.bfloat16, 32007, True)])
+def test_paired_forward_equals_the_fused_loss(V, dtype, ld, inplace):
+    # grpo_logprob_fwd_paired runs the sums in the fused loss's lane partition:
+    # logp, lse and entropy equal the fused call's bit for bit (the plain
+    # forward pass streams rows past 1024 vectors and agrees only to float32
+    # summation order).
+    print(f"paired forward V={V} {dtype} ld={ld} inplace={inplace}", flush=True)
+    n = 6 if V > 60000 else 24
+    d = make_chunk(n, V, dtype, seed=V + 5, ld=ld)
+    g = d["g"]
+    f_logp, f_lse, f_ent = ops.logprob_fwd(d["logits"], g["target"], g["mask"], paired=True)
+    ws = run_gpu(d, scale=0.05, dlogits="inplace" if inplace else "new")
+    torch.cuda.synchronize()
+    assert torch.equal(f_logp, ws["logp"])
+    assert torch.equal(f_lse, ws["lse"])
+    assert torch.equal(f_ent, ws["entropy"])

@@ -805,7 +805,8 @@ def main():
                              if args.graph else ""),
                 "algorithmic_bytes_per_launch": int(units // launches), "avg_launch_ms": round(tot_ms / launches, 4)}
         roof["device_copy_GBs"] = round(step.copy_context(), 1)
-        if wl in ("qwen", "long") and not (args.terms or args.ahead or args.epochs != 1 or args.shuffle or args.vocab):
+        if wl in ("qwen", "long", "dynamic") and not (args.terms or args.ahead or args.epochs != 1 or args.shuffle
+                                                     or args.vocab):
             from yardstick.prof_summary import load_traffic
             rec = load_traffic(os.path.join(ROOT, "profiles", f"fused_loss_{wl}_pmc.txt"))
             if rec is not None:

@@ -997,7 +997,7 @@ int scratch_ptr(void** out) {
     if (e != hipSuccess) return fail(GRPO_EDEVICE, "grpo_lmhead_fwd_bwd_noalloc: hipGetDevice: %s",
                                      hipGetErrorString(e));
     if (dev < 0 || dev >= kMaxDevices)
-        return fail(GRPO_EDEVICE, "grpo_lmhead_fwd_bwd_noalloc: device %d beyond the %d this build tracks", dev,
+        return fail(GRPO_EDEVICE, "grpo_lmhead_fwd_bwd_noalloc: device %d beyond the %d the library tracks", dev,
                     kMaxDevices);
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {

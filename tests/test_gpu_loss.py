@@ -65,6 +65,9 @@ CASES = [
     (32001, torch.bfloat16, torch.bfloat16, 13),
     (151939, torch.bfloat16, torch.bfloat16, 5),
     (20001, torch.float32, torch.float32, 6),
+    # 512-thread blocks: 12 and 16 vectors per lane
+    (57344, torch.bfloat16, torch.float32, 5),
+    (65536, torch.bfloat16, torch.bfloat16, 4),
     (200000, torch.bfloat16, torch.bfloat16, 5),
     # rows past the register file: the tail of each lane's vectors in LDS
     (155656, torch.bfloat16, torch.bfloat16, 5),
@@ -181,7 +184,7 @@ def test_bad_targets_and_nan_logits_are_flagged_not_read():
                                            (4096, torch.bfloat16, 512), (1024, torch.float32, 256),
                                            (202048, torch.bfloat16, 8192), (256000, torch.bfloat16, 8192),
                                            (262152, torch.bfloat16, 2056), (50257, torch.bfloat16, 8192),
-                                           (32001, torch.bfloat16, 2048),
+                                           (32001, torch.bfloat16, 2048), (61440, torch.bfloat16, 4096),
                                            (40960, torch.bfloat16, 2048)])
 def test_special_rows(V, dtype, first):
     # Rows the one-sweep sums cannot take and that go through the exact

@@ -89,6 +89,38 @@ def test_shuffled_chunk_through_tok_src_equals_the_copied_chunk(dtype):
     assert_tokens_match(copy, ref, d)
 
 
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 1003), (torch.float32, 1001), (torch.bfloat16, 50257)])
+def test_shuffled_chunk_of_misaligned_rows_matches_oracle(dtype, V):
+    # Rows off 16-byte alignment (odd V, ld = V), read and written in the
+    # batch through tok_src: the register kernel over the aligned vectors that
+    # cover each row (dlogits shares the logits' layout).  A row's alignment
+    # phase depends on where it sits, so the chunk copied out contiguously is
+    # summed in another lane partition; both are checked against the oracle.
+    n_rows, T = (6, 8) if V > 10000 else (12, 40)
+    z, y, mask, adv, old = _batch(n_rows, T, V, dtype, seed=V)
+    rows = [4, 1, 5, 0] if V > 10000 else [7, 2, 11, 0]
+    src_off = np.arange(0, (n_rows + 1) * T, T, dtype=np.int64)
+    dst_off = np.arange(0, (len(rows) + 1) * T, T, dtype=np.int64)
+    src = np.array(oracle.chunk_token_sources(src_off.tolist(), rows), np.int64)
+    tok_src = ops.chunk_tok_src(G(src_off), G(np.array(rows, np.int64)), G(dst_off))
+    tok_row = ops.tok_row(G(dst_off), len(src))
+    adv_chunk = ops.gather(G(adv), G(np.array(rows, np.int64)))
+    zg = z.to(DEV)
+    dl_batch = torch.full_like(zg, 3.0)
+    via = ops.loss_fwd_bwd(zg, G(y), G(mask), G(old), tok_row, adv_chunk, G(dst_off), scale=0.01,
+                           dlogits=dl_batch, tok_src=tok_src)
+    torch.cuda.synchronize()
+    others = np.setdiff1d(np.arange(n_rows * T), src)
+    assert torch.all(dl_batch[torch.as_tensor(others, device=DEV)] == 3.0)   # rows outside the chunk untouched
+    out = {k: v[:len(src)] for k, v in via.items() if torch.is_tensor(v) and v.dim() == 1}
+    out["dlogits"] = dl_batch[torch.as_tensor(src, device=DEV)]
+    out["chunk_stats"], out["row_stats"] = via["chunk_stats"], via["row_stats"]
+    d = dict(z64=z.double().numpy()[src], target=y[src], mask=mask[src], old=old[src], dtype=dtype)
+    ref = oracle.loss_fwd_bwd(d["z64"], d["target"], d["mask"], d["old"].astype(np.float64),
+                              adv[np.repeat(rows, T)].astype(np.float64), 0.01)
+    assert_tokens_match(out, ref, d)
+
+
 def test_tok_src_outside_the_batch_poisons_the_token():
     z, y, mask, adv, old = _batch(2, 16, 256, torch.float32, seed=3)
     mask[:] = 1

@@ -28,7 +28,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import (DEV, compare_sampled, oracle_tokens, padded_on_gpu, sample_tokens, to_f64, torch_logp)
+from gpu_common import (DEV, compare_sampled, oracle_tokens, padded_on_gpu, sample_tokens, torch_logp)
 from grpo_token_level_amd import ops
 from oracle_pool import OraclePool
 

@@ -110,6 +110,7 @@ class Timed:
         self.torch = torch
         self.rec = []
         self.on = False
+        self.pending = None
 
     def begin(self):
         if not self.on:
@@ -124,6 +125,18 @@ class Timed:
         e1 = self.torch.cuda.Event(enable_timing=True)
         e1.record()
         self.rec.append((e0, e1, units, launches))
+
+    # The binding calls mark() (its on_launch hook) after marshalling a call's
+    # arguments, right before the library call, so that the window brackets
+    # the launch and not the Python work before it (when the GPU has drained
+    # its queue, as ahead of the single launch of a replicated tiny step, that
+    # work would otherwise count as kernel time).
+    def mark(self):
+        self.pending = self.begin()
+
+    def end_marked(self, units, launches=1):
+        self.end(self.pending, units, launches)
+        self.pending = None
 
     def totals(self):
         ms = sum(a.elapsed_time(b) for a, b, _, _ in self.rec)
@@ -263,10 +276,9 @@ class PaddedStep:
             for i in range(n_mini):
                 for j in range(n_micro):
                     a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
-                    ev = self.ahead_timed.begin()
                     self.cache.record(self.logits[a * T:e * T], self.target[a * T:e * T], self.mask[a * T:e * T],
-                                      paired=self.paired)
-                    self.ahead_timed.end(ev, self.ahead_units[(i, j)])
+                                      paired=self.paired, on_launch=self.ahead_timed.mark)
+                    self.ahead_timed.end_marked(self.ahead_units[(i, j)])
         k = 0
         for ep in range(self.mu):
             if self.ahead and not self.shuffle and ep > 0:
@@ -300,21 +312,19 @@ class PaddedStep:
                         old = self.cache.buf if self.ahead else self.old
                         if self.terms:
                             kw["ref_logp"] = self.ref
-                        ev = self.timed.begin()
                         ops.loss_fwd_bwd(self.logits, self.target, self.mask, old, self.tok_row, self.adv_chunk,
                                          self.row_off, dlogits=self.dlogits, ws=view, tok_src=self.tok_src,
-                                         defer_stats=True, **kw)
+                                         defer_stats=True, on_launch=self.timed.mark, **kw)
                     else:
                         a, e = ops.plan_chunk(n_rows, mini_rows, micro_rows, i, j)
                         t0, t1 = a * T, e * T
                         old = self.cache.replay(t1 - t0) if self.ahead else self.old[t0:t1]
                         if self.terms:
                             kw["ref_logp"] = self.ref[t0:t1]
-                        ev = self.timed.begin()
                         ops.loss_fwd_bwd(self.logits[t0:t1], self.target[t0:t1], self.mask[t0:t1], old,
                                          self.tok_row, self.adv_dev[a:e], self.row_off, dlogits=self.dlogits[t0:t1],
-                                         ws=view, defer_stats=True, **kw)
-                    self.timed.end(ev, self.chunk_units[(ep, i, j)])
+                                         ws=view, defer_stats=True, on_launch=self.timed.mark, **kw)
+                    self.timed.end_marked(self.chunk_units[(ep, i, j)])
                     k += 1
                 # the window's row reductions in one call (rows in mini-batch order)
                 self.ws["row_stats"] = self.stats_dev[w * mini_rows:(w + 1) * mini_rows]
@@ -459,11 +469,10 @@ class DynamicStep(PaddedStep):
             ro = self.meta_dev[starts[k]:starts[k] + e - a + 1]
             tr = ops.tok_row(ro, t1 - t0, out=self.tok_row[:t1 - t0])
             ws = {kk: self.ws[kk][t0:t1] for kk in ("logp", "lse", "entropy", "loss_tok", "kl_tok", "tok_flags")}
-            ev = self.timed.begin()
             ops.loss_fwd_bwd(self.logits[t0:t1], self.target[t0:t1], self.mask[t0:t1], self.old[t0:t1], tr,
                              self.adv_dev[a:e], ro, scale=1.0, denom=self.N, dlogits=self.dlogits[t0:t1], ws=ws,
-                             defer_stats=True)
-            self.timed.end(ev, chunk_bytes(self.mask_np[t0:t1], b["V"], 2, 2))
+                             defer_stats=True, on_launch=self.timed.mark)
+            self.timed.end_marked(chunk_bytes(self.mask_np[t0:t1], b["V"], 2, 2))
         self.ws["row_stats"] = self.stats_dev
         self.ws["chunk_stats"] = self.win_stats
         ops.loss_stats(self.ws, self.offB_dev, scale=1.0, denom=self.N)
@@ -560,11 +569,11 @@ class CompactStep:
                   for kk, v in self.ws.items()}
             ws["row_stats"] = self.ws["row_stats"][:e - a]
             ws["chunk_stats"] = self.stats_dev[k:k + 1]
-            ev = self.timed.begin()
             ops.lmhead_fwd_bwd(self.h[t0:t1], self.W, self.Wt, self.target[t0:t1], self.mask[t0:t1],
                                self.old[t0:t1], tr, self.adv_dev[a:e], ro, self.dW, denom=self.N,
-                               dh=self.dh[t0:t1], ws=ws, workspace=self.workspace, keep_z=self.keep_z)
-            self.timed.end(ev, 6.0 * self.V * self.H * int(self.mask_np[t0:t1].sum()))
+                               dh=self.dh[t0:t1], ws=ws, workspace=self.workspace, keep_z=self.keep_z,
+                               on_launch=self.timed.mark)
+            self.timed.end_marked(6.0 * self.V * self.H * int(self.mask_np[t0:t1].sum()))
         self.stats_host.copy_(self.stats_dev, non_blocking=True)
         torch.cuda.current_stream().synchronize()
         acc = ops.Accumulator(len(self.chunks))

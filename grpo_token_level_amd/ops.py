@@ -226,17 +226,20 @@ class OldLogprobCache:
         start = (addr - self.buf.data_ptr()) // 4 if n else 0
         return self.buf[start:start + n]
 
-    def record(self, logits, target, mask, paired=False):
+    def record(self, logits, target, mask, paired=False, on_launch=None):
         """Ahead pass of one chunk into the next record; returns its view.
         ``paired``: grpo_old_cache_record_paired (the record equals the fused
-        loss's log-probs bit for bit on unchanged logits)."""
+        loss's log-probs bit for bit on unchanged logits).  ``on_launch``: as
+        in loss_fwd_bwd."""
         n, V = logits.shape
         ld = _matrix(logits, "logits", n, V)
         slot = ctypes.c_void_p()
         entry = C.lib().grpo_old_cache_record_paired if paired else C.lib().grpo_old_cache_record
-        C.check(entry(_stream(), ctypes.byref(self.c), _dtype_code(logits),
-                                              logits.data_ptr(), ld, n, V, _need(target, "target", "int32", n),
-                                              _need(mask, "mask", "byte", n), ctypes.byref(slot)))
+        args = (_stream(), ctypes.byref(self.c), _dtype_code(logits), logits.data_ptr(), ld, n, V,
+                _need(target, "target", "int32", n), _need(mask, "mask", "byte", n), ctypes.byref(slot))
+        if on_launch is not None:
+            on_launch()
+        C.check(entry(*args))
         return self._view(slot.value or 0, n)
 
     def rewind(self):
@@ -511,7 +514,8 @@ def _set_common(a, target, mask, old_logp, tok_row_, adv_row, row_off, denom, ws
 
 def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, scale=1.0, denom=None,
                  eps_low=0.2, eps_high=0.2, dlogits="new", out_dtype=None, ws=None, row_weight=None,
-                 ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3, tok_src=None, defer_stats=False):
+                 ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3, tok_src=None, defer_stats=False,
+                 on_launch=None):
     """Fused GRPO loss forward/backward over one chunk (grpo_loss_fwd_bwd).
 
     ``defer_stats``: leave the row and chunk reductions to a later
@@ -528,6 +532,9 @@ def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, 
     is tok_src's length.
     Every tensor's device, element type and length are checked against what
     the call will touch before anything is launched (ValueError).
+    ``on_launch``: called with no arguments after the arguments are checked
+    and marshalled, right before the library call (a timing hook: an event
+    recorded there brackets the launch, not the Python work before it).
     Returns the workspace dict with ``dlogits`` added."""
     torch = _torch()
     if logits.dim() != 2:
@@ -563,6 +570,8 @@ def loss_fwd_bwd(logits, target, mask, old_logp, tok_row_, adv_row, row_off, *, 
     if tok_src is not None:
         a.tok_src = tok_src.data_ptr() if n else None
         a.n_src = n_src
+    if on_launch is not None:
+        on_launch()
     C.check(C.lib().grpo_loss_fwd_bwd(_stream(), ctypes.byref(a)))
     ws["dlogits"] = dl
     return ws
@@ -627,7 +636,8 @@ def lmhead_workspace_bytes(n_tok, H, V, keep_z=False):
 
 def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off, dW, *, scale=1.0, denom=None,
                    eps_low=0.2, eps_high=0.2, dh=None, ws=None, workspace=None, row_weight=None,
-                   ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3, noalloc=False, keep_z=False):
+                   ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3, noalloc=False, keep_z=False,
+                   on_launch=None):
     """Fused LM-head GRPO loss over one chunk (grpo_lmhead_fwd_bwd).
 
     ``dW`` (fp32 [V x H]) is accumulated into; ``dh`` (fp32 [n_tok x H]) is
@@ -637,7 +647,7 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
     fixed scratch (no workspace is passed; the caller still provides every
     input and output).  ``keep_z``: GRPO_LMHEAD_KEEP_Z (pass 1 keeps the
     chunk's fp32 logits in the workspace and pass 2 reads them back instead
-    of recomputing them)."""
+    of recomputing them).  ``on_launch``: as in loss_fwd_bwd."""
     torch = _torch()
     if h.dim() != 2 or W.dim() != 2:
         raise ValueError("h and W must be 2-D")
@@ -681,6 +691,8 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
         a.workspace_bytes = workspace.numel() * workspace.element_size()
     _set_terms(a, row_weight, ref_logp, ent_coef, kl_coef, kl_type, ws, n_rows, n, n)
     entry = C.lib().grpo_lmhead_fwd_bwd_noalloc if noalloc else C.lib().grpo_lmhead_fwd_bwd
+    if on_launch is not None:
+        on_launch()
     C.check(entry(_stream(), ctypes.byref(a)))
     ws["dh"] = dh
     ws["workspace"] = workspace

@@ -824,7 +824,8 @@ def main():
     out = {"metric": METRIC, "value": round(value, 1), "unit": "valid tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "ms_per_step_median": round(median_ms, 4),
            "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg, "roofline": roof}
+           "vs_baseline": None, "dtype": "bf16" if wl == "compact" else "f32", "data": "synthetic", "config": cfg,
+           "roofline": roof}
     if args.copy_calibration:
         # known-size plain copy for the byte counters: 1 GiB read, 1 GiB written
         x = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")

@@ -306,6 +306,25 @@ def test_old_cache_state_machine_without_device_work():
     assert L.grpo_old_cache_init(ctypes.byref(c), None, 0, C.ptr64(off), 0) == -1
 
 
+def test_paired_old_cache_record_keeps_the_same_bookkeeping():
+    # grpo_old_cache_record_paired differs only in the forward pass it runs:
+    # zero-token records exercise its bookkeeping on the CPU, interleaved with
+    # plain records in one walk
+    c = C.OldCache()
+    off = np.zeros(4, np.int64)
+    L = C.lib()
+    assert L.grpo_old_cache_init(ctypes.byref(c), None, 0, C.ptr64(off), 3) == 0
+    assert L.grpo_old_cache_record_paired(None, ctypes.byref(c), 1, None, 8, 0, 8, None, None, None) == 0
+    assert L.grpo_old_cache_record(None, ctypes.byref(c), 1, None, 8, 0, 8, None, None, None) == 0
+    assert L.grpo_old_cache_record_paired(None, ctypes.byref(c), 1, None, 8, 0, 8, None, None, None) == 0
+    assert c.recorded == 3
+    assert L.grpo_old_cache_record_paired(None, ctypes.byref(c), 1, None, 8, 0, 8, None, None, None) == -9
+    assert L.grpo_old_cache_reset(ctypes.byref(c)) == 0
+    assert L.grpo_old_cache_record_paired(None, ctypes.byref(c), 1, ctypes.c_void_p(16), 8, 4, 8,
+                                          ctypes.c_void_p(16), ctypes.c_void_p(16), None) == -7   # does not fit
+    assert L.grpo_old_cache_record_paired(None, None, 1, None, 8, 0, 8, None, None, None) == -1
+
+
 def test_epoch_plan_matches_oracle_bit_exact():
     rng = np.random.default_rng(6)
     cases = [(32, 4, 16, 8, 3, True, 7), (32, 4, 16, 8, 2, False, 7), (8, 2, 4, 2, 1, True, 0),

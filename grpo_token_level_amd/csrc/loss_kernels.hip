@@ -870,6 +870,150 @@ __global__ __launch_bounds__(TPR == 64 ? 256 : TPR) void tok_reg_kernel(const To
     }
 }
 
+// ---------------------------------------------------------------- paired forward kernel
+//
+// Forward only, with the fused loss's arithmetic: the register kernel's lane
+// partition (TPR lanes per row, lane tid taking vectors k*TPR + tid in
+// increasing k for k < NT = NV + NL + NG), its per-lane shift from the lane's
+// first vector, its block merge and its exact fallback, so logp, lse and
+// entropy come out with the fused call's bits.  The row need not stay on
+// chip for a gradient sweep, so the vectors stream through a window of PB
+// loads per lane (double-buffered), and two 1024-thread blocks fit a CU.
+template <int DTI, int TPR, int NT, bool MIS>
+__global__ __launch_bounds__(TPR == 64 ? 256 : TPR, TPR == 1024 ? 2 : 1) void tok_fwd_paired_kernel(const TokParams p) {
+    constexpr int VEC = In<DTI>::VEC;
+    constexpr int WPR = TPR / 64;
+    constexpr int RPB = TPR == 64 ? 4 : 1;
+    constexpr int PB = 4;   // loads in flight per lane (per half of the window)
+    const int lrow = RPB == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int tid = RPB == 1 ? (int)threadIdx.x : (int)(threadIdx.x & 63);
+    const int64_t t = (int64_t)xcd_runs(blockIdx.x, gridDim.x) * RPB + lrow;
+    if (t >= p.n_tok) return;   // wave-uniform (RPB > 1) or block-uniform (RPB == 1)
+
+    const int64_t src = token_source(p, t);
+    if (src < 0) {
+        if (tid == 0) bad_source_outputs<false>(p, t);
+        return;
+    }
+    if (p.mask[src] == 0) {
+        if (tid == 0) masked_outputs<false>(p, t);
+        return;
+    }
+    const char* irow = reinterpret_cast<const char*>(p.logits) + src * p.ld * In<DTI>::BYTES;
+    // row geometry as in the register kernel (aligned rows, or the aligned
+    // vectors covering a row off 16-byte alignment)
+    int hb = 0, nvec, ilo = 0, ihi;
+    const uint4* vrow;
+    if constexpr (MIS) {
+        const uintptr_t ia = reinterpret_cast<uintptr_t>(irow);
+        hb = (int)((ia & 15u) / In<DTI>::BYTES);
+        vrow = reinterpret_cast<const uint4*>(ia - (ia & 15u));
+        nvec = (int)((p.V + hb + VEC - 1) / VEC);
+        ilo = 1;
+        ihi = nvec - 1;
+    } else {
+        vrow = reinterpret_cast<const uint4*>(irow);
+        nvec = (int)(p.V / VEC);
+        ihi = nvec;
+    }
+    const unsigned nwhole = ihi > ilo ? (unsigned)(ihi - ilo) : 0u;
+    [[maybe_unused]] const int klast = (nvec - 1) / TPR, llast = (nvec - 1) % TPR;
+
+    const int32_t y = p.target[src];
+    const bool ybad = (uint32_t)y >= (uint64_t)p.V;
+    const int vy = ybad ? 0 : (y + hb) / VEC;
+    const int own_tid = vy % TPR;
+    float zy_mine = 0.0f;
+    if (!ybad && tid == own_tid) zy_mine = In<DTI>::scalar(irow, y);
+    [[maybe_unused]] __shared__ float s_part[WPR][3];
+    [[maybe_unused]] __shared__ float s_zy;
+    float zy;
+    if constexpr (WPR == 1) {
+        zy = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zy_mine), own_tid));
+    } else {
+        if (tid == own_tid) s_zy = zy_mine;   // read after the first barrier below
+    }
+
+    // one vector of the sweep: the whole-vector sums, or the row's elements of
+    // a partial vector (MIS), exactly as the register kernel takes vector k
+    auto sums = [&](int k, const uint4& v, float c, float& s, float& w, bool clamped) {
+        const int idx = k * TPR + tid;
+        if ((unsigned)(idx - ilo) < nwhole) {
+            if (clamped) sweep_sums_clamped<DTI>(v, c, s, w);
+            else sweep_sums<DTI>(v, c, s, w);
+        }
+        if constexpr (MIS) {
+            if ((k == 0 && tid == 0) || (k == klast && tid == llast && nvec > 1))
+                sweep_sums_part<DTI>(v, hb - idx * VEC, (int)p.V + hb - idx * VEC, c, s, w, clamped);
+        }
+    };
+    auto load = [&](int k) { return vrow[min(k * TPR + tid, nvec - 1)]; };
+
+    float c = -INFINITY, s = 0.0f, w = 0.0f;
+    uint4 buf[2][PB];
+#pragma unroll
+    for (int b = 0; b < PB; ++b)
+        if (b < NT) buf[0][b] = load(b);
+    if (tid < nvec) {
+        float f[VEC];
+        In<DTI>::unpack(buf[0][0], f);
+        float m0;
+        if constexpr (MIS) {
+            const int elo = hb - tid * VEC, ehi = (int)p.V + hb - tid * VEC;
+            m0 = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                if (e >= elo && e < ehi) m0 = fmaxf(m0, f[e]);
+        } else {
+            m0 = f[0];
+#pragma unroll
+            for (int e = 1; e < VEC; ++e) m0 = fmaxf(m0, f[e]);
+        }
+        c = m0 * kLog2e;
+        if (!isfinite(c)) c = 0.0f;
+    }
+    // window i holds vectors i*PB .. i*PB+PB-1; the next window's loads are
+    // issued before this window's sums
+#pragma unroll
+    for (int i = 0; i * PB < NT; ++i) {
+        const int cur = i & 1;
+        if ((i + 1) * PB < NT) {
+#pragma unroll
+            for (int b = 0; b < PB; ++b)
+                if ((i + 1) * PB + b < NT) buf[cur ^ 1][b] = load((i + 1) * PB + b);
+        }
+#pragma unroll
+        for (int b = 0; b < PB; ++b)
+            if (i * PB + b < NT) {
+                opaque_vec(buf[cur][b]);
+                sums(i * PB + b, buf[cur][b], c, s, w, false);
+            }
+    }
+    block_merge<WPR>(c, s, w, tid, s_part);
+    if constexpr (WPR > 1) zy = s_zy;
+
+    if (!(isfinite(s) && isfinite(w))) {
+        // the register kernel's exact sweeps, the row read again
+        float m = -INFINITY;
+        for (int k = 0; k < NT; ++k) {
+            const uint4 v = load(k);
+            const int idx = k * TPR + tid;
+            if ((unsigned)(idx - ilo) < nwhole) sweep_max<DTI>(v, m);
+            if constexpr (MIS) {
+                if ((k == 0 && tid == 0) || (k == klast && tid == llast && nvec > 1))
+                    sweep_max_part<DTI>(v, hb - idx * VEC, (int)p.V + hb - idx * VEC, m);
+            }
+        }
+        m = block_max<WPR>(m, tid, s_part);
+        c = m * kLog2e;
+        s = 0.0f;
+        w = 0.0f;
+        for (int k = 0; k < NT; ++k) sums(k, load(k), c, s, w, true);
+        block_sum2<WPR>(s, w, tid, s_part);
+    }
+    token_tail<false>(p, t, src, c, s, w, zy, ybad, tid == 0);
+}
+
 // ---------------------------------------------------------------- streaming kernel
 //
 // Rows the register/LDS path cannot take: V beyond its capacity, or rows off
@@ -1467,6 +1611,39 @@ hipError_t launch_reg(const RegCfg& c, const TokParams& p, hipStream_t st, bool 
     return hipErrorInvalidValue;
 }
 
+// The paired forward kernel for the register shape c (NT = its vectors per lane).
+template <int DTI>
+hipError_t launch_paired(const RegCfg& c, const TokParams& p, hipStream_t st, bool mis) {
+    const int rpb = c.tpr == 64 ? 4 : 1;
+    const dim3 grid((unsigned)((p.n_tok + rpb - 1) / rpb));
+    const dim3 block(c.tpr == 64 ? 256 : c.tpr);
+    const int nt = c.nv + c.nl + c.ng;
+#define GRPO_PAIRED_CASE(TPR_, NT_)                                                                         \
+    if (c.tpr == TPR_ && nt == NT_) {                                                                        \
+        if (mis) hipLaunchKernelGGL((tok_fwd_paired_kernel<DTI, TPR_, NT_, true>), grid, block, 0, st, p);  \
+        else hipLaunchKernelGGL((tok_fwd_paired_kernel<DTI, TPR_, NT_, false>), grid, block, 0, st, p);     \
+        return hipGetLastError();                                                                            \
+    }
+    GRPO_PAIRED_CASE(64, 1)
+    GRPO_PAIRED_CASE(64, 2)
+    GRPO_PAIRED_CASE(64, 4)
+    GRPO_PAIRED_CASE(64, 8)
+    GRPO_PAIRED_CASE(256, 4)
+    GRPO_PAIRED_CASE(256, 8)
+    GRPO_PAIRED_CASE(256, 16)
+    GRPO_PAIRED_CASE(256, 24)
+    GRPO_PAIRED_CASE(512, 12)
+    GRPO_PAIRED_CASE(512, 16)
+    GRPO_PAIRED_CASE(1024, 8)
+    GRPO_PAIRED_CASE(1024, 12)
+    GRPO_PAIRED_CASE(1024, 16)
+    GRPO_PAIRED_CASE(1024, 19)
+    GRPO_PAIRED_CASE(1024, 28)
+    GRPO_PAIRED_CASE(1024, 32)
+#undef GRPO_PAIRED_CASE
+    return hipErrorInvalidValue;
+}
+
 template <int DTI, int DTO, bool GRAD>
 hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st, bool mis_ok = false, bool paired = false) {
     if (p.n_tok == 0) return hipSuccess;
@@ -1481,7 +1658,12 @@ hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st, bool mis_
         const int64_t nvec = p.V / In<DTI>::VEC;
         for (const RegCfg& c : kRegCfgs) {
             if (c.ng > 0 && !(as_grad && DTI == GRPO_BF16)) continue;
-            if ((int64_t)c.tpr * (c.nv + c.nl + c.ng) >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st);
+            if ((int64_t)c.tpr * (c.nv + c.nl + c.ng) >= nvec) {
+                if constexpr (!GRAD) {
+                    if (paired) return launch_paired<DTI>(c, p, st, false);
+                }
+                return launch_reg<DTI, DTO, GRAD>(c, p, st);
+            }
         }
     }
     // Rows off 16-byte alignment whose gradient rows share their alignment
@@ -1492,7 +1674,12 @@ hipError_t launch_tok(const TokParams& p, bool vec_ok, hipStream_t st, bool mis_
         const int64_t nvec = (p.V + 2 * In<DTI>::VEC - 2) / In<DTI>::VEC;
         for (const RegCfg& c : kRegCfgs) {
             if (c.nl > 0 || c.ng > 0) continue;
-            if ((int64_t)c.tpr * c.nv >= nvec) return launch_reg<DTI, DTO, GRAD>(c, p, st, true);
+            if ((int64_t)c.tpr * c.nv >= nvec) {
+                if constexpr (!GRAD) {
+                    if (paired) return launch_paired<DTI>(c, p, st, true);
+                }
+                return launch_reg<DTI, DTO, GRAD>(c, p, st, true);
+            }
         }
     }
     hipLaunchKernelGGL((tok_stream_kernel<DTI, DTO, GRAD>), dim3((unsigned)p.n_tok), dim3(kStreamTPR), 0, st, p);

@@ -290,8 +290,9 @@ int grpo_logprob_fwd(void* stream, int32_t dtype, const void* logits, int64_t ld
  * chip (registers, then LDS, then for bf16 a part re-read) up to 262 144 bf16
  * or 114 688 fp32 logits, and rows off 16-byte alignment on chip as the fused
  * loss does when its dlogits rows share their phase (in place).  Where the
- * fused loss streams (longer rows, or misaligned rows with dlogits in another
- * phase or dtype) the two agree to float32 summation order only.  Slower than
+ * fused loss streams (longer rows, or rows whose dlogits rows are off 16-byte
+ * alignment in another phase or dtype, such as fp32 logits into bf16 dlogits
+ * with V not a multiple of 8) the two agree to float32 summation order only.  Slower than
  * grpo_logprob_fwd for rows past 1024 vectors (the row on chip instead of
  * streamed: 5.7 against 6.6 TB/s at V = 151 936 bf16).  Arguments, outputs and
  * errors as grpo_logprob_fwd. */

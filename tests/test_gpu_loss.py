@@ -389,6 +389,16 @@ def test_random_shapes_match_oracle(k, V, din, n, pad, mode):
         assert np.max(np.abs(to_f64(logp)[fin] - fwd["logp"][fin]), initial=0.0) <= tol
         assert np.max(np.abs(to_f64(lse) - fwd["lse"]), initial=0.0) <= tol
         assert_same_up_to_sum_order(logp, ws["logp"])
+        # the paired forward pass: the fused call's bits wherever that call keeps
+        # aligned rows on chip (logits and dlogits rows both 16-byte aligned, up
+        # to 262 144 bf16 / 114 688 fp32 logits)
+        vec = 8 if din == torch.bfloat16 else 4
+        out_b = 2 if dout == torch.bfloat16 else 4
+        if (V % vec == 0 and (V + pad) % vec == 0 and (V * out_b) % 16 == 0
+                and V // vec <= (32768 if din == torch.bfloat16 else 28672)):
+            p_logp, p_lse, p_ent = ops.logprob_fwd(d["logits"], d["g"]["target"], d["g"]["mask"], paired=True)
+            assert torch.equal(p_logp, ws["logp"]) and torch.equal(p_lse, ws["lse"])
+            assert torch.equal(p_ent, ws["entropy"])
 
 
 def test_count_valid_and_tok_row():

@@ -322,3 +322,56 @@ def sample_tokens(mask_np, row_len, n_valid=24, n_masked=8, seed=0):
     for r0 in np.cumsum(np.concatenate([[0], row_len]))[:-1][:4]:
         pick.append(int(r0))
     return np.unique(np.asarray(pick, np.int64))
+
+
+
+CLIP_EDGE = 1e-3
+
+
+def old_at_kernel_clip(flags, ref, old, adv_tok, eps=(0.2, 0.2)):
+    """Old log-probs that make the oracle take the kernel's clip decision
+    (bit 1 of ``flags``, the kernel's tok_flags over the tokens of ``ref``).
+
+    The gate of the clipped surrogate is an integer decision on the ratio: the
+    kernel takes it in float32, the oracle in float64, and where the ratio
+    lies within CLIP_EDGE (relative) of the bound that applies (1 + eps_high
+    for A > 0, 1 - eps_low for A < 0) both are right.  A token's own gradient
+    row follows its own decision, but a sum over tokens (dW) holds every one,
+    so the reference is re-evaluated at the kernel's decision: an edge token
+    whose decision differs gets the old log-prob that puts the oracle's ratio
+    1e-9 (relative) from the bound on the kernel's side, which moves its ratio
+    by no more than the kernel's own log-prob error; no other input changes.
+    A decision that differs away from an edge fails.
+
+    Returns ``(old2, n_moved)``, ``old2`` None when every decision agrees."""
+    old = np.asarray(old, np.float64)
+    adv_tok = np.asarray(adv_tok, np.float64)
+    valid = np.asarray(ref["valid"], bool)
+    gclip = ((np.asarray(flags) >> 1) & 1).astype(bool) & valid
+    differ = gclip != (np.asarray(ref["clipped"], bool) & valid)
+    if not differ.any():
+        return None, 0
+    bound = np.where(adv_tok > 0, 1.0 + eps[1], 1.0 - eps[0])
+    with np.errstate(over="ignore"):
+        rho = np.exp(ref["logp"] - old)
+    near = np.abs(rho - bound) <= CLIP_EDGE * bound
+    assert np.all(near[differ]), ("clip decision differs away from an edge", np.nonzero(differ & ~near))
+    side = np.sign(adv_tok) * np.where(gclip, 1.0, -1.0)   # +1: the ratio goes above the bound
+    old2 = old.copy()
+    old2[differ] = ref["logp"][differ] - (np.log(bound[differ]) + side[differ] * 1e-9)
+    return old2, int(differ.sum())
+
+
+def oracle_lmhead_at_kernel_clip(flags, h64, W64, target, mask, old, adv_tok, scale, eps=(0.2, 0.2), **terms):
+    """oracle.lmhead_fwd_bwd with each clip-edge token at the kernel's clip
+    decision (old_at_kernel_clip).  Returns ``(ref, n_moved)``."""
+    old = np.asarray(old, np.float64)
+    adv_tok = np.asarray(adv_tok, np.float64)
+    ref = oracle.lmhead_fwd_bwd(h64, W64, target, mask, old, adv_tok, scale, eps[0], eps[1], **terms)
+    old2, moved = old_at_kernel_clip(flags, ref, old, adv_tok, eps)
+    if old2 is None:
+        return ref, 0
+    ref2 = oracle.lmhead_fwd_bwd(h64, W64, target, mask, old2, adv_tok, scale, eps[0], eps[1], **terms)
+    gclip = ((np.asarray(flags) >> 1) & 1).astype(bool) & ref2["valid"]
+    assert np.array_equal(ref2["clipped"] & ref2["valid"], gclip)
+    return ref2, moved

@@ -21,7 +21,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import DEV, rel_l2, to_f64
+from gpu_common import DEV, old_at_kernel_clip, oracle_lmhead_at_kernel_clip, rel_l2, to_f64
 from grpo_token_level_amd import ops
 
 pytestmark = pytest.mark.gpu
@@ -62,6 +62,15 @@ def _run(c, dW, scale, Wt=None, eps=(0.2, 0.2), keep_z=False):
                               g["row_off"], dW, scale=scale, eps_low=eps[0], eps_high=eps[1], keep_z=keep_z)
 
 
+def _ref(c, ws, scale, mask=None, adv_tok=None, **terms):
+    """The oracle on the case's inputs, clip-edge tokens at the kernel's
+    decision (oracle_lmhead_at_kernel_clip)."""
+    ref, _ = oracle_lmhead_at_kernel_clip(
+        ws["tok_flags"].cpu().numpy(), c["h64"], c["W64"], c["target"], c["mask"] if mask is None else mask,
+        c["old"], c["adv"].astype(np.float64)[c["tok_row"]] if adv_tok is None else adv_tok, scale, **terms)
+    return ref
+
+
 GRAD_ROW = 2.0 ** -8 + 2.0 ** -12
 
 
@@ -86,11 +95,9 @@ def _check(ws, dW, ref, c, dW_ref, dz_ref=None):
     assert not lt[~valid].any() and not logp[~valid].any()
     L = float(np.sum(ref["loss_tok"][valid]))
     assert abs(float(np.sum(lt[valid])) - L) <= 1e-4 * max(abs(L), float(np.sum(np.abs(ref["loss_tok"])))) + 1e-12
-    with np.errstate(over="ignore"):
-        rho = np.exp(ref["logp"] - c["old"])
-    edge = (np.abs(rho - 1.2) < 1e-3) | (np.abs(rho - 0.8) < 1e-3)
+    # ref takes the kernel's decision on clip-edge tokens (_ref)
     gclip = ((flags >> 1) & 1).astype(bool)
-    assert not np.any((gclip != (ref["clipped"] & valid)) & ~edge)
+    assert np.array_equal(gclip, ref["clipped"] & valid)
     assert rel_l2(to_f64(ws["dh"]), ref["dh"]) <= TOL_GRAD, rel_l2(to_f64(ws["dh"]), ref["dh"])
     assert rel_l2(to_f64(dW), dW_ref) <= TOL_GRAD, rel_l2(to_f64(dW), dW_ref)
     assert not to_f64(ws["dh"])[~valid].any()
@@ -113,11 +120,39 @@ def test_lmhead_matches_oracle(n, H, V, keep_z):
     dW = torch.zeros((V, H), dtype=torch.float32, device=DEV)
     ws = _run(c, dW, 1.0 / N, keep_z=keep_z)
     torch.cuda.synchronize()
-    ref = oracle.lmhead_fwd_bwd(c["h64"], c["W64"], c["target"], c["mask"], c["old"].astype(np.float64),
-                                c["adv"].astype(np.float64)[c["tok_row"]], 1.0 / N)
+    ref = _ref(c, ws, 1.0 / N)
     _check(ws, dW, ref, c, ref["dW"])
     st = ops.stats_to_dicts(ws["chunk_stats"])[0]
     assert st["n_valid"] == int(c["mask"].sum())
+
+
+def _random_lmhead_shapes(count=32, seed=909):
+    """Seeded random shapes: tokens 1..1999, H and V multiples of 8 (V log-uniform
+    up to 80000, so some span two pass-2 chunks), masked fraction and segment
+    count drawn too, and keep_z on half of them; n is cut so that n*H*V stays
+    where the oracle takes well under a second."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(count):
+        n = int(rng.integers(1, 2000))
+        H = 8 * int(rng.integers(1, 193))
+        V = 8 * int(np.exp(rng.uniform(np.log(2), np.log(10000))))
+        n = max(1, min(n, int(1e11 // (H * V))))
+        out.append((k, n, H, V, bool(rng.random() < 0.5), float(rng.choice([0.0, 0.2, 0.9])),
+                    int(rng.integers(1, 6))))
+    return out
+
+
+@pytest.mark.parametrize("k,n,H,V,keep_z,masked,n_rows", _random_lmhead_shapes())
+def test_lmhead_random_shapes_match_oracle(k, n, H, V, keep_z, masked, n_rows):
+    print(f"lmhead random k={k} n={n} H={H} V={V} keep_z={keep_z} masked={masked} rows={n_rows}", flush=True)
+    c = _case(n, H, V, seed=3000 + k, masked_frac=masked, n_rows=n_rows)
+    N = max(1, int(c["mask"].sum()))
+    dW = torch.zeros((V, H), dtype=torch.float32, device=DEV)
+    ws = _run(c, dW, 1.0 / N, keep_z=keep_z)
+    torch.cuda.synchronize()
+    ref = _ref(c, ws, 1.0 / N)
+    _check(ws, dW, ref, c, ref["dW"])
 
 
 def test_lmhead_accumulates_dW_over_chunks():
@@ -127,7 +162,7 @@ def test_lmhead_accumulates_dW_over_chunks():
     N = int(c["mask"].sum())
     Wt = ops.transpose_bf16(c["W"])
     dW = torch.zeros((V, H), dtype=torch.float32, device=DEV)
-    dhs = []
+    dhs, flags = [], []
     for a, b in ((0, 90), (90, n)):
         sub = dict(c)
         sub["h"] = c["h"][a:b]
@@ -139,10 +174,10 @@ def test_lmhead_accumulates_dW_over_chunks():
         sub["g"]["row_off"] = torch.tensor([0, b - a], dtype=torch.int64, device=DEV)
         ws = _run(sub, dW, 1.0 / N, Wt=Wt)
         dhs.append(ws["dh"].clone())
+        flags.append(ws["tok_flags"].clone())
     torch.cuda.synchronize()
     adv_tok = np.full(n, float(c["adv"][0]))
-    ref = oracle.lmhead_fwd_bwd(c["h64"], c["W64"], c["target"], c["mask"], c["old"].astype(np.float64), adv_tok,
-                                1.0 / N)
+    ref = _ref(c, {"tok_flags": torch.cat(flags)}, 1.0 / N, adv_tok=adv_tok)
     assert rel_l2(to_f64(dW), ref["dW"]) <= TOL_GRAD
     assert rel_l2(to_f64(torch.cat(dhs)), ref["dh"]) <= TOL_GRAD
 
@@ -225,8 +260,7 @@ def test_lmhead_skips_masked_tokens(pattern):
     dW = base.clone()
     ws = _run(c, dW, 1.0 / N)
     torch.cuda.synchronize()
-    ref = oracle.lmhead_fwd_bwd(c["h64"], c["W64"], c["target"], m, c["old"].astype(np.float64),
-                                c["adv"].astype(np.float64)[c["tok_row"]], 1.0 / N)
+    ref = _ref(c, ws, 1.0 / N, mask=m)
     _check(ws, dW - base, ref, c, ref["dW"])
     assert ops.stats_to_dicts(ws["chunk_stats"])[0]["n_valid"] == N
 
@@ -337,9 +371,10 @@ def test_compaction_workload_full_size_sampled():
     hh = h[torch.as_tensor(idx, device=DEV)].double().cpu().numpy()
     row_of = np.searchsorted(off, idx, side="right") - 1
     Nn = int(mask.sum())
-    ref = oracle.lmhead_fwd_bwd(hh, W64, target[idx], mask[idx], old[torch.as_tensor(idx, device=DEV)].double().cpu().numpy(),
-                                adv_row.astype(np.float64)[row_of], 1.0 / Nn)
     ii = torch.as_tensor(idx, device=DEV)
+    ref, _ = oracle_lmhead_at_kernel_clip(out["tok_flags"][ii].cpu().numpy(), hh, W64, target[idx], mask[idx],
+                                          old[ii].double().cpu().numpy(), adv_row.astype(np.float64)[row_of],
+                                          1.0 / Nn)
     v = ref["valid"]
     assert np.max(np.abs(to_f64(out["logp"][ii])[v] - ref["logp"][v])) <= 1e-4
     assert rel_l2(to_f64(dh[ii]), ref["dh"]) <= TOL_GRAD
@@ -393,10 +428,16 @@ def test_compaction_workload_full_size_sampled():
     while len(cols) < 64:
         cols = np.unique(np.concatenate([cols, rng.choice(V, 64 - len(cols), replace=False)]))
     from oracle_pool import OraclePool
+    old_c, adv_c = old[t0:t1].double().cpu().numpy(), adv_row.astype(np.float64)[a + row_c]
     with OraclePool() as P:
-        ref = P.loss_host(z, target[t0:t1], m_c, old[t0:t1].double().cpu().numpy(),
-                          adv_row.astype(np.float64)[a + row_c], 1.0 / Nn, cols=cols, rows=rows)
+        ref = P.loss_host(z, target[t0:t1], m_c, old_c, adv_c, 1.0 / Nn, cols=cols, rows=rows)
+        # clip-edge tokens at the kernel's decision (old_at_kernel_clip)
+        old2, _ = old_at_kernel_clip(ws1["tok_flags"].cpu().numpy(), ref, old_c, adv_c)
+        if old2 is not None:
+            ref = P.loss_host(z, target[t0:t1], m_c, old2, adv_c, 1.0 / Nn, cols=cols, rows=rows)
     del z
+    gclip = ((ws1["tok_flags"].cpu().numpy() >> 1) & 1).astype(bool)
+    assert np.array_equal(gclip, ref["clipped"] & ref["valid"])
     for key in ("logp", "entropy"):
         got = to_f64(ws1[key])
         assert np.max(np.abs(got[m_c == 1] - ref[key][m_c == 1])) <= 1e-4, key

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import DEV, assert_tokens_match, make_chunk, rel_l2, to_f64
+from gpu_common import DEV, assert_tokens_match, make_chunk, oracle_lmhead_at_kernel_clip, rel_l2, to_f64
 from grpo_token_level_amd import ops
 from grpo_token_level_amd._capi import KL_K1, KL_K2, KL_K3, AGG_SEQ_MEAN_TOKEN_MEAN, AGG_SEQ_MEAN_TOKEN_SUM, \
     AGG_TOKEN_MEAN
@@ -274,9 +274,10 @@ def test_lmhead_terms_match_oracle(n, H, V):
     off = c["row_off"].tolist()
     w_tok = np.repeat(oracle.row_weights(c["mask"], off, AGG_SEQ_MEAN_TOKEN_MEAN, oracle.count_rows(c["mask"], off)),
                       np.diff(off))
-    ref = oracle.lmhead_fwd_bwd(c["h64"], c["W64"], c["target"], c["mask"], c["old"].astype(np.float64),
-                                c["adv"].astype(np.float64)[c["tok_row"]], 1.0, w_tok=w_tok, ent_coef=0.02,
-                                kl_coef=0.1, ref_logp=c["ref"].astype(np.float64), kl_type=KL_K3)
+    ref, _ = oracle_lmhead_at_kernel_clip(ws["tok_flags"].cpu().numpy(), c["h64"], c["W64"], c["target"],
+                                          c["mask"], c["old"], c["adv"].astype(np.float64)[c["tok_row"]], 1.0,
+                                          w_tok=w_tok, ent_coef=0.02, kl_coef=0.1,
+                                          ref_logp=c["ref"].astype(np.float64), kl_type=KL_K3)
     valid = ref["valid"]
     assert np.max(np.abs(to_f64(ws["logp"])[valid] - ref["logp"][valid])) <= 1e-4
     assert np.max(np.abs(to_f64(ws["kl_tok"])[valid] - ref["kl"][valid])) <= 2e-4

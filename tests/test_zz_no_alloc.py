@@ -15,8 +15,7 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
-from gpu_common import DEV, to_f64
+from gpu_common import DEV, oracle_lmhead_at_kernel_clip, to_f64
 from grpo_token_level_amd import ops
 from grpo_token_level_amd._capi import LMHEAD_NOALLOC_SCRATCH_BYTES
 
@@ -87,8 +86,8 @@ def test_noalloc_matches_the_workspace_entry_point_two_calls_in_a_row():
     # the smaller call against the oracle (as the workspace path is checked)
     h64, W64 = small["h_cpu"].double().numpy(), small["W_cpu"].double().numpy()
     N = int(small["mask"].sum())
-    ref = oracle.lmhead_fwd_bwd(h64, W64, small["target"], small["mask"], small["old"].astype(np.float64),
-                                small["adv"].astype(np.float64)[small["tok_row"]], 1.0 / N)
+    ref, _ = oracle_lmhead_at_kernel_clip(ws["tok_flags"].cpu().numpy(), h64, W64, small["target"], small["mask"],
+                                          small["old"], small["adv"].astype(np.float64)[small["tok_row"]], 1.0 / N)
     v = ref["valid"]
     assert np.max(np.abs(to_f64(ws["logp"])[v] - ref["logp"][v])) <= 1e-4
     bound = 2.0 ** -8 + 2.0 ** -12

@@ -94,6 +94,9 @@ def parse():
     ap.add_argument("--keep-z", action="store_true",
                     help="compact workload: the LM head keeps each chunk's fp32 logits for pass 2 "
                          "(GRPO_LMHEAD_KEEP_Z: one [tokens x V] matrix per chunk in place of the recompute)")
+    ap.add_argument("--defer-dw", action="store_true",
+                    help="compact workload: each chunk appends h^T and dz^T to a dW window and one GEMM per step "
+                         "adds the step's dW (GRPO_LMHEAD_DEFER_DW + grpo_lmhead_dw_flush)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     return ap.parse_args()
@@ -496,7 +499,7 @@ class DynamicStep(PaddedStep):
 # ---------------------------------------------------------------- compaction: fused LM head
 
 class CompactStep:
-    def __init__(self, wl, seed, torch, ops, timed, keep_z=False):
+    def __init__(self, wl, seed, torch, ops, timed, keep_z=False, defer_dw=False):
         from synth import compaction_batch
         self.torch, self.ops, self.timed = torch, ops, timed
         b = self.b = compaction_batch(seed=seed)
@@ -535,8 +538,12 @@ class CompactStep:
         self.chunks = [(a, min(a + b["micro"], plan["n_rows"])) for a in range(0, plan["n_rows"], b["micro"])]
         max_tok = int(max(self.off[e] - self.off[a] for a, e in self.chunks))
         self.keep_z = keep_z
-        self.workspace = torch.empty(ops.lmhead_workspace_bytes(max_tok, H, V, keep_z), dtype=torch.uint8,
+        self.defer_dw = defer_dw
+        self.workspace = torch.empty(ops.lmhead_workspace_bytes(max_tok, H, V, keep_z, defer_dw), dtype=torch.uint8,
                                      device="cuda")
+        # the dW window holds every chunk's columns (its tokens rounded up to 64)
+        self.window = (ops.LmheadDwWindow(sum(-(-int(self.off[e] - self.off[a]) // 64) * 64 for a, e in self.chunks),
+                                          H, V, device="cuda") if defer_dw else None)
         self.ws = ops.loss_workspace(max_tok, b["micro"], "cuda")
         self.tok_row = torch.empty(max_tok, dtype=torch.int32, device="cuda")
         self.row_off_dev = _g(torch, np.concatenate([self.off[a:e + 1] - self.off[a] for a, e in self.chunks]))
@@ -570,10 +577,15 @@ class CompactStep:
             ws["row_stats"] = self.ws["row_stats"][:e - a]
             ws["chunk_stats"] = self.stats_dev[k:k + 1]
             ops.lmhead_fwd_bwd(self.h[t0:t1], self.W, self.Wt, self.target[t0:t1], self.mask[t0:t1],
-                               self.old[t0:t1], tr, self.adv_dev[a:e], ro, self.dW, denom=self.N,
-                               dh=self.dh[t0:t1], ws=ws, workspace=self.workspace, keep_z=self.keep_z,
-                               on_launch=self.timed.mark)
-            self.timed.end_marked(6.0 * self.V * self.H * int(self.mask_np[t0:t1].sum()))
+                               self.old[t0:t1], tr, self.adv_dev[a:e], ro, None if self.defer_dw else self.dW,
+                               denom=self.N, dh=self.dh[t0:t1], ws=ws, workspace=self.workspace,
+                               keep_z=self.keep_z, dw_window=self.window, on_launch=self.timed.mark)
+            # logits, dh and (unless deferred) dW: 2VH each per valid token
+            self.timed.end_marked((4.0 if self.defer_dw else 6.0) * self.V * self.H
+                                  * int(self.mask_np[t0:t1].sum()))
+        if self.defer_dw:
+            self.window.flush(self.dW, on_launch=self.timed.mark)
+            self.timed.end_marked(2.0 * self.V * self.H * self.n_valid)
         self.stats_host.copy_(self.stats_dev, non_blocking=True)
         torch.cuda.current_stream().synchronize()
         acc = ops.Accumulator(len(self.chunks))
@@ -741,6 +753,11 @@ def main():
             print("--keep-z applies to the compact workload", file=sys.stderr)
             sys.exit(2)
         extra["keep_z"] = True
+    if args.defer_dw:
+        if cls is not CompactStep:
+            print("--defer-dw applies to the compact workload", file=sys.stderr)
+            sys.exit(2)
+        extra["defer_dw"] = True
     if args.vocab:
         if cls is not PaddedStep or args.vocab < 1:
             print("--vocab applies to the padded workloads (qwen, long, tiny) and must be positive", file=sys.stderr)
@@ -782,7 +799,8 @@ def main():
                        + ("; rows reshuffled every epoch (seeded)" if args.shuffle else "")
                        + (f"; replicated x{args.replicate} as one batch, one launch" if args.replicate != 1 else "")
                        + ("; device work replayed from a HIP graph" if args.graph else "")
-                       + (f"; vocabulary {args.vocab} in place of the workload's" if args.vocab else ""),
+                       + (f"; vocabulary {args.vocab} in place of the workload's" if args.vocab else "")
+                       + ("; dW of the step's chunks as one GEMM from a dW window" if args.defer_dw else ""),
            "logits_dtype": step.logits_dtype,
            "valid_tokens": step.n_valid, "launches_per_step": launches // args.steps,
            "step_loss": res[0]["loss"] if res and res[0] else None}
@@ -801,8 +819,10 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "kernel": "grpo_lmhead_fwd_bwd per 4-row chunk (bf16 MFMA GEMMs + epilogues"
-                          + ("; pass 2 from the kept fp32 logits)" if getattr(step, "keep_z", False) else
-                             "; pass 2 recomputes the logits)"),
+                          + ("; pass 2 from the kept fp32 logits" if getattr(step, "keep_z", False) else
+                             "; pass 2 recomputes the logits")
+                          + ("; dW deferred to one grpo_lmhead_dw_flush GEMM per step, counted as a launch)"
+                             if getattr(step, "defer_dw", False) else ")"),
                 "algorithmic_flops_per_launch": int(units // launches), "avg_launch_ms": round(tot_ms / launches, 4)}
     else:
         achieved = (units / launches) / (tot_ms / launches * 1e-3) / 1e9

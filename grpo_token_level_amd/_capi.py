@@ -79,7 +79,13 @@ class LmheadArgs(ctypes.Structure):
                 ("logp", _p), ("lse", _p), ("entropy", _p), ("loss_tok", _p), ("tok_flags", _p),
                 ("row_stats", _p), ("chunk_stats", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
                 ("row_weight", _p), ("ref_logp", _p), ("kl_tok", _p),
-                ("ent_coef", _f32), ("kl_coef", _f32), ("kl_type", _i32), ("reserved2", _i32)]
+                ("ent_coef", _f32), ("kl_coef", _f32), ("kl_type", _i32), ("reserved2", _i32),
+                ("dw_window", _p)]
+
+
+class DwWindow(ctypes.Structure):
+    _fields_ = [("buf", _p), ("bytes", ctypes.c_size_t), ("cap_tok", _i64), ("H", _i64), ("V", _i64),
+                ("reserved", _i64)]
 
 
 class TracePlan(ctypes.Structure):
@@ -109,6 +115,7 @@ class Probe(ctypes.Structure):
 
 
 LMHEAD_KEEP_Z = 1
+LMHEAD_DEFER_DW = 2
 LMHEAD_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 PROBE_STRICT_BOUND = 0.05
@@ -151,6 +158,10 @@ PROTOTYPES = {
     "grpo_lmhead_workspace_size_flags": (ctypes.c_size_t, [_i64, _i64, _i64, _i32]),
     "grpo_lmhead_fwd_bwd": (ctypes.c_int, [_p, ctypes.POINTER(LmheadArgs)]),
     "grpo_lmhead_fwd_bwd_noalloc": (ctypes.c_int, [_p, ctypes.POINTER(LmheadArgs)]),
+    "grpo_lmhead_dw_window_size": (ctypes.c_size_t, [_i64, _i64, _i64]),
+    "grpo_lmhead_dw_window_init": (ctypes.c_int, [_p, ctypes.POINTER(DwWindow), _p, ctypes.c_size_t, _i64, _i64,
+                                                  _i64]),
+    "grpo_lmhead_dw_flush": (ctypes.c_int, [_p, ctypes.POINTER(DwWindow), _p]),
     "grpo_needs_ahead_pass": (ctypes.c_int32, [_i64, _i32, _i32]),
     "grpo_old_cache_init": (ctypes.c_int, [ctypes.POINTER(OldCache), _p, _i64, _P64, _i64]),
     "grpo_old_cache_reset": (ctypes.c_int, [ctypes.POINTER(OldCache)]),

@@ -98,6 +98,44 @@ __device__ __attribute__((aligned(64))) uint16_t g_zero_page[32];
 
 enum { EPI_STATS = 0, EPI_DZ = 1, EPI_ACC = 2 };
 
+// Measured rates behind the pass-2 cost model: a 256 x 256 x 64 block step
+// takes ~2 us at ~1 PFLOP/s; HBM moves ~5 bytes per ns.
+constexpr float kKstepUs = 2.0f, kHbmBytesPerUs = 5.0e6f;
+
+// The dh GEMM's split-K count, chosen on the device from the chunk's valid
+// rows (the host plan counts every token, pads included, and a mostly padded
+// chunk would leave most compute units idle): the count s <= cap minimising
+// rounds(tiles(rows) * s blocks on cus compute units) x the k-steps of the
+// widest vocabulary chunk split s ways, over the call's chunks, plus the HBM
+// time of the s fp32 partials.  The same for every chunk of a call, and
+// recomputed identically by the sum of the partials.
+struct SplitRule {
+    int cap;       // 0: off (GemmArgs ksplit / kper hold)
+    int kref;      // width of the widest vocabulary chunk
+    int chunks;    // vocabulary chunks in the call
+    int cus;       // compute units
+    int tiles_n;   // tiles along H
+    int cols;      // H
+};
+
+__device__ __forceinline__ int dev_split_count(const SplitRule& r, int rows) {
+    const int tiles = (rows + BM - 1) / BM * r.tiles_n;
+    int best = 1;
+    float best_cost = -1.0f;
+    for (int sp = 1; sp <= r.cap; ++sp) {
+        const float rounds = (float)((tiles * sp + r.cus - 1) / r.cus);
+        const float ks = (float)(((r.kref + sp - 1) / sp + BK - 1) / BK);
+        const float partials = 2.0f * (float)r.chunks * (float)sp * (float)rows * (float)r.cols * 4.0f;
+        const float cost = rounds * ks * (float)r.chunks + partials / (kHbmBytesPerUs * kKstepUs);
+        // a split must save at least 1 % to be worth its partial
+        if (best_cost < 0.0f || cost * 100.0f < best_cost * 99.0f) {
+            best_cost = cost;
+            best = sp;
+        }
+    }
+    return best;
+}
+
 struct GemmArgs {
     const uint16_t* A;   // row m at A + m*lda (A + a_rows[m]*lda with a row map), K contiguous
     int64_t lda;
@@ -114,6 +152,8 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int ksplit, kper;    // K range of split s: [s*kper, min(K, (s+1)*kper)), kper % BK == 0
     int n_fast;          // tile order: N index fastest (else M fastest)
+    SplitRule split;     // cap > 0: tiles from the device row count, split count by the rule (ksplit sizes
+                         // the grid: at least the rule's cap)
     // EPI_STATS
     float4* part;        // part[m * n_parts + n/64] = {max, sum e, sum e*t, 0}
     int n_parts;
@@ -132,8 +172,9 @@ struct GemmArgs {
                          // with m_dev, m_out = *m_dev rounded up to kTokPad
     uint16_t* dz;        // dz[m * ld_dz + n]
     int64_t ld_dz;
-    uint16_t* dzT;       // dzT[n * ld_dzT + m]
+    uint16_t* dzT;       // dzT[n * ld_dzT + koff + m]
     int64_t ld_dzT;
+    const int32_t* dzT_off;   // NULL (koff = 0), or the device column offset koff (a dW window's fill)
     // EPI_ACC
     float* C;            // split s: (C + s*c_split)[m * ldc + n] = (beta ? that : 0) + acc
     int64_t ldc;
@@ -180,19 +221,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
-    const int nt = g.tiles_m * g.tiles_n;
-    const int logical = xcd_logical(blockIdx.x, nt * g.ksplit);
-    const int tile = logical % nt, split = logical / nt;
-    const int tm = g.n_fast ? tile / g.tiles_n : tile % g.tiles_m;
-    const int tn = g.n_fast ? tile % g.tiles_n : tile / g.tiles_m;
-    const int m0 = tm * BM, n0 = tn * BN;
     const int M = g.m_dev ? min(g.M, *g.m_dev) : g.M;
+    int tiles_m = g.tiles_m, ksplit = g.ksplit, kper = g.kper, n_fast = g.n_fast;
+    if (g.split.cap > 0) {
+        // only the valid rows' tiles, split by the rule; the active blocks are
+        // the grid's first, spread over the XCDs like a grid of their own
+        tiles_m = (M + BM - 1) / BM;
+        ksplit = dev_split_count(g.split, M);
+        kper = ((g.K + ksplit - 1) / ksplit + BK - 1) / BK * BK;
+        n_fast = g.tiles_n < tiles_m;
+    }
+    const int nt = tiles_m * g.tiles_n;
+    if ((int)blockIdx.x >= nt * ksplit) return;   // block-uniform (never without the rule)
+    const int logical = xcd_logical(blockIdx.x, nt * ksplit);
+    const int tile = logical % nt, split = logical / nt;
+    const int tm = n_fast ? tile / g.tiles_n : tile % tiles_m;
+    const int tn = n_fast ? tile % g.tiles_n : tile / tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
     const int m_out = g.m_dev ? min(g.m_out, (M + kTokPad - 1) / kTokPad * kTokPad) : g.m_out;
     const int K = g.k_dev ? min(g.K, (*g.k_dev + kTokPad - 1) / kTokPad * kTokPad) : g.K;
     // tiles past the valid rows; an accumulation with an empty K range leaves C as it is
     if (m0 >= (EPI == EPI_DZ ? m_out : M)) return;
-    const int kbeg = split * g.kper;
-    const int kend = min(K, kbeg + g.kper);
+    const int kbeg = split * kper;
+    const int kend = min(K, kbeg + kper);
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
     if (EPI == EPI_ACC && nk == 0 && g.beta) return;
 
@@ -402,6 +453,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
         // each dz^T row segment of the wave (its 64 tokens, 128 bytes) by 8
         // lanes with 16-byte stores; the wave reads only what it wrote
         const int mg = m0 + wm * WM;
+        const int64_t koff = g.dzT_off ? *g.dzT_off : 0;
 #pragma unroll
         for (int it = 0; it < WN / 8; ++it) {
             const int nloc = it * 8 + (lane >> 3), c = lane & 7;
@@ -411,7 +463,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
                 const char* src = tcol + nloc * DZT_ROWB + c * 16;
                 const uint2 lo = *reinterpret_cast<const uint2*>(src);
                 const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
-                *reinterpret_cast<uint4*>(g.dzT + (int64_t)nl * g.ld_dzT + m) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                *reinterpret_cast<uint4*>(g.dzT + (int64_t)nl * g.ld_dzT + koff + m) =
+                    make_uint4(lo.x, lo.y, hi.x, hi.y);
             }
         }
         // then the same buffer as [token][column]: 2-byte writes of the kept
@@ -544,8 +597,9 @@ struct DzArgs {
     int bonus;
     uint16_t* dz;          // dz[m * ld_dz + c]
     int64_t ld_dz;
-    uint16_t* dzT;         // dzT[c * ld_dzT + m]
+    uint16_t* dzT;         // dzT[c * ld_dzT + koff + m]
     int64_t ld_dzT;
+    const int32_t* dzT_off;   // NULL (koff = 0), or the device column offset koff (a dW window's fill)
 };
 
 __global__ __launch_bounds__(256) void dz_from_z_kernel(const DzArgs a) {
@@ -603,24 +657,28 @@ __global__ __launch_bounds__(256) void dz_from_z_kernel(const DzArgs a) {
     }
     __syncthreads();
     // dz^T: 128 columns x 8 chunks of 16 bytes (8 tokens each)
+    const int64_t koff = a.dzT_off ? *a.dzT_off : 0;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int piece = it * 256 + tid, cl = piece >> 3, ch = piece & 7;
         const int cc = n0 + cl;
         if (cc < a.vc)
-            *reinterpret_cast<uint4*>(a.dzT + (int64_t)cc * a.ld_dzT + m0 + ch * 8) =
+            *reinterpret_cast<uint4*>(a.dzT + (int64_t)cc * a.ld_dzT + koff + m0 + ch * 8) =
                 *reinterpret_cast<const uint4*>(s_t + cl * TROW + ch * 16);
     }
 }
 
 // dh row t (H floats) = sum over s, in order, of the partials of t's compact
-// row inv[t]; a masked token (inv[t] < 0) gets a zero row.  Block (x, y):
-// columns [256x, 256x + 256) of tokens y, y + gridDim.y, ...
+// row inv[t]; a masked token (inv[t] < 0) gets a zero row.  The split count:
+// nsplit, or the dh GEMM's rule at the valid-token count (rule.cap > 0).
+// Block (x, y): columns [256x, 256x + 256) of tokens y, y + gridDim.y, ...
 __global__ __launch_bounds__(256) void sum_splits_kernel(float* __restrict__ dst, int64_t ld_dst,
                                                          const float* __restrict__ parts, int nsplit, int64_t c_split,
-                                                         const int32_t* __restrict__ inv, int64_t n, int64_t H) {
+                                                         const int32_t* __restrict__ inv, int64_t n, int64_t H,
+                                                         const int32_t* __restrict__ count, const SplitRule rule) {
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (c >= H) return;
+    if (rule.cap > 0) nsplit = dev_split_count(rule, *count);
     for (int64_t t = blockIdx.y; t < n; t += gridDim.y) {
         const int32_t j = inv[t];
         float s = 0.0f;
@@ -790,19 +848,28 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const MergeArgs a) {
     a.tok_flags[t] = (uint8_t)(1u | (sg.clipped ? 2u : 0u) | (sg.bad ? 4u : 0u));
 }
 
-// dst[c * ld_dst + r] = src[row(r) * ld_src + c] for r < rows, c < cols, with
-// row(r) = rmap ? rmap[r] : r and rows = min(rows, *rcount) when rcount is
-// set; columns [rows, rows_pad) of dst are written as zeros.  64x64 tiles
-// through LDS.
+// dst[c * ld_dst + off + r] = src[row(r) * ld_src + c] for r < rows, c < cols,
+// with row(r) = rmap ? rmap[r] : r and rows = min(rows, *rcount) when rcount
+// is set; columns [rows, rows_pad) of dst are written as zeros.  With dst_off
+// (a dW window's device fill), off = *dst_off and rows_pad is cut to rows
+// rounded up to 64, so that the window's next call starts there.  64x64
+// tiles through LDS.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t rows,
                                                              int64_t cols, int64_t ld_src, uint16_t* __restrict__ dst,
                                                              int64_t ld_dst, int64_t rows_pad,
                                                              const int32_t* __restrict__ rmap,
-                                                             const int32_t* __restrict__ rcount) {
+                                                             const int32_t* __restrict__ rcount,
+                                                             const int32_t* __restrict__ dst_off) {
     __shared__ uint16_t tile[64][66];
     const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     if (rcount && *rcount < rows) rows = *rcount;
+    if (dst_off) {
+        dst += *dst_off;
+        const int64_t rp = (rows + 63) / 64 * 64;
+        if (rp < rows_pad) rows_pad = rp;
+    }
+    if (r0 >= rows_pad) return;   // block-uniform
     for (int k = ty; k < 64; k += 4) {
         const int64_t r = r0 + k, c = c0 + tx;
         tile[k][tx] = (r < rows && c < cols) ? src[(rmap ? (int64_t)rmap[r] : r) * ld_src + c] : (uint16_t)0;
@@ -814,7 +881,45 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
     }
 }
 
+// A dW window's fill counter: advanced by the chunk's valid tokens rounded up
+// to 64 (count non-NULL), or cleared (count NULL).  Runs after every kernel
+// of the chunk that reads the counter.
+__global__ void dw_fill_kernel(int32_t* fill, const int32_t* count) {
+    if (threadIdx.x == 0) *fill = count ? *fill + (*count + kTokPad - 1) / kTokPad * kTokPad : 0;
+}
+
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// A dW window's buffer: the fill counter (columns written so far, a multiple
+// of 64), h^T [H x cap] and dz^T [V x cap], cap = cap_tok rounded up to 64.
+struct WindowLayout {
+    int32_t* fill;
+    uint16_t* hT;
+    uint16_t* dzT;
+    int64_t cap;
+    size_t bytes;
+};
+
+WindowLayout window_layout(void* buf, int64_t cap_tok, int64_t H, int64_t V) {
+    WindowLayout l{};
+    l.cap = round_up(cap_tok, kTokPad);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = (size_t)round_up((int64_t)(off + bytes), 256);
+        return reinterpret_cast<char*>(buf) + at;
+    };
+    l.fill = reinterpret_cast<int32_t*>(take(4));
+    l.hT = reinterpret_cast<uint16_t*>(take((size_t)H * l.cap * 2));
+    l.dzT = reinterpret_cast<uint16_t*>(take((size_t)V * l.cap * 2));
+    l.bytes = off;
+    return l;
+}
+
+bool window_sizes_ok(int64_t cap_tok, int64_t H, int64_t V) {
+    return cap_tok >= 1 && cap_tok <= (1LL << 30) && H > 0 && V > 0 && H % 8 == 0 && V % 8 == 0 && V <= (1 << 30) &&
+           H <= (1 << 20);
+}
 
 struct Workspace {
     float4* part;
@@ -857,8 +962,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // chunk_cap (a multiple of BN) and split_cap bound the plan to a smaller
 // workspace (the no-allocation entry point's fixed scratch).
 Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus, int64_t chunk_cap = kVocabChunkMax,
-                     int split_cap = kDhSplitMax, bool stash = false) {
-    constexpr double kKstepUs = 2.0, kHbmBytesPerUs = 5.0e6;
+                     int split_cap = kDhSplitMax, bool stash = false, bool defer = false) {
     const int64_t n_pad = round_up(n, kTokPad);
     const int64_t tm = cdiv(n, BM), th = cdiv(H, BN);
     const int64_t wcap = chunk_cap;
@@ -872,7 +976,7 @@ Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus, int64_t chunk
             for (int64_t c0 = 0; c0 < V; c0 += w) {
                 const int64_t vc = V - c0 < w ? V - c0 : w, tv = cdiv(vc, BN);
                 if (!stash) steps += cdiv(tm * tv, cus) * cdiv(H, BK);                  // dz (recomputed)
-                steps += cdiv(tv * th, cus) * cdiv(n_pad, BK);                          // dW
+                if (!defer) steps += cdiv(tv * th, cus) * cdiv(n_pad, BK);              // dW
                 steps += cdiv(tm * th * sp, cus) * (round_up(cdiv(vc, sp), BK) / BK);   // dh
                 ++chunks;
             }
@@ -889,7 +993,7 @@ Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus, int64_t chunk
 }
 
 Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V, int64_t chunk_cap = kVocabChunkMax,
-                int split_cap = kDhSplitMax, bool stash = false) {
+                int split_cap = kDhSplitMax, bool stash = false, bool defer = false) {
     const int64_t n_parts = (V + 63) / 64;
     const int64_t n_pad = round_up(n_tok > 0 ? n_tok : 1, kTokPad);
     const int64_t vc = V < chunk_cap ? V : chunk_cap;   // widest chunk any plan within the caps uses
@@ -906,10 +1010,11 @@ Workspace carve(void* base, int64_t n_tok, int64_t H, int64_t V, int64_t chunk_c
     w.coef = reinterpret_cast<float*>(take((size_t)n_tok * 4));
     w.ea = reinterpret_cast<float*>(take((size_t)n_tok * 4));
     w.eb = reinterpret_cast<float*>(take((size_t)n_tok * 4));
-    w.hT = reinterpret_cast<uint16_t*>(take((size_t)H * n_pad * 2));
+    // with a dW window, h^T and dz^T go there
+    w.hT = defer ? nullptr : reinterpret_cast<uint16_t*>(take((size_t)H * n_pad * 2));
     w.z = stash ? reinterpret_cast<float*>(take((size_t)n_tok * V * 4)) : nullptr;
     w.dz = reinterpret_cast<uint16_t*>(take((size_t)n_tok * vc * 2));
-    w.dzT = reinterpret_cast<uint16_t*>(take((size_t)vc * n_pad * 2));
+    w.dzT = defer ? nullptr : reinterpret_cast<uint16_t*>(take((size_t)vc * n_pad * 2));
     w.dh_part = reinterpret_cast<float*>(take((size_t)split_cap * n_tok * H * 4));
     w.vidx = reinterpret_cast<int32_t*>(take((size_t)n_tok * 4));
     w.inv = reinterpret_cast<int32_t*>(take((size_t)n_tok * 4));
@@ -953,9 +1058,67 @@ int64_t stash_chunk_cap(int64_t V) { return round_up(V, BN); }
 }  // namespace
 
 extern "C" size_t grpo_lmhead_workspace_size_flags(int64_t n_tok, int64_t H, int64_t V, int32_t flags) {
-    if (n_tok < 0 || H <= 0 || V <= 0 || (flags & ~GRPO_LMHEAD_KEEP_Z)) return 0;
-    if (flags & GRPO_LMHEAD_KEEP_Z) return carve(nullptr, n_tok, H, V, stash_chunk_cap(V), kDhSplitMax, true).bytes;
-    return carve(nullptr, n_tok, H, V).bytes;
+    if (n_tok < 0 || H <= 0 || V <= 0 || (flags & ~(GRPO_LMHEAD_KEEP_Z | GRPO_LMHEAD_DEFER_DW))) return 0;
+    const bool stash = (flags & GRPO_LMHEAD_KEEP_Z) != 0, defer = (flags & GRPO_LMHEAD_DEFER_DW) != 0;
+    return carve(nullptr, n_tok, H, V, stash ? stash_chunk_cap(V) : kVocabChunkMax, kDhSplitMax, stash, defer).bytes;
+}
+
+namespace {
+
+// A window as set up by grpo_lmhead_dw_window_init and kept by the calls.
+int check_window(const char* who, const grpo_lmhead_dw_window* w) {
+    if (!w || !w->buf || (reinterpret_cast<uintptr_t>(w->buf) & 255u) || !window_sizes_ok(w->cap_tok, w->H, w->V))
+        return fail(GRPO_EINVAL, "%s: dW window missing or not set up (grpo_lmhead_dw_window_init)", who);
+    const WindowLayout l = window_layout(nullptr, w->cap_tok, w->H, w->V);
+    if (w->bytes < l.bytes || w->reserved < 0 || w->reserved > l.cap || w->reserved % kTokPad)
+        return fail(GRPO_EINVAL, "%s: dW window fields changed since grpo_lmhead_dw_window_init", who);
+    return GRPO_OK;
+}
+
+}  // namespace
+
+extern "C" size_t grpo_lmhead_dw_window_size(int64_t cap_tok, int64_t H, int64_t V) {
+    return window_sizes_ok(cap_tok, H, V) ? window_layout(nullptr, cap_tok, H, V).bytes : 0;
+}
+
+extern "C" int grpo_lmhead_dw_window_init(void* stream, grpo_lmhead_dw_window* w, void* buf, size_t bytes,
+                                          int64_t cap_tok, int64_t H, int64_t V) {
+    if (!w || !buf || (reinterpret_cast<uintptr_t>(buf) & 255u) || !window_sizes_ok(cap_tok, H, V))
+        return fail(GRPO_EINVAL, "grpo_lmhead_dw_window_init: need w, a 256-byte aligned buf, 1 <= cap_tok <= 2^30, "
+                    "H and V positive multiples of 8");
+    const WindowLayout l = window_layout(buf, cap_tok, H, V);
+    if (bytes < l.bytes)
+        return fail(GRPO_ECAPACITY, "grpo_lmhead_dw_window_init: %zu bytes needed for %lld tokens", l.bytes,
+                    (long long)cap_tok);
+    hipLaunchKernelGGL(dw_fill_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, l.fill, nullptr);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(GRPO_EDEVICE, "grpo_lmhead_dw_window_init: %s", hipGetErrorString(e));
+    *w = grpo_lmhead_dw_window{buf, bytes, cap_tok, H, V, 0};
+    return ok();
+}
+
+extern "C" int grpo_lmhead_dw_flush(void* stream, grpo_lmhead_dw_window* w, float* dW) {
+    int rc = check_window("grpo_lmhead_dw_flush", w);
+    if (rc != GRPO_OK) return rc;
+    if (!dW || !al16(dW)) return fail(GRPO_EINVAL, "grpo_lmhead_dw_flush: dW is required (16-byte aligned)");
+    if (w->reserved == 0) return ok();
+    const WindowLayout l = window_layout(w->buf, w->cap_tok, w->H, w->V);
+    hipStream_t st = (hipStream_t)stream;
+    // dW += dz^T h over the window's columns: K bounded by the reserved
+    // columns on the host, by the fill counter (the valid tokens) in the kernel
+    GemmArgs gw{};
+    gw.A = l.dzT; gw.lda = l.cap; gw.B = l.hT; gw.ldb = l.cap;
+    gw.M = (int)w->V; gw.N = (int)w->H; gw.K = (int)w->reserved;
+    gw.k_dev = l.fill;
+    gw.C = dW; gw.ldc = w->H; gw.beta = 1;
+    hipError_t e = launch_gemm<EPI_ACC>(gw, st);
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(dw_fill_kernel, dim3(1), dim3(64), 0, st, l.fill, nullptr);
+        e = hipGetLastError();
+    }
+    if (e != hipSuccess) return fail(GRPO_EDEVICE, "grpo_lmhead_dw_flush: %s", hipGetErrorString(e));
+    w->reserved = 0;
+    return ok();
 }
 
 extern "C" size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V) {
@@ -971,7 +1134,7 @@ extern "C" int grpo_transpose_bf16(void* stream, const void* src, int64_t rows, 
         return fail(GRPO_EINVAL, "grpo_transpose_bf16: too many rows for one launch");
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64)),
                        dim3(256), 0, (hipStream_t)stream, (const uint16_t*)src, rows, cols, ld_src, (uint16_t*)dst,
-                       ld_dst, rows, nullptr, nullptr);
+                       ld_dst, rows, nullptr, nullptr, nullptr);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? ok() : fail(GRPO_EDEVICE, "grpo_transpose_bf16: %s", hipGetErrorString(e));
 }
@@ -1065,8 +1228,9 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
     if (n > kMaxTokens || V > (1 << 30) || H > (1 << 20))
         return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: n_tok above %lld or sizes beyond the kernels' 32-bit tile "
                     "indexing", (long long)kMaxTokens);
-    if (!a->W || !a->Wt || !a->dW || !al16(a->W) || !al16(a->Wt) || !al16(a->dW))
-        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: W, Wt and dW are required (16-byte aligned)");
+    const bool defer = (a->flags & GRPO_LMHEAD_DEFER_DW) != 0;
+    if (!a->W || !a->Wt || (!defer && !a->dW) || !al16(a->W) || !al16(a->Wt) || !al16(a->dW))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: W, Wt and dW (unless deferred) are required (16-byte aligned)");
     if (!a->chunk_stats || (a->n_rows > 0 && (!a->row_stats || !a->row_off)))
         return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: NULL stats pointer");
     if (n > 0 && (!a->h || !al16(a->h) || !a->target || !a->mask || !a->old_logp || !a->tok_row || !a->adv_row ||
@@ -1080,11 +1244,29 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
                                          a->kl_type);
         if (rc != GRPO_OK) return rc;
     }
-    if (a->flags & ~GRPO_LMHEAD_KEEP_Z) return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: unknown flags %d", a->flags);
+    if (a->flags & ~(GRPO_LMHEAD_KEEP_Z | GRPO_LMHEAD_DEFER_DW))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: unknown flags %d", a->flags);
     const bool stash = (a->flags & GRPO_LMHEAD_KEEP_Z) != 0;
     if (stash && noalloc)
         return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd_noalloc: GRPO_LMHEAD_KEEP_Z needs a caller workspace (the "
                     "chunk's logits do not fit the fixed scratch)");
+    if (defer && noalloc)
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd_noalloc: GRPO_LMHEAD_DEFER_DW belongs to the workspace path");
+    grpo_lmhead_dw_window* win = a->dw_window;
+    if (defer != (win != nullptr))
+        return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: GRPO_LMHEAD_DEFER_DW and dw_window go together");
+    const int64_t reserve = defer ? round_up(n, kTokPad) : 0;
+    if (defer) {
+        const int rc = check_window("grpo_lmhead_fwd_bwd", win);
+        if (rc != GRPO_OK) return rc;
+        if (win->H != H || win->V != V)
+            return fail(GRPO_EINVAL, "grpo_lmhead_fwd_bwd: the dW window is for H %lld, V %lld", (long long)win->H,
+                        (long long)win->V);
+        if (win->reserved + reserve > round_up(win->cap_tok, kTokPad))
+            return fail(GRPO_ECAPACITY, "grpo_lmhead_fwd_bwd: the dW window has %lld of %lld columns reserved and "
+                        "this chunk needs %lld more; flush it first", (long long)win->reserved,
+                        (long long)round_up(win->cap_tok, kTokPad), (long long)reserve);
+    }
     int dev = 0, cus = 0;
     hipError_t e;
     if ((e = hipGetDevice(&dev)) != hipSuccess ||
@@ -1110,14 +1292,20 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
         if (!a->workspace || a->workspace_bytes < need || !al16(a->workspace))
             return fail(GRPO_ECAPACITY, "grpo_lmhead_fwd_bwd: workspace of %zu bytes needed (16-byte aligned)", need);
         if (stash) chunk_cap = stash_chunk_cap(V);
-        plan = plan_pass2(n, H, V, cus, chunk_cap, split_cap, stash);
+        plan = plan_pass2(n, H, V, cus, chunk_cap, split_cap, stash, defer);
     }
     hipStream_t st = (hipStream_t)stream;
     const grpo::ObjTerms obj{a->scale, a->denom, a->row_weight, a->ent_coef, a->ref_logp ? a->kl_coef : 0.0f};
     float* kl_tok = a->ref_logp ? a->kl_tok : nullptr;
     if (n == 0) return grpo::launch_stats(stream, a->loss_tok, a->entropy, kl_tok, a->tok_flags, a->row_off,
                                           a->n_rows, 0, obj, a->row_stats, a->chunk_stats);
-    const Workspace w = carve(wsp, n, H, V, chunk_cap, split_cap, stash);
+    const Workspace w = carve(wsp, n, H, V, chunk_cap, split_cap, stash, defer);
+    // with a dW window, h^T and dz^T of the valid tokens are appended to it at
+    // its fill counter; else they live in the workspace
+    const WindowLayout wl = defer ? window_layout(win->buf, win->cap_tok, H, V) : WindowLayout{};
+    uint16_t* const hT = defer ? wl.hT : w.hT;
+    const int64_t ld_T = defer ? wl.cap : round_up(n, kTokPad);
+    const int32_t* const fill = defer ? wl.fill : nullptr;
     const int64_t n_pad = round_up(n, kTokPad);
     const int n_parts = (int)((V + 63) / 64);
     const uint16_t* h = (const uint16_t*)a->h;
@@ -1133,7 +1321,7 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
 
     // h^T of the valid tokens, zero columns up to n_pad (the K operand of dW's GEMM)
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((H + 63) / 64), (unsigned)((n_pad + 63) / 64)),
-                       dim3(256), 0, st, h, n, H, a->ldh, w.hT, n_pad, n_pad, w.vidx, w.count);
+                       dim3(256), 0, st, h, n, H, a->ldh, hT, ld_T, n_pad, w.vidx, w.count, fill);
     if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "transpose h");
 
     // pass 1: slice partials of the log-softmax and the target logit
@@ -1163,6 +1351,8 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
     // pass 2: per vocabulary chunk, dz then dh (+)= dz W_c and dW_c += dz^T h
     const int64_t chunk = plan.chunk;
     const int nsplit = plan.nsplit;
+    // dh's split count follows the valid rows, on the device (SplitRule)
+    const SplitRule rule{split_cap, (int)chunk, (int)cdiv(V, chunk), cus, (int)cdiv(H, BN), (int)H};
     for (int64_t c0 = 0; c0 < V; c0 += chunk) {
         const int vc = (int)(V - c0 < chunk ? V - c0 : chunk);
         if (stash) {
@@ -1170,7 +1360,8 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
             d.z = w.z; d.ld_z = V; d.col0 = (int)c0; d.vc = vc;
             d.count = w.count; d.vidx = w.vidx; d.target = a->target;
             d.c2 = w.c2; d.coef = w.coef; d.ea = w.ea; d.eb = w.eb; d.bonus = a->ent_coef != 0.0f;
-            d.dz = w.dz; d.ld_dz = vc; d.dzT = w.dzT; d.ld_dzT = n_pad;
+            d.dz = w.dz; d.ld_dz = vc; d.dzT = defer ? wl.dzT + c0 * wl.cap : w.dzT; d.ld_dzT = ld_T;
+            d.dzT_off = fill;
             hipLaunchKernelGGL(dz_from_z_kernel, dim3((unsigned)((vc + 127) / 128), (unsigned)(n_pad / 64)),
                                dim3(256), 0, st, d);
             if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "dz");
@@ -1181,7 +1372,8 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
             d.a_rows = w.vidx; d.m_dev = w.count;
             d.c2 = w.c2; d.coef = w.coef; d.target = a->target; d.col0 = (int)c0; d.m_out = (int)n_pad;
             d.ea = w.ea; d.eb = w.eb; d.bonus = a->ent_coef != 0.0f;
-            d.dz = w.dz; d.ld_dz = vc; d.dzT = w.dzT; d.ld_dzT = n_pad;
+            d.dz = w.dz; d.ld_dz = vc; d.dzT = defer ? wl.dzT + c0 * wl.cap : w.dzT; d.ld_dzT = ld_T;
+            d.dzT_off = fill;
             if ((e = launch_gemm<EPI_DZ>(d, st)) != hipSuccess) return dev_fail(e, "dz");
         }
 
@@ -1191,20 +1383,30 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
         gh.A = w.dz; gh.lda = vc; gh.B = Wt + c0; gh.ldb = V;
         gh.M = (int)n; gh.N = (int)H; gh.K = vc;
         gh.m_dev = w.count;
-        gh.ksplit = nsplit;
-        gh.kper = (int)round_up((vc + nsplit - 1) / nsplit, BK);
+        gh.split = rule;
+        gh.ksplit = rule.cap;
+        gh.kper = (int)round_up(vc, BK);
         gh.C = w.dh_part; gh.ldc = H; gh.c_split = n * H; gh.beta = c0 > 0;
         if ((e = launch_gemm<EPI_ACC>(gh, st)) != hipSuccess) return dev_fail(e, "dh");
 
-        GemmArgs gw{};
-        gw.A = w.dzT; gw.lda = n_pad; gw.B = w.hT; gw.ldb = n_pad;
-        gw.M = vc; gw.N = (int)H; gw.K = (int)n_pad;
-        gw.k_dev = w.count;
-        gw.C = a->dW + c0 * H; gw.ldc = H; gw.beta = 1;
-        if ((e = launch_gemm<EPI_ACC>(gw, st)) != hipSuccess) return dev_fail(e, "dW");
+        if (!defer) {
+            GemmArgs gw{};
+            gw.A = w.dzT; gw.lda = n_pad; gw.B = w.hT; gw.ldb = n_pad;
+            gw.M = vc; gw.N = (int)H; gw.K = (int)n_pad;
+            gw.k_dev = w.count;
+            gw.C = a->dW + c0 * H; gw.ldc = H; gw.beta = 1;
+            if ((e = launch_gemm<EPI_ACC>(gw, st)) != hipSuccess) return dev_fail(e, "dW");
+        }
+    }
+    if (defer) {
+        // the window's next chunk starts after this one's valid tokens
+        hipLaunchKernelGGL(dw_fill_kernel, dim3(1), dim3(64), 0, st, wl.fill, w.count);
+        if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "dW window");
+        // the host bound moves with the counter (the counter never passes it)
+        win->reserved += reserve;
     }
     hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((H + 255) / 256), (unsigned)(n < 65535 ? n : 65535)),
-                       dim3(256), 0, st, a->dh, H, w.dh_part, nsplit, n * H, w.inv, n, H);
+                       dim3(256), 0, st, a->dh, H, w.dh_part, nsplit, n * H, w.inv, n, H, w.count, rule);
     if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "dh splits");
     return ok();
 }

@@ -628,16 +628,52 @@ def transpose_bf16(x, out=None):
     return out
 
 
-def lmhead_workspace_bytes(n_tok, H, V, keep_z=False):
-    if keep_z:
-        return int(C.lib().grpo_lmhead_workspace_size_flags(n_tok, H, V, C.LMHEAD_KEEP_Z))
+def lmhead_workspace_bytes(n_tok, H, V, keep_z=False, defer_dw=False):
+    flags = (C.LMHEAD_KEEP_Z if keep_z else 0) | (C.LMHEAD_DEFER_DW if defer_dw else 0)
+    if flags:
+        return int(C.lib().grpo_lmhead_workspace_size_flags(n_tok, H, V, flags))
     return int(C.lib().grpo_lmhead_workspace_size(n_tok, H, V))
+
+
+def lmhead_dw_window_bytes(cap_tok, H, V):
+    return int(C.lib().grpo_lmhead_dw_window_size(cap_tok, H, V))
+
+
+class LmheadDwWindow:
+    """grpo_lmhead_dw_window: h^T and dz^T of several LM-head chunks, so that
+    dW takes one GEMM per flush instead of one per chunk.  ``buf``: a
+    contiguous uint8 GPU tensor of at least lmhead_dw_window_bytes bytes
+    (allocated here when None)."""
+
+    def __init__(self, cap_tok, H, V, device=None, buf=None):
+        torch = _torch()
+        if buf is None:
+            buf = torch.empty(max(lmhead_dw_window_bytes(cap_tok, H, V), 1), dtype=torch.uint8, device=device)
+        if buf.dtype != torch.uint8 or not buf.is_cuda or not buf.is_contiguous():
+            raise ValueError("buf must be a contiguous uint8 GPU tensor")
+        self.buf = buf
+        self.w = C.DwWindow()
+        C.check(C.lib().grpo_lmhead_dw_window_init(_stream(), ctypes.byref(self.w), ctypes.c_void_p(buf.data_ptr()),
+                                                   buf.numel(), cap_tok, H, V))
+
+    def flush(self, dW, on_launch=None):
+        """dW (fp32 [V x H]) += the window's dz^T h; empties the window."""
+        _matrix(dW, "dW", self.w.V, self.w.H, ("float32",), dense=True)
+        if dW.shape[0] != self.w.V:
+            raise ValueError(f"dW must be [{self.w.V} x {self.w.H}]")
+        if on_launch is not None:
+            on_launch()
+        C.check(C.lib().grpo_lmhead_dw_flush(_stream(), ctypes.byref(self.w), ctypes.c_void_p(dW.data_ptr())))
+
+    @property
+    def reserved(self):
+        return self.w.reserved
 
 
 def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off, dW, *, scale=1.0, denom=None,
                    eps_low=0.2, eps_high=0.2, dh=None, ws=None, workspace=None, row_weight=None,
                    ref_logp=None, ent_coef=0.0, kl_coef=0.0, kl_type=C.KL_K3, noalloc=False, keep_z=False,
-                   on_launch=None):
+                   dw_window=None, on_launch=None):
     """Fused LM-head GRPO loss over one chunk (grpo_lmhead_fwd_bwd).
 
     ``dW`` (fp32 [V x H]) is accumulated into; ``dh`` (fp32 [n_tok x H]) is
@@ -647,7 +683,9 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
     fixed scratch (no workspace is passed; the caller still provides every
     input and output).  ``keep_z``: GRPO_LMHEAD_KEEP_Z (pass 1 keeps the
     chunk's fp32 logits in the workspace and pass 2 reads them back instead
-    of recomputing them).  ``on_launch``: as in loss_fwd_bwd."""
+    of recomputing them).  ``dw_window`` (an LmheadDwWindow): GRPO_LMHEAD_DEFER_DW,
+    the chunk's h^T and dz^T go to the window and dW (which may then be None)
+    is left for the window's flush.  ``on_launch``: as in loss_fwd_bwd."""
     torch = _torch()
     if h.dim() != 2 or W.dim() != 2:
         raise ValueError("h and W must be 2-D")
@@ -659,11 +697,12 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
     if dh is None:
         dh = torch.empty((n, H), dtype=torch.float32, device=h.device)
     if workspace is None and not noalloc:
-        workspace = torch.empty(max(lmhead_workspace_bytes(n, H, V, keep_z), 1), dtype=torch.uint8,
-                                device=h.device)
+        workspace = torch.empty(max(lmhead_workspace_bytes(n, H, V, keep_z, dw_window is not None), 1),
+                                dtype=torch.uint8, device=h.device)
     a = C.LmheadArgs()
     a.struct_size = ctypes.sizeof(C.LmheadArgs)
-    a.flags = C.LMHEAD_KEEP_Z if keep_z else 0
+    a.flags = (C.LMHEAD_KEEP_Z if keep_z else 0) | (C.LMHEAD_DEFER_DW if dw_window is not None else 0)
+    a.dw_window = ctypes.addressof(dw_window.w) if dw_window is not None else None
     a.ldh = _matrix(h, "h", n, H, ("bfloat16",))
     a.h = h.data_ptr() if n else None
     _matrix(W, "W", V, H, ("bfloat16",), dense=True)
@@ -676,10 +715,15 @@ def lmhead_fwd_bwd(h, W, Wt, target, mask, old_logp, tok_row_, adv_row, row_off,
     a.eps_low, a.eps_high, a.scale = eps_low, eps_high, scale
     _matrix(dh, "dh", n, H, ("float32",), dense=True)
     a.dh = dh.data_ptr() if n else None
-    _matrix(dW, "dW", V, H, ("float32",), dense=True)
-    if dW.shape[0] != V:
-        raise ValueError(f"dW must be [{V} x {H}]")
-    a.dW = dW.data_ptr()
+    if dW is None:
+        if dw_window is None:
+            raise ValueError("dW is required unless a dW window takes the chunk")
+        a.dW = None
+    else:
+        _matrix(dW, "dW", V, H, ("float32",), dense=True)
+        if dW.shape[0] != V:
+            raise ValueError(f"dW must be [{V} x {H}]")
+        a.dW = dW.data_ptr()
     if noalloc:
         if workspace is not None:
             raise ValueError("noalloc calls take no workspace")

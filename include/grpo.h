@@ -405,6 +405,47 @@ int grpo_stats_sum(const grpo_stats* rows, int64_t n, grpo_stats* out);
 int grpo_transpose_bf16(void* stream, const void* src, int64_t rows, int64_t cols, int64_t ld_src,
                         void* dst, int64_t ld_dst);
 
+/* The weight-gradient window: dW of several chunks as one GEMM.  [P1] "The
+ * hard part: deferred normalization": the step's gradient is the sum of its
+ * chunks' gradients, and dW = sum over the step's valid tokens of
+ * dz_t^T h_t needs nothing else of a chunk.  A chunk called with a window
+ * (GRPO_LMHEAD_DEFER_DW) appends h^T and dz^T of its valid tokens to it
+ * instead of multiplying them out; grpo_lmhead_dw_flush then adds the whole
+ * window's dz^T h to dW in one GEMM, whose K (the window's tokens) is long
+ * enough to amortise each tile's start and end, and dW is read and written
+ * once instead of once per chunk.  Plain data, caller-allocated; buf is
+ * device memory, the rest host fields.  Not thread-safe: one stream of calls
+ * per window. */
+typedef struct grpo_lmhead_dw_window {
+    void* buf;          /* device, >= grpo_lmhead_dw_window_size(cap_tok, H, V) bytes, 256-byte aligned:
+                         * a fill counter, then h^T [H x cap] and dz^T [V x cap] (bf16, cap = cap_tok
+                         * rounded up to 64) */
+    size_t bytes;
+    int64_t cap_tok;    /* tokens the window holds */
+    int64_t H, V;
+    int64_t reserved;   /* host: columns reserved by the calls since the last flush (each call
+                         * reserves n_tok rounded up to 64; its valid tokens fill the front of that) */
+} grpo_lmhead_dw_window;
+
+/* host.  Bytes of a window of cap_tok tokens (0 for bad sizes):
+ * 256 + 2 * cap * (H + V) rounded up to 256-byte parts, cap = cap_tok rounded
+ * up to 64.  At V = 151 936, H = 2048: ~0.31 MB per token. */
+size_t grpo_lmhead_dw_window_size(int64_t cap_tok, int64_t H, int64_t V);
+
+/* device.  Sets up w over buf and empties it (a kernel on `stream` clears the
+ * fill counter; nothing else needs to start at zero).  EINVAL for NULL or
+ * misaligned buf, bad sizes or cap_tok above 2^30; ECAPACITY if bytes is
+ * below grpo_lmhead_dw_window_size. */
+int grpo_lmhead_dw_window_init(void* stream, grpo_lmhead_dw_window* w, void* buf, size_t bytes, int64_t cap_tok,
+                               int64_t H, int64_t V);
+
+/* device.  dW (fp32 [V x H], 16-byte aligned) += the sum over the window's
+ * tokens of dz_t^T h_t (one bf16 MFMA GEMM, fp32 accumulation), then empties
+ * the window.  An empty window leaves dW as it is.  Calls on the stream
+ * before it must be the ones that filled the window.  EINVAL for a NULL or
+ * uninitialised window or dW. */
+int grpo_lmhead_dw_flush(void* stream, grpo_lmhead_dw_window* w, float* dW);
+
 /* Arguments of grpo_lmhead_fwd_bwd (all pointers are device pointers). */
 typedef struct grpo_lmhead_args {
     int32_t struct_size;        /* = sizeof(grpo_lmhead_args) */
@@ -423,10 +464,11 @@ typedef struct grpo_lmhead_args {
     int64_t n_rows;
     float eps_low, eps_high;    /* clip band */
     float scale;                /* gradient factor (see grpo_loss_args) */
-    int32_t flags;              /* 0, or GRPO_LMHEAD_KEEP_Z */
+    int32_t flags;              /* 0, or GRPO_LMHEAD_KEEP_Z and / or GRPO_LMHEAD_DEFER_DW */
     const int64_t* denom;       /* NULL or device int64 N: factor further divided by max(N, 1) */
     float* dh;                  /* fp32 [n_tok x H]: dL/dh, overwritten */
-    float* dW;                  /* fp32 [V x H], 16-byte aligned: dL/dW of this chunk is ADDED (accumulate) */
+    float* dW;                  /* fp32 [V x H], 16-byte aligned: dL/dW of this chunk is ADDED (accumulate);
+                                 * unused (may be NULL) with GRPO_LMHEAD_DEFER_DW */
     float* logp;                /* [n_tok] required */
     float* lse;                 /* [n_tok] or NULL */
     float* entropy;             /* [n_tok] required */
@@ -443,6 +485,7 @@ typedef struct grpo_lmhead_args {
     float kl_coef;
     int32_t kl_type;
     int32_t reserved2;
+    grpo_lmhead_dw_window* dw_window;   /* host pointer, with GRPO_LMHEAD_DEFER_DW (else NULL) */
 } grpo_lmhead_args;
 
 /* grpo_lmhead_args.flags: keep the chunk's logits.  Pass 1 stores z (fp32,
@@ -452,6 +495,15 @@ typedef struct grpo_lmhead_args {
  * 4 * n_tok * V bytes more: the chunk's [tokens x V] logits, which the default
  * path never holds.  Not available with grpo_lmhead_fwd_bwd_noalloc. */
 #define GRPO_LMHEAD_KEEP_Z 1
+
+/* grpo_lmhead_args.flags: defer dW.  The chunk's h^T and dz^T (its valid
+ * tokens, in order) go to args->dw_window instead of a dW GEMM; dW is not
+ * touched until grpo_lmhead_dw_flush.  The workspace then holds neither.
+ * ECAPACITY, before any launch, if the window's reserved columns plus n_tok
+ * rounded up to 64 exceed its cap_tok rounded up to 64 (flush first);
+ * EINVAL if the window is missing or its H, V differ from the call's, or
+ * with grpo_lmhead_fwd_bwd_noalloc. */
+#define GRPO_LMHEAD_DEFER_DW 2
 
 /* host.  Workspace bytes grpo_lmhead_fwd_bwd needs for a chunk of n_tok tokens
  * without flags: per-token slice partials of the log-softmax (16 B per token
@@ -463,7 +515,8 @@ size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V);
 
 /* host.  The same for the given flags.  With GRPO_LMHEAD_KEEP_Z: plus the
  * fp32 logits (4 * n_tok * V), and dz in two layouts for up to the whole
- * vocabulary (4 * n_tok * V) in place of one 65536-column chunk.  0 for
+ * vocabulary (4 * n_tok * V) in place of one 65536-column chunk.  With
+ * GRPO_LMHEAD_DEFER_DW: without h^T and dz^T (they go to the window).  0 for
  * unknown flags or bad sizes. */
 size_t grpo_lmhead_workspace_size_flags(int64_t n_tok, int64_t H, int64_t V, int32_t flags);
 
@@ -503,7 +556,8 @@ int grpo_lmhead_fwd_bwd(void* stream, const grpo_lmhead_args* args);
  * on one GPU share that GPU's scratch: calls that overlap on one GPU (two
  * streams, or two threads) race and must be serialised by the caller.
  * flags must be 0 (EINVAL for GRPO_LMHEAD_KEEP_Z: the logits do not fit the
- * scratch). */
+ * scratch; EINVAL for GRPO_LMHEAD_DEFER_DW: the window is a caller buffer of
+ * the workspace path). */
 int grpo_lmhead_fwd_bwd_noalloc(void* stream, const grpo_lmhead_args* args);
 
 /* ===================================================== frozen pi_old (ahead pass) */

@@ -282,6 +282,107 @@ def test_lmhead_all_masked_chunk():
     assert st["n_valid"] == 0 and st["loss_sum"] == 0.0
 
 
+def _chunk_calls(c, bounds, scale, dW=None, window=None, keep_z=False, Wt=None):
+    """Each [a, b) of ``bounds`` as a call of its own (one row, the advantage
+    adv[i] of chunk i).  Returns the per-token outputs of all chunks
+    concatenated and each token's advantage."""
+    if Wt is None:
+        Wt = ops.transpose_bf16(c["W"])
+    n = c["h"].shape[0]
+    adv_tok = np.zeros(n)
+    out = {k: [] for k in ("dh", "logp", "entropy", "loss_tok", "tok_flags")}
+    for i, (a, b) in enumerate(bounds):
+        A = float(c["adv"][i % len(c["adv"])])
+        adv_tok[a:b] = A
+        g = c["g"]
+        ws = ops.lmhead_fwd_bwd(c["h"][a:b], c["W"], Wt, g["target"][a:b], g["mask"][a:b], g["old"][a:b],
+                                torch.zeros(b - a, dtype=torch.int32, device=DEV),
+                                torch.tensor([A], dtype=torch.float32, device=DEV),
+                                torch.tensor([0, b - a], dtype=torch.int64, device=DEV), dW, scale=scale,
+                                keep_z=keep_z, dw_window=window)
+        for k in out:
+            out[k].append(ws[k].clone())
+    return {k: torch.cat(v) for k, v in out.items()}, adv_tok
+
+
+# GRPO_LMHEAD_DEFER_DW: chunks of 130, 1, 319 and 250 tokens (a one-token
+# chunk; columns 192 + 64 + 320 + 256 = 832 = the window's exact capacity)
+# append to one window; the flush adds the step's dW to a non-zero dW.  H =
+# 320 has a ragged 256-wide tile column; V = 70000 spans two pass-2 chunks on
+# the default path.  Against the oracle over all tokens, and against the
+# chunk-by-chunk dW: the same dz bits, so the two differ only by the order of
+# the float32 sums (row by row within 2^-16 of the products' magnitudes).
+@pytest.mark.parametrize("keep_z", [False, True])
+def test_deferred_dW_matches_oracle(keep_z):
+    n, H, V = 700, 320, 70000
+    print(f"deferred dW n={n} H={H} V={V} keep_z={keep_z}", flush=True)
+    c = _case(n, H, V, seed=77)
+    N = int(c["mask"].sum())
+    bounds = [(0, 130), (130, 131), (131, 450), (450, n)]
+    Wt = ops.transpose_bf16(c["W"])
+    win = ops.LmheadDwWindow(832, H, V, device=DEV)
+    out, adv_tok = _chunk_calls(c, bounds, 1.0 / N, window=win, keep_z=keep_z, Wt=Wt)
+    assert win.reserved == 832
+    base = torch.randn((V, H), generator=torch.Generator(device="cpu").manual_seed(8)).to(DEV) * 1e-3
+    dW = base.clone()
+    win.flush(dW)
+    assert win.reserved == 0
+    dW_chunked = torch.zeros((V, H), dtype=torch.float32, device=DEV)
+    out2, _ = _chunk_calls(c, bounds, 1.0 / N, dW=dW_chunked, keep_z=keep_z, Wt=Wt)
+    torch.cuda.synchronize()
+    for k in ("logp", "entropy", "loss_tok", "tok_flags"):
+        assert torch.equal(out[k], out2[k]), k
+    ref = _ref(c, {"tok_flags": out["tok_flags"]}, 1.0 / N, adv_tok=adv_tok)
+    _check(out, dW - base, ref, c, ref["dW"])
+    got, chunked = to_f64(dW - base), to_f64(dW_chunked)
+    mag = np.abs(ref["dz"]).T @ np.abs(c["h64"])
+    err = np.sqrt(np.sum((got - chunked) ** 2, axis=1))
+    assert np.all(err <= 2.0 ** -16 * np.sqrt(np.sum(mag ** 2, axis=1))), float(np.max(err))
+
+
+def test_dW_window_capacity_reuse_and_empty_flushes():
+    n, H, V = 200, 64, 1000
+    c = _case(n, H, V, seed=12)
+    N = int(c["mask"].sum())
+    Wt = ops.transpose_bf16(c["W"])
+    win = ops.LmheadDwWindow(256, H, V, device=DEV)
+    dW = torch.zeros((V, H), dtype=torch.float32, device=DEV)
+    # an empty window's flush leaves dW as it is
+    win.flush(dW)
+    out_a, adv_a = _chunk_calls(c, [(0, 200)], 1.0 / N, window=win, Wt=Wt)
+    assert win.reserved == 256
+    # no room for one more token: refused before any launch, nothing reserved
+    with pytest.raises(ops.GrpoError) as e:
+        _chunk_calls(c, [(0, 1)], 1.0 / N, window=win, Wt=Wt)
+    assert e.value.kind == "ECAPACITY" and win.reserved == 256
+    win.flush(dW)
+    torch.cuda.synchronize()
+    ref = _ref(c, {"tok_flags": out_a["tok_flags"]}, 1.0 / N, adv_tok=adv_a)
+    _check(out_a, dW, ref, c, ref["dW"])
+    # a second empty flush, and an all-masked chunk, change no bit of dW
+    before = dW.clone()
+    win.flush(dW)
+    masked = dict(c)
+    masked["g"] = dict(c["g"])
+    masked["g"]["mask"] = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    _chunk_calls(masked, [(0, 150)], 1.0 / N, window=win, Wt=Wt)
+    assert win.reserved == 192
+    win.flush(dW)
+    torch.cuda.synchronize()
+    assert torch.equal(dW, before) and win.reserved == 0
+    # the window starts over after a flush: the same chunk again doubles dW
+    _chunk_calls(c, [(0, 200)], 1.0 / N, window=win, Wt=Wt)
+    win.flush(dW)
+    torch.cuda.synchronize()
+    check_grad_rows(to_f64(dW), 2.0 * ref["dW"], 2.0 * np.abs(ref["dz"]).T @ np.abs(c["h64"]), "dW twice")
+    # the fixed-scratch entry point refuses the window
+    g = c["g"]
+    with pytest.raises(ops.GrpoError) as e:
+        ops.lmhead_fwd_bwd(c["h"], c["W"], Wt, g["target"], g["mask"], g["old"], g["tok_row"], g["adv"],
+                           g["row_off"], None, noalloc=True, dw_window=win)
+    assert e.value.kind == "EINVAL"
+
+
 def test_lmhead_rejects_small_workspace_and_bad_shapes():
     c = _case(8, 64, 256, seed=1)
     Wt = ops.transpose_bf16(c["W"])

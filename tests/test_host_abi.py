@@ -59,7 +59,10 @@ int main(void) {
   F(grpo_lmhead_args, Wt) F(grpo_lmhead_args, n_rows) F(grpo_lmhead_args, denom) F(grpo_lmhead_args, workspace_bytes)
   F(grpo_loss_args, row_weight) F(grpo_loss_args, kl_tok) F(grpo_loss_args, kl_type)
   F(grpo_lmhead_args, row_weight) F(grpo_lmhead_args, ent_coef) F(grpo_lmhead_args, kl_type)
-  F(grpo_lmhead_args, flags)
+  F(grpo_lmhead_args, flags) F(grpo_lmhead_args, dw_window)
+  printf("grpo_lmhead_dw_window %zu\n", sizeof(grpo_lmhead_dw_window));
+  F(grpo_lmhead_dw_window, bytes) F(grpo_lmhead_dw_window, cap_tok) F(grpo_lmhead_dw_window, V)
+  F(grpo_lmhead_dw_window, reserved)
   F(grpo_stats, kl_sum) F(grpo_stats, obj_sum) F(grpo_stats, n_valid_rows)
   F(grpo_step_result, kl) F(grpo_step_result, obj_sum) F(grpo_step_result, n_clipped)
   return 0;
@@ -72,11 +75,13 @@ int main(void) {
     assert int(got["grpo_loss_args"]) == ctypes.sizeof(C.LossArgs)
     assert int(got["grpo_step_result"]) == ctypes.sizeof(C.StepResult)
     assert int(got["grpo_lmhead_args"]) == ctypes.sizeof(C.LmheadArgs)
+    assert int(got["grpo_lmhead_dw_window"]) == ctypes.sizeof(C.DwWindow)
     for key, v in got.items():
         if "." in key:
             struct, field = key.split(".")
             cls = {"grpo_loss_args": C.LossArgs, "grpo_lmhead_args": C.LmheadArgs,
-                   "grpo_stats": C.Stats, "grpo_step_result": C.StepResult}[struct]
+                   "grpo_stats": C.Stats, "grpo_step_result": C.StepResult,
+                   "grpo_lmhead_dw_window": C.DwWindow}[struct]
             assert getattr(cls, field).offset == int(v), key
 
 
@@ -377,6 +382,74 @@ def test_lmhead_workspace_sizes():
     assert keep >= base + 8 * n * V - 4 * n * 65536
     grow_keep = L.grpo_lmhead_workspace_size_flags(n, H, 2 * V, C.LMHEAD_KEEP_Z) - keep
     assert grow_keep >= 8 * n * V
-    assert L.grpo_lmhead_workspace_size_flags(n, H, V, 2) == 0           # unknown flag
+    # GRPO_LMHEAD_DEFER_DW: h^T and one chunk of dz^T leave the workspace
+    n_pad = (n + 63) // 64 * 64
+    defer = L.grpo_lmhead_workspace_size_flags(n, H, V, C.LMHEAD_DEFER_DW)
+    assert base - defer >= 2 * n_pad * (H + 65536) - 512
+    both = L.grpo_lmhead_workspace_size_flags(n, H, V, C.LMHEAD_KEEP_Z | C.LMHEAD_DEFER_DW)
+    assert keep - both >= 2 * n_pad * (H + V) - 512
+    assert L.grpo_lmhead_workspace_size_flags(n, H, V, 4) == 0           # unknown flag
     assert L.grpo_lmhead_workspace_size_flags(-1, H, V, 0) == 0
     assert L.grpo_lmhead_workspace_size_flags(0, H, V, C.LMHEAD_KEEP_Z) > 0
+
+
+def _lmhead_args(n, H, V, flags=0, window=None):
+    """grpo_lmhead_args with stand-in device addresses: every call below is
+    refused by the host checks before anything touches them."""
+    a = C.LmheadArgs()
+    a.struct_size = ctypes.sizeof(C.LmheadArgs)
+    fake = 1 << 40
+    a.h, a.ldh, a.W, a.Wt, a.dW = fake, H, fake, fake, fake
+    a.n_tok, a.H, a.V = n, H, V
+    for f in ("target", "mask", "old_logp", "tok_row", "adv_row", "row_off", "dh", "logp", "entropy", "loss_tok",
+              "tok_flags", "row_stats", "chunk_stats", "workspace"):
+        setattr(a, f, fake)
+    a.n_rows, a.eps_low, a.eps_high, a.scale = 1, 0.2, 0.2, 1.0
+    a.workspace_bytes = 1 << 50
+    a.flags = flags
+    a.dw_window = ctypes.addressof(window) if window is not None else None
+    return a
+
+
+@pytest.mark.skipif(C.HOST_ONLY, reason="the host-only sanitizer build carries no device entry points")
+def test_lmhead_dw_window_sizes_and_refusals():
+    L = C.lib()
+    kind = lambda rc: C.CODES[rc]  # noqa: E731
+    H, V = 2048, 151936
+    cap = (1000 + 63) // 64 * 64
+    r256 = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    need = L.grpo_lmhead_dw_window_size(1000, H, V)
+    assert need == 256 + r256(2 * H * cap) + r256(2 * V * cap)
+    for bad in ((0, H, V), ((1 << 30) + 1, H, V), (64, 7, V), (64, H, 0), (64, H, 12)):
+        assert L.grpo_lmhead_dw_window_size(*bad) == 0
+    # set-up refusals (no kernel is launched before these checks)
+    w = C.DwWindow()
+    fake = 1 << 40
+    assert kind(L.grpo_lmhead_dw_window_init(None, None, fake, need, 1000, H, V)) == "EINVAL"
+    assert kind(L.grpo_lmhead_dw_window_init(None, ctypes.byref(w), fake + 16, need, 1000, H, V)) == "EINVAL"
+    assert kind(L.grpo_lmhead_dw_window_init(None, ctypes.byref(w), fake, need, 1000, H, 12)) == "EINVAL"
+    assert kind(L.grpo_lmhead_dw_window_init(None, ctypes.byref(w), fake, need - 1, 1000, H, V)) == "ECAPACITY"
+    # a window as init leaves it, filled by hand (host fields only)
+    w.buf, w.bytes, w.cap_tok, w.H, w.V, w.reserved = fake, need, 1000, H, V, 0
+    assert kind(L.grpo_lmhead_dw_flush(None, None, fake)) == "EINVAL"
+    assert kind(L.grpo_lmhead_dw_flush(None, ctypes.byref(w), None)) == "EINVAL"
+    assert kind(L.grpo_lmhead_dw_flush(None, ctypes.byref(w), fake)) == "OK"        # empty: nothing to launch
+    w.reserved = 100                                                                # not a multiple of 64
+    assert kind(L.grpo_lmhead_dw_flush(None, ctypes.byref(w), fake)) == "EINVAL"
+    w.reserved = 0
+    # the loss call: the flag and the window go together, sizes must match,
+    # the window must have room, and the fixed-scratch entry point refuses it
+    D = C.LMHEAD_DEFER_DW
+    call = lambda a: kind(L.grpo_lmhead_fwd_bwd(None, ctypes.byref(a)))  # noqa: E731
+    assert call(_lmhead_args(100, H, V, D, None)) == "EINVAL"
+    assert call(_lmhead_args(100, H, V, 0, w)) == "EINVAL"
+    assert call(_lmhead_args(100, H, V - 8, D, w)) == "EINVAL"
+    assert call(_lmhead_args(1025, H, V, D, w)) == "ECAPACITY"       # 1088 columns > the window's 1024
+    w.reserved = 960
+    assert call(_lmhead_args(65, H, V, D, w)) == "ECAPACITY"         # 960 + 128 > 1024
+    assert w.reserved == 960                                           # a refused call reserves nothing
+    a = _lmhead_args(100, H, V, D, w)
+    assert kind(L.grpo_lmhead_fwd_bwd_noalloc(None, ctypes.byref(a))) == "EINVAL"
+    a = _lmhead_args(100, H, V, C.LMHEAD_KEEP_Z, None)
+    a.dW = None                                                        # dW is required unless deferred
+    assert call(a) == "EINVAL"

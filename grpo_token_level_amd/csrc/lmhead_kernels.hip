@@ -669,25 +669,48 @@ __global__ __launch_bounds__(256) void dz_from_z_kernel(const DzArgs a) {
 }
 
 // dh row t (H floats) = sum over s, in order, of the partials of t's compact
-// row inv[t]; a masked token (inv[t] < 0) gets a zero row.  The split count:
-// nsplit, or the dh GEMM's rule at the valid-token count (rule.cap > 0).
-// Block (x, y): columns [256x, 256x + 256) of tokens y, y + gridDim.y, ...
+// row inv[t]; a masked token (inv[t] < 0) gets a zero row.  The split count
+// (<= kDhSplitMax): nsplit, or the dh GEMM's rule at the valid-token count
+// (rule.cap > 0).  A thread sums four columns of a token, with every split's
+// 16-byte load issued before the in-order adds (H % 4 == 0; dst rows 16-byte
+// aligned when dst_vec).  Block (x, y): columns [1024x, 1024x + 1024) of
+// tokens y, y + gridDim.y, ...
 __global__ __launch_bounds__(256) void sum_splits_kernel(float* __restrict__ dst, int64_t ld_dst,
                                                          const float* __restrict__ parts, int nsplit, int64_t c_split,
                                                          const int32_t* __restrict__ inv, int64_t n, int64_t H,
-                                                         const int32_t* __restrict__ count, const SplitRule rule) {
-    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+                                                         const int32_t* __restrict__ count, const SplitRule rule,
+                                                         int dst_vec) {
+    const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= H) return;
     if (rule.cap > 0) nsplit = dev_split_count(rule, *count);
     for (int64_t t = blockIdx.y; t < n; t += gridDim.y) {
         const int32_t j = inv[t];
-        float s = 0.0f;
+        float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (j >= 0) {
             const float* p = parts + (int64_t)j * H + c;
-            s = p[0];
-            for (int k = 1; k < nsplit; ++k) s += p[(int64_t)k * c_split];
+            float4 v[kDhSplitMax];
+#pragma unroll
+            for (int k = 0; k < kDhSplitMax; ++k)
+                if (k < nsplit) v[k] = *reinterpret_cast<const float4*>(p + (int64_t)k * c_split);
+            s = v[0];
+#pragma unroll
+            for (int k = 1; k < kDhSplitMax; ++k)
+                if (k < nsplit) {
+                    s.x += v[k].x;
+                    s.y += v[k].y;
+                    s.z += v[k].z;
+                    s.w += v[k].w;
+                }
         }
-        dst[t * ld_dst + c] = s;
+        float* d = dst + t * ld_dst + c;
+        if (dst_vec) {
+            *reinterpret_cast<float4*>(d) = s;
+        } else {
+            d[0] = s.x;
+            d[1] = s.y;
+            d[2] = s.z;
+            d[3] = s.w;
+        }
     }
 }
 
@@ -1405,8 +1428,9 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
         // the host bound moves with the counter (the counter never passes it)
         win->reserved += reserve;
     }
-    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((H + 255) / 256), (unsigned)(n < 65535 ? n : 65535)),
-                       dim3(256), 0, st, a->dh, H, w.dh_part, nsplit, n * H, w.inv, n, H, w.count, rule);
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((H + 1023) / 1024), (unsigned)(n < 65535 ? n : 65535)),
+                       dim3(256), 0, st, a->dh, H, w.dh_part, nsplit, n * H, w.inv, n, H, w.count, rule,
+                       (int)al16(a->dh));
     if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "dh splits");
     return ok();
 }

@@ -1003,7 +1003,9 @@ Pass2Plan plan_pass2(int64_t n, int64_t H, int64_t V, int64_t cus, int64_t chunk
     Pass2Plan best{V < wcap ? V : wcap, 1, -1.0};
     double best_cost = -1.0;
     const int64_t wmax = V < wcap ? round_up(V, BN) : wcap;
-    const int64_t wmin = wmax < kVocabChunkMin ? wmax : kVocabChunkMin;
+    // with the logits kept, one chunk over all of V: one dh launch per call and
+    // partials written once, not rewritten (measured 0.4-0.9 % on the step)
+    const int64_t wmin = stash ? wmax : (wmax < kVocabChunkMin ? wmax : kVocabChunkMin);
     for (int64_t w = wmin; w <= wmax; w += 2048 > wmax - wmin ? BN : 2048) {
         for (int sp = 1; sp <= split_cap; ++sp) {
             int64_t steps = 0, chunks = 0;

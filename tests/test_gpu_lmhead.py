@@ -484,6 +484,34 @@ def test_compaction_workload_full_size_sampled():
     col = dW.double().sum(0).abs()
     scale_ref = dW.double().abs().sum(0)
     assert float((col / scale_ref).max()) <= 1e-2
+    # The step's chunks again, through one dW window (GRPO_LMHEAD_DEFER_DW, 23.6 GB
+    # here): the same dz bits, so the flushed dW differs from the chunk-by-chunk dW
+    # only by the order of its float32 sums over the step's 64.6 k valid tokens
+    # (relative L2 <= 1e-4), and the per-token outputs are equal bit for bit (dh
+    # rows to float32 summation order: the plan may split its vocabulary otherwise)
+    print("compaction: the step's chunks through one dW window", flush=True)
+    win = ops.LmheadDwWindow(sum((int(off[e] - off[a]) + 63) // 64 * 64 for a, e in chunks), H, V, device=DEV)
+    out_w = {kk: torch.empty_like(v) for kk, v in out.items()}
+    dh_w = torch.empty_like(dh)
+    for k, (a, e) in enumerate(chunks):
+        t0, t1 = int(off[a]), int(off[e])
+        ro = G(off[a:e + 1] - off[a])
+        ws = {kk: out_w[kk][t0:t1] for kk in out_w}
+        ws["row_stats"] = row_stats[a:e]
+        ws["chunk_stats"] = stats[k:k + 1]
+        ops.lmhead_fwd_bwd(h[t0:t1], W, Wt, tgt_d[t0:t1], mask_d[t0:t1], old[t0:t1], ops.tok_row(ro, t1 - t0),
+                           G(adv_row[a:e]), ro, None, denom=N, dh=dh_w[t0:t1], ws=ws, workspace=workspace,
+                           dw_window=win)
+    dW_w = torch.zeros_like(dW)
+    win.flush(dW_w)
+    torch.cuda.synchronize()
+    for key in ("logp", "entropy", "loss_tok", "tok_flags"):
+        assert torch.equal(out_w[key], out[key]), key
+    assert bool(((dh_w - dh).norm(dim=1) <= 1e-5 * dh.norm(dim=1) + 1e-30).all())
+    rel = float((dW_w - dW).norm() / dW.norm())
+    assert rel <= 1e-4, rel
+    print(f"compaction: window dW vs chunk-by-chunk dW, relative L2 {rel:.2e}", flush=True)
+    del win, dW_w, dh_w, out_w
     del dW
     gc.collect()
     torch.cuda.empty_cache()

@@ -1096,7 +1096,8 @@ int64_t stash_chunk_cap(int64_t V) { return round_up(V, BN); }
 extern "C" size_t grpo_lmhead_workspace_size_flags(int64_t n_tok, int64_t H, int64_t V, int32_t flags) {
     if (n_tok < 0 || H <= 0 || V <= 0 || (flags & ~(GRPO_LMHEAD_KEEP_Z | GRPO_LMHEAD_DEFER_DW))) return 0;
     const bool stash = (flags & GRPO_LMHEAD_KEEP_Z) != 0, defer = (flags & GRPO_LMHEAD_DEFER_DW) != 0;
-    return carve(nullptr, n_tok, H, V, stash ? stash_chunk_cap(V) : kVocabChunkMax, kDhSplitMax, stash, defer).bytes;
+    return carve(nullptr, n_tok, H, V, (stash || defer) ? stash_chunk_cap(V) : kVocabChunkMax, kDhSplitMax, stash,
+                 defer).bytes;
 }
 
 namespace {
@@ -1327,7 +1328,10 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
         const size_t need = grpo_lmhead_workspace_size_flags(n, H, V, a->flags);
         if (!a->workspace || a->workspace_bytes < need || !al16(a->workspace))
             return fail(GRPO_ECAPACITY, "grpo_lmhead_fwd_bwd: workspace of %zu bytes needed (16-byte aligned)", need);
-        if (stash) chunk_cap = stash_chunk_cap(V);
+        // with the logits kept or dz^T in a window the workspace holds no dz^T
+        // chunk, and the chunk may span all of V (measured +0.9 % on the step with
+        // the window alone; the plan still chooses the width)
+        if (stash || defer) chunk_cap = stash_chunk_cap(V);
         plan = plan_pass2(n, H, V, cus, chunk_cap, split_cap, stash, defer);
     }
     hipStream_t st = (hipStream_t)stream;

@@ -516,8 +516,9 @@ size_t grpo_lmhead_workspace_size(int64_t n_tok, int64_t H, int64_t V);
 /* host.  The same for the given flags.  With GRPO_LMHEAD_KEEP_Z: plus the
  * fp32 logits (4 * n_tok * V), and dz in two layouts for up to the whole
  * vocabulary (4 * n_tok * V) in place of one 65536-column chunk.  With
- * GRPO_LMHEAD_DEFER_DW: without h^T and dz^T (they go to the window).  0 for
- * unknown flags or bad sizes. */
+ * GRPO_LMHEAD_DEFER_DW: without h^T and dz^T (they go to the window), and dz
+ * (bf16) for up to the whole vocabulary (2 * n_tok * V).  0 for unknown flags
+ * or bad sizes. */
 size_t grpo_lmhead_workspace_size_flags(int64_t n_tok, int64_t H, int64_t V, int32_t flags);
 
 /* device.  The fused loss of grpo_loss_fwd_bwd with the logits produced by the

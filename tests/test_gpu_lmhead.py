@@ -340,6 +340,38 @@ def test_deferred_dW_matches_oracle(keep_z):
     assert np.all(err <= 2.0 ** -16 * np.sqrt(np.sum(mag ** 2, axis=1))), float(np.max(err))
 
 
+def _random_window_cases(count=12, seed=31):
+    """Seeded random chunk splits through one dW window: tokens 2..1499 in 1-5
+    chunks, H and V multiples of 8 (V up to 96000), masked fraction drawn,
+    kept logits on half of them, and a window with 0-2 spare 64-column blocks."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(count):
+        n = int(rng.integers(2, 1500))
+        H = 8 * int(rng.integers(1, 129))
+        V = 8 * int(np.exp(rng.uniform(np.log(2), np.log(12000))))
+        n = max(2, min(n, int(8e10 // (H * V))))
+        keep = bool(rng.random() < 0.5)
+        cuts = np.sort(rng.choice(np.arange(1, n), size=min(int(rng.integers(0, 5)), n - 1), replace=False))
+        bounds = tuple(zip([0, *cuts.tolist()], [*cuts.tolist(), n]))
+        out.append((k, n, H, V, keep, bounds, float(rng.choice([0.0, 0.2, 0.9])), int(rng.integers(0, 3))))
+    return out
+
+
+@pytest.mark.parametrize("k,n,H,V,keep_z,bounds,masked,spare", _random_window_cases())
+def test_random_chunk_splits_through_a_window_match_oracle(k, n, H, V, keep_z, bounds, masked, spare):
+    print(f"window random k={k} n={n} H={H} V={V} keep_z={keep_z} chunks={len(bounds)}", flush=True)
+    c = _case(n, H, V, seed=6000 + k, masked_frac=masked)
+    N = max(1, int(c["mask"].sum()))
+    win = ops.LmheadDwWindow(sum((b - a + 63) // 64 * 64 for a, b in bounds) + 64 * spare, H, V, device=DEV)
+    out, adv_tok = _chunk_calls(c, list(bounds), 1.0 / N, window=win, keep_z=keep_z)
+    dW = torch.zeros((V, H), dtype=torch.float32, device=DEV)
+    win.flush(dW)
+    torch.cuda.synchronize()
+    ref = _ref(c, {"tok_flags": out["tok_flags"]}, 1.0 / N, adv_tok=adv_tok)
+    _check(out, dW, ref, c, ref["dW"])
+
+
 def test_dW_window_capacity_reuse_and_empty_flushes():
     n, H, V = 200, 64, 1000
     c = _case(n, H, V, seed=12)
@@ -491,6 +523,8 @@ def test_compaction_workload_full_size_sampled():
     # rows to float32 summation order: the plan may split its vocabulary otherwise)
     print("compaction: the step's chunks through one dW window", flush=True)
     win = ops.LmheadDwWindow(sum((int(off[e] - off[a]) + 63) // 64 * 64 for a, e in chunks), H, V, device=DEV)
+    ws_defer = torch.empty(ops.lmhead_workspace_bytes(int(max(off[e] - off[a] for a, e in chunks)), H, V,
+                                                      defer_dw=True), dtype=torch.uint8, device=DEV)
     out_w = {kk: torch.empty_like(v) for kk, v in out.items()}
     dh_w = torch.empty_like(dh)
     for k, (a, e) in enumerate(chunks):
@@ -500,7 +534,7 @@ def test_compaction_workload_full_size_sampled():
         ws["row_stats"] = row_stats[a:e]
         ws["chunk_stats"] = stats[k:k + 1]
         ops.lmhead_fwd_bwd(h[t0:t1], W, Wt, tgt_d[t0:t1], mask_d[t0:t1], old[t0:t1], ops.tok_row(ro, t1 - t0),
-                           G(adv_row[a:e]), ro, None, denom=N, dh=dh_w[t0:t1], ws=ws, workspace=workspace,
+                           G(adv_row[a:e]), ro, None, denom=N, dh=dh_w[t0:t1], ws=ws, workspace=ws_defer,
                            dw_window=win)
     dW_w = torch.zeros_like(dW)
     win.flush(dW_w)
@@ -511,7 +545,7 @@ def test_compaction_workload_full_size_sampled():
     rel = float((dW_w - dW).norm() / dW.norm())
     assert rel <= 1e-4, rel
     print(f"compaction: window dW vs chunk-by-chunk dW, relative L2 {rel:.2e}", flush=True)
-    del win, dW_w, dh_w, out_w
+    del win, ws_defer, dW_w, dh_w, out_w
     del dW
     gc.collect()
     torch.cuda.empty_cache()

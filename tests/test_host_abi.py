@@ -382,10 +382,12 @@ def test_lmhead_workspace_sizes():
     assert keep >= base + 8 * n * V - 4 * n * 65536
     grow_keep = L.grpo_lmhead_workspace_size_flags(n, H, 2 * V, C.LMHEAD_KEEP_Z) - keep
     assert grow_keep >= 8 * n * V
-    # GRPO_LMHEAD_DEFER_DW: h^T and one chunk of dz^T leave the workspace
+    # GRPO_LMHEAD_DEFER_DW: h^T and the chunk of dz^T leave the workspace, and dz
+    # spans up to the whole vocabulary
     n_pad = (n + 63) // 64 * 64
     defer = L.grpo_lmhead_workspace_size_flags(n, H, V, C.LMHEAD_DEFER_DW)
-    assert base - defer >= 2 * n_pad * (H + 65536) - 512
+    assert defer >= 2 * n * V
+    assert defer <= base + 2 * n * ((V + 255) // 256 * 256) - 2 * n_pad * (H + 65536) + 4096
     both = L.grpo_lmhead_workspace_size_flags(n, H, V, C.LMHEAD_KEEP_Z | C.LMHEAD_DEFER_DW)
     assert keep - both >= 2 * n_pad * (H + V) - 512
     assert L.grpo_lmhead_workspace_size_flags(n, H, V, 4) == 0           # unknown flag

@@ -464,8 +464,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_nt_kernel(const GemmArgs g) 
                 const char* src = tcol + nloc * DZT_ROWB + c * 16;
                 const uint2 lo = *reinterpret_cast<const uint2*>(src);
                 const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
-                *reinterpret_cast<uint4*>(g.dzT + (int64_t)nl * g.ld_dzT + koff + m) =
-                    make_uint4(lo.x, lo.y, hi.x, hi.y);
+                // non-temporal: dz^T is read by a later GEMM (measured +0.4-0.5 %)
+                const u32x4 v4 = {lo.x, lo.y, hi.x, hi.y};
+                __builtin_nontemporal_store(v4, reinterpret_cast<u32x4*>(g.dzT + (int64_t)nl * g.ld_dzT + koff + m));
             }
         }
         // then the same buffer as [token][column]: 2-byte writes of the kept

@@ -837,8 +837,18 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const MergeArgs a) {
         return;
     }
     float M = 0.0f, S = 0.0f, W = 0.0f;
-    for (int p = lane; p < a.n_parts; p += 64) {
-        const float4 q = a.part[(int64_t)j * a.n_parts + p];
+    // four slices' loads in flight per lane, merged in the same order as one at a time
+    const float4* pp = a.part + (int64_t)j * a.n_parts;
+    int p = lane;
+    for (; p + 192 < a.n_parts; p += 256) {
+        const float4 q0 = pp[p], q1 = pp[p + 64], q2 = pp[p + 128], q3 = pp[p + 192];
+        merge_part(M, S, W, q0.x, q0.y, q0.z);
+        merge_part(M, S, W, q1.x, q1.y, q1.z);
+        merge_part(M, S, W, q2.x, q2.y, q2.z);
+        merge_part(M, S, W, q3.x, q3.y, q3.z);
+    }
+    for (; p < a.n_parts; p += 64) {
+        const float4 q = pp[p];
         merge_part(M, S, W, q.x, q.y, q.z);
     }
 #pragma unroll
@@ -888,16 +898,19 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const MergeArgs a) {
 // is set; columns [rows, rows_pad) of dst are written as zeros.  With dst_off
 // (a dW window's device fill), off = *dst_off and rows_pad is cut to rows
 // rounded up to 64, so that the window's next call starts there.  64x64
-// tiles through LDS.
+// tiles through LDS, moved as pieces of eight elements: 16-byte loads and
+// stores when vec (src and dst 16-byte aligned, ld_src and ld_dst multiples
+// of 8), element by element otherwise and at the edges.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t rows,
                                                              int64_t cols, int64_t ld_src, uint16_t* __restrict__ dst,
                                                              int64_t ld_dst, int64_t rows_pad,
                                                              const int32_t* __restrict__ rmap,
                                                              const int32_t* __restrict__ rcount,
-                                                             const int32_t* __restrict__ dst_off) {
-    __shared__ uint16_t tile[64][66];
+                                                             const int32_t* __restrict__ dst_off, int vec) {
+    // tile[r][c]: 64 source rows of 64 columns, rows 144 bytes apart (16-byte pieces stay aligned)
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
     const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
     if (rcount && *rcount < rows) rows = *rcount;
     if (dst_off) {
         dst += *dst_off;
@@ -905,14 +918,42 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
         if (rp < rows_pad) rows_pad = rp;
     }
     if (r0 >= rows_pad) return;   // block-uniform
-    for (int k = ty; k < 64; k += 4) {
-        const int64_t r = r0 + k, c = c0 + tx;
-        tile[k][tx] = (r < rows && c < cols) ? src[(rmap ? (int64_t)rmap[r] : r) * ld_src + c] : (uint16_t)0;
+    // in: piece i of 512 is source row i/8, columns (i%8)*8 .. +8 (zeros past rows and cols)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int i = h * 256 + tid, r = i >> 3, cc = (i & 7) * 8;
+        const int64_t gr = r0 + r, gc = c0 + cc;
+        uint4 q = make_uint4(0u, 0u, 0u, 0u);
+        if (gr < rows) {
+            const uint16_t* sp = src + (rmap ? (int64_t)rmap[gr] : gr) * ld_src + gc;
+            if (vec && gc + 8 <= cols) {
+                q = *reinterpret_cast<const uint4*>(sp);
+            } else {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+                for (int e = 0; e < 8; ++e)
+                    if (gc + e < cols) w[e >> 1] |= (uint32_t)sp[e] << ((e & 1) * 16);
+                q = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        *reinterpret_cast<uint4*>(&tile[r][cc]) = q;
     }
     __syncthreads();
-    for (int k = ty; k < 64; k += 4) {
-        const int64_t c = c0 + k, r = r0 + tx;
-        if (c < cols && r < rows_pad) dst[c * ld_dst + r] = tile[tx][k];
+    // out: piece i of 512 is destination row (source column) i/8, tokens (i%8)*8 .. +8
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int i = h * 256 + tid, c = i >> 3, rr = (i & 7) * 8;
+        const int64_t gc = c0 + c, gr = r0 + rr;
+        if (gc >= cols || gr >= rows_pad) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[rr + 2 * e][c] | ((uint32_t)tile[rr + 2 * e + 1][c] << 16);
+        uint16_t* dp = dst + gc * ld_dst + gr;
+        if (vec && gr + 8 <= rows_pad) {
+            *reinterpret_cast<uint4*>(dp) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            for (int e = 0; e < 8; ++e)
+                if (gr + e < rows_pad) dp[e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+        }
     }
 }
 
@@ -1172,7 +1213,8 @@ extern "C" int grpo_transpose_bf16(void* stream, const void* src, int64_t rows, 
         return fail(GRPO_EINVAL, "grpo_transpose_bf16: too many rows for one launch");
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64)),
                        dim3(256), 0, (hipStream_t)stream, (const uint16_t*)src, rows, cols, ld_src, (uint16_t*)dst,
-                       ld_dst, rows, nullptr, nullptr, nullptr);
+                       ld_dst, rows, nullptr, nullptr, nullptr, (int)(al16(src) && al16(dst) && ld_src % 8 == 0 &&
+                                                                      ld_dst % 8 == 0));
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? ok() : fail(GRPO_EDEVICE, "grpo_transpose_bf16: %s", hipGetErrorString(e));
 }
@@ -1362,7 +1404,8 @@ int lmhead_run(void* stream, const grpo_lmhead_args* a, bool noalloc) {
 
     // h^T of the valid tokens, zero columns up to n_pad (the K operand of dW's GEMM)
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((H + 63) / 64), (unsigned)((n_pad + 63) / 64)),
-                       dim3(256), 0, st, h, n, H, a->ldh, hT, ld_T, n_pad, w.vidx, w.count, fill);
+                       dim3(256), 0, st, h, n, H, a->ldh, hT, ld_T, n_pad, w.vidx, w.count, fill,
+                       (int)(al16(h) && al16(hT) && a->ldh % 8 == 0 && ld_T % 8 == 0));
     if ((e = hipGetLastError()) != hipSuccess) return dev_fail(e, "transpose h");
 
     // pass 1: slice partials of the log-softmax and the target logit

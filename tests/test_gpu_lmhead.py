@@ -415,6 +415,26 @@ def test_dW_window_capacity_reuse_and_empty_flushes():
     assert e.value.kind == "EINVAL"
 
 
+# grpo_transpose_bf16 equals torch's transpose bit for bit: the 16-byte path
+# (aligned pointers, row strides multiples of 8) and the element-wise one
+# (a source stride of 1003, a destination view one element off 16-byte
+# alignment), ragged edges of the 64 x 64 tiles, and the LM head's W
+@pytest.mark.parametrize("rows,cols,ld_src,out_off", [(1, 1, 1, 0), (7, 13, 13, 0), (64, 64, 64, 0),
+                                                     (65, 130, 136, 0), (300, 1000, 1003, 0), (257, 520, 520, 1),
+                                                     (151936, 2048, 2048 + 8, 0)])
+def test_transpose_bf16_matches_torch(rows, cols, ld_src, out_off):
+    print(f"transpose rows={rows} cols={cols} ld_src={ld_src} out_off={out_off}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(rows + cols)
+    base = torch.randn((rows, ld_src), generator=g, device=DEV).to(torch.bfloat16)
+    x = base[:, :cols]
+    store = torch.full((cols * rows + out_off,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = store[out_off:].view(cols, rows)
+    ops.transpose_bf16(x, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, x.t())
+    assert out_off == 0 or float(store[0]) == 7.0
+
+
 def test_lmhead_rejects_small_workspace_and_bad_shapes():
     c = _case(8, 64, 256, seed=1)
     Wt = ops.transpose_bf16(c["W"])

@@ -764,6 +764,9 @@ def main():
             sys.exit(2)
         extra.setdefault("over", {})["V"] = args.vocab
     step = cls(wl, args.seed, torch, ops, timed, **extra)
+    # device memory of the steps alone (the set-up's own peak is left out)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
     # A full garbage collection walks every tracked Python object, most of them
     # torch's own (~170 k): tens of milliseconds on one host thread.  Inside the
     # timed steps such a pause can fall between a launch's start event and the
@@ -841,6 +844,11 @@ def main():
             if rec is not None:
                 roof["traffic"] = rec["traffic_bytes_per_launch"]
     cfg["llc"] = step.llc_note() if hasattr(step, "llc_note") else None
+    if wl == "compact":
+        # the LM head's memory claim: the default path never holds a [tokens x V]
+        # matrix (the kept logits and the dW window do, on request)
+        cfg["peak_device_GB"] = round(torch.cuda.max_memory_allocated() / 1e9, 2)
+        cfg["tokens_x_V_bf16_GB"] = round(int(step.off[-1]) * step.V * 2 / 1e9, 2)
     out = {"metric": METRIC, "value": round(value, 1), "unit": "valid tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "ms_per_step_median": round(median_ms, 4),
            "higher_is_better": True, "scaling": "weak",
